@@ -1,0 +1,294 @@
+"""Python binding of libcsa2 (CSA2 decode hot path, HIP for MI355X / gfx950).
+
+Argument marshalling only: torch tensors on the GPU are checked for dtype,
+shape and contiguity, and their device pointers plus torch's current HIP
+stream are passed to the C ABI declared in include/csa2.h.  Every step of the
+path runs in the library's kernels; there is no fallback.  If libcsa2.so is
+missing or cannot be loaded, importing the binding's entry points raises.
+
+torch is imported before the library is loaded so that both use the one HIP
+runtime torch has already mapped (they share the soname libamdhip64.so.7).
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa2.so")
+
+HEAD_DIM = 128
+KV_CODE_BYTES = 128
+KV_SCALE_BYTES = 16
+IDX_HEADS = 4
+IDX_DIM = 64
+IDX_TILE = 64
+BLOCK = 8
+WINDOW = 128
+DEFAULT_TOPK = 512
+DEFAULT_POOL_BLOCKS = 2048
+
+FP8_ROWS = 0
+FP8_IDX_TILED = 1
+OP_INDEX_FULL = 1
+OP_INDEX_REINDEX = 2
+OP_ATTN_DECODE = 3
+OP_ATTN_CHUNK = 4
+
+STATUS = {0: "ok", -1: "CSA2_E_ARG", -2: "CSA2_E_UNSUPPORTED", -3: "CSA2_E_WORKSPACE",
+          -4: "CSA2_E_HIP"}
+
+EXPORTS = ("csa2_quant_fp4", "csa2_quant_fp8", "csa2_index_full", "csa2_index_reindex",
+           "csa2_sparse_attn_decode", "csa2_sparse_attn_chunk", "csa2_workspace_size",
+           "csa2_status_str", "csa2_abi_version", "csa2_codec_probe")
+
+_lib = None
+
+_vp, _i64, _int, _f, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "csa2_quant_fp4": (_int, [_vp, _vp, _i64, _int, _vp, _vp, _vp, _vp, _vp]),
+    "csa2_quant_fp8": (_int, [_vp, _i64, _int, _int, _vp, _vp, _vp, _vp]),
+    "csa2_index_full": (_int, [_vp, _vp, _i64, _int, _int, _vp, _vp, _vp, _int, _int, _vp, _vp,
+                               _vp, _sz, _vp]),
+    "csa2_index_reindex": (_int, [_vp, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _int, _int,
+                                  _vp, _vp, _sz, _vp]),
+    "csa2_sparse_attn_decode": (_int, [_vp, _int, _int, _vp, _vp, _i64, _vp, _int, _vp, _vp, _vp,
+                                       _vp, _vp, _f, _vp, _vp, _vp, _sz, _vp]),
+    "csa2_sparse_attn_chunk": (_int, [_vp, _int, _int, _int, _vp, _vp, _i64, _vp, _int, _vp, _vp,
+                                      _vp, _vp, _f, _vp, _vp, _vp, _sz, _vp]),
+    "csa2_workspace_size": (_sz, [_int, _int, _int, _i64, _int, _int, _int]),
+    "csa2_status_str": (ctypes.c_char_p, [_int]),
+    "csa2_abi_version": (_int, []),
+    "csa2_codec_probe": (_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp]),
+}
+
+
+class Csa2Error(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libcsa2.so (built in-tree by build.py); raise if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise Csa2Error(f"{LIB_PATH} is missing: build it with "
+                            "`python compressed_kv_cache_decode_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc, what):
+    if rc != 0:
+        msg = lib().csa2_status_str(rc).decode()
+        raise Csa2Error(f"{what}: {STATUS.get(rc, rc)} ({msg})")
+
+
+def _ptr(t, dtype, name, numel=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: needs at least {numel} elements, has {t.numel()}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def workspace_size(op, B, Q, cap, topk, pool_blocks, H):
+    n = lib().csa2_workspace_size(op, B, Q, cap, topk, pool_blocks, H)
+    if n == ctypes.c_size_t(-1).value:
+        raise Csa2Error("workspace_size: invalid sizes")
+    return n
+
+
+def alloc_workspace(nbytes, device=None):
+    """A caller-owned byte buffer for the workspace argument."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8,
+                       device=device or torch.cuda.current_device())
+
+
+# ---------------------------------------------------------------------------
+# caches
+# ---------------------------------------------------------------------------
+class Cache:
+    """Device arrays of one shared global KV (B sequences x cap entries).
+
+    kv_codes [B*cap][128] u8, kv_scales [B*cap][16] u8: FP4 main KV;
+    ik_codes [B*cap*64] u8 (tile layout), ik_sigma [B*cap] f32: FP8 indexer K."""
+
+    def __init__(self, B, cap, device=None):
+        if cap % IDX_TILE:
+            raise ValueError("cap must be a multiple of 64")
+        dev = device or torch.cuda.current_device()
+        self.B, self.cap = B, cap
+        n = B * cap
+        self.kv_codes = torch.zeros((n, KV_CODE_BYTES), dtype=torch.uint8, device=dev)
+        self.kv_scales = torch.zeros((n, KV_SCALE_BYTES), dtype=torch.uint8, device=dev)
+        self.ik_codes = torch.zeros(n * IDX_DIM, dtype=torch.uint8, device=dev)
+        self.ik_sigma = torch.zeros(n, dtype=torch.float32, device=dev)
+
+    def rows(self, b, positions):
+        """int64 device tensor of row numbers b*cap + positions."""
+        pos = torch.as_tensor(positions, dtype=torch.int64)
+        return (pos + b * self.cap).to(self.kv_codes.device)
+
+    @property
+    def nbytes(self):
+        return sum(t.numel() * t.element_size()
+                   for t in (self.kv_codes, self.kv_scales, self.ik_codes, self.ik_sigma))
+
+
+def rope_table(positions, base=10000.0):
+    """(cos, sin) of position * base^(-j/32), j < 32, in fp64, rounded to fp32.
+
+    Host-side table that csa2_quant_fp4 takes as input: [n][32][2] float32."""
+    pos = np.asarray(positions, dtype=np.float64).reshape(-1, 1)
+    theta = np.power(float(base), -np.arange(32, dtype=np.float64) / 32.0)
+    ang = pos * theta[None, :]
+    return np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def quant_fp4(k_tok, v_tok, kv_codes, kv_scales, ratio=1, rope_cs=None, dst_rows=None,
+              stream=None):
+    n_tok = k_tok.shape[0] if k_tok.dim() > 1 else 0
+    if k_tok.shape != v_tok.shape or (k_tok.dim() != 2 or k_tok.shape[1] != HEAD_DIM):
+        raise ValueError("k_tok, v_tok must be [n_tok][128]")
+    n_ent = n_tok // ratio
+    rc = lib().csa2_quant_fp4(
+        _ptr(k_tok, torch.float32, "k_tok"), _ptr(v_tok, torch.float32, "v_tok"), n_tok, ratio,
+        _ptr(rope_cs, torch.float32, "rope_cs", n_ent * 64),
+        _ptr(dst_rows, torch.int64, "dst_rows", n_ent),
+        _ptr(kv_codes, torch.uint8, "kv_codes"), _ptr(kv_scales, torch.uint8, "kv_scales"),
+        _stream(stream))
+    _check(rc, "csa2_quant_fp4")
+
+
+def quant_fp8(x, codes, sigma, layout=FP8_ROWS, dst_rows=None, stream=None):
+    if x.dim() != 2:
+        raise ValueError("x must be [n_rows][dim]")
+    n, dim = x.shape
+    rc = lib().csa2_quant_fp8(_ptr(x, torch.float32, "x"), n, dim, layout,
+                              _ptr(dst_rows, torch.int64, "dst_rows", n),
+                              _ptr(codes, torch.uint8, "codes"),
+                              _ptr(sigma, torch.float32, "sigma"), _stream(stream))
+    _check(rc, "csa2_quant_fp8")
+
+
+def index_full(cache, iq, iw, n_vis, topk_idx, pool_idx=None, topk=DEFAULT_TOPK,
+               pool_blocks=0, ws=None, stream=None):
+    """iq [B][Q][4][64] f32, iw [B][Q][4] f32, n_vis [B][Q] i32 ->
+    topk_idx [B][Q][topk] i32, pool_idx [B][Q][pool_blocks] i32."""
+    B, Q = iq.shape[0], iq.shape[1]
+    need = workspace_size(OP_INDEX_FULL, B, Q, cache.cap, topk, pool_blocks, 0)
+    if ws is None:
+        ws = alloc_workspace(need, iq.device)
+    rc = lib().csa2_index_full(
+        _ptr(cache.ik_codes, torch.uint8, "ik_codes"), _ptr(cache.ik_sigma, torch.float32, "ik_sigma"),
+        cache.cap, B, Q, _ptr(iq, torch.float32, "iq", B * Q * 256),
+        _ptr(iw, torch.float32, "iw", B * Q * 4), _ptr(n_vis, torch.int32, "n_vis", B * Q),
+        topk, pool_blocks, _ptr(topk_idx, torch.int32, "topk_idx", B * Q * topk),
+        _ptr(pool_idx, torch.int32, "pool_idx", B * Q * pool_blocks) if pool_blocks else None,
+        _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream))
+    _check(rc, "csa2_index_full")
+
+
+def index_reindex(cache, iq, iw, n_vis, pool_idx, topk_idx, topk=DEFAULT_TOPK, ws=None,
+                  stream=None):
+    B, Q = iq.shape[0], iq.shape[1]
+    pool_blocks = pool_idx.shape[-1]
+    need = workspace_size(OP_INDEX_REINDEX, B, Q, cache.cap, topk, pool_blocks, 0)
+    if ws is None:
+        ws = alloc_workspace(need, iq.device)
+    rc = lib().csa2_index_reindex(
+        _ptr(cache.ik_codes, torch.uint8, "ik_codes"), _ptr(cache.ik_sigma, torch.float32, "ik_sigma"),
+        cache.cap, B, Q, _ptr(iq, torch.float32, "iq", B * Q * 256),
+        _ptr(iw, torch.float32, "iw", B * Q * 4), _ptr(n_vis, torch.int32, "n_vis", B * Q),
+        _ptr(pool_idx, torch.int32, "pool_idx", B * Q * pool_blocks), pool_blocks, topk,
+        _ptr(topk_idx, torch.int32, "topk_idx", B * Q * topk),
+        _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream))
+    _check(rc, "csa2_index_reindex")
+
+
+def sparse_attn_decode(q, cache, topk_idx, swa_k, swa_v, swa_ks, swa_vs, swa_len, out, lse,
+                       sm_scale=None, ws=None, stream=None):
+    """q [B][H][128] f32; topk_idx [B][topk]; swa_k/v [B][128][128] u8; swa_ks/vs [B][128];
+    swa_len [B] i32 -> out [B][H][128], lse [B][H]."""
+    B, H = q.shape[0], q.shape[1]
+    topk = topk_idx.shape[-1]
+    sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else sm_scale
+    need = workspace_size(OP_ATTN_DECODE, B, 1, cache.cap, topk, 0, H)
+    if ws is None and need:
+        ws = alloc_workspace(need, q.device)
+    rc = lib().csa2_sparse_attn_decode(
+        _ptr(q, torch.float32, "q", B * H * HEAD_DIM), B, H,
+        _ptr(cache.kv_codes, torch.uint8, "kv_codes"), _ptr(cache.kv_scales, torch.uint8, "kv_scales"),
+        cache.cap, _ptr(topk_idx, torch.int32, "topk_idx", B * topk), topk,
+        _ptr(swa_k, torch.uint8, "swa_k", B * WINDOW * HEAD_DIM),
+        _ptr(swa_v, torch.uint8, "swa_v", B * WINDOW * HEAD_DIM),
+        _ptr(swa_ks, torch.float32, "swa_ks", B * WINDOW),
+        _ptr(swa_vs, torch.float32, "swa_vs", B * WINDOW),
+        _ptr(swa_len, torch.int32, "swa_len", B), sm,
+        _ptr(out, torch.float32, "out", B * H * HEAD_DIM), _ptr(lse, torch.float32, "lse", B * H),
+        _ptr(ws, torch.uint8, "ws") if ws is not None else None,
+        ws.numel() if ws is not None else 0, _stream(stream))
+    _check(rc, "csa2_sparse_attn_decode")
+
+
+def sparse_attn_chunk(q, cache, topk_idx, swa_k, swa_v, swa_ks, swa_vs, out, lse, sm_scale=None,
+                      ws=None, stream=None):
+    """q [B][Q][H][128]; topk_idx [B][Q][topk]; chunk window swa_k/v [B][Q][128], swa_ks/vs [B][Q]."""
+    B, Q, H = q.shape[0], q.shape[1], q.shape[2]
+    topk = topk_idx.shape[-1]
+    sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else sm_scale
+    need = workspace_size(OP_ATTN_CHUNK, B, Q, cache.cap, topk, 0, H)
+    if ws is None and need:
+        ws = alloc_workspace(need, q.device)
+    rc = lib().csa2_sparse_attn_chunk(
+        _ptr(q, torch.float32, "q", B * Q * H * HEAD_DIM), B, Q, H,
+        _ptr(cache.kv_codes, torch.uint8, "kv_codes"), _ptr(cache.kv_scales, torch.uint8, "kv_scales"),
+        cache.cap, _ptr(topk_idx, torch.int32, "topk_idx", B * Q * topk), topk,
+        _ptr(swa_k, torch.uint8, "swa_k", B * Q * HEAD_DIM),
+        _ptr(swa_v, torch.uint8, "swa_v", B * Q * HEAD_DIM),
+        _ptr(swa_ks, torch.float32, "swa_ks", B * Q), _ptr(swa_vs, torch.float32, "swa_vs", B * Q),
+        sm, _ptr(out, torch.float32, "out", B * Q * H * HEAD_DIM),
+        _ptr(lse, torch.float32, "lse", B * Q * H),
+        _ptr(ws, torch.uint8, "ws") if ws is not None else None,
+        ws.numel() if ws is not None else 0, _stream(stream))
+    _check(rc, "csa2_sparse_attn_chunk")
+
+
+def codec_probe(x, stream=None):
+    """Run the device codecs: returns (e4m3 decode [256], e2m1 decode [16],
+    e4m3 encode of x, e2m1 encode of x), all on the GPU."""
+    dev = x.device
+    e4 = torch.empty(256, dtype=torch.float32, device=dev)
+    e2 = torch.empty(16, dtype=torch.float32, device=dev)
+    enc4 = torch.empty(x.numel(), dtype=torch.uint8, device=dev)
+    enc2 = torch.empty(x.numel(), dtype=torch.uint8, device=dev)
+    rc = lib().csa2_codec_probe(_ptr(e4, torch.float32, "e4m3_dec"), _ptr(e2, torch.float32, "e2m1_dec"),
+                                _ptr(x, torch.float32, "x"), x.numel(),
+                                _ptr(enc4, torch.uint8, "e4m3_enc"), _ptr(enc2, torch.uint8, "e2m1_enc"),
+                                _stream(stream))
+    _check(rc, "csa2_codec_probe")
+    return e4, e2, enc4, enc2

@@ -1,0 +1,274 @@
+// csa2_abi.cpp -- the extern "C" boundary of libcsa2 (declared in include/csa2.h).
+//
+// Every entry point validates its scalar arguments on the host first and
+// returns a status without touching the HIP runtime when they are invalid;
+// only then are kernels enqueued on the caller's stream.  No entry point
+// allocates, frees, synchronises or keeps state.
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/csa2.h"
+#include "csa2_internal.hpp"
+
+using namespace csa2;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct IndexLayout {
+    size_t qd, wq, keys, bkeys, ipool, total;
+};
+
+// workspace of csa2_index_full: decoded query, folded weights, per-position
+// keys, per-block keys, internal pool (pool_blocks == 0)
+IndexLayout full_layout(int B, int Q, int64_t cap, int topk, int pool_blocks) {
+    IndexLayout L{};
+    const size_t nq = (size_t)B * Q;
+    size_t off = 0;
+    L.qd = off; off += align_up(nq * 256 * sizeof(float));
+    L.wq = off; off += align_up(nq * 4 * sizeof(float));
+    L.keys = off; off += align_up(nq * (size_t)cap * sizeof(uint32_t));
+    L.bkeys = off; off += align_up(nq * (size_t)(cap / 8) * sizeof(uint32_t));
+    L.ipool = off;
+    if (pool_blocks == 0) off += align_up(nq * (size_t)topk * sizeof(int32_t));
+    L.total = off;
+    return L;
+}
+
+// workspace of csa2_index_reindex: decoded query, folded weights, pool keys
+IndexLayout reindex_layout(int B, int Q, int pool_blocks) {
+    IndexLayout L{};
+    const size_t nq = (size_t)B * Q;
+    size_t off = 0;
+    L.qd = off; off += align_up(nq * 256 * sizeof(float));
+    L.wq = off; off += align_up(nq * 4 * sizeof(float));
+    L.keys = off; off += align_up(nq * (size_t)pool_blocks * 8 * sizeof(uint32_t));
+    L.total = off;
+    return L;
+}
+
+int check_cache_dims(int64_t cap, int B, int Q) {
+    if (cap <= 0 || B <= 0 || Q <= 0) return CSA2_E_ARG;
+    if (cap % CSA2_IDX_TILE != 0) return CSA2_E_ARG;
+    if (cap > (int64_t)INT32_MAX) return CSA2_E_UNSUPPORTED;  // positions are int32
+    if (B > 65535) return CSA2_E_UNSUPPORTED;                 // grid.y
+    if ((int64_t)B * Q > (int64_t)INT32_MAX) return CSA2_E_UNSUPPORTED;
+    return CSA2_OK;
+}
+
+int validate_index_full(const void* ikc, const void* iks, int64_t cap, int B, int Q,
+                        const void* iq, const void* iw, const void* n_vis, int topk,
+                        int pool_blocks, const void* topk_idx, const void* pool_idx) {
+    if (!ikc || !iks || !iq || !iw || !n_vis || !topk_idx) return CSA2_E_ARG;
+    if (pool_blocks < 0) return CSA2_E_ARG;
+    if (pool_blocks > 0 && !pool_idx) return CSA2_E_ARG;
+    int rc = check_cache_dims(cap, B, Q);
+    if (rc) return rc;
+    if (topk < 1) return CSA2_E_ARG;
+    if (topk > CSA2_MAX_TOPK) return CSA2_E_UNSUPPORTED;
+    if (pool_blocks > CSA2_MAX_POOL_BLOCKS) return CSA2_E_UNSUPPORTED;
+    if (pool_blocks > 0 && pool_blocks < topk) return CSA2_E_UNSUPPORTED;
+    return CSA2_OK;
+}
+
+int validate_index_reindex(const void* ikc, const void* iks, int64_t cap, int B, int Q,
+                           const void* iq, const void* iw, const void* n_vis, const void* pool,
+                           int pool_blocks, int topk, const void* topk_idx) {
+    if (!ikc || !iks || !iq || !iw || !n_vis || !pool || !topk_idx) return CSA2_E_ARG;
+    int rc = check_cache_dims(cap, B, Q);
+    if (rc) return rc;
+    if (pool_blocks < 1 || topk < 1) return CSA2_E_ARG;
+    if (pool_blocks > CSA2_MAX_POOL_BLOCKS || topk > CSA2_MAX_TOPK) return CSA2_E_UNSUPPORTED;
+    return CSA2_OK;
+}
+
+int validate_attn(const void* q, int B, int Q, int H, const void* kvc, const void* kvs,
+                  int64_t cap, const void* idx, int topk, const void* swk, const void* swv,
+                  const void* swks, const void* swvs, float sm_scale, const void* out,
+                  const void* lse) {
+    if (!q || !kvc || !kvs || !swk || !swv || !swks || !swvs || !out || !lse) return CSA2_E_ARG;
+    if (topk < 0) return CSA2_E_ARG;
+    if (topk > 0 && !idx) return CSA2_E_ARG;
+    if (topk > CSA2_MAX_TOPK) return CSA2_E_UNSUPPORTED;
+    if (B <= 0 || Q <= 0 || H <= 0 || cap <= 0) return CSA2_E_ARG;
+    if (H % 16 != 0) return CSA2_E_UNSUPPORTED;
+    if (H > CSA2_MAX_HEADS) return CSA2_E_UNSUPPORTED;
+    if ((int64_t)B * Q > 65535) return CSA2_E_UNSUPPORTED;  // grid.y
+    if (!(sm_scale == sm_scale) || sm_scale > 3.0e38f || sm_scale < -3.0e38f) return CSA2_E_ARG;
+    return CSA2_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+__attribute__((visibility("default"))) int csa2_abi_version(void) { return CSA2_ABI_VERSION; }
+
+__attribute__((visibility("default"))) const char* csa2_status_str(int status) {
+    switch (status) {
+        case CSA2_OK: return "ok";
+        case CSA2_E_ARG: return "invalid argument (null pointer or bad dimension)";
+        case CSA2_E_UNSUPPORTED: return "unsupported argument value";
+        case CSA2_E_WORKSPACE: return "workspace missing or too small";
+        case CSA2_E_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+__attribute__((visibility("default"))) size_t csa2_workspace_size(int op, int B, int Q,
+                                                                 int64_t cap, int topk,
+                                                                 int pool_blocks, int H) {
+    switch (op) {
+        case CSA2_OP_INDEX_FULL:
+            if (check_cache_dims(cap, B, Q) || topk < 1 || topk > CSA2_MAX_TOPK ||
+                pool_blocks < 0 || pool_blocks > CSA2_MAX_POOL_BLOCKS)
+                return SIZE_MAX;
+            return full_layout(B, Q, cap, topk, pool_blocks).total;
+        case CSA2_OP_INDEX_REINDEX:
+            if (check_cache_dims(cap, B, Q) || pool_blocks < 1 ||
+                pool_blocks > CSA2_MAX_POOL_BLOCKS)
+                return SIZE_MAX;
+            return reindex_layout(B, Q, pool_blocks).total;
+        case CSA2_OP_ATTN_DECODE:
+            if (B <= 0 || H <= 0 || topk < 0) return SIZE_MAX;
+            return attn_workspace_bytes(B, H, topk, CSA2_WINDOW);
+        case CSA2_OP_ATTN_CHUNK:
+            if (B <= 0 || Q <= 0 || H <= 0 || topk < 0) return SIZE_MAX;
+            return attn_workspace_bytes((int64_t)B * Q, H, topk, Q);
+        default:
+            return SIZE_MAX;
+    }
+}
+
+__attribute__((visibility("default"))) int csa2_quant_fp4(const float* k_tok, const float* v_tok,
+                                                         int64_t n_tok, int ratio,
+                                                         const float* rope_cs,
+                                                         const int64_t* dst_rows,
+                                                         uint8_t* kv_codes, uint8_t* kv_scales,
+                                                         hipStream_t stream) {
+    if (n_tok < 0) return CSA2_E_ARG;
+    if (ratio != 1 && ratio != 2) return CSA2_E_UNSUPPORTED;
+    if (ratio == 2 && rope_cs) return CSA2_E_UNSUPPORTED;
+    if (n_tok % ratio != 0) return CSA2_E_ARG;
+    if (n_tok == 0) return CSA2_OK;
+    if (!k_tok || !v_tok || !kv_codes || !kv_scales) return CSA2_E_ARG;
+    return hip_status(launch_quant_fp4(k_tok, v_tok, n_tok / ratio, ratio, rope_cs, dst_rows,
+                                       kv_codes, kv_scales, stream));
+}
+
+__attribute__((visibility("default"))) int csa2_quant_fp8(const float* x, int64_t n_rows, int dim,
+                                                         int layout, const int64_t* dst_rows,
+                                                         uint8_t* codes, float* sigma,
+                                                         hipStream_t stream) {
+    if (n_rows < 0) return CSA2_E_ARG;
+    if (dim != 64 && dim != 128) return CSA2_E_UNSUPPORTED;
+    if (layout != CSA2_FP8_ROWS && layout != CSA2_FP8_IDX_TILED) return CSA2_E_ARG;
+    if (layout == CSA2_FP8_IDX_TILED && dim != 64) return CSA2_E_UNSUPPORTED;
+    if (n_rows == 0) return CSA2_OK;
+    if (!x || !codes || !sigma) return CSA2_E_ARG;
+    return hip_status(launch_quant_fp8(x, n_rows, dim, layout, dst_rows, codes, sigma, stream));
+}
+
+__attribute__((visibility("default"))) int csa2_index_full(
+    const uint8_t* ik_codes, const float* ik_sigma, int64_t cap, int B, int Q, const float* iq,
+    const float* iw, const int32_t* n_vis, int topk, int pool_blocks, int32_t* topk_idx,
+    int32_t* pool_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int rc = validate_index_full(ik_codes, ik_sigma, cap, B, Q, iq, iw, n_vis, topk, pool_blocks,
+                                 topk_idx, pool_idx);
+    if (rc) return rc;
+    const IndexLayout L = full_layout(B, Q, cap, topk, pool_blocks);
+    if (!ws || ws_bytes < L.total) return CSA2_E_WORKSPACE;
+    char* w = static_cast<char*>(ws);
+    float* qd = reinterpret_cast<float*>(w + L.qd);
+    float* wq = reinterpret_cast<float*>(w + L.wq);
+    uint32_t* keys = reinterpret_cast<uint32_t*>(w + L.keys);
+    uint32_t* bkeys = reinterpret_cast<uint32_t*>(w + L.bkeys);
+    const int64_t nq = (int64_t)B * Q;
+    // The Full layer's own top-K over every visible position equals the top-K
+    // inside its best P >= K blocks (ties to the lower index on both levels),
+    // so the position select only ever looks at P*8 candidates.
+    int32_t* pool = pool_blocks > 0 ? pool_idx : reinterpret_cast<int32_t*>(w + L.ipool);
+    const int P = pool_blocks > 0 ? pool_blocks : topk;
+
+    hipError_t e = launch_prep_iq(iq, iw, nq, qd, wq, stream);
+    if (e == hipSuccess) e = launch_scan(ik_codes, ik_sigma, cap, B, Q, qd, wq, n_vis, keys, bkeys, stream);
+    if (e == hipSuccess)
+        e = launch_select(kModeBlocks, bkeys, cap / 8, nullptr, 0, n_vis, cap, nq, P, pool, P, stream);
+    if (e == hipSuccess)
+        e = launch_select(kModeGather, keys, cap, pool, P, n_vis, cap, nq, topk, topk_idx, topk, stream);
+    return hip_status(e);
+}
+
+__attribute__((visibility("default"))) int csa2_index_reindex(
+    const uint8_t* ik_codes, const float* ik_sigma, int64_t cap, int B, int Q, const float* iq,
+    const float* iw, const int32_t* n_vis, const int32_t* pool_idx, int pool_blocks, int topk,
+    int32_t* topk_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int rc = validate_index_reindex(ik_codes, ik_sigma, cap, B, Q, iq, iw, n_vis, pool_idx,
+                                    pool_blocks, topk, topk_idx);
+    if (rc) return rc;
+    const IndexLayout L = reindex_layout(B, Q, pool_blocks);
+    if (!ws || ws_bytes < L.total) return CSA2_E_WORKSPACE;
+    char* w = static_cast<char*>(ws);
+    float* qd = reinterpret_cast<float*>(w + L.qd);
+    float* wq = reinterpret_cast<float*>(w + L.wq);
+    uint32_t* ckeys = reinterpret_cast<uint32_t*>(w + L.keys);
+    const int64_t nq = (int64_t)B * Q;
+    hipError_t e = launch_prep_iq(iq, iw, nq, qd, wq, stream);
+    if (e == hipSuccess)
+        e = launch_pool_score(ik_codes, ik_sigma, cap, B, Q, qd, wq, n_vis, pool_idx, pool_blocks,
+                              ckeys, stream);
+    if (e == hipSuccess)
+        e = launch_select(kModeCompact, ckeys, (int64_t)pool_blocks * 8, pool_idx, pool_blocks,
+                          n_vis, cap, nq, topk, topk_idx, topk, stream);
+    return hip_status(e);
+}
+
+__attribute__((visibility("default"))) int csa2_sparse_attn_decode(
+    const float* q, int B, int H, const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t cap,
+    const int32_t* topk_idx, int topk, const uint8_t* swa_k, const uint8_t* swa_v,
+    const float* swa_ks, const float* swa_vs, const int32_t* swa_len, float sm_scale, float* out,
+    float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int rc = validate_attn(q, B, 1, H, kv_codes, kv_scales, cap, topk_idx, topk, swa_k, swa_v,
+                           swa_ks, swa_vs, sm_scale, out, lse);
+    if (rc) return rc;
+    if (!swa_len) return CSA2_E_ARG;
+    const size_t need = attn_workspace_bytes(B, H, topk, CSA2_WINDOW);
+    if (need > 0 && (!ws || ws_bytes < need)) return CSA2_E_WORKSPACE;
+    AttnArgs a{q, H, 1, kv_codes, kv_scales, cap, topk_idx, topk, swa_k, swa_v, swa_ks, swa_vs,
+               swa_len, CSA2_WINDOW, sm_scale, out, lse, (int64_t)B};
+    return hip_status(launch_attn(a, ws, ws_bytes, stream));
+}
+
+__attribute__((visibility("default"))) int csa2_sparse_attn_chunk(
+    const float* q, int B, int Q, int H, const uint8_t* kv_codes, const uint8_t* kv_scales,
+    int64_t cap, const int32_t* topk_idx, int topk, const uint8_t* swa_k, const uint8_t* swa_v,
+    const float* swa_ks, const float* swa_vs, float sm_scale, float* out, float* lse, void* ws,
+    size_t ws_bytes, hipStream_t stream) {
+    int rc = validate_attn(q, B, Q, H, kv_codes, kv_scales, cap, topk_idx, topk, swa_k, swa_v,
+                           swa_ks, swa_vs, sm_scale, out, lse);
+    if (rc) return rc;
+    const int64_t nq = (int64_t)B * Q;
+    const size_t need = attn_workspace_bytes(nq, H, topk, Q);
+    if (need > 0 && (!ws || ws_bytes < need)) return CSA2_E_WORKSPACE;
+    AttnArgs a{q, H, Q, kv_codes, kv_scales, cap, topk_idx, topk, swa_k, swa_v, swa_ks, swa_vs,
+               nullptr, Q, sm_scale, out, lse, nq};
+    return hip_status(launch_attn(a, ws, ws_bytes, stream));
+}
+
+__attribute__((visibility("default"))) int csa2_codec_probe(float* e4m3_dec, float* e2m1_dec,
+                                                           const float* x, int64_t n,
+                                                           uint8_t* e4m3_enc, uint8_t* e2m1_enc,
+                                                           hipStream_t stream) {
+    if (!e4m3_dec || !e2m1_dec || n < 0) return CSA2_E_ARG;
+    if (n > 0 && (!x || !e4m3_enc || !e2m1_enc)) return CSA2_E_ARG;
+    return hip_status(launch_codec_probe(e4m3_dec, e2m1_dec, x, n, e4m3_enc, e2m1_enc, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+// csa2_device.hpp -- device-side number formats and wave helpers for gfx950.
+//
+// Formats ("DeepSeek V4.1 Flash: architecture study notes", section 4; "DeepSeek
+// V4.1 Flash is live", "cache precision and persistence tiers"): main KV is
+// E2M1 with one E4M3 scale per 16 channels; the SWA window and the indexer key
+// are E4M3 with one fp32 scale per row.  E4M3 is the OCP 8-bit format (bias 7,
+// max 448, no infinities); E2M1 is the OCP MX 4-bit format.
+//
+// Everything in this library is compiled with -ffp-contract=off: a float
+// expression is the sequence of IEEE operations it reads as, and fused
+// multiply-adds appear only where fmaf() is written.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+constexpr int kHeadDim = 128;
+constexpr int kIdxHeads = 4;
+constexpr int kIdxDim = 64;
+constexpr int kIdxTile = 64;
+constexpr int kBlock = 8;
+
+// ---------------------------------------------------------------------------
+// E4M3 encode: round to nearest, ties to even, saturate to +-448.
+// Normal range: round the fp32 bit pattern to 3 mantissa bits with the usual
+// add-half-minus-one-plus-lsb trick (the carry walks into the exponent), then
+// rebias the exponent from 127 to 7.  Subnormal range (|x| < 2^-6): the code
+// is rint(|x| * 2^9), which is exact scaling followed by one RNE rounding;
+// a result of 8 is the smallest normal 2^-6, whose code is also 8.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a >= 0x43E00000u) {                 // |x| >= 448 (also inf / nan)
+        code = 0x7Eu;
+    } else if (a < 0x3C800000u) {           // |x| < 2^-6
+        code = (uint32_t)rintf(__uint_as_float(a) * 512.0f);
+    } else {
+        const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+        code = r - (120u << 3);
+        if (code > 0x7Eu) code = 0x7Eu;
+    }
+    return sign | code;
+}
+
+// E4M3 decode from bits (used outside hot loops and as the cross-check of
+// the hardware converter).
+__device__ __forceinline__ float e4m3_decode_bits(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * (1.0f / 512.0f);
+    return (c & 0x80u) ? -mag : mag;
+}
+
+// Hardware conversion of two E4M3 bytes (gfx950 uses the OCP encoding).
+// WORD = false converts bytes 0,1 of `packed`; WORD = true converts bytes 2,3.
+template <bool WORD>
+__device__ __forceinline__ float2 e4m3x2_to_f32(uint32_t packed) {
+    auto v = __builtin_amdgcn_cvt_pk_f32_fp8((int)packed, WORD);
+    return make_float2(v[0], v[1]);
+}
+
+// ---------------------------------------------------------------------------
+// E2M1 encode of t = x / scale: ladder of the midpoints between the eight
+// magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}; a value exactly on a midpoint goes
+// to the even code; anything above 5 saturates to 6.  Sign in bit 3.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e2m1_encode(float t) {
+    const uint32_t sign = (__float_as_uint(t) >> 28) & 8u;
+    const float a = fabsf(t);
+    uint32_t c;
+    if (a <= 0.25f) c = 0;
+    else if (a < 0.75f) c = 1;
+    else if (a <= 1.25f) c = 2;
+    else if (a < 1.75f) c = 3;
+    else if (a <= 2.5f) c = 4;
+    else if (a < 3.5f) c = 5;
+    else if (a <= 5.0f) c = 6;
+    else c = 7;
+    return sign | c;
+}
+
+// E2M1 code -> fp16 bit pattern (exact): exponent field e (bias 1) and
+// mantissa bit m map to fp16 exponent e - 1 + 15; code 1 is 0.5 (0x3800).
+__device__ __forceinline__ uint32_t e2m1_to_f16_bits(uint32_t c) {
+    const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+    uint32_t mag = e ? (((e + 14u) << 10) | (m << 9)) : (m ? 0x3800u : 0u);
+    return ((c & 8u) << 12) | mag;
+}
+
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+    const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+    float mag = e ? __uint_as_float(((e + 126u) << 23) | (m << 22)) : (m ? 0.5f : 0.0f);
+    return (c & 8u) ? -mag : mag;
+}
+
+// ---------------------------------------------------------------------------
+// Ranking keys: an order-preserving map from fp32 scores to uint32 where a
+// larger score gives a larger key.  -0 is first folded onto +0 (x + 0.0f),
+// so equal scores always give equal keys.  Every non-NaN float maps to a key
+// >= 0x00800000, which leaves 0 free to mean "not visible".
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t score_key(float s) {
+    const uint32_t u = __float_as_uint(s + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane helpers (wave64).  DPP controls: quad_perm [1,0,3,2] = 0xB1,
+// quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141 (lane i <-> 7-i within
+// each group of 8).
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// max over each aligned group of 8 lanes, result in every lane of the group
+__device__ __forceinline__ uint32_t max8_u32(uint32_t v) {
+    v = max(v, dpp<0xB1>(v));
+    v = max(v, dpp<0x4E>(v));
+    v = max(v, dpp<0x141>(v));
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__device__ __forceinline__ float group8_max_f32(float v) {
+    v = fmaxf(v, __shfl_xor(v, 1, 64));
+    v = fmaxf(v, __shfl_xor(v, 2, 64));
+    v = fmaxf(v, __shfl_xor(v, 4, 64));
+    return v;
+}
+
+__device__ __forceinline__ int clamp_nvis(int32_t n, int64_t cap) {
+    return n < 0 ? 0 : (n > cap ? (int)cap : n);
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load that is not expected to be reused (nontemporal hint)
+__device__ __forceinline__ uint4 load16_stream(const uint8_t* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// byte offset of (row, channel group g) in the tiled indexer-K layout
+__device__ __forceinline__ int64_t ik_offset(int64_t row, int g) {
+    return (((row >> 6) * 4 + g) * 64 + (row & 63)) * 16;
+}
+
+}  // namespace csa2

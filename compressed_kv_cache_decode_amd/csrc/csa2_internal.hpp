@@ -1,0 +1,59 @@
+// csa2_internal.hpp -- launchers shared between the kernel files and the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+constexpr int kMaxPoolBlocks = 4096;
+constexpr int kMaxTopk = 2048;
+constexpr int kModeBlocks = 0;
+constexpr int kModeGather = 1;
+constexpr int kModeCompact = 2;
+
+hipError_t launch_quant_fp4(const float* k, const float* v, int64_t n_ent, int ratio,
+                            const float* rope_cs, const int64_t* dst_rows, uint8_t* codes,
+                            uint8_t* scales, hipStream_t stream);
+hipError_t launch_quant_fp8(const float* x, int64_t n_rows, int dim, int layout,
+                            const int64_t* dst_rows, uint8_t* codes, float* sigma,
+                            hipStream_t stream);
+hipError_t launch_prep_iq(const float* iq, const float* iw, int64_t n_q, float* qd, float* wq,
+                          hipStream_t stream);
+hipError_t launch_codec_probe(float* e4m3_dec, float* e2m1_dec, const float* x, int64_t n,
+                              uint8_t* e4m3_enc, uint8_t* e2m1_enc, hipStream_t stream);
+
+hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
+                       const float* qd, const float* wq, const int32_t* n_vis, uint32_t* keys,
+                       uint32_t* bkeys, hipStream_t stream);
+hipError_t launch_pool_score(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
+                             const float* qd, const float* wq, const int32_t* n_vis,
+                             const int32_t* pool, int P, uint32_t* ckeys, hipStream_t stream);
+hipError_t launch_select(int mode, const uint32_t* src, int64_t src_stride, const int32_t* pool,
+                         int P, const int32_t* n_vis, int64_t cap, int64_t n_queries, int K,
+                         int32_t* out, int64_t out_stride, hipStream_t stream);
+
+struct AttnArgs {
+    const float* q;          // [n_q][H][128]
+    int H;
+    int Q;                   // queries per sequence (query bq belongs to sequence bq / Q)
+    const uint8_t* kvc;      // [B*cap][128]
+    const uint8_t* kvs;      // [B*cap][16]
+    int64_t cap;
+    const int32_t* idx;      // [n_q][topk]
+    int topk;
+    const uint8_t* swk;      // window K codes
+    const uint8_t* swv;
+    const float* swks;
+    const float* swvs;
+    const int32_t* swa_len;  // decode: [B]; chunk: nullptr (query i sees tokens [0, i])
+    int swa_rows;            // rows per sequence in the window arrays (128 or Q)
+    float sm_scale;
+    float* out;              // [n_q][H][128]
+    float* lse;              // [n_q][H]
+    int64_t n_q;
+};
+
+size_t attn_workspace_bytes(int64_t n_q, int H, int topk, int swa_rows);
+hipError_t launch_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
+
+}  // namespace csa2

@@ -1,0 +1,187 @@
+// csa2_quant.hip -- write path: FP4 main KV, FP8 rows (SWA / indexer K), the
+// per-call indexer-query quantisation, and the codec probe.
+//
+// FP4 main KV: "DeepSeek V4.1 Flash: architecture study notes", section 4 (E2M1
+// values, one 8-bit E4M3 scale per 16 channels, 4.5 bits per value) and section
+// 3 (encoder groups average 2 tokens into 1 entry); "DeepSeek V4.1 Flash is
+// live", "CSA2 attention" (compressed entries do not overlap) and "cache
+// precision and persistence tiers" (quantise after RoPE, no global scale).
+//
+// These kernels are bandwidth-trivial (one entry per sequence per decode step,
+// 128 per replay chunk); they are written for exactness: every division is an
+// IEEE fp32 division and every rounding is spelled out.
+#include "csa2_device.hpp"
+#include "csa2_internal.hpp"
+
+namespace csa2 {
+
+// One wave per entry; lane l owns channels 2l and 2l+1 of K and of V, so a
+// 16-channel scale group is 8 adjacent lanes and one code byte per lane.
+__global__ __launch_bounds__(256) void k_quant_fp4(const float* __restrict__ k,
+                                                   const float* __restrict__ v, int64_t n_ent,
+                                                   int ratio, const float* __restrict__ rope_cs,
+                                                   const int64_t* __restrict__ dst_rows,
+                                                   uint8_t* __restrict__ codes,
+                                                   uint8_t* __restrict__ scales) {
+    const int lane = threadIdx.x & 63;
+    const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e >= n_ent) return;
+
+    float k0, k1, v0, v1;
+    if (ratio == 1) {
+        const float2 kk = reinterpret_cast<const float2*>(k + e * kHeadDim)[lane];
+        const float2 vv = reinterpret_cast<const float2*>(v + e * kHeadDim)[lane];
+        k0 = kk.x; k1 = kk.y; v0 = vv.x; v1 = vv.y;
+    } else {
+        // mean of tokens 2e and 2e+1: fl(fl(a + b) * 0.5)
+        const float2 ka = reinterpret_cast<const float2*>(k + (2 * e) * kHeadDim)[lane];
+        const float2 kb = reinterpret_cast<const float2*>(k + (2 * e + 1) * kHeadDim)[lane];
+        const float2 va = reinterpret_cast<const float2*>(v + (2 * e) * kHeadDim)[lane];
+        const float2 vb = reinterpret_cast<const float2*>(v + (2 * e + 1) * kHeadDim)[lane];
+        k0 = (ka.x + kb.x) * 0.5f; k1 = (ka.y + kb.y) * 0.5f;
+        v0 = (va.x + vb.x) * 0.5f; v1 = (va.y + vb.y) * 0.5f;
+    }
+    if (rope_cs != nullptr && lane < 32) {
+        // rotate the interleaved pair (2l, 2l+1) of the first 64 K channels
+        const float2 cs = reinterpret_cast<const float2*>(rope_cs + e * 64)[lane];
+        const float a = k0 * cs.x, b = k1 * cs.y, c = k0 * cs.y, d = k1 * cs.x;
+        k0 = a - b;
+        k1 = c + d;
+    }
+
+    // per-group absolute maximum over 8 lanes x 2 channels
+    const float kmax = group8_max_f32(fmaxf(fabsf(k0), fabsf(k1)));
+    const float vmax = group8_max_f32(fmaxf(fabsf(v0), fabsf(v1)));
+    const uint32_t ksc = e4m3_encode(kmax / 6.0f);
+    const uint32_t vsc = e4m3_encode(vmax / 6.0f);
+    const float ksd = e4m3_decode_bits(ksc);
+    const float vsd = e4m3_decode_bits(vsc);
+
+    auto code = [](float x, float sd) -> uint32_t {
+        if (sd == 0.0f) return (__float_as_uint(x) >> 28) & 8u;  // signed zero
+        return e2m1_encode(x / sd);
+    };
+    const uint32_t kb = code(k0, ksd) | (code(k1, ksd) << 4);
+    const uint32_t vb = code(v0, vsd) | (code(v1, vsd) << 4);
+
+    const int64_t row = dst_rows ? dst_rows[e] : e;
+    codes[row * 128 + lane] = (uint8_t)kb;
+    codes[row * 128 + 64 + lane] = (uint8_t)vb;
+    if ((lane & 7) == 0) {
+        scales[row * 16 + (lane >> 3)] = (uint8_t)ksc;
+        scales[row * 16 + 8 + (lane >> 3)] = (uint8_t)vsc;
+    }
+}
+
+// One wave per row of 64 or 128 values; sigma = fl(amax / 448),
+// code = RNE_E4M3(fl(x / sigma)).
+__global__ __launch_bounds__(256) void k_quant_fp8(const float* __restrict__ x, int64_t n_rows,
+                                                   int dim, int layout,
+                                                   const int64_t* __restrict__ dst_rows,
+                                                   uint8_t* __restrict__ codes,
+                                                   float* __restrict__ sigma) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= n_rows) return;
+    const int per = dim / 64;  // channels per lane: 1 or 2
+    float xv[2] = {0.0f, 0.0f};
+    for (int i = 0; i < per; ++i) xv[i] = x[r * dim + lane * per + i];
+    float amax = fabsf(xv[0]);
+    if (per == 2) amax = fmaxf(amax, fabsf(xv[1]));
+    amax = wave_max_f32(amax);
+    const float s = amax / 448.0f;
+    const int64_t row = dst_rows ? dst_rows[r] : r;
+    for (int i = 0; i < per; ++i) {
+        const uint32_t c = (s == 0.0f) ? ((__float_as_uint(xv[i]) >> 24) & 0x80u)
+                                       : e4m3_encode(xv[i] / s);
+        const int ch = lane * per + i;
+        if (layout == 1) {
+            codes[ik_offset(row, ch >> 4) + (ch & 15)] = (uint8_t)c;
+        } else {
+            codes[row * dim + ch] = (uint8_t)c;
+        }
+    }
+    if (lane == 0) sigma[row] = s;
+}
+
+// Indexer query per (sequence, query): per head sq = fl(amax/448), codes
+// RNE_E4M3(fl(q/sq)) stored back as their exact fp32 values, and the head
+// weight with the scale folded in, w' = fl(w * sq).  One wave per query,
+// lane = channel.
+__global__ __launch_bounds__(64) void k_prep_iq(const float* __restrict__ iq,
+                                                const float* __restrict__ iw, int64_t n_q,
+                                                float* __restrict__ qd, float* __restrict__ wq) {
+    const int lane = threadIdx.x;
+    const int64_t bq = blockIdx.x;
+    if (bq >= n_q) return;
+    for (int h = 0; h < kIdxHeads; ++h) {
+        const float x = iq[(bq * kIdxHeads + h) * kIdxDim + lane];
+        const float amax = wave_max_f32(fabsf(x));
+        const float sq = amax / 448.0f;
+        const uint32_t c = (sq == 0.0f) ? ((__float_as_uint(x) >> 24) & 0x80u) : e4m3_encode(x / sq);
+        qd[(bq * kIdxHeads + h) * kIdxDim + lane] = e4m3_decode_bits(c);
+        if (lane == 0) wq[bq * kIdxHeads + h] = iw[bq * kIdxHeads + h] * sq;
+    }
+}
+
+// Codec probe: decode every E4M3 code with the hardware converter used by the
+// hot loops, every E2M1 code with the bit decoder used by attention, and run
+// both encoders on caller values.
+__global__ __launch_bounds__(256) void k_codec_probe(float* __restrict__ e4m3_dec,
+                                                     float* __restrict__ e2m1_dec,
+                                                     const float* __restrict__ x, int64_t n,
+                                                     uint8_t* __restrict__ e4m3_enc,
+                                                     uint8_t* __restrict__ e2m1_enc) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < 128) {
+        const uint32_t packed = (uint32_t)(2 * t) | ((uint32_t)(2 * t + 1) << 8);
+        const float2 f = e4m3x2_to_f32<false>(packed);
+        e4m3_dec[2 * t] = f.x;
+        e4m3_dec[2 * t + 1] = f.y;
+    }
+    if (t < 16) {
+        const uint32_t h = e2m1_to_f16_bits((uint32_t)t);
+        e2m1_dec[t] = (float)__builtin_bit_cast(_Float16, (unsigned short)h);
+    }
+    if (t < n) {
+        e4m3_enc[t] = (uint8_t)e4m3_encode(x[t]);
+        e2m1_enc[t] = (uint8_t)e2m1_encode(x[t]);
+    }
+}
+
+hipError_t launch_quant_fp4(const float* k, const float* v, int64_t n_ent, int ratio,
+                            const float* rope_cs, const int64_t* dst_rows, uint8_t* codes,
+                            uint8_t* scales, hipStream_t stream) {
+    if (n_ent == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((n_ent + 3) / 4);
+    hipLaunchKernelGGL(k_quant_fp4, dim3(grid), dim3(256), 0, stream, k, v, n_ent, ratio, rope_cs,
+                       dst_rows, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_fp8(const float* x, int64_t n_rows, int dim, int layout,
+                            const int64_t* dst_rows, uint8_t* codes, float* sigma,
+                            hipStream_t stream) {
+    if (n_rows == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((n_rows + 3) / 4);
+    hipLaunchKernelGGL(k_quant_fp8, dim3(grid), dim3(256), 0, stream, x, n_rows, dim, layout,
+                       dst_rows, codes, sigma);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep_iq(const float* iq, const float* iw, int64_t n_q, float* qd, float* wq,
+                          hipStream_t stream) {
+    hipLaunchKernelGGL(k_prep_iq, dim3((unsigned)n_q), dim3(64), 0, stream, iq, iw, n_q, qd, wq);
+    return hipGetLastError();
+}
+
+hipError_t launch_codec_probe(float* e4m3_dec, float* e2m1_dec, const float* x, int64_t n,
+                              uint8_t* e4m3_enc, uint8_t* e2m1_enc, hipStream_t stream) {
+    const int64_t threads = n > 256 ? n : 256;
+    const unsigned grid = (unsigned)((threads + 255) / 256);
+    hipLaunchKernelGGL(k_codec_probe, dim3(grid), dim3(256), 0, stream, e4m3_dec, e2m1_dec, x, n,
+                       e4m3_enc, e2m1_enc);
+    return hipGetLastError();
+}
+
+}  // namespace csa2

@@ -1,0 +1,85 @@
+"""Layer-plan driver: one decode step of a CSA2 layer stack over a shared cache.
+
+"DeepSeek V4.1 Flash: architecture study notes", section 2: every CSA2 layer
+is statically Full, Reindex or Reuse; the decoder is one Full layer, four
+Reindex and fifteen Reuse layers over one shared global KV; every layer keeps
+its own attention query and its own local window.  "DeepSeek V4.1 Flash is
+live", "CSA2 attention": the decoder's groups are headed by Reindex layers.
+
+A plan is a string over {F, X, R}: F = Full (index_full, writes the pool),
+X = Reindex (index_reindex inside the latest pool), R = Reuse (no indexer
+call; attends to the most recent Full/Reindex top-K).  Every layer calls the
+sparse attention with its own q and window.  This module only sequences
+library calls; buffers are allocated once, up front.
+"""
+import torch
+
+from . import (DEFAULT_POOL_BLOCKS, DEFAULT_TOPK, HEAD_DIM, OP_ATTN_DECODE, OP_INDEX_FULL,
+               OP_INDEX_REINDEX, alloc_workspace, index_full, index_reindex, sparse_attn_decode,
+               workspace_size)
+
+
+def check_plan(plan, pool_blocks):
+    if not plan or plan[0] != "F":
+        raise ValueError("a plan starts with a Full layer")
+    if any(m not in "FXR" for m in plan):
+        raise ValueError("plan letters are F (Full), X (Reindex), R (Reuse)")
+    if "X" in plan and pool_blocks <= 0:
+        raise ValueError("Reindex layers need a pool (pool_blocks > 0)")
+
+
+def reuse_sources(plan):
+    """For each layer, the index of the layer whose top-K it attends with."""
+    src, last = [], None
+    for i, m in enumerate(plan):
+        if m in "FX":
+            last = i
+        src.append(last)
+    return src
+
+
+class DecodeStack:
+    """Buffers and workspaces for one stack of `plan` over `cache`, batch B, H heads."""
+
+    def __init__(self, cache, plan, B, H, topk=DEFAULT_TOPK, pool_blocks=DEFAULT_POOL_BLOCKS):
+        check_plan(plan, pool_blocks)
+        self.cache, self.plan, self.B, self.H = cache, plan, B, H
+        self.topk, self.pool_blocks = topk, pool_blocks
+        dev = cache.kv_codes.device
+        n_idx = sum(1 for m in plan if m in "FX")
+        self.topk_bufs = torch.empty((n_idx, B, 1, topk), dtype=torch.int32, device=dev)
+        self.pool = torch.empty((B, 1, max(pool_blocks, 1)), dtype=torch.int32, device=dev)
+        self.ws_full = alloc_workspace(
+            workspace_size(OP_INDEX_FULL, B, 1, cache.cap, topk, pool_blocks, 0), dev)
+        self.ws_reindex = (alloc_workspace(
+            workspace_size(OP_INDEX_REINDEX, B, 1, cache.cap, topk, pool_blocks, 0), dev)
+            if "X" in plan else None)
+        n_attn = workspace_size(OP_ATTN_DECODE, B, 1, cache.cap, topk, 0, H)
+        self.ws_attn = alloc_workspace(n_attn, dev) if n_attn else None
+        self.out = torch.empty((len(plan), B, H, HEAD_DIM), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((len(plan), B, H), dtype=torch.float32, device=dev)
+        self.sources = reuse_sources(plan)
+
+    def step(self, iq, iw, n_vis, q, swa_k, swa_v, swa_ks, swa_vs, swa_len, stream=None):
+        """One decode step.
+
+        iq [n_idx][B][1][4][64], iw [n_idx][B][1][4]: one indexer query per
+        Full/Reindex layer; n_vis [B][1] int32; q [L][B][H][128];
+        swa_k/v [L][B][128][128] u8, swa_ks/vs [L][B][128] f32, swa_len [B].
+        Returns the list of top-K buffers each layer attended with."""
+        used, cur, k = [], None, 0
+        for layer, mode in enumerate(self.plan):
+            if mode == "F":
+                index_full(self.cache, iq[k], iw[k], n_vis, self.topk_bufs[k],
+                           self.pool if self.pool_blocks else None, topk=self.topk,
+                           pool_blocks=self.pool_blocks, ws=self.ws_full, stream=stream)
+                cur, k = self.topk_bufs[k], k + 1
+            elif mode == "X":
+                index_reindex(self.cache, iq[k], iw[k], n_vis, self.pool, self.topk_bufs[k],
+                              topk=self.topk, ws=self.ws_reindex, stream=stream)
+                cur, k = self.topk_bufs[k], k + 1
+            sparse_attn_decode(q[layer], self.cache, cur.view(self.B, self.topk), swa_k[layer],
+                               swa_v[layer], swa_ks[layer], swa_vs[layer], swa_len,
+                               self.out[layer], self.lse[layer], ws=self.ws_attn, stream=stream)
+            used.append(cur)
+        return used

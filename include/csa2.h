@@ -1,0 +1,249 @@
+/*
+ * csa2.h -- C ABI of libcsa2: the CSA2 decode hot path on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * CSA2 ("Compressed Sparse Attention 2") keeps one global KV cache that many
+ * layers share.  Its main KV is stored in FP4 (E2M1 values, one E4M3 scale
+ * per 16 channels, no second-level scale); a per-position FP8 indexer key
+ * drives retrieval.  Layers run in one of three modes:
+ *   Full    scans every causally visible position with its own indexer query,
+ *           keeps a top-K and (in the decoder) a pool of the best blocks of
+ *           8 positions, at most 2048 blocks = 16384 positions;
+ *   Reindex rescores only the pool with its own indexer query -> own top-K;
+ *   Reuse   takes the most recent top-K unchanged (no call needed).
+ * Every layer then attends to its top-K global entries (dequantised on read)
+ * together with its own 128-token FP8 sliding window.
+ * Sources: "DeepSeek V4.1 Flash: architecture study notes" (macin.top),
+ * sections 1-4 and Figure 5; "DeepSeek V4.1 Flash is live" (myzaker.com),
+ * sections "CSA2 attention" and "cache precision and persistence tiers".
+ *
+ * Conventions for every call
+ *   - Array arguments are DEVICE pointers (hipMalloc'd, caller-owned); scalars
+ *     are passed by value.  The library never allocates, frees or keeps a
+ *     pointer after a call returns, and has no global mutable state.
+ *   - A call validates its scalar arguments on the host, then enqueues its
+ *     kernels on `stream` and returns without synchronising.  Calls on one
+ *     stream are ordered; calls on different streams that share an output or
+ *     workspace race.
+ *   - Return value: CSA2_OK (0) or a negative status (csa2_status_str()).
+ *     On a non-zero status nothing was enqueued, except CSA2_E_HIP, which
+ *     reports a launch error from the HIP runtime.
+ *   - Device data is not read to validate.  Out-of-range device values are
+ *     clamped or skipped by the kernels (visible counts are clamped to
+ *     [0, cap]; indices outside [0, cap) or [0, cap/8) are ignored), never
+ *     dereferenced.  NaN or infinite inputs give unspecified (but memory-safe)
+ *     results.
+ *
+ * Cache layouts (B independent sequences, each with capacity `cap` entries,
+ * cap a multiple of 64; row r = b*cap + position)
+ *   main KV codes   [B*cap][128] uint8: bytes 0..63 K, 64..127 V; byte j holds
+ *                   channel 2j in its low nibble and 2j+1 in its high nibble;
+ *                   a nibble is sign(bit 3) | E2M1 magnitude code (bits 0..2).
+ *   main KV scales  [B*cap][16] uint8: bytes 0..7 K, 8..15 V; byte g is the
+ *                   E4M3 scale of channels 16g..16g+15.
+ *                   128 + 16 = 144 bytes per entry = 4.5 bits per value.
+ *   indexer K codes tiled by 64 positions: position p of row r = b*cap + p
+ *                   lives in tile t = r/64 at lane i = r%64; its channels
+ *                   16g..16g+15 (g = 0..3) are the 16 bytes at offset
+ *                   ((t*4 + g)*64 + i)*16.  E4M3 codes.
+ *   indexer K sigma [B*cap] fp32 per-position scale (value = sigma * E4M3).
+ *   SWA K / V       [rows][128] uint8 E4M3, per-row fp32 scale [rows].
+ *   E4M3 is the OCP 8-bit format (bias 7, max 448, S.1111.111 = NaN);
+ *   E2M1 is the OCP MX 4-bit format (magnitudes 0,.5,1,1.5,2,3,4,6).
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_ABI_VERSION 1
+
+#define CSA2_HEAD_DIM 128        /* main K and V width */
+#define CSA2_KV_CODE_BYTES 128   /* per entry: K 64 B | V 64 B */
+#define CSA2_KV_SCALE_BYTES 16   /* per entry: K 8 | V 8 E4M3 scales */
+#define CSA2_IDX_HEADS 4         /* indexer heads */
+#define CSA2_IDX_DIM 64          /* indexer width per head */
+#define CSA2_IDX_TILE 64         /* positions per indexer-K tile */
+#define CSA2_BLOCK 8             /* positions per pool block */
+#define CSA2_WINDOW 128          /* SWA window */
+#define CSA2_DEFAULT_TOPK 512
+#define CSA2_DEFAULT_POOL_BLOCKS 2048
+#define CSA2_MAX_TOPK 2048
+#define CSA2_MAX_POOL_BLOCKS 4096
+#define CSA2_MAX_HEADS 128       /* attention heads, multiple of 16 */
+
+/* status codes */
+#define CSA2_OK 0
+#define CSA2_E_ARG (-1)          /* null pointer or bad dimension */
+#define CSA2_E_UNSUPPORTED (-2)  /* valid but not supported (ratio, sizes) */
+#define CSA2_E_WORKSPACE (-3)    /* workspace missing or too small */
+#define CSA2_E_HIP (-4)          /* HIP runtime reported a launch error */
+
+/* csa2_quant_fp8 layouts */
+#define CSA2_FP8_ROWS 0          /* codes [row][dim] */
+#define CSA2_FP8_IDX_TILED 1     /* dim == 64, indexer-K tile layout above */
+
+/* csa2_workspace_size ops */
+#define CSA2_OP_INDEX_FULL 1
+#define CSA2_OP_INDEX_REINDEX 2
+#define CSA2_OP_ATTN_DECODE 3
+#define CSA2_OP_ATTN_CHUNK 4
+
+/*
+ * csa2_quant_fp4 -- write path of the main KV.
+ * "DeepSeek V4.1 Flash: architecture study notes" section 4 (E2M1 with one
+ * 8-bit scale per 16 channels, 4 + 8/16 = 4.5 bits) and section 3 (encoder
+ * groups merge 2 tokens into 1 entry); "DeepSeek V4.1 Flash is live",
+ * "CSA2 attention" (no overlap between compressed entries) and "cache
+ * precision" (quantise after RoPE, no global scale).
+ *   k_tok, v_tok  [n_tok][128] fp32 token K and V.
+ *   ratio         1, or 2: entry e is the mean fl(fl(a+b)*0.5) of tokens
+ *                 2e and 2e+1 (n_tok must be even).
+ *   rope_cs       NULL, or [n_ent][32][2] fp32 (cos, sin): K channels
+ *                 (2j, 2j+1), j < 32, are rotated as
+ *                 (fl(fl(x0 c) - fl(x1 s)), fl(fl(x0 s) + fl(x1 c))) before
+ *                 quantisation.  Only with ratio 1.
+ *   dst_rows      NULL (entry e -> row e) or [n_ent] int64 destination rows;
+ *                 every row must lie inside kv_codes / kv_scales (not checked).
+ *   kv_codes, kv_scales  main KV arrays (layout above); rows written only.
+ * Per 16-channel group: scale = RNE_E4M3(amax/6) (saturating at 448); a zero
+ * scale gives signed-zero codes; code = RNE_E2M1(x/scale), ties to the even
+ * code, saturating at 6.  Divisions are IEEE fp32.
+ */
+int csa2_quant_fp4(const float* k_tok, const float* v_tok, int64_t n_tok, int ratio,
+                   const float* rope_cs, const int64_t* dst_rows, uint8_t* kv_codes,
+                   uint8_t* kv_scales, hipStream_t stream);
+
+/*
+ * csa2_quant_fp8 -- FP8 rows for the SWA K/V and the indexer K
+ * ("DeepSeek V4.1 Flash: architecture study notes" section 4: the local SWA KV
+ * stays FP8; the indexer key is the retrieval half of the global KV, section 1).
+ *   x         [n_rows][dim] fp32; dim 64 or 128 (64 for CSA2_FP8_IDX_TILED).
+ *   dst_rows  NULL (row r -> r) or [n_rows] int64 destination rows inside
+ *             codes / sigma (not checked).
+ *   codes     CSA2_FP8_ROWS: [rows][dim]; CSA2_FP8_IDX_TILED: tile layout.
+ *   sigma     [rows] fp32.
+ * sigma = fl(amax/448); code = RNE_E4M3(fl(x/sigma)); sigma == 0 gives
+ * signed-zero codes.
+ */
+int csa2_quant_fp8(const float* x, int64_t n_rows, int dim, int layout, const int64_t* dst_rows,
+                   uint8_t* codes, float* sigma, hipStream_t stream);
+
+/*
+ * csa2_index_full -- Full-layer indexer ("DeepSeek V4.1 Flash: architecture
+ * study notes" section 2: Full picks this step's positions, at most 512 per
+ * query; the decoder's first Full layer scans every causally visible position
+ * and builds a pool of at most 2048 blocks x 8 positions, Figure 5).
+ *   ik_codes, ik_sigma  indexer K (tile layout), capacity cap per sequence.
+ *   B, Q        sequences, queries per sequence (Q = 1 decode; Q > 1 e.g. a
+ *               128-token replay chunk).
+ *   iq          [B][Q][4][64] fp32 indexer queries; iw [B][Q][4] head weights.
+ *   n_vis       [B][Q] int32: query (b,q) sees positions [0, n_vis).
+ *   topk        1..2048; pool_blocks 0 (no pool) or topk/8 .. 4096 rounded
+ *               as given (pool_blocks*8 >= topk required when > 0).
+ *   topk_idx    [B][Q][topk] int32 out: the min(topk, n_vis) best positions,
+ *               ascending, then -1.
+ *   pool_idx    [B][Q][pool_blocks] int32 out (ignored when pool_blocks == 0):
+ *               the best min(pool_blocks, ceil(n_vis/8)) blocks, ascending,
+ *               then -1.
+ * Score of position s: the query is quantised per head to E4M3 with
+ * sq = fl(amax/448), w'_h = fl(w_h*sq); dot_h = fp32 sum over channels
+ * 0..63 in order of E4M3(q) * E4M3(k); r_h = max(dot_h, +0);
+ * t = w'_0 r_0 + w'_1 r_1 + w'_2 r_2 + w'_3 r_3 (left to right, each product
+ * rounded); score = fl(sigma_s * t).  Block score = max over its visible
+ * positions.  Ranking: larger score first, equal scores -> lower position
+ * (block) first; -0 == +0.
+ * ws / ws_bytes: device workspace of at least
+ *   csa2_workspace_size(CSA2_OP_INDEX_FULL, B, Q, cap, topk, pool_blocks, 0).
+ */
+int csa2_index_full(const uint8_t* ik_codes, const float* ik_sigma, int64_t cap, int B, int Q,
+                    const float* iq, const float* iw, const int32_t* n_vis, int topk,
+                    int pool_blocks, int32_t* topk_idx, int32_t* pool_idx, void* ws,
+                    size_t ws_bytes, hipStream_t stream);
+
+/*
+ * csa2_index_reindex -- Reindex layer ("DeepSeek V4.1 Flash: architecture
+ * study notes" section 2: reuses the Full layer's indexer K, rescores with its
+ * own indexer query, only inside the pool).
+ *   pool_idx   [B][Q][pool_blocks] as written by csa2_index_full (-1 ignored).
+ *   topk_idx   [B][Q][topk] out: best min(topk, #visible pool positions)
+ *              positions inside the pool, ascending, then -1.
+ * Same score and ranking as csa2_index_full.  ws: at least
+ *   csa2_workspace_size(CSA2_OP_INDEX_REINDEX, B, Q, cap, topk, pool_blocks, 0).
+ */
+int csa2_index_reindex(const uint8_t* ik_codes, const float* ik_sigma, int64_t cap, int B, int Q,
+                       const float* iq, const float* iw, const int32_t* n_vis,
+                       const int32_t* pool_idx, int pool_blocks, int topk, int32_t* topk_idx,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * csa2_sparse_attn_decode -- sparse attention of one decode query per
+ * sequence ("DeepSeek V4.1 Flash: architecture study notes" section 2: at most
+ * 512 selected global records together with the local window; section 4:
+ * dequantise on read, then ordinary attention).
+ *   q          [B][H][128] fp32, H a multiple of 16, <= 128.
+ *   kv_codes, kv_scales, cap  the shared main KV (one cache per sequence).
+ *   topk_idx   [B][topk] int32 positions (-1 = none), e.g. from a Full,
+ *              Reindex or (reused) earlier layer.
+ *   swa_k, swa_v    [B][128][128] E4M3; swa_ks, swa_vs [B][128] fp32;
+ *   swa_len    [B] int32, tokens [0, swa_len) of the window are used.
+ *   out        [B][H][128] fp32; lse [B][H] fp32 = ln(sum exp(logit)).
+ * logit = sm_scale * q . k over the union of selected entries
+ * (k = E2M1 * E4M3 scale) and window tokens (k = sigma * E4M3); one softmax
+ * over the union; out = sum p v / sum p.  No keys -> out 0, lse -inf.
+ * ws: at least csa2_workspace_size(CSA2_OP_ATTN_DECODE, B, 1, cap, topk, 0, H).
+ */
+int csa2_sparse_attn_decode(const float* q, int B, int H, const uint8_t* kv_codes,
+                            const uint8_t* kv_scales, int64_t cap, const int32_t* topk_idx,
+                            int topk, const uint8_t* swa_k, const uint8_t* swa_v,
+                            const float* swa_ks, const float* swa_vs, const int32_t* swa_len,
+                            float sm_scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/*
+ * csa2_sparse_attn_chunk -- attention of a Q-token bounded-replay chunk
+ * ("DeepSeek V4.1 Flash: architecture study notes" section 5: the decoder
+ * replays only the last 128 tokens of the prompt to rebuild its SWA state;
+ * earlier local dependencies are cut off).
+ *   q          [B][Q][H][128] fp32; topk_idx [B][Q][topk].
+ *   swa_k, swa_v    [B][Q][128] E4M3, the chunk's own tokens; swa_ks,
+ *              swa_vs [B][Q].  Query i attends to chunk tokens [0, i].
+ *   out [B][Q][H][128], lse [B][Q][H].  Otherwise as the decode call.
+ * ws: at least csa2_workspace_size(CSA2_OP_ATTN_CHUNK, B, Q, cap, topk, 0, H).
+ */
+int csa2_sparse_attn_chunk(const float* q, int B, int Q, int H, const uint8_t* kv_codes,
+                           const uint8_t* kv_scales, int64_t cap, const int32_t* topk_idx,
+                           int topk, const uint8_t* swa_k, const uint8_t* swa_v,
+                           const float* swa_ks, const float* swa_vs, float sm_scale, float* out,
+                           float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes needed by `op` for these sizes (0 if none; SIZE_MAX if the
+ * sizes are invalid).  Pure host function. */
+size_t csa2_workspace_size(int op, int B, int Q, int64_t cap, int topk, int pool_blocks, int H);
+
+/* Static description of a status code. */
+const char* csa2_status_str(int status);
+
+/* CSA2_ABI_VERSION of the built library. */
+int csa2_abi_version(void);
+
+/*
+ * csa2_codec_probe -- diagnostics: runs the library's own device codecs.
+ *   e4m3_dec [256] fp32 out: decode of every E4M3 code.
+ *   e2m1_dec [16]  fp32 out: decode of every E2M1 code.
+ *   x [n] fp32 in -> e4m3_enc [n], e2m1_enc [n] uint8 out (encoders as used
+ *   by the write path).  Enqueued on `stream` like every call.
+ */
+int csa2_codec_probe(float* e4m3_dec, float* e2m1_dec, const float* x, int64_t n,
+                     uint8_t* e4m3_enc, uint8_t* e2m1_enc, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

@@ -1,0 +1,115 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every
+function include/csa2.h declares, and rejects bad scalar arguments with the
+documented status codes before touching the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch  # noqa: F401  (same HIP runtime as the binding)
+    import compressed_kv_cache_decode_amd as csa2
+    return csa2.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    import compressed_kv_cache_decode_amd as csa2
+    assert set(csa2.EXPORTS) == set(names)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.csa2_abi_version() == 1
+    for st in (0, -1, -2, -3, -4):
+        assert lib.csa2_status_str(st)
+    assert lib.csa2_status_str(12345) == b"unknown status"
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def test_quant_validation(lib):
+    q = lib.csa2_quant_fp4
+    assert q(FAKE, FAKE, 8, 3, None, None, FAKE, FAKE, None) == -2   # ratio
+    assert q(FAKE, FAKE, 8, 2, FAKE, None, FAKE, FAKE, None) == -2   # RoPE with ratio 2
+    assert q(FAKE, FAKE, 7, 2, None, None, FAKE, FAKE, None) == -1   # odd token count
+    assert q(None, FAKE, 8, 1, None, None, FAKE, FAKE, None) == -1   # null
+    assert q(FAKE, FAKE, -1, 1, None, None, FAKE, FAKE, None) == -1
+    assert q(None, None, 0, 1, None, None, None, None, None) == 0    # nothing to do
+    f8 = lib.csa2_quant_fp8
+    assert f8(FAKE, 4, 96, 0, None, FAKE, FAKE, None) == -2          # dim
+    assert f8(FAKE, 4, 128, 1, None, FAKE, FAKE, None) == -2         # tiled needs dim 64
+    assert f8(FAKE, 4, 64, 7, None, FAKE, FAKE, None) == -1          # layout
+    assert f8(FAKE, 4, 64, 0, None, None, FAKE, None) == -1
+
+
+def test_index_validation(lib):
+    f = lib.csa2_index_full
+    ok = dict(cap=1024, B=2, Q=1, topk=512, pool=2048)
+
+    def call(cap=1024, B=2, Q=1, topk=512, pool=2048, ws=FAKE, ws_bytes=1 << 40, ptr=FAKE):
+        return f(ptr, FAKE, cap, B, Q, FAKE, FAKE, FAKE, topk, pool, FAKE, FAKE, ws, ws_bytes, None)
+
+    assert call(ptr=None) == -1
+    assert call(cap=1000) == -1          # not a multiple of 64
+    assert call(cap=0) == -1
+    assert call(B=0) == -1
+    assert call(topk=0) == -1
+    assert call(topk=4096) == -2
+    assert call(pool=8192) == -2
+    assert call(pool=256) == -2          # pool < topk blocks
+    assert call(ws=None) == -3
+    assert call(ws_bytes=10) == -3
+    r = lib.csa2_index_reindex
+    assert r(FAKE, FAKE, 1024, 1, 1, FAKE, FAKE, FAKE, None, 16, 8, FAKE, FAKE, 1 << 40, None) == -1
+    assert r(FAKE, FAKE, 1024, 1, 1, FAKE, FAKE, FAKE, FAKE, 0, 8, FAKE, FAKE, 1 << 40, None) == -1
+    assert r(FAKE, FAKE, 1024, 1, 1, FAKE, FAKE, FAKE, FAKE, 16, 8, FAKE, FAKE, 0, None) == -3
+    del ok
+
+
+def test_attention_validation(lib):
+    a = lib.csa2_sparse_attn_decode
+
+    def call(B=4, H=64, topk=512, sm=0.088, swa_len=FAKE, q=FAKE, ws=FAKE, wsb=1 << 40):
+        return a(q, B, H, FAKE, FAKE, 4096, FAKE, topk, FAKE, FAKE, FAKE, FAKE, swa_len,
+                 ctypes.c_float(sm), FAKE, FAKE, ws, wsb, None)
+
+    assert call(q=None) == -1
+    assert call(H=24) == -2
+    assert call(H=256) == -2
+    assert call(topk=-1) == -1
+    assert call(topk=4096) == -2
+    assert call(sm=float("nan")) == -1
+    assert call(swa_len=None) == -1
+    assert call(ws=None) == -3
+    c = lib.csa2_sparse_attn_chunk
+    assert c(FAKE, 1, 128, 40, FAKE, FAKE, 4096, FAKE, 512, FAKE, FAKE, FAKE, FAKE,
+             ctypes.c_float(0.088), FAKE, FAKE, FAKE, 1 << 40, None) == -2
+
+
+def test_workspace_sizes(lib):
+    ws = lib.csa2_workspace_size
+    big = ctypes.c_size_t(-1).value
+    n_full = ws(1, 16, 1, 131072, 512, 2048, 0)
+    # keys (4 B/position) + block keys (0.5 B/position) dominate
+    assert 16 * 131072 * 4.5 <= n_full < 16 * 131072 * 4.5 + (1 << 20)
+    assert ws(1, 16, 1, 131072, 512, 0, 0) > n_full          # internal pool added
+    assert ws(2, 16, 1, 131072, 512, 2048, 0) >= 16 * 2048 * 8 * 4
+    assert ws(1, 16, 1, 1000, 512, 2048, 0) == big
+    assert ws(99, 1, 1, 64, 1, 1, 16) == big
+    assert ws(3, 16, 1, 131072, 512, 0, 64) > 0               # split-K partials

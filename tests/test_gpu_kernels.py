@@ -1,0 +1,281 @@
+"""GPU parity of every entry point against the CPU oracle, on the same seeded
+inputs, at sizes the oracle finishes in seconds that still span several tiles
+and a ragged tail.
+
+Bit-exact: FP4 codes, E4M3 scales, FP8 codes and sigmas, top-K and pool
+indices.  Attention: per (query, head) row, max |o - o_ref| / max |o_ref|
+<= 2e-3 against the fp64 oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import dev, host, row_rel_err, tile_ik, untile_ik
+
+pytestmark = pytest.mark.gpu
+ATOL_ROW = 2e-3
+SM = 1.0 / math.sqrt(128.0)
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+# --------------------------------------------------------------------------- codecs
+def test_codec_probe_matches_oracle(gpu, oracle_mod):
+    say("codec probe")
+    g = np.random.default_rng(100)
+    finite = np.array([oracle_mod.e4m3_decode(c) for c in range(0x7F)], np.float32)
+    mids = ((finite[1:] + finite[:-1]) / 2).astype(np.float32)
+    x = np.concatenate([finite, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+                        np.exp2(g.uniform(-24, 10, 20000)).astype(np.float32),
+                        np.array([0.0, 1e-45, 1e-40, 447.99, 448, 464, 480, 1e30, 0.25, 0.75,
+                                  1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0], np.float32)])
+    x = np.concatenate([x, -x]).astype(np.float32)
+    e4, e2, enc4, enc2 = gpu.codec_probe(dev(x))
+    e4, e2, enc4, enc2 = host(e4), host(e2), host(enc4), host(enc2)
+    for c in range(256):
+        ref = oracle_mod.e4m3_decode(c)
+        if c & 0x7F == 0x7F:
+            continue  # NaN codes are never produced by the encoders
+        assert e4[c] == ref, (hex(c), e4[c], ref)
+    for c in range(16):
+        assert e2[c] == oracle_mod.e2m1_decode(c), c
+    ref4 = np.array([oracle_mod.e4m3_encode(float(v)) for v in x], np.uint8)
+    ref2 = np.array([oracle_mod.e2m1_encode(float(v)) for v in x], np.uint8)
+    np.testing.assert_array_equal(enc4, ref4)
+    np.testing.assert_array_equal(enc2, ref2)
+
+
+# --------------------------------------------------------------------------- write path
+@pytest.mark.parametrize("ratio,rope,n_tok", [(1, False, 1), (1, False, 203), (1, True, 131),
+                                              (2, False, 2), (2, False, 390)])
+def test_quant_fp4_bit_exact(gpu, oracle_mod, ratio, rope, n_tok):
+    say(f"quant_fp4 ratio={ratio} rope={rope} n_tok={n_tok}")
+    g = np.random.default_rng(200 + n_tok)
+    k = (g.standard_normal((n_tok, 128)) * np.exp2(g.integers(-10, 10, (n_tok, 1)))).astype(np.float32)
+    v = g.standard_normal((n_tok, 128)).astype(np.float32)
+    k[0, :16] = 0.0          # a zero group
+    k[0, 16] = -0.0
+    if n_tok > 1:
+        k[1, :] = 1e5        # saturated scale
+    n_ent = n_tok // ratio
+    cs = oracle_mod.rope_table(np.arange(5000, 5000 + n_ent)) if rope else None
+    codes_ref, scales_ref = oracle_mod.quant_fp4(k, v, ratio, cs)
+    # the binding's own table must equal the oracle's (both fp64 -> fp32)
+    if rope:
+        np.testing.assert_array_equal(gpu.rope_table(np.arange(5000, 5000 + n_ent)), cs)
+    # scatter into a larger cache through dst_rows (reversed order)
+    rows = np.arange(n_ent)[::-1].copy() + 7
+    codes = torch.zeros((n_ent + 9, 128), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((n_ent + 9, 16), dtype=torch.uint8, device="cuda")
+    gpu.quant_fp4(dev(k), dev(v), codes, scales, ratio=ratio,
+                  rope_cs=dev(gpu.rope_table(np.arange(5000, 5000 + n_ent))) if rope else None,
+                  dst_rows=dev(rows))
+    c, s = host(codes), host(scales)
+    np.testing.assert_array_equal(c[rows], codes_ref)
+    np.testing.assert_array_equal(s[rows], scales_ref)
+    untouched = np.setdiff1d(np.arange(n_ent + 9), rows)
+    assert np.all(c[untouched] == 0) and np.all(s[untouched] == 0)
+
+
+@pytest.mark.parametrize("dim,layout,n", [(128, 0, 1), (128, 0, 300), (64, 0, 77), (64, 1, 320)])
+def test_quant_fp8_bit_exact(gpu, oracle_mod, dim, layout, n):
+    say(f"quant_fp8 dim={dim} layout={layout} n={n}")
+    g = np.random.default_rng(300 + n)
+    x = (g.standard_normal((n, dim)) * np.exp2(g.integers(-30, 30, (n, 1)))).astype(np.float32)
+    x[0] = 0.0
+    x[0, 3] = -0.0
+    codes_ref, sig_ref = oracle_mod.quant_fp8_rows(x)
+    codes = torch.zeros(n * dim, dtype=torch.uint8, device="cuda")
+    sigma = torch.zeros(n, dtype=torch.float32, device="cuda")
+    gpu.quant_fp8(dev(x), codes, sigma, layout=layout)
+    c = host(codes)
+    if layout == 1:
+        c = untile_ik(c, 1, n)[0]
+    np.testing.assert_array_equal(c.reshape(n, dim), codes_ref)
+    np.testing.assert_array_equal(host(sigma), sig_ref)
+
+
+# --------------------------------------------------------------------------- indexer
+def make_idx_cache(gpu, oracle_mod, B, cap, seed, dup_frac=0.0):
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((B, cap, 64)).astype(np.float32)
+    if dup_frac:
+        n = int(dup_frac * cap)
+        for b in range(B):
+            x[b, g.integers(0, cap, n)] = x[b, g.integers(0, cap, n)]
+    ikc, iks = oracle_mod.quant_fp8_rows(x)
+    cache = gpu.Cache(B, cap)
+    cache.ik_codes.copy_(dev(tile_ik(ikc)))
+    cache.ik_sigma.copy_(dev(iks.reshape(-1)))
+    return cache, ikc, iks
+
+
+@pytest.mark.parametrize("B,Q,cap,nvis,topk,pool", [
+    (1, 1, 1024, [1024], 512, 0),                 # the 1K single Full layer
+    (2, 1, 4096, [4093, 1500], 512, 2048),        # pool larger than the visible blocks
+    (3, 1, 8192, [8192, 8000, 13], 64, 128),      # ragged tails, fewer visible than K
+    (2, 3, 2048, [[2048, 2047, 1], [0, 999, 1024]], 40, 40),
+    (1, 1, 32768, [32765], 512, 2048),            # more blocks than the pool
+    (4, 1, 16384, [16384, 16384, 16000, 8], 512, 0),
+])
+def test_index_full_bit_exact(gpu, oracle_mod, B, Q, cap, nvis, topk, pool):
+    say(f"index_full B={B} Q={Q} cap={cap} topk={topk} pool={pool}")
+    cache, ikc, iks = make_idx_cache(gpu, oracle_mod, B, cap, 400 + cap + B, dup_frac=0.2)
+    g = np.random.default_rng(401)
+    iq = g.standard_normal((B, Q, 4, 64)).astype(np.float32)
+    iw = g.random((B, Q, 4)).astype(np.float32)
+    nv = np.array(nvis, np.int32).reshape(B, Q)
+    tk_ref, pl_ref = oracle_mod.index_full_batch(ikc, iks, iq, iw, nv, topk, pool)
+    tk = torch.full((B, Q, topk), -7, dtype=torch.int32, device="cuda")
+    pl = torch.full((B, Q, max(pool, 1)), -7, dtype=torch.int32, device="cuda")
+    gpu.index_full(cache, dev(iq), dev(iw), dev(nv), tk, pl if pool else None, topk=topk,
+                   pool_blocks=pool)
+    np.testing.assert_array_equal(host(tk), tk_ref)
+    if pool:
+        np.testing.assert_array_equal(host(pl), pl_ref)
+
+
+def test_index_full_all_ties(gpu, oracle_mod):
+    say("index_full all-equal scores")
+    B, cap = 1, 4096
+    x = np.tile(np.random.default_rng(5).standard_normal((1, 1, 64)), (B, cap, 1)).astype(np.float32)
+    ikc, iks = oracle_mod.quant_fp8_rows(x)
+    cache = gpu.Cache(B, cap)
+    cache.ik_codes.copy_(dev(tile_ik(ikc)))
+    cache.ik_sigma.copy_(dev(iks.reshape(-1)))
+    iq = np.random.default_rng(6).standard_normal((B, 1, 4, 64)).astype(np.float32)
+    iw = np.ones((B, 1, 4), np.float32)
+    nv = np.array([[4000]], np.int32)
+    tk = torch.empty((B, 1, 512), dtype=torch.int32, device="cuda")
+    pl = torch.empty((B, 1, 2048), dtype=torch.int32, device="cuda")
+    gpu.index_full(cache, dev(iq), dev(iw), dev(nv), tk, pl, topk=512, pool_blocks=2048)
+    assert host(tk)[0, 0].tolist() == list(range(512))
+    p = host(pl)[0, 0]
+    assert p[:500].tolist() == list(range(500)) and np.all(p[500:] == -1)
+
+
+@pytest.mark.parametrize("B,cap,nvis,pool,topk", [(2, 8192, [8192, 5001], 512, 512),
+                                                  (3, 32768, [32768, 30000, 77], 2048, 512),
+                                                  (1, 4096, [4096], 64, 100)])
+def test_index_reindex_bit_exact(gpu, oracle_mod, B, cap, nvis, pool, topk):
+    say(f"index_reindex B={B} cap={cap} pool={pool} topk={topk}")
+    cache, ikc, iks = make_idx_cache(gpu, oracle_mod, B, cap, 500 + cap, dup_frac=0.1)
+    g = np.random.default_rng(501)
+    iq = g.standard_normal((B, 1, 4, 64)).astype(np.float32)
+    iw = g.random((B, 1, 4)).astype(np.float32)
+    iq2 = g.standard_normal((B, 1, 4, 64)).astype(np.float32)
+    iw2 = g.random((B, 1, 4)).astype(np.float32)
+    nv = np.array(nvis, np.int32).reshape(B, 1)
+    _, pool_ref = oracle_mod.index_full_batch(ikc, iks, iq, iw, nv, min(topk, pool), pool)
+    tk_ref = oracle_mod.index_reindex_batch(ikc, iks, iq2, iw2, nv, pool_ref, topk)
+    tk = torch.full((B, 1, topk), -7, dtype=torch.int32, device="cuda")
+    gpu.index_reindex(cache, dev(iq2), dev(iw2), dev(nv), dev(pool_ref), tk, topk=topk)
+    np.testing.assert_array_equal(host(tk), tk_ref)
+
+
+def test_full_topk_equals_reindex_with_own_query(gpu, oracle_mod):
+    say("Full top-K == Reindex(own query, own pool)")
+    B, cap = 2, 16384
+    cache, ikc, iks = make_idx_cache(gpu, oracle_mod, B, cap, 600, dup_frac=0.3)
+    g = np.random.default_rng(601)
+    iq = dev(g.standard_normal((B, 1, 4, 64)).astype(np.float32))
+    iw = dev(g.random((B, 1, 4)).astype(np.float32))
+    nv = dev(np.array([[16384], [12345]], np.int32))
+    tk = torch.empty((B, 1, 512), dtype=torch.int32, device="cuda")
+    pl = torch.empty((B, 1, 2048), dtype=torch.int32, device="cuda")
+    tk2 = torch.empty_like(tk)
+    gpu.index_full(cache, iq, iw, nv, tk, pl, topk=512, pool_blocks=2048)
+    gpu.index_reindex(cache, iq, iw, nv, pl, tk2, topk=512)
+    np.testing.assert_array_equal(host(tk), host(tk2))
+
+
+# --------------------------------------------------------------------------- attention
+def make_attn_case(gpu, oracle_mod, B, cap, H, seed, Q=1):
+    g = np.random.default_rng(seed)
+    k = g.standard_normal((B, cap, 128)).astype(np.float32)
+    v = g.standard_normal((B, cap, 128)).astype(np.float32)
+    codes, scales = oracle_mod.quant_fp4(k.reshape(-1, 128), v.reshape(-1, 128))
+    cache = gpu.Cache(B, cap)
+    cache.kv_codes.copy_(dev(codes))
+    cache.kv_scales.copy_(dev(scales))
+    rows = 128 if Q == 1 else Q
+    sk, sks = oracle_mod.quant_fp8_rows(g.standard_normal((B, rows, 128)).astype(np.float32))
+    sv, svs = oracle_mod.quant_fp8_rows(g.standard_normal((B, rows, 128)).astype(np.float32))
+    shape = (B, H, 128) if Q == 1 else (B, Q, H, 128)
+    q = g.standard_normal(shape).astype(np.float32)
+    return cache, codes.reshape(B, cap, 128), scales.reshape(B, cap, 16), sk, sv, sks, svs, q
+
+
+@pytest.mark.parametrize("B,cap,H,topk,swa_len,n_sel", [
+    (1, 1024, 16, 512, [128], [512]),
+    (3, 4096, 64, 512, [128, 5, 0], [512, 300, 0]),
+    (2, 2048, 32, 100, [77, 128], [100, 3]),
+    (4, 1024, 128, 512, [128, 128, 1, 64], [512, 511, 512, 17]),
+    (1, 640, 48, 0, [128], [0]),
+])
+def test_sparse_attn_decode(gpu, oracle_mod, B, cap, H, topk, swa_len, n_sel):
+    say(f"attn_decode B={B} cap={cap} H={H} topk={topk}")
+    cache, codes, scales, sk, sv, sks, svs, q = make_attn_case(gpu, oracle_mod, B, cap, H, 700 + H)
+    g = np.random.default_rng(701)
+    idx = np.full((B, max(topk, 1)), -1, np.int32)[:, :topk]
+    for b in range(B):
+        sel = np.sort(g.choice(cap, n_sel[b], replace=False))
+        idx[b, :n_sel[b]] = sel
+    sl = np.array(swa_len, np.int32)
+    out_ref, lse_ref = oracle_mod.attn_decode_batch(q, codes, scales,
+                                                    idx if topk else np.zeros((B, 0), np.int32),
+                                                    sk, sv, sks, svs, sl, SM)
+    out = torch.empty((B, H, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    idx_d = dev(idx) if topk else torch.empty((B, 0), dtype=torch.int32, device="cuda")
+    gpu.sparse_attn_decode(dev(q), cache, idx_d, dev(sk), dev(sv), dev(sks), dev(svs), dev(sl),
+                           out, lse)
+    o, l = host(out), host(lse)
+    empty = (np.array(n_sel) == 0) & (sl == 0)
+    for b in range(B):
+        if empty[b]:
+            assert np.all(o[b] == 0) and np.all(np.isneginf(l[b]))
+            continue
+        err = row_rel_err(o[b], out_ref[b])
+        assert err.max() <= ATOL_ROW, (b, err.max())
+        np.testing.assert_allclose(l[b], lse_ref[b], rtol=2e-3, atol=2e-3)
+
+
+def test_sparse_attn_decode_ignores_out_of_range_indices(gpu, oracle_mod):
+    say("attn_decode with out-of-range indices")
+    B, cap, H = 1, 1024, 16
+    cache, codes, scales, sk, sv, sks, svs, q = make_attn_case(gpu, oracle_mod, B, cap, H, 720)
+    idx = np.full((B, 64), -1, np.int32)
+    idx[0, :10] = np.arange(10) * 7
+    bad = idx.copy()
+    bad[0, 10:20] = [cap, cap + 5, 1 << 30, -5, -100, cap * 2, 99999, 4096, 2048, 1025]
+    sl = np.array([128], np.int32)
+    out_ref, _ = oracle_mod.attn_decode_batch(q, codes, scales, idx, sk, sv, sks, svs, sl, SM)
+    out = torch.empty((B, H, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    gpu.sparse_attn_decode(dev(q), cache, dev(bad), dev(sk), dev(sv), dev(sks), dev(svs), dev(sl),
+                           out, lse)
+    assert row_rel_err(host(out)[0], out_ref[0]).max() <= ATOL_ROW
+
+
+@pytest.mark.parametrize("B,Q,cap,H", [(1, 128, 2048, 64), (2, 37, 1024, 16)])
+def test_sparse_attn_chunk(gpu, oracle_mod, B, Q, cap, H):
+    say(f"attn_chunk B={B} Q={Q} cap={cap} H={H}")
+    cache, codes, scales, sk, sv, sks, svs, q = make_attn_case(gpu, oracle_mod, B, cap, H, 800, Q=Q)
+    g = np.random.default_rng(801)
+    idx = np.full((B, Q, 512), -1, np.int32)
+    for b in range(B):
+        for i in range(Q):
+            n = min(512, cap - Q + i + 1)
+            idx[b, i, :n] = np.sort(g.choice(cap - Q + i + 1, n, replace=False))
+    out_ref, lse_ref = oracle_mod.attn_chunk_batch(q, codes, scales, idx, sk, sv, sks, svs, SM)
+    out = torch.empty((B, Q, H, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Q, H), dtype=torch.float32, device="cuda")
+    gpu.sparse_attn_chunk(dev(q), cache, dev(idx), dev(sk), dev(sv), dev(sks), dev(svs), out, lse)
+    err = row_rel_err(host(out), out_ref)
+    assert err.max() <= ATOL_ROW, err.max()
+    np.testing.assert_allclose(host(lse), lse_ref, rtol=2e-3, atol=2e-3)

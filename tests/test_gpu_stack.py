@@ -1,0 +1,153 @@
+"""GPU parity of whole layer stacks against the oracle, including the full-size
+workloads in the launch configuration the bench times, checked on sampled
+sequences / queries that the oracle computes one by one.
+
+The caches are written by the library's own write path (csa2_quant_fp4 /
+csa2_quant_fp8) from the seeded fp32 inputs; the oracle quantises the same
+inputs itself, and the bytes of the sampled sequences are compared first.
+"""
+import math
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from compressed_kv_cache_decode_amd import synth
+from gpu_util import dev, host, row_rel_err, untile_ik
+
+pytestmark = pytest.mark.gpu
+SM = 1.0 / math.sqrt(128.0)
+
+
+def say(msg):
+    print(f"[gpu-case] {time.strftime('%H:%M:%S')} {msg}", flush=True)
+
+
+def build_cache_on_gpu(gpu, inp, cap, rope=False):
+    """Write the main KV and indexer K of every sequence with the library."""
+    B, n_tok = inp.k_tok.shape[:2]
+    n_ent = n_tok // inp.wl.ratio
+    cache = gpu.Cache(B, cap)
+    for b in range(B):
+        rows = cache.rows(b, np.arange(n_ent))
+        cs = dev(gpu.rope_table(np.arange(n_ent))) if rope else None
+        gpu.quant_fp4(dev(inp.k_tok[b]), dev(inp.v_tok[b]), cache.kv_codes, cache.kv_scales,
+                      ratio=inp.wl.ratio, rope_cs=cs, dst_rows=rows)
+        gpu.quant_fp8(dev(inp.idx_k[b]), cache.ik_codes, cache.ik_sigma, layout=gpu.FP8_IDX_TILED,
+                      dst_rows=rows)
+    return cache
+
+
+def quantize_windows(gpu, swa_k, swa_v):
+    """[L][B][128][128] fp32 -> device E4M3 codes and fp32 sigmas (library)."""
+    shp = swa_k.shape
+    out = []
+    for x in (swa_k, swa_v):
+        codes = torch.empty(int(np.prod(shp)), dtype=torch.uint8, device="cuda")
+        sig = torch.empty(int(np.prod(shp[:-1])), dtype=torch.float32, device="cuda")
+        gpu.quant_fp8(dev(x.reshape(-1, 128)), codes, sig)
+        out += [codes.view(*shp), sig.view(*shp[:-1])]
+    return out
+
+
+def oracle_stack(oracle_mod, inp, b, topk, pool_blocks, plan, rope=False):
+    """Oracle run of one sequence: bytes, per-layer indices and outputs."""
+    n_ent = inp.k_tok.shape[1] // inp.wl.ratio
+    cs = oracle_mod.rope_table(np.arange(n_ent)) if rope else None
+    codes, scales = oracle_mod.quant_fp4(inp.k_tok[b], inp.v_tok[b], inp.wl.ratio, cs)
+    ikc, iks = oracle_mod.quant_fp8_rows(inp.idx_k[b])
+    res = {"codes": codes, "scales": scales, "ikc": ikc, "iks": iks, "topk": [], "out": [],
+           "lse": []}
+    cur, pool, k = None, None, 0
+    for layer, mode in enumerate(plan):
+        if mode == "F":
+            cur, pool = oracle_mod.index_full(ikc, iks, n_ent, inp.iq[k, b], inp.iw[k, b], topk,
+                                              pool_blocks)
+            k += 1
+        elif mode == "X":
+            cur = oracle_mod.index_reindex(ikc, iks, n_ent, inp.iq[k, b], inp.iw[k, b], pool, topk)
+            k += 1
+        sk, sks = oracle_mod.quant_fp8_rows(inp.swa_k[layer, b])
+        sv, svs = oracle_mod.quant_fp8_rows(inp.swa_v[layer, b])
+        o, l = oracle_mod.attn(inp.q[layer, b], codes, scales, cur, sk, sv, sks, svs,
+                               int(inp.swa_len[b]), SM)
+        res["topk"].append(cur)
+        res["out"].append(o)
+        res["lse"].append(l)
+    return res
+
+
+def run_stack_case(gpu, oracle_mod, wl, n_ent=None, B=None, layers=None, sample=None,
+                   topk=512, pool_blocks=None):
+    from compressed_kv_cache_decode_amd.stack import DecodeStack
+    pool_blocks = wl.pool_blocks if pool_blocks is None else pool_blocks
+    say(f"{wl.name}: drawing inputs")
+    inp = synth.decode_inputs(wl, n_ent=n_ent, B=B, layers=layers)
+    B, n_tok = inp.k_tok.shape[:2]
+    n_ent = n_tok // wl.ratio
+    plan = wl.plan if layers is None else wl.plan[:layers]
+    cap = (n_ent + 63) // 64 * 64
+    say(f"{wl.name}: B={B} n_ent={n_ent} plan={plan} -> writing caches on the GPU")
+    cache = build_cache_on_gpu(gpu, inp, cap)
+    swk, sks, swv, svs = quantize_windows(gpu, inp.swa_k, inp.swa_v)
+    st = DecodeStack(cache, plan, B, wl.H, topk=topk, pool_blocks=pool_blocks)
+    n_vis = dev(np.full((B, 1), n_ent, np.int32))
+    say(f"{wl.name}: stack step on the GPU")
+    used = st.step(dev(inp.iq[:, :, None]), dev(inp.iw[:, :, None]), n_vis, dev(inp.q), swk, swv,
+                   sks, svs, dev(inp.swa_len))
+    torch.cuda.synchronize()
+    # Reuse layers attend with exactly their source layer's buffer
+    for layer, src in enumerate(st.sources):
+        assert used[layer].data_ptr() == used[src].data_ptr()
+    kvc, kvs = host(cache.kv_codes), host(cache.kv_scales)
+    ikc_all = untile_ik(host(cache.ik_codes), B, cap)
+    iks_all = host(cache.ik_sigma).reshape(B, cap)
+    tk_all = [host(t) for t in used]
+    out_all, lse_all = host(st.out), host(st.lse)
+    sample = range(B) if sample is None else sample
+    for b in sample:
+        say(f"{wl.name}: oracle for sequence {b}")
+        ref = oracle_stack(oracle_mod, inp, b, topk, pool_blocks, plan)
+        r0 = b * cap
+        np.testing.assert_array_equal(kvc[r0:r0 + n_ent], ref["codes"])
+        np.testing.assert_array_equal(kvs[r0:r0 + n_ent], ref["scales"])
+        np.testing.assert_array_equal(ikc_all[b, :n_ent], ref["ikc"])
+        np.testing.assert_array_equal(iks_all[b, :n_ent], ref["iks"])
+        for layer in range(len(plan)):
+            np.testing.assert_array_equal(tk_all[layer][b, 0], ref["topk"][layer],
+                                          err_msg=f"layer {layer} ({plan[layer]})")
+            err = row_rel_err(out_all[layer, b], ref["out"][layer])
+            assert err.max() <= 2e-3, (layer, err.max())
+            np.testing.assert_allclose(lse_all[layer, b], ref["lse"][layer], rtol=2e-3, atol=2e-3)
+    return inp, tk_all
+
+
+def test_small_decoder_stack(gpu, oracle_mod):
+    wl = synth.WORKLOADS["decoder_stack_128k"]
+    run_stack_case(gpu, oracle_mod, wl, n_ent=20000, B=3, layers=9, topk=128, pool_blocks=256)
+
+
+def test_full_layer_1k(gpu, oracle_mod):
+    run_stack_case(gpu, oracle_mod, synth.WORKLOADS["full_1k"])
+
+
+def test_encoder_group_16k(gpu, oracle_mod):
+    """Encoder-style group: 32768 tokens averaged 2:1, 1 Full + 5 Reuse, batch 8."""
+    run_stack_case(gpu, oracle_mod, synth.WORKLOADS["encoder_group_16k"])
+
+
+def test_decoder_stack_128k_full_size(gpu, oracle_mod):
+    """The 128K decoder stack at full size (B=16, 20 layers); oracle on 3 sequences."""
+    run_stack_case(gpu, oracle_mod, synth.WORKLOADS["decoder_stack_128k"], sample=[0, 9, 15])
+
+
+def test_decoder_stack_1m_full_size(gpu, oracle_mod):
+    """1M-position stack (B=4) with planted clusters; oracle on 2 sequences;
+    the planted blocks must dominate the Full layer's pool."""
+    wl = synth.WORKLOADS["decoder_stack_1m"]
+    inp, tk_all = run_stack_case(gpu, oracle_mod, wl, sample=[0, 3], layers=5)
+    for b in range(wl.B):
+        planted = set((inp.planted[b][:, None] * 8 + np.arange(8)).ravel().tolist())
+        sel = [p for p in tk_all[0][b, 0].tolist() if p >= 0]
+        assert sum(p in planted for p in sel) > 0.5 * len(sel)
