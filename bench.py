@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Throughput of one CSA2 decode stack step on one MI355X.
+
+Workload (default decoder_stack_128k): 16 sequences, each with its own shared
+global KV of 131072 entries (FP4 main KV + FP8 indexer K), 20 layers planned
+F RRR X RRR X RRR X RRR X RRR (1 Full, 4 Reindex, 15 Reuse), 64 query heads,
+top-512, pool of 2048 blocks x 8, every layer with its own FP8 128-token
+window.  One step = the write path of the new token (FP4 main KV entry after
+RoPE + FP8 indexer key, for every sequence) + the Full-layer scan, block pool
+and top-K + 4 Reindex selections + 20 sparse attentions.  All inputs are
+resident in HBM before timing; `cache_sets` identical copies of the caches at
+different addresses are used in rotation so that consecutive steps cannot be
+served from the 256 MB last-level cache.
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+  value       = sequences (decode queries) per second through the whole stack
+  roofline    = the Full-layer scan kernel (the only one whose work grows with
+                context): algorithmic bytes (68 B per visible position) over
+                its mean duration from HIP events, against 8 TB/s
+  cpu_baseline= the CPU oracle on a bounded sample of the same workload
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0
+METRIC = "CSA2 decode queries/s per layer stack at 128K ctx; achieved HBM GB/s vs peak"
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="decoder_stack_128k")
+    p.add_argument("--cache-sets", type=int, default=3)
+    p.add_argument("--no-graph", action="store_true", help="time eager launches, no HIP graph")
+    p.add_argument("--cpu-seqs", type=int, default=0,
+                   help="sequences in the CPU-oracle sample (0 = one whole batch)")
+    p.add_argument("--skip-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+# --------------------------------------------------------------------------- bytes
+def attn_bytes(n_sel, n_swa, H):
+    """Algorithmic bytes of one query's attention in one layer: 144 B per
+    selected FP4 entry, 264 B per window token (2 x 128 E4M3 + 2 fp32 scales),
+    fp32 q and out."""
+    return 144 * n_sel + 264 * n_swa + 2 * H * 128 * 4
+
+
+def step_bytes(wl):
+    """Algorithmic HBM bytes of one stack step (all queries)."""
+    B, N, H = wl.B, wl.n_ent, wl.H
+    scan = 68 * N * B
+    n_x = wl.plan.count("X")
+    reindex = n_x * 68 * min(wl.pool_blocks * 8, N) * B
+    attn = len(wl.plan) * B * attn_bytes(min(wl.topk, N), 128, H)
+    write = B * (2 * 128 * 4 + 144 + 64 * 4 + 68)
+    return scan + reindex + attn + write, scan
+
+
+# --------------------------------------------------------------------------- GPU side
+class StepSet:
+    """One complete, independent copy of a step's device inputs."""
+
+    def __init__(self, csa2, DecodeStack, cache, wl, dev_inputs):
+        self.cache, self.ratio = cache, wl.ratio
+        self.stack = DecodeStack(cache, wl.plan, wl.B, wl.H, topk=wl.topk,
+                                 pool_blocks=wl.pool_blocks)
+        self.inp = {k: v.clone() for k, v in dev_inputs.items()}
+        self.csa2 = csa2
+
+    def run(self, scan_timer=None):
+        c, i = self.csa2, self.inp
+        # write path of the new token of every sequence (position n_ent - 1)
+        c.quant_fp4(i["k_new"], i["v_new"], self.cache.kv_codes, self.cache.kv_scales,
+                    ratio=self.ratio, rope_cs=i["rope_new"], dst_rows=i["rows_new"])
+        c.quant_fp8(i["idx_new"], self.cache.ik_codes, self.cache.ik_sigma,
+                    layout=c.FP8_IDX_TILED, dst_rows=i["rows_new"])
+        self.stack.step(i["iq"], i["iw"], i["n_vis"], i["q"], i["swk"], i["swv"], i["sks"],
+                        i["svs"], i["swa_len"], scan_timer=scan_timer)
+
+
+def build_sets(args, wl, inp):
+    import numpy as np
+    import torch
+
+    import compressed_kv_cache_decode_amd as csa2
+    from compressed_kv_cache_decode_amd.stack import DecodeStack
+
+    B, N = wl.B, wl.n_ent
+    cap = (N + 63) // 64 * 64
+    log(f"writing the caches with the library: B={B} entries={N} ratio={wl.ratio}")
+    cache0 = csa2.Cache(B, cap)
+    for b in range(B):
+        rows = cache0.rows(b, np.arange(N))
+        k = torch.from_numpy(inp.k_tok[b]).cuda()
+        v = torch.from_numpy(inp.v_tok[b]).cuda()
+        cs = torch.from_numpy(csa2.rope_table(np.arange(N))).cuda() if wl.ratio == 1 else None
+        csa2.quant_fp4(k, v, cache0.kv_codes, cache0.kv_scales, ratio=wl.ratio, rope_cs=cs,
+                       dst_rows=rows)
+        csa2.quant_fp8(torch.from_numpy(inp.idx_k[b]).cuda(), cache0.ik_codes, cache0.ik_sigma,
+                       layout=csa2.FP8_IDX_TILED, dst_rows=rows)
+        del k, v, cs
+    L = len(wl.plan)
+    swk = torch.empty((L, B, 128, 128), dtype=torch.uint8, device="cuda")
+    swv = torch.empty_like(swk)
+    sks = torch.empty((L, B, 128), dtype=torch.float32, device="cuda")
+    svs = torch.empty_like(sks)
+    csa2.quant_fp8(torch.from_numpy(inp.swa_k.reshape(-1, 128)).cuda(), swk, sks)
+    csa2.quant_fp8(torch.from_numpy(inp.swa_v.reshape(-1, 128)).cuda(), swv, svs)
+    last = N - 1
+    tok = last * wl.ratio  # the new token (pair) of every sequence
+    if wl.ratio == 1:
+        k_new, v_new = inp.k_tok[:, last], inp.v_tok[:, last]
+    else:  # the newest pair is re-averaged by the write path
+        k_new = inp.k_tok[:, tok:tok + 2].reshape(-1, 128)
+        v_new = inp.v_tok[:, tok:tok + 2].reshape(-1, 128)
+    dev_inputs = {
+        "k_new": torch.from_numpy(np.ascontiguousarray(k_new)).cuda(),
+        "v_new": torch.from_numpy(np.ascontiguousarray(v_new)).cuda(),
+        "idx_new": torch.from_numpy(np.ascontiguousarray(inp.idx_k[:, last])).cuda(),
+        "rope_new": (torch.from_numpy(csa2.rope_table(np.full(B, last))).cuda()
+                     if wl.ratio == 1 else None),
+        "rows_new": torch.arange(B, dtype=torch.int64, device="cuda") * cap + last,
+        "iq": torch.from_numpy(inp.iq[:, :, None]).cuda(),
+        "iw": torch.from_numpy(inp.iw[:, :, None]).cuda(),
+        "n_vis": torch.full((B, 1), N, dtype=torch.int32, device="cuda"),
+        "q": torch.from_numpy(inp.q).cuda(),
+        "swk": swk, "swv": swv, "sks": sks, "svs": svs,
+        "swa_len": torch.from_numpy(inp.swa_len).cuda(),
+    }
+    if dev_inputs["rope_new"] is None:
+        del dev_inputs["rope_new"]
+    sets = []
+    for s in range(args.cache_sets):
+        cache = cache0 if s == 0 else csa2.Cache(B, cap)
+        if s:
+            for name in ("kv_codes", "kv_scales", "ik_codes", "ik_sigma"):
+                getattr(cache, name).copy_(getattr(cache0, name))
+        ss = StepSet(csa2, DecodeStack, cache, wl, dev_inputs)
+        if "rope_new" not in ss.inp:
+            ss.inp["rope_new"] = None
+        sets.append(ss)
+    torch.cuda.synchronize()
+    log(f"{len(sets)} cache sets of {cache0.nbytes / 1e6:.1f} MB each")
+    return csa2, sets
+
+
+def time_gpu(args, wl, csa2, sets):
+    import torch
+    stream = torch.cuda.Stream()
+    graphs = None
+    with torch.cuda.stream(stream):
+        for i in range(max(args.warmup, 1)):
+            sets[i % len(sets)].run()
+        torch.cuda.synchronize()
+        if not args.no_graph:
+            graphs = []
+            for s in sets:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    s.run()
+                graphs.append(g)
+            for i in range(args.warmup):
+                graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+
+        log(f"timing {args.steps} steps ({'graph replay' if graphs else 'eager'})")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            if graphs:
+                graphs[i % len(graphs)].replay()
+            else:
+                sets[i % len(sets)].run()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+
+        # the dominant kernel, timed with HIP events around its own dispatch
+        timer = csa2.KernelTimer(args.steps)
+        for i in range(args.steps):
+            sets[i % len(sets)].run(scan_timer=timer)
+        torch.cuda.synchronize()
+        scan_ms = timer.durations_ms()
+        timer.close()
+        t1 = time.perf_counter()
+        for i in range(args.steps):
+            sets[i % len(sets)].run()
+        torch.cuda.synchronize()
+        eager_elapsed = time.perf_counter() - t1
+    return elapsed, scan_ms, eager_elapsed
+
+
+# --------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(args, wl, inp):
+    """The oracle as it stands, on its own caches (built before timing), for a
+    sample of the batch's sequences: one whole stack step per sequence."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    sys.path.insert(0, ROOT)
+    import oracle
+
+    S = min(args.cpu_seqs or wl.B, wl.B)
+    N = wl.n_ent
+    threads = oracle.num_threads()
+    log(f"cpu baseline: oracle caches for {S} sequences ({threads} threads)")
+
+    def prep(b):
+        cs = oracle.rope_table(np.arange(N)) if wl.ratio == 1 else None
+        c, s = oracle.quant_fp4(inp.k_tok[b], inp.v_tok[b], wl.ratio, cs)
+        ik, iks = oracle.quant_fp8_rows(inp.idx_k[b])
+        return c, s, ik, iks
+
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        parts = list(ex.map(prep, range(S)))
+    codes = np.stack([p[0] for p in parts])
+    scales = np.stack([p[1] for p in parts])
+    ikc = np.stack([p[2] for p in parts])
+    iks = np.stack([p[3] for p in parts])
+    L = len(wl.plan)
+    swk, sks = oracle.quant_fp8_rows(inp.swa_k[:, :S])
+    swv, svs = oracle.quant_fp8_rows(inp.swa_v[:, :S])
+    nv = np.full((S, 1), N, np.int32)
+    sm = 1.0 / math.sqrt(128.0)
+    log("cpu baseline: timing one stack step of the sample")
+    t0 = time.perf_counter()
+    pool, cur, k = None, None, 0
+    for layer, mode in enumerate(wl.plan):
+        if mode == "F":
+            cur, pool = oracle.index_full_batch(ikc, iks, inp.iq[k, :S, None], inp.iw[k, :S, None],
+                                                nv, wl.topk, wl.pool_blocks)
+            k += 1
+        elif mode == "X":
+            cur = oracle.index_reindex_batch(ikc, iks, inp.iq[k, :S, None], inp.iw[k, :S, None],
+                                             nv, pool, wl.topk)
+            k += 1
+        oracle.attn_decode_batch(inp.q[layer, :S], codes, scales, cur[:, 0], swk[layer],
+                                 swv[layer], sks[layer], svs[layer], inp.swa_len[:S], sm)
+    dt = time.perf_counter() - t0
+    del L
+    return {"value": S / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{S} of the {wl.B} sequences, one full {len(wl.plan)}-layer stack step "
+                      f"each ({N} entries); oracle caches built before timing",
+            "seconds": dt}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); the path is "
+              "data-parallel over sequences and is measured on one GPU's share.", file=sys.stderr)
+        sys.exit(2)
+    sys.path.insert(0, ROOT)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+    from compressed_kv_cache_decode_amd import synth
+    wl = synth.WORKLOADS[args.workload]
+    if wl.Q != 1:
+        print("bench.py times decode stacks; the replay chunk is covered by the tests",
+              file=sys.stderr)
+        sys.exit(2)
+    log(f"workload {wl.name}: drawing inputs (seed {wl.seed})")
+    inp = synth.decode_inputs(wl)
+    csa2, sets = build_sets(args, wl, inp)
+    elapsed, scan_ms, eager_elapsed = time_gpu(args, wl, csa2, sets)
+
+    total_bytes, scan_bytes = step_bytes(wl)
+    ms_per_step = elapsed / args.steps * 1e3
+    value = wl.B * args.steps / elapsed
+    scan_mean = sum(scan_ms) / len(scan_ms)
+    scan_gbs = scan_bytes / (scan_mean * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "sequences": wl.B, "entries": wl.n_ent,
+                   "layers": len(wl.plan), "plan": wl.plan, "heads": wl.H, "topk": wl.topk,
+                   "pool_blocks": wl.pool_blocks, "window": 128, "cache_sets": args.cache_sets,
+                   "launch": "eager" if args.no_graph else "hip-graph"},
+        "roofline": {"bound": "hbm", "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "k_scan (Full-layer indexer scan)",
+                     "bytes_per_launch": scan_bytes, "mean_us": round(scan_mean * 1e3, 2)},
+        "step": {"algorithmic_bytes": total_bytes,
+                 "achieved_GBps": round(total_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                 "frac_of_hbm_peak": round(total_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "eager_ms_per_step": round(eager_elapsed / args.steps * 1e3, 4)},
+    }
+    if not args.skip_cpu_baseline:
+        cb = cpu_baseline(args, wl, inp)
+        result["cpu_baseline"] = {k: (round(v, 3) if isinstance(v, float) else v)
+                                  for k, v in cb.items()}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

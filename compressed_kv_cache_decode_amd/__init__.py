@@ -40,7 +40,8 @@ OP_ATTN_CHUNK = 4
 STATUS = {0: "ok", -1: "CSA2_E_ARG", -2: "CSA2_E_UNSUPPORTED", -3: "CSA2_E_WORKSPACE",
           -4: "CSA2_E_HIP"}
 
-EXPORTS = ("csa2_quant_fp4", "csa2_quant_fp8", "csa2_index_full", "csa2_index_reindex",
+EXPORTS = ("csa2_quant_fp4", "csa2_quant_fp8", "csa2_index_full", "csa2_index_full_timed",
+           "csa2_index_reindex",
            "csa2_sparse_attn_decode", "csa2_sparse_attn_chunk", "csa2_workspace_size",
            "csa2_status_str", "csa2_abi_version", "csa2_codec_probe")
 
@@ -52,6 +53,8 @@ _SIGS = {
     "csa2_quant_fp8": (_int, [_vp, _i64, _int, _int, _vp, _vp, _vp, _vp]),
     "csa2_index_full": (_int, [_vp, _vp, _i64, _int, _int, _vp, _vp, _vp, _int, _int, _vp, _vp,
                                _vp, _sz, _vp]),
+    "csa2_index_full_timed": (_int, [_vp, _vp, _i64, _int, _int, _vp, _vp, _vp, _int, _int, _vp,
+                                     _vp, _vp, _sz, _vp, _vp, _vp]),
     "csa2_index_reindex": (_int, [_vp, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _int, _int,
                                   _vp, _vp, _sz, _vp]),
     "csa2_sparse_attn_decode": (_int, [_vp, _int, _int, _vp, _vp, _i64, _vp, _int, _vp, _vp, _vp,
@@ -61,7 +64,7 @@ _SIGS = {
     "csa2_workspace_size": (_sz, [_int, _int, _int, _i64, _int, _int, _int]),
     "csa2_status_str": (ctypes.c_char_p, [_int]),
     "csa2_abi_version": (_int, []),
-    "csa2_codec_probe": (_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp]),
+    "csa2_codec_probe": (_int, [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),
 }
 
 
@@ -196,20 +199,22 @@ def quant_fp8(x, codes, sigma, layout=FP8_ROWS, dst_rows=None, stream=None):
 
 
 def index_full(cache, iq, iw, n_vis, topk_idx, pool_idx=None, topk=DEFAULT_TOPK,
-               pool_blocks=0, ws=None, stream=None):
+               pool_blocks=0, ws=None, stream=None, scan_timer=None):
     """iq [B][Q][4][64] f32, iw [B][Q][4] f32, n_vis [B][Q] i32 ->
-    topk_idx [B][Q][topk] i32, pool_idx [B][Q][pool_blocks] i32."""
+    topk_idx [B][Q][topk] i32, pool_idx [B][Q][pool_blocks] i32.
+    scan_timer: optional KernelTimer whose events bracket the scan kernel."""
     B, Q = iq.shape[0], iq.shape[1]
     need = workspace_size(OP_INDEX_FULL, B, Q, cache.cap, topk, pool_blocks, 0)
     if ws is None:
         ws = alloc_workspace(need, iq.device)
-    rc = lib().csa2_index_full(
+    ev = scan_timer.next_pair() if scan_timer is not None else (None, None)
+    rc = lib().csa2_index_full_timed(
         _ptr(cache.ik_codes, torch.uint8, "ik_codes"), _ptr(cache.ik_sigma, torch.float32, "ik_sigma"),
         cache.cap, B, Q, _ptr(iq, torch.float32, "iq", B * Q * 256),
         _ptr(iw, torch.float32, "iw", B * Q * 4), _ptr(n_vis, torch.int32, "n_vis", B * Q),
         topk, pool_blocks, _ptr(topk_idx, torch.int32, "topk_idx", B * Q * topk),
         _ptr(pool_idx, torch.int32, "pool_idx", B * Q * pool_blocks) if pool_blocks else None,
-        _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream))
+        _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream), ev[0], ev[1])
     _check(rc, "csa2_index_full")
 
 
@@ -279,16 +284,80 @@ def sparse_attn_chunk(q, cache, topk_idx, swa_k, swa_v, swa_ks, swa_vs, out, lse
 
 
 def codec_probe(x, stream=None):
-    """Run the device codecs: returns (e4m3 decode [256], e2m1 decode [16],
-    e4m3 encode of x, e2m1 encode of x), all on the GPU."""
+    """Run the device codecs: returns (E4M3 decode [256] via the scan's fp32
+    converter, E4M3 decode [256] via the attention's fp16 converter, FP4 code x
+    scale products [256][16], E4M3 encode of x, E2M1 encode of x)."""
     dev = x.device
     e4 = torch.empty(256, dtype=torch.float32, device=dev)
-    e2 = torch.empty(16, dtype=torch.float32, device=dev)
+    e4h = torch.empty(256, dtype=torch.float32, device=dev)
+    fp4 = torch.empty((256, 16), dtype=torch.float32, device=dev)
     enc4 = torch.empty(x.numel(), dtype=torch.uint8, device=dev)
     enc2 = torch.empty(x.numel(), dtype=torch.uint8, device=dev)
-    rc = lib().csa2_codec_probe(_ptr(e4, torch.float32, "e4m3_dec"), _ptr(e2, torch.float32, "e2m1_dec"),
+    rc = lib().csa2_codec_probe(_ptr(e4, torch.float32, "e4m3_dec"),
+                                _ptr(e4h, torch.float32, "e4m3_dec16"),
+                                _ptr(fp4, torch.float32, "fp4_dec16"),
                                 _ptr(x, torch.float32, "x"), x.numel(),
                                 _ptr(enc4, torch.uint8, "e4m3_enc"), _ptr(enc2, torch.uint8, "e2m1_enc"),
                                 _stream(stream))
     _check(rc, "csa2_codec_probe")
-    return e4, e2, enc4, enc2
+    return e4, e4h, fp4, enc4, enc2
+
+
+# ---------------------------------------------------------------------------
+# HIP events for kernel timing (plumbing for the bench)
+# ---------------------------------------------------------------------------
+_hip = None
+
+
+def _hiprt():
+    """The HIP runtime torch has loaded (same soname as the one libcsa2 uses)."""
+    global _hip
+    if _hip is None:
+        h = ctypes.CDLL("libamdhip64.so.7", mode=ctypes.RTLD_GLOBAL)
+        h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                          ctypes.c_void_p]
+        _hip = h
+    return _hip
+
+
+class KernelTimer:
+    """A ring of (start, stop) HIP event pairs; elapsed_ms() averages them."""
+
+    def __init__(self, n):
+        h = _hiprt()
+        self.events = []
+        for _ in range(2 * n):
+            e = ctypes.c_void_p()
+            if h.hipEventCreate(ctypes.byref(e)) != 0:
+                raise Csa2Error("hipEventCreate failed")
+            self.events.append(e)
+        self.n, self.used = n, 0
+
+    def next_pair(self):
+        i = self.used % self.n
+        self.used += 1
+        return self.events[2 * i], self.events[2 * i + 1]
+
+    def durations_ms(self):
+        h = _hiprt()
+        out = []
+        for i in range(min(self.used, self.n)):
+            a, b = self.events[2 * i], self.events[2 * i + 1]
+            h.hipEventSynchronize(b)
+            ms = ctypes.c_float()
+            if h.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+                raise Csa2Error("hipEventElapsedTime failed")
+            out.append(ms.value)
+        return out
+
+    def reset(self):
+        self.used = 0
+
+    def close(self):
+        h = _hiprt()
+        for e in self.events:
+            h.hipEventDestroy(e)
+        self.events = []

@@ -9,7 +9,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "../../include/csa2.h"
+#include "csa2.h"
 #include "csa2_internal.hpp"
 
 using namespace csa2;
@@ -21,11 +21,11 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct IndexLayout {
-    size_t qd, wq, keys, bkeys, ipool, total;
+    size_t qd, wq, keys, bkeys, total;
 };
 
 // workspace of csa2_index_full: decoded query, folded weights, per-position
-// keys, per-block keys, internal pool (pool_blocks == 0)
+// keys, per-block keys
 IndexLayout full_layout(int B, int Q, int64_t cap, int topk, int pool_blocks) {
     IndexLayout L{};
     const size_t nq = (size_t)B * Q;
@@ -34,19 +34,15 @@ IndexLayout full_layout(int B, int Q, int64_t cap, int topk, int pool_blocks) {
     L.wq = off; off += align_up(nq * 4 * sizeof(float));
     L.keys = off; off += align_up(nq * (size_t)cap * sizeof(uint32_t));
     L.bkeys = off; off += align_up(nq * (size_t)(cap / 8) * sizeof(uint32_t));
-    L.ipool = off;
-    if (pool_blocks == 0) off += align_up(nq * (size_t)topk * sizeof(int32_t));
     L.total = off;
     return L;
 }
 
-// workspace of csa2_index_reindex: decoded query, folded weights, pool keys
+// workspace of csa2_index_reindex: pool keys
 IndexLayout reindex_layout(int B, int Q, int pool_blocks) {
     IndexLayout L{};
     const size_t nq = (size_t)B * Q;
     size_t off = 0;
-    L.qd = off; off += align_up(nq * 256 * sizeof(float));
-    L.wq = off; off += align_up(nq * 4 * sizeof(float));
     L.keys = off; off += align_up(nq * (size_t)pool_blocks * 8 * sizeof(uint32_t));
     L.total = off;
     return L;
@@ -176,10 +172,11 @@ __attribute__((visibility("default"))) int csa2_quant_fp8(const float* x, int64_
     return hip_status(launch_quant_fp8(x, n_rows, dim, layout, dst_rows, codes, sigma, stream));
 }
 
-__attribute__((visibility("default"))) int csa2_index_full(
+__attribute__((visibility("default"))) int csa2_index_full_timed(
     const uint8_t* ik_codes, const float* ik_sigma, int64_t cap, int B, int Q, const float* iq,
     const float* iw, const int32_t* n_vis, int topk, int pool_blocks, int32_t* topk_idx,
-    int32_t* pool_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int32_t* pool_idx, void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t scan_start,
+    hipEvent_t scan_stop) {
     int rc = validate_index_full(ik_codes, ik_sigma, cap, B, Q, iq, iw, n_vis, topk, pool_blocks,
                                  topk_idx, pool_idx);
     if (rc) return rc;
@@ -193,17 +190,26 @@ __attribute__((visibility("default"))) int csa2_index_full(
     const int64_t nq = (int64_t)B * Q;
     // The Full layer's own top-K over every visible position equals the top-K
     // inside its best P >= K blocks (ties to the lower index on both levels),
-    // so the position select only ever looks at P*8 candidates.
-    int32_t* pool = pool_blocks > 0 ? pool_idx : reinterpret_cast<int32_t*>(w + L.ipool);
+    // so the position select only ever looks at P*8 candidates.  Without a
+    // requested pool, P = K blocks are kept internally.
     const int P = pool_blocks > 0 ? pool_blocks : topk;
 
     hipError_t e = launch_prep_iq(iq, iw, nq, qd, wq, stream);
-    if (e == hipSuccess) e = launch_scan(ik_codes, ik_sigma, cap, B, Q, qd, wq, n_vis, keys, bkeys, stream);
     if (e == hipSuccess)
-        e = launch_select(kModeBlocks, bkeys, cap / 8, nullptr, 0, n_vis, cap, nq, P, pool, P, stream);
+        e = launch_scan(ik_codes, ik_sigma, cap, B, Q, qd, wq, n_vis, keys, bkeys, stream,
+                        scan_start, scan_stop);
     if (e == hipSuccess)
-        e = launch_select(kModeGather, keys, cap, pool, P, n_vis, cap, nq, topk, topk_idx, topk, stream);
+        e = launch_select_full(keys, bkeys, cap, n_vis, nq, P, topk,
+                               pool_blocks > 0 ? pool_idx : nullptr, topk_idx, stream);
     return hip_status(e);
+}
+
+__attribute__((visibility("default"))) int csa2_index_full(
+    const uint8_t* ik_codes, const float* ik_sigma, int64_t cap, int B, int Q, const float* iq,
+    const float* iw, const int32_t* n_vis, int topk, int pool_blocks, int32_t* topk_idx,
+    int32_t* pool_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return csa2_index_full_timed(ik_codes, ik_sigma, cap, B, Q, iq, iw, n_vis, topk, pool_blocks,
+                                 topk_idx, pool_idx, ws, ws_bytes, stream, nullptr, nullptr);
 }
 
 __attribute__((visibility("default"))) int csa2_index_reindex(
@@ -216,17 +222,13 @@ __attribute__((visibility("default"))) int csa2_index_reindex(
     const IndexLayout L = reindex_layout(B, Q, pool_blocks);
     if (!ws || ws_bytes < L.total) return CSA2_E_WORKSPACE;
     char* w = static_cast<char*>(ws);
-    float* qd = reinterpret_cast<float*>(w + L.qd);
-    float* wq = reinterpret_cast<float*>(w + L.wq);
     uint32_t* ckeys = reinterpret_cast<uint32_t*>(w + L.keys);
     const int64_t nq = (int64_t)B * Q;
-    hipError_t e = launch_prep_iq(iq, iw, nq, qd, wq, stream);
+    hipError_t e = launch_pool_score(ik_codes, ik_sigma, cap, B, Q, iq, iw, n_vis, pool_idx,
+                                     pool_blocks, ckeys, stream);
     if (e == hipSuccess)
-        e = launch_pool_score(ik_codes, ik_sigma, cap, B, Q, qd, wq, n_vis, pool_idx, pool_blocks,
-                              ckeys, stream);
-    if (e == hipSuccess)
-        e = launch_select(kModeCompact, ckeys, (int64_t)pool_blocks * 8, pool_idx, pool_blocks,
-                          n_vis, cap, nq, topk, topk_idx, topk, stream);
+        e = launch_select_pool(ckeys, pool_idx, pool_blocks, n_vis, cap, nq, topk, topk_idx,
+                               stream);
     return hip_status(e);
 }
 
@@ -254,6 +256,7 @@ __attribute__((visibility("default"))) int csa2_sparse_attn_chunk(
     int rc = validate_attn(q, B, Q, H, kv_codes, kv_scales, cap, topk_idx, topk, swa_k, swa_v,
                            swa_ks, swa_vs, sm_scale, out, lse);
     if (rc) return rc;
+    if (Q > CSA2_WINDOW) return CSA2_E_UNSUPPORTED;  // a chunk replays at most one window
     const int64_t nq = (int64_t)B * Q;
     const size_t need = attn_workspace_bytes(nq, H, topk, Q);
     if (need > 0 && (!ws || ws_bytes < need)) return CSA2_E_WORKSPACE;
@@ -262,13 +265,14 @@ __attribute__((visibility("default"))) int csa2_sparse_attn_chunk(
     return hip_status(launch_attn(a, ws, ws_bytes, stream));
 }
 
-__attribute__((visibility("default"))) int csa2_codec_probe(float* e4m3_dec, float* e2m1_dec,
-                                                           const float* x, int64_t n,
-                                                           uint8_t* e4m3_enc, uint8_t* e2m1_enc,
-                                                           hipStream_t stream) {
-    if (!e4m3_dec || !e2m1_dec || n < 0) return CSA2_E_ARG;
+__attribute__((visibility("default"))) int csa2_codec_probe(float* e4m3_dec, float* e4m3_dec16,
+                                                           float* fp4_dec16, const float* x,
+                                                           int64_t n, uint8_t* e4m3_enc,
+                                                           uint8_t* e2m1_enc, hipStream_t stream) {
+    if (!e4m3_dec || !e4m3_dec16 || !fp4_dec16 || n < 0) return CSA2_E_ARG;
     if (n > 0 && (!x || !e4m3_enc || !e2m1_enc)) return CSA2_E_ARG;
-    return hip_status(launch_codec_probe(e4m3_dec, e2m1_dec, x, n, e4m3_enc, e2m1_enc, stream));
+    return hip_status(launch_codec_probe(e4m3_dec, e4m3_dec16, fp4_dec16, x, n, e4m3_enc,
+                                         e2m1_enc, stream));
 }
 
 }  // extern "C"

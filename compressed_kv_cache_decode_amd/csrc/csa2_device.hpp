@@ -138,6 +138,42 @@ __device__ __forceinline__ float group8_max_f32(float v) {
     return v;
 }
 
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// fp16 value of an E4M3 byte (exact), through the hardware converter
+__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t byte) {
+    const half2_t h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(byte, 1.0f, false);
+    return h[0];
+}
+
+// Eight E2M1 codes (one dword) -> eight fp16 values times an fp16 scale.
+// The converter runs with scale 1 (exact); the E4M3 scale is applied by an
+// fp16 multiply, exact because the product has at most 6 significant bits and
+// lies in [2^-10, 2688].
+__device__ __forceinline__ void fp4x8_to_f16(uint32_t w, _Float16 sc, _Float16* out) {
+    const half2_t s2 = {sc, sc};
+    const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+    const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+    const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+    const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+    out[0] = h0[0]; out[1] = h0[1]; out[2] = h1[0]; out[3] = h1[1];
+    out[4] = h2[0]; out[5] = h2[1]; out[6] = h3[0]; out[7] = h3[1];
+}
+
+// Eight E4M3 codes (two dwords) -> eight fp16 values (exact).
+__device__ __forceinline__ void fp8x8_to_f16(uint32_t w0, uint32_t w1, _Float16* out) {
+    const uint32_t w[2] = {w0, w1};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const half2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false);
+        const half2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true);
+        out[4 * i + 0] = lo[0];
+        out[4 * i + 1] = lo[1];
+        out[4 * i + 2] = hi[0];
+        out[4 * i + 3] = hi[1];
+    }
+}
+
 __device__ __forceinline__ int clamp_nvis(int32_t n, int64_t cap) {
     return n < 0 ? 0 : (n > cap ? (int)cap : n);
 }

@@ -21,6 +21,8 @@
 // Memory layout of the indexer K (per 64 positions: four 1 KB planes, plane g
 // holding channels 16g..16g+15 of the 64 positions, 16 bytes each) makes every
 // wave-wide load a contiguous 1 KB: lane i reads its position's 16 bytes.
+#include <hip/hip_ext.h>
+
 #include "csa2_device.hpp"
 #include "csa2_internal.hpp"
 
@@ -107,62 +109,93 @@ __global__ __launch_bounds__(256) void k_scan(const uint8_t* __restrict__ ikc,
 
 // ---------------------------------------------------------------------------
 // Reindex: score the positions of the pool blocks with the layer's own query.
-// grid = (ceil(P*8 / 256), B*Q).  Slot s of query bq is position
+// grid = (ceil(P*8 / 256), B*Q), 256 threads.  Slot s of query bq is position
 // pool[j]*8 + (s & 7) with j = s / 8; invisible or empty slots get key 0.
 // The eight lanes of one block read 8 x 16 contiguous bytes per plane.
+// Each workgroup quantises its query itself (wave h: head h, E4M3 codes
+// decoded back to fp32 in LDS, w' = w * sq), while its row loads are in
+// flight; the score then reads q from LDS (broadcast reads).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_pool_score(const uint8_t* __restrict__ ikc,
                                                     const float* __restrict__ iks, int64_t cap,
-                                                    int Q, const float* __restrict__ qd,
-                                                    const float* __restrict__ wq,
+                                                    int Q, const float* __restrict__ iq,
+                                                    const float* __restrict__ iw,
                                                     const int32_t* __restrict__ n_vis,
                                                     const int32_t* __restrict__ pool, int P,
                                                     uint32_t* __restrict__ ckeys) {
+    __shared__ __attribute__((aligned(16))) float sq[kIdxHeads * kIdxDim];
+    __shared__ float sw[kIdxHeads];
     const int64_t bq = blockIdx.y;
     const int64_t b = bq / Q;
     const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t n_slots = (int64_t)P * kBlock;
-    if (s >= n_slots) return;
     const int nv = clamp_nvis(n_vis[bq], cap);
-    const int32_t blk = pool[bq * P + (s >> 3)];
+    const int32_t blk = s < n_slots ? pool[bq * P + (s >> 3)] : -1;
     const int64_t pos = (int64_t)blk * kBlock + (s & 7);
-    uint32_t key = 0;
-    if (blk >= 0 && pos < nv) {
+    const bool valid = blk >= 0 && pos < nv;
+    uint4 raw[4];
+    float sigma = 0.0f;
+    if (valid) {
         const int64_t row = b * cap + pos;
-        uint4 raw[4];
         load_ik_row(ikc, row, raw);
-        key = score_key(score_row(raw, iks[row], qd + bq * kIdxHeads * kIdxDim, wq + bq * kIdxHeads));
+        sigma = iks[row];
     }
+    {   // the query's E4M3 codes (exact fp32 values) and folded weights
+        const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
+        const float x = iq[(bq * kIdxHeads + h) * kIdxDim + lane];
+        const float sqh = wave_max_f32(fabsf(x)) / 448.0f;
+        const uint32_t c = (sqh == 0.0f) ? ((__float_as_uint(x) >> 24) & 0x80u) : e4m3_encode(x / sqh);
+        sq[h * kIdxDim + lane] = e4m3_decode_bits(c);
+        if (lane == 0) sw[h] = iw[bq * kIdxHeads + h] * sqh;
+    }
+    __syncthreads();
+    if (s >= n_slots) return;
+    uint32_t key = 0;
+    if (valid) key = score_key(score_row(raw, sigma, sq, sw));
     ckeys[bq * n_slots + s] = key;
 }
 
 // ---------------------------------------------------------------------------
-// Exact top-K select, one workgroup of 1024 threads per query.
+// Exact top-K selection, one workgroup of 1024 threads per query.
 //
 // Slots are numbered in ascending index order; key 0 marks an empty slot.
-// The K-th largest key T is found by a 4-pass MSB-first radix select (8-bit
-// digits, LDS histogram).  The output is every slot with key > T plus the
-// lowest-numbered slots with key == T until K are taken, written in
-// ascending slot order (so ties go to the lowest position / block).
-// Fewer than K non-empty slots: all are output.  The rest is -1.
+// The K-th largest key T is found by range refinement: a min/max pass, then
+// up to three histogram passes, each splitting the current key interval
+// [lo, hi] into at most 2048 equal bins (bins follow the keys' actual range,
+// so a narrow score distribution does not pile every key into one LDS bin)
+// and keeping the bin that holds the K-th largest.  Output: every slot with
+// key > T, then the lowest-numbered slots with key == T until K are taken,
+// written in ascending slot order (ties go to the lowest position or block);
+// fewer than K non-empty slots: all of them; the rest of the row is -1.
 //
-//   MODE_BLOCKS  slots = blocks [0, ceil(n_vis/8)), key = block max key,
-//                index = block id.
-//   MODE_GATHER  slots = pool positions (P*8), key read from the full
-//                per-position key array, index = position.
-//   MODE_COMPACT slots = pool positions, key from a compact [P*8] array.
+// Up to 16384 slots are held in registers (16 per thread); larger counts are
+// streamed: wave w owns a contiguous range, lane l the slots range_begin +
+// 64 i + l, re-read from memory on every pass.
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSelLdsKeys = 16384;
+constexpr int kSelRegSlots = 16384;             // slots held in registers
+constexpr int kSelBins = 2048;
 
-template <int MODE>
-struct SlotSource {
+struct SelShared {
+    uint32_t hist[kSelBins + 3 * 16 + 16 + 2];  // also holds the register path's state
+    uint32_t keys[1];  // unused by the streaming path (keys are re-read)
+    int32_t pool[kMaxPoolBlocks];
+    uint32_t red[3][kSelWaves];
+    uint32_t wgt[kSelWaves], weq[kSelWaves];
+    uint32_t pick[2];
+};
+
+// key of slot s: block keys, position keys gathered through the pool, or a
+// compact pool-ordered array
+struct KeySrc {
     const uint32_t* src;
-    const int32_t* pool;  // LDS copy of the query's pool (MODE_GATHER / MODE_COMPACT)
+    const int32_t* pool;  // LDS, sanitised (-1 = empty)
+    int64_t n;
     int nv;
+    int kind;             // 0 direct, 1 gather through pool, 2 compact (pool order)
     __device__ __forceinline__ uint32_t key(int64_t s) const {
-        if (MODE == kModeGather) {
+        if (kind == 1) {
             const int32_t blk = pool[s >> 3];
             const int64_t pos = (int64_t)blk * kBlock + (s & 7);
             return (blk >= 0 && pos < nv) ? src[pos] : 0u;
@@ -170,151 +203,382 @@ struct SlotSource {
         return src[s];
     }
     __device__ __forceinline__ int32_t index(int64_t s) const {
-        if (MODE == kModeBlocks) return (int32_t)s;
-        return pool[s >> 3] * kBlock + (int32_t)(s & 7);
+        return kind == 0 ? (int32_t)s : pool[s >> 3] * kBlock + (int32_t)(s & 7);
     }
 };
 
-template <int MODE>
-__global__ __launch_bounds__(kSelThreads) void k_select(
-    const uint32_t* __restrict__ src, int64_t src_stride, const int32_t* __restrict__ pool, int P,
-    const int32_t* __restrict__ n_vis, int64_t cap, int K, int32_t* __restrict__ out,
-    int64_t out_stride) {
-    __shared__ uint32_t s_keys[kSelLdsKeys];
-    __shared__ int32_t s_pool[kMaxPoolBlocks];
-    __shared__ uint32_t s_hist[256];
-    __shared__ uint32_t s_wgt[kSelWaves], s_weq[kSelWaves];
-    __shared__ uint32_t s_state[3];
+struct SelRange {
+    int64_t beg, end;  // this wave's slots
+};
 
+__device__ __forceinline__ SelRange wave_range(int64_t n, int wave) {
+    const int64_t chunk = ((n + kSelWaves - 1) / kSelWaves + 63) / 64 * 64;
+    SelRange r;
+    r.beg = min(n, (int64_t)wave * chunk);
+    r.end = min(n, r.beg + chunk);
+    return r;
+}
+
+// Visit this thread's keys in ascending slot order, the same trip count in
+// every lane of a wave: f(key, slot, in_range).  CACHED: keys come from LDS.
+template <bool CACHED, class F>
+__device__ __forceinline__ void for_keys(const KeySrc& ks, const uint32_t* cache,
+                                         const SelRange& r, int lane, F f) {
+    for (int64_t base = r.beg; base < r.end; base += 64) {
+        const int64_t s = base + lane;
+        const bool in = s < r.end;
+        f(in ? (CACHED ? cache[s] : ks.key(s)) : 0u, s, in);
+    }
+}
+
+struct Threshold {
+    uint32_t t_ge;   // every key >= t_ge is taken
+    uint32_t t_eq;   // plus the first `quota` keys equal to t_eq
+    uint32_t quota;
+    uint32_t total;  // number taken
+};
+
+template <bool REG>
+__device__ __forceinline__ Threshold find_threshold(const KeySrc& ks, const uint32_t* reg,
+                                    const SelRange& r, int K, SelShared& sh) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t bq = blockIdx.x;
-    const int nv = clamp_nvis(n_vis[bq], cap);
-    int64_t n;
-    if (MODE == kModeBlocks) {
-        n = ((int64_t)nv + kBlock - 1) / kBlock;
-    } else {
-        n = (int64_t)P * kBlock;
-        const int64_t nbv = ((int64_t)nv + kBlock - 1) / kBlock;
-        for (int j = tid; j < P; j += kSelThreads) {
-            int32_t blk = pool[bq * P + j];
-            s_pool[j] = (blk >= 0 && blk < nbv) ? blk : -1;  // out-of-range ids are ignored
-        }
-        __syncthreads();
+    // count, min and max of the non-empty keys
+    uint32_t cnt = 0, kmin = 0xFFFFFFFFu, kmax = 0;
+    for_keys<REG>(ks, reg, r, lane, [&](uint32_t k, int64_t, bool) {
+        if (k) { ++cnt; kmin = min(kmin, k); kmax = max(kmax, k); }
+    });
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        cnt += __shfl_xor(cnt, off, 64);
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, 64));
     }
-    SlotSource<MODE> srcv{src + bq * src_stride, s_pool, nv};
-    const bool cached = n <= kSelLdsKeys;
-    if (cached) {
-        for (int64_t s = tid; s < n; s += kSelThreads) s_keys[s] = srcv.key(s);
-        __syncthreads();
+    if (lane == 0) { sh.red[0][wave] = cnt; sh.red[1][wave] = kmin; sh.red[2][wave] = kmax; }
+    __syncthreads();
+    cnt = 0; kmin = 0xFFFFFFFFu; kmax = 0;
+    for (int w = 0; w < kSelWaves; ++w) {
+        cnt += sh.red[0][w];
+        kmin = min(kmin, sh.red[1][w]);
+        kmax = max(kmax, sh.red[2][w]);
     }
-    auto key_at = [&](int64_t s) -> uint32_t { return cached ? s_keys[s] : srcv.key(s); };
+    if (cnt <= (uint32_t)K) return Threshold{1u, 0u, 0u, cnt};
 
-    // ---- radix select of the K-th largest key ----
-    uint32_t prefix = 0, mask = 0;
-    uint32_t remaining = (uint32_t)K;
-    uint32_t t_ge = 1, t_eq = 0, quota = 0;  // default: take every non-empty slot
-    bool resolved = false;
-    for (int pass = 0; pass < 4 && !resolved; ++pass) {
-        const int shift = 24 - 8 * pass;
-        if (tid < 256) s_hist[tid] = 0;
+    uint32_t lo = kmin, hi = kmax, remaining = (uint32_t)K;
+    for (int pass = 0; pass < 4; ++pass) {
+        const uint32_t width = hi - lo;
+        if (width == 0) return Threshold{lo + 1, lo, remaining, (uint32_t)K};
+        const int bits = 32 - __clz((int)width);
+        const int shift = bits > 11 ? bits - 11 : 0;
+        const int nbins = (int)(width >> shift) + 1;
+        __syncthreads();  // previous readers of hist are done
+        for (int i = tid; i < nbins; i += kSelThreads) sh.hist[i] = 0;
         __syncthreads();
-        for (int64_t s = tid; s < n; s += kSelThreads) {
-            const uint32_t k = key_at(s);
-            if (k != 0 && (k & mask) == prefix) atomicAdd(&s_hist[(k >> shift) & 255u], 1u);
-        }
+        for_keys<REG>(ks, reg, r, lane, [&](uint32_t k, int64_t, bool) {
+            if (k >= lo && k <= hi) atomicAdd(&sh.hist[(k - lo) >> shift], 1u);
+        });
         __syncthreads();
         if (wave == 0) {
-            // lane l holds digits 255-4l .. 252-4l (descending)
-            uint32_t h[4], loc = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { h[i] = s_hist[255 - 4 * lane - i]; loc += h[i]; }
-            uint32_t incl = loc;  // inclusive scan over lanes
+            // lane l scans bins nbins-1-32l .. nbins-32-32l (descending)
+            uint32_t loc = 0;
+            for (int j = 0; j < 32; ++j) {
+                const int bin = nbins - 1 - 32 * lane - j;
+                loc += bin >= 0 ? sh.hist[bin] : 0u;
+            }
+            uint32_t incl = loc;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const uint32_t y = __shfl_up(incl, off, 64);
                 if (lane >= off) incl += y;
             }
-            const uint32_t total = __shfl(incl, 63, 64);
             uint32_t above = incl - loc;
-            if (lane == 0) { s_state[0] = 0xFFFFFFFFu; s_state[2] = total; }
-            // exactly one (lane, i) satisfies above < remaining <= above + h
-            if (pass > 0 || total > remaining) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (above < remaining && above + h[i] >= remaining) {
-                        s_state[0] = (uint32_t)(255 - 4 * lane - i);
-                        s_state[1] = above;
+            if (above < remaining && incl >= remaining) {  // the bin is in this lane's run
+                for (int j = 0; j < 32; ++j) {
+                    const int bin = nbins - 1 - 32 * lane - j;
+                    const uint32_t h = sh.hist[bin];
+                    if (above + h >= remaining) {
+                        sh.pick[0] = (uint32_t)bin;
+                        sh.pick[1] = above;
+                        break;
                     }
-                    above += h[i];
+                    above += h;
                 }
             }
         }
         __syncthreads();
-        const uint32_t d = s_state[0];
-        if (pass == 0 && s_state[2] <= remaining) {  // K or fewer non-empty slots: take all
-            resolved = true;
-        } else {
-            const uint32_t above = s_state[1];
-            const uint32_t cnt = s_hist[d];
-            remaining -= above;
-            prefix |= d << shift;
-            mask |= 0xFFu << shift;
-            if (cnt == remaining) {  // the whole bin is taken: threshold is its lowest key
-                t_ge = prefix;
-                quota = 0;
-                resolved = true;
-            } else if (pass == 3) {  // T = prefix exactly; take `remaining` of the ties
-                t_ge = prefix + 1;
-                t_eq = prefix;
-                quota = remaining;
-                resolved = true;
-            }
-        }
-        __syncthreads();
+        const uint32_t d = sh.pick[0], above = sh.pick[1];
+        const uint32_t in_bin = sh.hist[d];
+        remaining -= above;
+        const uint32_t new_lo = lo + (d << shift);
+        const uint32_t span = (shift == 0) ? 0u : ((1u << shift) - 1u);
+        const uint32_t new_hi = (hi - new_lo > span) ? new_lo + span : hi;
+        if (in_bin == remaining) return Threshold{new_lo, 0u, 0u, (uint32_t)K};
+        lo = new_lo;
+        hi = new_hi;
     }
+    return Threshold{lo + 1, lo, remaining, (uint32_t)K};  // not reached: width hits 0
+}
 
-    // ---- compaction in ascending slot order (each wave owns a contiguous range) ----
-    const int64_t chunk = ((n + kSelWaves - 1) / kSelWaves + 63) / 64 * 64;
-    const int64_t beg = (int64_t)wave * chunk;
-    const int64_t end = min(n, beg + chunk);
+// Write the selected indices of this query in ascending slot order; the
+// rest of out[0, K) becomes -1.  When `lds_out` is set, also mirror them there.
+template <bool REG>
+__device__ __forceinline__ void compact(const KeySrc& ks, const uint32_t* reg, const SelRange& r,
+                        const Threshold& th, int K, int32_t* out, int32_t* lds_out,
+                        SelShared& sh) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint32_t c_gt = 0, c_eq = 0;
-    for (int64_t base = beg; base < end; base += 64) {
-        const int64_t s = base + lane;
-        const uint32_t k = s < end ? key_at(s) : 0u;
-        const bool gt = k != 0 && k >= t_ge;
-        const bool eq = k != 0 && quota != 0 && k == t_eq;
-        c_gt += __popcll(__ballot(gt));
-        c_eq += __popcll(__ballot(eq));
-    }
-    if (lane == 0) { s_wgt[wave] = c_gt; s_weq[wave] = c_eq; }
+    for_keys<REG>(ks, reg, r, lane, [&](uint32_t k, int64_t, bool) {
+        c_gt += __popcll(__ballot(k != 0 && k >= th.t_ge));
+        c_eq += __popcll(__ballot(k != 0 && th.quota != 0 && k == th.t_eq));
+    });
     __syncthreads();
-    // per-wave prefix of ties and of outputs (16 values, every thread)
-    uint32_t eq_before = 0, out_before = 0, total_sel = 0, eb = 0;
+    if (lane == 0) { sh.wgt[wave] = c_gt; sh.weq[wave] = c_eq; }
+    __syncthreads();
+    uint32_t eq_before = 0, out_before = 0, total = 0, eb = 0;
     for (int w = 0; w < kSelWaves; ++w) {
-        const uint32_t take_eq = quota > eb ? min(quota - eb, s_weq[w]) : 0u;
-        if (w == wave) { eq_before = eb; out_before = total_sel; }
-        total_sel += s_wgt[w] + take_eq;
-        eb += s_weq[w];
+        const uint32_t take_eq = th.quota > eb ? min(th.quota - eb, sh.weq[w]) : 0u;
+        if (w == wave) { eq_before = eb; out_before = total; }
+        total += sh.wgt[w] + take_eq;
+        eb += sh.weq[w];
     }
-    int32_t* o = out + bq * out_stride;
     uint32_t eq_seen = 0, taken = 0;
-    for (int64_t base = beg; base < end; base += 64) {
-        const int64_t s = base + lane;
-        const uint32_t k = s < end ? key_at(s) : 0u;
-        const bool gt = k != 0 && k >= t_ge;
-        const bool eq = k != 0 && quota != 0 && k == t_eq;
+    for_keys<REG>(ks, reg, r, lane, [&](uint32_t k, int64_t s, bool) {
+        const bool gt = k != 0 && k >= th.t_ge;
+        const bool eq = k != 0 && th.quota != 0 && k == th.t_eq;
         const uint64_t eq_mask = __ballot(eq);
         const uint32_t eq_rank = eq_before + eq_seen +
-            __builtin_amdgcn_mbcnt_hi((uint32_t)(eq_mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eq_mask, 0));
-        const bool take = gt || (eq && eq_rank < quota);
+            __builtin_amdgcn_mbcnt_hi((uint32_t)(eq_mask >> 32),
+                                      __builtin_amdgcn_mbcnt_lo((uint32_t)eq_mask, 0));
+        const bool take = gt || (eq && eq_rank < th.quota);
         const uint64_t tk_mask = __ballot(take);
         const uint32_t rank = out_before + taken +
-            __builtin_amdgcn_mbcnt_hi((uint32_t)(tk_mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)tk_mask, 0));
-        if (take && rank < (uint32_t)K) o[rank] = srcv.index(s);
+            __builtin_amdgcn_mbcnt_hi((uint32_t)(tk_mask >> 32),
+                                      __builtin_amdgcn_mbcnt_lo((uint32_t)tk_mask, 0));
+        if (take && rank < (uint32_t)K) {
+            const int32_t idx = ks.index(s);
+            if (out) out[rank] = idx;
+            if (lds_out) lds_out[rank] = idx;
+        }
+        eq_seen += __popcll(eq_mask);
+        taken += __popcll(tk_mask);
+    });
+    for (int64_t i = (int64_t)total + tid; i < K; i += kSelThreads) {
+        if (out) out[i] = -1;
+        if (lds_out) lds_out[i] = -1;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Register path (at most 16384 slots): lane l of wave w holds the keys of
+// slots w*1024 + 64 i + l, i < 16, so every sweep is 16 unrolled register
+// operations, wave-wide sums are DPP scans, and the bin search is spread
+// over all 1024 threads.
+// ---------------------------------------------------------------------------
+constexpr int kSelKpt = 16;
+
+// inclusive prefix sum over the 64 lanes (DPP row shifts, then row broadcasts)
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false); // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false); // row_bcast:31
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(v), 63);
+}
+
+template <class OP>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, OP op) {
+    v = op(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = op(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = op(v, dpp<0x141>(v));  // row_half_mirror
+    v = op(v, dpp<0x140>(v));  // row_mirror
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return op(op(r0, r1), op(r2, r3));
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+struct SelRegShared {
+    uint32_t hist[kSelBins];
+    uint32_t part[3][kSelWaves];
+    uint32_t pick[2];
+};
+
+__device__ __forceinline__ Threshold threshold_reg(const uint32_t (&k)[kSelKpt], int K,
+                                                   SelRegShared& sh) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t cnt = 0, kmin = 0xFFFFFFFFu, kmax = 0;
+#pragma unroll
+    for (int i = 0; i < kSelKpt; ++i) {
+        cnt += k[i] != 0;
+        kmin = k[i] ? min(kmin, k[i]) : kmin;
+        kmax = max(kmax, k[i]);
+    }
+    cnt = wave_sum(cnt);
+    kmin = wave_reduce(kmin, [](uint32_t x, uint32_t y) { return min(x, y); });
+    kmax = wave_reduce(kmax, [](uint32_t x, uint32_t y) { return max(x, y); });
+    if (lane == 0) { sh.part[0][wave] = cnt; sh.part[1][wave] = kmin; sh.part[2][wave] = kmax; }
+    __syncthreads();
+    cnt = 0; kmin = 0xFFFFFFFFu; kmax = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+        cnt += sh.part[0][w];
+        kmin = min(kmin, sh.part[1][w]);
+        kmax = max(kmax, sh.part[2][w]);
+    }
+    if (cnt <= (uint32_t)K) return Threshold{1u, 0u, 0u, cnt};
+
+    uint32_t lo = kmin, hi = kmax, remaining = (uint32_t)K;
+    for (int pass = 0; pass < 4; ++pass) {
+        const uint32_t width = hi - lo;
+        if (width == 0) return Threshold{lo + 1, lo, remaining, (uint32_t)K};
+        const int bits = 32 - __clz((int)width);
+        const int shift = bits > 11 ? bits - 11 : 0;
+        const int nbins = (int)(width >> shift) + 1;
+        __syncthreads();  // earlier readers of hist / part are done
+        sh.hist[2 * tid] = 0;
+        sh.hist[2 * tid + 1] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kSelKpt; ++i)
+            if (k[i] >= lo && k[i] <= hi) atomicAdd(&sh.hist[(k[i] - lo) >> shift], 1u);
+        __syncthreads();
+        // thread t owns bins nbins-1-2t and nbins-2-2t (descending order)
+        const int b0 = nbins - 1 - 2 * tid, b1 = b0 - 1;
+        const uint32_t h0 = b0 >= 0 ? sh.hist[b0] : 0u, h1 = b1 >= 0 ? sh.hist[b1] : 0u;
+        const uint32_t mine = h0 + h1;
+        const uint32_t incl = wave_incl_scan(mine);
+        if (lane == 63) sh.part[0][wave] = incl;
+        __syncthreads();
+        uint32_t above = incl - mine;
+        for (int w = 0; w < wave; ++w) above += sh.part[0][w];
+        if (above < remaining && above + mine >= remaining) {
+            if (above + h0 >= remaining) { sh.pick[0] = (uint32_t)b0; sh.pick[1] = above; }
+            else { sh.pick[0] = (uint32_t)b1; sh.pick[1] = above + h0; }
+        }
+        __syncthreads();
+        const uint32_t d = sh.pick[0];
+        const uint32_t in_bin = sh.hist[d];
+        remaining -= sh.pick[1];
+        const uint32_t new_lo = lo + (d << shift);
+        const uint32_t span = (shift == 0) ? 0u : ((1u << shift) - 1u);
+        const uint32_t new_hi = (hi - new_lo > span) ? new_lo + span : hi;
+        if (in_bin == remaining) return Threshold{new_lo, 0u, 0u, (uint32_t)K};
+        lo = new_lo;
+        hi = new_hi;
+    }
+    return Threshold{lo + 1, lo, remaining, (uint32_t)K};  // not reached: width hits 0
+}
+
+template <class IDX>
+__device__ __forceinline__ void compact_reg(const uint32_t (&k)[kSelKpt], const Threshold& th,
+                                            int K, IDX index_of, int32_t* out, int32_t* lds_out,
+                                            SelRegShared& sh) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t c_gt = 0, c_eq = 0;
+#pragma unroll
+    for (int i = 0; i < kSelKpt; ++i) {
+        c_gt += __popcll(__ballot(k[i] != 0 && k[i] >= th.t_ge));
+        c_eq += __popcll(__ballot(k[i] != 0 && th.quota != 0 && k[i] == th.t_eq));
+    }
+    __syncthreads();
+    if (lane == 0) { sh.part[0][wave] = c_gt; sh.part[1][wave] = c_eq; }
+    __syncthreads();
+    uint32_t eq_before = 0, out_before = 0, total = 0, eb = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+        const uint32_t take_eq = th.quota > eb ? min(th.quota - eb, sh.part[1][w]) : 0u;
+        if (w == wave) { eq_before = eb; out_before = total; }
+        total += sh.part[0][w] + take_eq;
+        eb += sh.part[1][w];
+    }
+    uint32_t eq_seen = 0, taken = 0;
+#pragma unroll
+    for (int i = 0; i < kSelKpt; ++i) {
+        const bool gt = k[i] != 0 && k[i] >= th.t_ge;
+        const bool eq = k[i] != 0 && th.quota != 0 && k[i] == th.t_eq;
+        const uint64_t eq_mask = __ballot(eq);
+        const uint32_t eq_rank = eq_before + eq_seen + lanes_below(eq_mask);
+        const bool take = gt || (eq && eq_rank < th.quota);
+        const uint64_t tk_mask = __ballot(take);
+        const uint32_t rank = out_before + taken + lanes_below(tk_mask);
+        if (take && rank < (uint32_t)K) {
+            const int32_t v = index_of(wave * 1024 + 64 * i + lane);
+            if (out) out[rank] = v;
+            if (lds_out) lds_out[rank] = v;
+        }
         eq_seen += __popcll(eq_mask);
         taken += __popcll(tk_mask);
     }
-    for (int64_t i = (int64_t)total_sel + tid; i < K; i += kSelThreads) o[i] = -1;
+    for (int i = (int)total + tid; i < K; i += kSelThreads) {
+        if (out) out[i] = -1;
+        if (lds_out) lds_out[i] = -1;
+    }
+}
+
+// Select through the register path when the slot count allows it, else the
+// streaming path.  `ks` gives keys and indices of slots.
+__device__ __forceinline__ void select_into(const KeySrc& ks, int K, int32_t* out, int32_t* lds_out,
+                                            SelShared& sh) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (ks.n <= kSelRegSlots) {
+        uint32_t k[kSelKpt];
+#pragma unroll
+        for (int i = 0; i < kSelKpt; ++i) {
+            const int64_t s = (int64_t)wave * 1024 + 64 * i + lane;
+            k[i] = s < ks.n ? ks.key(s) : 0u;
+        }
+        SelRegShared& rs = *reinterpret_cast<SelRegShared*>(&sh.hist[0]);
+        const Threshold th = threshold_reg(k, K, rs);
+        compact_reg(k, th, K, [&](int64_t s) { return ks.index(s); }, out, lds_out, rs);
+    } else {
+        const SelRange r = wave_range(ks.n, wave);
+        const Threshold th = find_threshold<false>(ks, sh.keys, r, K, sh);
+        compact<false>(ks, sh.keys, r, th, K, out, lds_out, sh);
+    }
+}
+
+// Full layer: best P blocks (pool), then the best K positions inside it.
+// pool_out may be null (internal pool).
+__global__ __launch_bounds__(kSelThreads) void k_select_full(
+    const uint32_t* __restrict__ keys, const uint32_t* __restrict__ bkeys, int64_t cap,
+    const int32_t* __restrict__ n_vis, int P, int K, int32_t* __restrict__ pool_out,
+    int32_t* __restrict__ topk_out) {
+    __shared__ SelShared sh;
+    const int64_t bq = blockIdx.x;
+    const int nv = clamp_nvis(n_vis[bq], cap);
+    KeySrc blocks{bkeys + bq * (cap / kBlock), nullptr, ((int64_t)nv + kBlock - 1) / kBlock, nv, 0};
+    select_into(blocks, P, pool_out ? pool_out + bq * P : nullptr, sh.pool, sh);
+    __syncthreads();
+    KeySrc pos{keys + bq * cap, sh.pool, (int64_t)P * kBlock, nv, 1};
+    select_into(pos, K, topk_out + bq * K, nullptr, sh);
+}
+
+// Reindex: best K positions of the compact pool-ordered keys.
+__global__ __launch_bounds__(kSelThreads) void k_select_pool(
+    const uint32_t* __restrict__ ckeys, const int32_t* __restrict__ pool, int P,
+    const int32_t* __restrict__ n_vis, int64_t cap, int K, int32_t* __restrict__ topk_out) {
+    __shared__ SelShared sh;
+    const int64_t bq = blockIdx.x;
+    const int nv = clamp_nvis(n_vis[bq], cap);
+    const int64_t nbv = ((int64_t)nv + kBlock - 1) / kBlock;
+    for (int j = threadIdx.x; j < P; j += kSelThreads) {
+        const int32_t blk = pool[bq * P + j];
+        sh.pool[j] = (blk >= 0 && blk < nbv) ? blk : -1;
+    }
+    __syncthreads();
+    KeySrc ks{ckeys + bq * (int64_t)P * kBlock, sh.pool, (int64_t)P * kBlock, nv, 2};
+    select_into(ks, K, topk_out + bq * K, nullptr, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -322,41 +586,42 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
 // ---------------------------------------------------------------------------
 hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                        const float* qd, const float* wq, const int32_t* n_vis, uint32_t* keys,
-                       uint32_t* bkeys, hipStream_t stream) {
+                       uint32_t* bkeys, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     dim3 grid((unsigned)((cap + 255) / 256), (unsigned)B);
-    hipLaunchKernelGGL(k_scan, grid, dim3(256), 0, stream, ikc, iks, cap, Q, qd, wq, n_vis, keys,
-                       bkeys);
+    if (start != nullptr && stop != nullptr) {
+        // the runtime records `start` / `stop` immediately around this dispatch
+        hipExtLaunchKernelGGL(k_scan, grid, dim3(256), 0, stream, start, stop, 0, ikc, iks, cap, Q,
+                              qd, wq, n_vis, keys, bkeys);
+    } else {
+        hipLaunchKernelGGL(k_scan, grid, dim3(256), 0, stream, ikc, iks, cap, Q, qd, wq, n_vis,
+                           keys, bkeys);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_pool_score(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
-                             const float* qd, const float* wq, const int32_t* n_vis,
+                             const float* iq, const float* iw, const int32_t* n_vis,
                              const int32_t* pool, int P, uint32_t* ckeys, hipStream_t stream) {
     const int64_t n_slots = (int64_t)P * kBlock;
     dim3 grid((unsigned)((n_slots + 255) / 256), (unsigned)(B * Q));
-    hipLaunchKernelGGL(k_pool_score, grid, dim3(256), 0, stream, ikc, iks, cap, Q, qd, wq, n_vis,
+    hipLaunchKernelGGL(k_pool_score, grid, dim3(256), 0, stream, ikc, iks, cap, Q, iq, iw, n_vis,
                        pool, P, ckeys);
     return hipGetLastError();
 }
 
-hipError_t launch_select(int mode, const uint32_t* src, int64_t src_stride, const int32_t* pool,
-                         int P, const int32_t* n_vis, int64_t cap, int64_t n_queries, int K,
-                         int32_t* out, int64_t out_stride, hipStream_t stream) {
-    dim3 grid((unsigned)n_queries);
-    switch (mode) {
-        case kModeBlocks:
-            hipLaunchKernelGGL(k_select<kModeBlocks>, grid, dim3(kSelThreads), 0, stream, src,
-                               src_stride, pool, P, n_vis, cap, K, out, out_stride);
-            break;
-        case kModeGather:
-            hipLaunchKernelGGL(k_select<kModeGather>, grid, dim3(kSelThreads), 0, stream, src,
-                               src_stride, pool, P, n_vis, cap, K, out, out_stride);
-            break;
-        default:
-            hipLaunchKernelGGL(k_select<kModeCompact>, grid, dim3(kSelThreads), 0, stream, src,
-                               src_stride, pool, P, n_vis, cap, K, out, out_stride);
-            break;
-    }
+hipError_t launch_select_full(const uint32_t* keys, const uint32_t* bkeys, int64_t cap,
+                              const int32_t* n_vis, int64_t n_queries, int P, int K,
+                              int32_t* pool_out, int32_t* topk_out, hipStream_t stream) {
+    hipLaunchKernelGGL(k_select_full, dim3((unsigned)n_queries), dim3(kSelThreads), 0, stream, keys,
+                       bkeys, cap, n_vis, P, K, pool_out, topk_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_select_pool(const uint32_t* ckeys, const int32_t* pool, int P,
+                              const int32_t* n_vis, int64_t cap, int64_t n_queries, int K,
+                              int32_t* topk_out, hipStream_t stream) {
+    hipLaunchKernelGGL(k_select_pool, dim3((unsigned)n_queries), dim3(kSelThreads), 0, stream,
+                       ckeys, pool, P, n_vis, cap, K, topk_out);
     return hipGetLastError();
 }
 

@@ -7,9 +7,6 @@ namespace csa2 {
 
 constexpr int kMaxPoolBlocks = 4096;
 constexpr int kMaxTopk = 2048;
-constexpr int kModeBlocks = 0;
-constexpr int kModeGather = 1;
-constexpr int kModeCompact = 2;
 
 hipError_t launch_quant_fp4(const float* k, const float* v, int64_t n_ent, int ratio,
                             const float* rope_cs, const int64_t* dst_rows, uint8_t* codes,
@@ -19,18 +16,23 @@ hipError_t launch_quant_fp8(const float* x, int64_t n_rows, int dim, int layout,
                             hipStream_t stream);
 hipError_t launch_prep_iq(const float* iq, const float* iw, int64_t n_q, float* qd, float* wq,
                           hipStream_t stream);
-hipError_t launch_codec_probe(float* e4m3_dec, float* e2m1_dec, const float* x, int64_t n,
-                              uint8_t* e4m3_enc, uint8_t* e2m1_enc, hipStream_t stream);
+hipError_t launch_codec_probe(float* e4m3_dec, float* e4m3_dec16, float* fp4_dec16,
+                              const float* x, int64_t n, uint8_t* e4m3_enc, uint8_t* e2m1_enc,
+                              hipStream_t stream);
 
 hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                        const float* qd, const float* wq, const int32_t* n_vis, uint32_t* keys,
-                       uint32_t* bkeys, hipStream_t stream);
+                       uint32_t* bkeys, hipStream_t stream, hipEvent_t start = nullptr,
+                       hipEvent_t stop = nullptr);
 hipError_t launch_pool_score(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
-                             const float* qd, const float* wq, const int32_t* n_vis,
+                             const float* iq, const float* iw, const int32_t* n_vis,
                              const int32_t* pool, int P, uint32_t* ckeys, hipStream_t stream);
-hipError_t launch_select(int mode, const uint32_t* src, int64_t src_stride, const int32_t* pool,
-                         int P, const int32_t* n_vis, int64_t cap, int64_t n_queries, int K,
-                         int32_t* out, int64_t out_stride, hipStream_t stream);
+hipError_t launch_select_full(const uint32_t* keys, const uint32_t* bkeys, int64_t cap,
+                              const int32_t* n_vis, int64_t n_queries, int P, int K,
+                              int32_t* pool_out, int32_t* topk_out, hipStream_t stream);
+hipError_t launch_select_pool(const uint32_t* ckeys, const int32_t* pool, int P,
+                              const int32_t* n_vis, int64_t cap, int64_t n_queries, int K,
+                              int32_t* topk_out, hipStream_t stream);
 
 struct AttnArgs {
     const float* q;          // [n_q][H][128]

@@ -106,29 +106,28 @@ __global__ __launch_bounds__(256) void k_quant_fp8(const float* __restrict__ x, 
 
 // Indexer query per (sequence, query): per head sq = fl(amax/448), codes
 // RNE_E4M3(fl(q/sq)) stored back as their exact fp32 values, and the head
-// weight with the scale folded in, w' = fl(w * sq).  One wave per query,
-// lane = channel.
-__global__ __launch_bounds__(64) void k_prep_iq(const float* __restrict__ iq,
-                                                const float* __restrict__ iw, int64_t n_q,
-                                                float* __restrict__ qd, float* __restrict__ wq) {
-    const int lane = threadIdx.x;
+// weight with the scale folded in, w' = fl(w * sq).  One workgroup per query,
+// one wave per head, lane = channel.
+__global__ __launch_bounds__(256) void k_prep_iq(const float* __restrict__ iq,
+                                                 const float* __restrict__ iw, int64_t n_q,
+                                                 float* __restrict__ qd, float* __restrict__ wq) {
+    const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
     const int64_t bq = blockIdx.x;
     if (bq >= n_q) return;
-    for (int h = 0; h < kIdxHeads; ++h) {
-        const float x = iq[(bq * kIdxHeads + h) * kIdxDim + lane];
-        const float amax = wave_max_f32(fabsf(x));
-        const float sq = amax / 448.0f;
-        const uint32_t c = (sq == 0.0f) ? ((__float_as_uint(x) >> 24) & 0x80u) : e4m3_encode(x / sq);
-        qd[(bq * kIdxHeads + h) * kIdxDim + lane] = e4m3_decode_bits(c);
-        if (lane == 0) wq[bq * kIdxHeads + h] = iw[bq * kIdxHeads + h] * sq;
-    }
+    const float x = iq[(bq * kIdxHeads + h) * kIdxDim + lane];
+    const float amax = wave_max_f32(fabsf(x));
+    const float sq = amax / 448.0f;
+    const uint32_t c = (sq == 0.0f) ? ((__float_as_uint(x) >> 24) & 0x80u) : e4m3_encode(x / sq);
+    qd[(bq * kIdxHeads + h) * kIdxDim + lane] = e4m3_decode_bits(c);
+    if (lane == 0) wq[bq * kIdxHeads + h] = iw[bq * kIdxHeads + h] * sq;
 }
 
-// Codec probe: decode every E4M3 code with the hardware converter used by the
-// hot loops, every E2M1 code with the bit decoder used by attention, and run
-// both encoders on caller values.
+// Codec probe: decode every E4M3 code with the fp32 converter of the scan and
+// the fp16 converter of the attention, every (E2M1 code, E4M3 scale) pair
+// with the attention's FP4 path, and run both encoders on caller values.
 __global__ __launch_bounds__(256) void k_codec_probe(float* __restrict__ e4m3_dec,
-                                                     float* __restrict__ e2m1_dec,
+                                                     float* __restrict__ e4m3_dec16,
+                                                     float* __restrict__ fp4_dec16,
                                                      const float* __restrict__ x, int64_t n,
                                                      uint8_t* __restrict__ e4m3_enc,
                                                      uint8_t* __restrict__ e2m1_enc) {
@@ -139,9 +138,14 @@ __global__ __launch_bounds__(256) void k_codec_probe(float* __restrict__ e4m3_de
         e4m3_dec[2 * t] = f.x;
         e4m3_dec[2 * t + 1] = f.y;
     }
-    if (t < 16) {
-        const uint32_t h = e2m1_to_f16_bits((uint32_t)t);
-        e2m1_dec[t] = (float)__builtin_bit_cast(_Float16, (unsigned short)h);
+    if (t < 256) {
+        e4m3_dec16[t] = (float)e4m3_to_f16((uint32_t)t);
+        // scale byte t, all 16 codes: dword 0x76543210 and 0xFEDCBA98 hold codes 0..15
+        _Float16 v[16];
+        const _Float16 sc = e4m3_to_f16((uint32_t)t);
+        fp4x8_to_f16(0x76543210u, sc, v);
+        fp4x8_to_f16(0xFEDCBA98u, sc, v + 8);
+        for (int c = 0; c < 16; ++c) fp4_dec16[t * 16 + c] = (float)v[c];
     }
     if (t < n) {
         e4m3_enc[t] = (uint8_t)e4m3_encode(x[t]);
@@ -171,16 +175,17 @@ hipError_t launch_quant_fp8(const float* x, int64_t n_rows, int dim, int layout,
 
 hipError_t launch_prep_iq(const float* iq, const float* iw, int64_t n_q, float* qd, float* wq,
                           hipStream_t stream) {
-    hipLaunchKernelGGL(k_prep_iq, dim3((unsigned)n_q), dim3(64), 0, stream, iq, iw, n_q, qd, wq);
+    hipLaunchKernelGGL(k_prep_iq, dim3((unsigned)n_q), dim3(256), 0, stream, iq, iw, n_q, qd, wq);
     return hipGetLastError();
 }
 
-hipError_t launch_codec_probe(float* e4m3_dec, float* e2m1_dec, const float* x, int64_t n,
-                              uint8_t* e4m3_enc, uint8_t* e2m1_enc, hipStream_t stream) {
+hipError_t launch_codec_probe(float* e4m3_dec, float* e4m3_dec16, float* fp4_dec16,
+                              const float* x, int64_t n, uint8_t* e4m3_enc, uint8_t* e2m1_enc,
+                              hipStream_t stream) {
     const int64_t threads = n > 256 ? n : 256;
     const unsigned grid = (unsigned)((threads + 255) / 256);
-    hipLaunchKernelGGL(k_codec_probe, dim3(grid), dim3(256), 0, stream, e4m3_dec, e2m1_dec, x, n,
-                       e4m3_enc, e2m1_enc);
+    hipLaunchKernelGGL(k_codec_probe, dim3(grid), dim3(256), 0, stream, e4m3_dec, e4m3_dec16,
+                       fp4_dec16, x, n, e4m3_enc, e2m1_enc);
     return hipGetLastError();
 }
 

@@ -60,19 +60,22 @@ class DecodeStack:
         self.lse = torch.empty((len(plan), B, H), dtype=torch.float32, device=dev)
         self.sources = reuse_sources(plan)
 
-    def step(self, iq, iw, n_vis, q, swa_k, swa_v, swa_ks, swa_vs, swa_len, stream=None):
+    def step(self, iq, iw, n_vis, q, swa_k, swa_v, swa_ks, swa_vs, swa_len, stream=None,
+             scan_timer=None):
         """One decode step.
 
         iq [n_idx][B][1][4][64], iw [n_idx][B][1][4]: one indexer query per
         Full/Reindex layer; n_vis [B][1] int32; q [L][B][H][128];
         swa_k/v [L][B][128][128] u8, swa_ks/vs [L][B][128] f32, swa_len [B].
+        scan_timer: optional KernelTimer bracketing the Full layer's scan.
         Returns the list of top-K buffers each layer attended with."""
         used, cur, k = [], None, 0
         for layer, mode in enumerate(self.plan):
             if mode == "F":
                 index_full(self.cache, iq[k], iw[k], n_vis, self.topk_bufs[k],
                            self.pool if self.pool_blocks else None, topk=self.topk,
-                           pool_blocks=self.pool_blocks, ws=self.ws_full, stream=stream)
+                           pool_blocks=self.pool_blocks, ws=self.ws_full, stream=stream,
+                           scan_timer=scan_timer)
                 cur, k = self.topk_bufs[k], k + 1
             elif mode == "X":
                 index_reindex(self.cache, iq[k], iw[k], n_vis, self.pool, self.topk_bufs[k],

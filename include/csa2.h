@@ -168,6 +168,20 @@ int csa2_index_full(const uint8_t* ik_codes, const float* ik_sigma, int64_t cap,
                     size_t ws_bytes, hipStream_t stream);
 
 /*
+ * csa2_index_full_timed -- csa2_index_full with the Full-layer scan kernel
+ * (the only kernel of the path whose work grows with context) bracketed by two
+ * caller-created HIP events: the runtime records scan_start immediately before
+ * and scan_stop immediately after that dispatch (hipExtLaunchKernel), so
+ * hipEventElapsedTime(scan_start, scan_stop) is the scan's duration.  Both
+ * NULL: identical to csa2_index_full.  Not for use under stream capture.
+ */
+int csa2_index_full_timed(const uint8_t* ik_codes, const float* ik_sigma, int64_t cap, int B,
+                          int Q, const float* iq, const float* iw, const int32_t* n_vis, int topk,
+                          int pool_blocks, int32_t* topk_idx, int32_t* pool_idx, void* ws,
+                          size_t ws_bytes, hipStream_t stream, hipEvent_t scan_start,
+                          hipEvent_t scan_stop);
+
+/*
  * csa2_index_reindex -- Reindex layer ("DeepSeek V4.1 Flash: architecture
  * study notes" section 2: reuses the Full layer's indexer K, rescores with its
  * own indexer query, only inside the pool).
@@ -211,7 +225,7 @@ int csa2_sparse_attn_decode(const float* q, int B, int H, const uint8_t* kv_code
  * ("DeepSeek V4.1 Flash: architecture study notes" section 5: the decoder
  * replays only the last 128 tokens of the prompt to rebuild its SWA state;
  * earlier local dependencies are cut off).
- *   q          [B][Q][H][128] fp32; topk_idx [B][Q][topk].
+ *   q          [B][Q][H][128] fp32, Q <= 128; topk_idx [B][Q][topk].
  *   swa_k, swa_v    [B][Q][128] E4M3, the chunk's own tokens; swa_ks,
  *              swa_vs [B][Q].  Query i attends to chunk tokens [0, i].
  *   out [B][Q][H][128], lse [B][Q][H].  Otherwise as the decode call.
@@ -235,13 +249,16 @@ int csa2_abi_version(void);
 
 /*
  * csa2_codec_probe -- diagnostics: runs the library's own device codecs.
- *   e4m3_dec [256] fp32 out: decode of every E4M3 code.
- *   e2m1_dec [16]  fp32 out: decode of every E2M1 code.
- *   x [n] fp32 in -> e4m3_enc [n], e2m1_enc [n] uint8 out (encoders as used
- *   by the write path).  Enqueued on `stream` like every call.
+ *   e4m3_dec   [256] fp32 out: every E4M3 code through the scan's converter.
+ *   e4m3_dec16 [256] fp32 out: every E4M3 code through the attention's fp16
+ *              converter.
+ *   fp4_dec16  [256*16] fp32 out: [s*16 + c] = E2M1 code c (sign in bit 3)
+ *              times E4M3 scale byte s, through the attention's FP4 path.
+ *   x [n] fp32 in -> e4m3_enc [n], e2m1_enc [n] uint8 out (the write path's
+ *   encoders).  Enqueued on `stream` like every call.
  */
-int csa2_codec_probe(float* e4m3_dec, float* e2m1_dec, const float* x, int64_t n,
-                     uint8_t* e4m3_enc, uint8_t* e2m1_enc, hipStream_t stream);
+int csa2_codec_probe(float* e4m3_dec, float* e4m3_dec16, float* fp4_dec16, const float* x,
+                     int64_t n, uint8_t* e4m3_enc, uint8_t* e2m1_enc, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -108,7 +108,7 @@ def test_workspace_sizes(lib):
     n_full = ws(1, 16, 1, 131072, 512, 2048, 0)
     # keys (4 B/position) + block keys (0.5 B/position) dominate
     assert 16 * 131072 * 4.5 <= n_full < 16 * 131072 * 4.5 + (1 << 20)
-    assert ws(1, 16, 1, 131072, 512, 0, 0) > n_full          # internal pool added
+    assert ws(1, 16, 1, 131072, 512, 0, 0) == n_full         # internal pool lives in LDS
     assert ws(2, 16, 1, 131072, 512, 2048, 0) >= 16 * 2048 * 8 * 4
     assert ws(1, 16, 1, 1000, 512, 2048, 0) == big
     assert ws(99, 1, 1, 64, 1, 1, 16) == big

@@ -34,15 +34,15 @@ def test_codec_probe_matches_oracle(gpu, oracle_mod):
                         np.array([0.0, 1e-45, 1e-40, 447.99, 448, 464, 480, 1e30, 0.25, 0.75,
                                   1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0], np.float32)])
     x = np.concatenate([x, -x]).astype(np.float32)
-    e4, e2, enc4, enc2 = gpu.codec_probe(dev(x))
-    e4, e2, enc4, enc2 = host(e4), host(e2), host(enc4), host(enc2)
+    e4, e4h, fp4, enc4, enc2 = [host(t) for t in gpu.codec_probe(dev(x))]
     for c in range(256):
         ref = oracle_mod.e4m3_decode(c)
         if c & 0x7F == 0x7F:
             continue  # NaN codes are never produced by the encoders
         assert e4[c] == ref, (hex(c), e4[c], ref)
-    for c in range(16):
-        assert e2[c] == oracle_mod.e2m1_decode(c), c
+        assert e4h[c] == ref, (hex(c), e4h[c], ref)
+        for code in range(16):  # the attention's FP4 path: code x scale, exact
+            assert fp4[c, code] == oracle_mod.e2m1_decode(code) * ref, (hex(c), code)
     ref4 = np.array([oracle_mod.e4m3_encode(float(v)) for v in x], np.uint8)
     ref2 = np.array([oracle_mod.e2m1_encode(float(v)) for v in x], np.uint8)
     np.testing.assert_array_equal(enc4, ref4)

@@ -151,3 +151,38 @@ def test_decoder_stack_1m_full_size(gpu, oracle_mod):
         planted = set((inp.planted[b][:, None] * 8 + np.arange(8)).ravel().tolist())
         sel = [p for p in tk_all[0][b, 0].tolist() if p >= 0]
         assert sum(p in planted for p in sel) > 0.5 * len(sel)
+
+
+def test_graph_replay_matches_eager(gpu, oracle_mod):
+    """The stack captured in a HIP graph replays to the same bytes as eager
+    launches, on every replay, with unrelated eager work in between."""
+    from compressed_kv_cache_decode_amd.stack import DecodeStack
+    wl = synth.WORKLOADS["decoder_stack_128k"]
+    inp = synth.decode_inputs(wl, n_ent=12000, B=2, layers=6)
+    cap = 12032
+    cache = build_cache_on_gpu(gpu, inp, cap)
+    swk, sks, swv, svs = quantize_windows(gpu, inp.swa_k, inp.swa_v)
+    st = DecodeStack(cache, wl.plan[:6], 2, wl.H, topk=256, pool_blocks=512)
+    args = (dev(inp.iq[:, :, None]), dev(inp.iw[:, :, None]), dev(np.full((2, 1), 12000, np.int32)),
+            dev(inp.q), swk, swv, sks, svs, dev(inp.swa_len))
+    say("graph: eager reference")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        st.step(*args)
+    torch.cuda.synchronize()
+    ref_out, ref_lse, ref_tk = host(st.out).copy(), host(st.lse).copy(), host(st.topk_bufs).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        st.step(*args)
+    for rep in range(4):
+        st.out.zero_()
+        st.topk_bufs.fill_(-9)
+        junk = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"graph: replay {rep}")
+        np.testing.assert_array_equal(host(st.out), ref_out)
+        np.testing.assert_array_equal(host(st.lse), ref_lse)
+        np.testing.assert_array_equal(host(st.topk_bufs), ref_tk)
+        del junk
