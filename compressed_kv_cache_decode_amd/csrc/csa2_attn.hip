@@ -7,28 +7,37 @@
 // section 4: the FP4 cache is dequantised on read and fed to ordinary
 // attention (the saving is storage, not FP4 arithmetic); the SWA KV stays FP8.
 //
-// Design (gfx950).  A decode batch is small (16 queries) while every query
-// gathers ~108 KB from random rows, so the latency of the dependent
-// index -> row loads dominates.  The entry list of each query (selected
-// records, then window tokens) is cut into tiles of 32 entries and the work is
-// split over (query, run of tiles) workgroups -- 320 of them for 16 queries --
-// so all gathers are in flight at once; a second small kernel merges the
-// per-split softmax partials (one wave per query and head, one load round).
-// Within a workgroup, one wave per 16 heads: all heads share one KV head (MQA),
-// so the logits are a dense [heads x entries] contraction on MFMA
-// (v_mfma_f32_16x16x32_f16):
+// Design (gfx950).  The entry list of a query (selected records, then window
+// tokens) is cut into tiles of 32 entries.  One workgroup of 8 waves serves
+// one (query, group of 16 heads); wave w takes tiles w, w + 8, w + 16, ... and
+// keeps its own online softmax; the 8 partial states are merged through LDS at
+// the end, so one launch produces the output (no partials in HBM, no second
+// kernel).  All heads share one KV head (MQA), so per tile the logits are a
+// dense [16 heads x 32 entries] contraction on MFMA (v_mfma_f32_16x16x32_f16):
+//   - S^T = K Q^T: the K operand is dequantised straight from the gathered
+//     bytes into registers.  Lane (entry e, quarter g) loads channels
+//     [32g, 32g + 32) of its record, and MFMA step ks consumes channels
+//     32g + 8ks .. +8 from that lane group; q is laid out with the same
+//     channel permutation, which leaves the dot products unchanged.
+//   - O^T += V^T P^T: P comes straight from the S^T registers (each lane holds
+//     entries 4g..4g+3 and 16+4g..16+4g+3 of its head); V is dequantised by the
+//     lanes that own those entries and transposed through a wave-private LDS
+//     tile, so no workgroup barrier sits inside the tile loop.
 //   - dequantised E2M1 x E4M3 values have at most 6 significant bits and lie
 //     in [2^-10, 2688], so they are exact in fp16; E4M3 window codes are exact
 //     in fp16 and their fp32 row scale is applied to the logit (K) or to the
 //     probability (V) in fp32;
 //   - q is split into fp16 hi + lo parts, so q.k carries ~22 bits;
 //   - accumulation is fp32, softmax is online in fp32 (base-2 exponentials).
-// Per tile the workgroup dequantises the gathered bytes into LDS (K row-major,
-// V transposed); each wave computes S^T = K Q^T, rescales its running output
-// and accumulates O^T += V^T P^T with P taken straight from the S^T registers
-// (entry order inside the k dimension is permuted consistently).  With more
-// than one tile per split, the next tile's bytes are loaded while the current
-// one is used.
+// Memory instructions, not bytes, bound a gather this small: every vector load
+// costs the address unit about the same time whatever its width.  So the
+// workgroup reads q, the top-K row and the window scales once into LDS, and
+// each wave gathers a tile's rows with 16-byte loads only: the K operand
+// directly, the V codes and the scale bytes through a wave-private LDS stage
+// from which the lanes pick their operand bytes.  Each wave keeps two tiles'
+// bytes in flight.  Workgroups are numbered so that the head groups of one
+// query land on the same XCD (consecutive workgroup ids go round-robin over
+// the 8 XCDs), sharing its L2 for the gathered rows.
 #include "csa2_device.hpp"
 #include "csa2_internal.hpp"
 
@@ -37,61 +46,40 @@ namespace csa2 {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kTile = 32;          // entries per tile
-constexpr int kKPitch = 136;       // fp16 per K row in LDS (128 + 8)
-constexpr int kVPitch = 36;        // fp16 per V^T row in LDS (32 + 4)
+constexpr int kTile = 32;           // entries per tile
+constexpr int kWaves = 8;           // waves per workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kGroupHeads = 16;     // heads per workgroup (one MFMA column block)
+constexpr int kVPitch = 144;        // fp16 per V row in LDS (128 + 16)
+constexpr int kMergePitch = kHeadDim + 4;  // fp32 per merged output row in LDS
+constexpr int kXcds = 8;
+constexpr int kMaxWindow = 128;     // window rows per sequence (decode 128, chunk <= 128)
+constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag the true max
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-struct SplitPlan {
-    int n_tiles_global;  // ceil(topk / 32)
-    int n_tiles;         // global + window tiles
-    int n_splits;
-    int tiles_per_split;
-};
+// LDS map (bytes)
+constexpr int kWaveBytes = kTile * kVPitch * 2;              // one wave's V tile
+constexpr int kOffQ = 0;                                     // q [16][128] fp32
+constexpr int kOffIdx = kOffQ + kGroupHeads * kHeadDim * 4;  // top-K row, int32 [kMaxTopk]
+constexpr int kOffWin = kOffIdx + kMaxTopk * 4;              // window K scales [128], V scales [128]
+constexpr int kOffWave = kOffWin + 2 * kMaxWindow * 4;       // per-wave V tiles
+constexpr int kLdsBytes = kOffWave + kWaves * kWaveBytes;
+constexpr int kMergeBytes = (kWaves * kGroupHeads * kMergePitch + 2 * kWaves * kGroupHeads) * 4;
+static_assert(kMergeBytes <= kWaves * kWaveBytes, "merge area aliases the wave areas");
+static_assert(kLdsBytes <= 160 * 1024, "LDS");
 
-// Aim for about 512 workgroups: a decode batch of 16 queries spreads its 20
-// tiles over 20 workgroups per query; a 128-query chunk takes 4 per query.
-// At most 64 splits (the merge kernel gives one lane to each).
-static SplitPlan plan_splits(int64_t n_q, int topk, int swa_rows) {
-    SplitPlan p;
-    p.n_tiles_global = (topk + kTile - 1) / kTile;
-    p.n_tiles = p.n_tiles_global + (swa_rows + kTile - 1) / kTile;
-    if (p.n_tiles == 0) p.n_tiles = 1;
-    int64_t ns = (512 + n_q - 1) / n_q;
-    if (ns > p.n_tiles) ns = p.n_tiles;
-    if (ns > 64) ns = 64;
-    if (ns < 1) ns = 1;
-    p.tiles_per_split = (int)((p.n_tiles + ns - 1) / ns);
-    p.n_splits = (p.n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
-    return p;
-}
+size_t attn_workspace_bytes(int64_t, int, int, int) { return 0; }
 
-size_t attn_workspace_bytes(int64_t n_q, int H, int topk, int swa_rows) {
-    const SplitPlan p = plan_splits(n_q, topk, swa_rows);
-    if (p.n_splits <= 1) return 0;
-    return (size_t)n_q * p.n_splits * H * (kHeadDim + 2) * sizeof(float);
-}
-
-// One tile (32 entries) is loaded as 256 tasks:
-//   task <  128  K task: entry e = task/4, channels [32c, 32c+32), c = task%4
-//   task >= 128  V task: entries 4q..4q+3, channels [8o, 8o+8) (q, o from task-128)
-// The raw bytes of a task fit in 8 dwords; `flag` carries validity bits.
-struct TaskRegs {
-    uint32_t w[8];
-    uint32_t flag;
-    float mul[4];
-};
-
-struct TileCtx {
+// What one workgroup needs to locate its entries.
+struct SeqView {
     const uint8_t* kvc;
     const uint8_t* kvs;
     const uint8_t* swk;
     const uint8_t* swv;
-    const float* swks;
-    const float* swvs;
-    const int32_t* idx;  // this query's top-K row
+    const int32_t* idx_l;  // this query's top-K row, in LDS
     int64_t cap;
     int64_t b;
     int topk;
@@ -100,387 +88,430 @@ struct TileCtx {
     int n_tiles_global;
 };
 
-// global entry `slot` of this query -> cache row, or -1
-__device__ __forceinline__ int64_t entry_row(const TileCtx& c, int slot) {
-    if (slot >= c.topk) return -1;
-    const int32_t pos = c.idx[slot];
-    return (pos >= 0 && pos < c.cap) ? c.b * c.cap + pos : -1;
+// cache row of entry e of global tile t, or -1
+__device__ __forceinline__ int64_t global_row(const SeqView& s, int t, int e) {
+    const int slot = t * kTile + e;
+    if (slot >= s.topk) return -1;
+    const int32_t p = s.idx_l[slot];
+    return (p >= 0 && p < s.cap) ? s.b * s.cap + p : -1;
 }
 
-// window token t of this query -> window row, or -1
-__device__ __forceinline__ int64_t window_row(const TileCtx& c, int t) {
-    return t < c.swa_len ? c.b * c.swa_rows + t : -1;
+// window row of token e of window tile t, or -1
+__device__ __forceinline__ int64_t window_row(const SeqView& s, int t, int e) {
+    const int tok = (t - s.n_tiles_global) * kTile + e;
+    return tok < s.swa_len ? s.b * s.swa_rows + tok : -1;
 }
 
-__device__ __forceinline__ void load_task(const TileCtx& c, int tile, int task, TaskRegs& r) {
-    const bool global = tile < c.n_tiles_global;
-    r.flag = 0;
-    if (task < 128) {
-        const int e = task >> 2, q4 = task & 3;
-        const int64_t row = global ? entry_row(c, tile * kTile + e)
-                                   : window_row(c, (tile - c.n_tiles_global) * kTile + e);
-        if (row < 0) return;
-        r.flag = 1;
+// Raw bytes of one tile held by one lane (c = lane & 15, g = lane >> 4).
+// Absent rows load nothing and read as zero.
+//   k[blk]  K operand of entry 16 blk + c, channels [32g, 32g + 32):
+//           global 16 B of E2M1 codes (k[blk][0]); window 32 B of E4M3 (k[blk][0..1])
+//   v       V codes, whole 64-byte sectors per group of lanes: global v[j] = channels
+//           [32q, 32q + 32) of entry 16j + lane/4 (q = lane & 3); window v[j] =
+//           channels [16q8, 16q8 + 16) of token 8j + lane/8 (q8 = lane & 7)
+//   sc      global, lanes 0..31: the 16 scale bytes (K 0..7, V 8..15) of entry `lane`
+//   valid   bit e: entry e of the tile is present (same in every lane)
+struct TileRegs {
+    u32x4_t k[2][2];
+    u32x4_t v[4];
+    u32x4_t sc;
+    uint32_t valid;
+};
+
+__device__ __forceinline__ u32x4_t ld16(const uint8_t* p) {
+    return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// Issue the loads of tile t (rows come from LDS, so nothing here waits on HBM).
+__device__ __forceinline__ void fetch_tile(const SeqView& s, int t, int lane, TileRegs& r) {
+    const int c = lane & 15, g = lane >> 4;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    if (t < s.n_tiles_global) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const int64_t row = global_row(s, t, 16 * blk + c);
+            r.k[blk][0] = row >= 0 ? ld16(s.kvc + (row >= 0 ? row : 0) * 128 + 16 * g) : z;
+            r.k[blk][1] = z;
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t vrow = global_row(s, t, 16 * j + (lane >> 2));
+            r.v[j] = vrow >= 0 ? ld16(s.kvc + (vrow >= 0 ? vrow : 0) * 128 + 64 + 16 * (lane & 3)) : z;
+        }
+        r.v[2] = z;
+        r.v[3] = z;
+        const int64_t srow = lane < kTile ? global_row(s, t, lane) : -1;
+        r.sc = srow >= 0 ? ld16(s.kvs + (srow >= 0 ? srow : 0) * 16) : z;
+        r.valid = (uint32_t)__builtin_amdgcn_ballot_w64(srow >= 0);
+    } else {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const int64_t row = window_row(s, t, 16 * blk + c);
+            const uint8_t* src = s.swk + (row >= 0 ? row : 0) * kHeadDim + 32 * g;
+            r.k[blk][0] = row >= 0 ? ld16(src) : z;
+            r.k[blk][1] = row >= 0 ? ld16(src + 16) : z;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t vrow = window_row(s, t, 8 * j + (lane >> 3));
+            r.v[j] = vrow >= 0 ? ld16(s.swv + (vrow >= 0 ? vrow : 0) * kHeadDim + 16 * (lane & 7)) : z;
+        }
+        r.sc = z;
+        const int tok0 = (t - s.n_tiles_global) * kTile;
+        const int nv = s.swa_len - tok0;  // >= 1: window tiles end at swa_len
+        r.valid = nv >= kTile ? 0xFFFFFFFFu : ((1u << nv) - 1u);
+    }
+}
+
+// max / sum over the four lanes c, c+16, c+32, c+48 (v_permlane*_swap: each
+// call hands every lane its partner's value 32 resp. 16 lanes away)
+__device__ __forceinline__ float xmax4(float v) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float xsum4(float v) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Eight E2M1 codes times an fp16 scale, as one MFMA operand.
+__device__ __forceinline__ half8_t fp4x8_h8(uint32_t w, _Float16 sc) {
+    const half2_t s2 = {sc, sc};
+    const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+    const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+    const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+    const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+    const half4_t a = __builtin_shufflevector(h0, h1, 0, 1, 2, 3);
+    const half4_t b = __builtin_shufflevector(h2, h3, 0, 1, 2, 3);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Eight E4M3 codes (two dwords), exact in fp16, as one MFMA operand.
+__device__ __forceinline__ half8_t fp8x8_h8(uint32_t w0, uint32_t w1) {
+    const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+    const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+    const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+    const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+    const half4_t a = __builtin_shufflevector(h0, h1, 0, 1, 2, 3);
+    const half4_t b = __builtin_shufflevector(h2, h3, 0, 1, 2, 3);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+struct WaveState {
+    float4_t o[8];  // O^T[dim 16 dt + 4g + r][head c], relative to m
+    float m;        // reference (base-2 logit) of head c; lags its running max by < 8
+    float l;        // this lane's share of the running sum, relative to m
+};
+
+// The lane's C entries: 4g + i (i < 4) and 16 + 4g + i - 4 (i >= 4).
+__device__ __forceinline__ int c_entry(int i, int g) { return i < 4 ? 4 * g + i : 12 + 4 * g + i; }
+
+// One tile: V into LDS, logits, online softmax, PV.
+__device__ __forceinline__ void process_tile(const SeqView& s, int t, const TileRegs& r,
+                                             const float* __restrict__ win_l,
+                                             const half8_t (&qhi)[4], const half8_t (&qlo)[4],
+                                             _Float16* __restrict__ vtile, int lane,
+                                             WaveState& st) {
+    const int c = lane & 15, g = lane >> 4;
+    const bool global = t < s.n_tiles_global;
+
+    // scale bytes come from the lane that loaded the entry's 16-byte chunk:
+    // K scales 2g, 2g + 1 of entries c and 16 + c; V scales 2q, 2q + 1 of
+    // entries lane/4 and 16 + lane/4
+    const int q4 = lane & 3;
+    uint32_t ksc[2] = {0u, 0u}, vsc[2] = {0u, 0u};
+    if (global) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const int src = (16 * blk + c) << 2;
+            const uint32_t d0 = __builtin_amdgcn_ds_bpermute(src, r.sc[0]);
+            const uint32_t d1 = __builtin_amdgcn_ds_bpermute(src, r.sc[1]);
+            ksc[blk] = ((g >> 1) ? d1 : d0) >> (16 * (g & 1));
+            const int vsrc = (16 * blk + (lane >> 2)) << 2;
+            const uint32_t d2 = __builtin_amdgcn_ds_bpermute(vsrc, r.sc[2]);
+            const uint32_t d3 = __builtin_amdgcn_ds_bpermute(vsrc, r.sc[3]);
+            vsc[blk] = ((q4 >> 1) ? d3 : d2) >> (16 * (q4 & 1));
+        }
+    }
+
+    // ---- V codes of the lane, dequantised, row-major into the wave's V tile ----
+    if (global) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            half8_t* dst = reinterpret_cast<half8_t*>(vtile + (16 * j + (lane >> 2)) * kVPitch + 32 * q4);
+            const _Float16 s0 = e4m3_to_f16(vsc[j] & 0xFFu), s1 = e4m3_to_f16((vsc[j] >> 8) & 0xFFu);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) dst[m] = fp4x8_h8(r.v[j][m], m < 2 ? s0 : s1);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            half8_t* dst = reinterpret_cast<half8_t*>(vtile + (8 * j + (lane >> 3)) * kVPitch + 16 * (lane & 7));
+            dst[0] = fp8x8_h8(r.v[j][0], r.v[j][1]);
+            dst[1] = fp8x8_h8(r.v[j][2], r.v[j][3]);
+        }
+    }
+
+    // ---- S^T = K Q^T (base-2 logits up to the window row scale) ----
+    float4_t sacc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        half8_t ka[4];
         if (global) {
-            const uint4 v = *reinterpret_cast<const uint4*>(c.kvc + row * 128 + 16 * q4);
-            r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
-            r.w[4] = *reinterpret_cast<const uint16_t*>(c.kvs + row * 16 + 2 * q4);
-        } else {
-            const uint4 v0 = *reinterpret_cast<const uint4*>(c.swk + row * kHeadDim + 32 * q4);
-            const uint4 v1 = *reinterpret_cast<const uint4*>(c.swk + row * kHeadDim + 32 * q4 + 16);
-            r.w[0] = v0.x; r.w[1] = v0.y; r.w[2] = v0.z; r.w[3] = v0.w;
-            r.w[4] = v1.x; r.w[5] = v1.y; r.w[6] = v1.z; r.w[7] = v1.w;
-            r.mul[0] = c.swks[row];
-        }
-    } else {
-        const int u = task - 128, q = u >> 4, o = u & 15;
+            const uint32_t sb = ksc[blk];
+            const _Float16 s0 = e4m3_to_f16(sb & 0xFFu), s1 = e4m3_to_f16((sb >> 8) & 0xFFu);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = 4 * q + j;
-            const int64_t row = global ? entry_row(c, tile * kTile + e)
-                                       : window_row(c, (tile - c.n_tiles_global) * kTile + e);
-            if (row < 0) continue;
-            r.flag |= 1u << j;
-            if (global) {
-                r.w[2 * j] = *reinterpret_cast<const uint32_t*>(c.kvc + row * 128 + 64 + 4 * o);
-                r.w[2 * j + 1] = c.kvs[row * 16 + 8 + (o >> 1)];
-            } else {
-                const uint2 v = *reinterpret_cast<const uint2*>(c.swv + row * kHeadDim + 8 * o);
-                r.w[2 * j] = v.x;
-                r.w[2 * j + 1] = v.y;
-                r.mul[j] = c.swvs[row];
-            }
-        }
-    }
-}
-
-__device__ __forceinline__ void store_task(const TileCtx& c, int tile, int task,
-                                           const TaskRegs& r, _Float16* sK, _Float16* sVt,
-                                           float* sKmul, float* sVmul, float logit_mul) {
-    const bool global = tile < c.n_tiles_global;
-    if (task < 128) {
-        const int e = task >> 2, q4 = task & 3;
-        _Float16 v[32];
-        if (!r.flag) {
-#pragma unroll
-            for (int i = 0; i < 32; ++i) v[i] = (_Float16)0.0f;
-        } else if (global) {
-            const _Float16 s0 = e4m3_to_f16(r.w[4] & 0xFFu), s1 = e4m3_to_f16(r.w[4] >> 8);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) fp4x8_to_f16(r.w[i], i < 2 ? s0 : s1, v + 8 * i);
+            for (int ks = 0; ks < 4; ++ks) ka[ks] = fp4x8_h8(r.k[blk][0][ks], ks < 2 ? s0 : s1);
         } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) fp8x8_to_f16(r.w[2 * i], r.w[2 * i + 1], v + 8 * i);
+            for (int ks = 0; ks < 4; ++ks)
+                ka[ks] = fp8x8_h8(r.k[blk][ks >> 1][2 * (ks & 1)], r.k[blk][ks >> 1][2 * (ks & 1) + 1]);
         }
-        half8_t* dst = reinterpret_cast<half8_t*>(sK + e * kKPitch + 32 * q4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            half8_t h;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) h[i] = v[8 * j + i];
-            dst[j] = h;
-        }
-        if (q4 == 0)
-            sKmul[e] = !r.flag ? -INFINITY : (global ? logit_mul : r.mul[0] * logit_mul);
-    } else {
-        const int u = task - 128, q = u >> 4, o = u & 15;
-        _Float16 v[4][8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (!(r.flag >> j & 1u)) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) v[j][i] = (_Float16)0.0f;
-            } else if (global) {
-                fp4x8_to_f16(r.w[2 * j], e4m3_to_f16(r.w[2 * j + 1]), v[j]);
-            } else {
-                fp8x8_to_f16(r.w[2 * j], r.w[2 * j + 1], v[j]);
-            }
-        }
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            const half4_t h = {v[0][d], v[1][d], v[2][d], v[3][d]};
-            *reinterpret_cast<half4_t*>(sVt + (8 * o + d) * kVPitch + 4 * q) = h;
-        }
-        if (o == 0) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                sVmul[4 * q + j] = (r.flag >> j & 1u) ? (global ? 1.0f : r.mul[j]) : 0.0f;
-        }
-    }
-}
-
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void k_attn(AttnArgs a, SplitPlan plan,
-                                                  float* __restrict__ part) {
-    constexpr int kThreads = NW * 64;
-    constexpr int kTasksPerThread = (256 + kThreads - 1) / kThreads;
-    __shared__ __attribute__((aligned(16))) _Float16 sK[kTile * kKPitch];
-    __shared__ __attribute__((aligned(16))) _Float16 sVt[kHeadDim * kVPitch];
-    __shared__ __attribute__((aligned(16))) float sKmul[kTile];
-    __shared__ __attribute__((aligned(16))) float sVmul[kTile];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t bq = blockIdx.y;
-    const int split = blockIdx.x;
-    const int H = a.H;
-    const int head = wave * 16 + (lane & 15);
-    const int g = lane >> 4;
-    const float logit_mul = a.sm_scale * kLog2e;
-
-    TileCtx ctx;
-    ctx.kvc = a.kvc; ctx.kvs = a.kvs; ctx.swk = a.swk; ctx.swv = a.swv;
-    ctx.swks = a.swks; ctx.swvs = a.swvs;
-    ctx.idx = a.idx + bq * a.topk;
-    ctx.cap = a.cap;
-    ctx.b = bq / a.Q;
-    ctx.topk = a.topk;
-    ctx.swa_rows = a.swa_rows;
-    ctx.n_tiles_global = plan.n_tiles_global;
-    if (a.swa_len != nullptr) {
-        const int sl = a.swa_len[ctx.b];
-        ctx.swa_len = sl < 0 ? 0 : (sl > a.swa_rows ? a.swa_rows : sl);
-    } else {
-        ctx.swa_len = (int)(bq % a.Q) + 1;
-    }
-
-    const int t_beg = split * plan.tiles_per_split;
-    const int t_end = min(plan.n_tiles, t_beg + plan.tiles_per_split);
-
-    // q loads go out first (they depend on nothing), then the index -> row
-    // chain of the first tile; q is converted while the rows travel
-    float4 qraw[8];
-    {
-        const float* qrow = a.q + (bq * H + min(head, H - 1)) * kHeadDim;
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            qraw[2 * ks] = *reinterpret_cast<const float4*>(qrow + 32 * ks + 8 * g);
-            qraw[2 * ks + 1] = *reinterpret_cast<const float4*>(qrow + 32 * ks + 8 * g + 4);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[ks], qhi[ks], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[ks], qlo[ks], acc, 0, 0, 0);
         }
-    }
-    TaskRegs regs[kTasksPerThread];
-#pragma unroll
-    for (int k = 0; k < kTasksPerThread; ++k) {
-        const int task = tid + k * kThreads;
-        if (task < 256 && t_beg < t_end) load_task(ctx, t_beg, task, regs[k]);
+        sacc[blk] = acc;
     }
 
-    // ---- q as fp16 hi/lo in B-operand layout: head, dims 32ks + 8g .. +8 ----
-    half8_t qhi[4], qlo[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const float4 x0 = qraw[2 * ks], x1 = qraw[2 * ks + 1];
-        const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    // ---- logits of the lane's C entries; absent entries are -inf ----
+    float x[8], vmul[8];
+    const uint32_t vbits = ((r.valid >> (4 * g)) & 0xFu) | (((r.valid >> (16 + 4 * g)) & 0xFu) << 4);
+    if (global) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const _Float16 h = (_Float16)xs[i];
-            qhi[ks][i] = h;
-            qlo[ks][i] = (_Float16)(xs[i] - (float)h);
+            x[i] = (vbits >> i & 1u) ? sacc[i >> 2][i & 3] : -INFINITY;
+            vmul[i] = 1.0f;
+        }
+    } else {
+        const int tok0 = (t - s.n_tiles_global) * kTile;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int tok = tok0 + c_entry(i, g);
+            x[i] = (vbits >> i & 1u) ? sacc[i >> 2][i & 3] * win_l[tok] : -INFINITY;
+            vmul[i] = win_l[kMaxWindow + tok];
         }
     }
 
-    float4_t o[8];
+    // ---- online softmax; the reference m moves only when the tile max passes
+    // it by more than the slack, so most tiles skip the rescale ----
+    float tmax = x[0];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.0f;
-
-    for (int tile = t_beg; tile < t_end; ++tile) {
+    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
+    tmax = xmax4(tmax);
+    const bool move = tmax > st.m + kRescaleSlack || (st.m == -INFINITY && tmax != -INFINITY);
+    if (__builtin_amdgcn_ballot_w64(move)) {  // uniform branch
+        const float m_new = move ? tmax : st.m;
+        const float alpha = (st.m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(st.m - m_new);
 #pragma unroll
-        for (int k = 0; k < kTasksPerThread; ++k) {
-            const int task = tid + k * kThreads;
-            if (task < 256) store_task(ctx, tile, task, regs[k], sK, sVt, sKmul, sVmul, logit_mul);
+        for (int dt = 0; dt < 8; ++dt) st.o[dt] *= alpha;
+        st.l *= alpha;
+        st.m = m_new;
+    }
+    half8_t pb;
+    float psum = 0.0f;
+    if (st.m == -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[i] = (_Float16)0.0f;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p = __builtin_amdgcn_exp2f(x[i] - st.m);  // x - m <= 8; -inf -> 0
+            psum += p;
+            pb[i] = (_Float16)(p * vmul[i]);
         }
-        if (tile + 1 < t_end) {  // next tile's bytes travel during this tile's math
-#pragma unroll
-            for (int k = 0; k < kTasksPerThread; ++k) {
-                const int task = tid + k * kThreads;
-                if (task < 256) load_task(ctx, tile + 1, task, regs[k]);
-            }
-        }
-        __syncthreads();
+    }
+    st.l += psum;
 
-        if (head < H) {
-            // ---- S^T = K Q^T for entries [16 sub, +16), this wave's 16 heads ----
-            float4_t s[2];
+    wave_lds_sync();
+    // ---- O^T += V^T P^T; the A operand is read transposed from the row-major
+    // V tile: in each 16-lane group, lane 4j + i/4 supplies channels
+    // [16dt + 4(i/4), +4) of the entry at k slot j, and lane i receives channel
+    // 16dt + i of the four entries ----
+    const int sq = lane & 15;
+    const int ent0 = 4 * g + (sq >> 2), ent1 = 16 + 4 * g + (sq >> 2);
 #pragma unroll
-            for (int sub = 0; sub < 2; ++sub) {
-                float4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < 8; ++dt) {
+        const int col = 16 * dt + 4 * (sq & 3);
+        const half4_t v0 = __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4_t*)(vtile + ent0 * kVPitch + col)));
+        const half4_t v1 = __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4_t*)(vtile + ent1 * kVPitch + col)));
+        const half8_t va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, st.o[dt], 0, 0, 0);
+    }
+    wave_lds_sync();  // the next tile rewrites the V tile
+}
+
+// grid = ceil(n_q / 8) * 8 * (H / 16) workgroups of 512 threads.
+// Workgroup id -> (query bq, head group hg): ids with the same id % 8 share an
+// XCD, and all head groups of one query get ids with the same id % 8.
+__global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a, int n_tiles_global) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = lane & 15, g = lane >> 4;
+    const int G = a.H / kGroupHeads;
+    const int id = blockIdx.x;
+    const int round = (id / kXcds) / G;
+    const int hg = (id / kXcds) - round * G;
+    const int64_t bq = (int64_t)round * kXcds + (id % kXcds);
+    if (bq >= a.n_q) return;  // uniform over the workgroup
+
+    float* q_l = reinterpret_cast<float*>(smem + kOffQ);
+    int32_t* idx_l = reinterpret_cast<int32_t*>(smem + kOffIdx);
+    float* win_l = reinterpret_cast<float*>(smem + kOffWin);
+
+    SeqView s;
+    s.kvc = a.kvc; s.kvs = a.kvs; s.swk = a.swk; s.swv = a.swv;
+    s.idx_l = idx_l;
+    s.cap = a.cap;
+    s.b = bq / a.Q;
+    s.topk = a.topk;
+    s.swa_rows = a.swa_rows;
+    s.n_tiles_global = n_tiles_global;
+    if (a.swa_len != nullptr) {
+        const int sl = a.swa_len[s.b];
+        s.swa_len = sl < 0 ? 0 : (sl > a.swa_rows ? a.swa_rows : sl);
+    } else {
+        s.swa_len = (int)(bq % a.Q) + 1;  // chunk query i sees window tokens [0, i]
+    }
+    const int n_tiles = n_tiles_global + (s.swa_len + kTile - 1) / kTile;
+    const float logit_mul = a.sm_scale * kLog2e;
+
+    // ---- once per workgroup: q of the 16 heads, the top-K row, window scales ----
+    {
+        const float4 qv = reinterpret_cast<const float4*>(
+            a.q + (bq * a.H + hg * kGroupHeads) * kHeadDim)[tid];
+        int32_t iv[kMaxTopk / kThreads];
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const half8_t kv = *reinterpret_cast<const half8_t*>(
-                        sK + (16 * sub + (lane & 15)) * kKPitch + 32 * ks + 8 * g);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qhi[ks], acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qlo[ks], acc, 0, 0, 0);
-                }
-                s[sub] = acc;
-            }
-            // lane holds entries 16 sub + 4g + r for its head
-            const float4 km0 = *reinterpret_cast<const float4*>(sKmul + 4 * g);
-            const float4 km1 = *reinterpret_cast<const float4*>(sKmul + 16 + 4 * g);
-            const float km[8] = {km0.x, km0.y, km0.z, km0.w, km1.x, km1.y, km1.z, km1.w};
-            const float4 vm0 = *reinterpret_cast<const float4*>(sVmul + 4 * g);
-            const float4 vm1 = *reinterpret_cast<const float4*>(sVmul + 16 + 4 * g);
-            const float vm[8] = {vm0.x, vm0.y, vm0.z, vm0.w, vm1.x, vm1.y, vm1.z, vm1.w};
-            float x[8];
-            float tmax = -INFINITY;
+        for (int k = 0; k < kMaxTopk / kThreads; ++k) {
+            const int j = tid + k * kThreads;
+            iv[k] = j < a.topk ? a.idx[bq * a.topk + j] : -1;
+        }
+        float wv = 0.0f;
+        const int tok = tid & (kMaxWindow - 1);
+        if (tid < 2 * kMaxWindow && tok < s.swa_len)
+            wv = (tid < kMaxWindow ? a.swks : a.swvs)[s.b * s.swa_rows + tok];
+        reinterpret_cast<float4*>(q_l)[tid] = qv;
+#pragma unroll
+        for (int k = 0; k < kMaxTopk / kThreads; ++k) {
+            const int j = tid + k * kThreads;
+            if (j < a.topk) idx_l[j] = iv[k];
+        }
+        if (tid < 2 * kMaxWindow) win_l[tid] = wv;
+    }
+    __syncthreads();
+
+    const int t0 = wave, t1 = wave + kWaves;
+    TileRegs ra, rb;
+    if (t0 < n_tiles) fetch_tile(s, t0, lane, ra);
+    if (t1 < n_tiles) fetch_tile(s, t1, lane, rb);
+
+    // q * sm_scale * log2(e) (so that logits come out in base-2 units) as fp16
+    // hi + lo, B-operand layout: head c, MFMA step ks takes channels 32g + 8ks .. +8
+    half8_t qhi[4], qlo[4];
+    {
+        const float4* qrow = reinterpret_cast<const float4*>(q_l + c * kHeadDim + 32 * g);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const float4 x0 = qrow[2 * ks], x1 = qrow[2 * ks + 1];
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float v = (km[i] == -INFINITY) ? -INFINITY : s[i >> 2][i & 3] * km[i];
-                x[i] = v;
-                tmax = fmaxf(tmax, v);
-            }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-            const float m_new = fmaxf(m_run, tmax);
-            float alpha, psum = 0.0f;
-            half8_t pb;
-            if (m_new == -INFINITY) {
-                alpha = 1.0f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) pb[i] = (_Float16)0.0f;
-            } else {
-                alpha = exp2f(m_run - m_new);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float p = exp2f(x[i] - m_new);
-                    psum += p;
-                    pb[i] = (_Float16)(p * vm[i]);
-                }
-            }
-            psum += __shfl_xor(psum, 16, 64);
-            psum += __shfl_xor(psum, 32, 64);
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
-            // ---- O^T = O^T * alpha + V^T P^T ----
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const _Float16* vrow = sVt + (16 * dt + (lane & 15)) * kVPitch;
-                const half4_t v0 = *reinterpret_cast<const half4_t*>(vrow + 4 * g);
-                const half4_t v1 = *reinterpret_cast<const half4_t*>(vrow + 16 + 4 * g);
-                const half8_t va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-                float4_t acc = o[dt] * alpha;
-                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, acc, 0, 0, 0);
+                const float xq = xs[i] * logit_mul;
+                const _Float16 hq = (_Float16)xq;
+                qhi[ks][i] = hq;
+                qlo[ks][i] = (_Float16)(xq - (float)hq);
             }
         }
-        __syncthreads();
     }
 
-    if (head >= H) return;
-    // lane holds O^T[dim 16 dt + 4g + r][head]
-    if (plan.n_splits == 1) {
-        const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-        float* orow = a.out + (bq * H + head) * kHeadDim;
+    WaveState st;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            float4 v = make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
-            *reinterpret_cast<float4*>(orow + 16 * dt + 4 * g) = v;
+    for (int dt = 0; dt < 8; ++dt) st.o[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    st.m = -INFINITY;
+    st.l = 0.0f;
+    _Float16* vtile = reinterpret_cast<_Float16*>(smem + kOffWave + wave * kWaveBytes);
+
+    for (int t = t0; t < n_tiles; t += 2 * kWaves) {
+        process_tile(s, t, ra, win_l, qhi, qlo, vtile, lane, st);
+        if (t + 2 * kWaves < n_tiles) fetch_tile(s, t + 2 * kWaves, lane, ra);
+        const int u = t + kWaves;
+        if (u < n_tiles) {
+            process_tile(s, u, rb, win_l, qhi, qlo, vtile, lane, st);
+            if (u + 2 * kWaves < n_tiles) fetch_tile(s, u + 2 * kWaves, lane, rb);
         }
-        if (g == 0) a.lse[bq * H + head] = l_run > 0.0f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
-    } else {
-        float* prow = part + ((bq * plan.n_splits + split) * H + head) * (kHeadDim + 2);
+    }
+
+    // ---- merge the 8 waves' states through LDS (aliases the wave areas) ----
+    const float l_wave = xsum4(st.l);
+    __syncthreads();
+    float* mo = reinterpret_cast<float*>(smem + kOffWave);
+    float* mm = mo + kWaves * kGroupHeads * kMergePitch;
+    float* ml = mm + kWaves * kGroupHeads;
+    {
+        float* orow = mo + (wave * kGroupHeads + c) * kMergePitch + 4 * g;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            float4 v = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-            *reinterpret_cast<float4*>(prow + 16 * dt + 4 * g) = v;
-        }
+        for (int dt = 0; dt < 8; ++dt)
+            *reinterpret_cast<float4*>(orow + 16 * dt) =
+                make_float4(st.o[dt][0], st.o[dt][1], st.o[dt][2], st.o[dt][3]);
         if (g == 0) {
-            prow[kHeadDim] = m_run;
-            prow[kHeadDim + 1] = l_run;
+            mm[wave * kGroupHeads + c] = st.m;
+            ml[wave * kGroupHeads + c] = l_wave;
         }
     }
-}
-
-// Merge the per-split partials: one wave per (query, head).  Every load is
-// issued in one round (lane s reads split s's (m, l); each lane reads its two
-// channels of every split), then the weights exp2(m_s - M) are formed with
-// DPP reductions and broadcast with readlane.  grid (n_q, H/4), 256 threads.
-// n_splits <= 64.
-__device__ __forceinline__ float wave_max_dpp(float v) {
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-}
-
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return (r0 + r1) + (r2 + r3);
-}
-
-__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part, int n_splits,
-                                                      int H, float* __restrict__ out,
-                                                      float* __restrict__ lse) {
-    constexpr int kChunk = 16;  // splits whose channels are loaded per round
-    const int lane = threadIdx.x & 63;
-    const int64_t bq = blockIdx.x;
-    const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
-    const int64_t sstride = (int64_t)H * (kHeadDim + 2);
-    const float* base = part + (bq * n_splits * H + h) * (kHeadDim + 2);
-    float m = -INFINITY, l = 0.0f;
-    if (lane < n_splits) {
-        m = base[lane * sstride + kHeadDim];
-        l = base[lane * sstride + kHeadDim + 1];
-    }
-    float2 v[kChunk];
+    __syncthreads();
+    for (int item = tid; item < kGroupHeads * (kHeadDim / 4); item += kThreads) {
+        const int hh = item / (kHeadDim / 4), d4 = item % (kHeadDim / 4);
+        float M = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < kChunk; ++s)
-        v[s] = s < n_splits ? *reinterpret_cast<const float2*>(base + s * sstride + 2 * lane)
-                            : make_float2(0.0f, 0.0f);
-    const float M = wave_max_dpp(m);
-    const float w = (M != -INFINITY && lane < n_splits) ? exp2f(m - M) : 0.0f;  // m = -inf -> 0
-    const float L = wave_sum_dpp(l * w);
-    float2 acc = make_float2(0.0f, 0.0f);
-    for (int s0 = 0; s0 < n_splits; s0 += kChunk) {
-        if (s0 > 0) {
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mm[w * kGroupHeads + hh]);
+        float L = 0.0f;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (M != -INFINITY) {
 #pragma unroll
-            for (int s = 0; s < kChunk; ++s)
-                v[s] = s0 + s < n_splits
-                           ? *reinterpret_cast<const float2*>(base + (s0 + s) * sstride + 2 * lane)
-                           : make_float2(0.0f, 0.0f);
+            for (int w = 0; w < kWaves; ++w) {
+                const float mw = mm[w * kGroupHeads + hh];
+                const float wt = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+                L += wt * ml[w * kGroupHeads + hh];
+                const float4 ow = *reinterpret_cast<const float4*>(
+                    mo + (w * kGroupHeads + hh) * kMergePitch + 4 * d4);
+                acc.x += wt * ow.x;
+                acc.y += wt * ow.y;
+                acc.z += wt * ow.z;
+                acc.w += wt * ow.w;
+            }
         }
-#pragma unroll
-        for (int s = 0; s < kChunk; ++s) {
-            const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s0 + s));
-            acc.x += v[s].x * ws;
-            acc.y += v[s].y * ws;
-        }
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        const int64_t oh = bq * a.H + hg * kGroupHeads + hh;
+        *reinterpret_cast<float4*>(a.out + oh * kHeadDim + 4 * d4) =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+        if (d4 == 0) a.lse[oh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
     }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    *reinterpret_cast<float2*>(out + (bq * H + h) * kHeadDim + 2 * lane) =
-        make_float2(acc.x * inv, acc.y * inv);
-    if (lane == 0) lse[bq * H + h] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
-hipError_t launch_attn(const AttnArgs& a, void* ws, size_t, hipStream_t stream) {
-    const SplitPlan plan = plan_splits(a.n_q, a.topk, a.swa_rows);
-    float* part = static_cast<float*>(ws);
-    dim3 grid((unsigned)plan.n_splits, (unsigned)a.n_q);
-    const int nw = (a.H + 15) / 16;
-    switch (nw) {
-        case 1: hipLaunchKernelGGL(k_attn<1>, grid, dim3(64), 0, stream, a, plan, part); break;
-        case 2: hipLaunchKernelGGL(k_attn<2>, grid, dim3(128), 0, stream, a, plan, part); break;
-        case 3: hipLaunchKernelGGL(k_attn<3>, grid, dim3(192), 0, stream, a, plan, part); break;
-        case 4: hipLaunchKernelGGL(k_attn<4>, grid, dim3(256), 0, stream, a, plan, part); break;
-        case 5: hipLaunchKernelGGL(k_attn<5>, grid, dim3(320), 0, stream, a, plan, part); break;
-        case 6: hipLaunchKernelGGL(k_attn<6>, grid, dim3(384), 0, stream, a, plan, part); break;
-        case 7: hipLaunchKernelGGL(k_attn<7>, grid, dim3(448), 0, stream, a, plan, part); break;
-        default: hipLaunchKernelGGL(k_attn<8>, grid, dim3(512), 0, stream, a, plan, part); break;
-    }
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess || plan.n_splits == 1) return err;
-    hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)a.n_q, (unsigned)(a.H / 4)), dim3(256), 0,
-                       stream, part, plan.n_splits, a.H, a.out, a.lse);
+hipError_t launch_attn(const AttnArgs& a, void* /*ws*/, size_t /*ws_bytes*/, hipStream_t stream) {
+    if (a.n_q <= 0) return hipSuccess;
+    if (a.topk > kMaxTopk || a.swa_rows > kMaxWindow || a.H % kGroupHeads != 0)
+        return hipErrorInvalidValue;
+    const int n_tiles_global = (a.topk + kTile - 1) / kTile;
+    const int G = a.H / kGroupHeads;
+    const int64_t rounds = (a.n_q + kXcds - 1) / kXcds;
+    const unsigned grid = (unsigned)(rounds * kXcds * G);
+    hipLaunchKernelGGL(k_attn, dim3(grid), dim3(kThreads), 0, stream, a, n_tiles_global);
     return hipGetLastError();
 }
 

@@ -96,7 +96,6 @@ def test_attention_validation(lib):
     assert call(topk=4096) == -2
     assert call(sm=float("nan")) == -1
     assert call(swa_len=None) == -1
-    assert call(ws=None) == -3
     c = lib.csa2_sparse_attn_chunk
     assert c(FAKE, 1, 128, 40, FAKE, FAKE, 4096, FAKE, 512, FAKE, FAKE, FAKE, FAKE,
              ctypes.c_float(0.088), FAKE, FAKE, FAKE, 1 << 40, None) == -2
@@ -112,4 +111,5 @@ def test_workspace_sizes(lib):
     assert ws(2, 16, 1, 131072, 512, 2048, 0) >= 16 * 2048 * 8 * 4
     assert ws(1, 16, 1, 1000, 512, 2048, 0) == big
     assert ws(99, 1, 1, 64, 1, 1, 16) == big
-    assert ws(3, 16, 1, 131072, 512, 0, 64) > 0               # split-K partials
+    assert ws(3, 16, 1, 131072, 512, 0, 64) == 0              # attention needs no workspace
+    assert ws(4, 1, 128, 131072, 512, 0, 64) == 0
