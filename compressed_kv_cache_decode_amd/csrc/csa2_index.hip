@@ -176,6 +176,7 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kSelRegSlots = 16384;             // slots held in registers
 constexpr int kSelBins = 2048;
+static_assert(kSelBins >= kMaxTopk, "the histogram area stages a top-K row");
 
 struct SelShared {
     uint32_t hist[kSelBins + 3 * 16 + 16 + 2];  // also holds the register path's state
@@ -204,6 +205,36 @@ struct KeySrc {
     }
     __device__ __forceinline__ int32_t index(int64_t s) const {
         return kind == 0 ? (int32_t)s : pool[s >> 3] * kBlock + (int32_t)(s & 7);
+    }
+    // keys of the 16 slots s0 .. s0 + 15 (s0 a multiple of 16; 0 past n)
+    __device__ __forceinline__ void load16(int64_t s0, uint32_t (&k)[16]) const {
+        if (kind == 1) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int64_t sb = s0 + 8 * j;
+                const int32_t blk = sb < n ? pool[sb >> 3] : -1;
+                const int64_t pos = (int64_t)blk * kBlock;
+                if (blk >= 0 && pos + kBlock <= nv) {
+                    const uint4 a = *reinterpret_cast<const uint4*>(src + pos);
+                    const uint4 b = *reinterpret_cast<const uint4*>(src + pos + 4);
+                    k[8 * j + 0] = a.x; k[8 * j + 1] = a.y; k[8 * j + 2] = a.z; k[8 * j + 3] = a.w;
+                    k[8 * j + 4] = b.x; k[8 * j + 5] = b.y; k[8 * j + 6] = b.z; k[8 * j + 7] = b.w;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        k[8 * j + i] = (blk >= 0 && pos + i < nv) ? src[pos + i] : 0u;
+                }
+            }
+        } else if (s0 + 16 <= n) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint4 a = *reinterpret_cast<const uint4*>(src + s0 + 4 * j);
+                k[4 * j + 0] = a.x; k[4 * j + 1] = a.y; k[4 * j + 2] = a.z; k[4 * j + 3] = a.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) k[i] = s0 + i < n ? src[s0 + i] : 0u;
+        }
     }
 };
 
@@ -368,10 +399,11 @@ __device__ __forceinline__ void compact(const KeySrc& ks, const uint32_t* reg, c
 }
 
 // ---------------------------------------------------------------------------
-// Register path (at most 16384 slots): lane l of wave w holds the keys of
-// slots w*1024 + 64 i + l, i < 16, so every sweep is 16 unrolled register
-// operations, wave-wide sums are DPP scans, and the bin search is spread
-// over all 1024 threads.
+// Register path (at most 16384 slots): lane l of wave w holds the keys of the
+// 16 consecutive slots w*1024 + 16 l .. +15, so its keys load as 16-byte
+// vectors, wave-wide sums are DPP scans, the bin search is spread over all
+// 1024 threads, and output ranks follow from per-lane prefix counts (slot
+// order is lane order within a wave).
 // ---------------------------------------------------------------------------
 constexpr int kSelKpt = 16;
 
@@ -480,49 +512,77 @@ __device__ __forceinline__ Threshold threshold_reg(const uint32_t (&k)[kSelKpt],
     return Threshold{lo + 1, lo, remaining, (uint32_t)K};  // not reached: width hits 0
 }
 
+// unsigned minimum the optimiser cannot reason about (see compact_reg)
+__device__ __forceinline__ uint32_t umin_opaque(uint32_t a, uint32_t b) {
+    uint32_t r;
+    asm volatile("v_min_u32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// exclusive prefix sum over the 64 lanes
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v) { return wave_incl_scan(v) - v; }
+
+// Indices are ranked into an LDS stage (`lds_out` itself when given, else the
+// histogram area, so K <= 2048 there), then written out in one pass.  Keys
+// above the threshold are all taken; keys equal to it are taken in slot
+// order until the quota is met.
 template <class IDX>
 __device__ __forceinline__ void compact_reg(const uint32_t (&k)[kSelKpt], const Threshold& th,
                                             int K, IDX index_of, int32_t* out, int32_t* lds_out,
                                             SelRegShared& sh) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t c_gt = 0, c_eq = 0;
+    int32_t* stage = lds_out ? lds_out : reinterpret_cast<int32_t*>(sh.hist);
+    uint32_t gtm = 0, eqm = 0;
 #pragma unroll
     for (int i = 0; i < kSelKpt; ++i) {
-        c_gt += __popcll(__ballot(k[i] != 0 && k[i] >= th.t_ge));
-        c_eq += __popcll(__ballot(k[i] != 0 && th.quota != 0 && k[i] == th.t_eq));
+        gtm |= (k[i] != 0 && k[i] >= th.t_ge) ? (1u << i) : 0u;
+        eqm |= (k[i] != 0 && th.quota != 0 && k[i] == th.t_eq) ? (1u << i) : 0u;
     }
+    const uint32_t n_gt = __popc(gtm), n_eq = __popc(eqm);
+    const uint32_t gt_lane = wave_excl_scan(n_gt), eq_lane = wave_excl_scan(n_eq);
+    __syncthreads();  // the threshold search is done with hist / part
+    if (lane == 63) { sh.part[0][wave] = gt_lane + n_gt; sh.part[1][wave] = eq_lane + n_eq; }
     __syncthreads();
-    if (lane == 0) { sh.part[0][wave] = c_gt; sh.part[1][wave] = c_eq; }
-    __syncthreads();
-    uint32_t eq_before = 0, out_before = 0, total = 0, eb = 0;
+    uint32_t gt_before = 0, eq_before = 0, gt_total = 0, eq_total = 0;
 #pragma unroll
     for (int w = 0; w < kSelWaves; ++w) {
-        const uint32_t take_eq = th.quota > eb ? min(th.quota - eb, sh.part[1][w]) : 0u;
-        if (w == wave) { eq_before = eb; out_before = total; }
-        total += sh.part[0][w] + take_eq;
-        eb += sh.part[1][w];
+        const uint32_t a = sh.part[0][w], b = sh.part[1][w];
+        gt_before += w < wave ? a : 0u;
+        eq_before += w < wave ? b : 0u;
+        gt_total += a;
+        eq_total += b;
     }
-    uint32_t eq_seen = 0, taken = 0;
-#pragma unroll
-    for (int i = 0; i < kSelKpt; ++i) {
-        const bool gt = k[i] != 0 && k[i] >= th.t_ge;
-        const bool eq = k[i] != 0 && th.quota != 0 && k[i] == th.t_eq;
-        const uint64_t eq_mask = __ballot(eq);
-        const uint32_t eq_rank = eq_before + eq_seen + lanes_below(eq_mask);
-        const bool take = gt || (eq && eq_rank < th.quota);
-        const uint64_t tk_mask = __ballot(take);
-        const uint32_t rank = out_before + taken + lanes_below(tk_mask);
-        if (take && rank < (uint32_t)K) {
-            const int32_t v = index_of(wave * 1024 + 64 * i + lane);
-            if (out) out[rank] = v;
-            if (lds_out) lds_out[rank] = v;
-        }
-        eq_seen += __popcll(eq_mask);
-        taken += __popcll(tk_mask);
+    const uint32_t eq_off = eq_before + eq_lane;  // equal keys in earlier slots
+    // Equal keys are taken in slot order until the quota is met: this lane
+    // takes min(q, eq_off + n_eq) - min(q, eq_off) of them, after
+    // min(q, eq_off) taken in earlier slots.  The minima are explicit
+    // v_min_u32: with plain min() and a comparison here, this compiler
+    // (ROCm 7.2 clang, gfx950) folded both as if eq_off <= q always held,
+    // which mis-ranks the keys after an untaken tie.
+    const uint32_t eq_taken_before = umin_opaque(th.quota, eq_off);
+    uint32_t eq_take = umin_opaque(th.quota, eq_off + n_eq) - eq_taken_before;
+    uint32_t rank = gt_before + gt_lane + eq_taken_before;
+    const uint32_t total = gt_total + umin_opaque(th.quota, eq_total);
+    // taken slots: every key above the threshold plus the first eq_take
+    // equal ones; visit only the set bits (a wave loops as often as its
+    // busiest lane takes keys)
+    uint32_t takem = gtm, em = eqm;
+    for (; eq_take != 0 && em != 0; --eq_take) {
+        takem |= em & (0u - em);
+        em &= em - 1u;
     }
-    for (int i = (int)total + tid; i < K; i += kSelThreads) {
-        if (out) out[i] = -1;
-        if (lds_out) lds_out[i] = -1;
+    while (takem != 0) {
+        const int i = __builtin_ctz(takem);
+        if (rank < (uint32_t)K) stage[rank] = index_of(wave * 1024 + 16 * lane + i);
+        ++rank;
+        takem &= takem - 1u;
+    }
+    // one coalesced pass writes the row
+    __syncthreads();
+    for (int i = tid; i < K; i += kSelThreads) {
+        const int32_t v = i < (int)total ? stage[i] : -1;
+        if (out) out[i] = v;
+        if (lds_out) lds_out[i] = v;
     }
 }
 
@@ -533,11 +593,7 @@ __device__ __forceinline__ void select_into(const KeySrc& ks, int K, int32_t* ou
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (ks.n <= kSelRegSlots) {
         uint32_t k[kSelKpt];
-#pragma unroll
-        for (int i = 0; i < kSelKpt; ++i) {
-            const int64_t s = (int64_t)wave * 1024 + 64 * i + lane;
-            k[i] = s < ks.n ? ks.key(s) : 0u;
-        }
+        ks.load16((int64_t)wave * 1024 + 16 * lane, k);
         SelRegShared& rs = *reinterpret_cast<SelRegShared*>(&sh.hist[0]);
         const Threshold th = threshold_reg(k, K, rs);
         compact_reg(k, th, K, [&](int64_t s) { return ks.index(s); }, out, lds_out, rs);

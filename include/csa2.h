@@ -211,7 +211,8 @@ int csa2_index_reindex(const uint8_t* ik_codes, const float* ik_sigma, int64_t c
  * logit = sm_scale * q . k over the union of selected entries
  * (k = E2M1 * E4M3 scale) and window tokens (k = sigma * E4M3); one softmax
  * over the union; out = sum p v / sum p.  No keys -> out 0, lse -inf.
- * ws: at least csa2_workspace_size(CSA2_OP_ATTN_DECODE, B, 1, cap, topk, 0, H).
+ * ws: csa2_workspace_size(CSA2_OP_ATTN_DECODE, B, 1, cap, topk, 0, H) bytes,
+ * currently 0 (ws may then be NULL); kept so that a later kernel may use one.
  */
 int csa2_sparse_attn_decode(const float* q, int B, int H, const uint8_t* kv_codes,
                             const uint8_t* kv_scales, int64_t cap, const int32_t* topk_idx,
@@ -229,7 +230,8 @@ int csa2_sparse_attn_decode(const float* q, int B, int H, const uint8_t* kv_code
  *   swa_k, swa_v    [B][Q][128] E4M3, the chunk's own tokens; swa_ks,
  *              swa_vs [B][Q].  Query i attends to chunk tokens [0, i].
  *   out [B][Q][H][128], lse [B][Q][H].  Otherwise as the decode call.
- * ws: at least csa2_workspace_size(CSA2_OP_ATTN_CHUNK, B, Q, cap, topk, 0, H).
+ * ws: csa2_workspace_size(CSA2_OP_ATTN_CHUNK, B, Q, cap, topk, 0, H) bytes
+ * (currently 0; ws may then be NULL).
  */
 int csa2_sparse_attn_chunk(const float* q, int B, int Q, int H, const uint8_t* kv_codes,
                            const uint8_t* kv_scales, int64_t cap, const int32_t* topk_idx,
