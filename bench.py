@@ -14,9 +14,16 @@ served from the 256 MB last-level cache.
 
 Prints ONE JSON line on stdout (progress goes to stderr):
   value       = sequences (decode queries) per second through the whole stack
-  roofline    = the Full-layer scan kernel (the only one whose work grows with
-                context): algorithmic bytes (68 B per visible position) over
-                its mean duration from HIP events, against 8 TB/s
+  rooflines   = per timed kernel: algorithmic bytes per launch over its mean
+                duration from HIP events recorded around its own dispatch,
+                against 8 TB/s -- the sparse attention (launched once per
+                layer) and the Full-layer scan (the only kernel whose work
+                grows with context)
+  roofline    = the entry of `rooflines` that takes the most time per step;
+                `traffic` = measured HBM bytes per launch (FETCH_SIZE +
+                WRITE_SIZE counters scaled by a copy kernel of known size, from
+                profiles/traffic.json), or null when those counters were taken
+                on a different version of the kernel's source
   cpu_baseline= the CPU oracle on a bounded sample of the same workload
 """
 import argparse
@@ -46,6 +53,9 @@ def parse_args():
     p.add_argument("--cpu-seqs", type=int, default=0,
                    help="sequences in the CPU-oracle sample (0 = one whole batch)")
     p.add_argument("--skip-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration-mb", type=int, default=0,
+                   help="also run one device-to-device copy of this many MiB (a known-size "
+                        "kernel for scaling hardware byte counters)")
     return p.parse_args()
 
 
@@ -79,7 +89,7 @@ class StepSet:
         self.inp = {k: v.clone() for k, v in dev_inputs.items()}
         self.csa2 = csa2
 
-    def run(self, scan_timer=None):
+    def run(self, scan_timer=None, attn_timer=None):
         c, i = self.csa2, self.inp
         # write path of the new token of every sequence (position n_ent - 1)
         c.quant_fp4(i["k_new"], i["v_new"], self.cache.kv_codes, self.cache.kv_scales,
@@ -87,7 +97,7 @@ class StepSet:
         c.quant_fp8(i["idx_new"], self.cache.ik_codes, self.cache.ik_sigma,
                     layout=c.FP8_IDX_TILED, dst_rows=i["rows_new"])
         self.stack.step(i["iq"], i["iw"], i["n_vis"], i["q"], i["swk"], i["swv"], i["sks"],
-                        i["svs"], i["swa_len"], scan_timer=scan_timer)
+                        i["svs"], i["swa_len"], scan_timer=scan_timer, attn_timer=attn_timer)
 
 
 def build_sets(args, wl, inp):
@@ -186,19 +196,22 @@ def time_gpu(args, wl, csa2, sets):
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
 
-        # the dominant kernel, timed with HIP events around its own dispatch
+        # per-kernel durations, HIP events recorded around each kernel's own dispatch
         timer = csa2.KernelTimer(args.steps)
+        attn_timer = csa2.KernelTimer(args.steps * len(wl.plan))
         for i in range(args.steps):
-            sets[i % len(sets)].run(scan_timer=timer)
+            sets[i % len(sets)].run(scan_timer=timer, attn_timer=attn_timer)
         torch.cuda.synchronize()
         scan_ms = timer.durations_ms()
+        attn_ms = attn_timer.durations_ms()
         timer.close()
+        attn_timer.close()
         t1 = time.perf_counter()
         for i in range(args.steps):
             sets[i % len(sets)].run()
         torch.cuda.synchronize()
         eager_elapsed = time.perf_counter() - t1
-    return elapsed, scan_ms, eager_elapsed
+    return elapsed, {"scan": scan_ms, "attn": attn_ms}, eager_elapsed
 
 
 # --------------------------------------------------------------------------- CPU baseline
@@ -256,6 +269,64 @@ def cpu_baseline(args, wl, inp):
             "seconds": dt}
 
 
+def roofline_entry(name, what, ms_list, bytes_per_launch, launches_per_step, ms_per_step,
+                   traffic):
+    mean_ms = sum(ms_list) / len(ms_list)
+    gbs = bytes_per_launch / (mean_ms * 1e-3) / 1e9
+    t = traffic.get(name)
+    return {"kernel": f"{name} ({what})", "bound": "hbm", "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": t, "bytes_per_launch": bytes_per_launch,
+            "mean_us": round(mean_ms * 1e3, 2), "launches_per_step": launches_per_step,
+            "us_per_step": round(mean_ms * 1e3 * launches_per_step, 1),
+            "share_of_step": round(mean_ms * launches_per_step / ms_per_step, 3)}
+
+
+# sources each kernel's counters depend on (the counters are void once these change)
+KERNEL_SOURCES = {
+    "k_attn": ["csa2_attn.hip", "csa2_device.hpp", "csa2_internal.hpp"],
+    "k_scan": ["csa2_index.hip", "csa2_device.hpp", "csa2_internal.hpp"],
+}
+
+
+def kernel_source_hash(name):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[name]:
+        with open(os.path.join(ROOT, "compressed_kv_cache_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def load_traffic():
+    """Measured HBM bytes per launch from profiles/traffic.json, per kernel, kept
+    only where the kernel's sources still hash to what was profiled."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as fh:
+        data = json.load(fh)
+    out = {}
+    for name, rec in data.get("kernels", {}).items():
+        if name in KERNEL_SOURCES and rec.get("source_sha256") == kernel_source_hash(name):
+            out[name] = rec["bytes_per_launch"]
+    return out
+
+
+def copy_calibration(mib):
+    """One device-to-device copy of `mib` MiB: a kernel of known traffic
+    (reads and writes mib MiB each) for scaling the hardware byte counters."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {mib} MiB device-to-device")
+    del src, dst
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -276,13 +347,22 @@ def main():
     log(f"workload {wl.name}: drawing inputs (seed {wl.seed})")
     inp = synth.decode_inputs(wl)
     csa2, sets = build_sets(args, wl, inp)
-    elapsed, scan_ms, eager_elapsed = time_gpu(args, wl, csa2, sets)
+    if args.copy_calibration_mb:
+        copy_calibration(args.copy_calibration_mb)
+    elapsed, kernel_ms, eager_elapsed = time_gpu(args, wl, csa2, sets)
 
     total_bytes, scan_bytes = step_bytes(wl)
     ms_per_step = elapsed / args.steps * 1e3
     value = wl.B * args.steps / elapsed
-    scan_mean = sum(scan_ms) / len(scan_ms)
-    scan_gbs = scan_bytes / (scan_mean * 1e-3) / 1e9
+    attn_launch_bytes = wl.B * attn_bytes(min(wl.topk, wl.n_ent), 128, wl.H)
+    traffic = load_traffic()
+    rooflines = [
+        roofline_entry("k_attn", "sparse attention, one launch per layer", kernel_ms["attn"],
+                       attn_launch_bytes, len(wl.plan), ms_per_step, traffic),
+        roofline_entry("k_scan", "Full-layer indexer scan", kernel_ms["scan"], scan_bytes, 1,
+                       ms_per_step, traffic),
+    ]
+    dominant = max(rooflines, key=lambda r: r["us_per_step"])
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -300,10 +380,10 @@ def main():
                    "layers": len(wl.plan), "plan": wl.plan, "heads": wl.H, "topk": wl.topk,
                    "pool_blocks": wl.pool_blocks, "window": 128, "cache_sets": args.cache_sets,
                    "launch": "eager" if args.no_graph else "hip-graph"},
-        "roofline": {"bound": "hbm", "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "k_scan (Full-layer indexer scan)",
-                     "bytes_per_launch": scan_bytes, "mean_us": round(scan_mean * 1e3, 2)},
+        "roofline": {k: dominant[k] for k in ("bound", "achieved", "peak", "unit", "frac",
+                                               "traffic", "kernel", "bytes_per_launch",
+                                               "mean_us")},
+        "rooflines": rooflines,
         "step": {"algorithmic_bytes": total_bytes,
                  "achieved_GBps": round(total_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                  "frac_of_hbm_peak": round(total_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -42,7 +42,8 @@ STATUS = {0: "ok", -1: "CSA2_E_ARG", -2: "CSA2_E_UNSUPPORTED", -3: "CSA2_E_WORKS
 
 EXPORTS = ("csa2_quant_fp4", "csa2_quant_fp8", "csa2_index_full", "csa2_index_full_timed",
            "csa2_index_reindex",
-           "csa2_sparse_attn_decode", "csa2_sparse_attn_chunk", "csa2_workspace_size",
+           "csa2_sparse_attn_decode", "csa2_sparse_attn_decode_timed", "csa2_sparse_attn_chunk",
+           "csa2_workspace_size",
            "csa2_status_str", "csa2_abi_version", "csa2_codec_probe")
 
 _lib = None
@@ -59,6 +60,9 @@ _SIGS = {
                                   _vp, _vp, _sz, _vp]),
     "csa2_sparse_attn_decode": (_int, [_vp, _int, _int, _vp, _vp, _i64, _vp, _int, _vp, _vp, _vp,
                                        _vp, _vp, _f, _vp, _vp, _vp, _sz, _vp]),
+    "csa2_sparse_attn_decode_timed": (_int, [_vp, _int, _int, _vp, _vp, _i64, _vp, _int, _vp, _vp,
+                                             _vp, _vp, _vp, _f, _vp, _vp, _vp, _sz, _vp, _vp,
+                                             _vp]),
     "csa2_sparse_attn_chunk": (_int, [_vp, _int, _int, _int, _vp, _vp, _i64, _vp, _int, _vp, _vp,
                                       _vp, _vp, _f, _vp, _vp, _vp, _sz, _vp]),
     "csa2_workspace_size": (_sz, [_int, _int, _int, _i64, _int, _int, _int]),
@@ -236,16 +240,18 @@ def index_reindex(cache, iq, iw, n_vis, pool_idx, topk_idx, topk=DEFAULT_TOPK, w
 
 
 def sparse_attn_decode(q, cache, topk_idx, swa_k, swa_v, swa_ks, swa_vs, swa_len, out, lse,
-                       sm_scale=None, ws=None, stream=None):
+                       sm_scale=None, ws=None, stream=None, timer=None):
     """q [B][H][128] f32; topk_idx [B][topk]; swa_k/v [B][128][128] u8; swa_ks/vs [B][128];
-    swa_len [B] i32 -> out [B][H][128], lse [B][H]."""
+    swa_len [B] i32 -> out [B][H][128], lse [B][H].
+    timer: optional KernelTimer; its next event pair brackets the kernel's dispatch."""
     B, H = q.shape[0], q.shape[1]
     topk = topk_idx.shape[-1]
     sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else sm_scale
     need = workspace_size(OP_ATTN_DECODE, B, 1, cache.cap, topk, 0, H)
     if ws is None and need:
         ws = alloc_workspace(need, q.device)
-    rc = lib().csa2_sparse_attn_decode(
+    ev = timer.next_pair() if timer is not None else (None, None)
+    rc = lib().csa2_sparse_attn_decode_timed(
         _ptr(q, torch.float32, "q", B * H * HEAD_DIM), B, H,
         _ptr(cache.kv_codes, torch.uint8, "kv_codes"), _ptr(cache.kv_scales, torch.uint8, "kv_scales"),
         cache.cap, _ptr(topk_idx, torch.int32, "topk_idx", B * topk), topk,
@@ -256,7 +262,7 @@ def sparse_attn_decode(q, cache, topk_idx, swa_k, swa_v, swa_ks, swa_vs, swa_len
         _ptr(swa_len, torch.int32, "swa_len", B), sm,
         _ptr(out, torch.float32, "out", B * H * HEAD_DIM), _ptr(lse, torch.float32, "lse", B * H),
         _ptr(ws, torch.uint8, "ws") if ws is not None else None,
-        ws.numel() if ws is not None else 0, _stream(stream))
+        ws.numel() if ws is not None else 0, _stream(stream), ev[0], ev[1])
     _check(rc, "csa2_sparse_attn_decode")
 
 

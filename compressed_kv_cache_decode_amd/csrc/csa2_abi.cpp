@@ -232,11 +232,12 @@ __attribute__((visibility("default"))) int csa2_index_reindex(
     return hip_status(e);
 }
 
-__attribute__((visibility("default"))) int csa2_sparse_attn_decode(
+__attribute__((visibility("default"))) int csa2_sparse_attn_decode_timed(
     const float* q, int B, int H, const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t cap,
     const int32_t* topk_idx, int topk, const uint8_t* swa_k, const uint8_t* swa_v,
     const float* swa_ks, const float* swa_vs, const int32_t* swa_len, float sm_scale, float* out,
-    float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+    float* lse, void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t start,
+    hipEvent_t stop) {
     int rc = validate_attn(q, B, 1, H, kv_codes, kv_scales, cap, topk_idx, topk, swa_k, swa_v,
                            swa_ks, swa_vs, sm_scale, out, lse);
     if (rc) return rc;
@@ -245,7 +246,17 @@ __attribute__((visibility("default"))) int csa2_sparse_attn_decode(
     if (need > 0 && (!ws || ws_bytes < need)) return CSA2_E_WORKSPACE;
     AttnArgs a{q, H, 1, kv_codes, kv_scales, cap, topk_idx, topk, swa_k, swa_v, swa_ks, swa_vs,
                swa_len, CSA2_WINDOW, sm_scale, out, lse, (int64_t)B};
-    return hip_status(launch_attn(a, ws, ws_bytes, stream));
+    return hip_status(launch_attn(a, ws, ws_bytes, stream, start, stop));
+}
+
+__attribute__((visibility("default"))) int csa2_sparse_attn_decode(
+    const float* q, int B, int H, const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t cap,
+    const int32_t* topk_idx, int topk, const uint8_t* swa_k, const uint8_t* swa_v,
+    const float* swa_ks, const float* swa_vs, const int32_t* swa_len, float sm_scale, float* out,
+    float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return csa2_sparse_attn_decode_timed(q, B, H, kv_codes, kv_scales, cap, topk_idx, topk, swa_k,
+                                         swa_v, swa_ks, swa_vs, swa_len, sm_scale, out, lse, ws,
+                                         ws_bytes, stream, nullptr, nullptr);
 }
 
 __attribute__((visibility("default"))) int csa2_sparse_attn_chunk(

@@ -38,6 +38,8 @@
 // bytes in flight.  Workgroups are numbered so that the head groups of one
 // query land on the same XCD (consecutive workgroup ids go round-robin over
 // the 8 XCDs), sharing its L2 for the gathered rows.
+#include <hip/hip_ext.h>
+
 #include "csa2_device.hpp"
 #include "csa2_internal.hpp"
 
@@ -503,7 +505,8 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a, int n_tiles_globa
     }
 }
 
-hipError_t launch_attn(const AttnArgs& a, void* /*ws*/, size_t /*ws_bytes*/, hipStream_t stream) {
+hipError_t launch_attn(const AttnArgs& a, void* /*ws*/, size_t /*ws_bytes*/, hipStream_t stream,
+                       hipEvent_t start, hipEvent_t stop) {
     if (a.n_q <= 0) return hipSuccess;
     if (a.topk > kMaxTopk || a.swa_rows > kMaxWindow || a.H % kGroupHeads != 0)
         return hipErrorInvalidValue;
@@ -511,7 +514,13 @@ hipError_t launch_attn(const AttnArgs& a, void* /*ws*/, size_t /*ws_bytes*/, hip
     const int G = a.H / kGroupHeads;
     const int64_t rounds = (a.n_q + kXcds - 1) / kXcds;
     const unsigned grid = (unsigned)(rounds * kXcds * G);
-    hipLaunchKernelGGL(k_attn, dim3(grid), dim3(kThreads), 0, stream, a, n_tiles_global);
+    if (start != nullptr && stop != nullptr) {
+        // the runtime records `start` / `stop` immediately around this dispatch
+        hipExtLaunchKernelGGL(k_attn, dim3(grid), dim3(kThreads), 0, stream, start, stop, 0, a,
+                              n_tiles_global);
+    } else {
+        hipLaunchKernelGGL(k_attn, dim3(grid), dim3(kThreads), 0, stream, a, n_tiles_global);
+    }
     return hipGetLastError();
 }
 

@@ -56,6 +56,7 @@ struct AttnArgs {
 };
 
 size_t attn_workspace_bytes(int64_t n_q, int H, int topk, int swa_rows);
-hipError_t launch_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
+hipError_t launch_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t stream,
+                       hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 }  // namespace csa2

@@ -61,13 +61,14 @@ class DecodeStack:
         self.sources = reuse_sources(plan)
 
     def step(self, iq, iw, n_vis, q, swa_k, swa_v, swa_ks, swa_vs, swa_len, stream=None,
-             scan_timer=None):
+             scan_timer=None, attn_timer=None):
         """One decode step.
 
         iq [n_idx][B][1][4][64], iw [n_idx][B][1][4]: one indexer query per
         Full/Reindex layer; n_vis [B][1] int32; q [L][B][H][128];
         swa_k/v [L][B][128][128] u8, swa_ks/vs [L][B][128] f32, swa_len [B].
-        scan_timer: optional KernelTimer bracketing the Full layer's scan.
+        scan_timer: optional KernelTimer bracketing the Full layer's scan;
+        attn_timer: optional KernelTimer bracketing every layer's attention kernel.
         Returns the list of top-K buffers each layer attended with."""
         used, cur, k = [], None, 0
         for layer, mode in enumerate(self.plan):
@@ -83,6 +84,7 @@ class DecodeStack:
                 cur, k = self.topk_bufs[k], k + 1
             sparse_attn_decode(q[layer], self.cache, cur.view(self.B, self.topk), swa_k[layer],
                                swa_v[layer], swa_ks[layer], swa_vs[layer], swa_len,
-                               self.out[layer], self.lse[layer], ws=self.ws_attn, stream=stream)
+                               self.out[layer], self.lse[layer], ws=self.ws_attn, stream=stream,
+                               timer=attn_timer)
             used.append(cur)
         return used

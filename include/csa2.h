@@ -222,6 +222,21 @@ int csa2_sparse_attn_decode(const float* q, int B, int H, const uint8_t* kv_code
                             hipStream_t stream);
 
 /*
+ * csa2_sparse_attn_decode_timed -- csa2_sparse_attn_decode, with the HIP
+ * events `start` and `stop` (created by the caller, hipEventDefault) recorded
+ * by the runtime immediately before and after the attention kernel's own
+ * dispatch, so hipEventElapsedTime(start, stop) is that kernel's duration.
+ * NULL events: identical to csa2_sparse_attn_decode.
+ */
+int csa2_sparse_attn_decode_timed(const float* q, int B, int H, const uint8_t* kv_codes,
+                                  const uint8_t* kv_scales, int64_t cap, const int32_t* topk_idx,
+                                  int topk, const uint8_t* swa_k, const uint8_t* swa_v,
+                                  const float* swa_ks, const float* swa_vs,
+                                  const int32_t* swa_len, float sm_scale, float* out, float* lse,
+                                  void* ws, size_t ws_bytes, hipStream_t stream,
+                                  hipEvent_t start, hipEvent_t stop);
+
+/*
  * csa2_sparse_attn_chunk -- attention of a Q-token bounded-replay chunk
  * ("DeepSeek V4.1 Flash: architecture study notes" section 5: the decoder
  * replays only the last 128 tokens of the prompt to rebuild its SWA state;
