@@ -108,6 +108,96 @@ __global__ __launch_bounds__(256) void k_scan(const uint8_t* __restrict__ ikc,
 }
 
 // ---------------------------------------------------------------------------
+// Full-layer scan for many queries per sequence (the replay chunk).  Same
+// scores, bit for bit, as k_scan; the position's key row is converted to fp32
+// once and the queries are staged in LDS, 32 at a time, so every lane reads the
+// query values as LDS broadcasts.  grid = (ceil(cap / 256), B), 256 threads.
+// ---------------------------------------------------------------------------
+constexpr int kScanQChunk = 32;
+
+__global__ __launch_bounds__(256) void k_scan_multi(const uint8_t* __restrict__ ikc,
+                                                    const float* __restrict__ iks, int64_t cap,
+                                                    int Q, const float* __restrict__ qd,
+                                                    const float* __restrict__ wq,
+                                                    const int32_t* __restrict__ n_vis,
+                                                    uint32_t* __restrict__ keys,
+                                                    uint32_t* __restrict__ bkeys) {
+    __shared__ __attribute__((aligned(16))) float sq[kScanQChunk * kIdxHeads * kIdxDim];
+    __shared__ float sw[kScanQChunk * kIdxHeads];
+    const int b = blockIdx.y;
+    const int64_t p0 = (int64_t)blockIdx.x * 256;
+    const int64_t p = p0 + threadIdx.x;
+    int nv_max = 0;
+    for (int q = 0; q < Q; ++q) nv_max = max(nv_max, clamp_nvis(n_vis[(int64_t)b * Q + q], cap));
+    if (p0 >= nv_max) return;  // uniform over the block
+    // cap is a multiple of 64: a wave is wholly inside or wholly past it; waves
+    // past it still take part in the barriers below
+    const bool live = p0 + (threadIdx.x & ~63) < cap;
+
+    float kf[kIdxDim];
+    float sigma = 0.0f;
+    if (live) {
+        const int64_t row = (int64_t)b * cap + p;
+        uint4 raw[4];
+        load_ik_row(ikc, row, raw);
+        sigma = iks[row];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint32_t w[4] = {raw[g].x, raw[g].y, raw[g].z, raw[g].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float2 lo = e4m3x2_to_f32<false>(w[i]);
+                const float2 hi = e4m3x2_to_f32<true>(w[i]);
+                kf[16 * g + 4 * i + 0] = lo.x;
+                kf[16 * g + 4 * i + 1] = lo.y;
+                kf[16 * g + 4 * i + 2] = hi.x;
+                kf[16 * g + 4 * i + 3] = hi.y;
+            }
+        }
+    }
+    const int64_t nb = cap / kBlock;
+    for (int q0 = 0; q0 < Q; q0 += kScanQChunk) {
+        const int nq = min(kScanQChunk, Q - q0);
+        __syncthreads();  // the previous chunk's readers are done
+        const float* src = qd + ((int64_t)b * Q + q0) * kIdxHeads * kIdxDim;
+        for (int i = threadIdx.x; i < nq * kIdxHeads * kIdxDim / 4; i += 256)
+            reinterpret_cast<float4*>(sq)[i] = reinterpret_cast<const float4*>(src)[i];
+        if (threadIdx.x < nq * kIdxHeads)
+            sw[threadIdx.x] = wq[((int64_t)b * Q + q0) * kIdxHeads + threadIdx.x];
+        __syncthreads();
+        if (!live) continue;
+        for (int j = 0; j < nq; ++j) {
+            const int64_t bq = (int64_t)b * Q + q0 + j;
+            const int nv = clamp_nvis(n_vis[bq], cap);
+            if (p0 >= nv) continue;  // uniform
+            // the sequence of IEEE operations of score_row
+            float t = 0.0f;
+#pragma unroll
+            for (int h = 0; h < kIdxHeads; ++h) {
+                const float4* qh = reinterpret_cast<const float4*>(sq + (j * kIdxHeads + h) * kIdxDim);
+                float dot = 0.0f;
+#pragma unroll
+                for (int c4 = 0; c4 < kIdxDim / 4; ++c4) {
+                    const float4 qv = qh[c4];
+                    dot = fmaf(qv.x, kf[4 * c4 + 0], dot);
+                    dot = fmaf(qv.y, kf[4 * c4 + 1], dot);
+                    dot = fmaf(qv.z, kf[4 * c4 + 2], dot);
+                    dot = fmaf(qv.w, kf[4 * c4 + 3], dot);
+                }
+                const float r = dot > 0.0f ? dot : 0.0f;
+                const float wr = sw[j * kIdxHeads + h] * r;
+                t = (h == 0) ? wr : t + wr;
+            }
+            const float score = sigma * t;
+            const uint32_t key = (p < nv) ? score_key(score) : 0u;
+            keys[bq * cap + p] = key;
+            const uint32_t bk = max8_u32(key);
+            if ((threadIdx.x & 7) == 0) bkeys[bq * nb + (p >> 3)] = bk;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Reindex: score the positions of the pool blocks with the layer's own query.
 // grid = (ceil(P*8 / 256), B*Q), 256 threads.  Slot s of query bq is position
 // pool[j]*8 + (s & 7) with j = s / 8; invisible or empty slots get key 0.
@@ -644,12 +734,15 @@ hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B,
                        const float* qd, const float* wq, const int32_t* n_vis, uint32_t* keys,
                        uint32_t* bkeys, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     dim3 grid((unsigned)((cap + 255) / 256), (unsigned)B);
+    // a few queries per sequence: k_scan reads them through the scalar cache;
+    // many (the replay chunk): k_scan_multi stages them in LDS
+    auto kern = Q >= 4 ? k_scan_multi : k_scan;
     if (start != nullptr && stop != nullptr) {
         // the runtime records `start` / `stop` immediately around this dispatch
-        hipExtLaunchKernelGGL(k_scan, grid, dim3(256), 0, stream, start, stop, 0, ikc, iks, cap, Q,
+        hipExtLaunchKernelGGL(kern, grid, dim3(256), 0, stream, start, stop, 0, ikc, iks, cap, Q,
                               qd, wq, n_vis, keys, bkeys);
     } else {
-        hipLaunchKernelGGL(k_scan, grid, dim3(256), 0, stream, ikc, iks, cap, Q, qd, wq, n_vis,
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, ikc, iks, cap, Q, qd, wq, n_vis,
                            keys, bkeys);
     }
     return hipGetLastError();

@@ -121,6 +121,8 @@ def make_idx_cache(gpu, oracle_mod, B, cap, seed, dup_frac=0.0):
     (2, 3, 2048, [[2048, 2047, 1], [0, 999, 1024]], 40, 40),
     (1, 1, 32768, [32765], 512, 2048),            # more blocks than the pool
     (4, 1, 16384, [16384, 16384, 16000, 8], 512, 0),
+    # many queries per sequence (the multi-query scan), ragged visible counts
+    (2, 37, 4096, [[4096 - 13 * i for i in range(37)], [1 + 97 * i for i in range(37)]], 64, 0),
 ])
 def test_index_full_bit_exact(gpu, oracle_mod, B, Q, cap, nvis, topk, pool):
     say(f"index_full B={B} Q={Q} cap={cap} topk={topk} pool={pool}")
