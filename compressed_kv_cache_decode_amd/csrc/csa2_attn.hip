@@ -219,14 +219,16 @@ struct WaveState {
 // The lane's C entries: 4g + i (i < 4) and 16 + 4g + i - 4 (i >= 4).
 __device__ __forceinline__ int c_entry(int i, int g) { return i < 4 ? 4 * g + i : 12 + 4 * g + i; }
 
-// One tile: V into LDS, logits, online softmax, PV.
+// One tile: V into LDS, logits, online softmax, PV.  GLOBAL: a tile of
+// selected FP4 records, else a tile of FP8 window tokens.
+template <bool GLOBAL>
 __device__ __forceinline__ void process_tile(const SeqView& s, int t, const TileRegs& r,
                                              const float* __restrict__ win_l,
                                              const half8_t (&qhi)[4], const half8_t (&qlo)[4],
                                              _Float16* __restrict__ vtile, int lane,
                                              WaveState& st) {
     const int c = lane & 15, g = lane >> 4;
-    const bool global = t < s.n_tiles_global;
+    constexpr bool global = GLOBAL;
 
     // scale bytes come from the lane that loaded the entry's 16-byte chunk:
     // K scales 2g, 2g + 1 of entries c and 16 + c; V scales 2q, 2q + 1 of
@@ -449,11 +451,17 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a, int n_tiles_globa
     _Float16* vtile = reinterpret_cast<_Float16*>(smem + kOffWave + wave * kWaveBytes);
 
     for (int t = t0; t < n_tiles; t += 2 * kWaves) {
-        process_tile(s, t, ra, win_l, qhi, qlo, vtile, lane, st);
+        if (t < n_tiles_global)
+            process_tile<true>(s, t, ra, win_l, qhi, qlo, vtile, lane, st);
+        else
+            process_tile<false>(s, t, ra, win_l, qhi, qlo, vtile, lane, st);
         if (t + 2 * kWaves < n_tiles) fetch_tile(s, t + 2 * kWaves, lane, ra);
         const int u = t + kWaves;
         if (u < n_tiles) {
-            process_tile(s, u, rb, win_l, qhi, qlo, vtile, lane, st);
+            if (u < n_tiles_global)
+                process_tile<true>(s, u, rb, win_l, qhi, qlo, vtile, lane, st);
+            else
+                process_tile<false>(s, u, rb, win_l, qhi, qlo, vtile, lane, st);
             if (u + 2 * kWaves < n_tiles) fetch_tile(s, u + 2 * kWaves, lane, rb);
         }
     }
