@@ -123,6 +123,11 @@ def make_idx_cache(gpu, oracle_mod, B, cap, seed, dup_frac=0.0):
     (4, 1, 16384, [16384, 16384, 16000, 8], 512, 0),
     # many queries per sequence (the multi-query scan), ragged visible counts
     (2, 37, 4096, [[4096 - 13 * i for i in range(37)], [1 + 97 * i for i in range(37)]], 64, 0),
+    # the largest top-K and pool the boundary accepts; 32768 pool positions take
+    # the streaming selection path
+    (1, 1, 65536, [65533], 2048, 4096),
+    # more than 16384 blocks: the block selection streams too
+    (1, 1, 262144, [262141], 512, 2048),
 ])
 def test_index_full_bit_exact(gpu, oracle_mod, B, Q, cap, nvis, topk, pool):
     say(f"index_full B={B} Q={Q} cap={cap} topk={topk} pool={pool}")
@@ -162,7 +167,8 @@ def test_index_full_all_ties(gpu, oracle_mod):
 
 @pytest.mark.parametrize("B,cap,nvis,pool,topk", [(2, 8192, [8192, 5001], 512, 512),
                                                   (3, 32768, [32768, 30000, 77], 2048, 512),
-                                                  (1, 4096, [4096], 64, 100)])
+                                                  (1, 4096, [4096], 64, 100),
+                                                  (1, 65536, [65531], 4096, 2048)])
 def test_index_reindex_bit_exact(gpu, oracle_mod, B, cap, nvis, pool, topk):
     say(f"index_reindex B={B} cap={cap} pool={pool} topk={topk}")
     cache, ikc, iks = make_idx_cache(gpu, oracle_mod, B, cap, 500 + cap, dup_frac=0.1)
@@ -218,6 +224,7 @@ def make_attn_case(gpu, oracle_mod, B, cap, H, seed, Q=1):
     (2, 2048, 32, 100, [77, 128], [100, 3]),
     (4, 1024, 128, 512, [128, 128, 1, 64], [512, 511, 512, 17]),
     (1, 640, 48, 0, [128], [0]),
+    (2, 8192, 128, 2048, [128, 100], [2048, 1500]),   # the largest top-K and head count
 ])
 def test_sparse_attn_decode(gpu, oracle_mod, B, cap, H, topk, swa_len, n_sel):
     say(f"attn_decode B={B} cap={cap} H={H} topk={topk}")
