@@ -65,8 +65,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 // LDS map (bytes)
 constexpr int kWaveBytes = kTile * kVPitch * 2;              // one wave's V tile
 constexpr int kOffQ = 0;                                     // q [16][128] fp32
-constexpr int kOffIdx = kOffQ + kGroupHeads * kHeadDim * 4;  // top-K row, int32 [kMaxTopk]
-constexpr int kOffWin = kOffIdx + kMaxTopk * 4;              // window K scales [128], V scales [128]
+constexpr int kOffWin = kOffQ + kGroupHeads * kHeadDim * 4;  // window K scales [128], V scales [128]
 constexpr int kOffWave = kOffWin + 2 * kMaxWindow * 4;       // per-wave V tiles
 constexpr int kLdsBytes = kOffWave + kWaves * kWaveBytes;
 constexpr int kMergeBytes = (kWaves * kGroupHeads * kMergePitch + 2 * kWaves * kGroupHeads) * 4;
@@ -81,7 +80,7 @@ struct SeqView {
     const uint8_t* kvs;
     const uint8_t* swk;
     const uint8_t* swv;
-    const int32_t* idx_l;  // this query's top-K row, in LDS
+    const int32_t* idx;    // this query's top-K row
     int64_t cap;
     int64_t b;
     int topk;
@@ -90,12 +89,17 @@ struct SeqView {
     int n_tiles_global;
 };
 
-// cache row of entry e of global tile t, or -1
-__device__ __forceinline__ int64_t global_row(const SeqView& s, int t, int e) {
-    const int slot = t * kTile + e;
-    if (slot >= s.topk) return -1;
-    const int32_t p = s.idx_l[slot];
-    return (p >= 0 && p < s.cap) ? s.b * s.cap + p : -1;
+// Position of entry lane % 32 of global tile t, or -1 when absent (slot past
+// topk, or a position outside [0, cap)); lanes 32..63 repeat lanes 0..31.
+__device__ __forceinline__ int32_t tile_position(const SeqView& s, int t, int lane) {
+    const int slot = t * kTile + (lane & (kTile - 1));
+    const int32_t p = slot < s.topk ? s.idx[slot] : -1;
+    return (p >= 0 && p < s.cap) ? p : -1;
+}
+
+// position of entry e of the tile, from the lane that loaded it (or -1)
+__device__ __forceinline__ int32_t entry_position(int32_t pos, int e) {
+    return __builtin_amdgcn_ds_bpermute(e << 2, pos);
 }
 
 // window row of token e of window tile t, or -1
@@ -124,27 +128,30 @@ __device__ __forceinline__ u32x4_t ld16(const uint8_t* p) {
     return *reinterpret_cast<const u32x4_t*>(p);
 }
 
-// Issue the loads of tile t (rows come from LDS, so nothing here waits on HBM).
-__device__ __forceinline__ void fetch_tile(const SeqView& s, int t, int lane, TileRegs& r) {
+// Issue the loads of tile t.  pos: tile_position(s, t, lane) for a global
+// tile (unused for a window tile).
+__device__ __forceinline__ void fetch_tile(const SeqView& s, int t, int32_t pos, int lane,
+                                           TileRegs& r) {
     const int c = lane & 15, g = lane >> 4;
     const u32x4_t z = {0u, 0u, 0u, 0u};
     if (t < s.n_tiles_global) {
+        const int64_t base = s.b * s.cap;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-            const int64_t row = global_row(s, t, 16 * blk + c);
-            r.k[blk][0] = row >= 0 ? ld16(s.kvc + (row >= 0 ? row : 0) * 128 + 16 * g) : z;
+            const int32_t p = entry_position(pos, 16 * blk + c);
+            r.k[blk][0] = p >= 0 ? ld16(s.kvc + (base + (p >= 0 ? p : 0)) * 128 + 16 * g) : z;
             r.k[blk][1] = z;
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int64_t vrow = global_row(s, t, 16 * j + (lane >> 2));
-            r.v[j] = vrow >= 0 ? ld16(s.kvc + (vrow >= 0 ? vrow : 0) * 128 + 64 + 16 * (lane & 3)) : z;
+            const int32_t p = entry_position(pos, 16 * j + (lane >> 2));
+            r.v[j] = p >= 0 ? ld16(s.kvc + (base + (p >= 0 ? p : 0)) * 128 + 64 + 16 * (lane & 3)) : z;
         }
         r.v[2] = z;
         r.v[3] = z;
-        const int64_t srow = lane < kTile ? global_row(s, t, lane) : -1;
-        r.sc = srow >= 0 ? ld16(s.kvs + (srow >= 0 ? srow : 0) * 16) : z;
-        r.valid = (uint32_t)__builtin_amdgcn_ballot_w64(srow >= 0);
+        const bool has = lane < kTile && pos >= 0;
+        r.sc = has ? ld16(s.kvs + (base + (has ? pos : 0)) * 16) : z;
+        r.valid = (uint32_t)__builtin_amdgcn_ballot_w64(has);
     } else {
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
@@ -363,8 +370,20 @@ __device__ __forceinline__ void process_tile(const SeqView& s, int t, const Tile
 // grid = ceil(n_q / 8) * 8 * (H / 16) workgroups of 512 threads.
 // Workgroup id -> (query bq, head group hg): ids with the same id % 8 share an
 // XCD, and all head groups of one query get ids with the same id % 8.
+// Every argument is needed before the first gather; touching them all at
+// kernel entry makes the compiler fetch them in one batch of scalar loads
+// instead of one dependent batch per first use.
+template <class T>
+__device__ __forceinline__ void touch(const T& v) {
+    asm volatile("" ::"s"(v));
+}
+
 __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a, int n_tiles_global) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
+    touch(a.q); touch(a.H); touch(a.Q); touch(a.kvc); touch(a.kvs); touch(a.cap);
+    touch(a.idx); touch(a.topk); touch(a.swk); touch(a.swv); touch(a.swks); touch(a.swvs);
+    touch(a.swa_len); touch(a.swa_rows); touch(a.sm_scale); touch(a.out); touch(a.lse);
+    touch(a.n_q); touch(n_tiles_global);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane & 15, g = lane >> 4;
     const int G = a.H / kGroupHeads;
@@ -375,17 +394,29 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a, int n_tiles_globa
     if (bq >= a.n_q) return;  // uniform over the workgroup
 
     float* q_l = reinterpret_cast<float*>(smem + kOffQ);
-    int32_t* idx_l = reinterpret_cast<int32_t*>(smem + kOffIdx);
     float* win_l = reinterpret_cast<float*>(smem + kOffWin);
 
     SeqView s;
     s.kvc = a.kvc; s.kvs = a.kvs; s.swk = a.swk; s.swv = a.swv;
-    s.idx_l = idx_l;
+    s.idx = a.idx + bq * a.topk;
     s.cap = a.cap;
     s.b = bq / a.Q;
     s.topk = a.topk;
     s.swa_rows = a.swa_rows;
     s.n_tiles_global = n_tiles_global;
+    const float logit_mul = a.sm_scale * kLog2e;
+
+    // ---- each wave starts gathering its first two tiles at once; tiles of
+    // selected records do not wait for the window length ----
+    const int t0 = wave, t1 = wave + kWaves;
+    TileRegs ra, rb;
+    {
+        const int32_t p0 = t0 < n_tiles_global ? tile_position(s, t0, lane) : -1;
+        const int32_t p1 = t1 < n_tiles_global ? tile_position(s, t1, lane) : -1;
+        s.swa_len = 0;  // not read on the path of selected records
+        if (t0 < n_tiles_global) fetch_tile(s, t0, p0, lane, ra);
+        if (t1 < n_tiles_global) fetch_tile(s, t1, p1, lane, rb);
+    }
     if (a.swa_len != nullptr) {
         const int sl = a.swa_len[s.b];
         s.swa_len = sl < 0 ? 0 : (sl > a.swa_rows ? a.swa_rows : sl);
@@ -393,36 +424,21 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a, int n_tiles_globa
         s.swa_len = (int)(bq % a.Q) + 1;  // chunk query i sees window tokens [0, i]
     }
     const int n_tiles = n_tiles_global + (s.swa_len + kTile - 1) / kTile;
-    const float logit_mul = a.sm_scale * kLog2e;
+    if (t0 >= n_tiles_global && t0 < n_tiles) fetch_tile(s, t0, -1, lane, ra);
+    if (t1 >= n_tiles_global && t1 < n_tiles) fetch_tile(s, t1, -1, lane, rb);
 
-    // ---- once per workgroup: q of the 16 heads, the top-K row, window scales ----
+    // ---- meanwhile, once per workgroup: q of the 16 heads, window scales ----
     {
         const float4 qv = reinterpret_cast<const float4*>(
             a.q + (bq * a.H + hg * kGroupHeads) * kHeadDim)[tid];
-        int32_t iv[kMaxTopk / kThreads];
-#pragma unroll
-        for (int k = 0; k < kMaxTopk / kThreads; ++k) {
-            const int j = tid + k * kThreads;
-            iv[k] = j < a.topk ? a.idx[bq * a.topk + j] : -1;
-        }
         float wv = 0.0f;
         const int tok = tid & (kMaxWindow - 1);
         if (tid < 2 * kMaxWindow && tok < s.swa_len)
             wv = (tid < kMaxWindow ? a.swks : a.swvs)[s.b * s.swa_rows + tok];
         reinterpret_cast<float4*>(q_l)[tid] = qv;
-#pragma unroll
-        for (int k = 0; k < kMaxTopk / kThreads; ++k) {
-            const int j = tid + k * kThreads;
-            if (j < a.topk) idx_l[j] = iv[k];
-        }
         if (tid < 2 * kMaxWindow) win_l[tid] = wv;
     }
     __syncthreads();
-
-    const int t0 = wave, t1 = wave + kWaves;
-    TileRegs ra, rb;
-    if (t0 < n_tiles) fetch_tile(s, t0, lane, ra);
-    if (t1 < n_tiles) fetch_tile(s, t1, lane, rb);
 
     // q * sm_scale * log2(e) (so that logits come out in base-2 units) as fp16
     // hi + lo, B-operand layout: head c, MFMA step ks takes channels 32g + 8ks .. +8
@@ -455,14 +471,18 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a, int n_tiles_globa
             process_tile<true>(s, t, ra, win_l, qhi, qlo, vtile, lane, st);
         else
             process_tile<false>(s, t, ra, win_l, qhi, qlo, vtile, lane, st);
-        if (t + 2 * kWaves < n_tiles) fetch_tile(s, t + 2 * kWaves, lane, ra);
+        const int ta = t + 2 * kWaves;
+        if (ta < n_tiles)
+            fetch_tile(s, ta, ta < n_tiles_global ? tile_position(s, ta, lane) : -1, lane, ra);
         const int u = t + kWaves;
         if (u < n_tiles) {
             if (u < n_tiles_global)
                 process_tile<true>(s, u, rb, win_l, qhi, qlo, vtile, lane, st);
             else
                 process_tile<false>(s, u, rb, win_l, qhi, qlo, vtile, lane, st);
-            if (u + 2 * kWaves < n_tiles) fetch_tile(s, u + 2 * kWaves, lane, rb);
+            const int ub = u + 2 * kWaves;
+            if (ub < n_tiles)
+                fetch_tile(s, ub, ub < n_tiles_global ? tile_position(s, ub, lane) : -1, lane, rb);
         }
     }
 
