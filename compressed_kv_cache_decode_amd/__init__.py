@@ -36,13 +36,17 @@ OP_INDEX_FULL = 1
 OP_INDEX_REINDEX = 2
 OP_ATTN_DECODE = 3
 OP_ATTN_CHUNK = 4
+OP_ATTN_STAGE = 5
+STAGE_WRITE = 1
+STAGE_READ = 2
 
 STATUS = {0: "ok", -1: "CSA2_E_ARG", -2: "CSA2_E_UNSUPPORTED", -3: "CSA2_E_WORKSPACE",
           -4: "CSA2_E_HIP"}
 
 EXPORTS = ("csa2_quant_fp4", "csa2_quant_fp8", "csa2_index_full", "csa2_index_full_timed",
            "csa2_index_reindex",
-           "csa2_sparse_attn_decode", "csa2_sparse_attn_decode_timed", "csa2_sparse_attn_chunk",
+           "csa2_sparse_attn_decode", "csa2_sparse_attn_decode_timed",
+           "csa2_sparse_attn_decode_reuse", "csa2_sparse_attn_chunk",
            "csa2_workspace_size",
            "csa2_status_str", "csa2_abi_version", "csa2_codec_probe")
 
@@ -63,6 +67,9 @@ _SIGS = {
     "csa2_sparse_attn_decode_timed": (_int, [_vp, _int, _int, _vp, _vp, _i64, _vp, _int, _vp, _vp,
                                              _vp, _vp, _vp, _f, _vp, _vp, _vp, _sz, _vp, _vp,
                                              _vp]),
+    "csa2_sparse_attn_decode_reuse": (_int, [_vp, _int, _int, _vp, _vp, _i64, _vp, _int, _vp, _sz,
+                                             _int, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp,
+                                             _sz, _vp, _vp, _vp]),
     "csa2_sparse_attn_chunk": (_int, [_vp, _int, _int, _int, _vp, _vp, _i64, _vp, _int, _vp, _vp,
                                       _vp, _vp, _f, _vp, _vp, _vp, _sz, _vp]),
     "csa2_workspace_size": (_sz, [_int, _int, _int, _i64, _int, _int, _int]),
@@ -264,6 +271,44 @@ def sparse_attn_decode(q, cache, topk_idx, swa_k, swa_v, swa_ks, swa_vs, swa_len
         _ptr(ws, torch.uint8, "ws") if ws is not None else None,
         ws.numel() if ws is not None else 0, _stream(stream), ev[0], ev[1])
     _check(rc, "csa2_sparse_attn_decode")
+
+
+def sparse_attn_decode_reuse(q, cache, topk_idx, topk, stage, stage_mode, swa_k, swa_v, swa_ks,
+                             swa_vs, swa_len, out, lse, sm_scale=None, ws=None, stream=None,
+                             timer=None):
+    """sparse_attn_decode for layers sharing one selection.  stage_mode
+    STAGE_WRITE: gather through topk_idx [B][topk] (cache required) and write
+    the staged records to `stage` (u8, workspace_size(OP_ATTN_STAGE, ...)
+    bytes); STAGE_READ: take the records from `stage` (cache and topk_idx may
+    be None)."""
+    B, H = q.shape[0], q.shape[1]
+    sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else sm_scale
+    cap = cache.cap if cache is not None else 1
+    need = workspace_size(OP_ATTN_DECODE, B, 1, cap, topk, 0, H)
+    if ws is None and need:
+        ws = alloc_workspace(need, q.device)
+    if stage_mode == STAGE_WRITE:
+        if cache is None or topk_idx is None:
+            raise ValueError("STAGE_WRITE gathers through the cache: cache and topk_idx needed")
+        if topk_idx.shape[-1] != topk:
+            raise ValueError("topk_idx must be [B][topk]")
+    ev = timer.next_pair() if timer is not None else (None, None)
+    rc = lib().csa2_sparse_attn_decode_reuse(
+        _ptr(q, torch.float32, "q", B * H * HEAD_DIM), B, H,
+        _ptr(cache.kv_codes, torch.uint8, "kv_codes") if cache is not None else None,
+        _ptr(cache.kv_scales, torch.uint8, "kv_scales") if cache is not None else None, cap,
+        _ptr(topk_idx, torch.int32, "topk_idx", B * topk) if topk_idx is not None else None, topk,
+        _ptr(stage, torch.uint8, "stage") if stage is not None else None,
+        stage.numel() if stage is not None else 0, stage_mode,
+        _ptr(swa_k, torch.uint8, "swa_k", B * WINDOW * HEAD_DIM),
+        _ptr(swa_v, torch.uint8, "swa_v", B * WINDOW * HEAD_DIM),
+        _ptr(swa_ks, torch.float32, "swa_ks", B * WINDOW),
+        _ptr(swa_vs, torch.float32, "swa_vs", B * WINDOW),
+        _ptr(swa_len, torch.int32, "swa_len", B), sm,
+        _ptr(out, torch.float32, "out", B * H * HEAD_DIM), _ptr(lse, torch.float32, "lse", B * H),
+        _ptr(ws, torch.uint8, "ws") if ws is not None else None,
+        ws.numel() if ws is not None else 0, _stream(stream), ev[0], ev[1])
+    _check(rc, "csa2_sparse_attn_decode_reuse")
 
 
 def sparse_attn_chunk(q, cache, topk_idx, swa_k, swa_v, swa_ks, swa_vs, out, lse, sm_scale=None,

@@ -138,6 +138,9 @@ __attribute__((visibility("default"))) size_t csa2_workspace_size(int op, int B,
         case CSA2_OP_ATTN_CHUNK:
             if (B <= 0 || Q <= 0 || H <= 0 || topk < 0) return SIZE_MAX;
             return attn_workspace_bytes((int64_t)B * Q, H, topk, Q);
+        case CSA2_OP_ATTN_STAGE:
+            if (B <= 0 || topk < 0 || topk > CSA2_MAX_TOPK) return SIZE_MAX;
+            return attn_stage_bytes(B, topk);
         default:
             return SIZE_MAX;
     }
@@ -257,6 +260,33 @@ __attribute__((visibility("default"))) int csa2_sparse_attn_decode(
     return csa2_sparse_attn_decode_timed(q, B, H, kv_codes, kv_scales, cap, topk_idx, topk, swa_k,
                                          swa_v, swa_ks, swa_vs, swa_len, sm_scale, out, lse, ws,
                                          ws_bytes, stream, nullptr, nullptr);
+}
+
+__attribute__((visibility("default"))) int csa2_sparse_attn_decode_reuse(
+    const float* q, int B, int H, const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t cap,
+    const int32_t* topk_idx, int topk, uint8_t* stage, size_t stage_bytes, int stage_mode,
+    const uint8_t* swa_k, const uint8_t* swa_v, const float* swa_ks, const float* swa_vs,
+    const int32_t* swa_len, float sm_scale, float* out, float* lse, void* ws, size_t ws_bytes,
+    hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+    if (stage_mode != CSA2_STAGE_WRITE && stage_mode != CSA2_STAGE_READ) return CSA2_E_ARG;
+    if (topk > 0 && !stage) return CSA2_E_ARG;
+    const bool read = stage_mode == CSA2_STAGE_READ;
+    // a reading call takes the records from the stage: cache and positions unused
+    const uint8_t* kvc = read ? stage : kv_codes;
+    const uint8_t* kvs = read ? stage : kv_scales;
+    const int32_t* idx = read ? reinterpret_cast<const int32_t*>(stage) : topk_idx;
+    int rc = validate_attn(q, B, 1, H, kvc, kvs, read ? 1 : cap, idx, topk, swa_k, swa_v, swa_ks,
+                           swa_vs, sm_scale, out, lse);
+    if (rc) return rc;
+    if (!swa_len) return CSA2_E_ARG;
+    if (topk > 0 && stage_bytes < attn_stage_bytes(B, topk)) return CSA2_E_WORKSPACE;
+    const size_t need = attn_workspace_bytes(B, H, topk, CSA2_WINDOW);
+    if (need > 0 && (!ws || ws_bytes < need)) return CSA2_E_WORKSPACE;
+    AttnArgs a{q, H, 1, read ? nullptr : kv_codes, read ? nullptr : kv_scales, read ? 1 : cap,
+               read ? nullptr : topk_idx, topk, swa_k, swa_v, swa_ks, swa_vs, swa_len,
+               CSA2_WINDOW, sm_scale, out, lse, (int64_t)B, topk > 0 ? stage : nullptr,
+               topk > 0 ? (read ? kStageRead : kStageWrite) : 0};
+    return hip_status(launch_attn(a, ws, ws_bytes, stream, start, stop));
 }
 
 __attribute__((visibility("default"))) int csa2_sparse_attn_chunk(

@@ -81,6 +81,8 @@ struct SeqView {
     const uint8_t* swk;
     const uint8_t* swv;
     const int32_t* idx;    // this query's top-K row
+    uint8_t* stage;        // this query's staged tiles (stage mode), or null
+    int stage_rem, stage_mod;  // a writing workgroup writes the tiles t with t % mod == rem
     int64_t cap;
     int64_t b;
     int topk;
@@ -129,12 +131,27 @@ __device__ __forceinline__ u32x4_t ld16(const uint8_t* p) {
 }
 
 // Issue the loads of tile t.  pos: tile_position(s, t, lane) for a global
-// tile (unused for a window tile).
+// tile (unused for a window tile, or when the tile comes from the stage).
+template <int STAGE>
 __device__ __forceinline__ void fetch_tile(const SeqView& s, int t, int32_t pos, int lane,
                                            TileRegs& r) {
     const int c = lane & 15, g = lane >> 4;
     const u32x4_t z = {0u, 0u, 0u, 0u};
-    if (t < s.n_tiles_global) {
+    if (STAGE == kStageRead && t < s.n_tiles_global) {
+        // the lanes' bytes as the gathering layer held them: 16 coalesced bytes
+        // per lane and register
+        const uint8_t* src = s.stage + (int64_t)t * kStageTileBytes + 16 * lane;
+        r.k[0][0] = ld16(src);
+        r.k[1][0] = ld16(src + 1024);
+        r.v[0] = ld16(src + 2048);
+        r.v[1] = ld16(src + 3072);
+        r.sc = lane < kTile ? ld16(src + 4096) : z;
+        r.valid = *reinterpret_cast<const uint32_t*>(s.stage + (int64_t)t * kStageTileBytes + 4608);
+        r.k[0][1] = z;
+        r.k[1][1] = z;
+        r.v[2] = z;
+        r.v[3] = z;
+    } else if (t < s.n_tiles_global) {
         const int64_t base = s.b * s.cap;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
@@ -228,7 +245,7 @@ __device__ __forceinline__ int c_entry(int i, int g) { return i < 4 ? 4 * g + i 
 
 // One tile: V into LDS, logits, online softmax, PV.  GLOBAL: a tile of
 // selected FP4 records, else a tile of FP8 window tokens.
-template <bool GLOBAL>
+template <bool GLOBAL, int STAGE>
 __device__ __forceinline__ void process_tile(const SeqView& s, int t, const TileRegs& r,
                                              const float* __restrict__ win_l,
                                              const half8_t (&qhi)[4], const half8_t (&qlo)[4],
@@ -236,6 +253,18 @@ __device__ __forceinline__ void process_tile(const SeqView& s, int t, const Tile
                                              WaveState& st) {
     const int c = lane & 15, g = lane >> 4;
     constexpr bool global = GLOBAL;
+
+    if (global && STAGE == kStageWrite && t % s.stage_mod == s.stage_rem) {
+        // hand the gathered bytes on to the layers that reuse this selection
+        uint8_t* dst = s.stage + (int64_t)t * kStageTileBytes;
+        u32x4_t* d = reinterpret_cast<u32x4_t*>(dst + 16 * lane);
+        d[0] = r.k[0][0];
+        d[64] = r.k[1][0];
+        d[128] = r.v[0];
+        d[192] = r.v[1];
+        if (lane < kTile) d[256] = r.sc;
+        if (lane == 0) *reinterpret_cast<uint32_t*>(dst + 4608) = r.valid;
+    }
 
     // scale bytes come from the lane that loaded the entry's 16-byte chunk:
     // K scales 2g, 2g + 1 of entries c and 16 + c; V scales 2q, 2q + 1 of
@@ -378,12 +407,13 @@ __device__ __forceinline__ void touch(const T& v) {
     asm volatile("" ::"s"(v));
 }
 
+template <int STAGE>
 __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a, int n_tiles_global) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
     touch(a.q); touch(a.H); touch(a.Q); touch(a.kvc); touch(a.kvs); touch(a.cap);
     touch(a.idx); touch(a.topk); touch(a.swk); touch(a.swv); touch(a.swks); touch(a.swvs);
     touch(a.swa_len); touch(a.swa_rows); touch(a.sm_scale); touch(a.out); touch(a.lse);
-    touch(a.n_q); touch(n_tiles_global);
+    touch(a.n_q); touch(n_tiles_global); touch(a.stage);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane & 15, g = lane >> 4;
     const int G = a.H / kGroupHeads;
@@ -399,6 +429,10 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a, int n_tiles_globa
     SeqView s;
     s.kvc = a.kvc; s.kvs = a.kvs; s.swk = a.swk; s.swv = a.swv;
     s.idx = a.idx + bq * a.topk;
+    // in a gathering launch the head groups' workgroups share the stage writes
+    s.stage = STAGE != 0 ? a.stage + bq * n_tiles_global * kStageTileBytes : nullptr;
+    s.stage_rem = hg;
+    s.stage_mod = G;
     s.cap = a.cap;
     s.b = bq / a.Q;
     s.topk = a.topk;
@@ -411,11 +445,12 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a, int n_tiles_globa
     const int t0 = wave, t1 = wave + kWaves;
     TileRegs ra, rb;
     {
-        const int32_t p0 = t0 < n_tiles_global ? tile_position(s, t0, lane) : -1;
-        const int32_t p1 = t1 < n_tiles_global ? tile_position(s, t1, lane) : -1;
+        const bool pos = STAGE != kStageRead;  // positions needed
+        const int32_t p0 = pos && t0 < n_tiles_global ? tile_position(s, t0, lane) : -1;
+        const int32_t p1 = pos && t1 < n_tiles_global ? tile_position(s, t1, lane) : -1;
         s.swa_len = 0;  // not read on the path of selected records
-        if (t0 < n_tiles_global) fetch_tile(s, t0, p0, lane, ra);
-        if (t1 < n_tiles_global) fetch_tile(s, t1, p1, lane, rb);
+        if (t0 < n_tiles_global) fetch_tile<STAGE>(s, t0, p0, lane, ra);
+        if (t1 < n_tiles_global) fetch_tile<STAGE>(s, t1, p1, lane, rb);
     }
     if (a.swa_len != nullptr) {
         const int sl = a.swa_len[s.b];
@@ -424,8 +459,8 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a, int n_tiles_globa
         s.swa_len = (int)(bq % a.Q) + 1;  // chunk query i sees window tokens [0, i]
     }
     const int n_tiles = n_tiles_global + (s.swa_len + kTile - 1) / kTile;
-    if (t0 >= n_tiles_global && t0 < n_tiles) fetch_tile(s, t0, -1, lane, ra);
-    if (t1 >= n_tiles_global && t1 < n_tiles) fetch_tile(s, t1, -1, lane, rb);
+    if (t0 >= n_tiles_global && t0 < n_tiles) fetch_tile<STAGE>(s, t0, -1, lane, ra);
+    if (t1 >= n_tiles_global && t1 < n_tiles) fetch_tile<STAGE>(s, t1, -1, lane, rb);
 
     // ---- meanwhile, once per workgroup: q of the 16 heads, window scales ----
     {
@@ -468,21 +503,25 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a, int n_tiles_globa
 
     for (int t = t0; t < n_tiles; t += 2 * kWaves) {
         if (t < n_tiles_global)
-            process_tile<true>(s, t, ra, win_l, qhi, qlo, vtile, lane, st);
+            process_tile<true, STAGE>(s, t, ra, win_l, qhi, qlo, vtile, lane, st);
         else
-            process_tile<false>(s, t, ra, win_l, qhi, qlo, vtile, lane, st);
+            process_tile<false, STAGE>(s, t, ra, win_l, qhi, qlo, vtile, lane, st);
         const int ta = t + 2 * kWaves;
         if (ta < n_tiles)
-            fetch_tile(s, ta, ta < n_tiles_global ? tile_position(s, ta, lane) : -1, lane, ra);
+            fetch_tile<STAGE>(s, ta,
+                              STAGE != kStageRead && ta < n_tiles_global ? tile_position(s, ta, lane) : -1,
+                              lane, ra);
         const int u = t + kWaves;
         if (u < n_tiles) {
             if (u < n_tiles_global)
-                process_tile<true>(s, u, rb, win_l, qhi, qlo, vtile, lane, st);
+                process_tile<true, STAGE>(s, u, rb, win_l, qhi, qlo, vtile, lane, st);
             else
-                process_tile<false>(s, u, rb, win_l, qhi, qlo, vtile, lane, st);
+                process_tile<false, STAGE>(s, u, rb, win_l, qhi, qlo, vtile, lane, st);
             const int ub = u + 2 * kWaves;
             if (ub < n_tiles)
-                fetch_tile(s, ub, ub < n_tiles_global ? tile_position(s, ub, lane) : -1, lane, rb);
+                fetch_tile<STAGE>(s, ub,
+                                  STAGE != kStageRead && ub < n_tiles_global ? tile_position(s, ub, lane) : -1,
+                                  lane, rb);
         }
     }
 
@@ -542,12 +581,16 @@ hipError_t launch_attn(const AttnArgs& a, void* /*ws*/, size_t /*ws_bytes*/, hip
     const int G = a.H / kGroupHeads;
     const int64_t rounds = (a.n_q + kXcds - 1) / kXcds;
     const unsigned grid = (unsigned)(rounds * kXcds * G);
+    if (a.stage_mode != 0 && (a.stage == nullptr || a.Q != 1)) return hipErrorInvalidValue;
+    void (*kern)(AttnArgs, int) = a.stage_mode == kStageWrite  ? k_attn<kStageWrite>
+                                  : a.stage_mode == kStageRead ? k_attn<kStageRead>
+                                                               : k_attn<0>;
     if (start != nullptr && stop != nullptr) {
         // the runtime records `start` / `stop` immediately around this dispatch
-        hipExtLaunchKernelGGL(k_attn, dim3(grid), dim3(kThreads), 0, stream, start, stop, 0, a,
+        hipExtLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, start, stop, 0, a,
                               n_tiles_global);
     } else {
-        hipLaunchKernelGGL(k_attn, dim3(grid), dim3(kThreads), 0, stream, a, n_tiles_global);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, a, n_tiles_global);
     }
     return hipGetLastError();
 }

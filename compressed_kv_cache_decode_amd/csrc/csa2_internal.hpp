@@ -53,7 +53,19 @@ struct AttnArgs {
     float* out;              // [n_q][H][128]
     float* lse;              // [n_q][H]
     int64_t n_q;
+    uint8_t* stage;          // staged selected records (stage_mode != 0), [n_q][tiles][kStageTileBytes]
+    int stage_mode;          // 0 none, kStageWrite, kStageRead
 };
+
+// Staged records: the raw bytes of one tile of 32 selected records exactly as
+// the attention lanes hold them, so that a layer that reuses a selection reads
+// them with coalesced loads instead of gathering through the positions again.
+constexpr int kStageWrite = 1;  // gather through the positions, also write the stage
+constexpr int kStageRead = 2;   // read the records from the stage (no positions, no cache)
+constexpr int kStageTileBytes = 4672;  // 4 x 1024 (K0, K1, V0, V1) + 512 (scales) + 4 (valid), padded
+inline size_t attn_stage_bytes(int64_t n_q, int topk) {
+    return (size_t)n_q * ((topk + 31) / 32) * kStageTileBytes;
+}
 
 size_t attn_workspace_bytes(int64_t n_q, int H, int topk, int swa_rows);
 hipError_t launch_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t stream,

@@ -9,13 +9,18 @@ live", "CSA2 attention": the decoder's groups are headed by Reindex layers.
 A plan is a string over {F, X, R}: F = Full (index_full, writes the pool),
 X = Reindex (index_reindex inside the latest pool), R = Reuse (no indexer
 call; attends to the most recent Full/Reindex top-K).  Every layer calls the
-sparse attention with its own q and window.  This module only sequences
-library calls; buffers are allocated once, up front.
+sparse attention with its own q and window.  With staging (the default), a
+Full/Reindex layer's attention also writes the records it gathered to a
+stage buffer, and the Reuse layers after it read them from there instead of
+gathering through the same positions again (the cache is shared by every
+layer, so the records are the same).  This module only sequences library
+calls; buffers are allocated once, up front.
 """
 import torch
 
-from . import (DEFAULT_POOL_BLOCKS, DEFAULT_TOPK, HEAD_DIM, OP_ATTN_DECODE, OP_INDEX_FULL,
-               OP_INDEX_REINDEX, alloc_workspace, index_full, index_reindex, sparse_attn_decode,
+from . import (DEFAULT_POOL_BLOCKS, DEFAULT_TOPK, HEAD_DIM, OP_ATTN_DECODE, OP_ATTN_STAGE,
+               OP_INDEX_FULL, OP_INDEX_REINDEX, STAGE_READ, STAGE_WRITE, alloc_workspace,
+               index_full, index_reindex, sparse_attn_decode, sparse_attn_decode_reuse,
                workspace_size)
 
 
@@ -41,7 +46,8 @@ def reuse_sources(plan):
 class DecodeStack:
     """Buffers and workspaces for one stack of `plan` over `cache`, batch B, H heads."""
 
-    def __init__(self, cache, plan, B, H, topk=DEFAULT_TOPK, pool_blocks=DEFAULT_POOL_BLOCKS):
+    def __init__(self, cache, plan, B, H, topk=DEFAULT_TOPK, pool_blocks=DEFAULT_POOL_BLOCKS,
+                 stage=True):
         check_plan(plan, pool_blocks)
         self.cache, self.plan, self.B, self.H = cache, plan, B, H
         self.topk, self.pool_blocks = topk, pool_blocks
@@ -59,6 +65,8 @@ class DecodeStack:
         self.out = torch.empty((len(plan), B, H, HEAD_DIM), dtype=torch.float32, device=dev)
         self.lse = torch.empty((len(plan), B, H), dtype=torch.float32, device=dev)
         self.sources = reuse_sources(plan)
+        self.stage = (alloc_workspace(workspace_size(OP_ATTN_STAGE, B, 1, cache.cap, topk, 0, H),
+                                      dev) if stage and topk > 0 else None)
 
     def step(self, iq, iw, n_vis, q, swa_k, swa_v, swa_ks, swa_vs, swa_len, stream=None,
              scan_timer=None, attn_timer=None):
@@ -82,9 +90,16 @@ class DecodeStack:
                 index_reindex(self.cache, iq[k], iw[k], n_vis, self.pool, self.topk_bufs[k],
                               topk=self.topk, ws=self.ws_reindex, stream=stream)
                 cur, k = self.topk_bufs[k], k + 1
-            sparse_attn_decode(q[layer], self.cache, cur.view(self.B, self.topk), swa_k[layer],
-                               swa_v[layer], swa_ks[layer], swa_vs[layer], swa_len,
-                               self.out[layer], self.lse[layer], ws=self.ws_attn, stream=stream,
-                               timer=attn_timer)
+            if self.stage is None:
+                sparse_attn_decode(q[layer], self.cache, cur.view(self.B, self.topk),
+                                   swa_k[layer], swa_v[layer], swa_ks[layer], swa_vs[layer],
+                                   swa_len, self.out[layer], self.lse[layer], ws=self.ws_attn,
+                                   stream=stream, timer=attn_timer)
+            else:
+                sparse_attn_decode_reuse(
+                    q[layer], self.cache, cur.view(self.B, self.topk), self.topk, self.stage,
+                    STAGE_READ if mode == "R" else STAGE_WRITE, swa_k[layer], swa_v[layer],
+                    swa_ks[layer], swa_vs[layer], swa_len, self.out[layer], self.lse[layer],
+                    ws=self.ws_attn, stream=stream, timer=attn_timer)
             used.append(cur)
         return used

@@ -94,6 +94,11 @@ extern "C" {
 #define CSA2_OP_INDEX_REINDEX 2
 #define CSA2_OP_ATTN_DECODE 3
 #define CSA2_OP_ATTN_CHUNK 4
+#define CSA2_OP_ATTN_STAGE 5     /* staged-records buffer of csa2_sparse_attn_decode_reuse */
+
+/* stage_mode of csa2_sparse_attn_decode_reuse */
+#define CSA2_STAGE_WRITE 1       /* gather through topk_idx and write the stage */
+#define CSA2_STAGE_READ 2        /* take the selected records from the stage */
 
 /*
  * csa2_quant_fp4 -- write path of the main KV.
@@ -231,6 +236,37 @@ int csa2_sparse_attn_decode(const float* q, int B, int H, const uint8_t* kv_code
 int csa2_sparse_attn_decode_timed(const float* q, int B, int H, const uint8_t* kv_codes,
                                   const uint8_t* kv_scales, int64_t cap, const int32_t* topk_idx,
                                   int topk, const uint8_t* swa_k, const uint8_t* swa_v,
+                                  const float* swa_ks, const float* swa_vs,
+                                  const int32_t* swa_len, float sm_scale, float* out, float* lse,
+                                  void* ws, size_t ws_bytes, hipStream_t stream,
+                                  hipEvent_t start, hipEvent_t stop);
+
+/*
+ * csa2_sparse_attn_decode_reuse -- csa2_sparse_attn_decode for a stack of
+ * layers that share one selection ("DeepSeek V4.1 Flash: architecture study
+ * notes" section 2: a Reuse layer keeps the shared global KV and the latest
+ * top-K positions and has only its own query and window; with one cache
+ * shared by every layer, the selected records themselves are identical
+ * across those layers).
+ *   stage_mode CSA2_STAGE_WRITE: as csa2_sparse_attn_decode, and the raw bytes
+ *              of every selected record (codes, scales, presence) are also
+ *              written to `stage`, laid out as the attention kernel's lanes
+ *              hold them.
+ *   stage_mode CSA2_STAGE_READ: the records come from `stage` as written by
+ *              an earlier CSA2_STAGE_WRITE call with the same B and topk (and
+ *              the cache unchanged since); kv_codes, kv_scales, cap and
+ *              topk_idx are not read (may be NULL / 0).
+ * Outputs are bit-identical to csa2_sparse_attn_decode with the source
+ * layer's topk_idx.  stage: device memory owned by the caller, at least
+ * csa2_workspace_size(CSA2_OP_ATTN_STAGE, B, 1, cap, topk, 0, H) =
+ * B * ceil(topk / 32) * 4672 bytes (smaller -> CSA2_E_WORKSPACE; NULL allowed
+ * when topk == 0).  A reading call must not overlap the writing call in time.
+ * start / stop: as csa2_sparse_attn_decode_timed (NULL: not recorded).
+ */
+int csa2_sparse_attn_decode_reuse(const float* q, int B, int H, const uint8_t* kv_codes,
+                                  const uint8_t* kv_scales, int64_t cap, const int32_t* topk_idx,
+                                  int topk, uint8_t* stage, size_t stage_bytes, int stage_mode,
+                                  const uint8_t* swa_k, const uint8_t* swa_v,
                                   const float* swa_ks, const float* swa_vs,
                                   const int32_t* swa_len, float sm_scale, float* out, float* lse,
                                   void* ws, size_t ws_bytes, hipStream_t stream,

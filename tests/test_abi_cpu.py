@@ -96,6 +96,16 @@ def test_attention_validation(lib):
     assert call(topk=4096) == -2
     assert call(sm=float("nan")) == -1
     assert call(swa_len=None) == -1
+    r = lib.csa2_sparse_attn_decode_reuse
+
+    def reuse(mode=2, stage=FAKE, stage_bytes=1 << 40, topk=512, ws=FAKE):
+        return r(FAKE, 4, 64, None, None, 0, None, topk, stage, stage_bytes, mode, FAKE, FAKE,
+                 FAKE, FAKE, FAKE, ctypes.c_float(0.088), FAKE, FAKE, ws, 1 << 40, None, None, None)
+
+    assert reuse(mode=0) == -1 and reuse(mode=3) == -1
+    assert reuse(stage=None) == -1                    # records must come from somewhere
+    assert reuse(stage_bytes=4 * 16 * 4672 - 1) == -3  # B * ceil(topk / 32) tiles of 4672 B
+    assert reuse(mode=1) == -1                        # a writing call gathers: cache needed
     c = lib.csa2_sparse_attn_chunk
     assert c(FAKE, 1, 128, 40, FAKE, FAKE, 4096, FAKE, 512, FAKE, FAKE, FAKE, FAKE,
              ctypes.c_float(0.088), FAKE, FAKE, FAKE, 1 << 40, None) == -2
@@ -111,5 +121,8 @@ def test_workspace_sizes(lib):
     assert ws(2, 16, 1, 131072, 512, 2048, 0) >= 16 * 2048 * 8 * 4
     assert ws(1, 16, 1, 1000, 512, 2048, 0) == big
     assert ws(99, 1, 1, 64, 1, 1, 16) == big
+    assert ws(5, 16, 1, 131072, 512, 0, 64) == 16 * 16 * 4672  # staged records
+    assert ws(5, 2, 1, 131072, 100, 0, 64) == 2 * 4 * 4672
+    assert ws(5, 2, 1, 131072, 0, 0, 64) == 0
     assert ws(3, 16, 1, 131072, 512, 0, 64) == 0              # attention needs no workspace
     assert ws(4, 1, 128, 131072, 512, 0, 64) == 0

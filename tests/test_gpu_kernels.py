@@ -254,6 +254,54 @@ def test_sparse_attn_decode(gpu, oracle_mod, B, cap, H, topk, swa_len, n_sel):
         np.testing.assert_allclose(l[b], lse_ref[b], rtol=2e-3, atol=2e-3)
 
 
+@pytest.mark.parametrize("B,cap,H,topk,swa_len,n_sel", [
+    (3, 4096, 64, 512, [128, 5, 0], [512, 300, 0]),
+    (2, 2048, 32, 100, [77, 128], [100, 3]),
+    (2, 8192, 128, 2048, [128, 100], [2048, 1500]),
+])
+def test_sparse_attn_decode_reuse_stage(gpu, oracle_mod, B, cap, H, topk, swa_len, n_sel):
+    """A gathering call writes the stage; later calls with other queries and
+    windows read it (no cache, no positions): every output equals the plain
+    call's bit for bit, and the oracle's to the attention tolerance."""
+    say(f"attn_decode_reuse B={B} cap={cap} H={H} topk={topk}")
+    cache, codes, scales, sk, sv, sks, svs, q = make_attn_case(gpu, oracle_mod, B, cap, H, 740 + H)
+    g = np.random.default_rng(741)
+    idx = np.full((B, topk), -1, np.int32)
+    for b in range(B):
+        idx[b, :n_sel[b]] = np.sort(g.choice(cap, n_sel[b], replace=False))
+    clean = idx.copy()
+    clean[0, -1] = -1
+    idx[0, -1] = cap + 3   # an out-of-range position is staged as absent (the oracle sees -1)
+    sl = np.array(swa_len, np.int32)
+    stage = gpu.alloc_workspace(gpu.workspace_size(gpu.OP_ATTN_STAGE, B, 1, cap, topk, 0, H))
+    assert stage.numel() == B * ((topk + 31) // 32) * 4672
+    stage.fill_(0xAB)  # no byte of a previous content may leak through
+    for layer in range(3):
+        ql = q if layer == 0 else g.standard_normal(q.shape).astype(np.float32)
+        skl, svl = (sk, sv) if layer == 0 else (np.roll(sk, layer, axis=1), np.roll(sv, layer, axis=1))
+        sksl, svsl = (sks, svs) if layer == 0 else (sks[:, ::-1].copy(), svs[:, ::-1].copy())
+        args = (dev(skl), dev(svl), dev(sksl), dev(svsl), dev(sl))
+        out_p = torch.empty((B, H, 128), dtype=torch.float32, device="cuda")
+        lse_p = torch.empty((B, H), dtype=torch.float32, device="cuda")
+        gpu.sparse_attn_decode(dev(ql), cache, dev(idx), *args, out_p, lse_p)
+        out = torch.empty((B, H, 128), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+        if layer == 0:
+            gpu.sparse_attn_decode_reuse(dev(ql), cache, dev(idx), topk, stage, gpu.STAGE_WRITE,
+                                         *args, out, lse)
+        else:
+            gpu.sparse_attn_decode_reuse(dev(ql), None, None, topk, stage, gpu.STAGE_READ,
+                                         *args, out, lse)
+        np.testing.assert_array_equal(host(out), host(out_p))
+        np.testing.assert_array_equal(host(lse), host(lse_p))
+        out_ref, _ = oracle_mod.attn_decode_batch(ql, codes, scales, clean, skl, svl, sksl, svsl,
+                                                  sl, SM)
+        for b in range(B):
+            if n_sel[b] == 0 and sl[b] == 0:
+                continue
+            assert row_rel_err(host(out)[b], out_ref[b]).max() <= ATOL_ROW
+
+
 def test_sparse_attn_decode_ignores_out_of_range_indices(gpu, oracle_mod):
     say("attn_decode with out-of-range indices")
     B, cap, H = 1, 1024, 16

@@ -177,6 +177,8 @@ def test_graph_replay_matches_eager(gpu, oracle_mod):
     for rep in range(4):
         st.out.zero_()
         st.topk_bufs.fill_(-9)
+        if st.stage is not None:
+            st.stage.fill_(0x5A)  # each replay must write the stage before the Reuse layers read it
         junk = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work
         torch.cuda.synchronize()
         g.replay()
@@ -186,3 +188,26 @@ def test_graph_replay_matches_eager(gpu, oracle_mod):
         np.testing.assert_array_equal(host(st.lse), ref_lse)
         np.testing.assert_array_equal(host(st.topk_bufs), ref_tk)
         del junk
+
+
+def test_staged_stack_equals_plain_stack(gpu, oracle_mod):
+    """Reuse layers reading the staged records give the same bytes as Reuse
+    layers gathering through the positions again."""
+    from compressed_kv_cache_decode_amd.stack import DecodeStack
+    wl = synth.WORKLOADS["decoder_stack_128k"]
+    inp = synth.decode_inputs(wl, n_ent=9000, B=3, layers=10)
+    cap = 9024
+    cache = build_cache_on_gpu(gpu, inp, cap)
+    swk, sks, swv, svs = quantize_windows(gpu, inp.swa_k, inp.swa_v)
+    args = (dev(inp.iq[:, :, None]), dev(inp.iw[:, :, None]), dev(np.full((3, 1), 9000, np.int32)),
+            dev(inp.q), swk, swv, sks, svs, dev(inp.swa_len))
+    outs = []
+    for staged in (True, False):
+        say(f"stack with staging={staged}")
+        st = DecodeStack(cache, wl.plan[:10], 3, wl.H, topk=512, pool_blocks=1024, stage=staged)
+        assert (st.stage is not None) == staged
+        st.step(*args)
+        torch.cuda.synchronize()
+        outs.append((host(st.out).copy(), host(st.lse).copy()))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
