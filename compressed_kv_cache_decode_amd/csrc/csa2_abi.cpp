@@ -22,10 +22,18 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct IndexLayout {
     size_t qd, wq, keys, bkeys, total;
+    // MFMA chunk path only
+    size_t cq, bkeys_hi, cpool, ckeys, flag;
 };
 
+// A multi-query Full layer without a pool output (the replay chunk) scores on
+// MFMA with guard bands (csa2_chunk.hip); otherwise the exact VALU scan.
+bool mma_path(int Q, int pool_blocks) { return Q >= 4 && pool_blocks == 0; }
+
 // workspace of csa2_index_full: decoded query, folded weights, per-position
-// keys, per-block keys
+// keys, per-block keys; on the MFMA path also the guard constants, upper-bound
+// block keys (the lower bounds use the per-block keys), the candidate pools,
+// their exact keys and the fallback flags
 IndexLayout full_layout(int B, int Q, int64_t cap, int topk, int pool_blocks) {
     IndexLayout L{};
     const size_t nq = (size_t)B * Q;
@@ -34,6 +42,14 @@ IndexLayout full_layout(int B, int Q, int64_t cap, int topk, int pool_blocks) {
     L.wq = off; off += align_up(nq * 4 * sizeof(float));
     L.keys = off; off += align_up(nq * (size_t)cap * sizeof(uint32_t));
     L.bkeys = off; off += align_up(nq * (size_t)(cap / 8) * sizeof(uint32_t));
+    if (mma_path(Q, pool_blocks)) {
+        L.cq = off; off += align_up(nq * sizeof(float));
+        const size_t pc = (size_t)cand_pool_blocks(topk);
+        L.bkeys_hi = off; off += align_up(nq * (size_t)(cap / 8) * sizeof(uint32_t));
+        L.cpool = off; off += align_up(nq * pc * sizeof(int32_t));
+        L.ckeys = off; off += align_up(nq * pc * 8 * sizeof(uint32_t));
+        L.flag = off; off += align_up(nq * sizeof(int32_t));
+    }
     L.total = off;
     return L;
 }
@@ -196,6 +212,37 @@ __attribute__((visibility("default"))) int csa2_index_full_timed(
     // so the position select only ever looks at P*8 candidates.  Without a
     // requested pool, P = K blocks are kept internally.
     const int P = pool_blocks > 0 ? pool_blocks : topk;
+
+    if (mma_path(Q, pool_blocks)) {
+        // block bounds on MFMA -> candidate blocks (upper bound reaches the
+        // K-th largest lower bound) -> exact rescore and top-K inside them;
+        // queries whose candidates overflow the pool are recomputed by the
+        // exact scan
+        const int Pc = cand_pool_blocks(topk);
+        float* cq = reinterpret_cast<float*>(w + L.cq);
+        uint32_t* bkeys_hi = reinterpret_cast<uint32_t*>(w + L.bkeys_hi);
+        int32_t* cpool = reinterpret_cast<int32_t*>(w + L.cpool);
+        uint32_t* ckeys = reinterpret_cast<uint32_t*>(w + L.ckeys);
+        int32_t* flag = reinterpret_cast<int32_t*>(w + L.flag);
+        hipError_t e = launch_prep_iq(iq, iw, nq, qd, wq, stream, cq);
+        if (e == hipSuccess)
+            e = launch_scan_mma(ik_codes, ik_sigma, cap, B, Q, qd, wq, cq, n_vis, bkeys,
+                                bkeys_hi, stream, scan_start, scan_stop);
+        if (e == hipSuccess)
+            e = launch_cand_pool(bkeys, bkeys_hi, cap, n_vis, nq, topk, Pc, cpool, flag, stream);
+        if (e == hipSuccess)
+            e = launch_pool_score(ik_codes, ik_sigma, cap, B, Q, iq, iw, n_vis, cpool, Pc, ckeys,
+                                  stream);
+        if (e == hipSuccess)
+            e = launch_select_pool(ckeys, cpool, Pc, n_vis, cap, nq, topk, topk_idx, stream);
+        if (e == hipSuccess)
+            e = launch_scan(ik_codes, ik_sigma, cap, B, Q, qd, wq, n_vis, keys, bkeys, stream,
+                            nullptr, nullptr, flag);
+        if (e == hipSuccess)
+            e = launch_select_full(keys, bkeys, cap, n_vis, nq, P, topk, nullptr, topk_idx,
+                                   stream, flag);
+        return hip_status(e);
+    }
 
     hipError_t e = launch_prep_iq(iq, iw, nq, qd, wq, stream);
     if (e == hipSuccess)

@@ -80,12 +80,15 @@ __global__ __launch_bounds__(256) void k_scan(const uint8_t* __restrict__ ikc,
                                               const float* __restrict__ wq,
                                               const int32_t* __restrict__ n_vis,
                                               uint32_t* __restrict__ keys,
-                                              uint32_t* __restrict__ bkeys) {
+                                              uint32_t* __restrict__ bkeys,
+                                              const int32_t* __restrict__ active) {
     const int b = blockIdx.y;
     const int64_t p0 = (int64_t)blockIdx.x * 256;
     const int64_t p = p0 + threadIdx.x;
     int nv_max = 0;
-    for (int q = 0; q < Q; ++q) nv_max = max(nv_max, clamp_nvis(n_vis[(int64_t)b * Q + q], cap));
+    for (int q = 0; q < Q; ++q)
+        if (active == nullptr || active[(int64_t)b * Q + q])
+            nv_max = max(nv_max, clamp_nvis(n_vis[(int64_t)b * Q + q], cap));
     if (p0 >= nv_max) return;  // uniform over the block
     // cap is a multiple of 64, so a wave is either wholly inside or wholly past it
     if (p0 + (threadIdx.x & ~63) >= cap) return;
@@ -97,6 +100,7 @@ __global__ __launch_bounds__(256) void k_scan(const uint8_t* __restrict__ ikc,
     const int64_t nb = cap / kBlock;
     for (int q = 0; q < Q; ++q) {
         const int64_t bq = (int64_t)b * Q + q;
+        if (active != nullptr && !active[bq]) continue;  // uniform
         const int nv = clamp_nvis(n_vis[bq], cap);
         if (p0 >= nv) continue;  // uniform
         const float s = score_row(raw, sigma, qd + bq * kIdxHeads * kIdxDim, wq + bq * kIdxHeads);
@@ -121,14 +125,15 @@ __global__ __launch_bounds__(256) void k_scan_multi(const uint8_t* __restrict__ 
                                                     const float* __restrict__ wq,
                                                     const int32_t* __restrict__ n_vis,
                                                     uint32_t* __restrict__ keys,
-                                                    uint32_t* __restrict__ bkeys) {
+                                                    uint32_t* __restrict__ bkeys,
+                                                    const int32_t* __restrict__ active) {
     __shared__ __attribute__((aligned(16))) float sq[kScanQChunk * kIdxHeads * kIdxDim];
     __shared__ float sw[kScanQChunk * kIdxHeads];
+    __shared__ int red[4];
     const int b = blockIdx.y;
     const int64_t p0 = (int64_t)blockIdx.x * 256;
     const int64_t p = p0 + threadIdx.x;
-    int nv_max = 0;
-    for (int q = 0; q < Q; ++q) nv_max = max(nv_max, clamp_nvis(n_vis[(int64_t)b * Q + q], cap));
+    const int nv_max = workgroup_nv_max(n_vis, active, b, Q, cap, red);
     if (p0 >= nv_max) return;  // uniform over the block
     // cap is a multiple of 64: a wave is wholly inside or wholly past it; waves
     // past it still take part in the barriers below
@@ -168,6 +173,7 @@ __global__ __launch_bounds__(256) void k_scan_multi(const uint8_t* __restrict__ 
         if (!live) continue;
         for (int j = 0; j < nq; ++j) {
             const int64_t bq = (int64_t)b * Q + q0 + j;
+            if (active != nullptr && !active[bq]) continue;  // uniform
             const int nv = clamp_nvis(n_vis[bq], cap);
             if (p0 >= nv) continue;  // uniform
             // the sequence of IEEE operations of score_row
@@ -699,9 +705,10 @@ __device__ __forceinline__ void select_into(const KeySrc& ks, int K, int32_t* ou
 __global__ __launch_bounds__(kSelThreads) void k_select_full(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ bkeys, int64_t cap,
     const int32_t* __restrict__ n_vis, int P, int K, int32_t* __restrict__ pool_out,
-    int32_t* __restrict__ topk_out) {
+    int32_t* __restrict__ topk_out, const int32_t* __restrict__ active) {
     __shared__ SelShared sh;
     const int64_t bq = blockIdx.x;
+    if (active != nullptr && !active[bq]) return;  // uniform over the workgroup
     const int nv = clamp_nvis(n_vis[bq], cap);
     KeySrc blocks{bkeys + bq * (cap / kBlock), nullptr, ((int64_t)nv + kBlock - 1) / kBlock, nv, 0};
     select_into(blocks, P, pool_out ? pool_out + bq * P : nullptr, sh.pool, sh);
@@ -727,12 +734,87 @@ __global__ __launch_bounds__(kSelThreads) void k_select_pool(
     select_into(ks, K, topk_out + bq * K, nullptr, sh);
 }
 
+// Candidate blocks of the multi-query MFMA scan.  x = the K-th largest
+// lower-bound block key of the query (1 when fewer than K blocks hold a
+// visible position); K distinct blocks then each hold a position whose exact
+// score is >= x, so every position the exact top-K can take lies in a block
+// whose upper-bound key reaches x.  Those blocks, in ascending order, fill
+// pool[bq][0, Pc) (-1 after them); flag[bq] = 1 when more than Pc qualify.
+__global__ __launch_bounds__(kSelThreads) void k_cand_pool(
+    const uint32_t* __restrict__ bkeys_lo, const uint32_t* __restrict__ bkeys_hi, int64_t cap,
+    const int32_t* __restrict__ n_vis, int K, int Pc, int32_t* __restrict__ pool,
+    int32_t* __restrict__ flag) {
+    __shared__ SelShared sh;
+    __shared__ uint32_t part[kSelWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t bq = blockIdx.x;
+    const int nv = clamp_nvis(n_vis[bq], cap);
+    const int64_t nb = cap / kBlock, nbv = ((int64_t)nv + kBlock - 1) / kBlock;
+    const KeySrc lo{bkeys_lo + bq * nb, nullptr, nbv, nv, 0};
+    const KeySrc hi{bkeys_hi + bq * nb, nullptr, nbv, nv, 0};
+
+    // K-th largest lower-bound key: the threshold's tie value, else the
+    // smallest key at or above its cut
+    Threshold th;
+    uint32_t m = 0xFFFFFFFFu;
+    if (nbv <= kSelRegSlots) {
+        uint32_t k[kSelKpt];
+        lo.load16((int64_t)wave * 1024 + 16 * lane, k);
+        th = threshold_reg(k, K, *reinterpret_cast<SelRegShared*>(&sh.hist[0]));
+#pragma unroll
+        for (int i = 0; i < kSelKpt; ++i)
+            m = (k[i] != 0 && k[i] >= th.t_ge) ? min(m, k[i]) : m;
+    } else {
+        const SelRange r = wave_range(nbv, wave);
+        th = find_threshold<false>(lo, sh.keys, r, K, sh);
+        for_keys<false>(lo, sh.keys, r, lane, [&](uint32_t k, int64_t, bool) {
+            m = (k != 0 && k >= th.t_ge) ? min(m, k) : m;
+        });
+    }
+    m = wave_reduce(m, [](uint32_t a, uint32_t b) { return min(a, b); });
+    if (lane == 0) part[wave] = m;
+    __syncthreads();
+    m = 0xFFFFFFFFu;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) m = min(m, part[w]);
+    const uint32_t x = th.total < (uint32_t)K ? 1u : (th.quota != 0 ? th.t_eq : m);
+
+    // ordered compaction of the qualifying blocks, 16 per thread per sweep
+    uint32_t base = 0;
+    for (int64_t b0 = 0; b0 < nbv; b0 += (int64_t)kSelThreads * kSelKpt) {
+        const int64_t first = b0 + (int64_t)tid * kSelKpt;
+        uint32_t h[kSelKpt];
+        hi.load16(first, h);  // 0 past the visible blocks, and x >= 1
+        uint32_t mask = 0;
+#pragma unroll
+        for (int i = 0; i < kSelKpt; ++i) mask |= h[i] >= x ? (1u << i) : 0u;
+        const uint32_t cnt = __popc(mask);
+        const uint32_t excl = wave_excl_scan(cnt);
+        __syncthreads();  // earlier readers of part are done
+        if (lane == 63) part[wave] = excl + cnt;
+        __syncthreads();
+        uint32_t before = base, total = 0;
+#pragma unroll
+        for (int w = 0; w < kSelWaves; ++w) {
+            before += w < wave ? part[w] : 0u;
+            total += part[w];
+        }
+        uint32_t r = before + excl;
+        for (uint32_t mm = mask; mm != 0; mm &= mm - 1u, ++r)
+            if (r < (uint32_t)Pc) pool[bq * Pc + r] = (int32_t)(first + __builtin_ctz(mm));
+        base += total;
+    }
+    for (int64_t i = (int64_t)base + tid; i < Pc; i += kSelThreads) pool[bq * Pc + i] = -1;
+    if (tid == 0) flag[bq] = base > (uint32_t)Pc ? 1 : 0;
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                        const float* qd, const float* wq, const int32_t* n_vis, uint32_t* keys,
-                       uint32_t* bkeys, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+                       uint32_t* bkeys, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
+                       const int32_t* active) {
     dim3 grid((unsigned)((cap + 255) / 256), (unsigned)B);
     // a few queries per sequence: k_scan reads them through the scalar cache;
     // many (the replay chunk): k_scan_multi stages them in LDS
@@ -740,10 +822,10 @@ hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B,
     if (start != nullptr && stop != nullptr) {
         // the runtime records `start` / `stop` immediately around this dispatch
         hipExtLaunchKernelGGL(kern, grid, dim3(256), 0, stream, start, stop, 0, ikc, iks, cap, Q,
-                              qd, wq, n_vis, keys, bkeys);
+                              qd, wq, n_vis, keys, bkeys, active);
     } else {
         hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, ikc, iks, cap, Q, qd, wq, n_vis,
-                           keys, bkeys);
+                           keys, bkeys, active);
     }
     return hipGetLastError();
 }
@@ -760,9 +842,10 @@ hipError_t launch_pool_score(const uint8_t* ikc, const float* iks, int64_t cap, 
 
 hipError_t launch_select_full(const uint32_t* keys, const uint32_t* bkeys, int64_t cap,
                               const int32_t* n_vis, int64_t n_queries, int P, int K,
-                              int32_t* pool_out, int32_t* topk_out, hipStream_t stream) {
+                              int32_t* pool_out, int32_t* topk_out, hipStream_t stream,
+                              const int32_t* active) {
     hipLaunchKernelGGL(k_select_full, dim3((unsigned)n_queries), dim3(kSelThreads), 0, stream, keys,
-                       bkeys, cap, n_vis, P, K, pool_out, topk_out);
+                       bkeys, cap, n_vis, P, K, pool_out, topk_out, active);
     return hipGetLastError();
 }
 
@@ -771,6 +854,14 @@ hipError_t launch_select_pool(const uint32_t* ckeys, const int32_t* pool, int P,
                               int32_t* topk_out, hipStream_t stream) {
     hipLaunchKernelGGL(k_select_pool, dim3((unsigned)n_queries), dim3(kSelThreads), 0, stream,
                        ckeys, pool, P, n_vis, cap, K, topk_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_cand_pool(const uint32_t* bkeys_lo, const uint32_t* bkeys_hi, int64_t cap,
+                            const int32_t* n_vis, int64_t n_queries, int K, int Pc, int32_t* pool,
+                            int32_t* flag, hipStream_t stream) {
+    hipLaunchKernelGGL(k_cand_pool, dim3((unsigned)n_queries), dim3(kSelThreads), 0, stream,
+                       bkeys_lo, bkeys_hi, cap, n_vis, K, Pc, pool, flag);
     return hipGetLastError();
 }
 

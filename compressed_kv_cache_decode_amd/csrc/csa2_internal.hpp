@@ -15,21 +15,39 @@ hipError_t launch_quant_fp8(const float* x, int64_t n_rows, int dim, int layout,
                             const int64_t* dst_rows, uint8_t* codes, float* sigma,
                             hipStream_t stream);
 hipError_t launch_prep_iq(const float* iq, const float* iw, int64_t n_q, float* qd, float* wq,
-                          hipStream_t stream);
+                          hipStream_t stream, float* cq = nullptr);
 hipError_t launch_codec_probe(float* e4m3_dec, float* e4m3_dec16, float* fp4_dec16,
                               const float* x, int64_t n, uint8_t* e4m3_enc, uint8_t* e2m1_enc,
                               hipStream_t stream);
 
+// active: null, or one flag per query; queries whose flag is 0 are skipped
 hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                        const float* qd, const float* wq, const int32_t* n_vis, uint32_t* keys,
                        uint32_t* bkeys, hipStream_t stream, hipEvent_t start = nullptr,
-                       hipEvent_t stop = nullptr);
+                       hipEvent_t stop = nullptr, const int32_t* active = nullptr);
+// MFMA scan of a multi-query chunk with guard-band bounds (csa2_chunk.hip):
+// per block of 8 positions, the largest lower-bound and upper-bound score keys
+hipError_t launch_scan_mma(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
+                           const float* qd, const float* wq, const float* cq,
+                           const int32_t* n_vis, uint32_t* bkeys_lo, uint32_t* bkeys_hi,
+                           hipStream_t stream, hipEvent_t start = nullptr,
+                           hipEvent_t stop = nullptr);
+// candidate blocks of the MFMA scan (csa2_index.hip)
+hipError_t launch_cand_pool(const uint32_t* bkeys_lo, const uint32_t* bkeys_hi, int64_t cap,
+                            const int32_t* n_vis, int64_t n_queries, int K, int Pc, int32_t* pool,
+                            int32_t* flag, hipStream_t stream);
+// candidate blocks per chunk query before the exact fallback: 1.5 K, at least 256
+inline int cand_pool_blocks(int K) {
+    const int p = K + K / 2;
+    return p < 256 ? 256 : (p > kMaxPoolBlocks ? kMaxPoolBlocks : p);
+}
 hipError_t launch_pool_score(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                              const float* iq, const float* iw, const int32_t* n_vis,
                              const int32_t* pool, int P, uint32_t* ckeys, hipStream_t stream);
 hipError_t launch_select_full(const uint32_t* keys, const uint32_t* bkeys, int64_t cap,
                               const int32_t* n_vis, int64_t n_queries, int P, int K,
-                              int32_t* pool_out, int32_t* topk_out, hipStream_t stream);
+                              int32_t* pool_out, int32_t* topk_out, hipStream_t stream,
+                              const int32_t* active = nullptr);
 hipError_t launch_select_pool(const uint32_t* ckeys, const int32_t* pool, int P,
                               const int32_t* n_vis, int64_t cap, int64_t n_queries, int K,
                               int32_t* topk_out, hipStream_t stream);

@@ -110,7 +110,9 @@ __global__ __launch_bounds__(256) void k_quant_fp8(const float* __restrict__ x, 
 // one wave per head, lane = channel.
 __global__ __launch_bounds__(256) void k_prep_iq(const float* __restrict__ iq,
                                                  const float* __restrict__ iw, int64_t n_q,
-                                                 float* __restrict__ qd, float* __restrict__ wq) {
+                                                 float* __restrict__ qd, float* __restrict__ wq,
+                                                 float* __restrict__ cq) {
+    __shared__ float sd[kIdxHeads];
     const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
     const int64_t bq = blockIdx.x;
     if (bq >= n_q) return;
@@ -118,8 +120,20 @@ __global__ __launch_bounds__(256) void k_prep_iq(const float* __restrict__ iq,
     const float amax = wave_max_f32(fabsf(x));
     const float sq = amax / 448.0f;
     const uint32_t c = (sq == 0.0f) ? ((__float_as_uint(x) >> 24) & 0x80u) : e4m3_encode(x / sq);
-    qd[(bq * kIdxHeads + h) * kIdxDim + lane] = e4m3_decode_bits(c);
-    if (lane == 0) wq[bq * kIdxHeads + h] = iw[bq * kIdxHeads + h] * sq;
+    const float v = e4m3_decode_bits(c);
+    qd[(bq * kIdxHeads + h) * kIdxDim + lane] = v;
+    const float w = iw[bq * kIdxHeads + h] * sq;
+    if (lane == 0) wq[bq * kIdxHeads + h] = w;
+    if (cq != nullptr) {
+        // guard-band constant of the MFMA scan (csa2_chunk.hip):
+        // C_q = (1 + 2^-10) sum_h |w'_h| 2^-16 448 ||q_h||_1
+        float l1 = fabsf(v);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) l1 += __shfl_xor(l1, o, 64);
+        if (lane == 0) sd[h] = fabsf(w) * (0x1p-16f * 448.0f * l1);
+        __syncthreads();
+        if (threadIdx.x == 0) cq[bq] = (sd[0] + sd[1] + sd[2] + sd[3]) * (1.0f + 0x1p-10f);
+    }
 }
 
 // Codec probe: decode every E4M3 code with the fp32 converter of the scan and
@@ -174,8 +188,9 @@ hipError_t launch_quant_fp8(const float* x, int64_t n_rows, int dim, int layout,
 }
 
 hipError_t launch_prep_iq(const float* iq, const float* iw, int64_t n_q, float* qd, float* wq,
-                          hipStream_t stream) {
-    hipLaunchKernelGGL(k_prep_iq, dim3((unsigned)n_q), dim3(256), 0, stream, iq, iw, n_q, qd, wq);
+                          hipStream_t stream, float* cq) {
+    hipLaunchKernelGGL(k_prep_iq, dim3((unsigned)n_q), dim3(256), 0, stream, iq, iw, n_q, qd, wq,
+                       cq);
     return hipGetLastError();
 }
 

@@ -123,6 +123,17 @@ def make_idx_cache(gpu, oracle_mod, B, cap, seed, dup_frac=0.0):
     (4, 1, 16384, [16384, 16384, 16000, 8], 512, 0),
     # many queries per sequence (the multi-query scan), ragged visible counts
     (2, 37, 4096, [[4096 - 13 * i for i in range(37)], [1 + 97 * i for i in range(37)]], 64, 0),
+    # multi-query Full layers without a pool take the MFMA guard-band path:
+    # two staging passes of queries (130 > 128), queries seeing fewer than K
+    # positions (down to none), duplicated key rows (ties)
+    (1, 130, 8192, [[8192 - 37 * i if i % 5 else (97 * i) % 600 for i in range(130)]], 512, 0),
+    (2, 16, 16384, [[0, 1, 5, 300, 511, 512, 513, 4096, 8191, 8192, 12000, 16383, 16384,
+                     16384, 7, 9000], [16384 - 1000 * i for i in range(16)]], 512, 0),
+    (1, 4, 1024, [[1024, 1024, 1000, 3]], 2048, 0),   # top-K larger than what is visible
+    # the largest top-K: a 3072-block candidate pool (streaming selection);
+    # more than 16384 blocks: the candidate threshold streams too
+    (1, 5, 65536, [[65536, 65000, 40000, 20000, 9]], 2048, 0),
+    (1, 4, 262144, [[262144, 262000, 131073, 70000]], 512, 0),
     # the largest top-K and pool the boundary accepts; 32768 pool positions take
     # the streaming selection path
     (1, 1, 65536, [65533], 2048, 4096),
@@ -144,6 +155,28 @@ def test_index_full_bit_exact(gpu, oracle_mod, B, Q, cap, nvis, topk, pool):
     np.testing.assert_array_equal(host(tk), tk_ref)
     if pool:
         np.testing.assert_array_equal(host(pl), pl_ref)
+
+
+def test_index_full_chunk_candidate_overflow(gpu, oracle_mod):
+    """Identical key rows tie every score of a query, so every visible block is
+    a candidate of the MFMA path and the candidates overflow its pool: the
+    flagged queries must come out of the exact fallback scan unchanged."""
+    say("index_full multi-query, all-equal scores (candidate overflow)")
+    B, Q, cap = 1, 8, 16384
+    x = np.tile(np.random.default_rng(9).standard_normal((1, 1, 64)), (B, cap, 1)).astype(np.float32)
+    ikc, iks = oracle_mod.quant_fp8_rows(x)
+    cache = gpu.Cache(B, cap)
+    cache.ik_codes.copy_(dev(tile_ik(ikc)))
+    cache.ik_sigma.copy_(dev(iks.reshape(-1)))
+    g = np.random.default_rng(10)
+    iq = g.standard_normal((B, Q, 4, 64)).astype(np.float32)
+    iw = g.random((B, Q, 4)).astype(np.float32)
+    nv = np.array([[16384, 16000, 9000, 8200, 600, 512, 100, 16384]], np.int32)
+    tk_ref, _ = oracle_mod.index_full_batch(ikc.reshape(B, cap, 64), iks.reshape(B, cap), iq, iw,
+                                            nv, 512, 0)
+    tk = torch.full((B, Q, 512), -7, dtype=torch.int32, device="cuda")
+    gpu.index_full(cache, dev(iq), dev(iw), dev(nv), tk, None, topk=512, pool_blocks=0)
+    np.testing.assert_array_equal(host(tk), tk_ref)
 
 
 def test_index_full_all_ties(gpu, oracle_mod):
