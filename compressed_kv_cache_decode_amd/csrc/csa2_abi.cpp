@@ -23,7 +23,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct IndexLayout {
     size_t qd, wq, keys, bkeys, total;
     // MFMA chunk path only
-    size_t cq, bkeys_hi, cpool, ckeys, flag;
+    size_t cq, qh, bkeys_hi, cpool, ckeys, flag;
 };
 
 // A multi-query Full layer without a pool output (the replay chunk) scores on
@@ -31,7 +31,7 @@ struct IndexLayout {
 bool mma_path(int Q, int pool_blocks) { return Q >= 4 && pool_blocks == 0; }
 
 // workspace of csa2_index_full: decoded query, folded weights, per-position
-// keys, per-block keys; on the MFMA path also the guard constants, upper-bound
+// keys, per-block keys; on the MFMA path also the guard constants, fp16 queries, upper-bound
 // block keys (the lower bounds use the per-block keys), the candidate pools,
 // their exact keys and the fallback flags
 IndexLayout full_layout(int B, int Q, int64_t cap, int topk, int pool_blocks) {
@@ -44,6 +44,7 @@ IndexLayout full_layout(int B, int Q, int64_t cap, int topk, int pool_blocks) {
     L.bkeys = off; off += align_up(nq * (size_t)(cap / 8) * sizeof(uint32_t));
     if (mma_path(Q, pool_blocks)) {
         L.cq = off; off += align_up(nq * sizeof(float));
+        L.qh = off; off += align_up(nq * 256 * sizeof(uint16_t));
         const size_t pc = (size_t)cand_pool_blocks(topk);
         L.bkeys_hi = off; off += align_up(nq * (size_t)(cap / 8) * sizeof(uint32_t));
         L.cpool = off; off += align_up(nq * pc * sizeof(int32_t));
@@ -220,13 +221,14 @@ __attribute__((visibility("default"))) int csa2_index_full_timed(
         // exact scan
         const int Pc = cand_pool_blocks(topk);
         float* cq = reinterpret_cast<float*>(w + L.cq);
+        _Float16* qh = reinterpret_cast<_Float16*>(w + L.qh);
         uint32_t* bkeys_hi = reinterpret_cast<uint32_t*>(w + L.bkeys_hi);
         int32_t* cpool = reinterpret_cast<int32_t*>(w + L.cpool);
         uint32_t* ckeys = reinterpret_cast<uint32_t*>(w + L.ckeys);
         int32_t* flag = reinterpret_cast<int32_t*>(w + L.flag);
-        hipError_t e = launch_prep_iq(iq, iw, nq, qd, wq, stream, cq);
+        hipError_t e = launch_prep_iq(iq, iw, nq, qd, wq, stream, cq, qh);
         if (e == hipSuccess)
-            e = launch_scan_mma(ik_codes, ik_sigma, cap, B, Q, qd, wq, cq, n_vis, bkeys,
+            e = launch_scan_mma(ik_codes, ik_sigma, cap, B, Q, qh, wq, cq, n_vis, bkeys,
                                 bkeys_hi, stream, scan_start, scan_stop);
         if (e == hipSuccess)
             e = launch_cand_pool(bkeys, bkeys_hi, cap, n_vis, nq, topk, Pc, cpool, flag, stream);

@@ -15,24 +15,33 @@
 //   S = sum_c |q_c k_c| <= 448 ||q_h||_1       (every E4M3 key value <= 448)
 //
 // so per head |dot_mfma - dot_seq| <= D_h = 2^-16 * 448 * ||q_h||_1 (twice the
-// sum above).  ReLU does not widen it; the head combine t = sum_h w'_h r_h and
-// the scale s = sigma * t are the same IEEE operations on both sides, whose
-// roundings are covered by the terms 2^-18 T (T = sum_h |w'_h| r_h) and
-// 2^-20 |s| below.  Every visible position has a lower bound lo <= s and an
-// upper bound hi >= s:
+// sum above).  ReLU does not widen it.  The head combine t = sum_h w'_h r_h
+// and the scale s = sigma * t are fp32 operations on both sides; their
+// rounding is at most a few 2^-24 T (T = sum_h |w'_h| r_h, and every r_h is at
+// most (1 + 2^-18) 448 ||q_h||_1), covered by 2^-18 T, plus 2^-24 |s| per
+// operation on s, covered by 2^-20 |s|.  So each visible position's score lies
+// within
 //
-//   d = sigma * (C_q + 2^-18 T) + 2^-20 |s|,  C_q = (1 + 2^-10) sum_h |w'_h| D_h
-//   lo = s - d,  hi = s + d,
+//   d = sigma * C'_q + 2^-20 |s|,  C'_q = (1 + 2^-10) (2^-16 + 2^-18) 448 sum_h |w'_h| ||q_h||_1
 //
-// and the kernel writes, per block of 8 positions, the largest key of each.
-// If x is the K-th largest block maximum of lo, K distinct blocks each hold a
-// position with s >= lo >= x, so the K-th largest exact score t is >= x, and
-// every position with s >= t (every position the exact top-K can take, ties
-// included) has hi >= x.  The blocks whose largest hi reaches x thus hold the
-// exact top-K (k_cand_pool); rescoring their positions exactly (the Reindex
-// kernels: same scores, bit for bit, as the VALU scan) and selecting there
-// gives the exact top-K with its tie rule, as the candidate blocks are listed
-// in ascending order.  A query whose candidate blocks do not fit the pool is
+// of the exact one (the factor 1 + 2^-10 absorbs the rounding of the bound
+// arithmetic itself).  A lane holds 4 positions of a block of 8; with
+// m = max s, a = max |s| and g = max sigma over its visible ones,
+// M = g C'_q + 2^-20 a bounds every d there, so m - M is at most the exact
+// score of the position that attains m, and m + M at least every exact score
+// of the four.  Per block, the larger of the two lanes' values gives a lower
+// bound lo (some position's exact score reaches it) and an upper bound hi (no
+// exact score exceeds it); the kernel writes their keys (0 for a block with no
+// visible position).
+//
+// If x is the K-th largest block lo, K distinct blocks each hold a position
+// with exact score >= x, so the K-th largest exact score t is >= x, and every
+// position with score >= t (every position the exact top-K can take, ties
+// included) lies in a block whose hi reaches x.  Those blocks hold the exact
+// top-K (k_cand_pool); rescoring their positions exactly (the Reindex kernels:
+// same scores, bit for bit, as the VALU scan) and selecting there gives the
+// exact top-K with its tie rule, as the candidate blocks are listed in
+// ascending order.  A query whose candidate blocks do not fit the pool is
 // flagged and recomputed by the exact VALU scan.
 #include <hip/hip_ext.h>
 
@@ -61,18 +70,26 @@ __device__ __forceinline__ half8_t e4m3x8_h8(uint32_t w0, uint32_t w1) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// max(x, 0) as one signed integer max of the bits: every float with the sign
+// bit set (-0 included) becomes +0, the rest stay (an fmaxf would also quiet
+// its operand first)
+__device__ __forceinline__ float relu(float x) {
+    return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // grid = (ceil(cap / 256), B), 512 threads.  Wave w scores positions
 // p0 + 32w .. +32 (two MFMA row tiles of 16) against every query of sequence
 // b, 16 queries per MFMA column tile, one accumulator per head:
 // S_h^T[16 positions x 16 queries] += K[16 x 32 channels] Q_h^T[32 x 16], two
-// channel steps per head.  Lane l holds rows 4(l/16) .. +4 of column l % 16.
-__global__ __launch_bounds__(kMmaThreads) void k_scan_mma(
+// channel steps per head.  Lane l holds rows 4(l/16) .. +4 of column l % 16;
+// lanes l and l ^ 16 share a block of 8 positions.
+__global__ __launch_bounds__(kMmaThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_scan_mma(
     const uint8_t* __restrict__ ikc, const float* __restrict__ iks, int64_t cap, int Q,
-    const float* __restrict__ qd, const float* __restrict__ wq, const float* __restrict__ cq,
+    const _Float16* __restrict__ qh, const float* __restrict__ wq, const float* __restrict__ cq,
     const int32_t* __restrict__ n_vis, uint32_t* __restrict__ bkeys_lo,
     uint32_t* __restrict__ bkeys_hi) {
     __shared__ __attribute__((aligned(16))) _Float16 sq[kMmaQ * kMmaPitch];
-    __shared__ float sw[kMmaQ * kIdxHeads];
+    __shared__ __attribute__((aligned(16))) float sw[kMmaQ * kIdxHeads];
     __shared__ float sc[kMmaQ];
     __shared__ int snv[kMmaQ];
     __shared__ int red[kMmaThreads / 64];
@@ -89,6 +106,7 @@ __global__ __launch_bounds__(kMmaThreads) void k_scan_mma(
     // output rows 4 (l / 16) + i
     half8_t a[2][2];
     float4 sig[2];
+    float gmax[2];
     bool inside[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -109,15 +127,30 @@ __global__ __launch_bounds__(kMmaThreads) void k_scan_mma(
             a[st][1] = z;
             sig[st] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
+        gmax[st] = fmaxf(fmaxf(sig[st].x, sig[st].y), fmaxf(sig[st].z, sig[st].w));
     }
 
     for (int q0 = 0; q0 < Q; q0 += kMmaQ) {
         const int nqp = min(kMmaQ, Q - q0);
         const int64_t bq0 = (int64_t)b * Q + q0;
         __syncthreads();  // the previous pass's readers are done
-        for (int i = tid; i < nqp * kIdxHeads * kIdxDim; i += kMmaThreads) {
-            const int j = i >> 8, hc = i & 255;
-            sq[j * kMmaPitch + hc] = (_Float16)qd[(bq0 + j) * kIdxHeads * kIdxDim + hc];  // exact
+        {
+            // the pass's queries, 16 bytes a lane, every load in flight at once
+            constexpr int kPer = kMmaQ * kIdxHeads * kIdxDim / 8 / kMmaThreads;
+            const int n16 = nqp * (kIdxHeads * kIdxDim / 8);
+            const uint4* src = reinterpret_cast<const uint4*>(qh + bq0 * kIdxHeads * kIdxDim);
+            uint4 v[kPer];
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+                const int i = tid + k * kMmaThreads;
+                v[k] = i < n16 ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+                const int i = tid + k * kMmaThreads;
+                if (i < n16)
+                    *reinterpret_cast<uint4*>(sq + (i >> 5) * kMmaPitch + 8 * (i & 31)) = v[k];
+            }
         }
         for (int i = tid; i < nqp * kIdxHeads; i += kMmaThreads) sw[i] = wq[bq0 * kIdxHeads + i];
         for (int j = tid; j < nqp; j += kMmaThreads) {
@@ -126,59 +159,71 @@ __global__ __launch_bounds__(kMmaThreads) void k_scan_mma(
         }
         __syncthreads();
 
+        for (int qt = 0; qt < nqp; qt += 16) {
+            const int j = qt + (lane & 15);  // this lane's query (column)
+            const bool qok = j < nqp;
+            const int jj = qok ? j : 0;  // columns past the pass read query 0, unused
+            half8_t bop[kIdxHeads][2];
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            if (!inside[st]) continue;  // uniform over the wave
-            const int64_t base = p0 + 32 * wave + 16 * st;
-            const int64_t pos0 = base + 4 * (lane >> 4);  // this lane's four rows
-            const float sg[4] = {sig[st].x, sig[st].y, sig[st].z, sig[st].w};
-            for (int qt = 0; qt < nqp; qt += 16) {
-                const int j = qt + (lane & 15);  // this lane's query (column)
+            for (int h = 0; h < kIdxHeads; ++h)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    bop[h][ks] = *reinterpret_cast<const half8_t*>(
+                        sq + jj * kMmaPitch + h * kIdxDim + 32 * ks + 8 * (lane >> 4));
+            const float4 w = *reinterpret_cast<const float4*>(sw + jj * 4);
+            const float cqj = sc[jj];
+            const int nv = snv[jj];
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                if (!inside[st]) continue;  // uniform over the wave
+                const int64_t base = p0 + 32 * wave + 16 * st;
+                const int64_t pos0 = base + 4 * (lane >> 4);  // this lane's four rows
                 float4_t acc[kIdxHeads];
 #pragma unroll
                 for (int h = 0; h < kIdxHeads; ++h) {
                     acc[h] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        const int jj = j < nqp ? j : 0;  // columns past the pass read query 0, unused
-                        const half8_t bop = *reinterpret_cast<const half8_t*>(
-                            sq + jj * kMmaPitch + h * kIdxDim + 32 * ks + 8 * (lane >> 4));
-                        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[st][ks], bop, acc[h], 0, 0, 0);
-                    }
+                    for (int ks = 0; ks < 2; ++ks)
+                        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[st][ks], bop[h][ks],
+                                                                       acc[h], 0, 0, 0);
                 }
-                const bool qok = j < nqp;
-                const int jj = qok ? j : 0;
-                const float w0 = sw[jj * 4 + 0], w1 = sw[jj * 4 + 1], w2 = sw[jj * 4 + 2], w3 = sw[jj * 4 + 3];
-                const float cqj = sc[jj];
-                const int nv = snv[jj];
-                uint32_t klo[4], khi[4];
+                const float sg[4] = {sig[st].x, sig[st].y, sig[st].z, sig[st].w};
+                float s[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float r0 = acc[0][i] > 0.0f ? acc[0][i] : 0.0f;
-                    const float r1 = acc[1][i] > 0.0f ? acc[1][i] : 0.0f;
-                    const float r2 = acc[2][i] > 0.0f ? acc[2][i] : 0.0f;
-                    const float r3 = acc[3][i] > 0.0f ? acc[3][i] : 0.0f;
-                    // the head combine of the score, operation by operation
-                    float t = w0 * r0;
-                    t = t + w1 * r1;
-                    t = t + w2 * r2;
-                    t = t + w3 * r3;
-                    const float s = sg[i] * t;
-                    const float T = fabsf(w0) * r0 + fabsf(w1) * r1 + fabsf(w2) * r2 + fabsf(w3) * r3;
-                    const float d = sg[i] * (cqj + 0x1p-18f * T) + 0x1p-20f * fabsf(s);
-                    const bool vis = pos0 + i < nv;
-                    klo[i] = vis ? score_key(s - d) : 0u;
-                    khi[i] = vis ? score_key(s + d) : 0u;
+                    const float r0 = relu(acc[0][i]), r1 = relu(acc[1][i]);
+                    const float r2 = relu(acc[2][i]), r3 = relu(acc[3][i]);
+                    float t = w.x * r0;
+                    t = fmaf(w.y, r1, t);
+                    t = fmaf(w.z, r2, t);
+                    t = fmaf(w.w, r3, t);
+                    s[i] = sg[i] * t;
                 }
-                // block of 8 = rows 0..7 (lanes l / 16 = 0, 1) or 8..15 (2, 3)
-                uint32_t mlo = max(max(klo[0], klo[1]), max(klo[2], klo[3]));
-                uint32_t mhi = max(max(khi[0], khi[1]), max(khi[2], khi[3]));
-                mlo = max(mlo, (uint32_t)__shfl_xor((int)mlo, 16, 64));
-                mhi = max(mhi, (uint32_t)__shfl_xor((int)mhi, 16, 64));
+                float m, a_abs;
+                if (pos0 + 3 < nv) {
+                    m = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+                    const float lo4 = fminf(fminf(s[0], s[1]), fminf(s[2], s[3]));
+                    a_abs = fmaxf(m, -lo4);
+                } else {  // the query's visible range ends in these four rows
+                    m = -INFINITY;
+                    float lo4 = INFINITY;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (pos0 + i < nv) {
+                            m = fmaxf(m, s[i]);
+                            lo4 = fminf(lo4, s[i]);
+                        }
+                    a_abs = m >= lo4 ? fmaxf(m, -lo4) : 0.0f;  // m = -inf: none visible
+                }
+                const float M = fmaf(a_abs, 0x1p-20f, gmax[st] * cqj);
+                float lo = m - M, hi = m + M;  // -inf when no row is visible
+                lo = fmaxf(lo, __shfl_xor(lo, 16, 64));
+                hi = fmaxf(hi, __shfl_xor(hi, 16, 64));
                 if (qok && ((lane >> 4) & 1) == 0) {
                     const int64_t blk = (base >> 3) + (lane >> 5);
-                    bkeys_lo[(bq0 + j) * nb + blk] = mlo;
-                    bkeys_hi[(bq0 + j) * nb + blk] = mhi;
+                    const bool any = lo != -INFINITY;
+                    bkeys_lo[(bq0 + j) * nb + blk] = any ? score_key(lo) : 0u;
+                    bkeys_hi[(bq0 + j) * nb + blk] = any ? score_key(hi) : 0u;
                 }
             }
         }
@@ -186,15 +231,15 @@ __global__ __launch_bounds__(kMmaThreads) void k_scan_mma(
 }
 
 hipError_t launch_scan_mma(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
-                           const float* qd, const float* wq, const float* cq,
+                           const _Float16* qh, const float* wq, const float* cq,
                            const int32_t* n_vis, uint32_t* bkeys_lo, uint32_t* bkeys_hi,
                            hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     dim3 grid((unsigned)((cap + kMmaPos - 1) / kMmaPos), (unsigned)B);
     if (start != nullptr && stop != nullptr) {
         hipExtLaunchKernelGGL(k_scan_mma, grid, dim3(kMmaThreads), 0, stream, start, stop, 0, ikc,
-                              iks, cap, Q, qd, wq, cq, n_vis, bkeys_lo, bkeys_hi);
+                              iks, cap, Q, qh, wq, cq, n_vis, bkeys_lo, bkeys_hi);
     } else {
-        hipLaunchKernelGGL(k_scan_mma, grid, dim3(kMmaThreads), 0, stream, ikc, iks, cap, Q, qd,
+        hipLaunchKernelGGL(k_scan_mma, grid, dim3(kMmaThreads), 0, stream, ikc, iks, cap, Q, qh,
                            wq, cq, n_vis, bkeys_lo, bkeys_hi);
     }
     return hipGetLastError();

@@ -14,8 +14,9 @@ hipError_t launch_quant_fp4(const float* k, const float* v, int64_t n_ent, int r
 hipError_t launch_quant_fp8(const float* x, int64_t n_rows, int dim, int layout,
                             const int64_t* dst_rows, uint8_t* codes, float* sigma,
                             hipStream_t stream);
+// cq, qh: the MFMA scan's guard constants and fp16 queries (null: not written)
 hipError_t launch_prep_iq(const float* iq, const float* iw, int64_t n_q, float* qd, float* wq,
-                          hipStream_t stream, float* cq = nullptr);
+                          hipStream_t stream, float* cq = nullptr, _Float16* qh = nullptr);
 hipError_t launch_codec_probe(float* e4m3_dec, float* e4m3_dec16, float* fp4_dec16,
                               const float* x, int64_t n, uint8_t* e4m3_enc, uint8_t* e2m1_enc,
                               hipStream_t stream);
@@ -28,7 +29,7 @@ hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B,
 // MFMA scan of a multi-query chunk with guard-band bounds (csa2_chunk.hip):
 // per block of 8 positions, the largest lower-bound and upper-bound score keys
 hipError_t launch_scan_mma(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
-                           const float* qd, const float* wq, const float* cq,
+                           const _Float16* qh, const float* wq, const float* cq,
                            const int32_t* n_vis, uint32_t* bkeys_lo, uint32_t* bkeys_hi,
                            hipStream_t stream, hipEvent_t start = nullptr,
                            hipEvent_t stop = nullptr);

@@ -111,7 +111,8 @@ __global__ __launch_bounds__(256) void k_quant_fp8(const float* __restrict__ x, 
 __global__ __launch_bounds__(256) void k_prep_iq(const float* __restrict__ iq,
                                                  const float* __restrict__ iw, int64_t n_q,
                                                  float* __restrict__ qd, float* __restrict__ wq,
-                                                 float* __restrict__ cq) {
+                                                 float* __restrict__ cq,
+                                                 _Float16* __restrict__ qh) {
     __shared__ float sd[kIdxHeads];
     const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
     const int64_t bq = blockIdx.x;
@@ -122,15 +123,16 @@ __global__ __launch_bounds__(256) void k_prep_iq(const float* __restrict__ iq,
     const uint32_t c = (sq == 0.0f) ? ((__float_as_uint(x) >> 24) & 0x80u) : e4m3_encode(x / sq);
     const float v = e4m3_decode_bits(c);
     qd[(bq * kIdxHeads + h) * kIdxDim + lane] = v;
+    if (qh != nullptr) qh[(bq * kIdxHeads + h) * kIdxDim + lane] = (_Float16)v;  // exact
     const float w = iw[bq * kIdxHeads + h] * sq;
     if (lane == 0) wq[bq * kIdxHeads + h] = w;
     if (cq != nullptr) {
         // guard-band constant of the MFMA scan (csa2_chunk.hip):
-        // C_q = (1 + 2^-10) sum_h |w'_h| 2^-16 448 ||q_h||_1
+        // C'_q = (1 + 2^-10) (2^-16 + 2^-18) 448 sum_h |w'_h| ||q_h||_1
         float l1 = fabsf(v);
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) l1 += __shfl_xor(l1, o, 64);
-        if (lane == 0) sd[h] = fabsf(w) * (0x1p-16f * 448.0f * l1);
+        if (lane == 0) sd[h] = fabsf(w) * ((0x1p-16f + 0x1p-18f) * 448.0f * l1);
         __syncthreads();
         if (threadIdx.x == 0) cq[bq] = (sd[0] + sd[1] + sd[2] + sd[3]) * (1.0f + 0x1p-10f);
     }
@@ -188,9 +190,9 @@ hipError_t launch_quant_fp8(const float* x, int64_t n_rows, int dim, int layout,
 }
 
 hipError_t launch_prep_iq(const float* iq, const float* iw, int64_t n_q, float* qd, float* wq,
-                          hipStream_t stream, float* cq) {
+                          hipStream_t stream, float* cq, _Float16* qh) {
     hipLaunchKernelGGL(k_prep_iq, dim3((unsigned)n_q), dim3(256), 0, stream, iq, iw, n_q, qd, wq,
-                       cq);
+                       cq, qh);
     return hipGetLastError();
 }
 
