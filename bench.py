@@ -314,7 +314,7 @@ def run_chunk_bench(args, wl):
     scan_tfs = flops / (scan_mean * 1e-3) / 1e12
     peak = 2500.0
     rl = {"bound": "mfma", "achieved": round(scan_tfs, 2), "peak": peak, "unit": "TFLOP/s",
-          "frac": round(scan_tfs / peak, 4), "traffic": None,
+          "frac": round(scan_tfs / peak, 4), "traffic": load_traffic().get("k_scan_mma"),
           "kernel": "k_scan_mma (Full-layer indexer bounds of 128 chunk queries, fp16 MFMA)",
           "flops_per_launch": flops, "mean_us": round(scan_mean * 1e3, 2)}
     return {
@@ -402,6 +402,7 @@ def roofline_entry(name, what, ms_list, bytes_per_launch, launches_per_step, ms_
 KERNEL_SOURCES = {
     "k_attn": ["csa2_attn.hip", "csa2_device.hpp", "csa2_internal.hpp"],
     "k_scan": ["csa2_index.hip", "csa2_device.hpp", "csa2_internal.hpp"],
+    "k_scan_mma": ["csa2_chunk.hip", "csa2_device.hpp", "csa2_internal.hpp"],
 }
 
 
@@ -456,14 +457,14 @@ def main():
         sys.exit(3)
     from compressed_kv_cache_decode_amd import synth
     wl = synth.WORKLOADS[args.workload]
+    if args.copy_calibration_mb:
+        copy_calibration(args.copy_calibration_mb)
     if wl.Q != 1:
         print(json.dumps(run_chunk_bench(args, wl)), flush=True)
         return
     log(f"workload {wl.name}: drawing inputs (seed {wl.seed})")
     inp = synth.decode_inputs(wl)
     csa2, sets = build_sets(args, wl, inp)
-    if args.copy_calibration_mb:
-        copy_calibration(args.copy_calibration_mb)
     elapsed, kernel_ms, eager_elapsed = time_gpu(args, wl, csa2, sets)
 
     total_bytes, scan_bytes = step_bytes(wl)

@@ -700,16 +700,13 @@ __device__ __forceinline__ void select_into(const KeySrc& ks, int K, int32_t* ou
     }
 }
 
-// Full layer: best P blocks (pool), then the best K positions inside it.
-// pool_out may be null (internal pool).
-__global__ __launch_bounds__(kSelThreads) void k_select_full(
-    const uint32_t* __restrict__ keys, const uint32_t* __restrict__ bkeys, int64_t cap,
-    const int32_t* __restrict__ n_vis, int P, int K, int32_t* __restrict__ pool_out,
-    int32_t* __restrict__ topk_out, const int32_t* __restrict__ active) {
-    __shared__ SelShared sh;
-    const int64_t bq = blockIdx.x;
-    if (active != nullptr && !active[bq]) return;  // uniform over the workgroup
-    const int nv = clamp_nvis(n_vis[bq], cap);
+// Full layer for query bq: best P blocks (pool), then the best K positions
+// inside it.  pool_out may be null (internal pool).
+__device__ __forceinline__ void select_full_query(const uint32_t* __restrict__ keys,
+                                                  const uint32_t* __restrict__ bkeys, int64_t cap,
+                                                  int64_t bq, int nv, int P, int K,
+                                                  int32_t* pool_out, int32_t* topk_out,
+                                                  SelShared& sh) {
     KeySrc blocks{bkeys + bq * (cap / kBlock), nullptr, ((int64_t)nv + kBlock - 1) / kBlock, nv, 0};
     select_into(blocks, P, pool_out ? pool_out + bq * P : nullptr, sh.pool, sh);
     __syncthreads();
@@ -717,13 +714,32 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(
     select_into(pos, K, topk_out + bq * K, nullptr, sh);
 }
 
-// Reindex: best K positions of the compact pool-ordered keys.
+__global__ __launch_bounds__(kSelThreads) void k_select_full(
+    const uint32_t* __restrict__ keys, const uint32_t* __restrict__ bkeys, int64_t cap,
+    const int32_t* __restrict__ n_vis, int P, int K, int32_t* __restrict__ pool_out,
+    int32_t* __restrict__ topk_out) {
+    __shared__ SelShared sh;
+    const int64_t bq = blockIdx.x;
+    select_full_query(keys, bkeys, cap, bq, clamp_nvis(n_vis[bq], cap), P, K, pool_out, topk_out,
+                      sh);
+}
+
+// Reindex: best K positions of the compact pool-ordered keys.  With `flag`
+// set, a query whose flag is 1 instead takes the Full layer's selection over
+// its exact per-position keys (keys / bkeys, K blocks then K positions): the
+// multi-query MFMA scan's fallback for candidates that overflowed the pool.
 __global__ __launch_bounds__(kSelThreads) void k_select_pool(
     const uint32_t* __restrict__ ckeys, const int32_t* __restrict__ pool, int P,
-    const int32_t* __restrict__ n_vis, int64_t cap, int K, int32_t* __restrict__ topk_out) {
+    const int32_t* __restrict__ n_vis, int64_t cap, int K, int32_t* __restrict__ topk_out,
+    const int32_t* __restrict__ flag, const uint32_t* __restrict__ keys,
+    const uint32_t* __restrict__ bkeys) {
     __shared__ SelShared sh;
     const int64_t bq = blockIdx.x;
     const int nv = clamp_nvis(n_vis[bq], cap);
+    if (flag != nullptr && flag[bq]) {  // uniform over the workgroup
+        select_full_query(keys, bkeys, cap, bq, nv, K, K, nullptr, topk_out, sh);
+        return;
+    }
     const int64_t nbv = ((int64_t)nv + kBlock - 1) / kBlock;
     for (int j = threadIdx.x; j < P; j += kSelThreads) {
         const int32_t blk = pool[bq * P + j];
@@ -842,18 +858,18 @@ hipError_t launch_pool_score(const uint8_t* ikc, const float* iks, int64_t cap, 
 
 hipError_t launch_select_full(const uint32_t* keys, const uint32_t* bkeys, int64_t cap,
                               const int32_t* n_vis, int64_t n_queries, int P, int K,
-                              int32_t* pool_out, int32_t* topk_out, hipStream_t stream,
-                              const int32_t* active) {
+                              int32_t* pool_out, int32_t* topk_out, hipStream_t stream) {
     hipLaunchKernelGGL(k_select_full, dim3((unsigned)n_queries), dim3(kSelThreads), 0, stream, keys,
-                       bkeys, cap, n_vis, P, K, pool_out, topk_out, active);
+                       bkeys, cap, n_vis, P, K, pool_out, topk_out);
     return hipGetLastError();
 }
 
 hipError_t launch_select_pool(const uint32_t* ckeys, const int32_t* pool, int P,
                               const int32_t* n_vis, int64_t cap, int64_t n_queries, int K,
-                              int32_t* topk_out, hipStream_t stream) {
+                              int32_t* topk_out, hipStream_t stream, const int32_t* flag,
+                              const uint32_t* keys, const uint32_t* bkeys) {
     hipLaunchKernelGGL(k_select_pool, dim3((unsigned)n_queries), dim3(kSelThreads), 0, stream,
-                       ckeys, pool, P, n_vis, cap, K, topk_out);
+                       ckeys, pool, P, n_vis, cap, K, topk_out, flag, keys, bkeys);
     return hipGetLastError();
 }
 

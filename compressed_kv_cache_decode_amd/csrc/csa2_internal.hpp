@@ -47,11 +47,13 @@ hipError_t launch_pool_score(const uint8_t* ikc, const float* iks, int64_t cap, 
                              const int32_t* pool, int P, uint32_t* ckeys, hipStream_t stream);
 hipError_t launch_select_full(const uint32_t* keys, const uint32_t* bkeys, int64_t cap,
                               const int32_t* n_vis, int64_t n_queries, int P, int K,
-                              int32_t* pool_out, int32_t* topk_out, hipStream_t stream,
-                              const int32_t* active = nullptr);
+                              int32_t* pool_out, int32_t* topk_out, hipStream_t stream);
+// flag (with keys / bkeys): null, or one per query; flagged queries take the
+// Full layer's selection over exact per-position keys instead of the pool
 hipError_t launch_select_pool(const uint32_t* ckeys, const int32_t* pool, int P,
                               const int32_t* n_vis, int64_t cap, int64_t n_queries, int K,
-                              int32_t* topk_out, hipStream_t stream);
+                              int32_t* topk_out, hipStream_t stream, const int32_t* flag = nullptr,
+                              const uint32_t* keys = nullptr, const uint32_t* bkeys = nullptr);
 
 struct AttnArgs {
     const float* q;          // [n_q][H][128]
