@@ -80,15 +80,12 @@ __global__ __launch_bounds__(256) void k_scan(const uint8_t* __restrict__ ikc,
                                               const float* __restrict__ wq,
                                               const int32_t* __restrict__ n_vis,
                                               uint32_t* __restrict__ keys,
-                                              uint32_t* __restrict__ bkeys,
-                                              const int32_t* __restrict__ active) {
+                                              uint32_t* __restrict__ bkeys) {
     const int b = blockIdx.y;
     const int64_t p0 = (int64_t)blockIdx.x * 256;
     const int64_t p = p0 + threadIdx.x;
     int nv_max = 0;
-    for (int q = 0; q < Q; ++q)
-        if (active == nullptr || active[(int64_t)b * Q + q])
-            nv_max = max(nv_max, clamp_nvis(n_vis[(int64_t)b * Q + q], cap));
+    for (int q = 0; q < Q; ++q) nv_max = max(nv_max, clamp_nvis(n_vis[(int64_t)b * Q + q], cap));
     if (p0 >= nv_max) return;  // uniform over the block
     // cap is a multiple of 64, so a wave is either wholly inside or wholly past it
     if (p0 + (threadIdx.x & ~63) >= cap) return;
@@ -100,7 +97,6 @@ __global__ __launch_bounds__(256) void k_scan(const uint8_t* __restrict__ ikc,
     const int64_t nb = cap / kBlock;
     for (int q = 0; q < Q; ++q) {
         const int64_t bq = (int64_t)b * Q + q;
-        if (active != nullptr && !active[bq]) continue;  // uniform
         const int nv = clamp_nvis(n_vis[bq], cap);
         if (p0 >= nv) continue;  // uniform
         const float s = score_row(raw, sigma, qd + bq * kIdxHeads * kIdxDim, wq + bq * kIdxHeads);
@@ -272,10 +268,12 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kSelRegSlots = 16384;             // slots held in registers
 constexpr int kSelBins = 2048;
+constexpr int kSelSub = 4;  // register path: counters per bin, picked by lane & 3
 static_assert(kSelBins >= kMaxTopk, "the histogram area stages a top-K row");
 
 struct SelShared {
-    uint32_t hist[kSelBins + 3 * 16 + 16 + 2];  // also holds the register path's state
+    // also holds the register path's state (SelRegShared)
+    alignas(16) uint32_t hist[kSelBins * kSelSub + 3 * kSelWaves + 4];
     uint32_t keys[1];  // unused by the streaming path (keys are re-read)
     int32_t pool[kMaxPoolBlocks];
     uint32_t red[3][kSelWaves];
@@ -536,11 +534,16 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
 }
 
+// Each bin has kSelSub counters and lane l adds to counter l % kSelSub, so
+// lanes of one atomic instruction that land in the same bin still hit
+// different words.
 struct SelRegShared {
-    uint32_t hist[kSelBins];
+    alignas(16) uint32_t hist[kSelBins * kSelSub];
     uint32_t part[3][kSelWaves];
-    uint32_t pick[2];
+    uint32_t pick[3];
 };
+static_assert(sizeof(SelRegShared) <= sizeof(SelShared::hist), "register state fits the histogram area");
+static_assert(kSelSub == 4, "a bin's counters are read as one uint4");
 
 __device__ __forceinline__ Threshold threshold_reg(const uint32_t (&k)[kSelKpt], int K,
                                                    SelRegShared& sh) {
@@ -574,16 +577,27 @@ __device__ __forceinline__ Threshold threshold_reg(const uint32_t (&k)[kSelKpt],
         const int shift = bits > 11 ? bits - 11 : 0;
         const int nbins = (int)(width >> shift) + 1;
         __syncthreads();  // earlier readers of hist / part are done
-        sh.hist[2 * tid] = 0;
-        sh.hist[2 * tid + 1] = 0;
+        static_assert(kSelBins * kSelSub == 8 * kSelThreads, "two 16-byte clears per thread");
+        reinterpret_cast<uint4*>(sh.hist)[2 * tid] = make_uint4(0u, 0u, 0u, 0u);
+        reinterpret_cast<uint4*>(sh.hist)[2 * tid + 1] = make_uint4(0u, 0u, 0u, 0u);
         __syncthreads();
+        const uint32_t sub = (uint32_t)lane & (kSelSub - 1);
 #pragma unroll
         for (int i = 0; i < kSelKpt; ++i)
-            if (k[i] >= lo && k[i] <= hi) atomicAdd(&sh.hist[(k[i] - lo) >> shift], 1u);
+            if (k[i] >= lo && k[i] <= hi)
+                atomicAdd(&sh.hist[((k[i] - lo) >> shift) * kSelSub + sub], 1u);
         __syncthreads();
         // thread t owns bins nbins-1-2t and nbins-2-2t (descending order)
         const int b0 = nbins - 1 - 2 * tid, b1 = b0 - 1;
-        const uint32_t h0 = b0 >= 0 ? sh.hist[b0] : 0u, h1 = b1 >= 0 ? sh.hist[b1] : 0u;
+        uint32_t h0 = 0, h1 = 0;
+        if (b0 >= 0) {
+            const uint4 c = reinterpret_cast<const uint4*>(sh.hist)[b0];
+            h0 = c.x + c.y + c.z + c.w;
+        }
+        if (b1 >= 0) {
+            const uint4 c = reinterpret_cast<const uint4*>(sh.hist)[b1];
+            h1 = c.x + c.y + c.z + c.w;
+        }
         const uint32_t mine = h0 + h1;
         const uint32_t incl = wave_incl_scan(mine);
         if (lane == 63) sh.part[0][wave] = incl;
@@ -591,12 +605,12 @@ __device__ __forceinline__ Threshold threshold_reg(const uint32_t (&k)[kSelKpt],
         uint32_t above = incl - mine;
         for (int w = 0; w < wave; ++w) above += sh.part[0][w];
         if (above < remaining && above + mine >= remaining) {
-            if (above + h0 >= remaining) { sh.pick[0] = (uint32_t)b0; sh.pick[1] = above; }
-            else { sh.pick[0] = (uint32_t)b1; sh.pick[1] = above + h0; }
+            if (above + h0 >= remaining) { sh.pick[0] = (uint32_t)b0; sh.pick[1] = above; sh.pick[2] = h0; }
+            else { sh.pick[0] = (uint32_t)b1; sh.pick[1] = above + h0; sh.pick[2] = h1; }
         }
         __syncthreads();
         const uint32_t d = sh.pick[0];
-        const uint32_t in_bin = sh.hist[d];
+        const uint32_t in_bin = sh.pick[2];
         remaining -= sh.pick[1];
         const uint32_t new_lo = lo + (d << shift);
         const uint32_t span = (shift == 0) ? 0u : ((1u << shift) - 1u);
@@ -618,10 +632,10 @@ __device__ __forceinline__ uint32_t umin_opaque(uint32_t a, uint32_t b) {
 // exclusive prefix sum over the 64 lanes
 __device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v) { return wave_incl_scan(v) - v; }
 
-// Indices are ranked into an LDS stage (`lds_out` itself when given, else the
-// histogram area, so K <= 2048 there), then written out in one pass.  Keys
-// above the threshold are all taken; keys equal to it are taken in slot
-// order until the quota is met.
+// Keys above the threshold are all taken; keys equal to it are taken in slot
+// order until the quota is met.  With an LDS copy requested (`lds_out`), the
+// indices are ranked into it and then written out in one coalesced pass;
+// otherwise each lane writes its ranks straight to `out`.
 template <class IDX>
 __device__ __forceinline__ void compact_reg(const uint32_t (&k)[kSelKpt], const Threshold& th,
                                             int K, IDX index_of, int32_t* out, int32_t* lds_out,
@@ -666,6 +680,16 @@ __device__ __forceinline__ void compact_reg(const uint32_t (&k)[kSelKpt], const 
     for (; eq_take != 0 && em != 0; --eq_take) {
         takem |= em & (0u - em);
         em &= em - 1u;
+    }
+    if (lds_out == nullptr) {  // global row only: write each rank where it goes
+        while (takem != 0) {
+            const int i = __builtin_ctz(takem);
+            if (rank < (uint32_t)K) out[rank] = index_of(wave * 1024 + 16 * lane + i);
+            ++rank;
+            takem &= takem - 1u;
+        }
+        for (int i = (int)total + tid; i < K; i += kSelThreads) out[i] = -1;
+        return;
     }
     while (takem != 0) {
         const int i = __builtin_ctz(takem);
@@ -741,13 +765,31 @@ __global__ __launch_bounds__(kSelThreads) void k_select_pool(
         return;
     }
     const int64_t nbv = ((int64_t)nv + kBlock - 1) / kBlock;
-    for (int j = threadIdx.x; j < P; j += kSelThreads) {
-        const int32_t blk = pool[bq * P + j];
-        sh.pool[j] = (blk >= 0 && blk < nbv) ? blk : -1;
+    const KeySrc ks{ckeys + bq * (int64_t)P * kBlock, sh.pool, (int64_t)P * kBlock, nv, 2};
+    auto stage_pool = [&]() {
+        for (int j = threadIdx.x; j < P; j += kSelThreads) {
+            const int32_t blk = pool[bq * P + j];
+            sh.pool[j] = (blk >= 0 && blk < nbv) ? blk : -1;
+        }
+    };
+    if (ks.n <= kSelRegSlots) {
+        // compact keys do not go through the pool: their loads go out first,
+        // and the pool (needed only to name the selected positions) is staged
+        // meanwhile; the threshold search's first barrier orders it before
+        // compact_reg reads it
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        uint32_t k[kSelKpt];
+        ks.load16((int64_t)wave * 1024 + 16 * lane, k);
+        stage_pool();
+        SelRegShared& rs = *reinterpret_cast<SelRegShared*>(&sh.hist[0]);
+        const Threshold th = threshold_reg(k, K, rs);
+        compact_reg(k, th, K, [&](int64_t s) { return ks.index(s); }, topk_out + bq * K, nullptr,
+                    rs);
+    } else {
+        stage_pool();
+        __syncthreads();
+        select_into(ks, K, topk_out + bq * K, nullptr, sh);
     }
-    __syncthreads();
-    KeySrc ks{ckeys + bq * (int64_t)P * kBlock, sh.pool, (int64_t)P * kBlock, nv, 2};
-    select_into(ks, K, topk_out + bq * K, nullptr, sh);
 }
 
 // Candidate blocks of the multi-query MFMA scan.  x = the K-th largest
@@ -833,15 +875,24 @@ hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B,
                        const int32_t* active) {
     dim3 grid((unsigned)((cap + 255) / 256), (unsigned)B);
     // a few queries per sequence: k_scan reads them through the scalar cache;
-    // many (the replay chunk): k_scan_multi stages them in LDS
-    auto kern = Q >= 4 ? k_scan_multi : k_scan;
-    if (start != nullptr && stop != nullptr) {
-        // the runtime records `start` / `stop` immediately around this dispatch
-        hipExtLaunchKernelGGL(kern, grid, dim3(256), 0, stream, start, stop, 0, ikc, iks, cap, Q,
-                              qd, wq, n_vis, keys, bkeys, active);
+    // many (the replay chunk): k_scan_multi stages them in LDS, and only it
+    // takes an active mask
+    if (Q < 4 && active != nullptr) return hipErrorInvalidValue;
+    if (Q >= 4) {
+        if (start != nullptr && stop != nullptr) {
+            // the runtime records `start` / `stop` immediately around this dispatch
+            hipExtLaunchKernelGGL(k_scan_multi, grid, dim3(256), 0, stream, start, stop, 0, ikc,
+                                  iks, cap, Q, qd, wq, n_vis, keys, bkeys, active);
+        } else {
+            hipLaunchKernelGGL(k_scan_multi, grid, dim3(256), 0, stream, ikc, iks, cap, Q, qd, wq,
+                               n_vis, keys, bkeys, active);
+        }
+    } else if (start != nullptr && stop != nullptr) {
+        hipExtLaunchKernelGGL(k_scan, grid, dim3(256), 0, stream, start, stop, 0, ikc, iks, cap, Q,
+                              qd, wq, n_vis, keys, bkeys);
     } else {
-        hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, ikc, iks, cap, Q, qd, wq, n_vis,
-                           keys, bkeys, active);
+        hipLaunchKernelGGL(k_scan, grid, dim3(256), 0, stream, ikc, iks, cap, Q, qd, wq, n_vis,
+                           keys, bkeys);
     }
     return hipGetLastError();
 }
