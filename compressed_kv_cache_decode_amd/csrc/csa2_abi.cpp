@@ -217,8 +217,9 @@ __attribute__((visibility("default"))) int csa2_index_full_timed(
     if (mma_path(Q, pool_blocks)) {
         // block bounds on MFMA -> candidate blocks (upper bound reaches the
         // K-th largest lower bound) -> exact rescore and top-K inside them;
-        // queries whose candidates overflow the pool are rescored by the
-        // exact scan and take the plain Full-layer selection instead
+        // a query whose candidates overflow the pool is rescored over all its
+        // positions by its selection workgroup and takes the plain Full-layer
+        // selection instead
         const int Pc = cand_pool_blocks(topk);
         float* cq = reinterpret_cast<float*>(w + L.cq);
         _Float16* qh = reinterpret_cast<_Float16*>(w + L.qh);
@@ -233,14 +234,11 @@ __attribute__((visibility("default"))) int csa2_index_full_timed(
         if (e == hipSuccess)
             e = launch_cand_pool(bkeys, bkeys_hi, cap, n_vis, nq, topk, Pc, cpool, flag, stream);
         if (e == hipSuccess)
-            e = launch_scan(ik_codes, ik_sigma, cap, B, Q, qd, wq, n_vis, keys, bkeys, stream,
-                            nullptr, nullptr, flag);
-        if (e == hipSuccess)
             e = launch_pool_score(ik_codes, ik_sigma, cap, B, Q, iq, iw, n_vis, cpool, Pc, ckeys,
                                   stream);
         if (e == hipSuccess)
             e = launch_select_pool(ckeys, cpool, Pc, n_vis, cap, nq, topk, topk_idx, stream, flag,
-                                   keys, bkeys);
+                                   ik_codes, ik_sigma, qd, wq, Q, keys, bkeys);
         return hip_status(e);
     }
 

@@ -42,7 +42,7 @@
 // same scores, bit for bit, as the VALU scan) and selecting there gives the
 // exact top-K with its tie rule, as the candidate blocks are listed in
 // ascending order.  A query whose candidate blocks do not fit the pool is
-// flagged and recomputed by the exact VALU scan.
+// flagged, and the selection kernel rescores all its positions exactly.
 #include <hip/hip_ext.h>
 
 #include "csa2_device.hpp"
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kMmaThreads) __attribute__((amdgpu_waves_per_eu(4))
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.y;
     const int64_t p0 = (int64_t)blockIdx.x * kMmaPos;
-    const int nv_max = workgroup_nv_max(n_vis, nullptr, b, Q, cap, red);
+    const int nv_max = workgroup_nv_max(n_vis, b, Q, cap, red);
     if (p0 >= nv_max) return;  // uniform over the workgroup
     const int64_t nb = cap / kBlock;
 

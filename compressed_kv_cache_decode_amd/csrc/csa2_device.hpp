@@ -178,17 +178,14 @@ __device__ __forceinline__ int clamp_nvis(int32_t n, int64_t cap) {
     return n < 0 ? 0 : (n > cap ? (int)cap : n);
 }
 
-// Largest visible count over the Q queries of sequence b (queries whose
-// `active` flag is 0 are left out; null = all), read by the workgroup's
-// threads in parallel and reduced through LDS.  Call from every thread.
-__device__ __forceinline__ int workgroup_nv_max(const int32_t* __restrict__ n_vis,
-                                                const int32_t* __restrict__ active, int b, int Q,
+// Largest visible count over the Q queries of sequence b, read by the
+// workgroup's threads in parallel and reduced through LDS.  Call from every
+// thread.
+__device__ __forceinline__ int workgroup_nv_max(const int32_t* __restrict__ n_vis, int b, int Q,
                                                 int64_t cap, int* red) {
     int m = 0;
-    for (int q = threadIdx.x; q < Q; q += blockDim.x) {
-        const int64_t bq = (int64_t)b * Q + q;
-        if (active == nullptr || active[bq]) m = max(m, clamp_nvis(n_vis[bq], cap));
-    }
+    for (int q = threadIdx.x; q < Q; q += blockDim.x)
+        m = max(m, clamp_nvis(n_vis[(int64_t)b * Q + q], cap));
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o, 64));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;

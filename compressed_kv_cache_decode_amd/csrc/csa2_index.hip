@@ -68,6 +68,33 @@ __device__ __forceinline__ void load_ik_row(const uint8_t* __restrict__ ikc, int
         raw[g] = load16_stream(ikc + ik_offset(row, g));
 }
 
+// Keys of one query over its nv visible positions (and the block keys of the
+// blocks they fill), computed by a whole workgroup of `nthreads` threads with
+// k_scan's arithmetic: the replay chunk's fallback for a query whose MFMA
+// candidates overflowed.  Positions past nv in the last block get key 0.
+__device__ __forceinline__ void scan_query_exact(const uint8_t* __restrict__ ikc,
+                                                 const float* __restrict__ iks, int64_t row0,
+                                                 const float* __restrict__ qd,
+                                                 const float* __restrict__ wq, int nv, int nthreads,
+                                                 uint32_t* __restrict__ keys,
+                                                 uint32_t* __restrict__ bkeys) {
+    const int64_t nv8 = ((int64_t)nv + kBlock - 1) / kBlock * kBlock;
+    for (int64_t p0 = 0; p0 < nv8; p0 += nthreads) {  // uniform trip count
+        const int64_t p = p0 + threadIdx.x;
+        uint32_t key = 0u;
+        if (p < nv) {
+            uint4 raw[4];
+            load_ik_row(ikc, row0 + p, raw);
+            key = score_key(score_row(raw, iks[row0 + p], qd, wq));
+        }
+        const uint32_t bk = max8_u32(key);  // every lane of the wave takes part
+        if (p < nv8) {
+            keys[p] = key;
+            if ((threadIdx.x & 7) == 0) bkeys[p >> 3] = bk;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Full-layer scan.  grid = (ceil(cap / 256), B); 256 threads, one position each.
 // For every query of the sequence: key of each position, and the max key of
@@ -121,15 +148,14 @@ __global__ __launch_bounds__(256) void k_scan_multi(const uint8_t* __restrict__ 
                                                     const float* __restrict__ wq,
                                                     const int32_t* __restrict__ n_vis,
                                                     uint32_t* __restrict__ keys,
-                                                    uint32_t* __restrict__ bkeys,
-                                                    const int32_t* __restrict__ active) {
+                                                    uint32_t* __restrict__ bkeys) {
     __shared__ __attribute__((aligned(16))) float sq[kScanQChunk * kIdxHeads * kIdxDim];
     __shared__ float sw[kScanQChunk * kIdxHeads];
     __shared__ int red[4];
     const int b = blockIdx.y;
     const int64_t p0 = (int64_t)blockIdx.x * 256;
     const int64_t p = p0 + threadIdx.x;
-    const int nv_max = workgroup_nv_max(n_vis, active, b, Q, cap, red);
+    const int nv_max = workgroup_nv_max(n_vis, b, Q, cap, red);
     if (p0 >= nv_max) return;  // uniform over the block
     // cap is a multiple of 64: a wave is wholly inside or wholly past it; waves
     // past it still take part in the barriers below
@@ -169,7 +195,6 @@ __global__ __launch_bounds__(256) void k_scan_multi(const uint8_t* __restrict__ 
         if (!live) continue;
         for (int j = 0; j < nq; ++j) {
             const int64_t bq = (int64_t)b * Q + q0 + j;
-            if (active != nullptr && !active[bq]) continue;  // uniform
             const int nv = clamp_nvis(n_vis[bq], cap);
             if (p0 >= nv) continue;  // uniform
             // the sequence of IEEE operations of score_row
@@ -748,20 +773,35 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(
                       sh);
 }
 
-// Reindex: best K positions of the compact pool-ordered keys.  With `flag`
-// set, a query whose flag is 1 instead takes the Full layer's selection over
-// its exact per-position keys (keys / bkeys, K blocks then K positions): the
-// multi-query MFMA scan's fallback for candidates that overflowed the pool.
+// Reindex: best K positions of the compact pool-ordered keys.  With `fb`
+// set (the multi-query MFMA scan), a query whose flag is 1 instead has all
+// its visible positions scored exactly here (into fb.keys / fb.bkeys) and
+// takes the Full layer's selection over them, K blocks then K positions: the
+// fallback for candidates that overflowed the pool.
+struct ExactFallback {
+    const int32_t* flag;
+    const uint8_t* ikc;
+    const float* iks;
+    const float* qd;
+    const float* wq;
+    uint32_t* keys;
+    uint32_t* bkeys;
+    int Q;
+};
+
 __global__ __launch_bounds__(kSelThreads) void k_select_pool(
     const uint32_t* __restrict__ ckeys, const int32_t* __restrict__ pool, int P,
     const int32_t* __restrict__ n_vis, int64_t cap, int K, int32_t* __restrict__ topk_out,
-    const int32_t* __restrict__ flag, const uint32_t* __restrict__ keys,
-    const uint32_t* __restrict__ bkeys) {
+    ExactFallback fb) {
     __shared__ SelShared sh;
     const int64_t bq = blockIdx.x;
     const int nv = clamp_nvis(n_vis[bq], cap);
-    if (flag != nullptr && flag[bq]) {  // uniform over the workgroup
-        select_full_query(keys, bkeys, cap, bq, nv, K, K, nullptr, topk_out, sh);
+    if (fb.flag != nullptr && fb.flag[bq]) {  // uniform over the workgroup
+        scan_query_exact(fb.ikc, fb.iks, (bq / fb.Q) * cap, fb.qd + bq * kIdxHeads * kIdxDim,
+                         fb.wq + bq * kIdxHeads, nv, kSelThreads, fb.keys + bq * cap,
+                         fb.bkeys + bq * (cap / kBlock));
+        __syncthreads();  // the keys are the workgroup's own global writes
+        select_full_query(fb.keys, fb.bkeys, cap, bq, nv, K, K, nullptr, topk_out, sh);
         return;
     }
     const int64_t nbv = ((int64_t)nv + kBlock - 1) / kBlock;
@@ -871,27 +911,17 @@ __global__ __launch_bounds__(kSelThreads) void k_cand_pool(
 // ---------------------------------------------------------------------------
 hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                        const float* qd, const float* wq, const int32_t* n_vis, uint32_t* keys,
-                       uint32_t* bkeys, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
-                       const int32_t* active) {
+                       uint32_t* bkeys, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     dim3 grid((unsigned)((cap + 255) / 256), (unsigned)B);
     // a few queries per sequence: k_scan reads them through the scalar cache;
-    // many (the replay chunk): k_scan_multi stages them in LDS, and only it
-    // takes an active mask
-    if (Q < 4 && active != nullptr) return hipErrorInvalidValue;
-    if (Q >= 4) {
-        if (start != nullptr && stop != nullptr) {
-            // the runtime records `start` / `stop` immediately around this dispatch
-            hipExtLaunchKernelGGL(k_scan_multi, grid, dim3(256), 0, stream, start, stop, 0, ikc,
-                                  iks, cap, Q, qd, wq, n_vis, keys, bkeys, active);
-        } else {
-            hipLaunchKernelGGL(k_scan_multi, grid, dim3(256), 0, stream, ikc, iks, cap, Q, qd, wq,
-                               n_vis, keys, bkeys, active);
-        }
-    } else if (start != nullptr && stop != nullptr) {
-        hipExtLaunchKernelGGL(k_scan, grid, dim3(256), 0, stream, start, stop, 0, ikc, iks, cap, Q,
+    // many (the replay chunk): k_scan_multi stages them in LDS
+    auto kern = Q >= 4 ? k_scan_multi : k_scan;
+    if (start != nullptr && stop != nullptr) {
+        // the runtime records `start` / `stop` immediately around this dispatch
+        hipExtLaunchKernelGGL(kern, grid, dim3(256), 0, stream, start, stop, 0, ikc, iks, cap, Q,
                               qd, wq, n_vis, keys, bkeys);
     } else {
-        hipLaunchKernelGGL(k_scan, grid, dim3(256), 0, stream, ikc, iks, cap, Q, qd, wq, n_vis,
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, ikc, iks, cap, Q, qd, wq, n_vis,
                            keys, bkeys);
     }
     return hipGetLastError();
@@ -918,9 +948,11 @@ hipError_t launch_select_full(const uint32_t* keys, const uint32_t* bkeys, int64
 hipError_t launch_select_pool(const uint32_t* ckeys, const int32_t* pool, int P,
                               const int32_t* n_vis, int64_t cap, int64_t n_queries, int K,
                               int32_t* topk_out, hipStream_t stream, const int32_t* flag,
-                              const uint32_t* keys, const uint32_t* bkeys) {
+                              const uint8_t* ikc, const float* iks, const float* qd,
+                              const float* wq, int Q, uint32_t* keys, uint32_t* bkeys) {
+    const ExactFallback fb{flag, ikc, iks, qd, wq, keys, bkeys, Q};
     hipLaunchKernelGGL(k_select_pool, dim3((unsigned)n_queries), dim3(kSelThreads), 0, stream,
-                       ckeys, pool, P, n_vis, cap, K, topk_out, flag, keys, bkeys);
+                       ckeys, pool, P, n_vis, cap, K, topk_out, fb);
     return hipGetLastError();
 }
 

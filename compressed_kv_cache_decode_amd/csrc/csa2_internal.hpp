@@ -21,11 +21,10 @@ hipError_t launch_codec_probe(float* e4m3_dec, float* e4m3_dec16, float* fp4_dec
                               const float* x, int64_t n, uint8_t* e4m3_enc, uint8_t* e2m1_enc,
                               hipStream_t stream);
 
-// active: null, or one flag per query; queries whose flag is 0 are skipped
 hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                        const float* qd, const float* wq, const int32_t* n_vis, uint32_t* keys,
                        uint32_t* bkeys, hipStream_t stream, hipEvent_t start = nullptr,
-                       hipEvent_t stop = nullptr, const int32_t* active = nullptr);
+                       hipEvent_t stop = nullptr);
 // MFMA scan of a multi-query chunk with guard-band bounds (csa2_chunk.hip):
 // per block of 8 positions, the largest lower-bound and upper-bound score keys
 hipError_t launch_scan_mma(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
@@ -48,12 +47,16 @@ hipError_t launch_pool_score(const uint8_t* ikc, const float* iks, int64_t cap, 
 hipError_t launch_select_full(const uint32_t* keys, const uint32_t* bkeys, int64_t cap,
                               const int32_t* n_vis, int64_t n_queries, int P, int K,
                               int32_t* pool_out, int32_t* topk_out, hipStream_t stream);
-// flag (with keys / bkeys): null, or one per query; flagged queries take the
-// Full layer's selection over exact per-position keys instead of the pool
+// flag: null, or one per query; a flagged query is instead scored exactly
+// over all its visible positions (ikc / iks with the decoded query qd, wq of
+// Q queries per sequence, keys into keys / bkeys) and takes the Full layer's
+// selection there
 hipError_t launch_select_pool(const uint32_t* ckeys, const int32_t* pool, int P,
                               const int32_t* n_vis, int64_t cap, int64_t n_queries, int K,
                               int32_t* topk_out, hipStream_t stream, const int32_t* flag = nullptr,
-                              const uint32_t* keys = nullptr, const uint32_t* bkeys = nullptr);
+                              const uint8_t* ikc = nullptr, const float* iks = nullptr,
+                              const float* qd = nullptr, const float* wq = nullptr, int Q = 1,
+                              uint32_t* keys = nullptr, uint32_t* bkeys = nullptr);
 
 struct AttnArgs {
     const float* q;          // [n_q][H][128]

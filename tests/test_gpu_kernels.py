@@ -160,7 +160,8 @@ def test_index_full_bit_exact(gpu, oracle_mod, B, Q, cap, nvis, topk, pool):
 def test_index_full_chunk_candidate_overflow(gpu, oracle_mod):
     """Identical key rows tie every score of a query, so every visible block is
     a candidate of the MFMA path and the candidates overflow its pool: the
-    flagged queries must come out of the exact fallback scan unchanged."""
+    flagged queries are rescored exactly by their selection workgroup and
+    must come out unchanged (the lowest positions, by the tie rule)."""
     say("index_full multi-query, all-equal scores (candidate overflow)")
     B, Q, cap = 1, 8, 16384
     x = np.tile(np.random.default_rng(9).standard_normal((1, 1, 64)), (B, cap, 1)).astype(np.float32)
@@ -171,7 +172,8 @@ def test_index_full_chunk_candidate_overflow(gpu, oracle_mod):
     g = np.random.default_rng(10)
     iq = g.standard_normal((B, Q, 4, 64)).astype(np.float32)
     iw = g.random((B, Q, 4)).astype(np.float32)
-    nv = np.array([[16384, 16000, 9000, 8200, 600, 512, 100, 16384]], np.int32)
+    # ragged visible counts (not multiples of 8) among the overflowing queries
+    nv = np.array([[16384, 16001, 9003, 8200, 600, 512, 100, 16384]], np.int32)
     tk_ref, _ = oracle_mod.index_full_batch(ikc.reshape(B, cap, 64), iks.reshape(B, cap), iq, iw,
                                             nv, 512, 0)
     tk = torch.full((B, Q, 512), -7, dtype=torch.int32, device="cuda")
