@@ -91,11 +91,13 @@ class StepSet:
 
     def run(self, scan_timer=None, attn_timer=None):
         c, i = self.csa2, self.inp
-        # write path of the new token of every sequence (position n_ent - 1)
-        c.quant_fp4(i["k_new"], i["v_new"], self.cache.kv_codes, self.cache.kv_scales,
-                    ratio=self.ratio, rope_cs=i["rope_new"], dst_rows=i["rows_new"])
-        c.quant_fp8(i["idx_new"], self.cache.ik_codes, self.cache.ik_sigma,
-                    layout=c.FP8_IDX_TILED, dst_rows=i["rows_new"])
+        # write path of the new token of every sequence (position n_ent - 1):
+        # its FP4 record and its FP8 indexer key, in one launch
+        c.write_entries(i["k_new"], i["v_new"], self.cache.kv_codes, self.cache.kv_scales,
+                        ratio=self.ratio, rope_cs=i["rope_new"], dst_rows=i["rows_new"],
+                        fp8_jobs=[dict(x=i["idx_new"], codes=self.cache.ik_codes,
+                                       sigma=self.cache.ik_sigma, layout=c.FP8_IDX_TILED,
+                                       dst_rows=i["rows_new"])])
         self.stack.step(i["iq"], i["iw"], i["n_vis"], i["q"], i["swk"], i["swv"], i["sks"],
                         i["svs"], i["swa_len"], scan_timer=scan_timer, attn_timer=attn_timer)
 
@@ -268,12 +270,15 @@ def run_chunk_bench(args, wl):
     d = dev_in
 
     def step(cache, scan_timer=None):
-        csa2.quant_fp4(d["k_new"], d["v_new"], cache.kv_codes, cache.kv_scales,
-                       rope_cs=d["rope_new"], dst_rows=rows_new)
-        csa2.quant_fp8(d["idx_new"], cache.ik_codes, cache.ik_sigma, layout=csa2.FP8_IDX_TILED,
-                       dst_rows=rows_new)
-        csa2.quant_fp8(d["swa_k"], swk, sks)
-        csa2.quant_fp8(d["swa_v"], swv, svs)
+        # the chunk's 128 entries (RoPE + FP4), their indexer keys and the
+        # window's K and V, in one launch
+        csa2.write_entries(d["k_new"], d["v_new"], cache.kv_codes, cache.kv_scales,
+                           rope_cs=d["rope_new"], dst_rows=rows_new,
+                           fp8_jobs=[dict(x=d["idx_new"], codes=cache.ik_codes,
+                                          sigma=cache.ik_sigma, layout=csa2.FP8_IDX_TILED,
+                                          dst_rows=rows_new),
+                                     dict(x=d["swa_k"], codes=swk, sigma=sks),
+                                     dict(x=d["swa_v"], codes=swv, sigma=svs)])
         csa2.index_full(cache, d["iq"], d["iw"], d["n_vis"], tk, None, topk=wl.topk,
                         pool_blocks=0, ws=ws, scan_timer=scan_timer)
         csa2.sparse_attn_chunk(d["q"], cache, tk, swk, swv, sks, svs, out, lse)

@@ -43,7 +43,8 @@ STAGE_READ = 2
 STATUS = {0: "ok", -1: "CSA2_E_ARG", -2: "CSA2_E_UNSUPPORTED", -3: "CSA2_E_WORKSPACE",
           -4: "CSA2_E_HIP"}
 
-EXPORTS = ("csa2_quant_fp4", "csa2_quant_fp8", "csa2_index_full", "csa2_index_full_timed",
+EXPORTS = ("csa2_quant_fp4", "csa2_quant_fp8", "csa2_write_entries", "csa2_index_full",
+           "csa2_index_full_timed",
            "csa2_index_reindex",
            "csa2_sparse_attn_decode", "csa2_sparse_attn_decode_timed",
            "csa2_sparse_attn_decode_reuse", "csa2_sparse_attn_chunk",
@@ -53,8 +54,20 @@ EXPORTS = ("csa2_quant_fp4", "csa2_quant_fp8", "csa2_index_full", "csa2_index_fu
 _lib = None
 
 _vp, _i64, _int, _f, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+MAX_FP8_JOBS = 3
+
+
+class _Fp8Job(ctypes.Structure):
+    """csa2_fp8_job of include/csa2.h."""
+    _fields_ = [("x", ctypes.c_void_p), ("n_rows", ctypes.c_int64), ("dim", ctypes.c_int),
+                ("layout", ctypes.c_int), ("dst_rows", ctypes.c_void_p),
+                ("codes", ctypes.c_void_p), ("sigma", ctypes.c_void_p)]
+
+
 _SIGS = {
     "csa2_quant_fp4": (_int, [_vp, _vp, _i64, _int, _vp, _vp, _vp, _vp, _vp]),
+    "csa2_write_entries": (_int, [_vp, _vp, _i64, _int, _vp, _vp, _vp, _vp,
+                                  ctypes.POINTER(_Fp8Job), _int, _vp]),
     "csa2_quant_fp8": (_int, [_vp, _i64, _int, _int, _vp, _vp, _vp, _vp]),
     "csa2_index_full": (_int, [_vp, _vp, _i64, _int, _int, _vp, _vp, _vp, _int, _int, _vp, _vp,
                                _vp, _sz, _vp]),
@@ -207,6 +220,37 @@ def quant_fp8(x, codes, sigma, layout=FP8_ROWS, dst_rows=None, stream=None):
                               _ptr(codes, torch.uint8, "codes"),
                               _ptr(sigma, torch.float32, "sigma"), _stream(stream))
     _check(rc, "csa2_quant_fp8")
+
+
+def write_entries(k_tok, v_tok, kv_codes, kv_scales, ratio=1, rope_cs=None, dst_rows=None,
+                  fp8_jobs=(), stream=None):
+    """quant_fp4(k_tok, v_tok, ...) and quant_fp8 of each job in one launch.
+
+    fp8_jobs: up to 3 dicts with the arguments of quant_fp8: x, codes, sigma,
+    and optionally layout (FP8_ROWS) and dst_rows."""
+    n_tok = k_tok.shape[0] if k_tok.dim() > 1 else 0
+    if k_tok.shape != v_tok.shape or (k_tok.dim() != 2 or k_tok.shape[1] != HEAD_DIM):
+        raise ValueError("k_tok, v_tok must be [n_tok][128]")
+    if len(fp8_jobs) > MAX_FP8_JOBS:
+        raise ValueError(f"at most {MAX_FP8_JOBS} FP8 jobs")
+    n_ent = n_tok // ratio
+    jobs = (_Fp8Job * max(len(fp8_jobs), 1))()
+    for i, jb in enumerate(fp8_jobs):
+        x = jb["x"]
+        if x.dim() != 2:
+            raise ValueError("an FP8 job's x must be [n_rows][dim]")
+        n, dim = x.shape
+        jobs[i] = _Fp8Job(_ptr(x, torch.float32, "x"), n, dim, jb.get("layout", FP8_ROWS),
+                          _ptr(jb.get("dst_rows"), torch.int64, "dst_rows", n),
+                          _ptr(jb["codes"], torch.uint8, "codes"),
+                          _ptr(jb["sigma"], torch.float32, "sigma"))
+    rc = lib().csa2_write_entries(
+        _ptr(k_tok, torch.float32, "k_tok"), _ptr(v_tok, torch.float32, "v_tok"), n_tok, ratio,
+        _ptr(rope_cs, torch.float32, "rope_cs", n_ent * 64),
+        _ptr(dst_rows, torch.int64, "dst_rows", n_ent),
+        _ptr(kv_codes, torch.uint8, "kv_codes"), _ptr(kv_scales, torch.uint8, "kv_scales"),
+        jobs, len(fp8_jobs), _stream(stream))
+    _check(rc, "csa2_write_entries")
 
 
 def index_full(cache, iq, iw, n_vis, topk_idx, pool_idx=None, topk=DEFAULT_TOPK,

@@ -163,18 +163,42 @@ __attribute__((visibility("default"))) size_t csa2_workspace_size(int op, int B,
     }
 }
 
-__attribute__((visibility("default"))) int csa2_quant_fp4(const float* k_tok, const float* v_tok,
-                                                         int64_t n_tok, int ratio,
-                                                         const float* rope_cs,
-                                                         const int64_t* dst_rows,
-                                                         uint8_t* kv_codes, uint8_t* kv_scales,
-                                                         hipStream_t stream) {
+static_assert(CSA2_MAX_FP8_JOBS == kMaxFp8Jobs, "FP8 jobs per write launch");
+
+namespace {
+
+int validate_quant_fp4(const float* k_tok, const float* v_tok, int64_t n_tok, int ratio,
+                       const float* rope_cs, const uint8_t* kv_codes, const uint8_t* kv_scales) {
     if (n_tok < 0) return CSA2_E_ARG;
     if (ratio != 1 && ratio != 2) return CSA2_E_UNSUPPORTED;
     if (ratio == 2 && rope_cs) return CSA2_E_UNSUPPORTED;
     if (n_tok % ratio != 0) return CSA2_E_ARG;
     if (n_tok == 0) return CSA2_OK;
     if (!k_tok || !v_tok || !kv_codes || !kv_scales) return CSA2_E_ARG;
+    return CSA2_OK;
+}
+
+int validate_quant_fp8(const float* x, int64_t n_rows, int dim, int layout, const uint8_t* codes,
+                       const float* sigma) {
+    if (n_rows < 0) return CSA2_E_ARG;
+    if (dim != 64 && dim != 128) return CSA2_E_UNSUPPORTED;
+    if (layout != CSA2_FP8_ROWS && layout != CSA2_FP8_IDX_TILED) return CSA2_E_ARG;
+    if (layout == CSA2_FP8_IDX_TILED && dim != 64) return CSA2_E_UNSUPPORTED;
+    if (n_rows == 0) return CSA2_OK;
+    if (!x || !codes || !sigma) return CSA2_E_ARG;
+    return CSA2_OK;
+}
+
+}  // namespace
+
+__attribute__((visibility("default"))) int csa2_quant_fp4(const float* k_tok, const float* v_tok,
+                                                         int64_t n_tok, int ratio,
+                                                         const float* rope_cs,
+                                                         const int64_t* dst_rows,
+                                                         uint8_t* kv_codes, uint8_t* kv_scales,
+                                                         hipStream_t stream) {
+    const int rc = validate_quant_fp4(k_tok, v_tok, n_tok, ratio, rope_cs, kv_codes, kv_scales);
+    if (rc != CSA2_OK || n_tok == 0) return rc;
     return hip_status(launch_quant_fp4(k_tok, v_tok, n_tok / ratio, ratio, rope_cs, dst_rows,
                                        kv_codes, kv_scales, stream));
 }
@@ -183,13 +207,28 @@ __attribute__((visibility("default"))) int csa2_quant_fp8(const float* x, int64_
                                                          int layout, const int64_t* dst_rows,
                                                          uint8_t* codes, float* sigma,
                                                          hipStream_t stream) {
-    if (n_rows < 0) return CSA2_E_ARG;
-    if (dim != 64 && dim != 128) return CSA2_E_UNSUPPORTED;
-    if (layout != CSA2_FP8_ROWS && layout != CSA2_FP8_IDX_TILED) return CSA2_E_ARG;
-    if (layout == CSA2_FP8_IDX_TILED && dim != 64) return CSA2_E_UNSUPPORTED;
-    if (n_rows == 0) return CSA2_OK;
-    if (!x || !codes || !sigma) return CSA2_E_ARG;
+    const int rc = validate_quant_fp8(x, n_rows, dim, layout, codes, sigma);
+    if (rc != CSA2_OK || n_rows == 0) return rc;
     return hip_status(launch_quant_fp8(x, n_rows, dim, layout, dst_rows, codes, sigma, stream));
+}
+
+__attribute__((visibility("default"))) int csa2_write_entries(
+    const float* k_tok, const float* v_tok, int64_t n_tok, int ratio, const float* rope_cs,
+    const int64_t* dst_rows, uint8_t* kv_codes, uint8_t* kv_scales, const csa2_fp8_job* jobs,
+    int n_jobs, hipStream_t stream) {
+    if (n_jobs < 0 || n_jobs > CSA2_MAX_FP8_JOBS || (n_jobs > 0 && !jobs)) return CSA2_E_ARG;
+    int rc = validate_quant_fp4(k_tok, v_tok, n_tok, ratio, rope_cs, kv_codes, kv_scales);
+    if (rc != CSA2_OK) return rc;
+    Fp8Jobs j{};
+    for (int i = 0; i < n_jobs; ++i) {
+        const csa2_fp8_job& b = jobs[i];
+        rc = validate_quant_fp8(b.x, b.n_rows, b.dim, b.layout, b.codes, b.sigma);
+        if (rc != CSA2_OK) return rc;
+        if (b.n_rows == 0) continue;
+        j.job[j.n++] = Fp8Job{b.x, b.n_rows, b.dim, b.layout, b.dst_rows, b.codes, b.sigma};
+    }
+    const Fp4Job f{k_tok, v_tok, n_tok / ratio, ratio, rope_cs, dst_rows, kv_codes, kv_scales};
+    return hip_status(launch_write_entries(f, j, stream));
 }
 
 __attribute__((visibility("default"))) int csa2_index_full_timed(

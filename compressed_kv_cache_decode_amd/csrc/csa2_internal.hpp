@@ -14,6 +14,33 @@ hipError_t launch_quant_fp4(const float* k, const float* v, int64_t n_ent, int r
 hipError_t launch_quant_fp8(const float* x, int64_t n_rows, int dim, int layout,
                             const int64_t* dst_rows, uint8_t* codes, float* sigma,
                             hipStream_t stream);
+// one-launch write path: FP4 entries (as launch_quant_fp4, n_ent entries) and
+// up to kMaxFp8Jobs FP8 row sets (each as launch_quant_fp8)
+struct Fp4Job {
+    const float* k;
+    const float* v;
+    int64_t n_ent;
+    int ratio;
+    const float* rope_cs;
+    const int64_t* dst_rows;
+    uint8_t* codes;
+    uint8_t* scales;
+};
+struct Fp8Job {
+    const float* x;
+    int64_t n_rows;
+    int dim;
+    int layout;
+    const int64_t* dst_rows;
+    uint8_t* codes;
+    float* sigma;
+};
+constexpr int kMaxFp8Jobs = 3;
+struct Fp8Jobs {
+    Fp8Job job[kMaxFp8Jobs];
+    int n;
+};
+hipError_t launch_write_entries(const Fp4Job& f, const Fp8Jobs& j, hipStream_t stream);
 // cq, qh: the MFMA scan's guard constants and fp16 queries (null: not written)
 hipError_t launch_prep_iq(const float* iq, const float* iw, int64_t n_q, float* qd, float* wq,
                           hipStream_t stream, float* cq = nullptr, _Float16* qh = nullptr);

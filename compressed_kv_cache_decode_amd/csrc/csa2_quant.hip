@@ -15,18 +15,14 @@
 
 namespace csa2 {
 
-// One wave per entry; lane l owns channels 2l and 2l+1 of K and of V, so a
+// Entry e by one wave; lane l owns channels 2l and 2l+1 of K and of V, so a
 // 16-channel scale group is 8 adjacent lanes and one code byte per lane.
-__global__ __launch_bounds__(256) void k_quant_fp4(const float* __restrict__ k,
-                                                   const float* __restrict__ v, int64_t n_ent,
-                                                   int ratio, const float* __restrict__ rope_cs,
-                                                   const int64_t* __restrict__ dst_rows,
-                                                   uint8_t* __restrict__ codes,
-                                                   uint8_t* __restrict__ scales) {
-    const int lane = threadIdx.x & 63;
-    const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (e >= n_ent) return;
-
+__device__ __forceinline__ void quant_fp4_entry(const float* __restrict__ k,
+                                                const float* __restrict__ v, int64_t e, int ratio,
+                                                const float* __restrict__ rope_cs,
+                                                const int64_t* __restrict__ dst_rows,
+                                                uint8_t* __restrict__ codes,
+                                                uint8_t* __restrict__ scales, int lane) {
     float k0, k1, v0, v1;
     if (ratio == 1) {
         const float2 kk = reinterpret_cast<const float2*>(k + e * kHeadDim)[lane];
@@ -73,16 +69,23 @@ __global__ __launch_bounds__(256) void k_quant_fp4(const float* __restrict__ k,
     }
 }
 
-// One wave per row of 64 or 128 values; sigma = fl(amax / 448),
-// code = RNE_E4M3(fl(x / sigma)).
-__global__ __launch_bounds__(256) void k_quant_fp8(const float* __restrict__ x, int64_t n_rows,
-                                                   int dim, int layout,
+__global__ __launch_bounds__(256) void k_quant_fp4(const float* __restrict__ k,
+                                                   const float* __restrict__ v, int64_t n_ent,
+                                                   int ratio, const float* __restrict__ rope_cs,
                                                    const int64_t* __restrict__ dst_rows,
                                                    uint8_t* __restrict__ codes,
-                                                   float* __restrict__ sigma) {
-    const int lane = threadIdx.x & 63;
-    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (r >= n_rows) return;
+                                                   uint8_t* __restrict__ scales) {
+    const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e >= n_ent) return;  // uniform over the wave
+    quant_fp4_entry(k, v, e, ratio, rope_cs, dst_rows, codes, scales, threadIdx.x & 63);
+}
+
+// Row r of 64 or 128 values by one wave; sigma = fl(amax / 448),
+// code = RNE_E4M3(fl(x / sigma)).
+__device__ __forceinline__ void quant_fp8_row(const float* __restrict__ x, int64_t r, int dim,
+                                              int layout, const int64_t* __restrict__ dst_rows,
+                                              uint8_t* __restrict__ codes,
+                                              float* __restrict__ sigma, int lane) {
     const int per = dim / 64;  // channels per lane: 1 or 2
     float xv[2] = {0.0f, 0.0f};
     for (int i = 0; i < per; ++i) xv[i] = x[r * dim + lane * per + i];
@@ -102,6 +105,38 @@ __global__ __launch_bounds__(256) void k_quant_fp8(const float* __restrict__ x, 
         }
     }
     if (lane == 0) sigma[row] = s;
+}
+
+__global__ __launch_bounds__(256) void k_quant_fp8(const float* __restrict__ x, int64_t n_rows,
+                                                   int dim, int layout,
+                                                   const int64_t* __restrict__ dst_rows,
+                                                   uint8_t* __restrict__ codes,
+                                                   float* __restrict__ sigma) {
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= n_rows) return;  // uniform over the wave
+    quant_fp8_row(x, r, dim, layout, dst_rows, codes, sigma, threadIdx.x & 63);
+}
+
+// The write path of new entries in one launch: wave w < n_ent quantises entry
+// w as k_quant_fp4 does, the following waves the rows of the FP8 jobs in
+// order, each as k_quant_fp8 does.
+__global__ __launch_bounds__(256) void k_write_entries(Fp4Job f, Fp8Jobs j) {
+    const int lane = threadIdx.x & 63;
+    int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (w < f.n_ent) {
+        quant_fp4_entry(f.k, f.v, w, f.ratio, f.rope_cs, f.dst_rows, f.codes, f.scales, lane);
+        return;
+    }
+    w -= f.n_ent;
+#pragma unroll
+    for (int i = 0; i < kMaxFp8Jobs; ++i) {
+        if (i < j.n && w < j.job[i].n_rows) {
+            const Fp8Job& b = j.job[i];
+            quant_fp8_row(b.x, w, b.dim, b.layout, b.dst_rows, b.codes, b.sigma, lane);
+            return;
+        }
+        if (i < j.n) w -= j.job[i].n_rows;
+    }
 }
 
 // Indexer query per (sequence, query): per head sq = fl(amax/448), codes
@@ -186,6 +221,15 @@ hipError_t launch_quant_fp8(const float* x, int64_t n_rows, int dim, int layout,
     const unsigned grid = (unsigned)((n_rows + 3) / 4);
     hipLaunchKernelGGL(k_quant_fp8, dim3(grid), dim3(256), 0, stream, x, n_rows, dim, layout,
                        dst_rows, codes, sigma);
+    return hipGetLastError();
+}
+
+hipError_t launch_write_entries(const Fp4Job& f, const Fp8Jobs& j, hipStream_t stream) {
+    int64_t waves = f.n_ent;
+    for (int i = 0; i < j.n; ++i) waves += j.job[i].n_rows;
+    if (waves == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((waves + 3) / 4);
+    hipLaunchKernelGGL(k_write_entries, dim3(grid), dim3(256), 0, stream, f, j);
     return hipGetLastError();
 }
 

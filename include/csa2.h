@@ -140,6 +140,40 @@ int csa2_quant_fp4(const float* k_tok, const float* v_tok, int64_t n_tok, int ra
 int csa2_quant_fp8(const float* x, int64_t n_rows, int dim, int layout, const int64_t* dst_rows,
                    uint8_t* codes, float* sigma, hipStream_t stream);
 
+/* One FP8 row set of csa2_write_entries: the arguments of csa2_quant_fp8. */
+typedef struct csa2_fp8_job {
+    const float* x;
+    int64_t n_rows;
+    int dim;
+    int layout;
+    const int64_t* dst_rows;
+    uint8_t* codes;
+    float* sigma;
+} csa2_fp8_job;
+
+#define CSA2_MAX_FP8_JOBS 3
+
+/*
+ * csa2_write_entries -- the write path of new entries in one launch (the
+ * same pages and sections as csa2_quant_fp4 and csa2_quant_fp8): writes
+ * exactly what csa2_quant_fp4(k_tok, v_tok, n_tok, ratio, rope_cs, dst_rows,
+ * kv_codes, kv_scales) and then csa2_quant_fp8 of each job would write, byte
+ * for byte; e.g. a decode step's new entry and its indexer key, or a replay
+ * chunk's 128 entries, their indexer keys and the window's K and V.
+ *   n_tok        may be 0 (FP8 jobs only); the other FP4 arguments as in
+ *                csa2_quant_fp4.
+ *   jobs         host array of n_jobs (0..CSA2_MAX_FP8_JOBS) descriptors,
+ *                read during the call only; jobs with n_rows 0 are skipped.
+ * The rows written by the FP4 part and by the jobs must not overlap (not
+ * checked).  Errors: CSA2_E_ARG for n_jobs out of range or jobs NULL with
+ * n_jobs > 0; otherwise the first error csa2_quant_fp4 or csa2_quant_fp8
+ * would return for its part.  Nothing is launched on an error.
+ */
+int csa2_write_entries(const float* k_tok, const float* v_tok, int64_t n_tok, int ratio,
+                       const float* rope_cs, const int64_t* dst_rows, uint8_t* kv_codes,
+                       uint8_t* kv_scales, const csa2_fp8_job* jobs, int n_jobs,
+                       hipStream_t stream);
+
 /*
  * csa2_index_full -- Full-layer indexer ("DeepSeek V4.1 Flash: architecture
  * study notes" section 2: Full picks this step's positions, at most 512 per

@@ -58,6 +58,34 @@ def test_quant_validation(lib):
     assert f8(FAKE, 4, 64, 0, None, None, FAKE, None) == -1
 
 
+def test_write_entries_validation(lib):
+    import compressed_kv_cache_decode_amd as csa2
+    w = lib.csa2_write_entries
+    J = csa2._Fp8Job
+
+    def jobs(*js):
+        arr = (J * max(len(js), 1))()
+        for i, j in enumerate(js):
+            arr[i] = j
+        return arr
+
+    ok = J(FAKE, 4, 64, 1, None, FAKE, FAKE)
+    # the FP4 part is checked as csa2_quant_fp4 checks it
+    assert w(FAKE, FAKE, 8, 3, None, None, FAKE, FAKE, jobs(), 0, None) == -2
+    assert w(None, FAKE, 8, 1, None, None, FAKE, FAKE, jobs(), 0, None) == -1
+    # job count and table
+    assert w(FAKE, FAKE, 8, 1, None, None, FAKE, FAKE, jobs(ok), 4, None) == -1
+    assert w(FAKE, FAKE, 8, 1, None, None, FAKE, FAKE, jobs(ok), -1, None) == -1
+    assert w(FAKE, FAKE, 8, 1, None, None, FAKE, FAKE, None, 1, None) == -1
+    # each job is checked as csa2_quant_fp8 checks it
+    assert w(FAKE, FAKE, 8, 1, None, None, FAKE, FAKE, jobs(ok, J(FAKE, 4, 96, 0, None, FAKE, FAKE)), 2, None) == -2
+    assert w(FAKE, FAKE, 8, 1, None, None, FAKE, FAKE, jobs(J(FAKE, 4, 128, 1, None, FAKE, FAKE)), 1, None) == -2
+    assert w(FAKE, FAKE, 8, 1, None, None, FAKE, FAKE, jobs(J(FAKE, 4, 64, 0, None, None, FAKE)), 1, None) == -1
+    assert w(FAKE, FAKE, 8, 1, None, None, FAKE, FAKE, jobs(J(FAKE, -2, 64, 0, None, FAKE, FAKE)), 1, None) == -1
+    # nothing to write: no launch
+    assert w(None, None, 0, 1, None, None, None, None, jobs(J(None, 0, 64, 0, None, None, None)), 1, None) == 0
+
+
 def test_index_validation(lib):
     f = lib.csa2_index_full
     ok = dict(cap=1024, B=2, Q=1, topk=512, pool=2048)

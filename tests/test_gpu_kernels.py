@@ -99,6 +99,56 @@ def test_quant_fp8_bit_exact(gpu, oracle_mod, dim, layout, n):
     np.testing.assert_array_equal(host(sigma), sig_ref)
 
 
+@pytest.mark.parametrize("n_tok,ratio,rope,n_rows", [(128, 1, True, 128), (16, 1, False, 16),
+                                                     (10, 2, False, 3), (0, 1, False, 200)])
+def test_write_entries_bit_exact(gpu, oracle_mod, n_tok, ratio, rope, n_rows):
+    """One launch writes what quant_fp4 and three quant_fp8 calls write: the
+    entries' FP4 records (scattered rows), their tiled indexer keys, and two
+    FP8 row sets (window K and V), each equal to the oracle's codes."""
+    say(f"write_entries n_tok={n_tok} ratio={ratio} rope={rope} n_rows={n_rows}")
+    g = np.random.default_rng(700 + n_tok + n_rows)
+    n_ent = n_tok // ratio
+    k = (g.standard_normal((n_tok, 128)) * np.exp2(g.integers(-8, 8, (n_tok, 1)))).astype(np.float32)
+    v = g.standard_normal((n_tok, 128)).astype(np.float32)
+    ik = g.standard_normal((n_rows, 64)).astype(np.float32)
+    wk = (g.standard_normal((n_rows, 128)) * 3).astype(np.float32)
+    wv = g.standard_normal((n_rows, 128)).astype(np.float32)
+    if n_rows:
+        wk[0] = 0.0
+    cap = 64 * ((max(n_ent, n_rows) + 9 + 63) // 64)
+    rows = (np.arange(n_ent)[::-1] + 5).astype(np.int64)
+    irows = (np.arange(n_rows)[::-1] + 3).astype(np.int64)
+    pos = np.arange(900, 900 + n_ent)
+    cs = oracle_mod.rope_table(pos) if rope else None
+    codes = torch.zeros((cap, 128), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((cap, 16), dtype=torch.uint8, device="cuda")
+    ikc = torch.zeros(cap * 64, dtype=torch.uint8, device="cuda")
+    iks = torch.zeros(cap, dtype=torch.float32, device="cuda")
+    wkc = torch.zeros((max(n_rows, 1), 128), dtype=torch.uint8, device="cuda")
+    wks = torch.zeros(max(n_rows, 1), dtype=torch.float32, device="cuda")
+    wvc, wvs = torch.zeros_like(wkc), torch.zeros_like(wks)
+    gpu.write_entries(dev(k), dev(v), codes, scales, ratio=ratio,
+                      rope_cs=dev(gpu.rope_table(pos)) if rope else None, dst_rows=dev(rows),
+                      fp8_jobs=[dict(x=dev(ik), codes=ikc, sigma=iks, layout=gpu.FP8_IDX_TILED,
+                                     dst_rows=dev(irows)),
+                                dict(x=dev(wk), codes=wkc, sigma=wks),
+                                dict(x=dev(wv), codes=wvc, sigma=wvs)])
+    if n_ent:
+        cref, sref = oracle_mod.quant_fp4(k, v, ratio, cs)
+        np.testing.assert_array_equal(host(codes)[rows], cref)
+        np.testing.assert_array_equal(host(scales)[rows], sref)
+    untouched = np.setdiff1d(np.arange(cap), rows)
+    assert np.all(host(codes)[untouched] == 0) and np.all(host(scales)[untouched] == 0)
+    if n_rows:
+        ic_ref, is_ref = oracle_mod.quant_fp8_rows(ik)
+        np.testing.assert_array_equal(untile_ik(host(ikc), 1, cap)[0][irows], ic_ref)
+        np.testing.assert_array_equal(host(iks)[irows], is_ref)
+        for x, c, sg in ((wk, wkc, wks), (wv, wvc, wvs)):
+            c_ref, s_ref = oracle_mod.quant_fp8_rows(x)
+            np.testing.assert_array_equal(host(c), c_ref)
+            np.testing.assert_array_equal(host(sg), s_ref)
+
+
 # --------------------------------------------------------------------------- indexer
 def make_idx_cache(gpu, oracle_mod, B, cap, seed, dup_frac=0.0):
     g = np.random.default_rng(seed)
