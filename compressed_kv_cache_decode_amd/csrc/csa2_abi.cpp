@@ -23,17 +23,19 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct IndexLayout {
     size_t qd, wq, keys, bkeys, total;
     // MFMA chunk path only
-    size_t cq, qh, bkeys_hi, cpool, ckeys, flag;
+    size_t cq, qh, bkeys_hi;
 };
 
 // A multi-query Full layer without a pool output (the replay chunk) scores on
 // MFMA with guard bands (csa2_chunk.hip); otherwise the exact VALU scan.
-bool mma_path(int Q, int pool_blocks) { return Q >= 4 && pool_blocks == 0; }
+bool mma_path(int Q, int pool_blocks, int topk) {
+    return Q >= 4 && pool_blocks == 0 && topk <= kChunkMaxTopk;
+}
 
 // workspace of csa2_index_full: decoded query, folded weights, per-position
-// keys, per-block keys; on the MFMA path also the guard constants, fp16 queries, upper-bound
-// block keys (the lower bounds use the per-block keys), the candidate pools,
-// their exact keys and the fallback flags
+// keys, per-block keys; on the MFMA path also the guard constants, the fp16
+// queries and the upper-bound block keys (the lower bounds use the per-block
+// keys; the per-position keys serve the exact fallback)
 IndexLayout full_layout(int B, int Q, int64_t cap, int topk, int pool_blocks) {
     IndexLayout L{};
     const size_t nq = (size_t)B * Q;
@@ -42,14 +44,10 @@ IndexLayout full_layout(int B, int Q, int64_t cap, int topk, int pool_blocks) {
     L.wq = off; off += align_up(nq * 4 * sizeof(float));
     L.keys = off; off += align_up(nq * (size_t)cap * sizeof(uint32_t));
     L.bkeys = off; off += align_up(nq * (size_t)(cap / 8) * sizeof(uint32_t));
-    if (mma_path(Q, pool_blocks)) {
+    if (mma_path(Q, pool_blocks, topk)) {
         L.cq = off; off += align_up(nq * sizeof(float));
         L.qh = off; off += align_up(nq * 256 * sizeof(uint16_t));
-        const size_t pc = (size_t)cand_pool_blocks(topk);
         L.bkeys_hi = off; off += align_up(nq * (size_t)(cap / 8) * sizeof(uint32_t));
-        L.cpool = off; off += align_up(nq * pc * sizeof(int32_t));
-        L.ckeys = off; off += align_up(nq * pc * 8 * sizeof(uint32_t));
-        L.flag = off; off += align_up(nq * sizeof(int32_t));
     }
     L.total = off;
     return L;
@@ -253,31 +251,21 @@ __attribute__((visibility("default"))) int csa2_index_full_timed(
     // requested pool, P = K blocks are kept internally.
     const int P = pool_blocks > 0 ? pool_blocks : topk;
 
-    if (mma_path(Q, pool_blocks)) {
-        // block bounds on MFMA -> candidate blocks (upper bound reaches the
-        // K-th largest lower bound) -> exact rescore and top-K inside them;
-        // a query whose candidates overflow the pool is rescored over all its
-        // positions by its selection workgroup and takes the plain Full-layer
-        // selection instead
-        const int Pc = cand_pool_blocks(topk);
+    if (mma_path(Q, pool_blocks, topk)) {
+        // block bounds on MFMA, then per query: candidate blocks (upper bound
+        // reaches the K-th largest lower bound), their exact keys and the
+        // top-K, in one workgroup; a query whose candidates overflow is
+        // rescored over all its positions there and takes the Full selection
         float* cq = reinterpret_cast<float*>(w + L.cq);
         _Float16* qh = reinterpret_cast<_Float16*>(w + L.qh);
         uint32_t* bkeys_hi = reinterpret_cast<uint32_t*>(w + L.bkeys_hi);
-        int32_t* cpool = reinterpret_cast<int32_t*>(w + L.cpool);
-        uint32_t* ckeys = reinterpret_cast<uint32_t*>(w + L.ckeys);
-        int32_t* flag = reinterpret_cast<int32_t*>(w + L.flag);
         hipError_t e = launch_prep_iq(iq, iw, nq, qd, wq, stream, cq, qh);
         if (e == hipSuccess)
             e = launch_scan_mma(ik_codes, ik_sigma, cap, B, Q, qh, wq, cq, n_vis, bkeys,
                                 bkeys_hi, stream, scan_start, scan_stop);
         if (e == hipSuccess)
-            e = launch_cand_pool(bkeys, bkeys_hi, cap, n_vis, nq, topk, Pc, cpool, flag, stream);
-        if (e == hipSuccess)
-            e = launch_pool_score(ik_codes, ik_sigma, cap, B, Q, iq, iw, n_vis, cpool, Pc, ckeys,
-                                  stream);
-        if (e == hipSuccess)
-            e = launch_select_pool(ckeys, cpool, Pc, n_vis, cap, nq, topk, topk_idx, stream, flag,
-                                   ik_codes, ik_sigma, qd, wq, Q, keys, bkeys);
+            e = launch_chunk_select(ik_codes, ik_sigma, cap, Q, qd, wq, bkeys_hi, n_vis, nq, topk,
+                                    keys, bkeys, topk_idx, stream);
         return hip_status(e);
     }
 

@@ -38,11 +38,11 @@
 // with exact score >= x, so the K-th largest exact score t is >= x, and every
 // position with score >= t (every position the exact top-K can take, ties
 // included) lies in a block whose hi reaches x.  Those blocks hold the exact
-// top-K (k_cand_pool); rescoring their positions exactly (the Reindex kernels:
-// same scores, bit for bit, as the VALU scan) and selecting there gives the
-// exact top-K with its tie rule, as the candidate blocks are listed in
-// ascending order.  A query whose candidate blocks do not fit the pool is
-// flagged, and the selection kernel rescores all its positions exactly.
+// top-K; k_chunk_select (csa2_index.hip) lists them in ascending order,
+// scores their positions exactly (the VALU scan's arithmetic, same keys bit
+// for bit) and selects there, so ties still go to the lowest position.  A
+// query whose candidate blocks do not fit its pool is scored over all its
+// visible positions instead.
 #include <hip/hip_ext.h>
 
 #include "csa2_device.hpp"

@@ -773,37 +773,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(
                       sh);
 }
 
-// Reindex: best K positions of the compact pool-ordered keys.  With `fb`
-// set (the multi-query MFMA scan), a query whose flag is 1 instead has all
-// its visible positions scored exactly here (into fb.keys / fb.bkeys) and
-// takes the Full layer's selection over them, K blocks then K positions: the
-// fallback for candidates that overflowed the pool.
-struct ExactFallback {
-    const int32_t* flag;
-    const uint8_t* ikc;
-    const float* iks;
-    const float* qd;
-    const float* wq;
-    uint32_t* keys;
-    uint32_t* bkeys;
-    int Q;
-};
-
+// Reindex: best K positions of the compact pool-ordered keys.
 __global__ __launch_bounds__(kSelThreads) void k_select_pool(
     const uint32_t* __restrict__ ckeys, const int32_t* __restrict__ pool, int P,
-    const int32_t* __restrict__ n_vis, int64_t cap, int K, int32_t* __restrict__ topk_out,
-    ExactFallback fb) {
+    const int32_t* __restrict__ n_vis, int64_t cap, int K, int32_t* __restrict__ topk_out) {
     __shared__ SelShared sh;
     const int64_t bq = blockIdx.x;
     const int nv = clamp_nvis(n_vis[bq], cap);
-    if (fb.flag != nullptr && fb.flag[bq]) {  // uniform over the workgroup
-        scan_query_exact(fb.ikc, fb.iks, (bq / fb.Q) * cap, fb.qd + bq * kIdxHeads * kIdxDim,
-                         fb.wq + bq * kIdxHeads, nv, kSelThreads, fb.keys + bq * cap,
-                         fb.bkeys + bq * (cap / kBlock));
-        __syncthreads();  // the keys are the workgroup's own global writes
-        select_full_query(fb.keys, fb.bkeys, cap, bq, nv, K, K, nullptr, topk_out, sh);
-        return;
-    }
     const int64_t nbv = ((int64_t)nv + kBlock - 1) / kBlock;
     const KeySrc ks{ckeys + bq * (int64_t)P * kBlock, sh.pool, (int64_t)P * kBlock, nv, 2};
     auto stage_pool = [&]() {
@@ -832,33 +808,51 @@ __global__ __launch_bounds__(kSelThreads) void k_select_pool(
     }
 }
 
-// Candidate blocks of the multi-query MFMA scan.  x = the K-th largest
-// lower-bound block key of the query (1 when fewer than K blocks hold a
-// visible position); K distinct blocks then each hold a position whose exact
-// score is >= x, so every position the exact top-K can take lies in a block
-// whose upper-bound key reaches x.  Those blocks, in ascending order, fill
-// pool[bq][0, Pc) (-1 after them); flag[bq] = 1 when more than Pc qualify.
-__global__ __launch_bounds__(kSelThreads) void k_cand_pool(
-    const uint32_t* __restrict__ bkeys_lo, const uint32_t* __restrict__ bkeys_hi, int64_t cap,
-    const int32_t* __restrict__ n_vis, int K, int Pc, int32_t* __restrict__ pool,
-    int32_t* __restrict__ flag) {
+// Top-K of one query of the multi-query MFMA scan (csa2_chunk.hip), one
+// workgroup per query, from the scan's per-block lower / upper bound keys:
+//   1. x = the K-th largest lower-bound block key (1 when fewer than K blocks
+//      hold a visible position).  K distinct blocks each hold a position whose
+//      exact score is >= x, so every position the exact top-K can take lies
+//      in a block whose upper-bound key reaches x;
+//   2. those candidate blocks, in ascending order, are listed in LDS;
+//   3. their positions are scored exactly (k_scan's arithmetic, so the keys
+//      are bit-identical) into LDS;
+//   4. the register-path selection takes the top K there, ties to the lowest
+//      position since the slots are in ascending position order.
+// A query with more than Pc candidate blocks (heavy ties) is scored over all
+// its visible positions instead (into keys / bkeys, its own rows) and takes
+// the Full layer's selection, K blocks then K positions.
+constexpr int kChunkMaxPool = 1536;                    // candidate blocks held in LDS
+constexpr int kChunkSlots = kChunkMaxPool * kBlock;    // 12288 keys
+static_assert(kChunkSlots <= kSelRegSlots, "the candidates' keys fit the register path");
+
+__global__ __launch_bounds__(kSelThreads) void k_chunk_select(
+    const uint8_t* __restrict__ ikc, const float* __restrict__ iks, int64_t cap, int Q,
+    const float* __restrict__ qd, const float* __restrict__ wq,
+    const uint32_t* __restrict__ bkeys_hi, const int32_t* __restrict__ n_vis, int K, int Pc,
+    uint32_t* __restrict__ keys, uint32_t* __restrict__ bkeys, int32_t* __restrict__ topk_out) {
     __shared__ SelShared sh;
+    __shared__ uint32_t ck[kChunkSlots];
     __shared__ uint32_t part[kSelWaves];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t bq = blockIdx.x;
+    const int64_t row0 = (bq / Q) * cap;
     const int nv = clamp_nvis(n_vis[bq], cap);
     const int64_t nb = cap / kBlock, nbv = ((int64_t)nv + kBlock - 1) / kBlock;
-    const KeySrc lo{bkeys_lo + bq * nb, nullptr, nbv, nv, 0};
+    const KeySrc lo{bkeys + bq * nb, nullptr, nbv, nv, 0};  // the scan's lower bounds
     const KeySrc hi{bkeys_hi + bq * nb, nullptr, nbv, nv, 0};
+    const float* qrow = qd + bq * kIdxHeads * kIdxDim;
+    const float* wrow = wq + bq * kIdxHeads;
+    SelRegShared& rs = *reinterpret_cast<SelRegShared*>(&sh.hist[0]);
 
-    // K-th largest lower-bound key: the threshold's tie value, else the
+    // 1. the K-th largest lower-bound key: the threshold's tie value, else the
     // smallest key at or above its cut
     Threshold th;
     uint32_t m = 0xFFFFFFFFu;
     if (nbv <= kSelRegSlots) {
         uint32_t k[kSelKpt];
         lo.load16((int64_t)wave * 1024 + 16 * lane, k);
-        th = threshold_reg(k, K, *reinterpret_cast<SelRegShared*>(&sh.hist[0]));
+        th = threshold_reg(k, K, rs);
 #pragma unroll
         for (int i = 0; i < kSelKpt; ++i)
             m = (k[i] != 0 && k[i] >= th.t_ge) ? min(m, k[i]) : m;
@@ -877,8 +871,9 @@ __global__ __launch_bounds__(kSelThreads) void k_cand_pool(
     for (int w = 0; w < kSelWaves; ++w) m = min(m, part[w]);
     const uint32_t x = th.total < (uint32_t)K ? 1u : (th.quota != 0 ? th.t_eq : m);
 
-    // ordered compaction of the qualifying blocks, 16 per thread per sweep
-    uint32_t base = 0;
+    // 2. ordered compaction of the candidate blocks into sh.pool, 16 blocks
+    // per thread per sweep
+    uint32_t n_c = 0;
     for (int64_t b0 = 0; b0 < nbv; b0 += (int64_t)kSelThreads * kSelKpt) {
         const int64_t first = b0 + (int64_t)tid * kSelKpt;
         uint32_t h[kSelKpt];
@@ -891,7 +886,7 @@ __global__ __launch_bounds__(kSelThreads) void k_cand_pool(
         __syncthreads();  // earlier readers of part are done
         if (lane == 63) part[wave] = excl + cnt;
         __syncthreads();
-        uint32_t before = base, total = 0;
+        uint32_t before = n_c, total = 0;
 #pragma unroll
         for (int w = 0; w < kSelWaves; ++w) {
             before += w < wave ? part[w] : 0u;
@@ -899,11 +894,54 @@ __global__ __launch_bounds__(kSelThreads) void k_cand_pool(
         }
         uint32_t r = before + excl;
         for (uint32_t mm = mask; mm != 0; mm &= mm - 1u, ++r)
-            if (r < (uint32_t)Pc) pool[bq * Pc + r] = (int32_t)(first + __builtin_ctz(mm));
-        base += total;
+            if (r < (uint32_t)Pc) sh.pool[r] = (int32_t)(first + __builtin_ctz(mm));
+        n_c += total;  // uniform
     }
-    for (int64_t i = (int64_t)base + tid; i < Pc; i += kSelThreads) pool[bq * Pc + i] = -1;
-    if (tid == 0) flag[bq] = base > (uint32_t)Pc ? 1 : 0;
+
+    if (n_c > (uint32_t)Pc) {  // uniform: the exact fallback
+        scan_query_exact(ikc, iks, row0, qrow, wrow, nv, kSelThreads, keys + bq * cap,
+                         bkeys + bq * nb);
+        __syncthreads();  // the keys are the workgroup's own global writes
+        select_full_query(keys, bkeys, cap, bq, nv, K, K, nullptr, topk_out, sh);
+        return;
+    }
+    __syncthreads();  // the candidate list is complete
+
+    // 3. exact keys of the candidates' positions, two slots per thread in
+    // flight (consecutive threads take the 8 positions of a block)
+    const int n_slots = (int)n_c * kBlock;
+    for (int s0 = 0; s0 < n_slots; s0 += 2 * kSelThreads) {
+        uint4 raw[2][4];
+        float sg[2] = {0.0f, 0.0f};
+        bool vis[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int s = s0 + u * kSelThreads + tid;
+            const int64_t pos = s < n_slots ? (int64_t)sh.pool[s >> 3] * kBlock + (s & 7) : nv;
+            vis[u] = pos < nv;
+            if (vis[u]) {
+                load_ik_row(ikc, row0 + pos, raw[u]);
+                sg[u] = iks[row0 + pos];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int s = s0 + u * kSelThreads + tid;
+            if (s < n_slots) ck[s] = vis[u] ? score_key(score_row(raw[u], sg[u], qrow, wrow)) : 0u;
+        }
+    }
+    __syncthreads();
+
+    // 4. top-K of the candidates (register path: 16 consecutive slots a lane)
+    uint32_t k[kSelKpt];
+#pragma unroll
+    for (int i = 0; i < kSelKpt; ++i) {
+        const int s = 16 * tid + i;
+        k[i] = s < n_slots ? ck[s] : 0u;
+    }
+    const KeySrc ks{ck, sh.pool, n_slots, nv, 2};
+    const Threshold tk = threshold_reg(k, K, rs);
+    compact_reg(k, tk, K, [&](int64_t s) { return ks.index(s); }, topk_out + bq * K, nullptr, rs);
 }
 
 // ---------------------------------------------------------------------------
@@ -947,20 +985,20 @@ hipError_t launch_select_full(const uint32_t* keys, const uint32_t* bkeys, int64
 
 hipError_t launch_select_pool(const uint32_t* ckeys, const int32_t* pool, int P,
                               const int32_t* n_vis, int64_t cap, int64_t n_queries, int K,
-                              int32_t* topk_out, hipStream_t stream, const int32_t* flag,
-                              const uint8_t* ikc, const float* iks, const float* qd,
-                              const float* wq, int Q, uint32_t* keys, uint32_t* bkeys) {
-    const ExactFallback fb{flag, ikc, iks, qd, wq, keys, bkeys, Q};
+                              int32_t* topk_out, hipStream_t stream) {
     hipLaunchKernelGGL(k_select_pool, dim3((unsigned)n_queries), dim3(kSelThreads), 0, stream,
-                       ckeys, pool, P, n_vis, cap, K, topk_out, fb);
+                       ckeys, pool, P, n_vis, cap, K, topk_out);
     return hipGetLastError();
 }
 
-hipError_t launch_cand_pool(const uint32_t* bkeys_lo, const uint32_t* bkeys_hi, int64_t cap,
-                            const int32_t* n_vis, int64_t n_queries, int K, int Pc, int32_t* pool,
-                            int32_t* flag, hipStream_t stream) {
-    hipLaunchKernelGGL(k_cand_pool, dim3((unsigned)n_queries), dim3(kSelThreads), 0, stream,
-                       bkeys_lo, bkeys_hi, cap, n_vis, K, Pc, pool, flag);
+hipError_t launch_chunk_select(const uint8_t* ikc, const float* iks, int64_t cap, int Q,
+                               const float* qd, const float* wq, const uint32_t* bkeys_hi,
+                               const int32_t* n_vis, int64_t n_queries, int K, uint32_t* keys,
+                               uint32_t* bkeys, int32_t* topk_out, hipStream_t stream) {
+    const int Pc = cand_pool_blocks(K);
+    if (Pc > kChunkMaxPool) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_chunk_select, dim3((unsigned)n_queries), dim3(kSelThreads), 0, stream,
+                       ikc, iks, cap, Q, qd, wq, bkeys_hi, n_vis, K, Pc, keys, bkeys, topk_out);
     return hipGetLastError();
 }
 

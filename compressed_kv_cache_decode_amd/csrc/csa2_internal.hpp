@@ -59,31 +59,30 @@ hipError_t launch_scan_mma(const uint8_t* ikc, const float* iks, int64_t cap, in
                            const int32_t* n_vis, uint32_t* bkeys_lo, uint32_t* bkeys_hi,
                            hipStream_t stream, hipEvent_t start = nullptr,
                            hipEvent_t stop = nullptr);
-// candidate blocks of the MFMA scan (csa2_index.hip)
-hipError_t launch_cand_pool(const uint32_t* bkeys_lo, const uint32_t* bkeys_hi, int64_t cap,
-                            const int32_t* n_vis, int64_t n_queries, int K, int Pc, int32_t* pool,
-                            int32_t* flag, hipStream_t stream);
+// top-K of each query of the MFMA scan from its block bounds (csa2_index.hip):
+// candidate blocks, their exact keys and the selection in one workgroup per
+// query; keys / bkeys: scratch rows of the exact fallback (bkeys holds the
+// scan's lower bounds on entry)
+hipError_t launch_chunk_select(const uint8_t* ikc, const float* iks, int64_t cap, int Q,
+                               const float* qd, const float* wq, const uint32_t* bkeys_hi,
+                               const int32_t* n_vis, int64_t n_queries, int K, uint32_t* keys,
+                               uint32_t* bkeys, int32_t* topk_out, hipStream_t stream);
 // candidate blocks per chunk query before the exact fallback: 1.5 K, at least 256
 inline int cand_pool_blocks(int K) {
     const int p = K + K / 2;
     return p < 256 ? 256 : (p > kMaxPoolBlocks ? kMaxPoolBlocks : p);
 }
+// the MFMA scan path takes top-K up to this (its candidates' keys stay in LDS)
+constexpr int kChunkMaxTopk = 1024;
 hipError_t launch_pool_score(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                              const float* iq, const float* iw, const int32_t* n_vis,
                              const int32_t* pool, int P, uint32_t* ckeys, hipStream_t stream);
 hipError_t launch_select_full(const uint32_t* keys, const uint32_t* bkeys, int64_t cap,
                               const int32_t* n_vis, int64_t n_queries, int P, int K,
                               int32_t* pool_out, int32_t* topk_out, hipStream_t stream);
-// flag: null, or one per query; a flagged query is instead scored exactly
-// over all its visible positions (ikc / iks with the decoded query qd, wq of
-// Q queries per sequence, keys into keys / bkeys) and takes the Full layer's
-// selection there
 hipError_t launch_select_pool(const uint32_t* ckeys, const int32_t* pool, int P,
                               const int32_t* n_vis, int64_t cap, int64_t n_queries, int K,
-                              int32_t* topk_out, hipStream_t stream, const int32_t* flag = nullptr,
-                              const uint8_t* ikc = nullptr, const float* iks = nullptr,
-                              const float* qd = nullptr, const float* wq = nullptr, int Q = 1,
-                              uint32_t* keys = nullptr, uint32_t* bkeys = nullptr);
+                              int32_t* topk_out, hipStream_t stream);
 
 struct AttnArgs {
     const float* q;          // [n_q][H][128]

@@ -180,9 +180,11 @@ def make_idx_cache(gpu, oracle_mod, B, cap, seed, dup_frac=0.0):
     (2, 16, 16384, [[0, 1, 5, 300, 511, 512, 513, 4096, 8191, 8192, 12000, 16383, 16384,
                      16384, 7, 9000], [16384 - 1000 * i for i in range(16)]], 512, 0),
     (1, 4, 1024, [[1024, 1024, 1000, 3]], 2048, 0),   # top-K larger than what is visible
-    # the largest top-K: a 3072-block candidate pool (streaming selection);
-    # more than 16384 blocks: the candidate threshold streams too
+    # top-K above 1024 takes the exact multi-query scan; at 1024 the MFMA
+    # path's largest candidate pool (1536 blocks, 12288 keys in LDS); more than
+    # 16384 blocks: the candidate threshold streams
     (1, 5, 65536, [[65536, 65000, 40000, 20000, 9]], 2048, 0),
+    (1, 5, 65536, [[65536, 65000, 40000, 20000, 9]], 1024, 0),
     (1, 4, 262144, [[262144, 262000, 131073, 70000]], 512, 0),
     # the largest top-K and pool the boundary accepts; 32768 pool positions take
     # the streaming selection path
