@@ -23,7 +23,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct IndexLayout {
     size_t qd, wq, keys, bkeys, total;
     // MFMA chunk path only
-    size_t cq, qh, bkeys_hi;
+    size_t cq, qh, hkeys_hi;
 };
 
 // A multi-query Full layer without a pool output (the replay chunk) scores on
@@ -34,8 +34,8 @@ bool mma_path(int Q, int pool_blocks, int topk) {
 
 // workspace of csa2_index_full: decoded query, folded weights, per-position
 // keys, per-block keys; on the MFMA path also the guard constants, the fp16
-// queries and the upper-bound block keys (the lower bounds use the per-block
-// keys; the per-position keys serve the exact fallback)
+// queries and the upper-bound keys per half-block of 4 (the lower bounds use
+// the per-block keys; the per-position keys serve the exact fallback)
 IndexLayout full_layout(int B, int Q, int64_t cap, int topk, int pool_blocks) {
     IndexLayout L{};
     const size_t nq = (size_t)B * Q;
@@ -47,7 +47,7 @@ IndexLayout full_layout(int B, int Q, int64_t cap, int topk, int pool_blocks) {
     if (mma_path(Q, pool_blocks, topk)) {
         L.cq = off; off += align_up(nq * sizeof(float));
         L.qh = off; off += align_up(nq * 256 * sizeof(uint16_t));
-        L.bkeys_hi = off; off += align_up(nq * (size_t)(cap / 8) * sizeof(uint32_t));
+        L.hkeys_hi = off; off += align_up(nq * (size_t)(cap / 4) * sizeof(uint32_t));
     }
     L.total = off;
     return L;
@@ -252,19 +252,20 @@ __attribute__((visibility("default"))) int csa2_index_full_timed(
     const int P = pool_blocks > 0 ? pool_blocks : topk;
 
     if (mma_path(Q, pool_blocks, topk)) {
-        // block bounds on MFMA, then per query: candidate blocks (upper bound
-        // reaches the K-th largest lower bound), their exact keys and the
-        // top-K, in one workgroup; a query whose candidates overflow is
-        // rescored over all its positions there and takes the Full selection
+        // bounds on MFMA, then per query: candidate half-blocks (upper bound
+        // reaches the K-th largest lower bound of a block), their exact keys
+        // and the top-K, in one workgroup; a query whose candidates overflow
+        // is rescored over all its positions there and takes the Full
+        // selection
         float* cq = reinterpret_cast<float*>(w + L.cq);
         _Float16* qh = reinterpret_cast<_Float16*>(w + L.qh);
-        uint32_t* bkeys_hi = reinterpret_cast<uint32_t*>(w + L.bkeys_hi);
+        uint32_t* hkeys_hi = reinterpret_cast<uint32_t*>(w + L.hkeys_hi);
         hipError_t e = launch_prep_iq(iq, iw, nq, qd, wq, stream, cq, qh);
         if (e == hipSuccess)
             e = launch_scan_mma(ik_codes, ik_sigma, cap, B, Q, qh, wq, cq, n_vis, bkeys,
-                                bkeys_hi, stream, scan_start, scan_stop);
+                                hkeys_hi, stream, scan_start, scan_stop);
         if (e == hipSuccess)
-            e = launch_chunk_select(ik_codes, ik_sigma, cap, Q, qd, wq, bkeys_hi, n_vis, nq, topk,
+            e = launch_chunk_select(ik_codes, ik_sigma, cap, Q, qd, wq, hkeys_hi, n_vis, nq, topk,
                                     keys, bkeys, topk_idx, stream);
         return hip_status(e);
     }

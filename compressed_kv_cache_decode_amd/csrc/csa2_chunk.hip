@@ -29,20 +29,20 @@
 // m = max s, a = max |s| and g = max sigma over its visible ones,
 // M = g C'_q + 2^-20 a bounds every d there, so m - M is at most the exact
 // score of the position that attains m, and m + M at least every exact score
-// of the four.  Per block, the larger of the two lanes' values gives a lower
-// bound lo (some position's exact score reaches it) and an upper bound hi (no
-// exact score exceeds it); the kernel writes their keys (0 for a block with no
-// visible position).
+// of the four.  The kernel writes, per block of 8, the key of the larger lower
+// bound of its two lanes (lo: some position's exact score reaches it), and per
+// half-block of 4, the key of the lane's upper bound (hi: no exact score of
+// the four exceeds it); 0 where no position is visible.
 //
 // If x is the K-th largest block lo, K distinct blocks each hold a position
 // with exact score >= x, so the K-th largest exact score t is >= x, and every
 // position with score >= t (every position the exact top-K can take, ties
-// included) lies in a block whose hi reaches x.  Those blocks hold the exact
-// top-K; k_chunk_select (csa2_index.hip) lists them in ascending order,
-// scores their positions exactly (the VALU scan's arithmetic, same keys bit
-// for bit) and selects there, so ties still go to the lowest position.  A
-// query whose candidate blocks do not fit its pool is scored over all its
-// visible positions instead.
+// included) lies in a half-block whose hi reaches x.  Those half-blocks hold
+// the exact top-K; k_chunk_select (csa2_index.hip) lists them in ascending
+// order, scores their positions exactly (the VALU scan's arithmetic, same keys
+// bit for bit) and selects there, so ties still go to the lowest position.  A
+// query whose candidates do not fit its list is scored over all its visible
+// positions instead.
 #include <hip/hip_ext.h>
 
 #include "csa2_device.hpp"
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kMmaThreads) __attribute__((amdgpu_waves_per_eu(4))
     const uint8_t* __restrict__ ikc, const float* __restrict__ iks, int64_t cap, int Q,
     const _Float16* __restrict__ qh, const float* __restrict__ wq, const float* __restrict__ cq,
     const int32_t* __restrict__ n_vis, uint32_t* __restrict__ bkeys_lo,
-    uint32_t* __restrict__ bkeys_hi) {
+    uint32_t* __restrict__ hkeys_hi) {
     __shared__ __attribute__((aligned(16))) _Float16 sq[kMmaQ * kMmaPitch];
     __shared__ __attribute__((aligned(16))) float sw[kMmaQ * kIdxHeads];
     __shared__ float sc[kMmaQ];
@@ -216,15 +216,15 @@ __global__ __launch_bounds__(kMmaThreads) __attribute__((amdgpu_waves_per_eu(4))
                     a_abs = m >= lo4 ? fmaxf(m, -lo4) : 0.0f;  // m = -inf: none visible
                 }
                 const float M = fmaf(a_abs, 0x1p-20f, gmax[st] * cqj);
-                float lo = m - M, hi = m + M;  // -inf when no row is visible
+                const float hi = m + M;  // -inf when no row is visible
+                float lo = m - M;
+                if (qok)  // half-block (base + 4 (l / 16)) / 4
+                    hkeys_hi[(bq0 + j) * (2 * nb) + (base >> 2) + (lane >> 4)] =
+                        hi != -INFINITY ? score_key(hi) : 0u;
                 lo = fmaxf(lo, __shfl_xor(lo, 16, 64));
-                hi = fmaxf(hi, __shfl_xor(hi, 16, 64));
-                if (qok && ((lane >> 4) & 1) == 0) {
-                    const int64_t blk = (base >> 3) + (lane >> 5);
-                    const bool any = lo != -INFINITY;
-                    bkeys_lo[(bq0 + j) * nb + blk] = any ? score_key(lo) : 0u;
-                    bkeys_hi[(bq0 + j) * nb + blk] = any ? score_key(hi) : 0u;
-                }
+                if (qok && ((lane >> 4) & 1) == 0)
+                    bkeys_lo[(bq0 + j) * nb + (base >> 3) + (lane >> 5)] =
+                        lo != -INFINITY ? score_key(lo) : 0u;
             }
         }
     }
@@ -232,15 +232,15 @@ __global__ __launch_bounds__(kMmaThreads) __attribute__((amdgpu_waves_per_eu(4))
 
 hipError_t launch_scan_mma(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                            const _Float16* qh, const float* wq, const float* cq,
-                           const int32_t* n_vis, uint32_t* bkeys_lo, uint32_t* bkeys_hi,
+                           const int32_t* n_vis, uint32_t* bkeys_lo, uint32_t* hkeys_hi,
                            hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     dim3 grid((unsigned)((cap + kMmaPos - 1) / kMmaPos), (unsigned)B);
     if (start != nullptr && stop != nullptr) {
         hipExtLaunchKernelGGL(k_scan_mma, grid, dim3(kMmaThreads), 0, stream, start, stop, 0, ikc,
-                              iks, cap, Q, qh, wq, cq, n_vis, bkeys_lo, bkeys_hi);
+                              iks, cap, Q, qh, wq, cq, n_vis, bkeys_lo, hkeys_hi);
     } else {
         hipLaunchKernelGGL(k_scan_mma, grid, dim3(kMmaThreads), 0, stream, ikc, iks, cap, Q, qh,
-                           wq, cq, n_vis, bkeys_lo, bkeys_hi);
+                           wq, cq, n_vis, bkeys_lo, hkeys_hi);
     }
     return hipGetLastError();
 }

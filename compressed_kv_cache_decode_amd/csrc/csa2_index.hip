@@ -809,27 +809,30 @@ __global__ __launch_bounds__(kSelThreads) void k_select_pool(
 }
 
 // Top-K of one query of the multi-query MFMA scan (csa2_chunk.hip), one
-// workgroup per query, from the scan's per-block lower / upper bound keys:
+// workgroup per query, from the scan's lower-bound keys per block of 8 and
+// upper-bound keys per half-block of 4:
 //   1. x = the K-th largest lower-bound block key (1 when fewer than K blocks
 //      hold a visible position).  K distinct blocks each hold a position whose
 //      exact score is >= x, so every position the exact top-K can take lies
-//      in a block whose upper-bound key reaches x;
-//   2. those candidate blocks, in ascending order, are listed in LDS;
+//      in a half-block whose upper-bound key reaches x;
+//   2. those candidate half-blocks, in ascending order, are listed in LDS;
 //   3. their positions are scored exactly (k_scan's arithmetic, so the keys
 //      are bit-identical) into LDS;
 //   4. the register-path selection takes the top K there, ties to the lowest
 //      position since the slots are in ascending position order.
-// A query with more than Pc candidate blocks (heavy ties) is scored over all
-// its visible positions instead (into keys / bkeys, its own rows) and takes
-// the Full layer's selection, K blocks then K positions.
-constexpr int kChunkMaxPool = 1536;                    // candidate blocks held in LDS
-constexpr int kChunkSlots = kChunkMaxPool * kBlock;    // 12288 keys
+// A query with more than Pc candidate half-blocks (heavy ties) is scored over
+// all its visible positions instead (into keys / bkeys, its own rows) and
+// takes the Full layer's selection, K blocks then K positions.
+constexpr int kHalf = 4;                               // positions per half-block
+constexpr int kChunkMaxCand = 3072;                    // candidate half-blocks held in LDS
+constexpr int kChunkSlots = kChunkMaxCand * kHalf;     // 12288 keys
 static_assert(kChunkSlots <= kSelRegSlots, "the candidates' keys fit the register path");
+static_assert(kChunkMaxCand <= kMaxPoolBlocks, "the candidate list fits sh.pool");
 
 __global__ __launch_bounds__(kSelThreads) void k_chunk_select(
     const uint8_t* __restrict__ ikc, const float* __restrict__ iks, int64_t cap, int Q,
     const float* __restrict__ qd, const float* __restrict__ wq,
-    const uint32_t* __restrict__ bkeys_hi, const int32_t* __restrict__ n_vis, int K, int Pc,
+    const uint32_t* __restrict__ hkeys_hi, const int32_t* __restrict__ n_vis, int K, int Pc,
     uint32_t* __restrict__ keys, uint32_t* __restrict__ bkeys, int32_t* __restrict__ topk_out) {
     __shared__ SelShared sh;
     __shared__ uint32_t ck[kChunkSlots];
@@ -839,8 +842,9 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select(
     const int64_t row0 = (bq / Q) * cap;
     const int nv = clamp_nvis(n_vis[bq], cap);
     const int64_t nb = cap / kBlock, nbv = ((int64_t)nv + kBlock - 1) / kBlock;
+    const int64_t nhv = ((int64_t)nv + kHalf - 1) / kHalf;
     const KeySrc lo{bkeys + bq * nb, nullptr, nbv, nv, 0};  // the scan's lower bounds
-    const KeySrc hi{bkeys_hi + bq * nb, nullptr, nbv, nv, 0};
+    const KeySrc hi{hkeys_hi + bq * (cap / kHalf), nullptr, nhv, nv, 0};
     const float* qrow = qd + bq * kIdxHeads * kIdxDim;
     const float* wrow = wq + bq * kIdxHeads;
     SelRegShared& rs = *reinterpret_cast<SelRegShared*>(&sh.hist[0]);
@@ -871,13 +875,13 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select(
     for (int w = 0; w < kSelWaves; ++w) m = min(m, part[w]);
     const uint32_t x = th.total < (uint32_t)K ? 1u : (th.quota != 0 ? th.t_eq : m);
 
-    // 2. ordered compaction of the candidate blocks into sh.pool, 16 blocks
+    // 2. ordered compaction of the candidate half-blocks into sh.pool, 16
     // per thread per sweep
     uint32_t n_c = 0;
-    for (int64_t b0 = 0; b0 < nbv; b0 += (int64_t)kSelThreads * kSelKpt) {
+    for (int64_t b0 = 0; b0 < nhv; b0 += (int64_t)kSelThreads * kSelKpt) {
         const int64_t first = b0 + (int64_t)tid * kSelKpt;
         uint32_t h[kSelKpt];
-        hi.load16(first, h);  // 0 past the visible blocks, and x >= 1
+        hi.load16(first, h);  // 0 past the visible half-blocks, and x >= 1
         uint32_t mask = 0;
 #pragma unroll
         for (int i = 0; i < kSelKpt; ++i) mask |= h[i] >= x ? (1u << i) : 0u;
@@ -908,8 +912,8 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select(
     __syncthreads();  // the candidate list is complete
 
     // 3. exact keys of the candidates' positions, two slots per thread in
-    // flight (consecutive threads take the 8 positions of a block)
-    const int n_slots = (int)n_c * kBlock;
+    // flight (consecutive threads take the 4 positions of a half-block)
+    const int n_slots = (int)n_c * kHalf;
     for (int s0 = 0; s0 < n_slots; s0 += 2 * kSelThreads) {
         uint4 raw[2][4];
         float sg[2] = {0.0f, 0.0f};
@@ -917,7 +921,7 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select(
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int s = s0 + u * kSelThreads + tid;
-            const int64_t pos = s < n_slots ? (int64_t)sh.pool[s >> 3] * kBlock + (s & 7) : nv;
+            const int64_t pos = s < n_slots ? (int64_t)sh.pool[s >> 2] * kHalf + (s & 3) : nv;
             vis[u] = pos < nv;
             if (vis[u]) {
                 load_ik_row(ikc, row0 + pos, raw[u]);
@@ -939,9 +943,9 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select(
         const int s = 16 * tid + i;
         k[i] = s < n_slots ? ck[s] : 0u;
     }
-    const KeySrc ks{ck, sh.pool, n_slots, nv, 2};
     const Threshold tk = threshold_reg(k, K, rs);
-    compact_reg(k, tk, K, [&](int64_t s) { return ks.index(s); }, topk_out + bq * K, nullptr, rs);
+    compact_reg(k, tk, K, [&](int64_t s) { return sh.pool[s >> 2] * kHalf + (int32_t)(s & 3); },
+                topk_out + bq * K, nullptr, rs);
 }
 
 // ---------------------------------------------------------------------------
@@ -992,13 +996,13 @@ hipError_t launch_select_pool(const uint32_t* ckeys, const int32_t* pool, int P,
 }
 
 hipError_t launch_chunk_select(const uint8_t* ikc, const float* iks, int64_t cap, int Q,
-                               const float* qd, const float* wq, const uint32_t* bkeys_hi,
+                               const float* qd, const float* wq, const uint32_t* hkeys_hi,
                                const int32_t* n_vis, int64_t n_queries, int K, uint32_t* keys,
                                uint32_t* bkeys, int32_t* topk_out, hipStream_t stream) {
-    const int Pc = cand_pool_blocks(K);
-    if (Pc > kChunkMaxPool) return hipErrorInvalidValue;
+    const int Pc = chunk_cand_halves(K);
+    if (Pc > kChunkMaxCand) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_chunk_select, dim3((unsigned)n_queries), dim3(kSelThreads), 0, stream,
-                       ikc, iks, cap, Q, qd, wq, bkeys_hi, n_vis, K, Pc, keys, bkeys, topk_out);
+                       ikc, iks, cap, Q, qd, wq, hkeys_hi, n_vis, K, Pc, keys, bkeys, topk_out);
     return hipGetLastError();
 }
 

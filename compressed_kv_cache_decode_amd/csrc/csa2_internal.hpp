@@ -53,25 +53,24 @@ hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B,
                        uint32_t* bkeys, hipStream_t stream, hipEvent_t start = nullptr,
                        hipEvent_t stop = nullptr);
 // MFMA scan of a multi-query chunk with guard-band bounds (csa2_chunk.hip):
-// per block of 8 positions, the largest lower-bound and upper-bound score keys
+// the largest lower-bound score key per block of 8 positions [nq][cap / 8]
+// and the upper-bound key per half-block of 4 [nq][cap / 4]
 hipError_t launch_scan_mma(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                            const _Float16* qh, const float* wq, const float* cq,
-                           const int32_t* n_vis, uint32_t* bkeys_lo, uint32_t* bkeys_hi,
+                           const int32_t* n_vis, uint32_t* bkeys_lo, uint32_t* hkeys_hi,
                            hipStream_t stream, hipEvent_t start = nullptr,
                            hipEvent_t stop = nullptr);
-// top-K of each query of the MFMA scan from its block bounds (csa2_index.hip):
-// candidate blocks, their exact keys and the selection in one workgroup per
-// query; keys / bkeys: scratch rows of the exact fallback (bkeys holds the
+// top-K of each query of the MFMA scan from its bounds (csa2_index.hip):
+// candidate half-blocks, their exact keys and the selection in one workgroup
+// per query; keys / bkeys: scratch rows of the exact fallback (bkeys holds the
 // scan's lower bounds on entry)
 hipError_t launch_chunk_select(const uint8_t* ikc, const float* iks, int64_t cap, int Q,
-                               const float* qd, const float* wq, const uint32_t* bkeys_hi,
+                               const float* qd, const float* wq, const uint32_t* hkeys_hi,
                                const int32_t* n_vis, int64_t n_queries, int K, uint32_t* keys,
                                uint32_t* bkeys, int32_t* topk_out, hipStream_t stream);
-// candidate blocks per chunk query before the exact fallback: 1.5 K, at least 256
-inline int cand_pool_blocks(int K) {
-    const int p = K + K / 2;
-    return p < 256 ? 256 : (p > kMaxPoolBlocks ? kMaxPoolBlocks : p);
-}
+// candidate half-blocks per chunk query before the exact fallback: 3 K, at
+// least 512
+inline int chunk_cand_halves(int K) { return 3 * K < 512 ? 512 : 3 * K; }
 // the MFMA scan path takes top-K up to this (its candidates' keys stay in LDS)
 constexpr int kChunkMaxTopk = 1024;
 hipError_t launch_pool_score(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
