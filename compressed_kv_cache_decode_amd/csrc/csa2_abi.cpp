@@ -21,7 +21,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct IndexLayout {
-    size_t qd, wq, keys, bkeys, total;
+    size_t qd, wq, keys, bkeys, sbkeys, total;
     // MFMA chunk path only
     size_t cq, qh, hkeys_hi;
 };
@@ -33,7 +33,7 @@ bool mma_path(int Q, int pool_blocks, int topk) {
 }
 
 // workspace of csa2_index_full: decoded query, folded weights, per-position
-// keys, per-block keys; on the MFMA path also the guard constants, the fp16
+// keys, per-block keys, per-superblock keys; on the MFMA path also the guard constants, the fp16
 // queries and the upper-bound keys per half-block of 4 (the lower bounds use
 // the per-block keys; the per-position keys serve the exact fallback)
 IndexLayout full_layout(int B, int Q, int64_t cap, int topk, int pool_blocks) {
@@ -44,6 +44,7 @@ IndexLayout full_layout(int B, int Q, int64_t cap, int topk, int pool_blocks) {
     L.wq = off; off += align_up(nq * 4 * sizeof(float));
     L.keys = off; off += align_up(nq * (size_t)cap * sizeof(uint32_t));
     L.bkeys = off; off += align_up(nq * (size_t)(cap / 8) * sizeof(uint32_t));
+    L.sbkeys = off; off += align_up(nq * (size_t)(cap / kSuper) * sizeof(uint32_t));
     if (mma_path(Q, pool_blocks, topk)) {
         L.cq = off; off += align_up(nq * sizeof(float));
         L.qh = off; off += align_up(nq * 256 * sizeof(uint16_t));
@@ -270,13 +271,14 @@ __attribute__((visibility("default"))) int csa2_index_full_timed(
         return hip_status(e);
     }
 
+    uint32_t* sbkeys = reinterpret_cast<uint32_t*>(w + L.sbkeys);
     hipError_t e = launch_prep_iq(iq, iw, nq, qd, wq, stream);
     if (e == hipSuccess)
         e = launch_scan(ik_codes, ik_sigma, cap, B, Q, qd, wq, n_vis, keys, bkeys, stream,
-                        scan_start, scan_stop);
+                        scan_start, scan_stop, sbkeys);
     if (e == hipSuccess)
         e = launch_select_full(keys, bkeys, cap, n_vis, nq, P, topk,
-                               pool_blocks > 0 ? pool_idx : nullptr, topk_idx, stream);
+                               pool_blocks > 0 ? pool_idx : nullptr, topk_idx, stream, sbkeys);
     return hip_status(e);
 }
 

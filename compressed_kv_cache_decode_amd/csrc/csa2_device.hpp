@@ -125,6 +125,15 @@ __device__ __forceinline__ uint32_t max8_u32(uint32_t v) {
     return v;
 }
 
+// max over the wave of a value whose aligned 8-lane groups already hold their
+// group max (max8_u32): scalar reads of the eight groups
+__device__ __forceinline__ uint32_t wave_max_of_groups8(uint32_t g8) {
+    uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)g8, 0);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = max(m, (uint32_t)__builtin_amdgcn_readlane((int)g8, 8 * i));
+    return m;
+}
+
 __device__ __forceinline__ float wave_max_f32(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));

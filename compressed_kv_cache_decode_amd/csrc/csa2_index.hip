@@ -97,9 +97,10 @@ __device__ __forceinline__ void scan_query_exact(const uint8_t* __restrict__ ikc
 
 // ---------------------------------------------------------------------------
 // Full-layer scan.  grid = (ceil(cap / 256), B); 256 threads, one position each.
-// For every query of the sequence: key of each position, and the max key of
-// each 8-position block (DPP max over 8 adjacent lanes).  Tiles that no
-// query of the sequence can see are skipped entirely.
+// For every query of the sequence: key of each position, the max key of each
+// 8-position block (DPP max over 8 adjacent lanes) and, when sbkeys is set,
+// of each 64-position superblock (one wave).  Tiles that no query of the
+// sequence can see are skipped entirely.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_scan(const uint8_t* __restrict__ ikc,
                                               const float* __restrict__ iks, int64_t cap, int Q,
@@ -107,7 +108,8 @@ __global__ __launch_bounds__(256) void k_scan(const uint8_t* __restrict__ ikc,
                                               const float* __restrict__ wq,
                                               const int32_t* __restrict__ n_vis,
                                               uint32_t* __restrict__ keys,
-                                              uint32_t* __restrict__ bkeys) {
+                                              uint32_t* __restrict__ bkeys,
+                                              uint32_t* __restrict__ sbkeys) {
     const int b = blockIdx.y;
     const int64_t p0 = (int64_t)blockIdx.x * 256;
     const int64_t p = p0 + threadIdx.x;
@@ -131,6 +133,10 @@ __global__ __launch_bounds__(256) void k_scan(const uint8_t* __restrict__ ikc,
         keys[bq * cap + p] = key;
         const uint32_t bk = max8_u32(key);
         if ((threadIdx.x & 7) == 0) bkeys[bq * nb + (p >> 3)] = bk;
+        if (sbkeys != nullptr) {
+            const uint32_t sk = wave_max_of_groups8(bk);
+            if ((threadIdx.x & 63) == 0) sbkeys[bq * (cap / kSuper) + (p / kSuper)] = sk;
+        }
     }
 }
 
@@ -148,7 +154,8 @@ __global__ __launch_bounds__(256) void k_scan_multi(const uint8_t* __restrict__ 
                                                     const float* __restrict__ wq,
                                                     const int32_t* __restrict__ n_vis,
                                                     uint32_t* __restrict__ keys,
-                                                    uint32_t* __restrict__ bkeys) {
+                                                    uint32_t* __restrict__ bkeys,
+                                                    uint32_t* __restrict__ sbkeys) {
     __shared__ __attribute__((aligned(16))) float sq[kScanQChunk * kIdxHeads * kIdxDim];
     __shared__ float sw[kScanQChunk * kIdxHeads];
     __shared__ int red[4];
@@ -220,6 +227,10 @@ __global__ __launch_bounds__(256) void k_scan_multi(const uint8_t* __restrict__ 
             keys[bq * cap + p] = key;
             const uint32_t bk = max8_u32(key);
             if ((threadIdx.x & 7) == 0) bkeys[bq * nb + (p >> 3)] = bk;
+            if (sbkeys != nullptr) {
+                const uint32_t sk = wave_max_of_groups8(bk);
+                if ((threadIdx.x & 63) == 0) sbkeys[bq * (cap / kSuper) + (p / kSuper)] = sk;
+            }
         }
     }
 }
@@ -731,6 +742,25 @@ __device__ __forceinline__ void compact_reg(const uint32_t (&k)[kSelKpt], const 
     }
 }
 
+// The K-th largest of the workgroup's register keys (threshold_reg's result
+// th): the tie value, else the smallest key at or above the cut; 1 when fewer
+// than K keys are non-zero.  red: kSelWaves words of LDS.
+__device__ __forceinline__ uint32_t kth_key_reg(const uint32_t (&k)[kSelKpt], const Threshold& th,
+                                                int K, uint32_t* red) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t m = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < kSelKpt; ++i) m = (k[i] != 0 && k[i] >= th.t_ge) ? min(m, k[i]) : m;
+    m = wave_reduce(m, [](uint32_t a, uint32_t b) { return min(a, b); });
+    __syncthreads();  // earlier readers of red are done
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    m = 0xFFFFFFFFu;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) m = min(m, red[w]);
+    return th.total < (uint32_t)K ? 1u : (th.quota != 0 ? th.t_eq : m);
+}
+
 // Select through the register path when the slot count allows it, else the
 // streaming path.  `ks` gives keys and indices of slots.
 __device__ __forceinline__ void select_into(const KeySrc& ks, int K, int32_t* out, int32_t* lds_out,
@@ -749,15 +779,76 @@ __device__ __forceinline__ void select_into(const KeySrc& ks, int K, int32_t* ou
     }
 }
 
+// Blocks too many for the register path (more than 16384, e.g. a 1M-position
+// context): with x the P-th largest superblock key (max over 8 blocks), P
+// distinct superblocks each hold a block whose key is >= x, so the P-th
+// largest block key is >= x and every block of the pool lies in a superblock
+// whose key reaches x.  Those superblocks, in ascending order (at most 2048,
+// so their 16384 block keys fit the register path), give the pool with the
+// same ranking and tie rule.  Returns false (nothing selected) when more than
+// 2048 superblocks qualify (heavy ties): the caller then streams the blocks.
+constexpr int kSuperCand = 2048;
+static_assert(2 * kSuperCand <= kMaxPoolBlocks, "pool and superblock list share sh.pool");
+
+__device__ __forceinline__ bool select_blocks_super(const uint32_t* __restrict__ bkeys,
+                                                    const uint32_t* __restrict__ sbkeys,
+                                                    int64_t nbv, int64_t nsv, int P,
+                                                    int32_t* pool_out, SelShared& sh) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    SelRegShared& rs = *reinterpret_cast<SelRegShared*>(&sh.hist[0]);
+    const KeySrc sup{sbkeys, nullptr, nsv, (int)nsv, 0};
+    uint32_t k[kSelKpt];
+    sup.load16((int64_t)wave * 1024 + 16 * lane, k);
+    const Threshold th = threshold_reg(k, P, rs);
+    const uint32_t x = kth_key_reg(k, th, P, sh.red[0]);
+    // ordered compaction of the qualifying superblocks (this thread's 16 are
+    // consecutive) into the upper half of sh.pool
+    uint32_t mask = 0;
+#pragma unroll
+    for (int i = 0; i < kSelKpt; ++i) mask |= (k[i] != 0 && k[i] >= x) ? (1u << i) : 0u;
+    const uint32_t cnt = __popc(mask);
+    const uint32_t excl = wave_excl_scan(cnt);
+    if (lane == 63) sh.wgt[wave] = excl + cnt;
+    __syncthreads();
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+        before += w < wave ? sh.wgt[w] : 0u;
+        total += sh.wgt[w];
+    }
+    if (total > (uint32_t)kSuperCand) return false;  // uniform
+    int32_t* list = sh.pool + kSuperCand;
+    uint32_t r = before + excl;
+    for (uint32_t mm = mask; mm != 0; mm &= mm - 1u, ++r)
+        list[r] = 16 * tid + __builtin_ctz(mm);
+    __syncthreads();  // the list is complete
+    // block s of the candidates is block 8 list[s / 8] + s % 8 (absent past nbv)
+    const KeySrc cand{bkeys, list, (int64_t)total * kBlock, (int)nbv, 1};
+    select_into(cand, P, pool_out, sh.pool, sh);
+    return true;
+}
+
 // Full layer for query bq: best P blocks (pool), then the best K positions
-// inside it.  pool_out may be null (internal pool).
+// inside it.  pool_out may be null (internal pool).  sbkeys: null, or the
+// scan's superblock keys, used when the blocks do not fit the register path.
 __device__ __forceinline__ void select_full_query(const uint32_t* __restrict__ keys,
                                                   const uint32_t* __restrict__ bkeys, int64_t cap,
                                                   int64_t bq, int nv, int P, int K,
                                                   int32_t* pool_out, int32_t* topk_out,
-                                                  SelShared& sh) {
-    KeySrc blocks{bkeys + bq * (cap / kBlock), nullptr, ((int64_t)nv + kBlock - 1) / kBlock, nv, 0};
-    select_into(blocks, P, pool_out ? pool_out + bq * P : nullptr, sh.pool, sh);
+                                                  SelShared& sh,
+                                                  const uint32_t* __restrict__ sbkeys = nullptr) {
+    const int64_t nbv = ((int64_t)nv + kBlock - 1) / kBlock;
+    const int64_t nsv = ((int64_t)nv + kSuper - 1) / kSuper;
+    int32_t* prow = pool_out ? pool_out + bq * P : nullptr;
+    bool done = false;
+    if (sbkeys != nullptr && nbv > kSelRegSlots && nsv <= kSelRegSlots && P <= kSuperCand)
+        done = select_blocks_super(bkeys + bq * (cap / kBlock), sbkeys + bq * (cap / kSuper), nbv,
+                                   nsv, P, prow, sh);
+    if (!done) {
+        __syncthreads();
+        KeySrc blocks{bkeys + bq * (cap / kBlock), nullptr, nbv, nv, 0};
+        select_into(blocks, P, prow, sh.pool, sh);
+    }
     __syncthreads();
     KeySrc pos{keys + bq * cap, sh.pool, (int64_t)P * kBlock, nv, 1};
     select_into(pos, K, topk_out + bq * K, nullptr, sh);
@@ -766,11 +857,11 @@ __device__ __forceinline__ void select_full_query(const uint32_t* __restrict__ k
 __global__ __launch_bounds__(kSelThreads) void k_select_full(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ bkeys, int64_t cap,
     const int32_t* __restrict__ n_vis, int P, int K, int32_t* __restrict__ pool_out,
-    int32_t* __restrict__ topk_out) {
+    int32_t* __restrict__ topk_out, const uint32_t* __restrict__ sbkeys) {
     __shared__ SelShared sh;
     const int64_t bq = blockIdx.x;
     select_full_query(keys, bkeys, cap, bq, clamp_nvis(n_vis[bq], cap), P, K, pool_out, topk_out,
-                      sh);
+                      sh, sbkeys);
 }
 
 // Reindex: best K positions of the compact pool-ordered keys.
@@ -953,7 +1044,8 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select(
 // ---------------------------------------------------------------------------
 hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                        const float* qd, const float* wq, const int32_t* n_vis, uint32_t* keys,
-                       uint32_t* bkeys, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+                       uint32_t* bkeys, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
+                       uint32_t* sbkeys) {
     dim3 grid((unsigned)((cap + 255) / 256), (unsigned)B);
     // a few queries per sequence: k_scan reads them through the scalar cache;
     // many (the replay chunk): k_scan_multi stages them in LDS
@@ -961,10 +1053,10 @@ hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B,
     if (start != nullptr && stop != nullptr) {
         // the runtime records `start` / `stop` immediately around this dispatch
         hipExtLaunchKernelGGL(kern, grid, dim3(256), 0, stream, start, stop, 0, ikc, iks, cap, Q,
-                              qd, wq, n_vis, keys, bkeys);
+                              qd, wq, n_vis, keys, bkeys, sbkeys);
     } else {
         hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, ikc, iks, cap, Q, qd, wq, n_vis,
-                           keys, bkeys);
+                           keys, bkeys, sbkeys);
     }
     return hipGetLastError();
 }
@@ -981,9 +1073,10 @@ hipError_t launch_pool_score(const uint8_t* ikc, const float* iks, int64_t cap, 
 
 hipError_t launch_select_full(const uint32_t* keys, const uint32_t* bkeys, int64_t cap,
                               const int32_t* n_vis, int64_t n_queries, int P, int K,
-                              int32_t* pool_out, int32_t* topk_out, hipStream_t stream) {
+                              int32_t* pool_out, int32_t* topk_out, hipStream_t stream,
+                              const uint32_t* sbkeys) {
     hipLaunchKernelGGL(k_select_full, dim3((unsigned)n_queries), dim3(kSelThreads), 0, stream, keys,
-                       bkeys, cap, n_vis, P, K, pool_out, topk_out);
+                       bkeys, cap, n_vis, P, K, pool_out, topk_out, sbkeys);
     return hipGetLastError();
 }
 

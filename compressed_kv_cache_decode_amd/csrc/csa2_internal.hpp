@@ -48,10 +48,12 @@ hipError_t launch_codec_probe(float* e4m3_dec, float* e4m3_dec16, float* fp4_dec
                               const float* x, int64_t n, uint8_t* e4m3_enc, uint8_t* e2m1_enc,
                               hipStream_t stream);
 
+// sbkeys (may be null): also the max key per superblock of kSuper positions
+constexpr int kSuper = 64;
 hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                        const float* qd, const float* wq, const int32_t* n_vis, uint32_t* keys,
                        uint32_t* bkeys, hipStream_t stream, hipEvent_t start = nullptr,
-                       hipEvent_t stop = nullptr);
+                       hipEvent_t stop = nullptr, uint32_t* sbkeys = nullptr);
 // MFMA scan of a multi-query chunk with guard-band bounds (csa2_chunk.hip):
 // the largest lower-bound score key per block of 8 positions [nq][cap / 8]
 // and the upper-bound key per half-block of 4 [nq][cap / 4]
@@ -76,9 +78,12 @@ constexpr int kChunkMaxTopk = 1024;
 hipError_t launch_pool_score(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                              const float* iq, const float* iw, const int32_t* n_vis,
                              const int32_t* pool, int P, uint32_t* ckeys, hipStream_t stream);
+// sbkeys: null, or the scan's superblock keys (used when the blocks do not
+// fit the register path)
 hipError_t launch_select_full(const uint32_t* keys, const uint32_t* bkeys, int64_t cap,
                               const int32_t* n_vis, int64_t n_queries, int P, int K,
-                              int32_t* pool_out, int32_t* topk_out, hipStream_t stream);
+                              int32_t* pool_out, int32_t* topk_out, hipStream_t stream,
+                              const uint32_t* sbkeys = nullptr);
 hipError_t launch_select_pool(const uint32_t* ckeys, const int32_t* pool, int P,
                               const int32_t* n_vis, int64_t cap, int64_t n_queries, int K,
                               int32_t* topk_out, hipStream_t stream);

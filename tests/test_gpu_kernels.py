@@ -252,6 +252,28 @@ def test_index_full_all_ties(gpu, oracle_mod):
     assert p[:500].tolist() == list(range(500)) and np.all(p[500:] == -1)
 
 
+def test_index_full_all_ties_streaming_blocks(gpu, oracle_mod):
+    """More blocks than the register path holds, every score equal: all 4096
+    superblocks tie, more than the two-level block selection takes, so the
+    blocks are selected by streaming; ties go to the lowest blocks and
+    positions."""
+    say("index_full all-equal scores, 262144 positions")
+    B, cap = 1, 262144
+    x = np.tile(np.random.default_rng(15).standard_normal((1, 1, 64)), (B, cap, 1)).astype(np.float32)
+    ikc, iks = oracle_mod.quant_fp8_rows(x)
+    cache = gpu.Cache(B, cap)
+    cache.ik_codes.copy_(dev(tile_ik(ikc)))
+    cache.ik_sigma.copy_(dev(iks.reshape(-1)))
+    iq = np.random.default_rng(16).standard_normal((B, 1, 4, 64)).astype(np.float32)
+    iw = np.ones((B, 1, 4), np.float32)
+    nv = np.array([[262141]], np.int32)
+    tk = torch.empty((B, 1, 512), dtype=torch.int32, device="cuda")
+    pl = torch.empty((B, 1, 2048), dtype=torch.int32, device="cuda")
+    gpu.index_full(cache, dev(iq), dev(iw), dev(nv), tk, pl, topk=512, pool_blocks=2048)
+    assert host(tk)[0, 0].tolist() == list(range(512))
+    assert host(pl)[0, 0].tolist() == list(range(2048))
+
+
 @pytest.mark.parametrize("B,cap,nvis,pool,topk", [(2, 8192, [8192, 5001], 512, 512),
                                                   (3, 32768, [32768, 30000, 77], 2048, 512),
                                                   (1, 4096, [4096], 64, 100),
