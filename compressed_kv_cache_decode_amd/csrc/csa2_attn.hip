@@ -51,12 +51,15 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 32;           // entries per tile
-constexpr int kWaves = 8;           // waves per workgroup
-constexpr int kThreads = kWaves * 64;
+// waves per workgroup: 8, or 4 when there are enough (query, head group)
+// workgroups for two of them to share each CU (its LDS holds two 4-wave
+// workgroups, not two 8-wave ones), so that they all run in one round
+constexpr int kWavesWide = 8, kWavesNarrow = 4;
 constexpr int kGroupHeads = 16;     // heads per workgroup (one MFMA column block)
 constexpr int kVPitch = 144;        // fp16 per V row in LDS (128 + 16)
 constexpr int kMergePitch = kHeadDim + 4;  // fp32 per merged output row in LDS
 constexpr int kXcds = 8;
+constexpr int kCusPerChip = 256;
 constexpr int kMaxWindow = 128;     // window rows per sequence (decode 128, chunk <= 128)
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag the true max
 constexpr float kLog2e = 1.4426950408889634f;
@@ -67,10 +70,14 @@ constexpr int kWaveBytes = kTile * kVPitch * 2;              // one wave's V til
 constexpr int kOffQ = 0;                                     // q [16][128] fp32
 constexpr int kOffWin = kOffQ + kGroupHeads * kHeadDim * 4;  // window K scales [128], V scales [128]
 constexpr int kOffWave = kOffWin + 2 * kMaxWindow * 4;       // per-wave V tiles
-constexpr int kLdsBytes = kOffWave + kWaves * kWaveBytes;
-constexpr int kMergeBytes = (kWaves * kGroupHeads * kMergePitch + 2 * kWaves * kGroupHeads) * 4;
-static_assert(kMergeBytes <= kWaves * kWaveBytes, "merge area aliases the wave areas");
-static_assert(kLdsBytes <= 160 * 1024, "LDS");
+constexpr int lds_bytes(int W) { return kOffWave + W * kWaveBytes; }
+constexpr int merge_bytes(int W) {
+    return (W * kGroupHeads * kMergePitch + 2 * W * kGroupHeads) * 4;
+}
+static_assert(merge_bytes(kWavesWide) <= kWavesWide * kWaveBytes, "merge area aliases the wave areas");
+static_assert(merge_bytes(kWavesNarrow) <= kWavesNarrow * kWaveBytes, "merge area aliases the wave areas");
+static_assert(lds_bytes(kWavesWide) <= 160 * 1024, "LDS");
+static_assert(2 * lds_bytes(kWavesNarrow) <= 160 * 1024, "two narrow workgroups per CU");
 
 size_t attn_workspace_bytes(int64_t, int, int, int) { return 0; }
 
@@ -407,9 +414,10 @@ __device__ __forceinline__ void touch(const T& v) {
     asm volatile("" ::"s"(v));
 }
 
-template <int STAGE>
-__global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a, int n_tiles_global) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
+template <int STAGE, int kWaves>
+__global__ __launch_bounds__(kWaves * 64) void k_attn(AttnArgs a, int n_tiles_global) {
+    constexpr int kThreads = kWaves * 64;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[lds_bytes(kWaves)];
     touch(a.q); touch(a.H); touch(a.Q); touch(a.kvc); touch(a.kvs); touch(a.cap);
     touch(a.idx); touch(a.topk); touch(a.swk); touch(a.swv); touch(a.swks); touch(a.swvs);
     touch(a.swa_len); touch(a.swa_rows); touch(a.sm_scale); touch(a.out); touch(a.lse);
@@ -464,13 +472,16 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a, int n_tiles_globa
 
     // ---- meanwhile, once per workgroup: q of the 16 heads, window scales ----
     {
-        const float4 qv = reinterpret_cast<const float4*>(
-            a.q + (bq * a.H + hg * kGroupHeads) * kHeadDim)[tid];
+        static_assert(kGroupHeads * kHeadDim / 4 % kThreads == 0, "q staging");
+        static_assert(2 * kMaxWindow <= kThreads, "window scales staging");
+#pragma unroll
+        for (int i = tid; i < kGroupHeads * kHeadDim / 4; i += kThreads)
+            reinterpret_cast<float4*>(q_l)[i] = reinterpret_cast<const float4*>(
+                a.q + (bq * a.H + hg * kGroupHeads) * kHeadDim)[i];
         float wv = 0.0f;
         const int tok = tid & (kMaxWindow - 1);
         if (tid < 2 * kMaxWindow && tok < s.swa_len)
             wv = (tid < kMaxWindow ? a.swks : a.swvs)[s.b * s.swa_rows + tok];
-        reinterpret_cast<float4*>(q_l)[tid] = qv;
         if (tid < 2 * kMaxWindow) win_l[tid] = wv;
     }
     __syncthreads();
@@ -582,15 +593,19 @@ hipError_t launch_attn(const AttnArgs& a, void* /*ws*/, size_t /*ws_bytes*/, hip
     const int64_t rounds = (a.n_q + kXcds - 1) / kXcds;
     const unsigned grid = (unsigned)(rounds * kXcds * G);
     if (a.stage_mode != 0 && (a.stage == nullptr || a.Q != 1)) return hipErrorInvalidValue;
-    void (*kern)(AttnArgs, int) = a.stage_mode == kStageWrite  ? k_attn<kStageWrite>
-                                  : a.stage_mode == kStageRead ? k_attn<kStageRead>
-                                                               : k_attn<0>;
+    // narrow workgroups once two rounds of wide ones would be needed
+    const bool narrow = a.stage_mode == 0 && (int64_t)grid >= 2 * kCusPerChip;
+    void (*kern)(AttnArgs, int) = a.stage_mode == kStageWrite  ? k_attn<kStageWrite, kWavesWide>
+                                  : a.stage_mode == kStageRead ? k_attn<kStageRead, kWavesWide>
+                                  : narrow                     ? k_attn<0, kWavesNarrow>
+                                                               : k_attn<0, kWavesWide>;
+    const dim3 block((narrow ? kWavesNarrow : kWavesWide) * 64);
     if (start != nullptr && stop != nullptr) {
         // the runtime records `start` / `stop` immediately around this dispatch
-        hipExtLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, start, stop, 0, a,
+        hipExtLaunchKernelGGL(kern, dim3(grid), block, 0, stream, start, stop, 0, a,
                               n_tiles_global);
     } else {
-        hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, a, n_tiles_global);
+        hipLaunchKernelGGL(kern, dim3(grid), block, 0, stream, a, n_tiles_global);
     }
     return hipGetLastError();
 }
