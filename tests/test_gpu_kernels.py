@@ -180,6 +180,10 @@ def make_idx_cache(gpu, oracle_mod, B, cap, seed, dup_frac=0.0):
     (2, 16, 16384, [[0, 1, 5, 300, 511, 512, 513, 4096, 8191, 8192, 12000, 16383, 16384,
                      16384, 7, 9000], [16384 - 1000 * i for i in range(16)]], 512, 0),
     (1, 4, 1024, [[1024, 1024, 1000, 3]], 2048, 0),   # top-K larger than what is visible
+    # a capacity that is not a multiple of 256: the scans' last workgroup is
+    # partly past it (MFMA path with Q = 5, single-query scan with Q = 1)
+    (1, 5, 1088, [[1088, 1087, 1000, 700, 64]], 64, 0),
+    (2, 1, 1088, [1088, 1025], 64, 128),
     # top-K above 1024 takes the exact multi-query scan; at 1024 the MFMA
     # path's largest candidate pool (1536 blocks, 12288 keys in LDS); more than
     # 16384 blocks: the candidate threshold streams
