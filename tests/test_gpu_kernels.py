@@ -185,8 +185,8 @@ def make_idx_cache(gpu, oracle_mod, B, cap, seed, dup_frac=0.0):
     (1, 5, 1088, [[1088, 1087, 1000, 700, 64]], 64, 0),
     (2, 1, 1088, [1088, 1025], 64, 128),
     # top-K above 1024 takes the exact multi-query scan; at 1024 the MFMA
-    # path's largest candidate pool (1536 blocks, 12288 keys in LDS); more than
-    # 16384 blocks: the candidate threshold streams
+    # path's largest candidate list (3072 half-blocks, 12288 keys in LDS); more
+    # than 16384 blocks: the candidate threshold streams
     (1, 5, 65536, [[65536, 65000, 40000, 20000, 9]], 2048, 0),
     (1, 5, 65536, [[65536, 65000, 40000, 20000, 9]], 1024, 0),
     (1, 4, 262144, [[262144, 262000, 131073, 70000]], 512, 0),
