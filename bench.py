@@ -335,6 +335,119 @@ def run_chunk_bench(args, wl):
     }
 
 
+# --------------------------------------------------------------------------- replay chunk stack
+def run_chunk_stack_bench(args, wl):
+    """Bounded-replay chunk through the whole decoder stack: the chunk's 128
+    new entries (RoPE + FP4), their indexer keys and every layer's window K and
+    V in one write launch, then the 20 layers (Full with per-token pools, 4
+    Reindex, 15 Reuse), each with the chunk attention of its 128 tokens."""
+    import numpy as np
+    import torch
+
+    import compressed_kv_cache_decode_amd as csa2
+    from compressed_kv_cache_decode_amd import synth
+    from compressed_kv_cache_decode_amd.stack import ChunkStack
+
+    inp = synth.chunk_stack_inputs(wl)
+    B, N, Q, H, L = wl.B, wl.n_ent, wl.Q, wl.H, len(wl.plan)
+    cap = (N + 63) // 64 * 64
+    log(f"chunk stack: writing {args.cache_sets} cache sets of {N} entries, plan {wl.plan}")
+    caches = []
+    for s_ in range(args.cache_sets):
+        cache = csa2.Cache(B, cap)
+        if s_ == 0:
+            pre = np.arange(N - Q)
+            csa2.quant_fp4(torch.from_numpy(inp.k_tok[0, :N - Q]).cuda(),
+                           torch.from_numpy(inp.v_tok[0, :N - Q]).cuda(), cache.kv_codes,
+                           cache.kv_scales, rope_cs=torch.from_numpy(csa2.rope_table(pre)).cuda(),
+                           dst_rows=cache.rows(0, pre))
+            csa2.quant_fp8(torch.from_numpy(inp.idx_k[0, :N - Q]).cuda(), cache.ik_codes,
+                           cache.ik_sigma, layout=csa2.FP8_IDX_TILED, dst_rows=cache.rows(0, pre))
+        else:
+            for name in ("kv_codes", "kv_scales", "ik_codes", "ik_sigma"):
+                getattr(cache, name).copy_(getattr(caches[0], name))
+        caches.append(cache)
+    d = {
+        "k_new": torch.from_numpy(np.ascontiguousarray(inp.k_tok[0, N - Q:])).cuda(),
+        "v_new": torch.from_numpy(np.ascontiguousarray(inp.v_tok[0, N - Q:])).cuda(),
+        "rope_new": torch.from_numpy(csa2.rope_table(inp.positions)).cuda(),
+        "idx_new": torch.from_numpy(np.ascontiguousarray(inp.idx_k[0, N - Q:])).cuda(),
+        "swa_k": torch.from_numpy(inp.swa_k.reshape(-1, 128)).cuda(),
+        "swa_v": torch.from_numpy(inp.swa_v.reshape(-1, 128)).cuda(),
+        "iq": torch.from_numpy(inp.iq).cuda(), "iw": torch.from_numpy(inp.iw).cuda(),
+        "n_vis": torch.from_numpy(np.arange(N - Q + 1, N + 1, dtype=np.int32)[None]).cuda(),
+        "q": torch.from_numpy(inp.q).cuda(),
+    }
+    rows_new = caches[0].rows(0, inp.positions)
+    swk = torch.empty((L, B, Q, 128), dtype=torch.uint8, device="cuda")
+    swv = torch.empty_like(swk)
+    sks = torch.empty((L, B, Q), dtype=torch.float32, device="cuda")
+    svs = torch.empty_like(sks)
+    stacks = [ChunkStack(c, wl.plan, B, Q, H, topk=wl.topk, pool_blocks=wl.pool_blocks)
+              for c in caches]
+
+    def step(i, scan_timer=None):
+        cache, st = caches[i], stacks[i]
+        csa2.write_entries(d["k_new"], d["v_new"], cache.kv_codes, cache.kv_scales,
+                           rope_cs=d["rope_new"], dst_rows=rows_new,
+                           fp8_jobs=[dict(x=d["idx_new"], codes=cache.ik_codes,
+                                          sigma=cache.ik_sigma, layout=csa2.FP8_IDX_TILED,
+                                          dst_rows=rows_new),
+                                     dict(x=d["swa_k"], codes=swk, sigma=sks),
+                                     dict(x=d["swa_v"], codes=swv, sigma=svs)])
+        st.step(d["iq"], d["iw"], d["n_vis"], d["q"], swk, swv, sks, svs, scan_timer=scan_timer)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(max(args.warmup, 1)):
+            step(i % len(caches))
+        torch.cuda.synchronize()
+        graphs = []
+        if not args.no_graph:
+            for i in range(len(caches)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    step(i)
+                graphs.append(g)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            if graphs:
+                graphs[i % len(graphs)].replay()
+            else:
+                step(i % len(caches))
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        timer = csa2.KernelTimer(args.steps)
+        for i in range(args.steps):
+            step(i % len(caches), scan_timer=timer)
+        torch.cuda.synchronize()
+        scan_ms = timer.durations_ms()
+        timer.close()
+    scan_mean = sum(scan_ms) / len(scan_ms)
+    # the Full layer's scan with pools is the exact VALU scan: 4 heads x 64
+    # sequential fp32 FMAs per (token, position) pair, 2 flops each
+    flops = 2.0 * 256 * Q * N
+    tfs = flops / (scan_mean * 1e-3) / 1e12
+    peak = 157.3
+    return {
+        "metric": "CSA2 bounded-replay chunk through the decoder stack, queries/s (128 replayed "
+                  "tokens over 128K entries, 20 layers)",
+        "value": round(Q * B * args.steps / elapsed, 1), "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "sequences": B, "entries": N, "queries": Q, "heads": H,
+                   "plan": wl.plan, "topk": wl.topk, "pool_blocks": wl.pool_blocks,
+                   "cache_sets": args.cache_sets,
+                   "launch": "eager" if args.no_graph else "hip-graph"},
+        "roofline": {"bound": "alu", "achieved": round(tfs, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tfs / peak, 4), "traffic": None,
+                     "kernel": "k_scan_multi (Full-layer exact scan of 128 tokens, with pools)",
+                     "flops_per_launch": flops, "mean_us": round(scan_mean * 1e3, 2)},
+    }
+
+
 # --------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(args, wl, inp):
     """The oracle as it stands, on its own caches (built before timing), for a
@@ -465,7 +578,8 @@ def main():
     if args.copy_calibration_mb:
         copy_calibration(args.copy_calibration_mb)
     if wl.Q != 1:
-        print(json.dumps(run_chunk_bench(args, wl)), flush=True)
+        run = run_chunk_bench if wl.plan == "F" else run_chunk_stack_bench
+        print(json.dumps(run(args, wl)), flush=True)
         return
     log(f"workload {wl.name}: drawing inputs (seed {wl.seed})")
     inp = synth.decode_inputs(wl)

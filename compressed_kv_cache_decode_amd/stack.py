@@ -1,4 +1,5 @@
-"""Layer-plan driver: one decode step of a CSA2 layer stack over a shared cache.
+"""Layer-plan drivers: one decode step of a CSA2 layer stack over a shared
+cache, and one bounded-replay chunk through such a stack.
 
 "DeepSeek V4.1 Flash: architecture study notes", section 2: every CSA2 layer
 is statically Full, Reindex or Reuse; the decoder is one Full layer, four
@@ -15,13 +16,19 @@ stage buffer, and the Reuse layers after it read them from there instead of
 gathering through the same positions again (the cache is shared by every
 layer, so the records are the same).  This module only sequences library
 calls; buffers are allocated once, up front.
+
+"DeepSeek V4.1 Flash: architecture study notes", section 5: a decoder whose
+window state is gone replays the last 128 tokens; ChunkStack runs those
+tokens through every layer of the plan, each replayed token with its own
+Full/Reindex selection (and, for the Reindex layers, its own pool from the
+Full layer) and its in-chunk causal window.
 """
 import torch
 
-from . import (DEFAULT_POOL_BLOCKS, DEFAULT_TOPK, HEAD_DIM, OP_ATTN_DECODE, OP_ATTN_STAGE,
-               OP_INDEX_FULL, OP_INDEX_REINDEX, STAGE_READ, STAGE_WRITE, alloc_workspace,
-               index_full, index_reindex, sparse_attn_decode, sparse_attn_decode_reuse,
-               workspace_size)
+from . import (DEFAULT_POOL_BLOCKS, DEFAULT_TOPK, HEAD_DIM, OP_ATTN_CHUNK, OP_ATTN_DECODE,
+               OP_ATTN_STAGE, OP_INDEX_FULL, OP_INDEX_REINDEX, STAGE_READ, STAGE_WRITE,
+               alloc_workspace, index_full, index_reindex, sparse_attn_chunk, sparse_attn_decode,
+               sparse_attn_decode_reuse, workspace_size)
 
 
 def check_plan(plan, pool_blocks):
@@ -103,3 +110,55 @@ class DecodeStack:
                     ws=self.ws_attn, stream=stream, timer=attn_timer)
             used.append(cur)
         return used
+
+
+class ChunkStack:
+    """Buffers and workspaces for a Q-token replay chunk through `plan` over
+    `cache` (B sequences, H heads): per layer and chunk token, the indices it
+    attends with, its output and lse."""
+
+    def __init__(self, cache, plan, B, Q, H, topk=DEFAULT_TOPK, pool_blocks=DEFAULT_POOL_BLOCKS):
+        check_plan(plan, pool_blocks)
+        self.cache, self.plan, self.B, self.Q, self.H = cache, plan, B, Q, H
+        self.topk, self.pool_blocks = topk, pool_blocks
+        dev = cache.kv_codes.device
+        n_idx = sum(1 for m in plan if m in "FX")
+        self.topk_bufs = torch.empty((n_idx, B, Q, topk), dtype=torch.int32, device=dev)
+        self.pool = torch.empty((B, Q, max(pool_blocks, 1)), dtype=torch.int32, device=dev)
+        self.ws_full = alloc_workspace(
+            workspace_size(OP_INDEX_FULL, B, Q, cache.cap, topk, pool_blocks, 0), dev)
+        self.ws_reindex = (alloc_workspace(
+            workspace_size(OP_INDEX_REINDEX, B, Q, cache.cap, topk, pool_blocks, 0), dev)
+            if "X" in plan else None)
+        n_attn = workspace_size(OP_ATTN_CHUNK, B, Q, cache.cap, topk, 0, H)
+        self.ws_attn = alloc_workspace(n_attn, dev) if n_attn else None
+        self.out = torch.empty((len(plan), B, Q, H, HEAD_DIM), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((len(plan), B, Q, H), dtype=torch.float32, device=dev)
+        self.sources = reuse_sources(plan)
+
+    def step(self, iq, iw, n_vis, q, swa_k, swa_v, swa_ks, swa_vs, stream=None, scan_timer=None):
+        """One replay chunk through the stack.
+
+        iq [n_idx][B][Q][4][64], iw [n_idx][B][Q][4]: per Full/Reindex layer and
+        chunk token; n_vis [B][Q] int32 (token i sees entries [0, n_vis)); q
+        [L][B][Q][H][128]; swa_k/v [L][B][Q][128] u8, swa_ks/vs [L][B][Q] f32:
+        each layer's window over the chunk's tokens.  Returns the top-K buffer
+        each layer attended with."""
+        used, cur, k = [], None, 0
+        for layer, mode in enumerate(self.plan):
+            if mode == "F":
+                index_full(self.cache, iq[k], iw[k], n_vis, self.topk_bufs[k],
+                           self.pool if self.pool_blocks else None, topk=self.topk,
+                           pool_blocks=self.pool_blocks, ws=self.ws_full, stream=stream,
+                           scan_timer=scan_timer)
+                cur, k = self.topk_bufs[k], k + 1
+            elif mode == "X":
+                index_reindex(self.cache, iq[k], iw[k], n_vis, self.pool, self.topk_bufs[k],
+                              topk=self.topk, ws=self.ws_reindex, stream=stream)
+                cur, k = self.topk_bufs[k], k + 1
+            sparse_attn_chunk(q[layer], self.cache, cur, swa_k[layer], swa_v[layer],
+                              swa_ks[layer], swa_vs[layer], self.out[layer], self.lse[layer],
+                              ws=self.ws_attn, stream=stream)
+            used.append(cur)
+        return used
+

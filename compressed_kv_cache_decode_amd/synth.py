@@ -13,6 +13,8 @@ Workloads (positions are global-KV entries of one sequence):
   decoder_stack_1m   the same stack over 1048576 entries, batch 4, keys with
                      planted high-score clusters
   replay_chunk_128k  128 causal queries over 131072 entries (bounded replay)
+  replay_stack_128k  the same 128 replayed queries through the whole decoder
+                     stack (1 Full + 4 Reindex + 15 Reuse), per-query pools
 
 Every array is float32 N(0,1) unless stated; the indexer head weights are
 U(0,1); the indexer key of an entry is a fixed seeded 128->64 projection of
@@ -66,6 +68,8 @@ WORKLOADS = {
                                  plan=DECODER_PLAN, pool_blocks=POOL_BLOCKS, planted=True),
     "replay_chunk_128k": Workload("replay_chunk_128k", 1004, B=1, n_ent=131072, ratio=1, H=64,
                                   plan="F", pool_blocks=0, Q=128),
+    "replay_stack_128k": Workload("replay_stack_128k", 1005, B=1, n_ent=131072, ratio=1, H=64,
+                                  plan=DECODER_PLAN, pool_blocks=POOL_BLOCKS, Q=128),
 }
 
 
@@ -205,3 +209,45 @@ def chunk_inputs(wl, n_ent=None, Q=None, H=None, seed=None):
     swa_v = normal(g, (B, Q, HEAD_DIM))
     positions = np.arange(n_ent - Q, n_ent, dtype=np.int64)
     return ChunkInputs(wl, k_tok, v_tok, idx_k, iq, iw, q, swa_k, swa_v, positions)
+
+
+@dataclass
+class ChunkStackInputs:
+    """Host arrays for a bounded-replay chunk through a layer stack: the last
+    Q entries of each sequence are the chunk's; each Full/Reindex layer has
+    its own indexer query per chunk token, each layer its own attention
+    queries and its own window K / V over the chunk's tokens."""
+    wl: Workload
+    plan: str
+    k_tok: np.ndarray      # [B][N][128]
+    v_tok: np.ndarray      # [B][N][128]
+    idx_k: np.ndarray      # [B][N][64]
+    iq: np.ndarray         # [L_idx][B][Q][4][64]
+    iw: np.ndarray         # [L_idx][B][Q][4]
+    q: np.ndarray          # [L][B][Q][H][128]
+    swa_k: np.ndarray      # [L][B][Q][128]
+    swa_v: np.ndarray      # [L][B][Q][128]
+    positions: np.ndarray  # [Q] int64
+
+
+def chunk_stack_inputs(wl, n_ent=None, Q=None, H=None, B=None, layers=None, seed=None):
+    """Draw order: K, V, projection, indexer queries, attention queries, SWA K, SWA V."""
+    n_ent = wl.n_ent if n_ent is None else n_ent
+    Q = wl.Q if Q is None else Q
+    H = wl.H if H is None else H
+    B = wl.B if B is None else B
+    plan = wl.plan if layers is None else wl.plan[:layers]
+    g = rng(wl.seed if seed is None else seed)
+    k_tok = normal(g, (B, n_ent, HEAD_DIM))
+    v_tok = normal(g, (B, n_ent, HEAD_DIM))
+    proj = idx_projection(g)
+    idx_k = project_idx_k(k_tok, proj)
+    n_idx = sum(1 for m in plan if m in "FX")
+    iq = normal(g, (n_idx, B, Q, IDX_HEADS, IDX_DIM))
+    iw = g.random((n_idx, B, Q, IDX_HEADS), dtype=np.float32)
+    L = len(plan)
+    q = normal(g, (L, B, Q, H, HEAD_DIM))
+    swa_k = normal(g, (L, B, Q, HEAD_DIM))
+    swa_v = normal(g, (L, B, Q, HEAD_DIM))
+    positions = np.arange(n_ent - Q, n_ent, dtype=np.int64)
+    return ChunkStackInputs(wl, plan, k_tok, v_tok, idx_k, iq, iw, q, swa_k, swa_v, positions)

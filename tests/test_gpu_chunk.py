@@ -80,3 +80,89 @@ def test_chunk_small(gpu, oracle_mod):
 
 def test_chunk_128k_full_size(gpu, oracle_mod):
     run_chunk(gpu, oracle_mod, n_ent=131072, Q=128, H=64, sample=[0, 1, 2, 63, 100, 127])
+
+
+def run_chunk_stack(gpu, oracle_mod, n_ent, Q, H, layers, sample, B=1):
+    """A replay chunk through a layer stack: the chunk's entries, indexer keys
+    and every layer's window written in one call, then per layer the Full /
+    Reindex selection of each chunk token (per-token pools) and the chunk
+    attention; sampled tokens are checked against the oracle layer by layer
+    (indices and pools bit for bit)."""
+    from compressed_kv_cache_decode_amd.stack import ChunkStack
+    wl = synth.WORKLOADS["replay_stack_128k"]
+    inp = synth.chunk_stack_inputs(wl, n_ent=n_ent, Q=Q, H=H, B=B, layers=layers)
+    plan = inp.plan
+    L = len(plan)
+    cap = (n_ent + 63) // 64 * 64
+    say(f"chunk stack: n_ent={n_ent} Q={Q} H={H} plan={plan}: writing caches")
+    cache = gpu.Cache(B, cap)
+    swk = torch.empty((L, B, Q, 128), dtype=torch.uint8, device="cuda")
+    swv = torch.empty_like(swk)
+    sks = torch.empty((L, B, Q), dtype=torch.float32, device="cuda")
+    svs = torch.empty_like(sks)
+    for b in range(B):
+        pre = np.arange(n_ent - Q)
+        gpu.quant_fp4(dev(inp.k_tok[b, :n_ent - Q]), dev(inp.v_tok[b, :n_ent - Q]), cache.kv_codes,
+                      cache.kv_scales, rope_cs=dev(gpu.rope_table(pre)), dst_rows=cache.rows(b, pre))
+        gpu.quant_fp8(dev(inp.idx_k[b, :n_ent - Q]), cache.ik_codes, cache.ik_sigma,
+                      layout=gpu.FP8_IDX_TILED, dst_rows=cache.rows(b, pre))
+        rows = cache.rows(b, inp.positions)
+        jobs = [dict(x=dev(inp.idx_k[b, n_ent - Q:]), codes=cache.ik_codes, sigma=cache.ik_sigma,
+                     layout=gpu.FP8_IDX_TILED, dst_rows=rows)]
+        if b == 0:   # every layer's window of every sequence, in the same launch
+            jobs += [dict(x=dev(inp.swa_k.reshape(-1, 128)), codes=swk, sigma=sks),
+                     dict(x=dev(inp.swa_v.reshape(-1, 128)), codes=swv, sigma=svs)]
+        gpu.write_entries(dev(inp.k_tok[b, n_ent - Q:]), dev(inp.v_tok[b, n_ent - Q:]),
+                          cache.kv_codes, cache.kv_scales, rope_cs=dev(gpu.rope_table(inp.positions)),
+                          dst_rows=rows, fp8_jobs=jobs)
+    st = ChunkStack(cache, plan, B, Q, H, topk=512, pool_blocks=2048)
+    n_vis = np.tile(np.arange(n_ent - Q + 1, n_ent + 1, dtype=np.int32), (B, 1))
+    say("chunk stack: step")
+    used = st.step(dev(inp.iq), dev(inp.iw), dev(n_vis), dev(inp.q), swk, swv, sks, svs)
+    torch.cuda.synchronize()
+    for layer, src in enumerate(st.sources):
+        assert used[layer].data_ptr() == used[src].data_ptr()
+    tk_all = [host(t) for t in used]
+    pool_h = host(st.pool)
+    out_h, lse_h = host(st.out), host(st.lse)
+    kvc, kvs = host(cache.kv_codes), host(cache.kv_scales)
+    ikc = untile_ik(host(cache.ik_codes), B, cap)
+    for b in range(B):
+        say(f"chunk stack: oracle, sequence {b}")
+        codes, scales = oracle_mod.quant_fp4(inp.k_tok[b], inp.v_tok[b], 1,
+                                             oracle_mod.rope_table(np.arange(n_ent)))
+        np.testing.assert_array_equal(kvc[b * cap:b * cap + n_ent], codes)
+        np.testing.assert_array_equal(kvs[b * cap:b * cap + n_ent], scales)
+        ik_ref, iks_ref = oracle_mod.quant_fp8_rows(inp.idx_k[b])
+        np.testing.assert_array_equal(ikc[b, :n_ent], ik_ref)
+        wins = [(oracle_mod.quant_fp8_rows(inp.swa_k[layer, b]),
+                 oracle_mod.quant_fp8_rows(inp.swa_v[layer, b])) for layer in range(L)]
+        for i in sample:
+            nv = n_ent - Q + i + 1
+            cur, pool, k = None, None, 0
+            for layer, mode in enumerate(plan):
+                if mode == "F":
+                    cur, pool = oracle_mod.index_full(ik_ref, iks_ref, nv, inp.iq[k, b, i],
+                                                      inp.iw[k, b, i], 512, 2048)
+                    np.testing.assert_array_equal(pool_h[b, i], pool, err_msg=f"pool, token {i}")
+                    k += 1
+                elif mode == "X":
+                    cur = oracle_mod.index_reindex(ik_ref, iks_ref, nv, inp.iq[k, b, i],
+                                                   inp.iw[k, b, i], pool, 512)
+                    k += 1
+                np.testing.assert_array_equal(tk_all[layer][b, i], cur,
+                                              err_msg=f"layer {layer} ({mode}), token {i}")
+                (sk, sks_r), (sv, svs_r) = wins[layer]
+                o, l = oracle_mod.attn(inp.q[layer, b, i], codes, scales, cur, sk, sv, sks_r,
+                                       svs_r, i + 1, SM)
+                assert row_rel_err(out_h[layer, b, i], o).max() <= 2e-3, (layer, i)
+                np.testing.assert_allclose(lse_h[layer, b, i], l, rtol=2e-3, atol=2e-3)
+
+
+def test_chunk_stack_small(gpu, oracle_mod):
+    # 2500 blocks: more than the pool's 2048, so each token's pool is a real choice
+    run_chunk_stack(gpu, oracle_mod, n_ent=20000, Q=16, H=16, layers=8, sample=range(16), B=2)
+
+
+def test_chunk_stack_128k_full_size(gpu, oracle_mod):
+    run_chunk_stack(gpu, oracle_mod, n_ent=131072, Q=128, H=64, layers=20, sample=[0, 77, 127])
