@@ -28,8 +28,9 @@ struct IndexLayout {
 
 // A multi-query Full layer without a pool output (the replay chunk) scores on
 // MFMA with guard bands (csa2_chunk.hip); otherwise the exact VALU scan.
-bool mma_path(int Q, int pool_blocks, int topk) {
-    return Q >= 4 && pool_blocks == 0 && topk <= kChunkMaxTopk;
+bool mma_path(int Q, int64_t cap, int pool_blocks, int topk) {
+    return Q >= 4 && topk <= kChunkMaxTopk &&
+           (pool_blocks == 0 || cap / 8 <= kChunkPoolMaxBlocks);
 }
 
 // workspace of csa2_index_full: decoded query, folded weights, per-position
@@ -45,7 +46,7 @@ IndexLayout full_layout(int B, int Q, int64_t cap, int topk, int pool_blocks) {
     L.keys = off; off += align_up(nq * (size_t)cap * sizeof(uint32_t));
     L.bkeys = off; off += align_up(nq * (size_t)(cap / 8) * sizeof(uint32_t));
     L.sbkeys = off; off += align_up(nq * (size_t)(cap / kSuper) * sizeof(uint32_t));
-    if (mma_path(Q, pool_blocks, topk)) {
+    if (mma_path(Q, cap, pool_blocks, topk)) {
         L.cq = off; off += align_up(nq * sizeof(float));
         L.qh = off; off += align_up(nq * 256 * sizeof(uint16_t));
         L.hkeys_hi = off; off += align_up(nq * (size_t)(cap / 4) * sizeof(uint32_t));
@@ -252,12 +253,14 @@ __attribute__((visibility("default"))) int csa2_index_full_timed(
     // requested pool, P = K blocks are kept internally.
     const int P = pool_blocks > 0 ? pool_blocks : topk;
 
-    if (mma_path(Q, pool_blocks, topk)) {
-        // bounds on MFMA, then per query: candidate half-blocks (upper bound
-        // reaches the K-th largest lower bound of a block), their exact keys
-        // and the top-K, in one workgroup; a query whose candidates overflow
-        // is rescored over all its positions there and takes the Full
-        // selection
+    if (mma_path(Q, cap, pool_blocks, topk)) {
+        // bounds on MFMA, then per query, in one workgroup: with a pool, the
+        // blocks the bounds decide plus the best undecided ones by exact
+        // block key; then the candidate half-blocks (upper bound reaches the
+        // K-th largest lower bound of a block, of the pool's blocks with a
+        // pool), their exact keys and the top-K.  A query whose candidates
+        // overflow is rescored over all its positions there and takes the
+        // Full selection
         float* cq = reinterpret_cast<float*>(w + L.cq);
         _Float16* qh = reinterpret_cast<_Float16*>(w + L.qh);
         uint32_t* hkeys_hi = reinterpret_cast<uint32_t*>(w + L.hkeys_hi);
@@ -267,7 +270,8 @@ __attribute__((visibility("default"))) int csa2_index_full_timed(
                                 hkeys_hi, stream, scan_start, scan_stop);
         if (e == hipSuccess)
             e = launch_chunk_select(ik_codes, ik_sigma, cap, Q, qd, wq, hkeys_hi, n_vis, nq, topk,
-                                    keys, bkeys, topk_idx, stream);
+                                    keys, bkeys, topk_idx, stream, pool_blocks,
+                                    pool_blocks > 0 ? pool_idx : nullptr);
         return hip_status(e);
     }
 

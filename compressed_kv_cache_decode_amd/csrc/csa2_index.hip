@@ -920,6 +920,69 @@ constexpr int kChunkSlots = kChunkMaxCand * kHalf;     // 12288 keys
 static_assert(kChunkSlots <= kSelRegSlots, "the candidates' keys fit the register path");
 static_assert(kChunkMaxCand <= kMaxPoolBlocks, "the candidate list fits sh.pool");
 
+// Ordered compaction: this thread's first rank among the items the threads
+// before it hold (`cnt` of its own) and, in `total`, the workgroup's count.
+// part: kSelWaves words of LDS (earlier readers are waited for).
+__device__ __forceinline__ uint32_t rank_of_count(uint32_t cnt, uint32_t* part, uint32_t& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t excl = wave_excl_scan(cnt);
+    __syncthreads();
+    if (lane == 63) part[wave] = excl + cnt;
+    __syncthreads();
+    uint32_t before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+        before += w < wave ? part[w] : 0u;
+        total += part[w];
+    }
+    return before + excl;
+}
+
+// Exact keys of the n_c candidate half-blocks listed (ascending) in `list`,
+// scored with k_scan's arithmetic into ck, then their top K into out (ties to
+// the lowest position, since the slots ascend).  Two slots per thread in
+// flight; consecutive threads take the 4 positions of a half-block.
+__device__ __forceinline__ void topk_of_halves(const uint8_t* __restrict__ ikc,
+                                               const float* __restrict__ iks, int64_t row0,
+                                               const float* qrow, const float* wrow, int nv,
+                                               uint32_t n_c, const int32_t* list, uint32_t* ck,
+                                               int K, int32_t* out, SelRegShared& rs) {
+    const int tid = threadIdx.x;
+    const int n_slots = (int)n_c * kHalf;
+    for (int s0 = 0; s0 < n_slots; s0 += 2 * kSelThreads) {
+        uint4 raw[2][4];
+        float sg[2] = {0.0f, 0.0f};
+        bool vis[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int s = s0 + u * kSelThreads + tid;
+            const int64_t pos = s < n_slots ? (int64_t)list[s >> 2] * kHalf + (s & 3) : nv;
+            vis[u] = pos < nv;
+            if (vis[u]) {
+                load_ik_row(ikc, row0 + pos, raw[u]);
+                sg[u] = iks[row0 + pos];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int s = s0 + u * kSelThreads + tid;
+            if (s < n_slots) ck[s] = vis[u] ? score_key(score_row(raw[u], sg[u], qrow, wrow)) : 0u;
+        }
+    }
+    __syncthreads();
+    // register path: 16 consecutive slots a lane
+    uint32_t k[kSelKpt];
+#pragma unroll
+    for (int i = 0; i < kSelKpt; ++i) {
+        const int s = 16 * tid + i;
+        k[i] = s < n_slots ? ck[s] : 0u;
+    }
+    const Threshold tk = threshold_reg(k, K, rs);
+    compact_reg(k, tk, K, [&](int64_t s) { return list[s >> 2] * kHalf + (int32_t)(s & 3); }, out,
+                nullptr, rs);
+}
+
 __global__ __launch_bounds__(kSelThreads) void k_chunk_select(
     const uint8_t* __restrict__ ikc, const float* __restrict__ iks, int64_t cap, int Q,
     const float* __restrict__ qd, const float* __restrict__ wq,
@@ -976,18 +1039,8 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select(
         uint32_t mask = 0;
 #pragma unroll
         for (int i = 0; i < kSelKpt; ++i) mask |= h[i] >= x ? (1u << i) : 0u;
-        const uint32_t cnt = __popc(mask);
-        const uint32_t excl = wave_excl_scan(cnt);
-        __syncthreads();  // earlier readers of part are done
-        if (lane == 63) part[wave] = excl + cnt;
-        __syncthreads();
-        uint32_t before = n_c, total = 0;
-#pragma unroll
-        for (int w = 0; w < kSelWaves; ++w) {
-            before += w < wave ? part[w] : 0u;
-            total += part[w];
-        }
-        uint32_t r = before + excl;
+        uint32_t total;
+        uint32_t r = n_c + rank_of_count(__popc(mask), part, total);
         for (uint32_t mm = mask; mm != 0; mm &= mm - 1u, ++r)
             if (r < (uint32_t)Pc) sh.pool[r] = (int32_t)(first + __builtin_ctz(mm));
         n_c += total;  // uniform
@@ -1002,41 +1055,175 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select(
     }
     __syncthreads();  // the candidate list is complete
 
-    // 3. exact keys of the candidates' positions, two slots per thread in
-    // flight (consecutive threads take the 4 positions of a half-block)
-    const int n_slots = (int)n_c * kHalf;
-    for (int s0 = 0; s0 < n_slots; s0 += 2 * kSelThreads) {
-        uint4 raw[2][4];
-        float sg[2] = {0.0f, 0.0f};
-        bool vis[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int s = s0 + u * kSelThreads + tid;
-            const int64_t pos = s < n_slots ? (int64_t)sh.pool[s >> 2] * kHalf + (s & 3) : nv;
-            vis[u] = pos < nv;
-            if (vis[u]) {
-                load_ik_row(ikc, row0 + pos, raw[u]);
-                sg[u] = iks[row0 + pos];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int s = s0 + u * kSelThreads + tid;
-            if (s < n_slots) ck[s] = vis[u] ? score_key(score_row(raw[u], sg[u], qrow, wrow)) : 0u;
-        }
-    }
-    __syncthreads();
+    // 3-4. exact keys of the candidates' positions, and their top-K
+    topk_of_halves(ikc, iks, row0, qrow, wrow, nv, n_c, sh.pool, ck, K, topk_out + bq * K, rs);
+}
 
-    // 4. top-K of the candidates (register path: 16 consecutive slots a lane)
-    uint32_t k[kSelKpt];
+// Full layer with a pool of P blocks, for one query of the multi-query MFMA
+// scan (one workgroup per query, at most 16384 blocks: each thread holds the
+// bound keys of 16 consecutive blocks in registers).  lo and hi are the
+// scan's bound keys; a block's upper bound ub is the larger hi of its halves.
+//   1. x = the P-th largest lo: as for positions, every block the exact pool
+//      can take (ties included) has ub >= x;
+//   2. y = the (P+1)-th largest ub: a block with lo > y is in the pool, since
+//      only blocks with ub > y (at most P, itself among them) can rank above
+//      it; with at most P visible blocks, all of them are;
+//   3. the other blocks with ub >= x are undecided (a few near the cut).  When
+//      more of them remain than the pool has room for, their positions are
+//      scored exactly and the best of them by exact block key (the maximum
+//      over its positions), ties to the lowest block, fill the pool;
+//   4. the pool is written in ascending block order.  x' = the K-th largest
+//      lo among its blocks bounds the K-th largest exact score inside it, so
+//      the top-K lies in the pool's half-blocks whose hi reaches x'; those are
+//      scored exactly and the top-K taken as in k_chunk_select.
+// When a list overflows (heavy ties) the query is scored over all its
+// visible positions instead and takes the Full selection.
+constexpr int kPoolUndecided = 1024;  // undecided blocks held in LDS
+static_assert(kMaxPoolBlocks >= kChunkMaxCand, "sh.pool holds either list");
+
+__global__ __launch_bounds__(kSelThreads) void k_chunk_select_pool(
+    const uint8_t* __restrict__ ikc, const float* __restrict__ iks, int64_t cap, int Q,
+    const float* __restrict__ qd, const float* __restrict__ wq,
+    const uint32_t* __restrict__ hkeys_hi, const int32_t* __restrict__ n_vis, int P, int K, int Pc,
+    uint32_t* __restrict__ keys, uint32_t* __restrict__ bkeys, int32_t* __restrict__ pool_out,
+    int32_t* __restrict__ topk_out) {
+    __shared__ SelShared sh;
+    __shared__ uint32_t ck[kChunkSlots];
+    __shared__ uint32_t part[kSelWaves];
+    __shared__ int32_t ulist[kPoolUndecided];
+    __shared__ uint32_t ukey[kPoolUndecided];
+    __shared__ uint32_t taken[kSelRegSlots / 32];  // undecided blocks the pool takes
+    const int tid = threadIdx.x;
+    const int64_t bq = blockIdx.x;
+    const int64_t row0 = (bq / Q) * cap;
+    const int nv = clamp_nvis(n_vis[bq], cap);
+    const int64_t nb = cap / kBlock, nbv = ((int64_t)nv + kBlock - 1) / kBlock;
+    const int64_t nhv = ((int64_t)nv + kHalf - 1) / kHalf;
+    const KeySrc lo_src{bkeys + bq * nb, nullptr, nbv, nv, 0};  // the scan's lower bounds
+    const KeySrc hi_src{hkeys_hi + bq * (cap / kHalf), nullptr, nhv, nv, 0};
+    const float* qrow = qd + bq * kIdxHeads * kIdxDim;
+    const float* wrow = wq + bq * kIdxHeads;
+    SelRegShared& rs = *reinterpret_cast<SelRegShared*>(&sh.hist[0]);
+    const int32_t b0 = tid * kSelKpt;  // this thread's first block
+
+    for (int i = tid; i < kSelRegSlots / 32; i += kSelThreads) taken[i] = 0u;
+    uint32_t lo[kSelKpt], ub[kSelKpt];
+    lo_src.load16(b0, lo);  // 0 where no position is visible
+    {
+        uint32_t h[kSelKpt];
+        hi_src.load16(2 * b0, h);
+#pragma unroll
+        for (int i = 0; i < kSelKpt / 2; ++i) ub[i] = max(h[2 * i], h[2 * i + 1]);
+        hi_src.load16(2 * b0 + kSelKpt, h);
+#pragma unroll
+        for (int i = 0; i < kSelKpt / 2; ++i) ub[kSelKpt / 2 + i] = max(h[2 * i], h[2 * i + 1]);
+    }
+
+    // 1-2. x and y
+    const Threshold tx = threshold_reg(lo, P, rs);
+    const uint32_t x = kth_key_reg(lo, tx, P, part);
+    const Threshold ty = threshold_reg(ub, P + 1, rs);
+    const uint32_t y = kth_key_reg(ub, ty, P + 1, part);
+    const bool all_in = ty.total <= (uint32_t)P;
+    uint32_t sure = 0, und = 0;
 #pragma unroll
     for (int i = 0; i < kSelKpt; ++i) {
-        const int s = 16 * tid + i;
-        k[i] = s < n_slots ? ck[s] : 0u;
+        if (lo[i] != 0 && (all_in || lo[i] > y)) sure |= 1u << i;
+        else if (lo[i] != 0 && ub[i] >= x) und |= 1u << i;
     }
-    const Threshold tk = threshold_reg(k, K, rs);
-    compact_reg(k, tk, K, [&](int64_t s) { return sh.pool[s >> 2] * kHalf + (int32_t)(s & 3); },
-                topk_out + bq * K, nullptr, rs);
+    // both counts at once: sure in the high half-word (each total <= 16384)
+    uint32_t tot;
+    const uint32_t rk = rank_of_count(__popc(und) | (__popc(sure) << 16), part, tot);
+    const uint32_t n_und = tot & 0xFFFFu, n_sure = tot >> 16;
+    const uint32_t need = (uint32_t)P - n_sure;  // n_sure <= P
+
+    auto fallback = [&]() {
+        scan_query_exact(ikc, iks, row0, qrow, wrow, nv, kSelThreads, keys + bq * cap,
+                         bkeys + bq * nb);
+        __syncthreads();  // the keys are the workgroup's own global writes
+        select_full_query(keys, bkeys, cap, bq, nv, P, K, pool_out, topk_out, sh);
+    };
+
+    // 3. the undecided blocks, when the pool cannot take them all
+    uint32_t in_pool = sure | und;
+    if (n_und > need) {  // uniform
+        if (n_und > (uint32_t)kPoolUndecided) {
+            fallback();
+            return;
+        }
+        uint32_t r = rk & 0xFFFFu;
+        for (uint32_t mm = und; mm != 0; mm &= mm - 1u, ++r) ulist[r] = b0 + __builtin_ctz(mm);
+        __syncthreads();
+        // exact block keys: a block's 8 positions on 8 consecutive lanes (the
+        // trip count is uniform, so every lane takes part in the group max)
+        const int n_pos = (int)n_und * kBlock;
+        for (int s0 = 0; s0 < n_pos; s0 += kSelThreads) {
+            const int s = s0 + tid;
+            const int64_t pos = s < n_pos ? (int64_t)ulist[s >> 3] * kBlock + (s & 7) : nv;
+            uint32_t key = 0u;
+            if (pos < nv) {
+                uint4 raw[4];
+                load_ik_row(ikc, row0 + pos, raw);
+                key = score_key(score_row(raw, iks[row0 + pos], qrow, wrow));
+            }
+            key = max8_u32(key);
+            if (s < n_pos && (s & 7) == 0) ukey[s >> 3] = key;
+        }
+        __syncthreads();
+        uint32_t k[kSelKpt];
+#pragma unroll
+        for (int i = 0; i < kSelKpt; ++i) {
+            const int s = 16 * tid + i;
+            k[i] = s < (int)n_und ? ukey[s] : 0u;
+        }
+        const Threshold tu = threshold_reg(k, (int)need, rs);
+        compact_reg(k, tu, (int)need, [&](int64_t s) { return ulist[s]; }, nullptr, sh.pool, rs);
+        __syncthreads();
+        for (int j = tid; j < (int)need; j += kSelThreads) {
+            const int32_t blk = sh.pool[j];
+            if (blk >= 0) atomicOr(&taken[blk >> 5], 1u << (blk & 31));
+        }
+        __syncthreads();
+        in_pool = sure | ((taken[tid >> 1] >> (16 * (tid & 1))) & 0xFFFFu);
+    }
+
+    // 4. the pool, ascending
+    uint32_t n_pool;
+    {
+        uint32_t r = rank_of_count(__popc(in_pool), part, n_pool);
+        int32_t* prow = pool_out + bq * P;
+        for (uint32_t mm = in_pool; mm != 0; mm &= mm - 1u, ++r)
+            if (r < (uint32_t)P) prow[r] = b0 + __builtin_ctz(mm);  // n_pool <= P
+        for (int i = (int)n_pool + tid; i < P; i += kSelThreads) prow[i] = -1;
+    }
+    uint32_t kp[kSelKpt];
+#pragma unroll
+    for (int i = 0; i < kSelKpt; ++i) kp[i] = (in_pool >> i) & 1u ? lo[i] : 0u;
+    const Threshold tk = threshold_reg(kp, K, rs);
+    const uint32_t xk = kth_key_reg(kp, tk, K, part);
+    // candidate half-blocks of the pool: half 2 b0 + j of this thread
+    uint32_t cmask = 0;
+    {
+        uint32_t h[kSelKpt];
+        hi_src.load16(2 * b0, h);
+#pragma unroll
+        for (int j = 0; j < kSelKpt; ++j)
+            cmask |= ((in_pool >> (j >> 1)) & 1u) && h[j] >= xk ? (1u << j) : 0u;
+        hi_src.load16(2 * b0 + kSelKpt, h);
+#pragma unroll
+        for (int j = 0; j < kSelKpt; ++j)
+            cmask |= ((in_pool >> (8 + (j >> 1))) & 1u) && h[j] >= xk ? (1u << (16 + j)) : 0u;
+    }
+    uint32_t n_c;
+    uint32_t r = rank_of_count(__popc(cmask), part, n_c);
+    if (n_c > (uint32_t)Pc) {  // uniform
+        fallback();
+        return;
+    }
+    for (uint32_t mm = cmask; mm != 0; mm &= mm - 1u, ++r)
+        sh.pool[r] = 2 * b0 + __builtin_ctz(mm);
+    __syncthreads();  // the candidate list is complete
+    topk_of_halves(ikc, iks, row0, qrow, wrow, nv, n_c, sh.pool, ck, K, topk_out + bq * K, rs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1091,9 +1278,18 @@ hipError_t launch_select_pool(const uint32_t* ckeys, const int32_t* pool, int P,
 hipError_t launch_chunk_select(const uint8_t* ikc, const float* iks, int64_t cap, int Q,
                                const float* qd, const float* wq, const uint32_t* hkeys_hi,
                                const int32_t* n_vis, int64_t n_queries, int K, uint32_t* keys,
-                               uint32_t* bkeys, int32_t* topk_out, hipStream_t stream) {
+                               uint32_t* bkeys, int32_t* topk_out, hipStream_t stream, int P,
+                               int32_t* pool_out) {
     const int Pc = chunk_cand_halves(K);
     if (Pc > kChunkMaxCand) return hipErrorInvalidValue;
+    if (P > 0) {
+        if (cap / kBlock > kSelRegSlots || P > kMaxPoolBlocks || pool_out == nullptr)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL(k_chunk_select_pool, dim3((unsigned)n_queries), dim3(kSelThreads), 0,
+                           stream, ikc, iks, cap, Q, qd, wq, hkeys_hi, n_vis, P, K, Pc, keys,
+                           bkeys, pool_out, topk_out);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_chunk_select, dim3((unsigned)n_queries), dim3(kSelThreads), 0, stream,
                        ikc, iks, cap, Q, qd, wq, hkeys_hi, n_vis, K, Pc, keys, bkeys, topk_out);
     return hipGetLastError();

@@ -65,11 +65,16 @@ hipError_t launch_scan_mma(const uint8_t* ikc, const float* iks, int64_t cap, in
 // top-K of each query of the MFMA scan from its bounds (csa2_index.hip):
 // candidate half-blocks, their exact keys and the selection in one workgroup
 // per query; keys / bkeys: scratch rows of the exact fallback (bkeys holds the
-// scan's lower bounds on entry)
+// scan's lower bounds on entry).  P > 0: the pool of P blocks first (into
+// pool_out), then the top-K inside it; needs cap / 8 <= kChunkPoolMaxBlocks.
 hipError_t launch_chunk_select(const uint8_t* ikc, const float* iks, int64_t cap, int Q,
                                const float* qd, const float* wq, const uint32_t* hkeys_hi,
                                const int32_t* n_vis, int64_t n_queries, int K, uint32_t* keys,
-                               uint32_t* bkeys, int32_t* topk_out, hipStream_t stream);
+                               uint32_t* bkeys, int32_t* topk_out, hipStream_t stream, int P = 0,
+                               int32_t* pool_out = nullptr);
+// blocks per sequence up to which the MFMA path also selects pools (their
+// bound keys are held in registers, 16 per thread of a 1024-thread workgroup)
+constexpr int64_t kChunkPoolMaxBlocks = 16384;
 // candidate half-blocks per chunk query before the exact fallback: 3 K, at
 // least 512
 inline int chunk_cand_halves(int K) { return 3 * K < 512 ? 512 : 3 * K; }

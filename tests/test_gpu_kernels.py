@@ -195,6 +195,17 @@ def make_idx_cache(gpu, oracle_mod, B, cap, seed, dup_frac=0.0):
     (1, 1, 65536, [65533], 2048, 4096),
     # more than 16384 blocks: the block selection streams too
     (1, 1, 262144, [262141], 512, 2048),
+    # multi-query Full layers with a pool on the MFMA path (at most 16384
+    # blocks): pools larger than the visible blocks, queries seeing nothing,
+    # ragged tails, the full 16384 blocks, the largest pool and top-K, and a
+    # small pool (P + 1 = 129 upper bounds) under duplicated keys
+    (2, 16, 16384, [[0, 1, 5, 300, 511, 512, 513, 4096, 8191, 8192, 12000, 16383, 16384,
+                     16384, 7, 9000], [16384 - 1000 * i for i in range(16)]], 512, 2048),
+    (1, 8, 131072, [[131072, 131000, 100001, 65536, 20000, 16385, 2048, 9]], 512, 2048),
+    (1, 5, 65536, [[65536, 65000, 40000, 20000, 9]], 1024, 4096),
+    (1, 6, 8192, [[8192, 8191, 4000, 1030, 1024, 1017]], 64, 128),
+    # more than 16384 blocks with a pool: the exact multi-query scan
+    (1, 4, 262144, [[262144, 200000, 131080, 5]], 512, 2048),
 ])
 def test_index_full_bit_exact(gpu, oracle_mod, B, Q, cap, nvis, topk, pool):
     say(f"index_full B={B} Q={Q} cap={cap} topk={topk} pool={pool}")
@@ -235,6 +246,33 @@ def test_index_full_chunk_candidate_overflow(gpu, oracle_mod):
     tk = torch.full((B, Q, 512), -7, dtype=torch.int32, device="cuda")
     gpu.index_full(cache, dev(iq), dev(iw), dev(nv), tk, None, topk=512, pool_blocks=0)
     np.testing.assert_array_equal(host(tk), tk_ref)
+
+
+def test_index_full_chunk_pool_overflow(gpu, oracle_mod):
+    """All scores equal, with a pool: no block is decided by the bounds and
+    all the visible ones stay undecided, more than the MFMA path's list holds,
+    so each query is rescored exactly and takes the Full selection (pool of
+    the lowest blocks, then the lowest positions).  A query with 1013 visible
+    blocks fits the list: they are scored exactly and the tie rule takes the
+    lowest 1000; one with fewer visible blocks than the pool takes them all."""
+    say("index_full multi-query with a pool, all-equal scores")
+    B, Q, cap = 1, 6, 16384
+    x = np.tile(np.random.default_rng(19).standard_normal((1, 1, 64)), (B, cap, 1)).astype(np.float32)
+    ikc, iks = oracle_mod.quant_fp8_rows(x)
+    cache = gpu.Cache(B, cap)
+    cache.ik_codes.copy_(dev(tile_ik(ikc)))
+    cache.ik_sigma.copy_(dev(iks.reshape(-1)))
+    g = np.random.default_rng(20)
+    iq = g.standard_normal((B, Q, 4, 64)).astype(np.float32)
+    iw = g.random((B, Q, 4)).astype(np.float32)
+    nv = np.array([[16384, 16001, 9003, 8200, 8100, 100]], np.int32)
+    tk_ref, pl_ref = oracle_mod.index_full_batch(ikc.reshape(B, cap, 64), iks.reshape(B, cap), iq,
+                                                 iw, nv, 512, 1000)
+    tk = torch.full((B, Q, 512), -7, dtype=torch.int32, device="cuda")
+    pl = torch.full((B, Q, 1000), -7, dtype=torch.int32, device="cuda")
+    gpu.index_full(cache, dev(iq), dev(iw), dev(nv), tk, pl, topk=512, pool_blocks=1000)
+    np.testing.assert_array_equal(host(tk), tk_ref)
+    np.testing.assert_array_equal(host(pl), pl_ref)
 
 
 def test_index_full_all_ties(gpu, oracle_mod):
