@@ -90,14 +90,13 @@ class StepSet:
         self.csa2 = csa2
 
     def run(self, scan_timer=None, attn_timer=None):
-        c, i = self.csa2, self.inp
-        # write path of the new token of every sequence (position n_ent - 1):
-        # its FP4 record and its FP8 indexer key, in one launch
-        c.write_entries(i["k_new"], i["v_new"], self.cache.kv_codes, self.cache.kv_scales,
-                        ratio=self.ratio, rope_cs=i["rope_new"], dst_rows=i["rows_new"],
-                        fp8_jobs=[dict(x=i["idx_new"], codes=self.cache.ik_codes,
-                                       sigma=self.cache.ik_sigma, layout=c.FP8_IDX_TILED,
-                                       dst_rows=i["rows_new"])])
+        i = self.inp
+        # write path of the new token of every sequence (position n_ent - 1),
+        # in one launch: its FP4 record, its indexer key projected on the
+        # device from its K, and every layer's window token at its ring slot
+        self.stack.write(i["k_new"], i["v_new"], i["rows_new"], i["proj"], i["win_k"],
+                         i["win_v"], i["win_rows"], i["swk"], i["swv"], i["sks"], i["svs"],
+                         ratio=self.ratio, rope_cs=i.get("rope_new"))
         self.stack.step(i["iq"], i["iw"], i["n_vis"], i["q"], i["swk"], i["swv"], i["sks"],
                         i["svs"], i["swa_len"], scan_timer=scan_timer, attn_timer=attn_timer)
 
@@ -132,6 +131,7 @@ def build_sets(args, wl, inp):
     csa2.quant_fp8(torch.from_numpy(inp.swa_v.reshape(-1, 128)).cuda(), swv, svs)
     last = N - 1
     tok = last * wl.ratio  # the new token (pair) of every sequence
+    slot = (tok + wl.ratio - 1) % 128  # window ring slot of the newest token
     if wl.ratio == 1:
         k_new, v_new = inp.k_tok[:, last], inp.v_tok[:, last]
     else:  # the newest pair is re-averaged by the write path
@@ -140,7 +140,12 @@ def build_sets(args, wl, inp):
     dev_inputs = {
         "k_new": torch.from_numpy(np.ascontiguousarray(k_new)).cuda(),
         "v_new": torch.from_numpy(np.ascontiguousarray(v_new)).cuda(),
-        "idx_new": torch.from_numpy(np.ascontiguousarray(inp.idx_k[:, last])).cuda(),
+        "proj": torch.from_numpy(inp.proj).cuda(),
+        # the newest token's window row of every layer, at its ring slot
+        "win_k": torch.from_numpy(np.ascontiguousarray(inp.swa_k[:, :, slot].reshape(-1, 128))).cuda(),
+        "win_v": torch.from_numpy(np.ascontiguousarray(inp.swa_v[:, :, slot].reshape(-1, 128))).cuda(),
+        "win_rows": torch.from_numpy(((np.arange(L)[:, None] * B + np.arange(B)[None, :]) * 128
+                                      + slot).reshape(-1).astype(np.int64)).cuda(),
         "rope_new": (torch.from_numpy(csa2.rope_table(np.full(B, last))).cuda()
                      if wl.ratio == 1 else None),
         "rows_new": torch.arange(B, dtype=torch.int64, device="cuda") * cap + last,
@@ -236,7 +241,7 @@ def run_chunk_bench(args, wl):
         "k_new": torch.from_numpy(np.ascontiguousarray(inp.k_tok[0, N - Q:])).cuda(),
         "v_new": torch.from_numpy(np.ascontiguousarray(inp.v_tok[0, N - Q:])).cuda(),
         "rope_new": torch.from_numpy(csa2.rope_table(pos_new)).cuda(),
-        "idx_new": torch.from_numpy(np.ascontiguousarray(inp.idx_k[0, N - Q:])).cuda(),
+        "proj": torch.from_numpy(inp.proj).cuda(),
         "swa_k": torch.from_numpy(inp.swa_k.reshape(-1, 128)).cuda(),
         "swa_v": torch.from_numpy(inp.swa_v.reshape(-1, 128)).cuda(),
         "iq": torch.from_numpy(inp.iq).cuda(), "iw": torch.from_numpy(inp.iw).cuda(),
@@ -270,14 +275,12 @@ def run_chunk_bench(args, wl):
     d = dev_in
 
     def step(cache, scan_timer=None):
-        # the chunk's 128 entries (RoPE + FP4), their indexer keys and the
-        # window's K and V, in one launch
+        # the chunk's 128 entries (RoPE + FP4), their indexer keys projected
+        # on the device from their K, and the window's K and V, in one launch
         csa2.write_entries(d["k_new"], d["v_new"], cache.kv_codes, cache.kv_scales,
-                           rope_cs=d["rope_new"], dst_rows=rows_new,
-                           fp8_jobs=[dict(x=d["idx_new"], codes=cache.ik_codes,
-                                          sigma=cache.ik_sigma, layout=csa2.FP8_IDX_TILED,
-                                          dst_rows=rows_new),
-                                     dict(x=d["swa_k"], codes=swk, sigma=sks),
+                           rope_cs=d["rope_new"], dst_rows=rows_new, idx_proj=d["proj"],
+                           ik_codes=cache.ik_codes, ik_sigma=cache.ik_sigma,
+                           fp8_jobs=[dict(x=d["swa_k"], codes=swk, sigma=sks),
                                      dict(x=d["swa_v"], codes=swv, sigma=svs)])
         csa2.index_full(cache, d["iq"], d["iw"], d["n_vis"], tk, None, topk=wl.topk,
                         pool_blocks=0, ws=ws, scan_timer=scan_timer)
@@ -371,7 +374,7 @@ def run_chunk_stack_bench(args, wl):
         "k_new": torch.from_numpy(np.ascontiguousarray(inp.k_tok[0, N - Q:])).cuda(),
         "v_new": torch.from_numpy(np.ascontiguousarray(inp.v_tok[0, N - Q:])).cuda(),
         "rope_new": torch.from_numpy(csa2.rope_table(inp.positions)).cuda(),
-        "idx_new": torch.from_numpy(np.ascontiguousarray(inp.idx_k[0, N - Q:])).cuda(),
+        "proj": torch.from_numpy(inp.proj).cuda(),
         "swa_k": torch.from_numpy(inp.swa_k.reshape(-1, 128)).cuda(),
         "swa_v": torch.from_numpy(inp.swa_v.reshape(-1, 128)).cuda(),
         "iq": torch.from_numpy(inp.iq).cuda(), "iw": torch.from_numpy(inp.iw).cuda(),
@@ -389,11 +392,9 @@ def run_chunk_stack_bench(args, wl):
     def step(i, scan_timer=None):
         cache, st = caches[i], stacks[i]
         csa2.write_entries(d["k_new"], d["v_new"], cache.kv_codes, cache.kv_scales,
-                           rope_cs=d["rope_new"], dst_rows=rows_new,
-                           fp8_jobs=[dict(x=d["idx_new"], codes=cache.ik_codes,
-                                          sigma=cache.ik_sigma, layout=csa2.FP8_IDX_TILED,
-                                          dst_rows=rows_new),
-                                     dict(x=d["swa_k"], codes=swk, sigma=sks),
+                           rope_cs=d["rope_new"], dst_rows=rows_new, idx_proj=d["proj"],
+                           ik_codes=cache.ik_codes, ik_sigma=cache.ik_sigma,
+                           fp8_jobs=[dict(x=d["swa_k"], codes=swk, sigma=sks),
                                      dict(x=d["swa_v"], codes=swv, sigma=svs)])
         st.step(d["iq"], d["iw"], d["n_vis"], d["q"], swk, swv, sks, svs, scan_timer=scan_timer)
 
@@ -481,8 +482,21 @@ def cpu_baseline(args, wl, inp):
     swv, svs = oracle.quant_fp8_rows(inp.swa_v[:, :S])
     nv = np.full((S, 1), N, np.int32)
     sm = 1.0 / math.sqrt(128.0)
+    r = wl.ratio
+    tok = (N - 1) * r
+    slot = (tok + r - 1) % 128
+    cs_new = oracle.rope_table(np.array([N - 1])) if r == 1 else None
     log("cpu baseline: timing one stack step of the sample")
     t0 = time.perf_counter()
+    # write path: each sequence's new entry (FP4 record, projected indexer
+    # key) and every layer's window token at its ring slot
+    for b in range(S):
+        c1, s1, ik1, is1 = oracle.write_entries_proj(inp.k_tok[b, tok:tok + r],
+                                                     inp.v_tok[b, tok:tok + r], inp.proj, r,
+                                                     cs_new)
+        codes[b, N - 1], scales[b, N - 1], ikc[b, N - 1], iks[b, N - 1] = c1[0], s1[0], ik1[0], is1[0]
+    swk[:, :, slot], sks[:, :, slot] = oracle.quant_fp8_rows(inp.swa_k[:, :S, slot])
+    swv[:, :, slot], svs[:, :, slot] = oracle.quant_fp8_rows(inp.swa_v[:, :S, slot])
     pool, cur, k = None, None, 0
     for layer, mode in enumerate(wl.plan):
         if mode == "F":

@@ -43,7 +43,8 @@ STAGE_READ = 2
 STATUS = {0: "ok", -1: "CSA2_E_ARG", -2: "CSA2_E_UNSUPPORTED", -3: "CSA2_E_WORKSPACE",
           -4: "CSA2_E_HIP"}
 
-EXPORTS = ("csa2_quant_fp4", "csa2_quant_fp8", "csa2_write_entries", "csa2_index_full",
+EXPORTS = ("csa2_quant_fp4", "csa2_quant_fp8", "csa2_write_entries", "csa2_write_entries_proj",
+           "csa2_index_full",
            "csa2_index_full_timed",
            "csa2_index_reindex",
            "csa2_sparse_attn_decode", "csa2_sparse_attn_decode_timed",
@@ -68,6 +69,8 @@ _SIGS = {
     "csa2_quant_fp4": (_int, [_vp, _vp, _i64, _int, _vp, _vp, _vp, _vp, _vp]),
     "csa2_write_entries": (_int, [_vp, _vp, _i64, _int, _vp, _vp, _vp, _vp,
                                   ctypes.POINTER(_Fp8Job), _int, _vp]),
+    "csa2_write_entries_proj": (_int, [_vp, _vp, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       ctypes.POINTER(_Fp8Job), _int, _vp]),
     "csa2_quant_fp8": (_int, [_vp, _i64, _int, _int, _vp, _vp, _vp, _vp]),
     "csa2_index_full": (_int, [_vp, _vp, _i64, _int, _int, _vp, _vp, _vp, _int, _int, _vp, _vp,
                                _vp, _sz, _vp]),
@@ -223,11 +226,14 @@ def quant_fp8(x, codes, sigma, layout=FP8_ROWS, dst_rows=None, stream=None):
 
 
 def write_entries(k_tok, v_tok, kv_codes, kv_scales, ratio=1, rope_cs=None, dst_rows=None,
-                  fp8_jobs=(), stream=None):
+                  fp8_jobs=(), stream=None, idx_proj=None, ik_codes=None, ik_sigma=None):
     """quant_fp4(k_tok, v_tok, ...) and quant_fp8 of each job in one launch.
 
     fp8_jobs: up to 3 dicts with the arguments of quant_fp8: x, codes, sigma,
-    and optionally layout (FP8_ROWS) and dst_rows."""
+    and optionally layout (FP8_ROWS) and dst_rows.
+    idx_proj [64][128] f32 (optional): also each entry's indexer key, projected
+    on the device from its fp32 K and written in FP8 to ik_codes (tile layout)
+    and ik_sigma at the entry's row (csa2_write_entries_proj)."""
     n_tok = k_tok.shape[0] if k_tok.dim() > 1 else 0
     if k_tok.shape != v_tok.shape or (k_tok.dim() != 2 or k_tok.shape[1] != HEAD_DIM):
         raise ValueError("k_tok, v_tok must be [n_tok][128]")
@@ -244,13 +250,20 @@ def write_entries(k_tok, v_tok, kv_codes, kv_scales, ratio=1, rope_cs=None, dst_
                           _ptr(jb.get("dst_rows"), torch.int64, "dst_rows", n),
                           _ptr(jb["codes"], torch.uint8, "codes"),
                           _ptr(jb["sigma"], torch.float32, "sigma"))
-    rc = lib().csa2_write_entries(
-        _ptr(k_tok, torch.float32, "k_tok"), _ptr(v_tok, torch.float32, "v_tok"), n_tok, ratio,
-        _ptr(rope_cs, torch.float32, "rope_cs", n_ent * 64),
-        _ptr(dst_rows, torch.int64, "dst_rows", n_ent),
-        _ptr(kv_codes, torch.uint8, "kv_codes"), _ptr(kv_scales, torch.uint8, "kv_scales"),
-        jobs, len(fp8_jobs), _stream(stream))
-    _check(rc, "csa2_write_entries")
+    head = (_ptr(k_tok, torch.float32, "k_tok"), _ptr(v_tok, torch.float32, "v_tok"), n_tok,
+            ratio, _ptr(rope_cs, torch.float32, "rope_cs", n_ent * 64),
+            _ptr(dst_rows, torch.int64, "dst_rows", n_ent),
+            _ptr(kv_codes, torch.uint8, "kv_codes"), _ptr(kv_scales, torch.uint8, "kv_scales"))
+    if idx_proj is None:
+        rc = lib().csa2_write_entries(*head, jobs, len(fp8_jobs), _stream(stream))
+        _check(rc, "csa2_write_entries")
+        return
+    if tuple(idx_proj.shape) != (IDX_DIM, HEAD_DIM):
+        raise ValueError("idx_proj must be [64][128]")
+    rc = lib().csa2_write_entries_proj(
+        *head, _ptr(idx_proj, torch.float32, "idx_proj"), _ptr(ik_codes, torch.uint8, "ik_codes"),
+        _ptr(ik_sigma, torch.float32, "ik_sigma"), jobs, len(fp8_jobs), _stream(stream))
+    _check(rc, "csa2_write_entries_proj")
 
 
 def index_full(cache, iq, iw, n_vis, topk_idx, pool_idx=None, topk=DEFAULT_TOPK,

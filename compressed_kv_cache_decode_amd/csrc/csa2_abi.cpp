@@ -231,6 +231,28 @@ __attribute__((visibility("default"))) int csa2_write_entries(
     return hip_status(launch_write_entries(f, j, stream));
 }
 
+__attribute__((visibility("default"))) int csa2_write_entries_proj(
+    const float* k_tok, const float* v_tok, int64_t n_tok, int ratio, const float* rope_cs,
+    const int64_t* dst_rows, uint8_t* kv_codes, uint8_t* kv_scales, const float* idx_proj,
+    uint8_t* ik_codes, float* ik_sigma, const csa2_fp8_job* jobs, int n_jobs,
+    hipStream_t stream) {
+    if (n_jobs < 0 || n_jobs > CSA2_MAX_FP8_JOBS || (n_jobs > 0 && !jobs)) return CSA2_E_ARG;
+    int rc = validate_quant_fp4(k_tok, v_tok, n_tok, ratio, rope_cs, kv_codes, kv_scales);
+    if (rc != CSA2_OK) return rc;
+    if (n_tok > 0 && (!idx_proj || !ik_codes || !ik_sigma)) return CSA2_E_ARG;
+    Fp8Jobs j{};
+    for (int i = 0; i < n_jobs; ++i) {
+        const csa2_fp8_job& b = jobs[i];
+        rc = validate_quant_fp8(b.x, b.n_rows, b.dim, b.layout, b.codes, b.sigma);
+        if (rc != CSA2_OK) return rc;
+        if (b.n_rows == 0) continue;
+        j.job[j.n++] = Fp8Job{b.x, b.n_rows, b.dim, b.layout, b.dst_rows, b.codes, b.sigma};
+    }
+    const Fp4Job f{k_tok,    v_tok,     n_tok / ratio, ratio,   rope_cs, dst_rows,
+                   kv_codes, kv_scales, idx_proj,      ik_codes, ik_sigma};
+    return hip_status(launch_write_entries(f, j, stream));
+}
+
 __attribute__((visibility("default"))) int csa2_index_full_timed(
     const uint8_t* ik_codes, const float* ik_sigma, int64_t cap, int B, int Q, const float* iq,
     const float* iw, const int32_t* n_vis, int topk, int pool_blocks, int32_t* topk_idx,

@@ -25,6 +25,11 @@ struct Fp4Job {
     const int64_t* dst_rows;
     uint8_t* codes;
     uint8_t* scales;
+    // optional: the entries' indexer keys projected on the device from their
+    // fp32 K, proj [64][128], written to ik_codes (tile layout) / ik_sigma
+    const float* proj = nullptr;
+    uint8_t* ik_codes = nullptr;
+    float* ik_sigma = nullptr;
 };
 struct Fp8Job {
     const float* x;

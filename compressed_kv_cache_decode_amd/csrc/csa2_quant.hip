@@ -17,12 +17,64 @@ namespace csa2 {
 
 // Entry e by one wave; lane l owns channels 2l and 2l+1 of K and of V, so a
 // 16-channel scale group is 8 adjacent lanes and one code byte per lane.
+// Indexer key of the entry being written, on the lane that owns output
+// channel j = lane: key_j = fp32 chain over input channels c = 0..127 of
+// proj[j][c] * x[c], one fused multiply-add per channel, from +0; x[c] is
+// read from lane c/2 (k0 for even c, k1 for odd c), wave-uniform.
+__device__ __forceinline__ float project_idx_key(const float* __restrict__ proj, float k0,
+                                                 float k1, int lane) {
+    const float4* wr = reinterpret_cast<const float4*>(proj + lane * kHeadDim);
+    float acc = 0.0f;
+#pragma unroll
+    for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
+        const float4 w = wr[c4];
+        const float x0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k0), 2 * c4));
+        const float x1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k1), 2 * c4));
+        const float x2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k0), 2 * c4 + 1));
+        const float x3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k1), 2 * c4 + 1));
+        acc = __builtin_fmaf(w.x, x0, acc);
+        acc = __builtin_fmaf(w.y, x1, acc);
+        acc = __builtin_fmaf(w.z, x2, acc);
+        acc = __builtin_fmaf(w.w, x3, acc);
+    }
+    return acc;
+}
+
+// FP8 row values already in registers (per = 1 or 2 channels per lane):
+// sigma = fl(amax / 448), code = RNE_E4M3(fl(x / sigma)).
+__device__ __forceinline__ void quant_fp8_vals(const float* xv, int per, int layout, int64_t row,
+                                               uint8_t* __restrict__ codes,
+                                               float* __restrict__ sigma, int lane) {
+    float amax = fabsf(xv[0]);
+    if (per == 2) amax = fmaxf(amax, fabsf(xv[1]));
+    amax = wave_max_f32(amax);
+    const float s = amax / 448.0f;
+    const int dim = per * 64;
+    for (int i = 0; i < per; ++i) {
+        const uint32_t c = (s == 0.0f) ? ((__float_as_uint(xv[i]) >> 24) & 0x80u)
+                                       : e4m3_encode(xv[i] / s);
+        const int ch = lane * per + i;
+        if (layout == 1) {
+            codes[ik_offset(row, ch >> 4) + (ch & 15)] = (uint8_t)c;
+        } else {
+            codes[row * dim + ch] = (uint8_t)c;
+        }
+    }
+    if (lane == 0) sigma[row] = s;
+}
+
+// proj (may be null): also the entry's indexer key, projected from its fp32 K
+// (after averaging and RoPE) and written in FP8 to ik_codes (tile layout) /
+// ik_sigma at the entry's row.
 __device__ __forceinline__ void quant_fp4_entry(const float* __restrict__ k,
                                                 const float* __restrict__ v, int64_t e, int ratio,
                                                 const float* __restrict__ rope_cs,
                                                 const int64_t* __restrict__ dst_rows,
                                                 uint8_t* __restrict__ codes,
-                                                uint8_t* __restrict__ scales, int lane) {
+                                                uint8_t* __restrict__ scales, int lane,
+                                                const float* __restrict__ proj = nullptr,
+                                                uint8_t* __restrict__ ik_codes = nullptr,
+                                                float* __restrict__ ik_sigma = nullptr) {
     float k0, k1, v0, v1;
     if (ratio == 1) {
         const float2 kk = reinterpret_cast<const float2*>(k + e * kHeadDim)[lane];
@@ -61,6 +113,10 @@ __device__ __forceinline__ void quant_fp4_entry(const float* __restrict__ k,
     const uint32_t vb = code(v0, vsd) | (code(v1, vsd) << 4);
 
     const int64_t row = dst_rows ? dst_rows[e] : e;
+    if (proj != nullptr) {
+        const float key[1] = {project_idx_key(proj, k0, k1, lane)};
+        quant_fp8_vals(key, 1, 1, row, ik_codes, ik_sigma, lane);
+    }
     codes[row * 128 + lane] = (uint8_t)kb;
     codes[row * 128 + 64 + lane] = (uint8_t)vb;
     if ((lane & 7) == 0) {
@@ -80,8 +136,7 @@ __global__ __launch_bounds__(256) void k_quant_fp4(const float* __restrict__ k,
     quant_fp4_entry(k, v, e, ratio, rope_cs, dst_rows, codes, scales, threadIdx.x & 63);
 }
 
-// Row r of 64 or 128 values by one wave; sigma = fl(amax / 448),
-// code = RNE_E4M3(fl(x / sigma)).
+// Row r of 64 or 128 values by one wave.
 __device__ __forceinline__ void quant_fp8_row(const float* __restrict__ x, int64_t r, int dim,
                                               int layout, const int64_t* __restrict__ dst_rows,
                                               uint8_t* __restrict__ codes,
@@ -89,22 +144,8 @@ __device__ __forceinline__ void quant_fp8_row(const float* __restrict__ x, int64
     const int per = dim / 64;  // channels per lane: 1 or 2
     float xv[2] = {0.0f, 0.0f};
     for (int i = 0; i < per; ++i) xv[i] = x[r * dim + lane * per + i];
-    float amax = fabsf(xv[0]);
-    if (per == 2) amax = fmaxf(amax, fabsf(xv[1]));
-    amax = wave_max_f32(amax);
-    const float s = amax / 448.0f;
     const int64_t row = dst_rows ? dst_rows[r] : r;
-    for (int i = 0; i < per; ++i) {
-        const uint32_t c = (s == 0.0f) ? ((__float_as_uint(xv[i]) >> 24) & 0x80u)
-                                       : e4m3_encode(xv[i] / s);
-        const int ch = lane * per + i;
-        if (layout == 1) {
-            codes[ik_offset(row, ch >> 4) + (ch & 15)] = (uint8_t)c;
-        } else {
-            codes[row * dim + ch] = (uint8_t)c;
-        }
-    }
-    if (lane == 0) sigma[row] = s;
+    quant_fp8_vals(xv, per, layout, row, codes, sigma, lane);
 }
 
 __global__ __launch_bounds__(256) void k_quant_fp8(const float* __restrict__ x, int64_t n_rows,
@@ -124,7 +165,8 @@ __global__ __launch_bounds__(256) void k_write_entries(Fp4Job f, Fp8Jobs j) {
     const int lane = threadIdx.x & 63;
     int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (w < f.n_ent) {
-        quant_fp4_entry(f.k, f.v, w, f.ratio, f.rope_cs, f.dst_rows, f.codes, f.scales, lane);
+        quant_fp4_entry(f.k, f.v, w, f.ratio, f.rope_cs, f.dst_rows, f.codes, f.scales, lane,
+                        f.proj, f.ik_codes, f.ik_sigma);
         return;
     }
     w -= f.n_ent;

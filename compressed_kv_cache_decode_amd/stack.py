@@ -28,7 +28,7 @@ import torch
 from . import (DEFAULT_POOL_BLOCKS, DEFAULT_TOPK, HEAD_DIM, OP_ATTN_CHUNK, OP_ATTN_DECODE,
                OP_ATTN_STAGE, OP_INDEX_FULL, OP_INDEX_REINDEX, STAGE_READ, STAGE_WRITE,
                alloc_workspace, index_full, index_reindex, sparse_attn_chunk, sparse_attn_decode,
-               sparse_attn_decode_reuse, workspace_size)
+               sparse_attn_decode_reuse, workspace_size, write_entries)
 
 
 def check_plan(plan, pool_blocks):
@@ -74,6 +74,25 @@ class DecodeStack:
         self.sources = reuse_sources(plan)
         self.stage = (alloc_workspace(workspace_size(OP_ATTN_STAGE, B, 1, cache.cap, topk, 0, H),
                                       dev) if stage and topk > 0 else None)
+
+    def write(self, k_new, v_new, rows_new, idx_proj, win_k, win_v, win_rows, swa_k, swa_v,
+              swa_ks, swa_vs, ratio=1, rope_cs=None, stream=None):
+        """Write path of one decode step, in one launch: the new entry of every
+        sequence (FP4 record and its indexer key, projected on the device from
+        the entry's K by idx_proj [64][128], at rows_new [B] of the shared
+        cache) and every layer's new window token (FP8 K and V rows win_k,
+        win_v [L*B][128] f32 at rows win_rows [L*B] of the stacked windows
+        [L][B][128][128]: slot t mod 128 of a 128-token ring for token t).
+        k_new, v_new: [B*ratio][128] f32 (the tokens of each new entry)."""
+        L = len(self.plan)
+        write_entries(k_new, v_new, self.cache.kv_codes, self.cache.kv_scales, ratio=ratio,
+                      rope_cs=rope_cs, dst_rows=rows_new, idx_proj=idx_proj,
+                      ik_codes=self.cache.ik_codes, ik_sigma=self.cache.ik_sigma,
+                      fp8_jobs=[dict(x=win_k, codes=swa_k.view(L * self.B * 128, HEAD_DIM),
+                                     sigma=swa_ks.view(-1), dst_rows=win_rows),
+                                dict(x=win_v, codes=swa_v.view(L * self.B * 128, HEAD_DIM),
+                                     sigma=swa_vs.view(-1), dst_rows=win_rows)],
+                      stream=stream)
 
     def step(self, iq, iw, n_vis, q, swa_k, swa_v, swa_ks, swa_vs, swa_len, stream=None,
              scan_timer=None, attn_timer=None):

@@ -143,6 +143,7 @@ class DecodeInputs:
     swa_v: np.ndarray      # [L][B][128][128]
     swa_len: np.ndarray    # [B] int32
     planted: list = None
+    proj: np.ndarray = None  # [64][128] the indexer-key projection, rounded to fp32
 
 
 def decode_inputs(wl, n_ent=None, B=None, layers=None, seed=None):
@@ -175,7 +176,8 @@ def decode_inputs(wl, n_ent=None, B=None, layers=None, seed=None):
     swa_k = normal(g, (L, B, WINDOW, HEAD_DIM))
     swa_v = normal(g, (L, B, WINDOW, HEAD_DIM))
     swa_len = np.full(B, WINDOW, np.int32)
-    return DecodeInputs(wl, k_tok, v_tok, idx_k, iq, iw, q, swa_k, swa_v, swa_len, planted)
+    return DecodeInputs(wl, k_tok, v_tok, idx_k, iq, iw, q, swa_k, swa_v, swa_len, planted,
+                        proj.astype(np.float32))
 
 
 @dataclass
@@ -191,6 +193,7 @@ class ChunkInputs:
     swa_k: np.ndarray      # [B][Q][128]   the chunk's own SWA tokens
     swa_v: np.ndarray      # [B][Q][128]
     positions: np.ndarray  # [Q] int64 absolute positions of the chunk tokens
+    proj: np.ndarray = None  # [64][128] the indexer-key projection, rounded to fp32
 
 
 def chunk_inputs(wl, n_ent=None, Q=None, H=None, seed=None):
@@ -208,7 +211,8 @@ def chunk_inputs(wl, n_ent=None, Q=None, H=None, seed=None):
     swa_k = normal(g, (B, Q, HEAD_DIM))
     swa_v = normal(g, (B, Q, HEAD_DIM))
     positions = np.arange(n_ent - Q, n_ent, dtype=np.int64)
-    return ChunkInputs(wl, k_tok, v_tok, idx_k, iq, iw, q, swa_k, swa_v, positions)
+    return ChunkInputs(wl, k_tok, v_tok, idx_k, iq, iw, q, swa_k, swa_v, positions,
+                       proj.astype(np.float32))
 
 
 @dataclass
@@ -228,6 +232,7 @@ class ChunkStackInputs:
     swa_k: np.ndarray      # [L][B][Q][128]
     swa_v: np.ndarray      # [L][B][Q][128]
     positions: np.ndarray  # [Q] int64
+    proj: np.ndarray = None  # [64][128] the indexer-key projection, rounded to fp32
 
 
 def chunk_stack_inputs(wl, n_ent=None, Q=None, H=None, B=None, layers=None, seed=None):
@@ -250,4 +255,5 @@ def chunk_stack_inputs(wl, n_ent=None, Q=None, H=None, B=None, layers=None, seed
     swa_k = normal(g, (L, B, Q, HEAD_DIM))
     swa_v = normal(g, (L, B, Q, HEAD_DIM))
     positions = np.arange(n_ent - Q, n_ent, dtype=np.int64)
-    return ChunkStackInputs(wl, plan, k_tok, v_tok, idx_k, iq, iw, q, swa_k, swa_v, positions)
+    return ChunkStackInputs(wl, plan, k_tok, v_tok, idx_k, iq, iw, q, swa_k, swa_v, positions,
+                            proj.astype(np.float32))

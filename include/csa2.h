@@ -175,6 +175,33 @@ int csa2_write_entries(const float* k_tok, const float* v_tok, int64_t n_tok, in
                        hipStream_t stream);
 
 /*
+ * csa2_write_entries_proj -- csa2_write_entries that also computes each new
+ * entry's indexer key on the device ("DeepSeek V4.1 Flash is live", "CSA2
+ * attention": the indexer key is projected from the main-KV entry instead of
+ * being compressed from hidden states on its own; "DeepSeek V4.1 Flash:
+ * architecture study notes" section 1: the global KV is the main KV plus the
+ * indexer key).
+ *   idx_proj   [64][128] fp32, row-major, device: the 128 -> 64 projection.
+ *   ik_codes, ik_sigma  indexer K arrays (tile layout, fp32 sigma): the key of
+ *              entry e is written at row dst_rows[e] (or e), as
+ *              csa2_quant_fp8(..., dim 64, CSA2_FP8_IDX_TILED) would write the
+ *              fp32 key vector.
+ * Key of an entry: x = the entry's fp32 K exactly as the FP4 part quantises
+ * it (after the 2:1 mean and RoPE, before quantisation);
+ * key[j] = fp32 sum over c = 0..127 in order of idx_proj[j][c] * x[c], each
+ * step one fused multiply-add (one rounding), starting from +0.
+ * The other arguments, the launch and the errors are those of
+ * csa2_write_entries; in addition CSA2_E_ARG when n_tok > 0 and idx_proj,
+ * ik_codes or ik_sigma is NULL.  The FP8 jobs must not write the rows the
+ * keys go to (not checked).  idx_proj is read during the launch only.
+ */
+int csa2_write_entries_proj(const float* k_tok, const float* v_tok, int64_t n_tok, int ratio,
+                            const float* rope_cs, const int64_t* dst_rows, uint8_t* kv_codes,
+                            uint8_t* kv_scales, const float* idx_proj, uint8_t* ik_codes,
+                            float* ik_sigma, const csa2_fp8_job* jobs, int n_jobs,
+                            hipStream_t stream);
+
+/*
  * csa2_index_full -- Full-layer indexer ("DeepSeek V4.1 Flash: architecture
  * study notes" section 2: Full picks this step's positions, at most 512 per
  * query; the decoder's first Full layer scans every causally visible position

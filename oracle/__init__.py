@@ -40,6 +40,9 @@ def lib():
             "csa2o_rope_apply": (None, [f32p, f32p]),
             "csa2o_fp4_quant_vec": (None, [f32p, u8p, u8p]),
             "csa2o_quant_fp4": (c_int, [f32p, f32p, c_i64, c_int, ctypes.c_void_p, u8p, u8p]),
+            "csa2o_entry_k": (c_int, [f32p, c_i64, c_int, ctypes.c_void_p, f32p]),
+            "csa2o_project_idx": (None, [f32p, f32p, f32p]),
+            "csa2o_project_idx_rows": (None, [f32p, c_i64, f32p, f32p]),
             "csa2o_fp8_quant_row": (None, [f32p, c_int, u8p, f32p]),
             "csa2o_quant_fp8_rows": (None, [f32p, c_i64, c_int, u8p, f32p]),
             "csa2o_quant_iq": (None, [f32p, f32p, u8p, f32p]),
@@ -146,6 +149,34 @@ def quant_fp8_rows(x):
     sigma = np.empty(x.shape[:-1], np.float32)
     lib().csa2o_quant_fp8_rows(x, n, dim, codes, sigma)
     return codes, sigma
+
+
+def entry_k(k, ratio=1, rope_cs=None):
+    """k [n_tok][128] fp32 -> the entries' fp32 K as the write path quantises
+    them (pair mean for ratio 2, RoPE when rope_cs is given) [n_ent][128]."""
+    k = _c(k, np.float32)
+    out = np.empty((k.shape[0] // ratio, 128), np.float32)
+    cs = None if rope_cs is None else _c(rope_cs, np.float32)
+    rc = lib().csa2o_entry_k(k, k.shape[0], ratio, None if cs is None else cs.ctypes.data, out)
+    if rc != 0:
+        raise ValueError("oracle entry_k rejected its arguments")
+    return out
+
+
+def project_idx(x, W):
+    """x [n][128] fp32, W [64][128] fp32 -> indexer keys [n][64] fp32."""
+    x, W = _c(x, np.float32), _c(W, np.float32)
+    keys = np.empty((x.shape[0], 64), np.float32)
+    lib().csa2o_project_idx_rows(x, x.shape[0], W, keys)
+    return keys
+
+
+def write_entries_proj(k, v, W, ratio=1, rope_cs=None):
+    """The write path with the indexer key projected from each entry's K:
+    (codes, scales, indexer codes [n_ent][64], indexer sigma [n_ent])."""
+    codes, scales = quant_fp4(k, v, ratio, rope_cs)
+    ikc, iks = quant_fp8_rows(project_idx(entry_k(k, ratio, rope_cs), W))
+    return codes, scales, ikc, iks
 
 
 # ---- indexer ------------------------------------------------------------

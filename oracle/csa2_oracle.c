@@ -206,6 +206,39 @@ int csa2o_quant_fp4(const float* k, const float* v, int64_t n_tok, int ratio,
     return 0;
 }
 
+int csa2o_entry_k(const float* k, int64_t n_tok, int ratio, const float* rope_cs, float* out) {
+    if (ratio != 1 && ratio != 2) return -1;
+    if (n_tok % ratio != 0) return -1;
+    if (ratio == 2 && rope_cs != NULL) return -1;
+    for (int64_t e = 0; e < n_tok / ratio; ++e) {
+        float* x = out + e * HEAD_DIM;
+        if (ratio == 2)
+            csa2o_average_pair(k + (2 * e) * HEAD_DIM, k + (2 * e + 1) * HEAD_DIM, HEAD_DIM, x);
+        else
+            memcpy(x, k + e * HEAD_DIM, HEAD_DIM * sizeof(float));
+        if (rope_cs != NULL) csa2o_rope_apply(x, rope_cs + e * 64);
+    }
+    return 0;
+}
+
+/* [digest] "CSA2 attention": the indexer key is projected from the main-KV
+ * entry, not compressed from hidden states separately.  Reading: a 128 -> 64
+ * linear map of the entry's fp32 K (after the pair mean / RoPE, before FP4
+ * quantisation), each output one fp32 accumulation over the input channels in
+ * ascending order, every step a fused multiply-add (C99 fmaf: one rounding),
+ * starting from +0. */
+void csa2o_project_idx(const float* x, const float* W, float* key) {
+    for (int j = 0; j < IDX_DIM; ++j) {
+        float acc = 0.0f;
+        for (int c = 0; c < HEAD_DIM; ++c) acc = fmaf(W[j * HEAD_DIM + c], x[c], acc);
+        key[j] = acc;
+    }
+}
+
+void csa2o_project_idx_rows(const float* x, int64_t n, const float* W, float* keys) {
+    for (int64_t i = 0; i < n; ++i) csa2o_project_idx(x + i * HEAD_DIM, W, keys + i * IDX_DIM);
+}
+
 /* SWA K/V and indexer K are FP8 ([notes] section 4, [digest] "cache
  * precision").  Reading: one fp32 scale per row, sigma = amax/448. */
 void csa2o_fp8_quant_row(const float* x, int dim, uint8_t* codes, float* sigma) {

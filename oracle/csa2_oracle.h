@@ -59,6 +59,14 @@ void csa2o_fp4_quant_vec(const float* x, uint8_t* codes, uint8_t* scales);
  * scales [n_ent][16] (K 8 | V 8). Returns 0 or -1 on bad arguments. */
 int  csa2o_quant_fp4(const float* k, const float* v, int64_t n_tok, int ratio,
                      const float* rope_cs, uint8_t* codes, uint8_t* scales);
+/* the fp32 K of each entry as the write path quantises it: pair mean
+ * (ratio 2) or the token itself, then RoPE when rope_cs is given; out
+ * [n_tok/ratio][128].  Returns 0 or -1 on bad arguments. */
+int  csa2o_entry_k(const float* k, int64_t n_tok, int ratio, const float* rope_cs, float* out);
+/* indexer key of one entry: key[j] = fused multiply-add chain over input
+ * channels 0..127 in order of W[j][c] * x[c], from +0; W [64][128] */
+void csa2o_project_idx(const float* x, const float* W, float* key);
+void csa2o_project_idx_rows(const float* x, int64_t n, const float* W, float* keys);
 /* one row of `dim` values -> E4M3 codes and fp32 sigma */
 void csa2o_fp8_quant_row(const float* x, int dim, uint8_t* codes, float* sigma);
 void csa2o_quant_fp8_rows(const float* x, int64_t n_rows, int dim,

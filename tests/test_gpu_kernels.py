@@ -149,6 +149,55 @@ def test_write_entries_bit_exact(gpu, oracle_mod, n_tok, ratio, rope, n_rows):
             np.testing.assert_array_equal(host(sg), s_ref)
 
 
+@pytest.mark.parametrize("n_tok,ratio,rope,n_rows", [(128, 1, True, 128), (16, 1, True, 0),
+                                                     (21, 1, False, 5), (10, 2, False, 3)])
+def test_write_entries_proj_bit_exact(gpu, oracle_mod, n_tok, ratio, rope, n_rows):
+    """The write path with the indexer key projected on the device: FP4
+    records, the projected keys' FP8 codes and sigmas at the entries' rows
+    (tile layout) and the window rows of the FP8 jobs, each equal to the
+    oracle's bytes; rows not addressed stay untouched."""
+    say(f"write_entries_proj n_tok={n_tok} ratio={ratio} rope={rope} n_rows={n_rows}")
+    g = np.random.default_rng(900 + n_tok + n_rows)
+    n_ent = n_tok // ratio
+    k = (g.standard_normal((n_tok, 128)) * np.exp2(g.integers(-8, 8, (n_tok, 1)))).astype(np.float32)
+    v = g.standard_normal((n_tok, 128)).astype(np.float32)
+    k[-ratio:] = 0.0  # an all-zero entry: zero key, zero sigma
+    W = (g.standard_normal((64, 128)) / np.sqrt(128)).astype(np.float32)
+    wk = (g.standard_normal((max(n_rows, 1), 128)) * 3).astype(np.float32)[:n_rows]
+    wv = g.standard_normal((max(n_rows, 1), 128)).astype(np.float32)[:n_rows]
+    rows = (np.arange(n_ent)[::-1] * 2 + 7).astype(np.int64)
+    cap = 64 * ((int(rows.max()) + 1 + 63) // 64)
+    assert rows.max() < cap  # every destination row inside the arrays
+    pos = np.arange(5000, 5000 + n_ent)
+    cs = oracle_mod.rope_table(pos) if rope else None
+    codes = torch.zeros((cap, 128), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((cap, 16), dtype=torch.uint8, device="cuda")
+    ikc = torch.full((cap * 64,), 0x5A, dtype=torch.uint8, device="cuda")
+    iks = torch.full((cap,), -1.0, dtype=torch.float32, device="cuda")
+    wkc = torch.zeros((max(n_rows, 1), 128), dtype=torch.uint8, device="cuda")
+    wks = torch.zeros(max(n_rows, 1), dtype=torch.float32, device="cuda")
+    wvc, wvs = torch.zeros_like(wkc), torch.zeros_like(wks)
+    jobs = [dict(x=dev(wk), codes=wkc, sigma=wks), dict(x=dev(wv), codes=wvc, sigma=wvs)]
+    gpu.write_entries(dev(k), dev(v), codes, scales, ratio=ratio,
+                      rope_cs=dev(gpu.rope_table(pos)) if rope else None, dst_rows=dev(rows),
+                      fp8_jobs=jobs if n_rows else (), idx_proj=dev(W), ik_codes=ikc,
+                      ik_sigma=iks)
+    cref, sref, ikref, isref = oracle_mod.write_entries_proj(k, v, W, ratio, cs)
+    np.testing.assert_array_equal(host(codes)[rows], cref)
+    np.testing.assert_array_equal(host(scales)[rows], sref)
+    ik_rows = untile_ik(host(ikc), 1, cap)[0]
+    np.testing.assert_array_equal(ik_rows[rows], ikref)
+    np.testing.assert_array_equal(host(iks)[rows], isref)
+    assert isref[-1] == 0.0 and not ikref[-1].any()  # the all-zero last entry
+    untouched = np.setdiff1d(np.arange(cap), rows)
+    assert (ik_rows[untouched] == 0x5A).all() and (host(iks)[untouched] == -1.0).all()
+    if n_rows:
+        for (xc, xs), x in (((wkc, wks), wk), ((wvc, wvs), wv)):
+            c_ref, s_ref = oracle_mod.quant_fp8_rows(x)
+            np.testing.assert_array_equal(host(xc), c_ref)
+            np.testing.assert_array_equal(host(xs), s_ref)
+
+
 # --------------------------------------------------------------------------- indexer
 def make_idx_cache(gpu, oracle_mod, B, cap, seed, dup_frac=0.0):
     g = np.random.default_rng(seed)

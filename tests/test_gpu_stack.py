@@ -51,12 +51,19 @@ def quantize_windows(gpu, swa_k, swa_v):
     return out
 
 
-def oracle_stack(oracle_mod, inp, b, topk, pool_blocks, plan, rope=False):
-    """Oracle run of one sequence: bytes, per-layer indices and outputs."""
+def oracle_stack(oracle_mod, inp, b, topk, pool_blocks, plan, rope=False, new_entry_proj=None):
+    """Oracle run of one sequence: bytes, per-layer indices and outputs.
+    new_entry_proj: W [64][128]: the last entry's indexer key is the one the
+    write path projects from its K (the others are the fixture's keys)."""
     n_ent = inp.k_tok.shape[1] // inp.wl.ratio
     cs = oracle_mod.rope_table(np.arange(n_ent)) if rope else None
     codes, scales = oracle_mod.quant_fp4(inp.k_tok[b], inp.v_tok[b], inp.wl.ratio, cs)
     ikc, iks = oracle_mod.quant_fp8_rows(inp.idx_k[b])
+    if new_entry_proj is not None:
+        r = inp.wl.ratio
+        _, _, ikc[-1:], iks[-1:] = oracle_mod.write_entries_proj(
+            inp.k_tok[b, -r:], inp.v_tok[b, -r:], new_entry_proj, r,
+            None if cs is None else cs[-1:])
     res = {"codes": codes, "scales": scales, "ikc": ikc, "iks": iks, "topk": [], "out": [],
            "lse": []}
     cur, pool, k = None, None, 0
@@ -211,3 +218,71 @@ def test_staged_stack_equals_plain_stack(gpu, oracle_mod):
         outs.append((host(st.out).copy(), host(st.lse).copy()))
     np.testing.assert_array_equal(outs[0][0], outs[1][0])
     np.testing.assert_array_equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("ratio_wl", ["decoder_stack_128k", "encoder_group_16k"])
+def test_decode_step_with_write_path(gpu, oracle_mod, ratio_wl):
+    """One whole decode step: the write path in one launch (every sequence's
+    new entry with its indexer key projected on the device, and every layer's
+    new window token appended at ring slot t mod 128), then the stack; bytes,
+    indices and outputs against the oracle.  Before the step the new entry's
+    cache rows and the windows' ring slots hold other data."""
+    from compressed_kv_cache_decode_amd.stack import DecodeStack
+    wl = synth.WORKLOADS[ratio_wl]
+    layers = 9 if wl.ratio == 1 else 6
+    n_ent = 6001 if wl.ratio == 1 else 3001
+    inp = synth.decode_inputs(wl, n_ent=n_ent, B=3, layers=layers)
+    B, plan, r = 3, wl.plan[:layers], wl.ratio
+    rope = wl.ratio == 1
+    cap = (n_ent + 63) // 64 * 64
+    say(f"write path step {ratio_wl}: B={B} n_ent={n_ent} plan={plan}")
+    cache = build_cache_on_gpu(gpu, inp, cap, rope=rope)
+    last = n_ent - 1
+    slot = (last * r + r - 1) % 128  # ring slot of the newest token
+    stale_k, stale_v = inp.swa_k.copy(), inp.swa_v.copy()
+    stale_k[:, :, slot] = 7.0
+    stale_v[:, :, slot] = -3.0
+    swk, sks, swv, svs = quantize_windows(gpu, stale_k, stale_v)
+    for b in range(B):  # stale bytes in the new entry's rows
+        cache.kv_codes[b * cap + last].fill_(0x11)
+        cache.ik_sigma[b * cap + last] = 123.0
+    st = DecodeStack(cache, plan, B, wl.H, topk=128, pool_blocks=256 if "X" in plan else 0)
+    k_new = dev(np.ascontiguousarray(inp.k_tok[:, last * r:last * r + r].reshape(-1, 128)))
+    v_new = dev(np.ascontiguousarray(inp.v_tok[:, last * r:last * r + r].reshape(-1, 128)))
+    rows_new = torch.arange(B, dtype=torch.int64, device="cuda") * cap + last
+    L = len(plan)
+    win_rows = dev(((np.arange(L)[:, None] * B + np.arange(B)[None, :]) * 128 + slot)
+                   .reshape(-1).astype(np.int64))
+    win_k = dev(np.ascontiguousarray(inp.swa_k[:, :, slot].reshape(-1, 128)))
+    win_v = dev(np.ascontiguousarray(inp.swa_v[:, :, slot].reshape(-1, 128)))
+    st.write(k_new, v_new, rows_new, dev(inp.proj), win_k, win_v, win_rows, swk, swv, sks, svs,
+             ratio=r, rope_cs=dev(gpu.rope_table(np.full(B, last))) if rope else None)
+    used = st.step(dev(inp.iq[:, :, None]), dev(inp.iw[:, :, None]),
+                   dev(np.full((B, 1), n_ent, np.int32)), dev(inp.q), swk, swv, sks, svs,
+                   dev(inp.swa_len))
+    torch.cuda.synchronize()
+    kvc, kvs = host(cache.kv_codes), host(cache.kv_scales)
+    ikc_all = untile_ik(host(cache.ik_codes), B, cap)
+    iks_all = host(cache.ik_sigma).reshape(B, cap)
+    for li in range(L):
+        for b in range(B):
+            ck, sk_ = oracle_mod.quant_fp8_rows(inp.swa_k[li, b])
+            np.testing.assert_array_equal(host(swk[li, b]), ck)
+            np.testing.assert_array_equal(host(sks[li, b]), sk_)
+            cv, sv_ = oracle_mod.quant_fp8_rows(inp.swa_v[li, b])
+            np.testing.assert_array_equal(host(swv[li, b]), cv)
+            np.testing.assert_array_equal(host(svs[li, b]), sv_)
+    for b in range(B):
+        say(f"write path step {ratio_wl}: oracle for sequence {b}")
+        ref = oracle_stack(oracle_mod, inp, b, 128, st.pool_blocks, plan, rope=rope,
+                           new_entry_proj=inp.proj)
+        r0 = b * cap
+        np.testing.assert_array_equal(kvc[r0:r0 + n_ent], ref["codes"])
+        np.testing.assert_array_equal(kvs[r0:r0 + n_ent], ref["scales"])
+        np.testing.assert_array_equal(ikc_all[b, :n_ent], ref["ikc"])
+        np.testing.assert_array_equal(iks_all[b, :n_ent], ref["iks"])
+        for layer in range(L):
+            np.testing.assert_array_equal(host(used[layer])[b, 0], ref["topk"][layer],
+                                          err_msg=f"layer {layer} ({plan[layer]})")
+            err = row_rel_err(host(st.out)[layer, b], ref["out"][layer])
+            assert err.max() <= 2e-3, (layer, err.max())

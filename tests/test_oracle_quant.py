@@ -180,3 +180,74 @@ def test_fp8_rows_against_torch(oracle_mod):
         ref = e4m3_rne(np.clip(t, -463, 463))
         np.testing.assert_array_equal(codes[r], ref)
         assert np.abs(e4m3_value(codes[r])).max() == 448.0  # the amax element hits 448
+
+
+# ---- indexer-key projection (write path) ---------------------------------
+def _proj_case(x_vals, w_vals):
+    W = np.zeros((64, 128), np.float32)
+    x = np.zeros((1, 128), np.float32)
+    W[0, :len(w_vals)] = w_vals
+    x[0, :len(x_vals)] = x_vals
+    return x, W
+
+
+def test_projection_accumulates_channels_in_ascending_order(oracle_mod):
+    """[2^24, 0, 1, 1]: adding the 1s one at a time to 2^24 rounds each away
+    (half an ulp, ties to even), so the ascending chain gives 2^24, while a
+    pairwise tree or the reverse order gives 2^24 + 2."""
+    x, W = _proj_case([2.0 ** 24, 0.0, 1.0, 1.0], [1.0] * 4)
+    assert oracle_mod.project_idx(x, W)[0, 0] == np.float32(2.0 ** 24)
+    x, W = _proj_case([1.0, 1.0, 0.0, 2.0 ** 24], [1.0] * 4)
+    assert oracle_mod.project_idx(x, W)[0, 0] == np.float32(2.0 ** 24 + 2)
+
+
+def test_projection_steps_are_fused_multiply_adds(oracle_mod):
+    """(1 + 2^-12)^2 - 1 = 2^-11 + 2^-24 exactly when the product is not
+    rounded before the add; a rounded product would give 2^-11."""
+    a = 1.0 + 2.0 ** -12
+    x, W = _proj_case([-1.0, a], [1.0, a])
+    assert oracle_mod.project_idx(x, W)[0, 0] == np.float32(2.0 ** -11 + 2.0 ** -24)
+
+
+def test_projection_against_fp64_within_summation_bound(oracle_mod):
+    """Every output within gamma_128 * sum_c |W x| of the fp64 product (the
+    bound of a 128-term recursive sum with one rounding per step); a
+    transposed or dropped operand misses by orders of magnitude."""
+    g = np.random.default_rng(11)
+    W = (g.standard_normal((64, 128)) / np.sqrt(128)).astype(np.float32)
+    x = (g.standard_normal((50, 128)) * np.exp2(g.integers(-6, 6, (50, 1)))).astype(np.float32)
+    got = oracle_mod.project_idx(x, W).astype(np.float64)
+    exact = x.astype(np.float64) @ W.astype(np.float64).T
+    mag = np.abs(x.astype(np.float64)) @ np.abs(W.astype(np.float64)).T
+    u = 2.0 ** -24
+    gamma = 128 * u / (1 - 128 * u)
+    assert np.all(np.abs(got - exact) <= gamma * mag)
+    assert np.abs(got - exact).max() > 0  # rounding does happen: fp32, not fp64
+
+
+def test_projection_small_integers_exact(oracle_mod):
+    """Small-integer operands: every partial sum is an integer below 2^24, so
+    the chain equals the integer matrix product exactly."""
+    g = np.random.default_rng(12)
+    W = g.integers(-8, 9, (64, 128)).astype(np.float32)
+    x = g.integers(-8, 9, (7, 128)).astype(np.float32)
+    exact = x.astype(np.int64) @ W.astype(np.int64).T
+    np.testing.assert_array_equal(oracle_mod.project_idx(x, W), exact.astype(np.float32))
+
+
+def test_entry_k_is_what_the_fp4_write_quantises(oracle_mod):
+    """The projected input is the entry's K after the pair mean / RoPE: FP4 of
+    entry_k with ratio 1 and no RoPE reproduces the records of the full write."""
+    g = np.random.default_rng(13)
+    k = g.standard_normal((20, 128)).astype(np.float32)
+    v = g.standard_normal((20, 128)).astype(np.float32)
+    for ratio, cs in ((2, None), (1, oracle_mod.rope_table(np.arange(300, 320)))):
+        xk = oracle_mod.entry_k(k, ratio, cs)
+        xv = oracle_mod.entry_k(v, ratio, None)
+        assert xk.shape == (20 // ratio, 128)
+        direct = oracle_mod.quant_fp4(k, v, ratio, cs)
+        again = oracle_mod.quant_fp4(xk, xv, 1, None)
+        np.testing.assert_array_equal(direct[0], again[0])
+        np.testing.assert_array_equal(direct[1], again[1])
+    rot = oracle_mod.entry_k(k[:1], 1, oracle_mod.rope_table(np.array([0])))
+    np.testing.assert_array_equal(rot, k[:1])  # position 0: cos 1, sin 0
