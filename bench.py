@@ -53,6 +53,10 @@ def parse_args():
     p.add_argument("--cpu-seqs", type=int, default=0,
                    help="sequences in the CPU-oracle sample (0 = one whole batch)")
     p.add_argument("--skip-cpu-baseline", action="store_true")
+    p.add_argument("--contexts", default="4096,16384,65536,131072,262144,1048576",
+                   help="model_step workload: context lengths (tokens) of the sweep")
+    p.add_argument("--model-batch", type=int, default=4,
+                   help="model_step workload: sequences per step")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="also run one device-to-device copy of this many MiB (a known-size "
                         "kernel for scaling hardware byte counters)")
@@ -562,6 +566,148 @@ def load_traffic():
     return out
 
 
+# --------------------------------------------------------------------------- whole model
+MODEL_METRIC = ("CSA2 whole-model decode step (40 layers: 2 window-only, 3 encoder groups "
+                "F+5R over 2:1 entries, decoder F+4X+15R), queries/s vs context")
+
+
+def build_model_set(csa2, T, B, H, topk, pool, seed):
+    """Caches, windows and inputs of one model step at context T tokens (T
+    even): the step's token is T - 1, which completes encoder pair T/2 - 1.
+    Every global KV is written by the library's write path (FP4 records and
+    device-projected FP8 indexer keys) from N(0, 1) K and V drawn on the
+    device; the step writes the last entry of each."""
+    import numpy as np
+    import torch
+
+    from compressed_kv_cache_decode_amd import stack as S
+    from compressed_kv_cache_decode_amd import synth
+
+    gen = synth.device_generator(seed)
+    rnd = lambda *shape: synth.device_normal(gen, shape)
+    proj = rnd(64, 128) / math.sqrt(128.0)
+    n_enc, n_dec = T // 2, T
+    up = lambda n: (n + 63) // 64 * 64
+    enc_caches = [csa2.Cache(B, up(n_enc)) for _ in range(S.ENCODER_GROUPS)]
+    dec_cache = csa2.Cache(B, up(n_dec))
+    CH = 1 << 16
+    for b in range(B):
+        for c in enc_caches:
+            for t0 in range(0, 2 * (n_enc - 1), CH):
+                n = min(CH, 2 * (n_enc - 1) - t0)
+                csa2.write_entries(rnd(n, 128), rnd(n, 128), c.kv_codes, c.kv_scales, ratio=2,
+                                   dst_rows=c.rows(b, np.arange(t0 // 2, (t0 + n) // 2)),
+                                   idx_proj=proj, ik_codes=c.ik_codes, ik_sigma=c.ik_sigma)
+        for t0 in range(0, n_dec - 1, CH):
+            n = min(CH, n_dec - 1 - t0)
+            pos = np.arange(t0, t0 + n)
+            csa2.write_entries(rnd(n, 128), rnd(n, 128), dec_cache.kv_codes, dec_cache.kv_scales,
+                               rope_cs=torch.from_numpy(csa2.rope_table(pos)).cuda(),
+                               dst_rows=dec_cache.rows(b, pos), idx_proj=proj,
+                               ik_codes=dec_cache.ik_codes, ik_sigma=dec_cache.ik_sigma)
+    slot = (T - 1) % 128
+
+    def windows(L):
+        k8 = torch.empty((L, B, 128, 128), dtype=torch.uint8, device="cuda")
+        v8 = torch.empty_like(k8)
+        ks = torch.empty((L, B, 128), dtype=torch.float32, device="cuda")
+        vs = torch.empty_like(ks)
+        csa2.quant_fp8(rnd(L * B * 128, 128), k8, ks)
+        csa2.quant_fp8(rnd(L * B * 128, 128), v8, vs)
+        rows = torch.from_numpy(((np.arange(L)[:, None] * B + np.arange(B)[None, :]) * 128
+                                 + slot).reshape(-1).astype(np.int64)).cuda()
+        return dict(swk=k8, swv=v8, sks=ks, svs=vs), rows
+
+    def group_args(plan, n_vis):
+        L, n_idx = len(plan), sum(m in "FX" for m in plan)
+        w, rows = windows(L)
+        a = dict(iq=rnd(n_idx, B, 1, 4, 64),
+                 iw=torch.rand((n_idx, B, 1, 4), generator=gen, device="cuda"),
+                 n_vis=torch.full((B, 1), n_vis, dtype=torch.int32, device="cuda"),
+                 q=rnd(L, B, H, 128), swa_len=torch.full((B,), 128, dtype=torch.int32,
+                                                         device="cuda"), **w)
+        return a, rows
+
+    enc_args, new = [], []
+    for c in enc_caches:
+        a, rows = group_args(S.ENCODER_GROUP_PLAN, n_enc)
+        enc_args.append(a)
+        new.append(dict(k_new=rnd(2 * B, 128), v_new=rnd(2 * B, 128),
+                        rows_new=torch.arange(B, device="cuda") * c.cap + (n_enc - 1),
+                        idx_proj=proj, win_k=rnd(len(S.ENCODER_GROUP_PLAN) * B, 128),
+                        win_v=rnd(len(S.ENCODER_GROUP_PLAN) * B, 128), win_rows=rows, ratio=2,
+                        rope_cs=None))
+    dec_args, rows = group_args(S.DECODER_PLAN, n_dec)
+    new.append(dict(k_new=rnd(B, 128), v_new=rnd(B, 128),
+                    rows_new=torch.arange(B, device="cuda") * dec_cache.cap + (n_dec - 1),
+                    idx_proj=proj, win_k=rnd(len(S.DECODER_PLAN) * B, 128),
+                    win_v=rnd(len(S.DECODER_PLAN) * B, 128), win_rows=rows, ratio=1,
+                    rope_cs=torch.from_numpy(csa2.rope_table(np.full(B, n_dec - 1))).cuda()))
+    W = S.ENCODER_WINDOW_ONLY
+    w, rows = windows(W)
+    win = dict(q=rnd(W, B, H, 128), swa_len=torch.full((B,), 128, dtype=torch.int32, device="cuda"),
+               win_k=rnd(W * B, 128), win_v=rnd(W * B, 128), win_rows=rows,
+               k_empty=torch.empty((0, 128), dtype=torch.float32, device="cuda"), **w)
+    model = S.ModelStep(enc_caches, dec_cache, B, H, topk=topk, pool_blocks=pool)
+    nbytes = dec_cache.nbytes + sum(c.nbytes for c in enc_caches)
+    return model, (new, win, enc_args, dec_args), nbytes
+
+
+def run_model_sweep(args):
+    """Whole-model decode step at each context of --contexts (HIP-graph
+    replay, two cache sets rotated)."""
+    import torch
+
+    import compressed_kv_cache_decode_amd as csa2
+    B, H, topk, pool = args.model_batch, 64, 512, 2048
+    sweep = []
+    for T in [int(x) for x in args.contexts.split(",")]:
+        if T % 2 or T < 256:
+            raise SystemExit("contexts must be even and at least 256 tokens")
+        log(f"model step: context {T} tokens, B={B}: writing the caches")
+        sets = [build_model_set(csa2, T, B, H, topk, pool, 2000 + 7 * i + T)
+                for i in range(2)]
+        torch.cuda.synchronize()
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            for i in range(max(args.warmup, 1)):
+                m, a, _ = sets[i % 2]
+                m.step(*a)
+            torch.cuda.synchronize()
+            graphs = []
+            for m, a, _ in sets:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    m.step(*a)
+                graphs.append(g)
+            for i in range(args.warmup):
+                graphs[i % 2].replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                graphs[i % 2].replay()
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) / args.steps
+        sweep.append({"context": T, "ms_per_step": round(dt * 1e3, 4),
+                      "queries_per_s": round(B / dt, 1),
+                      "cache_MB_per_set": round(sets[0][2] / 1e6, 1)})
+        log(f"model step: context {T}: {dt * 1e3:.4f} ms per step")
+        del sets, graphs
+        torch.cuda.empty_cache()
+    head = next((r for r in sweep if r["context"] == 131072), sweep[0])
+    return {
+        "metric": MODEL_METRIC, "value": head["queries_per_s"], "unit": "queries/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "model_step", "sequences": B, "context": head["context"],
+                   "layers": 40, "heads": H, "topk": topk, "pool_blocks": pool, "window": 128,
+                   "cache_sets": 2, "launch": "hip-graph"},
+        "roofline": None, "sweep": sweep,
+        "step_time_growth_first_to_last": round(sweep[-1]["ms_per_step"] / sweep[0]["ms_per_step"], 3),
+    }
+
+
 def copy_calibration(mib):
     """One device-to-device copy of `mib` MiB: a kernel of known traffic
     (reads and writes mib MiB each) for scaling the hardware byte counters."""
@@ -588,6 +734,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(3)
     from compressed_kv_cache_decode_amd import synth
+    if args.workload == "model_step":
+        print(json.dumps(run_model_sweep(args)), flush=True)
+        return
     wl = synth.WORKLOADS[args.workload]
     if args.copy_calibration_mb:
         copy_calibration(args.copy_calibration_mb)

@@ -181,3 +181,78 @@ class ChunkStack:
             used.append(cur)
         return used
 
+
+
+# The model's layer plan ("DeepSeek V4.1 Flash: architecture study notes",
+# section 2, the layer table; section 3, sequence compression): encoder layers
+# 1-2 attend to their window only; encoder layers 3-20 are three groups of one
+# Full and five Reuse layers, each group over its own global KV of 2:1
+# compressed entries; decoder layers 21-40 are one Full, four Reindex and
+# fifteen Reuse layers over one shared global KV of uncompressed entries.
+ENCODER_WINDOW_ONLY = 2
+ENCODER_GROUP_PLAN = "FRRRRR"
+ENCODER_GROUPS = 3
+ENCODER_RATIO = 2
+DECODER_PLAN = "FRRRXRRRXRRRXRRRXRRR"
+
+
+class ModelStep:
+    """One decode step of the whole 40-layer plan for B sequences: the write
+    path of the new token into every global KV and every layer's window, then
+    the encoder's window-only layers, its three groups and the decoder stack.
+
+    enc_caches: three Cache objects (2:1 compressed entries), dec_cache: one
+    Cache (one entry per token).  Every layer has its own window, stacked per
+    group as [L][B][128][128] (window-only layers: [2][B][128][128])."""
+
+    def __init__(self, enc_caches, dec_cache, B, H, topk=DEFAULT_TOPK,
+                 pool_blocks=DEFAULT_POOL_BLOCKS):
+        if len(enc_caches) != ENCODER_GROUPS:
+            raise ValueError(f"{ENCODER_GROUPS} encoder caches expected")
+        self.B, self.H, self.topk = B, H, topk
+        self.enc = [DecodeStack(c, ENCODER_GROUP_PLAN, B, H, topk=topk, pool_blocks=0)
+                    for c in enc_caches]
+        self.dec = DecodeStack(dec_cache, DECODER_PLAN, B, H, topk=topk, pool_blocks=pool_blocks)
+        dev = dec_cache.kv_codes.device
+        W = ENCODER_WINDOW_ONLY
+        self.win_out = torch.empty((W, B, H, HEAD_DIM), dtype=torch.float32, device=dev)
+        self.win_lse = torch.empty((W, B, H), dtype=torch.float32, device=dev)
+        self.no_idx = torch.empty((B, 0), dtype=torch.int32, device=dev)
+        n_attn = workspace_size(OP_ATTN_DECODE, B, 1, dec_cache.cap, 0, 0, H)
+        self.ws_win = alloc_workspace(n_attn, dev) if n_attn else None
+
+    @property
+    def layers(self):
+        return ENCODER_WINDOW_ONLY + ENCODER_GROUPS * len(ENCODER_GROUP_PLAN) + len(DECODER_PLAN)
+
+    def step(self, new, win, enc_args, dec_args, stream=None):
+        """new: per global KV (three encoder groups, then the decoder) a dict
+        with the arguments of DecodeStack.write (k_new, v_new, rows_new,
+        idx_proj, win_k, win_v, win_rows, ratio, rope_cs); for an encoder
+        group whose pair the token does not complete, k_new / v_new have no
+        rows (only the window tokens are written);
+        win: the window-only layers' dict: q [2][B][H][128], swk / swv
+        [2][B][128][128] u8, sks / svs [2][B][128] f32, swa_len [B], the new
+        window rows win_k / win_v [2*B][128] f32 with their rows win_rows, and
+        k_empty, an f32 tensor of shape [0][128];
+        enc_args / dec_args: per group a dict iq, iw, n_vis, q, swk, swv, sks,
+        svs, swa_len with the meaning of DecodeStack.step's arguments.
+        Returns, per group, the top-K buffers its layers attended with."""
+        write_entries(win["k_empty"], win["k_empty"], self.dec.cache.kv_codes,
+                      self.dec.cache.kv_scales,
+                      fp8_jobs=[dict(x=win["win_k"], codes=win["swk"].view(-1, HEAD_DIM),
+                                     sigma=win["sks"].view(-1), dst_rows=win["win_rows"]),
+                                dict(x=win["win_v"], codes=win["swv"].view(-1, HEAD_DIM),
+                                     sigma=win["svs"].view(-1), dst_rows=win["win_rows"])],
+                      stream=stream)
+        for i in range(ENCODER_WINDOW_ONLY):
+            sparse_attn_decode(win["q"][i], self.dec.cache, self.no_idx, win["swk"][i],
+                               win["swv"][i], win["sks"][i], win["svs"][i], win["swa_len"],
+                               self.win_out[i], self.win_lse[i], ws=self.ws_win, stream=stream)
+        used = []
+        for st, wr, a in zip(self.enc + [self.dec], new, enc_args + [dec_args]):
+            st.write(**wr, swa_k=a["swk"], swa_v=a["swv"], swa_ks=a["sks"], swa_vs=a["svs"],
+                     stream=stream)
+            used.append(st.step(a["iq"], a["iw"], a["n_vis"], a["q"], a["swk"], a["swv"],
+                                a["sks"], a["svs"], a["swa_len"], stream=stream))
+        return used

@@ -257,3 +257,18 @@ def chunk_stack_inputs(wl, n_ent=None, Q=None, H=None, B=None, layers=None, seed
     positions = np.arange(n_ent - Q, n_ent, dtype=np.int64)
     return ChunkStackInputs(wl, plan, k_tok, v_tok, idx_k, iq, iw, q, swa_k, swa_v, positions,
                             proj.astype(np.float32))
+
+
+def device_generator(seed):
+    """Seeded torch generator on the GPU, for workloads too large to draw on
+    the host (their results are checked through sampled properties only)."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return g
+
+
+def device_normal(gen, shape):
+    """N(0, 1) fp32 tensor of `shape` on the GPU from `gen`."""
+    import torch
+    return torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)

@@ -286,3 +286,95 @@ def test_decode_step_with_write_path(gpu, oracle_mod, ratio_wl):
                                           err_msg=f"layer {layer} ({plan[layer]})")
             err = row_rel_err(host(st.out)[layer, b], ref["out"][layer])
             assert err.max() <= 2e-3, (layer, err.max())
+
+
+def prepare_group(gpu, inp, B, plan, rope):
+    """Caches and windows of one layer group with the step's ring slot and new
+    entry holding stale data, and the arguments of its write and its step."""
+    r = inp.wl.ratio
+    n_ent = inp.k_tok.shape[1] // r
+    cap = (n_ent + 63) // 64 * 64
+    cache = build_cache_on_gpu(gpu, inp, cap, rope=rope)
+    last = n_ent - 1
+    slot = (last * r + r - 1) % 128
+    stale_k, stale_v = inp.swa_k.copy(), inp.swa_v.copy()
+    stale_k[:, :, slot], stale_v[:, :, slot] = 5.0, -2.0
+    swk, sks, swv, svs = quantize_windows(gpu, stale_k, stale_v)
+    for b in range(B):
+        cache.kv_codes[b * cap + last].fill_(0x22)
+        cache.ik_sigma[b * cap + last] = 77.0
+    L = len(plan)
+    wr = dict(k_new=dev(np.ascontiguousarray(inp.k_tok[:, last * r:last * r + r].reshape(-1, 128))),
+              v_new=dev(np.ascontiguousarray(inp.v_tok[:, last * r:last * r + r].reshape(-1, 128))),
+              rows_new=torch.arange(B, dtype=torch.int64, device="cuda") * cap + last,
+              idx_proj=dev(inp.proj),
+              win_k=dev(np.ascontiguousarray(inp.swa_k[:, :, slot].reshape(-1, 128))),
+              win_v=dev(np.ascontiguousarray(inp.swa_v[:, :, slot].reshape(-1, 128))),
+              win_rows=dev(((np.arange(L)[:, None] * B + np.arange(B)[None, :]) * 128 + slot)
+                           .reshape(-1).astype(np.int64)),
+              ratio=r, rope_cs=dev(gpu.rope_table(np.full(B, last))) if rope else None)
+    args = dict(iq=dev(inp.iq[:, :, None]), iw=dev(inp.iw[:, :, None]),
+                n_vis=dev(np.full((B, 1), n_ent, np.int32)), q=dev(inp.q), swk=swk, swv=swv,
+                sks=sks, svs=svs, swa_len=dev(inp.swa_len))
+    return cache, wr, args
+
+
+def test_model_step_all_40_layers(gpu, oracle_mod):
+    """One decode step of the whole layer plan (2 window-only layers, three
+    encoder groups F+5R over 2:1 entries, the decoder F+4X+15R) at a 4000-token
+    context: every layer's indices and output against the oracle."""
+    from compressed_kv_cache_decode_amd import stack as S
+    B, T, topk, pool = 2, 4000, 512, 2048
+    wl_e, wl_d = synth.WORKLOADS["encoder_group_16k"], synth.WORKLOADS["decoder_stack_128k"]
+    groups = [(synth.decode_inputs(wl_e, n_ent=T // 2, B=B, seed=3000 + g), S.ENCODER_GROUP_PLAN,
+               False) for g in range(S.ENCODER_GROUPS)]
+    groups.append((synth.decode_inputs(wl_d, n_ent=T, B=B, seed=3100), S.DECODER_PLAN, True))
+    say("model step: writing four caches")
+    prepared = [prepare_group(gpu, inp, B, plan, rope) for inp, plan, rope in groups]
+    g = np.random.default_rng(3200)
+    H, W = wl_d.H, S.ENCODER_WINDOW_ONLY
+    wq = g.standard_normal((W, B, H, 128), dtype=np.float32)
+    wk = g.standard_normal((W, B, 128, 128), dtype=np.float32)
+    wv = g.standard_normal((W, B, 128, 128), dtype=np.float32)
+    slot = (T - 1) % 128
+    wsk, wsks, wsv, wsvs = quantize_windows(gpu, np.zeros_like(wk), np.zeros_like(wv))
+    win = dict(q=dev(wq), swk=wsk, swv=wsv, sks=wsks, svs=wsvs,
+               swa_len=dev(np.full(B, 128, np.int32)),
+               k_empty=torch.empty((0, 128), dtype=torch.float32, device="cuda"),
+               win_k=dev(np.ascontiguousarray(wk[:, :, slot].reshape(-1, 128))),
+               win_v=dev(np.ascontiguousarray(wv[:, :, slot].reshape(-1, 128))),
+               win_rows=dev(((np.arange(W)[:, None] * B + np.arange(B)[None, :]) * 128 + slot)
+                            .reshape(-1).astype(np.int64)))
+    # the window-only layers' other slots are written up front
+    wk_stale, wv_stale = wk.copy(), wv.copy()
+    wk_stale[:, :, slot], wv_stale[:, :, slot] = 1.0, 1.0
+    for x, codes, sig in ((wk_stale, wsk, wsks), (wv_stale, wsv, wsvs)):
+        gpu.quant_fp8(dev(x.reshape(-1, 128)), codes, sig)
+    model = S.ModelStep([p[0] for p in prepared[:3]], prepared[3][0], B, H, topk=topk,
+                        pool_blocks=pool)
+    assert model.layers == 40
+    say("model step: one step on the GPU")
+    used = model.step([p[1] for p in prepared], win, [p[2] for p in prepared[:3]],
+                      prepared[3][2])
+    torch.cuda.synchronize()
+    for i in range(W):
+        for b in range(B):
+            sk, sks_ = oracle_mod.quant_fp8_rows(wk[i, b])
+            sv, svs_ = oracle_mod.quant_fp8_rows(wv[i, b])
+            codes = np.zeros((1, 128), np.uint8)
+            scales = np.zeros((1, 16), np.uint8)
+            o, _ = oracle_mod.attn(wq[i, b], codes, scales, np.full(0, -1, np.int32), sk, sv,
+                                   sks_, svs_, 128, SM)
+            err = row_rel_err(host(model.win_out[i, b]), o)
+            assert err.max() <= 2e-3, ("window-only", i, b, err.max())
+    stacks = model.enc + [model.dec]
+    for gi, ((inp, plan, rope), st) in enumerate(zip(groups, stacks)):
+        for b in range(B):
+            say(f"model step: oracle for group {gi} sequence {b}")
+            ref = oracle_stack(oracle_mod, inp, b, topk, st.pool_blocks, plan, rope=rope,
+                               new_entry_proj=inp.proj)
+            for layer in range(len(plan)):
+                np.testing.assert_array_equal(host(used[gi][layer])[b, 0], ref["topk"][layer],
+                                              err_msg=f"group {gi} layer {layer}")
+                err = row_rel_err(host(st.out)[layer, b], ref["out"][layer])
+                assert err.max() <= 2e-3, (gi, layer, err.max())
