@@ -61,6 +61,17 @@ def lib():
                                                u8p, u8p, f32p, f32p, i32p, c_f, f32p, f32p]),
             "csa2o_attn_chunk_batch": (None, [f32p, c_int, c_int, c_int, u8p, u8p, c_i64, i32p,
                                               c_int, u8p, u8p, f32p, f32p, c_f, f32p, f32p]),
+            "csa2o_fp4_quant_groups": (None, [f32p, c_int, u8p, u8p]),
+            "csa2o_idx4_quant_rows": (None, [f32p, c_i64, u8p, u8p]),
+            "csa2o_score4": (c_f, [u8p, f32p, u8p, u8p]),
+            "csa2o_index_full4": (c_int, [u8p, u8p, c_i64, f32p, f32p, c_int, c_int, i32p,
+                                          ctypes.c_void_p, ctypes.c_void_p]),
+            "csa2o_index_reindex4": (c_int, [u8p, u8p, c_i64, f32p, f32p, i32p, c_int, c_int,
+                                             i32p]),
+            "csa2o_index_full4_batch": (c_int, [u8p, u8p, c_i64, c_int, c_int, f32p, f32p, i32p,
+                                                c_int, c_int, i32p, ctypes.c_void_p]),
+            "csa2o_index_reindex4_batch": (c_int, [u8p, u8p, c_i64, c_int, c_int, f32p, f32p,
+                                                   i32p, i32p, c_int, c_int, i32p]),
             "csa2o_num_threads": (c_int, []),
         }
         for name, (res, args) in sig.items():
@@ -245,6 +256,80 @@ def index_reindex_batch(ikc, iks, iq, iw, n_vis, pool_idx, topk):
                                          pool_idx.shape[-1], topk, topk_idx)
     if rc != 0:
         raise ValueError("oracle index_reindex_batch rejected its arguments")
+    return topk_idx
+
+
+# ---- FP4 indexer key -----------------------------------------------------
+# layout: codes [n][32] uint8 (low nibble = even channel), scales [n][4] uint8
+# (E4M3, one per 16 channels)
+def idx4_quant_rows(x):
+    """x [..., 64] fp32 -> (codes [..., 32] u8, scales [..., 4] u8)."""
+    x = _c(x, np.float32)
+    n = x.size // 64
+    codes = np.zeros(x.shape[:-1] + (32,), np.uint8)
+    scales = np.zeros(x.shape[:-1] + (4,), np.uint8)
+    lib().csa2o_idx4_quant_rows(x, n, codes, scales)
+    return codes, scales
+
+
+def score4(qc, wq, kc4, ks4):
+    return lib().csa2o_score4(_c(qc, np.uint8), _c(wq, np.float32), _c(kc4, np.uint8),
+                              _c(ks4, np.uint8))
+
+
+def index_full4(kc4, ks4, n_vis, iq, iw, topk, pool_blocks, want_scores=False):
+    kc4, ks4 = _c(kc4, np.uint8), _c(ks4, np.uint8)
+    topk_idx = np.empty(topk, np.int32)
+    pool = np.empty(max(pool_blocks, 1), np.int32)
+    sc = np.empty(max(int(n_vis), 1), np.float32)
+    rc = lib().csa2o_index_full4(kc4, ks4, int(n_vis), _c(iq, np.float32), _c(iw, np.float32),
+                                 topk, pool_blocks, topk_idx, pool.ctypes.data,
+                                 sc.ctypes.data if want_scores else None)
+    if rc != 0:
+        raise ValueError("oracle index_full4 rejected its arguments")
+    out = [topk_idx, pool[:pool_blocks]]
+    if want_scores:
+        out.append(sc[:int(n_vis)])
+    return tuple(out)
+
+
+def index_reindex4(kc4, ks4, n_vis, iq, iw, pool_idx, topk):
+    pool_idx = _c(pool_idx, np.int32)
+    topk_idx = np.empty(topk, np.int32)
+    rc = lib().csa2o_index_reindex4(_c(kc4, np.uint8), _c(ks4, np.uint8), int(n_vis),
+                                    _c(iq, np.float32), _c(iw, np.float32), pool_idx,
+                                    pool_idx.size, topk, topk_idx)
+    if rc != 0:
+        raise ValueError("oracle index_reindex4 rejected its arguments")
+    return topk_idx
+
+
+def index_full4_batch(kc4, ks4, iq, iw, n_vis, topk, pool_blocks):
+    """kc4 [B][cap][32], ks4 [B][cap][4], iq [B][Q][4][64], iw [B][Q][4], n_vis [B][Q]."""
+    kc4, ks4 = _c(kc4, np.uint8), _c(ks4, np.uint8)
+    B, cap = ks4.shape[:2]
+    Q = iq.shape[1]
+    topk_idx = np.empty((B, Q, topk), np.int32)
+    pool = np.empty((B, Q, max(pool_blocks, 1)), np.int32)
+    rc = lib().csa2o_index_full4_batch(kc4, ks4, cap, B, Q, _c(iq, np.float32),
+                                       _c(iw, np.float32), _c(n_vis, np.int32), topk,
+                                       pool_blocks, topk_idx, pool.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle index_full4_batch rejected its arguments")
+    return topk_idx, pool[:, :, :pool_blocks]
+
+
+def index_reindex4_batch(kc4, ks4, iq, iw, n_vis, pool_idx, topk):
+    kc4, ks4 = _c(kc4, np.uint8), _c(ks4, np.uint8)
+    B, cap = ks4.shape[:2]
+    Q = iq.shape[1]
+    pool_idx = _c(pool_idx, np.int32)
+    topk_idx = np.empty((B, Q, topk), np.int32)
+    rc = lib().csa2o_index_reindex4_batch(kc4, ks4, cap, B, Q, _c(iq, np.float32),
+                                          _c(iw, np.float32), _c(n_vis, np.int32), pool_idx,
+                                          pool_idx.shape[-1], topk, topk_idx)
+    if rc != 0:
+        raise ValueError("oracle index_reindex4_batch rejected its arguments")
     return topk_idx
 
 

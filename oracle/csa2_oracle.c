@@ -153,7 +153,11 @@ void csa2o_rope_apply(float* x, const float* cs_row) {
  * global scale.  Reading: scale = RNE_E4M3(amax/6); a zero scale gives
  * signed-zero codes; code = RNE_E2M1(x/scale). */
 void csa2o_fp4_quant_vec(const float* x, uint8_t* codes, uint8_t* scales) {
-    for (int g = 0; g < HEAD_DIM / 16; ++g) {
+    csa2o_fp4_quant_groups(x, HEAD_DIM / 16, codes, scales);
+}
+
+void csa2o_fp4_quant_groups(const float* x, int n_groups, uint8_t* codes, uint8_t* scales) {
+    for (int g = 0; g < n_groups; ++g) {
         const float* xg = x + 16 * g;
         float amax = 0.0f;
         for (int i = 0; i < 16; ++i) {
@@ -335,17 +339,31 @@ static void take_top(ranked_t* r, int64_t n, int cap, int32_t* out) {
     for (int64_t i = keep; i < cap; ++i) out[i] = -1;
 }
 
-int csa2o_index_full(const uint8_t* ikc, const float* iks, int64_t n_vis,
-                     const float* iq, const float* iw, int topk, int pool_blocks,
-                     int32_t* topk_idx, int32_t* pool_idx, float* scores) {
+/* score of visible position s of one sequence's indexer keys */
+typedef float (*row_score_fn)(const uint8_t* qc, const float* wq, const void* kc, const void* ks,
+                              int64_t s);
+
+static float score_fp8_row(const uint8_t* qc, const float* wq, const void* kc, const void* ks,
+                           int64_t s) {
+    return csa2o_score(qc, wq, (const uint8_t*)kc + s * IDX_DIM, ((const float*)ks)[s]);
+}
+
+static float score_fp4_row(const uint8_t* qc, const float* wq, const void* kc, const void* ks,
+                           int64_t s) {
+    return csa2o_score4(qc, wq, (const uint8_t*)kc + s * (IDX_DIM / 2),
+                        (const uint8_t*)ks + s * (IDX_DIM / 16));
+}
+
+static int index_full_any(row_score_fn fn, const void* kc, const void* ks, int64_t n_vis,
+                          const float* iq, const float* iw, int topk, int pool_blocks,
+                          int32_t* topk_idx, int32_t* pool_idx, float* scores) {
     if (n_vis < 0 || topk < 0 || pool_blocks < 0) return -1;
     uint8_t qc[IDX_HEADS * IDX_DIM];
     float wq[IDX_HEADS];
     csa2o_quant_iq(iq, iw, qc, wq);
 
     float* sc = (float*)malloc(sizeof(float) * (size_t)(n_vis > 0 ? n_vis : 1));
-    for (int64_t s = 0; s < n_vis; ++s)
-        sc[s] = csa2o_score(qc, wq, ikc + s * IDX_DIM, iks[s]);
+    for (int64_t s = 0; s < n_vis; ++s) sc[s] = fn(qc, wq, kc, ks, s);
     if (scores) memcpy(scores, sc, sizeof(float) * (size_t)n_vis);
 
     /* own top-K over every visible position */
@@ -371,9 +389,9 @@ int csa2o_index_full(const uint8_t* ikc, const float* iks, int64_t n_vis,
     return 0;
 }
 
-int csa2o_index_reindex(const uint8_t* ikc, const float* iks, int64_t n_vis,
-                        const float* iq, const float* iw, const int32_t* pool_idx,
-                        int pool_blocks, int topk, int32_t* topk_idx) {
+static int index_reindex_any(row_score_fn fn, const void* kc, const void* ks, int64_t n_vis,
+                             const float* iq, const float* iw, const int32_t* pool_idx,
+                             int pool_blocks, int topk, int32_t* topk_idx) {
     if (n_vis < 0 || topk < 0 || pool_blocks < 0) return -1;
     uint8_t qc[IDX_HEADS * IDX_DIM];
     float wq[IDX_HEADS];
@@ -385,7 +403,7 @@ int csa2o_index_reindex(const uint8_t* ikc, const float* iks, int64_t n_vis,
         if (b < 0) continue;
         for (int64_t s = (int64_t)b * BLOCK; s < (int64_t)b * BLOCK + BLOCK; ++s) {
             if (s >= n_vis) break;
-            r[n].key = csa2o_score(qc, wq, ikc + s * IDX_DIM, iks[s]);
+            r[n].key = fn(qc, wq, kc, ks, s);
             r[n].index = s;
             ++n;
         }
@@ -393,6 +411,110 @@ int csa2o_index_reindex(const uint8_t* ikc, const float* iks, int64_t n_vis,
     take_top(r, n, topk, topk_idx);
     free(r);
     return 0;
+}
+
+int csa2o_index_full(const uint8_t* ikc, const float* iks, int64_t n_vis,
+                     const float* iq, const float* iw, int topk, int pool_blocks,
+                     int32_t* topk_idx, int32_t* pool_idx, float* scores) {
+    return index_full_any(score_fp8_row, ikc, iks, n_vis, iq, iw, topk, pool_blocks, topk_idx,
+                          pool_idx, scores);
+}
+
+int csa2o_index_reindex(const uint8_t* ikc, const float* iks, int64_t n_vis,
+                        const float* iq, const float* iw, const int32_t* pool_idx,
+                        int pool_blocks, int topk, int32_t* topk_idx) {
+    return index_reindex_any(score_fp8_row, ikc, iks, n_vis, iq, iw, pool_idx, pool_blocks, topk,
+                             topk_idx);
+}
+
+/* ------------------------------------------------------------------------
+ * FP4 indexer key.  [notes] section 4: the FP4 main KV builds on the previous
+ * generation's FP4 indexer key.  Reading: the indexer key in the main KV's
+ * FP4 format -- E2M1 codes (low nibble = even channel) with one E4M3 scale
+ * per 16 channels, no per-position scale: 32 + 4 = 36 bytes per position.
+ * Score: the block-scaled dot product (the form the OCP Microscaling
+ * specification gives for the dot product of block-scaled vectors: each
+ * block's element products summed, then scaled by the block scale):
+ *   inner_hg = fp32 sum over the 16 channels c of group g in ascending order
+ *              of E4M3(q_hc) * E2M1(k_c) (each product exact), from +0;
+ *   dot_h    = fused multiply-add chain over g = 0..3 of scale_g * inner_hg,
+ *              from +0;
+ *   r_h, t as for the FP8 key; score = t (no per-position scale).
+ * ---------------------------------------------------------------------- */
+void csa2o_idx4_quant_rows(const float* x, int64_t n, uint8_t* codes, uint8_t* scales) {
+    for (int64_t i = 0; i < n; ++i)
+        csa2o_fp4_quant_groups(x + i * IDX_DIM, IDX_DIM / 16, codes + i * (IDX_DIM / 2),
+                               scales + i * (IDX_DIM / 16));
+}
+
+float csa2o_score4(const uint8_t* qc, const float* wq, const uint8_t* kc, const uint8_t* ks) {
+    float t = 0.0f;
+    for (int h = 0; h < IDX_HEADS; ++h) {
+        float dot = 0.0f;
+        for (int g = 0; g < IDX_DIM / 16; ++g) {
+            float inner = 0.0f;
+            for (int c = 16 * g; c < 16 * g + 16; ++c) {
+                uint8_t nib = (c % 2 == 0) ? (kc[c / 2] & 0x0F) : (kc[c / 2] >> 4);
+                float a = (float)csa2o_e4m3_decode(qc[h * IDX_DIM + c]);
+                float b = (float)csa2o_e2m1_decode(nib);
+                float p = a * b;
+                inner = inner + p;
+            }
+            dot = fmaf((float)csa2o_e4m3_decode(ks[g]), inner, dot);
+        }
+        float r = dot > 0.0f ? dot : 0.0f;
+        float wr = wq[h] * r;
+        t = (h == 0) ? wr : t + wr;
+    }
+    return t;
+}
+
+int csa2o_index_full4(const uint8_t* kc4, const uint8_t* ks4, int64_t n_vis, const float* iq,
+                      const float* iw, int topk, int pool_blocks, int32_t* topk_idx,
+                      int32_t* pool_idx, float* scores) {
+    return index_full_any(score_fp4_row, kc4, ks4, n_vis, iq, iw, topk, pool_blocks, topk_idx,
+                          pool_idx, scores);
+}
+
+int csa2o_index_reindex4(const uint8_t* kc4, const uint8_t* ks4, int64_t n_vis, const float* iq,
+                         const float* iw, const int32_t* pool_idx, int pool_blocks, int topk,
+                         int32_t* topk_idx) {
+    return index_reindex_any(score_fp4_row, kc4, ks4, n_vis, iq, iw, pool_idx, pool_blocks, topk,
+                             topk_idx);
+}
+
+int csa2o_index_full4_batch(const uint8_t* kc4, const uint8_t* ks4, int64_t cap, int B, int Q,
+                            const float* iq, const float* iw, const int32_t* n_vis, int topk,
+                            int pool_blocks, int32_t* topk_idx, int32_t* pool_idx) {
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t bq = 0; bq < (int64_t)B * Q; ++bq) {
+        int64_t b = bq / Q;
+        int rc = csa2o_index_full4(kc4 + b * cap * (IDX_DIM / 2), ks4 + b * cap * (IDX_DIM / 16),
+                                   n_vis[bq], iq + bq * IDX_HEADS * IDX_DIM, iw + bq * IDX_HEADS,
+                                   topk, pool_blocks, topk_idx + bq * topk,
+                                   pool_blocks > 0 ? pool_idx + bq * pool_blocks : NULL, NULL);
+        bad |= (rc != 0);
+    }
+    return bad ? -1 : 0;
+}
+
+int csa2o_index_reindex4_batch(const uint8_t* kc4, const uint8_t* ks4, int64_t cap, int B, int Q,
+                               const float* iq, const float* iw, const int32_t* n_vis,
+                               const int32_t* pool_idx, int pool_blocks, int topk,
+                               int32_t* topk_idx) {
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t bq = 0; bq < (int64_t)B * Q; ++bq) {
+        int64_t b = bq / Q;
+        int rc = csa2o_index_reindex4(kc4 + b * cap * (IDX_DIM / 2),
+                                      ks4 + b * cap * (IDX_DIM / 16), n_vis[bq],
+                                      iq + bq * IDX_HEADS * IDX_DIM, iw + bq * IDX_HEADS,
+                                      pool_idx + bq * pool_blocks, pool_blocks, topk,
+                                      topk_idx + bq * topk);
+        bad |= (rc != 0);
+    }
+    return bad ? -1 : 0;
 }
 
 int csa2o_index_full_batch(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,

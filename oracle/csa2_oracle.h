@@ -54,6 +54,8 @@ void csa2o_rope_table(const int64_t* pos, int64_t n, double base, float* cs);
 void csa2o_rope_apply(float* x, const float* cs_row);
 /* one 128-channel vector -> 64 code bytes (low nibble = even channel) + 8 E4M3 scales */
 void csa2o_fp4_quant_vec(const float* x, uint8_t* codes, uint8_t* scales);
+/* the same for n_groups groups of 16 channels */
+void csa2o_fp4_quant_groups(const float* x, int n_groups, uint8_t* codes, uint8_t* scales);
 /* write-path batch: n_tok tokens of K and V [n_tok][128]; ratio 1 or 2;
  * rope_cs NULL or [n_ent][32][2]; out codes [n_ent][128] (K 64 B | V 64 B),
  * scales [n_ent][16] (K 8 | V 8). Returns 0 or -1 on bad arguments. */
@@ -118,6 +120,23 @@ void csa2o_attn_chunk_batch(const float* q, int B, int Q, int H, const uint8_t* 
                             const uint8_t* scales, int64_t cap, const int32_t* idx, int topk,
                             const uint8_t* swa_k, const uint8_t* swa_v, const float* swa_ks,
                             const float* swa_vs, float sm_scale, float* out, float* lse);
+
+/* ---- FP4 indexer key (36 B per position: codes [n][32], scales [n][4]) ---- */
+void  csa2o_idx4_quant_rows(const float* x, int64_t n, uint8_t* codes, uint8_t* scales);
+float csa2o_score4(const uint8_t* qc, const float* wq, const uint8_t* kc, const uint8_t* ks);
+int csa2o_index_full4(const uint8_t* kc4, const uint8_t* ks4, int64_t n_vis, const float* iq,
+                      const float* iw, int topk, int pool_blocks, int32_t* topk_idx,
+                      int32_t* pool_idx, float* scores);
+int csa2o_index_reindex4(const uint8_t* kc4, const uint8_t* ks4, int64_t n_vis, const float* iq,
+                         const float* iw, const int32_t* pool_idx, int pool_blocks, int topk,
+                         int32_t* topk_idx);
+int csa2o_index_full4_batch(const uint8_t* kc4, const uint8_t* ks4, int64_t cap, int B, int Q,
+                            const float* iq, const float* iw, const int32_t* n_vis, int topk,
+                            int pool_blocks, int32_t* topk_idx, int32_t* pool_idx);
+int csa2o_index_reindex4_batch(const uint8_t* kc4, const uint8_t* ks4, int64_t cap, int B, int Q,
+                               const float* iq, const float* iw, const int32_t* n_vis,
+                               const int32_t* pool_idx, int pool_blocks, int topk,
+                               int32_t* topk_idx);
 
 int csa2o_num_threads(void);
 
