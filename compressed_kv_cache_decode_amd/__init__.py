@@ -50,7 +50,9 @@ EXPORTS = ("csa2_quant_fp4", "csa2_quant_fp8", "csa2_write_entries", "csa2_write
            "csa2_sparse_attn_decode", "csa2_sparse_attn_decode_timed",
            "csa2_sparse_attn_decode_reuse", "csa2_sparse_attn_chunk",
            "csa2_workspace_size",
-           "csa2_status_str", "csa2_abi_version", "csa2_codec_probe")
+           "csa2_status_str", "csa2_abi_version", "csa2_codec_probe",
+           "csa2_quant_idx_fp4", "csa2_write_entries_proj_fp4", "csa2_index_full_fp4",
+           "csa2_index_full_fp4_timed", "csa2_index_reindex_fp4")
 
 _lib = None
 
@@ -92,6 +94,15 @@ _SIGS = {
     "csa2_status_str": (ctypes.c_char_p, [_int]),
     "csa2_abi_version": (_int, []),
     "csa2_codec_probe": (_int, [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),
+    "csa2_quant_idx_fp4": (_int, [_vp, _i64, _vp, _vp, _vp, _vp]),
+    "csa2_write_entries_proj_fp4": (_int, [_vp, _vp, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp,
+                                           _vp, ctypes.POINTER(_Fp8Job), _int, _vp]),
+    "csa2_index_full_fp4": (_int, [_vp, _vp, _i64, _int, _int, _vp, _vp, _vp, _int, _int, _vp,
+                                   _vp, _vp, _sz, _vp]),
+    "csa2_index_full_fp4_timed": (_int, [_vp, _vp, _i64, _int, _int, _vp, _vp, _vp, _int, _int,
+                                         _vp, _vp, _vp, _sz, _vp, _vp, _vp]),
+    "csa2_index_reindex_fp4": (_int, [_vp, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _int, _int,
+                                      _vp, _vp, _sz, _vp]),
 }
 
 
@@ -162,18 +173,31 @@ class Cache:
     """Device arrays of one shared global KV (B sequences x cap entries).
 
     kv_codes [B*cap][128] u8, kv_scales [B*cap][16] u8: FP4 main KV;
-    ik_codes [B*cap*64] u8 (tile layout), ik_sigma [B*cap] f32: FP8 indexer K."""
+    indexer K, FP8 (default): ik_codes [B*cap*64] u8 (tile layout), ik_sigma
+    [B*cap] f32; FP4 (idx_fp4=True): ik_codes [B*cap*32] u8 (two-plane tile
+    layout), ik_scales4 [B*cap][4] u8 E4M3 (ik_sigma is None)."""
 
-    def __init__(self, B, cap, device=None):
+    def __init__(self, B, cap, device=None, idx_fp4=False):
         if cap % IDX_TILE:
             raise ValueError("cap must be a multiple of 64")
         dev = device or torch.cuda.current_device()
-        self.B, self.cap = B, cap
+        self.B, self.cap, self.idx_fp4 = B, cap, idx_fp4
         n = B * cap
         self.kv_codes = torch.zeros((n, KV_CODE_BYTES), dtype=torch.uint8, device=dev)
         self.kv_scales = torch.zeros((n, KV_SCALE_BYTES), dtype=torch.uint8, device=dev)
-        self.ik_codes = torch.zeros(n * IDX_DIM, dtype=torch.uint8, device=dev)
-        self.ik_sigma = torch.zeros(n, dtype=torch.float32, device=dev)
+        if idx_fp4:
+            self.ik_codes = torch.zeros(n * IDX_DIM // 2, dtype=torch.uint8, device=dev)
+            self.ik_scales4 = torch.zeros((n, 4), dtype=torch.uint8, device=dev)
+            self.ik_sigma = None
+        else:
+            self.ik_codes = torch.zeros(n * IDX_DIM, dtype=torch.uint8, device=dev)
+            self.ik_sigma = torch.zeros(n, dtype=torch.float32, device=dev)
+            self.ik_scales4 = None
+
+    @property
+    def ik_aux(self):
+        """The indexer key's per-row array: fp32 sigma (FP8) or scale bytes (FP4)."""
+        return self.ik_scales4 if self.idx_fp4 else self.ik_sigma
 
     def rows(self, b, positions):
         """int64 device tensor of row numbers b*cap + positions."""
@@ -183,7 +207,7 @@ class Cache:
     @property
     def nbytes(self):
         return sum(t.numel() * t.element_size()
-                   for t in (self.kv_codes, self.kv_scales, self.ik_codes, self.ik_sigma))
+                   for t in (self.kv_codes, self.kv_scales, self.ik_codes, self.ik_aux))
 
 
 def rope_table(positions, base=10000.0):
@@ -226,14 +250,16 @@ def quant_fp8(x, codes, sigma, layout=FP8_ROWS, dst_rows=None, stream=None):
 
 
 def write_entries(k_tok, v_tok, kv_codes, kv_scales, ratio=1, rope_cs=None, dst_rows=None,
-                  fp8_jobs=(), stream=None, idx_proj=None, ik_codes=None, ik_sigma=None):
+                  fp8_jobs=(), stream=None, idx_proj=None, ik_codes=None, ik_sigma=None,
+                  ik_scales4=None):
     """quant_fp4(k_tok, v_tok, ...) and quant_fp8 of each job in one launch.
 
     fp8_jobs: up to 3 dicts with the arguments of quant_fp8: x, codes, sigma,
     and optionally layout (FP8_ROWS) and dst_rows.
     idx_proj [64][128] f32 (optional): also each entry's indexer key, projected
     on the device from its fp32 K and written in FP8 to ik_codes (tile layout)
-    and ik_sigma at the entry's row (csa2_write_entries_proj)."""
+    and ik_sigma at the entry's row (csa2_write_entries_proj), or as FP4 keys to
+    ik_codes and ik_scales4 when ik_scales4 is given (csa2_write_entries_proj_fp4)."""
     n_tok = k_tok.shape[0] if k_tok.dim() > 1 else 0
     if k_tok.shape != v_tok.shape or (k_tok.dim() != 2 or k_tok.shape[1] != HEAD_DIM):
         raise ValueError("k_tok, v_tok must be [n_tok][128]")
@@ -260,10 +286,35 @@ def write_entries(k_tok, v_tok, kv_codes, kv_scales, ratio=1, rope_cs=None, dst_
         return
     if tuple(idx_proj.shape) != (IDX_DIM, HEAD_DIM):
         raise ValueError("idx_proj must be [64][128]")
+    if ik_scales4 is not None:
+        rc = lib().csa2_write_entries_proj_fp4(
+            *head, _ptr(idx_proj, torch.float32, "idx_proj"),
+            _ptr(ik_codes, torch.uint8, "ik_codes"), _ptr(ik_scales4, torch.uint8, "ik_scales4"),
+            jobs, len(fp8_jobs), _stream(stream))
+        _check(rc, "csa2_write_entries_proj_fp4")
+        return
     rc = lib().csa2_write_entries_proj(
         *head, _ptr(idx_proj, torch.float32, "idx_proj"), _ptr(ik_codes, torch.uint8, "ik_codes"),
         _ptr(ik_sigma, torch.float32, "ik_sigma"), jobs, len(fp8_jobs), _stream(stream))
     _check(rc, "csa2_write_entries_proj")
+
+
+def _ik_aux_ptr(cache):
+    if cache.idx_fp4:
+        return _ptr(cache.ik_scales4, torch.uint8, "ik_scales4")
+    return _ptr(cache.ik_sigma, torch.float32, "ik_sigma")
+
+
+def quant_idx_fp4(x, ik_codes, ik_scales4, dst_rows=None, stream=None):
+    """x [n][64] f32 -> FP4 indexer keys at rows dst_rows (or 0..n-1)."""
+    if x.dim() != 2 or x.shape[1] != IDX_DIM:
+        raise ValueError("x must be [n][64]")
+    n = x.shape[0]
+    rc = lib().csa2_quant_idx_fp4(_ptr(x, torch.float32, "x"), n,
+                                  _ptr(dst_rows, torch.int64, "dst_rows", n),
+                                  _ptr(ik_codes, torch.uint8, "ik_codes"),
+                                  _ptr(ik_scales4, torch.uint8, "ik_scales4"), _stream(stream))
+    _check(rc, "csa2_quant_idx_fp4")
 
 
 def index_full(cache, iq, iw, n_vis, topk_idx, pool_idx=None, topk=DEFAULT_TOPK,
@@ -276,9 +327,9 @@ def index_full(cache, iq, iw, n_vis, topk_idx, pool_idx=None, topk=DEFAULT_TOPK,
     if ws is None:
         ws = alloc_workspace(need, iq.device)
     ev = scan_timer.next_pair() if scan_timer is not None else (None, None)
-    rc = lib().csa2_index_full_timed(
-        _ptr(cache.ik_codes, torch.uint8, "ik_codes"), _ptr(cache.ik_sigma, torch.float32, "ik_sigma"),
-        cache.cap, B, Q, _ptr(iq, torch.float32, "iq", B * Q * 256),
+    fn = lib().csa2_index_full_fp4_timed if cache.idx_fp4 else lib().csa2_index_full_timed
+    rc = fn(
+        _ptr(cache.ik_codes, torch.uint8, "ik_codes"), _ik_aux_ptr(cache), cache.cap, B, Q, _ptr(iq, torch.float32, "iq", B * Q * 256),
         _ptr(iw, torch.float32, "iw", B * Q * 4), _ptr(n_vis, torch.int32, "n_vis", B * Q),
         topk, pool_blocks, _ptr(topk_idx, torch.int32, "topk_idx", B * Q * topk),
         _ptr(pool_idx, torch.int32, "pool_idx", B * Q * pool_blocks) if pool_blocks else None,
@@ -293,9 +344,9 @@ def index_reindex(cache, iq, iw, n_vis, pool_idx, topk_idx, topk=DEFAULT_TOPK, w
     need = workspace_size(OP_INDEX_REINDEX, B, Q, cache.cap, topk, pool_blocks, 0)
     if ws is None:
         ws = alloc_workspace(need, iq.device)
-    rc = lib().csa2_index_reindex(
-        _ptr(cache.ik_codes, torch.uint8, "ik_codes"), _ptr(cache.ik_sigma, torch.float32, "ik_sigma"),
-        cache.cap, B, Q, _ptr(iq, torch.float32, "iq", B * Q * 256),
+    fn = lib().csa2_index_reindex_fp4 if cache.idx_fp4 else lib().csa2_index_reindex
+    rc = fn(
+        _ptr(cache.ik_codes, torch.uint8, "ik_codes"), _ik_aux_ptr(cache), cache.cap, B, Q, _ptr(iq, torch.float32, "iq", B * Q * 256),
         _ptr(iw, torch.float32, "iw", B * Q * 4), _ptr(n_vis, torch.int32, "n_vis", B * Q),
         _ptr(pool_idx, torch.int32, "pool_idx", B * Q * pool_blocks), pool_blocks, topk,
         _ptr(topk_idx, torch.int32, "topk_idx", B * Q * topk),

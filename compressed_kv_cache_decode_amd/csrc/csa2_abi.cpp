@@ -253,6 +253,38 @@ __attribute__((visibility("default"))) int csa2_write_entries_proj(
     return hip_status(launch_write_entries(f, j, stream));
 }
 
+namespace {
+// The Full layer on the VALU scan: query prep, exact keys of every visible
+// position (and block / superblock maxima), then the pool and top-K
+// selection.  Arguments validated and the workspace checked by the caller.
+int index_full_valu(int fmt, const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
+                    const float* iq, const float* iw, const int32_t* n_vis, int topk,
+                    int pool_blocks, int32_t* topk_idx, int32_t* pool_idx, void* ws,
+                    hipStream_t stream, hipEvent_t scan_start, hipEvent_t scan_stop) {
+    const IndexLayout L = full_layout(B, Q, cap, topk, pool_blocks);
+    char* w = static_cast<char*>(ws);
+    float* qd = reinterpret_cast<float*>(w + L.qd);
+    float* wq = reinterpret_cast<float*>(w + L.wq);
+    uint32_t* keys = reinterpret_cast<uint32_t*>(w + L.keys);
+    uint32_t* bkeys = reinterpret_cast<uint32_t*>(w + L.bkeys);
+    uint32_t* sbkeys = reinterpret_cast<uint32_t*>(w + L.sbkeys);
+    const int64_t nq = (int64_t)B * Q;
+    // The Full layer's own top-K over every visible position equals the top-K
+    // inside its best P >= K blocks (ties to the lower index on both levels),
+    // so the position select only ever looks at P*8 candidates.  Without a
+    // requested pool, P = K blocks are kept internally.
+    const int P = pool_blocks > 0 ? pool_blocks : topk;
+    hipError_t e = launch_prep_iq(iq, iw, nq, qd, wq, stream);
+    if (e == hipSuccess)
+        e = launch_scan(ikc, iks, cap, B, Q, qd, wq, n_vis, keys, bkeys, stream, scan_start,
+                        scan_stop, sbkeys, fmt);
+    if (e == hipSuccess)
+        e = launch_select_full(keys, bkeys, cap, n_vis, nq, P, topk,
+                               pool_blocks > 0 ? pool_idx : nullptr, topk_idx, stream, sbkeys);
+    return hip_status(e);
+}
+}  // namespace
+
 __attribute__((visibility("default"))) int csa2_index_full_timed(
     const uint8_t* ik_codes, const float* ik_sigma, int64_t cap, int B, int Q, const float* iq,
     const float* iw, const int32_t* n_vis, int topk, int pool_blocks, int32_t* topk_idx,
@@ -269,12 +301,6 @@ __attribute__((visibility("default"))) int csa2_index_full_timed(
     uint32_t* keys = reinterpret_cast<uint32_t*>(w + L.keys);
     uint32_t* bkeys = reinterpret_cast<uint32_t*>(w + L.bkeys);
     const int64_t nq = (int64_t)B * Q;
-    // The Full layer's own top-K over every visible position equals the top-K
-    // inside its best P >= K blocks (ties to the lower index on both levels),
-    // so the position select only ever looks at P*8 candidates.  Without a
-    // requested pool, P = K blocks are kept internally.
-    const int P = pool_blocks > 0 ? pool_blocks : topk;
-
     if (mma_path(Q, cap, pool_blocks, topk)) {
         // bounds on MFMA, then per query, in one workgroup: with a pool, the
         // blocks the bounds decide plus the best undecided ones by exact
@@ -297,15 +323,8 @@ __attribute__((visibility("default"))) int csa2_index_full_timed(
         return hip_status(e);
     }
 
-    uint32_t* sbkeys = reinterpret_cast<uint32_t*>(w + L.sbkeys);
-    hipError_t e = launch_prep_iq(iq, iw, nq, qd, wq, stream);
-    if (e == hipSuccess)
-        e = launch_scan(ik_codes, ik_sigma, cap, B, Q, qd, wq, n_vis, keys, bkeys, stream,
-                        scan_start, scan_stop, sbkeys);
-    if (e == hipSuccess)
-        e = launch_select_full(keys, bkeys, cap, n_vis, nq, P, topk,
-                               pool_blocks > 0 ? pool_idx : nullptr, topk_idx, stream, sbkeys);
-    return hip_status(e);
+    return index_full_valu(kIdxFp8, ik_codes, ik_sigma, cap, B, Q, iq, iw, n_vis, topk,
+                           pool_blocks, topk_idx, pool_idx, ws, stream, scan_start, scan_stop);
 }
 
 __attribute__((visibility("default"))) int csa2_index_full(
@@ -333,6 +352,80 @@ __attribute__((visibility("default"))) int csa2_index_reindex(
     if (e == hipSuccess)
         e = launch_select_pool(ckeys, pool_idx, pool_blocks, n_vis, cap, nq, topk, topk_idx,
                                stream);
+    return hip_status(e);
+}
+
+__attribute__((visibility("default"))) int csa2_quant_idx_fp4(const float* x, int64_t n_rows,
+                                                              const int64_t* dst_rows,
+                                                              uint8_t* codes, uint8_t* scales,
+                                                              hipStream_t stream) {
+    if (n_rows < 0) return CSA2_E_ARG;
+    if (n_rows == 0) return CSA2_OK;
+    if (!x || !codes || !scales) return CSA2_E_ARG;
+    return hip_status(launch_quant_idx4(x, n_rows, dst_rows, codes, scales, stream));
+}
+
+__attribute__((visibility("default"))) int csa2_write_entries_proj_fp4(
+    const float* k_tok, const float* v_tok, int64_t n_tok, int ratio, const float* rope_cs,
+    const int64_t* dst_rows, uint8_t* kv_codes, uint8_t* kv_scales, const float* idx_proj,
+    uint8_t* ik4_codes, uint8_t* ik4_scales, const csa2_fp8_job* jobs, int n_jobs,
+    hipStream_t stream) {
+    if (n_jobs < 0 || n_jobs > CSA2_MAX_FP8_JOBS || (n_jobs > 0 && !jobs)) return CSA2_E_ARG;
+    int rc = validate_quant_fp4(k_tok, v_tok, n_tok, ratio, rope_cs, kv_codes, kv_scales);
+    if (rc != CSA2_OK) return rc;
+    if (n_tok > 0 && (!idx_proj || !ik4_codes || !ik4_scales)) return CSA2_E_ARG;
+    Fp8Jobs j{};
+    for (int i = 0; i < n_jobs; ++i) {
+        const csa2_fp8_job& b = jobs[i];
+        rc = validate_quant_fp8(b.x, b.n_rows, b.dim, b.layout, b.codes, b.sigma);
+        if (rc != CSA2_OK) return rc;
+        if (b.n_rows == 0) continue;
+        j.job[j.n++] = Fp8Job{b.x, b.n_rows, b.dim, b.layout, b.dst_rows, b.codes, b.sigma};
+    }
+    const Fp4Job f{k_tok,    v_tok,     n_tok / ratio, ratio,     rope_cs, dst_rows,
+                   kv_codes, kv_scales, idx_proj,      ik4_codes, nullptr, ik4_scales};
+    return hip_status(launch_write_entries(f, j, stream));
+}
+
+__attribute__((visibility("default"))) int csa2_index_full_fp4_timed(
+    const uint8_t* ik4_codes, const uint8_t* ik4_scales, int64_t cap, int B, int Q,
+    const float* iq, const float* iw, const int32_t* n_vis, int topk, int pool_blocks,
+    int32_t* topk_idx, int32_t* pool_idx, void* ws, size_t ws_bytes, hipStream_t stream,
+    hipEvent_t scan_start, hipEvent_t scan_stop) {
+    int rc = validate_index_full(ik4_codes, ik4_scales, cap, B, Q, iq, iw, n_vis, topk,
+                                 pool_blocks, topk_idx, pool_idx);
+    if (rc) return rc;
+    if (!ws || ws_bytes < full_layout(B, Q, cap, topk, pool_blocks).total) return CSA2_E_WORKSPACE;
+    return index_full_valu(kIdxFp4, ik4_codes, reinterpret_cast<const float*>(ik4_scales), cap, B,
+                           Q, iq, iw, n_vis, topk, pool_blocks, topk_idx, pool_idx, ws, stream,
+                           scan_start, scan_stop);
+}
+
+__attribute__((visibility("default"))) int csa2_index_full_fp4(
+    const uint8_t* ik4_codes, const uint8_t* ik4_scales, int64_t cap, int B, int Q,
+    const float* iq, const float* iw, const int32_t* n_vis, int topk, int pool_blocks,
+    int32_t* topk_idx, int32_t* pool_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return csa2_index_full_fp4_timed(ik4_codes, ik4_scales, cap, B, Q, iq, iw, n_vis, topk,
+                                     pool_blocks, topk_idx, pool_idx, ws, ws_bytes, stream,
+                                     nullptr, nullptr);
+}
+
+__attribute__((visibility("default"))) int csa2_index_reindex_fp4(
+    const uint8_t* ik4_codes, const uint8_t* ik4_scales, int64_t cap, int B, int Q,
+    const float* iq, const float* iw, const int32_t* n_vis, const int32_t* pool_idx,
+    int pool_blocks, int topk, int32_t* topk_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int rc = validate_index_reindex(ik4_codes, ik4_scales, cap, B, Q, iq, iw, n_vis, pool_idx,
+                                    pool_blocks, topk, topk_idx);
+    if (rc) return rc;
+    const IndexLayout L = reindex_layout(B, Q, pool_blocks);
+    if (!ws || ws_bytes < L.total) return CSA2_E_WORKSPACE;
+    uint32_t* ckeys = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + L.keys);
+    hipError_t e = launch_pool_score(ik4_codes, reinterpret_cast<const float*>(ik4_scales), cap,
+                                     B, Q, iq, iw, n_vis, pool_idx, pool_blocks, ckeys, stream,
+                                     kIdxFp4);
+    if (e == hipSuccess)
+        e = launch_select_pool(ckeys, pool_idx, pool_blocks, n_vis, cap, (int64_t)B * Q, topk,
+                               topk_idx, stream);
     return hip_status(e);
 }
 

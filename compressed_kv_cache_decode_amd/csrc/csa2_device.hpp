@@ -218,4 +218,11 @@ __device__ __forceinline__ int64_t ik_offset(int64_t row, int g) {
     return (((row >> 6) * 4 + g) * 64 + (row & 63)) * 16;
 }
 
+// FP4 indexer key, tiled the same way: per 64 positions two 1 KB planes,
+// plane h holding the 16 code bytes of channels 32h..32h+31 of each position
+// (low nibble = even channel); byte offset of (row, plane h)
+__device__ __forceinline__ int64_t ik4_offset(int64_t row, int h) {
+    return (((row >> 6) * 2 + h) * 64 + (row & 63)) * 16;
+}
+
 }  // namespace csa2

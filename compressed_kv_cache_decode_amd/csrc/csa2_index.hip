@@ -68,6 +68,79 @@ __device__ __forceinline__ void load_ik_row(const uint8_t* __restrict__ ikc, int
         raw[g] = load16_stream(ikc + ik_offset(row, g));
 }
 
+// FP4 indexer key (36 bytes: 32 bytes of E2M1 codes, low nibble = even
+// channel, and one E4M3 scale per 16 channels, no per-position scale).
+// Block-scaled score, in this order:
+//   inner_hg = fp32 sum over the 16 channels of group g ascending of
+//              E4M3(q_hc) * E2M1(k_c) (each product exact), from +0;
+//   dot_h    = fused multiply-add chain over g = 0..3 of scale_g * inner_hg;
+//   r_h, t as for the FP8 key; score = t.
+__device__ __forceinline__ float score_row4(const uint4 (&raw)[2], uint32_t sc4,
+                                            const float* __restrict__ qd,
+                                            const float* __restrict__ wq) {
+    float kf[kIdxDim];  // E2M1 values, unscaled
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t w[4] = {raw[h].x, raw[h].y, raw[h].z, raw[h].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // byte b of the word: channels 2b (low nibble) and 2b + 1
+            const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 0);
+            const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 1);
+            const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 2);
+            const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 3);
+            float* o = kf + 32 * h + 8 * i;
+            o[0] = v0[0]; o[1] = v0[1]; o[2] = v1[0]; o[3] = v1[1];
+            o[4] = v2[0]; o[5] = v2[1]; o[6] = v3[0]; o[7] = v3[1];
+        }
+    }
+    const float2 s01 = e4m3x2_to_f32<false>(sc4);
+    const float2 s23 = e4m3x2_to_f32<true>(sc4);
+    const float sg[4] = {s01.x, s01.y, s23.x, s23.y};
+    float t = 0.0f;
+#pragma unroll
+    for (int h = 0; h < kIdxHeads; ++h) {
+        float dot = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float inner = 0.0f;
+#pragma unroll
+            for (int c = 16 * g; c < 16 * g + 16; ++c)
+                inner = fmaf(qd[h * kIdxDim + c], kf[c], inner);
+            dot = fmaf(sg[g], inner, dot);
+        }
+        const float r = dot > 0.0f ? dot : 0.0f;
+        const float wr = wq[h] * r;
+        t = (h == 0) ? wr : t + wr;
+    }
+    return t;
+}
+
+// One position's key in either format: FP8 (codes in the 4-plane tiles, fp32
+// sigma per row in `aux`) or FP4 (codes in the 2-plane tiles, the four E4M3
+// scale bytes of the row as one 32-bit word of `aux`).
+template <int FMT>
+struct IdxRow {
+    uint4 raw[FMT == 0 ? 4 : 2];
+    uint32_t aux;
+    __device__ __forceinline__ void load(const uint8_t* __restrict__ ikc,
+                                         const float* __restrict__ iks, int64_t row) {
+        if constexpr (FMT == 0) {
+            load_ik_row(ikc, row, raw);
+            aux = __float_as_uint(iks[row]);
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) raw[h] = load16_stream(ikc + ik4_offset(row, h));
+            aux = reinterpret_cast<const uint32_t*>(iks)[row];
+        }
+    }
+    __device__ __forceinline__ float score(const float* __restrict__ qd,
+                                           const float* __restrict__ wq) const {
+        if constexpr (FMT == 0) return score_row(raw, __uint_as_float(aux), qd, wq);
+        else return score_row4(raw, aux, qd, wq);
+    }
+};
+
 // Keys of one query over its nv visible positions (and the block keys of the
 // blocks they fill), computed by a whole workgroup of `nthreads` threads with
 // k_scan's arithmetic: the replay chunk's fallback for a query whose MFMA
@@ -102,6 +175,9 @@ __device__ __forceinline__ void scan_query_exact(const uint8_t* __restrict__ ikc
 // of each 64-position superblock (one wave).  Tiles that no query of the
 // sequence can see are skipped entirely.
 // ---------------------------------------------------------------------------
+// FMT 0: FP8 keys (iks = fp32 sigma per row); FMT 1: FP4 keys (iks = the
+// rows' four E4M3 scale bytes, read as one 32-bit word per row).
+template <int FMT>
 __global__ __launch_bounds__(256) void k_scan(const uint8_t* __restrict__ ikc,
                                               const float* __restrict__ iks, int64_t cap, int Q,
                                               const float* __restrict__ qd,
@@ -120,15 +196,14 @@ __global__ __launch_bounds__(256) void k_scan(const uint8_t* __restrict__ ikc,
     if (p0 + (threadIdx.x & ~63) >= cap) return;
 
     const int64_t row = (int64_t)b * cap + p;
-    uint4 raw[4];
-    load_ik_row(ikc, row, raw);
-    const float sigma = iks[row];
+    IdxRow<FMT> r;
+    r.load(ikc, iks, row);
     const int64_t nb = cap / kBlock;
     for (int q = 0; q < Q; ++q) {
         const int64_t bq = (int64_t)b * Q + q;
         const int nv = clamp_nvis(n_vis[bq], cap);
         if (p0 >= nv) continue;  // uniform
-        const float s = score_row(raw, sigma, qd + bq * kIdxHeads * kIdxDim, wq + bq * kIdxHeads);
+        const float s = r.score(qd + bq * kIdxHeads * kIdxDim, wq + bq * kIdxHeads);
         const uint32_t key = (p < nv) ? score_key(s) : 0u;
         keys[bq * cap + p] = key;
         const uint32_t bk = max8_u32(key);
@@ -244,6 +319,7 @@ __global__ __launch_bounds__(256) void k_scan_multi(const uint8_t* __restrict__ 
 // decoded back to fp32 in LDS, w' = w * sq), while its row loads are in
 // flight; the score then reads q from LDS (broadcast reads).
 // ---------------------------------------------------------------------------
+template <int FMT>
 __global__ __launch_bounds__(256) void k_pool_score(const uint8_t* __restrict__ ikc,
                                                     const float* __restrict__ iks, int64_t cap,
                                                     int Q, const float* __restrict__ iq,
@@ -261,13 +337,8 @@ __global__ __launch_bounds__(256) void k_pool_score(const uint8_t* __restrict__ 
     const int32_t blk = s < n_slots ? pool[bq * P + (s >> 3)] : -1;
     const int64_t pos = (int64_t)blk * kBlock + (s & 7);
     const bool valid = blk >= 0 && pos < nv;
-    uint4 raw[4];
-    float sigma = 0.0f;
-    if (valid) {
-        const int64_t row = b * cap + pos;
-        load_ik_row(ikc, row, raw);
-        sigma = iks[row];
-    }
+    IdxRow<FMT> r;
+    if (valid) r.load(ikc, iks, b * cap + pos);
     {   // the query's E4M3 codes (exact fp32 values) and folded weights
         const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
         const float x = iq[(bq * kIdxHeads + h) * kIdxDim + lane];
@@ -279,7 +350,7 @@ __global__ __launch_bounds__(256) void k_pool_score(const uint8_t* __restrict__ 
     __syncthreads();
     if (s >= n_slots) return;
     uint32_t key = 0;
-    if (valid) key = score_key(score_row(raw, sigma, sq, sw));
+    if (valid) key = score_key(r.score(sq, sw));
     ckeys[bq * n_slots + s] = key;
 }
 
@@ -1232,11 +1303,12 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select_pool(
 hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                        const float* qd, const float* wq, const int32_t* n_vis, uint32_t* keys,
                        uint32_t* bkeys, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
-                       uint32_t* sbkeys) {
+                       uint32_t* sbkeys, int fmt) {
     dim3 grid((unsigned)((cap + 255) / 256), (unsigned)B);
     // a few queries per sequence: k_scan reads them through the scalar cache;
     // many (the replay chunk): k_scan_multi stages them in LDS
-    auto kern = Q >= 4 ? k_scan_multi : k_scan;
+    // FP4 keys: k_scan for any Q
+    auto kern = fmt == 1 ? k_scan<1> : (Q >= 4 ? k_scan_multi : k_scan<0>);
     if (start != nullptr && stop != nullptr) {
         // the runtime records `start` / `stop` immediately around this dispatch
         hipExtLaunchKernelGGL(kern, grid, dim3(256), 0, stream, start, stop, 0, ikc, iks, cap, Q,
@@ -1250,11 +1322,12 @@ hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B,
 
 hipError_t launch_pool_score(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                              const float* iq, const float* iw, const int32_t* n_vis,
-                             const int32_t* pool, int P, uint32_t* ckeys, hipStream_t stream) {
+                             const int32_t* pool, int P, uint32_t* ckeys, hipStream_t stream,
+                             int fmt) {
     const int64_t n_slots = (int64_t)P * kBlock;
     dim3 grid((unsigned)((n_slots + 255) / 256), (unsigned)(B * Q));
-    hipLaunchKernelGGL(k_pool_score, grid, dim3(256), 0, stream, ikc, iks, cap, Q, iq, iw, n_vis,
-                       pool, P, ckeys);
+    hipLaunchKernelGGL(fmt == 1 ? k_pool_score<1> : k_pool_score<0>, grid, dim3(256), 0, stream,
+                       ikc, iks, cap, Q, iq, iw, n_vis, pool, P, ckeys);
     return hipGetLastError();
 }
 

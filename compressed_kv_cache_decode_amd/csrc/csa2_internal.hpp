@@ -27,9 +27,11 @@ struct Fp4Job {
     uint8_t* scales;
     // optional: the entries' indexer keys projected on the device from their
     // fp32 K, proj [64][128], written to ik_codes (tile layout) / ik_sigma
+    // (FP8), or to ik_codes / ik_scales4 (FP4, when ik_scales4 is set)
     const float* proj = nullptr;
     uint8_t* ik_codes = nullptr;
     float* ik_sigma = nullptr;
+    uint8_t* ik_scales4 = nullptr;
 };
 struct Fp8Job {
     const float* x;
@@ -53,12 +55,17 @@ hipError_t launch_codec_probe(float* e4m3_dec, float* e4m3_dec16, float* fp4_dec
                               const float* x, int64_t n, uint8_t* e4m3_enc, uint8_t* e2m1_enc,
                               hipStream_t stream);
 
+// indexer-key formats: kIdxFp8 (4-plane tiles + fp32 sigma per row) and
+// kIdxFp4 (2-plane tiles of E2M1 codes + 4 E4M3 scale bytes per row, passed
+// where the sigma array goes)
+constexpr int kIdxFp8 = 0;
+constexpr int kIdxFp4 = 1;
 // sbkeys (may be null): also the max key per superblock of kSuper positions
 constexpr int kSuper = 64;
 hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                        const float* qd, const float* wq, const int32_t* n_vis, uint32_t* keys,
                        uint32_t* bkeys, hipStream_t stream, hipEvent_t start = nullptr,
-                       hipEvent_t stop = nullptr, uint32_t* sbkeys = nullptr);
+                       hipEvent_t stop = nullptr, uint32_t* sbkeys = nullptr, int fmt = kIdxFp8);
 // MFMA scan of a multi-query chunk with guard-band bounds (csa2_chunk.hip):
 // the largest lower-bound score key per block of 8 positions [nq][cap / 8]
 // and the upper-bound key per half-block of 4 [nq][cap / 4]
@@ -87,7 +94,12 @@ inline int chunk_cand_halves(int K) { return 3 * K < 512 ? 512 : 3 * K; }
 constexpr int kChunkMaxTopk = 1024;
 hipError_t launch_pool_score(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                              const float* iq, const float* iw, const int32_t* n_vis,
-                             const int32_t* pool, int P, uint32_t* ckeys, hipStream_t stream);
+                             const int32_t* pool, int P, uint32_t* ckeys, hipStream_t stream,
+                             int fmt = kIdxFp8);
+// FP4 indexer keys of n_rows fp32 rows [n_rows][64] into the 2-plane tiles and
+// the per-row scale bytes (row dst_rows[r], or r)
+hipError_t launch_quant_idx4(const float* x, int64_t n_rows, const int64_t* dst_rows,
+                             uint8_t* codes, uint8_t* scales, hipStream_t stream);
 // sbkeys: null, or the scan's superblock keys (used when the blocks do not
 // fit the register path)
 hipError_t launch_select_full(const uint32_t* keys, const uint32_t* bkeys, int64_t cap,

@@ -63,6 +63,23 @@ __device__ __forceinline__ void quant_fp8_vals(const float* xv, int per, int lay
     if (lane == 0) sigma[row] = s;
 }
 
+// FP4 indexer key of one row, one channel per lane (lane c = channel c):
+// per 16-channel group scale = RNE_E4M3(fl(amax/6)), code = RNE_E2M1(fl(x/scale))
+// (signed zero when the scale is 0), the main KV's FP4 rule over 64 channels.
+__device__ __forceinline__ void quant_idx4_val(float x, int64_t row, uint8_t* __restrict__ codes,
+                                               uint8_t* __restrict__ scales, int lane) {
+    float amax = fabsf(x);
+    amax = fmaxf(amax, __shfl_xor(amax, 8, 64));
+    amax = group8_max_f32(amax);
+    const uint32_t sc = e4m3_encode(amax / 6.0f);
+    const float sd = e4m3_decode_bits(sc);
+    const uint32_t code = (sd == 0.0f) ? ((__float_as_uint(x) >> 28) & 8u) : e2m1_encode(x / sd);
+    const uint32_t odd = __shfl_xor(code, 1, 64);
+    if ((lane & 1) == 0)
+        codes[ik4_offset(row, lane >> 5) + ((lane & 31) >> 1)] = (uint8_t)(code | (odd << 4));
+    if ((lane & 15) == 0) scales[row * 4 + (lane >> 4)] = (uint8_t)sc;
+}
+
 // proj (may be null): also the entry's indexer key, projected from its fp32 K
 // (after averaging and RoPE) and written in FP8 to ik_codes (tile layout) /
 // ik_sigma at the entry's row.
@@ -74,7 +91,8 @@ __device__ __forceinline__ void quant_fp4_entry(const float* __restrict__ k,
                                                 uint8_t* __restrict__ scales, int lane,
                                                 const float* __restrict__ proj = nullptr,
                                                 uint8_t* __restrict__ ik_codes = nullptr,
-                                                float* __restrict__ ik_sigma = nullptr) {
+                                                float* __restrict__ ik_sigma = nullptr,
+                                                uint8_t* __restrict__ ik_scales4 = nullptr) {
     float k0, k1, v0, v1;
     if (ratio == 1) {
         const float2 kk = reinterpret_cast<const float2*>(k + e * kHeadDim)[lane];
@@ -115,7 +133,8 @@ __device__ __forceinline__ void quant_fp4_entry(const float* __restrict__ k,
     const int64_t row = dst_rows ? dst_rows[e] : e;
     if (proj != nullptr) {
         const float key[1] = {project_idx_key(proj, k0, k1, lane)};
-        quant_fp8_vals(key, 1, 1, row, ik_codes, ik_sigma, lane);
+        if (ik_scales4 != nullptr) quant_idx4_val(key[0], row, ik_codes, ik_scales4, lane);
+        else quant_fp8_vals(key, 1, 1, row, ik_codes, ik_sigma, lane);
     }
     codes[row * 128 + lane] = (uint8_t)kb;
     codes[row * 128 + 64 + lane] = (uint8_t)vb;
@@ -158,6 +177,16 @@ __global__ __launch_bounds__(256) void k_quant_fp8(const float* __restrict__ x, 
     quant_fp8_row(x, r, dim, layout, dst_rows, codes, sigma, threadIdx.x & 63);
 }
 
+__global__ __launch_bounds__(256) void k_quant_idx4(const float* __restrict__ x, int64_t n_rows,
+                                                    const int64_t* __restrict__ dst_rows,
+                                                    uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ scales) {
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= n_rows) return;  // uniform over the wave
+    const int lane = threadIdx.x & 63;
+    quant_idx4_val(x[r * 64 + lane], dst_rows ? dst_rows[r] : r, codes, scales, lane);
+}
+
 // The write path of new entries in one launch: wave w < n_ent quantises entry
 // w as k_quant_fp4 does, the following waves the rows of the FP8 jobs in
 // order, each as k_quant_fp8 does.
@@ -166,7 +195,7 @@ __global__ __launch_bounds__(256) void k_write_entries(Fp4Job f, Fp8Jobs j) {
     int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (w < f.n_ent) {
         quant_fp4_entry(f.k, f.v, w, f.ratio, f.rope_cs, f.dst_rows, f.codes, f.scales, lane,
-                        f.proj, f.ik_codes, f.ik_sigma);
+                        f.proj, f.ik_codes, f.ik_sigma, f.ik_scales4);
         return;
     }
     w -= f.n_ent;
@@ -263,6 +292,14 @@ hipError_t launch_quant_fp8(const float* x, int64_t n_rows, int dim, int layout,
     const unsigned grid = (unsigned)((n_rows + 3) / 4);
     hipLaunchKernelGGL(k_quant_fp8, dim3(grid), dim3(256), 0, stream, x, n_rows, dim, layout,
                        dst_rows, codes, sigma);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_idx4(const float* x, int64_t n_rows, const int64_t* dst_rows,
+                             uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+    if (n_rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_quant_idx4, dim3((unsigned)((n_rows + 3) / 4)), dim3(256), 0, stream, x,
+                       n_rows, dst_rows, codes, scales);
     return hipGetLastError();
 }
 

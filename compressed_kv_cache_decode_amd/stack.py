@@ -88,6 +88,7 @@ class DecodeStack:
         write_entries(k_new, v_new, self.cache.kv_codes, self.cache.kv_scales, ratio=ratio,
                       rope_cs=rope_cs, dst_rows=rows_new, idx_proj=idx_proj,
                       ik_codes=self.cache.ik_codes, ik_sigma=self.cache.ik_sigma,
+                      ik_scales4=self.cache.ik_scales4,
                       fp8_jobs=[dict(x=win_k, codes=swa_k.view(L * self.B * 128, HEAD_DIM),
                                      sigma=swa_ks.view(-1), dst_rows=win_rows),
                                 dict(x=win_v, codes=swa_v.view(L * self.B * 128, HEAD_DIM),

@@ -86,6 +86,8 @@ extern "C" {
 #define CSA2_E_HIP (-4)          /* HIP runtime reported a launch error */
 
 /* csa2_quant_fp8 layouts */
+#define CSA2_IDX4_CODE_BYTES 32  /* FP4 indexer key: E2M1 codes per position */
+#define CSA2_IDX4_SCALE_BYTES 4  /* FP4 indexer key: E4M3 scales per position */
 #define CSA2_FP8_ROWS 0          /* codes [row][dim] */
 #define CSA2_FP8_IDX_TILED 1     /* dim == 64, indexer-K tile layout above */
 
@@ -261,6 +263,64 @@ int csa2_index_reindex(const uint8_t* ik_codes, const float* ik_sigma, int64_t c
                        const float* iq, const float* iw, const int32_t* n_vis,
                        const int32_t* pool_idx, int pool_blocks, int topk, int32_t* topk_idx,
                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * FP4 indexer key -- a second format for the indexer K ("DeepSeek V4.1
+ * Flash: architecture study notes" section 4: the FP4 main KV builds on the
+ * previous generation's FP4 indexer key).  The key is stored in the main KV's
+ * FP4 format: E2M1 codes (low nibble = even channel) with one E4M3 scale per
+ * 16 channels and no per-position scale, 32 + 4 = 36 bytes per position
+ * against 68 for the FP8 key.  Layout, row r = b*cap + p:
+ *   ik4_codes   tiles of 64 positions, two 1 KB planes per tile: plane h holds
+ *               the 16 code bytes of channels 32h..32h+31 of each of the 64
+ *               positions, at byte ((r/64)*2 + h)*1024 + (r%64)*16;
+ *   ik4_scales  [B*cap][4] E4M3 bytes, byte g scaling channels 16g..16g+15.
+ * Quantisation of a 64-channel key: per group scale = RNE_E4M3(fl(amax/6))
+ * (saturating), code = RNE_E2M1(fl(x/scale)), ties to the even code, a zero
+ * scale giving signed-zero codes (the rule of csa2_quant_fp4).
+ * Score of position s (the query quantised as in csa2_index_full):
+ *   inner_hg = fp32 sum over the 16 channels of group g, ascending, of
+ *              E4M3(q_hc) * E2M1(k_sc) (each product exact), from +0;
+ *   dot_h    = fused multiply-add chain over g = 0..3 of scale_g * inner_hg,
+ *              from +0;
+ *   score    = w'_0 r_0 + w'_1 r_1 + w'_2 r_2 + w'_3 r_3 (left to right, each
+ *              product rounded), r_h = max(dot_h, +0).
+ * Blocks, pools, ranking, ties and outputs are those of the FP8 calls.
+ */
+
+/* csa2_quant_idx_fp4 -- FP4 indexer keys of x [n_rows][64] fp32, written at
+ * rows dst_rows[r] (or r) of ik4_codes / ik4_scales (not checked).
+ * CSA2_E_ARG for n_rows < 0 or a NULL array with n_rows > 0. */
+int csa2_quant_idx_fp4(const float* x, int64_t n_rows, const int64_t* dst_rows,
+                       uint8_t* ik4_codes, uint8_t* ik4_scales, hipStream_t stream);
+
+/* csa2_write_entries_proj_fp4 -- csa2_write_entries_proj with the projected
+ * keys written as FP4 indexer keys to ik4_codes / ik4_scales. */
+int csa2_write_entries_proj_fp4(const float* k_tok, const float* v_tok, int64_t n_tok, int ratio,
+                                const float* rope_cs, const int64_t* dst_rows, uint8_t* kv_codes,
+                                uint8_t* kv_scales, const float* idx_proj, uint8_t* ik4_codes,
+                                uint8_t* ik4_scales, const csa2_fp8_job* jobs, int n_jobs,
+                                hipStream_t stream);
+
+/* csa2_index_full_fp4 -- csa2_index_full over FP4 indexer keys (any Q; the
+ * scan is the exact VALU scan for every Q).  Arguments, outputs, workspace
+ * and errors as csa2_index_full; _timed brackets the scan as
+ * csa2_index_full_timed does. */
+int csa2_index_full_fp4(const uint8_t* ik4_codes, const uint8_t* ik4_scales, int64_t cap, int B,
+                        int Q, const float* iq, const float* iw, const int32_t* n_vis, int topk,
+                        int pool_blocks, int32_t* topk_idx, int32_t* pool_idx, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+int csa2_index_full_fp4_timed(const uint8_t* ik4_codes, const uint8_t* ik4_scales, int64_t cap,
+                              int B, int Q, const float* iq, const float* iw,
+                              const int32_t* n_vis, int topk, int pool_blocks, int32_t* topk_idx,
+                              int32_t* pool_idx, void* ws, size_t ws_bytes, hipStream_t stream,
+                              hipEvent_t scan_start, hipEvent_t scan_stop);
+
+/* csa2_index_reindex_fp4 -- csa2_index_reindex over FP4 indexer keys. */
+int csa2_index_reindex_fp4(const uint8_t* ik4_codes, const uint8_t* ik4_scales, int64_t cap,
+                           int B, int Q, const float* iq, const float* iw, const int32_t* n_vis,
+                           const int32_t* pool_idx, int pool_blocks, int topk, int32_t* topk_idx,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * csa2_sparse_attn_decode -- sparse attention of one decode query per

@@ -42,3 +42,17 @@ def row_rel_err(out, ref):
     num = np.abs(out - ref).max(axis=-1)
     den = np.abs(ref).max(axis=-1)
     return num / np.maximum(den, 1e-30)
+
+
+def tile_ik4(codes):
+    """Oracle FP4 indexer codes [B][cap][32] -> library two-plane tile layout
+    (flat uint8): plane h of tile t, lane i at ((t*2 + h)*64 + i)*16."""
+    B, cap, d = codes.shape
+    assert d == IDX_DIM // 2 and cap % 64 == 0
+    t = codes.reshape(B * cap // 64, 64, 2, 16)          # [tile][lane][h][16]
+    return np.ascontiguousarray(t.transpose(0, 2, 1, 3)).reshape(-1)
+
+
+def untile_ik4(flat, B, cap):
+    t = np.asarray(flat).reshape(B * cap // 64, 2, 64, 16)  # [tile][h][lane][16]
+    return np.ascontiguousarray(t.transpose(0, 2, 1, 3)).reshape(B, cap, IDX_DIM // 2)
