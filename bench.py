@@ -71,12 +71,19 @@ def attn_bytes(n_sel, n_swa, H):
     return 144 * n_sel + 264 * n_swa + 2 * H * 128 * 4
 
 
+def idx_key_bytes(wl):
+    """Bytes of one position's indexer key: FP8 (64 codes + fp32 sigma) or FP4
+    (32 code bytes + 4 E4M3 scales)."""
+    return 36 if wl.idx_fp4 else 68
+
+
 def step_bytes(wl):
     """Algorithmic HBM bytes of one stack step (all queries)."""
     B, N, H = wl.B, wl.n_ent, wl.H
-    scan = 68 * N * B
+    key = idx_key_bytes(wl)
+    scan = key * N * B
     n_x = wl.plan.count("X")
-    reindex = n_x * 68 * min(wl.pool_blocks * 8, N) * B
+    reindex = n_x * key * min(wl.pool_blocks * 8, N) * B
     attn = len(wl.plan) * B * attn_bytes(min(wl.topk, N), 128, H)
     write = B * (2 * 128 * 4 + 144 + 64 * 4 + 68)
     return scan + reindex + attn + write, scan
@@ -115,7 +122,7 @@ def build_sets(args, wl, inp):
     B, N = wl.B, wl.n_ent
     cap = (N + 63) // 64 * 64
     log(f"writing the caches with the library: B={B} entries={N} ratio={wl.ratio}")
-    cache0 = csa2.Cache(B, cap)
+    cache0 = csa2.Cache(B, cap, idx_fp4=wl.idx_fp4)
     for b in range(B):
         rows = cache0.rows(b, np.arange(N))
         k = torch.from_numpy(inp.k_tok[b]).cuda()
@@ -123,8 +130,12 @@ def build_sets(args, wl, inp):
         cs = torch.from_numpy(csa2.rope_table(np.arange(N))).cuda() if wl.ratio == 1 else None
         csa2.quant_fp4(k, v, cache0.kv_codes, cache0.kv_scales, ratio=wl.ratio, rope_cs=cs,
                        dst_rows=rows)
-        csa2.quant_fp8(torch.from_numpy(inp.idx_k[b]).cuda(), cache0.ik_codes, cache0.ik_sigma,
-                       layout=csa2.FP8_IDX_TILED, dst_rows=rows)
+        ik = torch.from_numpy(inp.idx_k[b]).cuda()
+        if wl.idx_fp4:
+            csa2.quant_idx_fp4(ik, cache0.ik_codes, cache0.ik_scales4, dst_rows=rows)
+        else:
+            csa2.quant_fp8(ik, cache0.ik_codes, cache0.ik_sigma, layout=csa2.FP8_IDX_TILED,
+                           dst_rows=rows)
         del k, v, cs
     L = len(wl.plan)
     swk = torch.empty((L, B, 128, 128), dtype=torch.uint8, device="cuda")
@@ -164,10 +175,11 @@ def build_sets(args, wl, inp):
         del dev_inputs["rope_new"]
     sets = []
     for s in range(args.cache_sets):
-        cache = cache0 if s == 0 else csa2.Cache(B, cap)
+        cache = cache0 if s == 0 else csa2.Cache(B, cap, idx_fp4=wl.idx_fp4)
         if s:
-            for name in ("kv_codes", "kv_scales", "ik_codes", "ik_sigma"):
+            for name in ("kv_codes", "kv_scales", "ik_codes"):
                 getattr(cache, name).copy_(getattr(cache0, name))
+            cache.ik_aux.copy_(cache0.ik_aux)
         ss = StepSet(csa2, DecodeStack, cache, wl, dev_inputs)
         if "rope_new" not in ss.inp:
             ss.inp["rope_new"] = None
@@ -326,7 +338,7 @@ def run_chunk_bench(args, wl):
     scan_tfs = flops / (scan_mean * 1e-3) / 1e12
     peak = 2500.0
     rl = {"bound": "mfma", "achieved": round(scan_tfs, 2), "peak": peak, "unit": "TFLOP/s",
-          "frac": round(scan_tfs / peak, 4), "traffic": load_traffic().get("k_scan_mma"),
+          "frac": round(scan_tfs / peak, 4), "traffic": load_traffic(wl.name).get("k_scan_mma"),
           "kernel": "k_scan_mma (Full-layer indexer bounds of 128 chunk queries, fp16 MFMA)",
           "flops_per_launch": flops, "mean_us": round(scan_mean * 1e3, 2)}
     return {
@@ -469,10 +481,14 @@ def cpu_baseline(args, wl, inp):
     threads = oracle.num_threads()
     log(f"cpu baseline: oracle caches for {S} sequences ({threads} threads)")
 
+    quant_ik = oracle.idx4_quant_rows if wl.idx_fp4 else oracle.quant_fp8_rows
+    full_batch = oracle.index_full4_batch if wl.idx_fp4 else oracle.index_full_batch
+    reindex_batch = oracle.index_reindex4_batch if wl.idx_fp4 else oracle.index_reindex_batch
+
     def prep(b):
         cs = oracle.rope_table(np.arange(N)) if wl.ratio == 1 else None
         c, s = oracle.quant_fp4(inp.k_tok[b], inp.v_tok[b], wl.ratio, cs)
-        ik, iks = oracle.quant_fp8_rows(inp.idx_k[b])
+        ik, iks = quant_ik(inp.idx_k[b])
         return c, s, ik, iks
 
     with cf.ThreadPoolExecutor(max_workers=threads) as ex:
@@ -495,21 +511,22 @@ def cpu_baseline(args, wl, inp):
     # write path: each sequence's new entry (FP4 record, projected indexer
     # key) and every layer's window token at its ring slot
     for b in range(S):
-        c1, s1, ik1, is1 = oracle.write_entries_proj(inp.k_tok[b, tok:tok + r],
-                                                     inp.v_tok[b, tok:tok + r], inp.proj, r,
-                                                     cs_new)
+        c1, s1 = oracle.quant_fp4(inp.k_tok[b, tok:tok + r], inp.v_tok[b, tok:tok + r], r,
+                                  cs_new)
+        ik1, is1 = quant_ik(oracle.project_idx(
+            oracle.entry_k(inp.k_tok[b, tok:tok + r], r, cs_new), inp.proj))
         codes[b, N - 1], scales[b, N - 1], ikc[b, N - 1], iks[b, N - 1] = c1[0], s1[0], ik1[0], is1[0]
     swk[:, :, slot], sks[:, :, slot] = oracle.quant_fp8_rows(inp.swa_k[:, :S, slot])
     swv[:, :, slot], svs[:, :, slot] = oracle.quant_fp8_rows(inp.swa_v[:, :S, slot])
     pool, cur, k = None, None, 0
     for layer, mode in enumerate(wl.plan):
         if mode == "F":
-            cur, pool = oracle.index_full_batch(ikc, iks, inp.iq[k, :S, None], inp.iw[k, :S, None],
-                                                nv, wl.topk, wl.pool_blocks)
+            cur, pool = full_batch(ikc, iks, inp.iq[k, :S, None], inp.iw[k, :S, None], nv,
+                                   wl.topk, wl.pool_blocks)
             k += 1
         elif mode == "X":
-            cur = oracle.index_reindex_batch(ikc, iks, inp.iq[k, :S, None], inp.iw[k, :S, None],
-                                             nv, pool, wl.topk)
+            cur = reindex_batch(ikc, iks, inp.iq[k, :S, None], inp.iw[k, :S, None], nv, pool,
+                                wl.topk)
             k += 1
         oracle.attn_decode_batch(inp.q[layer, :S], codes, scales, cur[:, 0], swk[layer],
                                  swv[layer], sks[layer], svs[layer], inp.swa_len[:S], sm)
@@ -538,6 +555,7 @@ def roofline_entry(name, what, ms_list, bytes_per_launch, launches_per_step, ms_
 KERNEL_SOURCES = {
     "k_attn": ["csa2_attn.hip", "csa2_device.hpp", "csa2_internal.hpp"],
     "k_scan": ["csa2_index.hip", "csa2_device.hpp", "csa2_internal.hpp"],
+    "k_scan_fp4": ["csa2_index.hip", "csa2_device.hpp", "csa2_internal.hpp"],
     "k_scan_mma": ["csa2_chunk.hip", "csa2_device.hpp", "csa2_internal.hpp"],
 }
 
@@ -551,9 +569,10 @@ def kernel_source_hash(name):
     return h.hexdigest()
 
 
-def load_traffic():
+def load_traffic(workload=None):
     """Measured HBM bytes per launch from profiles/traffic.json, per kernel, kept
-    only where the kernel's sources still hash to what was profiled."""
+    only where the kernel's sources still hash to what was profiled and, when
+    `workload` is given, the counters were taken on that workload."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return {}
@@ -561,6 +580,8 @@ def load_traffic():
         data = json.load(fh)
     out = {}
     for name, rec in data.get("kernels", {}).items():
+        if workload is not None and rec.get("workload") != workload:
+            continue
         if name in KERNEL_SOURCES and rec.get("source_sha256") == kernel_source_hash(name):
             out[name] = rec["bytes_per_launch"]
     return out
@@ -753,12 +774,13 @@ def main():
     ms_per_step = elapsed / args.steps * 1e3
     value = wl.B * args.steps / elapsed
     attn_launch_bytes = wl.B * attn_bytes(min(wl.topk, wl.n_ent), 128, wl.H)
-    traffic = load_traffic()
+    traffic = load_traffic(wl.name)
     rooflines = [
         roofline_entry("k_attn", "sparse attention, one launch per layer", kernel_ms["attn"],
                        attn_launch_bytes, len(wl.plan), ms_per_step, traffic),
-        roofline_entry("k_scan", "Full-layer indexer scan", kernel_ms["scan"], scan_bytes, 1,
-                       ms_per_step, traffic),
+        roofline_entry("k_scan_fp4" if wl.idx_fp4 else "k_scan",
+                       "Full-layer indexer scan" + (", FP4 keys" if wl.idx_fp4 else ""),
+                       kernel_ms["scan"], scan_bytes, 1, ms_per_step, traffic),
     ]
     dominant = max(rooflines, key=lambda r: r["us_per_step"])
     result = {
@@ -775,6 +797,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "sequences": wl.B, "entries": wl.n_ent,
+                   "indexer_key": "fp4" if wl.idx_fp4 else "fp8",
                    "layers": len(wl.plan), "plan": wl.plan, "heads": wl.H, "topk": wl.topk,
                    "pool_blocks": wl.pool_blocks, "window": 128, "cache_sets": args.cache_sets,
                    "launch": "eager" if args.no_graph else "hip-graph"},

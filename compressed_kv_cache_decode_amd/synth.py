@@ -51,6 +51,7 @@ class Workload:
     planted: bool = False
     topk: int = TOPK
     extra: dict = field(default_factory=dict)
+    idx_fp4: bool = False  # indexer keys in the FP4 format (36 B) instead of FP8 (68 B)
 
     @property
     def n_tok(self):
@@ -66,6 +67,12 @@ WORKLOADS = {
                                    H=64, plan=DECODER_PLAN, pool_blocks=POOL_BLOCKS),
     "decoder_stack_1m": Workload("decoder_stack_1m", 1003, B=4, n_ent=1048576, ratio=1, H=64,
                                  plan=DECODER_PLAN, pool_blocks=POOL_BLOCKS, planted=True),
+    "decoder_stack_128k_fp4idx": Workload("decoder_stack_128k_fp4idx", 1002, B=16,
+                                          n_ent=131072, ratio=1, H=64, plan=DECODER_PLAN,
+                                          pool_blocks=POOL_BLOCKS, idx_fp4=True),
+    "decoder_stack_1m_fp4idx": Workload("decoder_stack_1m_fp4idx", 1003, B=4, n_ent=1048576,
+                                        ratio=1, H=64, plan=DECODER_PLAN,
+                                        pool_blocks=POOL_BLOCKS, planted=True, idx_fp4=True),
     "replay_chunk_128k": Workload("replay_chunk_128k", 1004, B=1, n_ent=131072, ratio=1, H=64,
                                   plan="F", pool_blocks=0, Q=128),
     "replay_stack_128k": Workload("replay_stack_128k", 1005, B=1, n_ent=131072, ratio=1, H=64,
