@@ -14,7 +14,7 @@ import pytest
 import torch
 
 from compressed_kv_cache_decode_amd import synth
-from gpu_util import dev, host, row_rel_err, untile_ik
+from gpu_util import dev, host, row_rel_err, untile_ik, untile_ik4
 
 pytestmark = pytest.mark.gpu
 SM = 1.0 / math.sqrt(128.0)
@@ -25,17 +25,21 @@ def say(msg):
 
 
 def build_cache_on_gpu(gpu, inp, cap, rope=False):
-    """Write the main KV and indexer K of every sequence with the library."""
+    """Write the main KV and indexer K of every sequence with the library
+    (indexer keys in the workload's format)."""
     B, n_tok = inp.k_tok.shape[:2]
     n_ent = n_tok // inp.wl.ratio
-    cache = gpu.Cache(B, cap)
+    cache = gpu.Cache(B, cap, idx_fp4=inp.wl.idx_fp4)
     for b in range(B):
         rows = cache.rows(b, np.arange(n_ent))
         cs = dev(gpu.rope_table(np.arange(n_ent))) if rope else None
         gpu.quant_fp4(dev(inp.k_tok[b]), dev(inp.v_tok[b]), cache.kv_codes, cache.kv_scales,
                       ratio=inp.wl.ratio, rope_cs=cs, dst_rows=rows)
-        gpu.quant_fp8(dev(inp.idx_k[b]), cache.ik_codes, cache.ik_sigma, layout=gpu.FP8_IDX_TILED,
-                      dst_rows=rows)
+        if inp.wl.idx_fp4:
+            gpu.quant_idx_fp4(dev(inp.idx_k[b]), cache.ik_codes, cache.ik_scales4, dst_rows=rows)
+        else:
+            gpu.quant_fp8(dev(inp.idx_k[b]), cache.ik_codes, cache.ik_sigma,
+                          layout=gpu.FP8_IDX_TILED, dst_rows=rows)
     return cache
 
 
@@ -58,8 +62,12 @@ def oracle_stack(oracle_mod, inp, b, topk, pool_blocks, plan, rope=False, new_en
     n_ent = inp.k_tok.shape[1] // inp.wl.ratio
     cs = oracle_mod.rope_table(np.arange(n_ent)) if rope else None
     codes, scales = oracle_mod.quant_fp4(inp.k_tok[b], inp.v_tok[b], inp.wl.ratio, cs)
-    ikc, iks = oracle_mod.quant_fp8_rows(inp.idx_k[b])
+    fp4 = inp.wl.idx_fp4
+    ikc, iks = (oracle_mod.idx4_quant_rows if fp4 else oracle_mod.quant_fp8_rows)(inp.idx_k[b])
+    full = oracle_mod.index_full4 if fp4 else oracle_mod.index_full
+    reindex = oracle_mod.index_reindex4 if fp4 else oracle_mod.index_reindex
     if new_entry_proj is not None:
+        assert not fp4
         r = inp.wl.ratio
         _, _, ikc[-1:], iks[-1:] = oracle_mod.write_entries_proj(
             inp.k_tok[b, -r:], inp.v_tok[b, -r:], new_entry_proj, r,
@@ -69,11 +77,10 @@ def oracle_stack(oracle_mod, inp, b, topk, pool_blocks, plan, rope=False, new_en
     cur, pool, k = None, None, 0
     for layer, mode in enumerate(plan):
         if mode == "F":
-            cur, pool = oracle_mod.index_full(ikc, iks, n_ent, inp.iq[k, b], inp.iw[k, b], topk,
-                                              pool_blocks)
+            cur, pool = full(ikc, iks, n_ent, inp.iq[k, b], inp.iw[k, b], topk, pool_blocks)
             k += 1
         elif mode == "X":
-            cur = oracle_mod.index_reindex(ikc, iks, n_ent, inp.iq[k, b], inp.iw[k, b], pool, topk)
+            cur = reindex(ikc, iks, n_ent, inp.iq[k, b], inp.iw[k, b], pool, topk)
             k += 1
         sk, sks = oracle_mod.quant_fp8_rows(inp.swa_k[layer, b])
         sv, svs = oracle_mod.quant_fp8_rows(inp.swa_v[layer, b])
@@ -108,8 +115,12 @@ def run_stack_case(gpu, oracle_mod, wl, n_ent=None, B=None, layers=None, sample=
     for layer, src in enumerate(st.sources):
         assert used[layer].data_ptr() == used[src].data_ptr()
     kvc, kvs = host(cache.kv_codes), host(cache.kv_scales)
-    ikc_all = untile_ik(host(cache.ik_codes), B, cap)
-    iks_all = host(cache.ik_sigma).reshape(B, cap)
+    if wl.idx_fp4:
+        ikc_all = untile_ik4(host(cache.ik_codes), B, cap)
+        iks_all = host(cache.ik_scales4).reshape(B, cap, 4)
+    else:
+        ikc_all = untile_ik(host(cache.ik_codes), B, cap)
+        iks_all = host(cache.ik_sigma).reshape(B, cap)
     tk_all = [host(t) for t in used]
     out_all, lse_all = host(st.out), host(st.lse)
     sample = range(B) if sample is None else sample
@@ -154,6 +165,24 @@ def test_decoder_stack_1m_full_size(gpu, oracle_mod):
     the planted blocks must dominate the Full layer's pool."""
     wl = synth.WORKLOADS["decoder_stack_1m"]
     inp, tk_all = run_stack_case(gpu, oracle_mod, wl, sample=[0, 3], layers=5)
+    for b in range(wl.B):
+        planted = set((inp.planted[b][:, None] * 8 + np.arange(8)).ravel().tolist())
+        sel = [p for p in tk_all[0][b, 0].tolist() if p >= 0]
+        assert sum(p in planted for p in sel) > 0.5 * len(sel)
+
+
+def test_decoder_stack_128k_fp4idx_full_size(gpu, oracle_mod):
+    """The 128K decoder stack with FP4 indexer keys at full size (B=16, 20
+    layers); oracle on 3 sequences."""
+    run_stack_case(gpu, oracle_mod, synth.WORKLOADS["decoder_stack_128k_fp4idx"],
+                   sample=[0, 7, 15])
+
+
+def test_decoder_stack_1m_fp4idx_full_size(gpu, oracle_mod):
+    """1M positions with FP4 indexer keys (B=4, planted clusters); oracle on one
+    sequence; the planted blocks dominate the Full layer's selection."""
+    wl = synth.WORKLOADS["decoder_stack_1m_fp4idx"]
+    inp, tk_all = run_stack_case(gpu, oracle_mod, wl, sample=[2], layers=5)
     for b in range(wl.B):
         planted = set((inp.planted[b][:, None] * 8 + np.arange(8)).ravel().tolist())
         sel = [p for p in tk_all[0][b, 0].tolist() if p >= 0]
