@@ -154,3 +154,42 @@ def test_workspace_sizes(lib):
     assert ws(5, 2, 1, 131072, 0, 0, 64) == 0
     assert ws(3, 16, 1, 131072, 512, 0, 64) == 0              # attention needs no workspace
     assert ws(4, 1, 128, 131072, 512, 0, 64) == 0
+
+
+def test_projected_write_and_fp4_key_validation(lib):
+    import compressed_kv_cache_decode_amd as csa2
+    J = csa2._Fp8Job
+    none = (J * 1)()
+    for w in (lib.csa2_write_entries_proj, lib.csa2_write_entries_proj_fp4):
+        # the FP4 part as csa2_quant_fp4, then the projection arrays
+        assert w(FAKE, FAKE, 8, 3, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, none, 0, None) == -2
+        assert w(FAKE, FAKE, 8, 1, None, None, FAKE, FAKE, None, FAKE, FAKE, none, 0, None) == -1
+        assert w(FAKE, FAKE, 8, 1, None, None, FAKE, FAKE, FAKE, None, FAKE, none, 0, None) == -1
+        assert w(FAKE, FAKE, 8, 1, None, None, FAKE, FAKE, FAKE, FAKE, None, none, 0, None) == -1
+        assert w(FAKE, FAKE, 8, 1, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, none, 4, None) == -1
+        bad = (J * 1)(J(FAKE, 4, 96, 0, None, FAKE, FAKE))
+        assert w(FAKE, FAKE, 8, 1, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, bad, 1, None) == -2
+        # no entries and no rows: nothing to launch, the projection is not needed
+        assert w(None, None, 0, 1, None, None, None, None, None, None, None, none, 0, None) == 0
+    q4 = lib.csa2_quant_idx_fp4
+    assert q4(FAKE, -1, None, FAKE, FAKE, None) == -1
+    assert q4(None, 4, None, FAKE, FAKE, None) == -1
+    assert q4(FAKE, 4, None, FAKE, None, None) == -1
+    assert q4(None, 0, None, None, None, None) == 0
+
+    f = lib.csa2_index_full_fp4
+
+    def call(cap=1024, B=2, Q=1, topk=512, pool=2048, ws=FAKE, ws_bytes=1 << 40, ptr=FAKE):
+        return f(ptr, FAKE, cap, B, Q, FAKE, FAKE, FAKE, topk, pool, FAKE, FAKE, ws, ws_bytes, None)
+
+    assert call(ptr=None) == -1
+    assert call(cap=1000) == -1
+    assert call(topk=0) == -1
+    assert call(topk=4096) == -2
+    assert call(pool=256) == -2
+    assert call(ws=None) == -3
+    assert call(ws_bytes=10) == -3
+    r = lib.csa2_index_reindex_fp4
+    assert r(FAKE, FAKE, 1024, 1, 1, FAKE, FAKE, FAKE, None, 16, 8, FAKE, FAKE, 1 << 40, None) == -1
+    assert r(FAKE, None, 1024, 1, 1, FAKE, FAKE, FAKE, FAKE, 16, 8, FAKE, FAKE, 1 << 40, None) == -1
+    assert r(FAKE, FAKE, 1024, 1, 1, FAKE, FAKE, FAKE, FAKE, 16, 8, FAKE, FAKE, 0, None) == -3
