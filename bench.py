@@ -57,6 +57,9 @@ def parse_args():
                    help="model_step workload: context lengths (tokens) of the sweep")
     p.add_argument("--model-batch", type=int, default=4,
                    help="model_step workload: sequences per step")
+    p.add_argument("--replay-tokens", type=int, default=0,
+                   help="replay_stack_128k workload: tokens per replay chunk (default 128; 2560 "
+                        "is the exact replay of a 20-layer stack)")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="also run one device-to-device copy of this many MiB (a known-size "
                         "kernel for scaling hardware byte counters)")
@@ -367,8 +370,9 @@ def run_chunk_stack_bench(args, wl):
     from compressed_kv_cache_decode_amd import synth
     from compressed_kv_cache_decode_amd.stack import ChunkStack
 
-    inp = synth.chunk_stack_inputs(wl)
-    B, N, Q, H, L = wl.B, wl.n_ent, wl.Q, wl.H, len(wl.plan)
+    Q = args.replay_tokens or wl.Q  # 128: bounded replay; 2560 = 20 x 128: exact replay
+    inp = synth.chunk_stack_inputs(wl, Q=Q)
+    B, N, H, L = wl.B, wl.n_ent, wl.H, len(wl.plan)
     cap = (N + 63) // 64 * 64
     log(f"chunk stack: writing {args.cache_sets} cache sets of {N} entries, plan {wl.plan}")
     caches = []
@@ -442,13 +446,17 @@ def run_chunk_stack_bench(args, wl):
         scan_ms = timer.durations_ms()
         timer.close()
     scan_mean = sum(scan_ms) / len(scan_ms)
-    # the Full layer's scan with pools is the exact VALU scan: 4 heads x 64
-    # sequential fp32 FMAs per (token, position) pair, 2 flops each
+    # 4 heads x 64 channels per (token, position) pair, 2 flops each; with at
+    # most 16384 blocks the Full layer with pools scores on fp16 MFMA
+    # (k_scan_mma, bounds + exact rescore), otherwise on the exact VALU scan
     flops = 2.0 * 256 * Q * N
     tfs = flops / (scan_mean * 1e-3) / 1e12
-    peak = 157.3
+    mma = Q >= 4 and cap // 8 <= 16384
+    peak = 2500.0 if mma else 157.3
+    kname = ("k_scan_mma (Full-layer indexer bounds of the chunk's tokens, fp16 MFMA)" if mma
+             else "k_scan_multi (Full-layer exact scan of the chunk's tokens)")
     return {
-        "metric": "CSA2 bounded-replay chunk through the decoder stack, queries/s (128 replayed "
+        "metric": f"CSA2 replay chunk through the decoder stack, queries/s ({Q} replayed "
                   "tokens over 128K entries, 20 layers)",
         "value": round(Q * B * args.steps / elapsed, 1), "unit": "queries/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
@@ -458,10 +466,10 @@ def run_chunk_stack_bench(args, wl):
                    "plan": wl.plan, "topk": wl.topk, "pool_blocks": wl.pool_blocks,
                    "cache_sets": args.cache_sets,
                    "launch": "eager" if args.no_graph else "hip-graph"},
-        "roofline": {"bound": "alu", "achieved": round(tfs, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tfs / peak, 4), "traffic": None,
-                     "kernel": "k_scan_multi (Full-layer exact scan of 128 tokens, with pools)",
-                     "flops_per_launch": flops, "mean_us": round(scan_mean * 1e3, 2)},
+        "roofline": {"bound": "mfma" if mma else "alu", "achieved": round(tfs, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(tfs / peak, 4),
+                     "traffic": None, "kernel": kname, "flops_per_launch": flops,
+                     "mean_us": round(scan_mean * 1e3, 2)},
     }
 
 

@@ -97,6 +97,7 @@ int validate_index_reindex(const void* ikc, const void* iks, int64_t cap, int B,
     if (rc) return rc;
     if (pool_blocks < 1 || topk < 1) return CSA2_E_ARG;
     if (pool_blocks > CSA2_MAX_POOL_BLOCKS || topk > CSA2_MAX_TOPK) return CSA2_E_UNSUPPORTED;
+    if ((int64_t)B * Q > 65535) return CSA2_E_UNSUPPORTED;  // one grid row per query
     return CSA2_OK;
 }
 
@@ -491,7 +492,6 @@ __attribute__((visibility("default"))) int csa2_sparse_attn_chunk(
     int rc = validate_attn(q, B, Q, H, kv_codes, kv_scales, cap, topk_idx, topk, swa_k, swa_v,
                            swa_ks, swa_vs, sm_scale, out, lse);
     if (rc) return rc;
-    if (Q > CSA2_WINDOW) return CSA2_E_UNSUPPORTED;  // a chunk replays at most one window
     const int64_t nq = (int64_t)B * Q;
     const size_t need = attn_workspace_bytes(nq, H, topk, Q);
     if (need > 0 && (!ws || ws_bytes < need)) return CSA2_E_WORKSPACE;

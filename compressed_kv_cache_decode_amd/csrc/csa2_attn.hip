@@ -60,7 +60,7 @@ constexpr int kVPitch = 144;        // fp16 per V row in LDS (128 + 16)
 constexpr int kMergePitch = kHeadDim + 4;  // fp32 per merged output row in LDS
 constexpr int kXcds = 8;
 constexpr int kCusPerChip = 256;
-constexpr int kMaxWindow = 128;     // window rows per sequence (decode 128, chunk <= 128)
+constexpr int kMaxWindow = 128;     // window tokens a query attends to
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag the true max
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -94,6 +94,7 @@ struct SeqView {
     int64_t b;
     int topk;
     int swa_rows;
+    int swa_start;  // first window row of this query (chunk: the last 128 tokens up to it)
     int swa_len;
     int n_tiles_global;
 };
@@ -114,7 +115,7 @@ __device__ __forceinline__ int32_t entry_position(int32_t pos, int e) {
 // window row of token e of window tile t, or -1
 __device__ __forceinline__ int64_t window_row(const SeqView& s, int t, int e) {
     const int tok = (t - s.n_tiles_global) * kTile + e;
-    return tok < s.swa_len ? s.b * s.swa_rows + tok : -1;
+    return tok < s.swa_len ? s.b * s.swa_rows + s.swa_start + tok : -1;
 }
 
 // Raw bytes of one tile held by one lane (c = lane & 15, g = lane >> 4).
@@ -462,9 +463,13 @@ __global__ __launch_bounds__(kWaves * 64) void k_attn(AttnArgs a, int n_tiles_gl
     }
     if (a.swa_len != nullptr) {
         const int sl = a.swa_len[s.b];
+        s.swa_start = 0;
         s.swa_len = sl < 0 ? 0 : (sl > a.swa_rows ? a.swa_rows : sl);
     } else {
-        s.swa_len = (int)(bq % a.Q) + 1;  // chunk query i sees window tokens [0, i]
+        // chunk query i sees the window tokens [max(0, i - 127), i]
+        const int i = (int)(bq % a.Q);
+        s.swa_start = i + 1 > kMaxWindow ? i + 1 - kMaxWindow : 0;
+        s.swa_len = i + 1 - s.swa_start;
     }
     const int n_tiles = n_tiles_global + (s.swa_len + kTile - 1) / kTile;
     if (t0 >= n_tiles_global && t0 < n_tiles) fetch_tile<STAGE>(s, t0, -1, lane, ra);
@@ -481,7 +486,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_attn(AttnArgs a, int n_tiles_gl
         float wv = 0.0f;
         const int tok = tid & (kMaxWindow - 1);
         if (tid < 2 * kMaxWindow && tok < s.swa_len)
-            wv = (tid < kMaxWindow ? a.swks : a.swvs)[s.b * s.swa_rows + tok];
+            wv = (tid < kMaxWindow ? a.swks : a.swvs)[s.b * s.swa_rows + s.swa_start + tok];
         if (tid < 2 * kMaxWindow) win_l[tid] = wv;
     }
     __syncthreads();
@@ -586,7 +591,10 @@ __global__ __launch_bounds__(kWaves * 64) void k_attn(AttnArgs a, int n_tiles_gl
 hipError_t launch_attn(const AttnArgs& a, void* /*ws*/, size_t /*ws_bytes*/, hipStream_t stream,
                        hipEvent_t start, hipEvent_t stop) {
     if (a.n_q <= 0) return hipSuccess;
-    if (a.topk > kMaxTopk || a.swa_rows > kMaxWindow || a.H % kGroupHeads != 0)
+    // decode: the window length is clamped to swa_rows, so at most 128 rows;
+    // chunk: swa_rows is the chunk length, each query reads at most 128 rows
+    if (a.topk > kMaxTopk || (a.swa_len != nullptr && a.swa_rows > kMaxWindow) ||
+        a.H % kGroupHeads != 0)
         return hipErrorInvalidValue;
     const int n_tiles_global = (a.topk + kTile - 1) / kTile;
     const int G = a.H / kGroupHeads;

@@ -256,7 +256,8 @@ int csa2_index_full_timed(const uint8_t* ik_codes, const float* ik_sigma, int64_
  *   pool_idx   [B][Q][pool_blocks] as written by csa2_index_full (-1 ignored).
  *   topk_idx   [B][Q][topk] out: best min(topk, #visible pool positions)
  *              positions inside the pool, ascending, then -1.
- * Same score and ranking as csa2_index_full.  ws: at least
+ * Same score and ranking as csa2_index_full.  B*Q <= 65535 (else
+ * CSA2_E_UNSUPPORTED).  ws: at least
  *   csa2_workspace_size(CSA2_OP_INDEX_REINDEX, B, Q, cap, topk, pool_blocks, 0).
  */
 int csa2_index_reindex(const uint8_t* ik_codes, const float* ik_sigma, int64_t cap, int B, int Q,
@@ -398,9 +399,11 @@ int csa2_sparse_attn_decode_reuse(const float* q, int B, int H, const uint8_t* k
  * ("DeepSeek V4.1 Flash: architecture study notes" section 5: the decoder
  * replays only the last 128 tokens of the prompt to rebuild its SWA state;
  * earlier local dependencies are cut off).
- *   q          [B][Q][H][128] fp32, Q <= 128; topk_idx [B][Q][topk].
+ *   q          [B][Q][H][128] fp32, B*Q <= 65535; topk_idx [B][Q][topk].
  *   swa_k, swa_v    [B][Q][128] E4M3, the chunk's own tokens; swa_ks,
- *              swa_vs [B][Q].  Query i attends to chunk tokens [0, i].
+ *              swa_vs [B][Q].  Query i attends to the chunk tokens
+ *              [max(0, i - 127), i]: the last 128 up to itself (all of
+ *              [0, i] in a chunk of at most 128 tokens).
  *   out [B][Q][H][128], lse [B][Q][H].  Otherwise as the decode call.
  * ws: csa2_workspace_size(CSA2_OP_ATTN_CHUNK, B, Q, cap, topk, 0, H) bytes
  * (currently 0; ws may then be NULL).

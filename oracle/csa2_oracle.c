@@ -22,6 +22,7 @@
 #define IDX_HEADS 4
 #define IDX_DIM 64
 #define HEAD_DIM 128
+#define WINDOW 128
 #define BLOCK 8
 
 int csa2o_num_threads(void) {
@@ -646,9 +647,13 @@ void csa2o_attn_chunk_batch(const float* q, int B, int Q, int H, const uint8_t* 
     for (int64_t bq = 0; bq < (int64_t)B * Q; ++bq) {
         int64_t b = bq / Q;
         int i = (int)(bq % Q);
+        /* the window of chunk token i: the last 128 chunk tokens up to and
+         * including it ([notes] section 1: a 128-token window per layer) */
+        int start = i + 1 > WINDOW ? i + 1 - WINDOW : 0;
+        int64_t w0 = b * Q + start;
         csa2o_attn(q + bq * H * HEAD_DIM, H, codes + b * cap * 128, scales + b * cap * 16,
-                   idx + bq * topk, topk, swa_k + b * Q * HEAD_DIM, swa_v + b * Q * HEAD_DIM,
-                   swa_ks + b * Q, swa_vs + b * Q, i + 1, sm_scale, out + bq * H * HEAD_DIM,
+                   idx + bq * topk, topk, swa_k + w0 * HEAD_DIM, swa_v + w0 * HEAD_DIM,
+                   swa_ks + w0, swa_vs + w0, i + 1 - start, sm_scale, out + bq * H * HEAD_DIM,
                    lse + bq * H);
     }
 }

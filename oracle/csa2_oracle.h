@@ -115,7 +115,7 @@ void csa2o_attn_decode_batch(const float* q, int B, int H, const uint8_t* codes,
                              const float* swa_vs, const int32_t* swa_len, float sm_scale,
                              float* out, float* lse);
 /* batched chunk: q [B][Q][H][128], idx [B][Q][topk], chunk SWA [B][Q][128];
- * query i sees chunk SWA tokens [0, i]. */
+ * query i sees chunk SWA tokens [max(0, i - 127), i]. */
 void csa2o_attn_chunk_batch(const float* q, int B, int Q, int H, const uint8_t* codes,
                             const uint8_t* scales, int64_t cap, const int32_t* idx, int topk,
                             const uint8_t* swa_k, const uint8_t* swa_v, const float* swa_ks,

@@ -193,3 +193,8 @@ def test_projected_write_and_fp4_key_validation(lib):
     assert r(FAKE, FAKE, 1024, 1, 1, FAKE, FAKE, FAKE, None, 16, 8, FAKE, FAKE, 1 << 40, None) == -1
     assert r(FAKE, None, 1024, 1, 1, FAKE, FAKE, FAKE, FAKE, 16, 8, FAKE, FAKE, 1 << 40, None) == -1
     assert r(FAKE, FAKE, 1024, 1, 1, FAKE, FAKE, FAKE, FAKE, 16, 8, FAKE, FAKE, 0, None) == -3
+
+
+def test_reindex_query_count_limit(lib):
+    r = lib.csa2_index_reindex
+    assert r(FAKE, FAKE, 1024, 2, 40000, FAKE, FAKE, FAKE, FAKE, 16, 8, FAKE, FAKE, 1 << 40, None) == -2

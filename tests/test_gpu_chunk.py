@@ -153,8 +153,9 @@ def run_chunk_stack(gpu, oracle_mod, n_ent, Q, H, layers, sample, B=1):
                 np.testing.assert_array_equal(tk_all[layer][b, i], cur,
                                               err_msg=f"layer {layer} ({mode}), token {i}")
                 (sk, sks_r), (sv, svs_r) = wins[layer]
-                o, l = oracle_mod.attn(inp.q[layer, b, i], codes, scales, cur, sk, sv, sks_r,
-                                       svs_r, i + 1, SM)
+                lo = max(0, i - 127)  # the window: the last 128 chunk tokens up to i
+                o, l = oracle_mod.attn(inp.q[layer, b, i], codes, scales, cur, sk[lo:], sv[lo:],
+                                       sks_r[lo:], svs_r[lo:], i + 1 - lo, SM)
                 assert row_rel_err(out_h[layer, b, i], o).max() <= 2e-3, (layer, i)
                 np.testing.assert_allclose(lse_h[layer, b, i], l, rtol=2e-3, atol=2e-3)
 
@@ -166,3 +167,10 @@ def test_chunk_stack_small(gpu, oracle_mod):
 
 def test_chunk_stack_128k_full_size(gpu, oracle_mod):
     run_chunk_stack(gpu, oracle_mod, n_ent=131072, Q=128, H=64, layers=20, sample=[0, 77, 127])
+
+
+def test_chunk_stack_longer_than_the_window(gpu, oracle_mod):
+    """A replay chunk of 300 tokens (the exact replay of several windows):
+    tokens past the 128th attend to the last 128 chunk tokens up to themselves."""
+    run_chunk_stack(gpu, oracle_mod, n_ent=20000, Q=300, H=16, layers=6,
+                    sample=[0, 127, 128, 129, 250, 299], B=1)

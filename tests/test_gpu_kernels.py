@@ -519,7 +519,8 @@ def test_sparse_attn_decode_ignores_out_of_range_indices(gpu, oracle_mod):
     assert row_rel_err(host(out)[0], out_ref[0]).max() <= ATOL_ROW
 
 
-@pytest.mark.parametrize("B,Q,cap,H", [(1, 128, 2048, 64), (2, 37, 1024, 16)])
+@pytest.mark.parametrize("B,Q,cap,H", [(1, 128, 2048, 64), (2, 37, 1024, 16),
+                                       (1, 300, 4096, 16)])   # window slides past 128 tokens
 def test_sparse_attn_chunk(gpu, oracle_mod, B, Q, cap, H):
     say(f"attn_chunk B={B} Q={Q} cap={cap} H={H}")
     cache, codes, scales, sk, sv, sks, svs, q = make_attn_case(gpu, oracle_mod, B, cap, H, 800, Q=Q)

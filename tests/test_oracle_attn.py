@@ -121,3 +121,29 @@ def test_chunk_batch_is_per_query_attention_with_causal_window(oracle_mod):
                                  svs[0], i + 1, SM)
         np.testing.assert_array_equal(out[0, i], o1)
         np.testing.assert_array_equal(lse[0, i], l1)
+
+
+def test_chunk_window_slides_past_128_tokens(oracle_mod):
+    """In a chunk longer than the window, token i attends to the chunk tokens
+    [i - 127, i] (the last 128 up to itself): checked against a dense numpy
+    attention over the independently dequantised selected entries and exactly
+    those window rows."""
+    g = np.random.default_rng(8)
+    n, Q, H = 300, 300, 16
+    k = g.standard_normal((1, n, 128)).astype(np.float32)
+    codes, scales = oracle_mod.quant_fp4(k[0], k[0][::-1].copy())
+    q = g.standard_normal((1, Q, H, 128)).astype(np.float32)
+    idx = np.sort(g.choice(n, (1, Q, 16)), axis=-1).astype(np.int32)
+    sk, sks = oracle_mod.quant_fp8_rows(g.standard_normal((1, Q, 128)).astype(np.float32))
+    sv, svs = oracle_mod.quant_fp8_rows(g.standard_normal((1, Q, 128)).astype(np.float32))
+    out, lse = oracle_mod.attn_chunk_batch(q, codes[None], scales[None], idx, sk, sv, sks, svs, SM)
+    K, V = fp4_matrix(codes, scales)
+    WK = e4m3_value(sk[0]) * sks[0][:, None].astype(np.float64)
+    WV = e4m3_value(sv[0]) * svs[0][:, None].astype(np.float64)
+    for i in (0, 5, 127, 128, 129, 200, 299):
+        lo = max(0, i - 127)
+        kk = np.concatenate([K[idx[0, i]], WK[lo:i + 1]])
+        vv = np.concatenate([V[idx[0, i]], WV[lo:i + 1]])
+        o, l = dense_attention(q[0, i], kk, vv, SM)
+        np.testing.assert_allclose(out[0, i], o, rtol=1e-6, atol=1e-6)
+        np.testing.assert_allclose(lse[0, i], l, rtol=1e-6, atol=1e-6)
