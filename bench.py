@@ -55,6 +55,8 @@ def parse_args():
     p.add_argument("--skip-cpu-baseline", action="store_true")
     p.add_argument("--contexts", default="4096,16384,65536,131072,262144,1048576",
                    help="model_step workload: context lengths (tokens) of the sweep")
+    p.add_argument("--batches", default="1,4,16,64,256,1024",
+                   help="attn_batch_sweep workload: batch sizes (sequences, one query each)")
     p.add_argument("--model-batch", type=int, default=4,
                    help="model_step workload: sequences per step")
     p.add_argument("--replay-tokens", type=int, default=0,
@@ -72,6 +74,12 @@ def attn_bytes(n_sel, n_swa, H):
     selected FP4 entry, 264 B per window token (2 x 128 E4M3 + 2 fp32 scales),
     fp32 q and out."""
     return 144 * n_sel + 264 * n_swa + 2 * H * 128 * 4
+
+
+def percentile(sorted_vals, f):
+    """Nearest-rank percentile of an ascending list."""
+    i = min(len(sorted_vals) - 1, max(0, int(round(f * (len(sorted_vals) - 1)))))
+    return sorted_vals[i]
 
 
 def idx_key_bytes(wl):
@@ -222,6 +230,19 @@ def time_gpu(args, wl, csa2, sets):
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
 
+        # the same replays once more with an event between consecutive steps:
+        # the distribution of single-step times
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        evs[0].record(stream)
+        for i in range(args.steps):
+            if graphs:
+                graphs[i % len(graphs)].replay()
+            else:
+                sets[i % len(sets)].run()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+
         # per-kernel durations, HIP events recorded around each kernel's own dispatch
         timer = csa2.KernelTimer(args.steps)
         attn_timer = csa2.KernelTimer(args.steps * len(wl.plan))
@@ -237,7 +258,7 @@ def time_gpu(args, wl, csa2, sets):
             sets[i % len(sets)].run()
         torch.cuda.synchronize()
         eager_elapsed = time.perf_counter() - t1
-    return elapsed, {"scan": scan_ms, "attn": attn_ms}, eager_elapsed
+    return elapsed, {"scan": scan_ms, "attn": attn_ms, "step": step_ms}, eager_elapsed
 
 
 # --------------------------------------------------------------------------- replay chunk
@@ -737,6 +758,84 @@ def run_model_sweep(args):
     }
 
 
+# --------------------------------------------------------------------------- gather sweep
+def run_attn_sweep(args):
+    """The gathering sparse attention (csa2_sparse_attn_decode: 512 selected
+    FP4 records and a 128-token FP8 window per query, 64 heads) at each batch
+    of --batches, timed with HIP events around its dispatch: where the kernel
+    leaves the latency regime.  Each sequence's cache holds 16384 entries
+    written by the library from N(0, 1) K and V drawn on the device; three
+    sets of indices, queries and windows rotate so that consecutive launches
+    gather different records."""
+    import torch
+
+    import compressed_kv_cache_decode_amd as csa2
+    from compressed_kv_cache_decode_amd import synth
+    H, topk, cap = 64, 512, 16384
+    sweep = []
+    for B in [int(x) for x in args.batches.split(",")]:
+        gen = synth.device_generator(4000 + B)
+        rnd = lambda *shape: synth.device_normal(gen, shape)
+        cache = csa2.Cache(B, cap)
+        CH = 1 << 18
+        for r0 in range(0, B * cap, CH):
+            n = min(CH, B * cap - r0)
+            csa2.quant_fp4(rnd(n, 128), rnd(n, 128), cache.kv_codes, cache.kv_scales,
+                           dst_rows=torch.arange(r0, r0 + n, dtype=torch.int64, device="cuda"))
+        sets = []
+        for _ in range(3):
+            idx = torch.rand((B, cap), generator=gen, device="cuda").topk(topk).indices
+            swk = torch.empty((B, 128, 128), dtype=torch.uint8, device="cuda")
+            swv = torch.empty_like(swk)
+            sks = torch.empty((B, 128), dtype=torch.float32, device="cuda")
+            svs = torch.empty_like(sks)
+            csa2.quant_fp8(rnd(B * 128, 128), swk, sks)
+            csa2.quant_fp8(rnd(B * 128, 128), swv, svs)
+            sets.append(dict(q=rnd(B, H, 128), idx=idx.sort().values.int().contiguous(),
+                             swk=swk, swv=swv, sks=sks, svs=svs,
+                             swa_len=torch.full((B,), 128, dtype=torch.int32, device="cuda"),
+                             out=torch.empty((B, H, 128), dtype=torch.float32, device="cuda"),
+                             lse=torch.empty((B, H), dtype=torch.float32, device="cuda")))
+        n_launch = max(args.steps, 30)
+        timer = csa2.KernelTimer(n_launch)
+        for rep in range(2):  # the first pass warms up
+            if rep:
+                timer.reset()
+            for i in range(n_launch):
+                d = sets[i % 3]
+                csa2.sparse_attn_decode(d["q"], cache, d["idx"], d["swk"], d["swv"], d["sks"],
+                                        d["svs"], d["swa_len"], d["out"], d["lse"],
+                                        timer=timer if rep else None)
+            torch.cuda.synchronize()
+        ms = sorted(timer.durations_ms())
+        timer.close()
+        mean = sum(ms) / len(ms)
+        nbytes = B * attn_bytes(topk, 128, H)
+        sweep.append({"batch": B, "mean_us": round(mean * 1e3, 2),
+                      "median_us": round(percentile(ms, 0.5) * 1e3, 2),
+                      "bytes_per_launch": nbytes,
+                      "achieved_GBps": round(nbytes / (mean * 1e-3) / 1e9, 1),
+                      "frac": round(nbytes / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+        log(f"attention sweep: B={B}: {mean * 1e3:.2f} us, "
+            f"{nbytes / (mean * 1e-3) / 1e9:.0f} GB/s")
+        del cache, sets
+        torch.cuda.empty_cache()
+    best = max(sweep, key=lambda r: r["achieved_GBps"])
+    return {"metric": "CSA2 sparse attention (gathering, 512 FP4 records + 128 FP8 window tokens "
+                      "per query, 64 heads): HBM GB/s vs batch",
+            "value": best["achieved_GBps"], "unit": "GB/s", "n_gpus": 1, "steps": n_launch,
+            "warmup": n_launch, "higher_is_better": True, "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic",
+            "config": {"workload": "attn_batch_sweep", "heads": H, "topk": topk, "window": 128,
+                       "entries_per_sequence": cap, "launch": "eager, HIP events per dispatch"},
+            "roofline": {"bound": "hbm", "achieved": best["achieved_GBps"], "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": best["frac"], "traffic": None,
+                         "kernel": f"k_attn (batch {best['batch']})",
+                         "bytes_per_launch": best["bytes_per_launch"],
+                         "mean_us": best["mean_us"]},
+            "sweep": sweep}
+
+
 def copy_calibration(mib):
     """One device-to-device copy of `mib` MiB: a kernel of known traffic
     (reads and writes mib MiB each) for scaling the hardware byte counters."""
@@ -765,6 +864,9 @@ def main():
     from compressed_kv_cache_decode_amd import synth
     if args.workload == "model_step":
         print(json.dumps(run_model_sweep(args)), flush=True)
+        return
+    if args.workload == "attn_batch_sweep":
+        print(json.dumps(run_attn_sweep(args)), flush=True)
         return
     wl = synth.WORKLOADS[args.workload]
     if args.copy_calibration_mb:
@@ -816,7 +918,9 @@ def main():
         "step": {"algorithmic_bytes": total_bytes,
                  "achieved_GBps": round(total_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                  "frac_of_hbm_peak": round(total_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                 "eager_ms_per_step": round(eager_elapsed / args.steps * 1e3, 4)},
+                 "eager_ms_per_step": round(eager_elapsed / args.steps * 1e3, 4),
+                 "ms_p10_median_p90": [round(percentile(kernel_ms["step"], f), 4)
+                                       for f in (0.1, 0.5, 0.9)]},
     }
     if not args.skip_cpu_baseline:
         cb = cpu_baseline(args, wl, inp)
