@@ -696,8 +696,7 @@ def build_model_set(csa2, T, B, H, topk, pool, seed):
     W = S.ENCODER_WINDOW_ONLY
     w, rows = windows(W)
     win = dict(q=rnd(W, B, H, 128), swa_len=torch.full((B,), 128, dtype=torch.int32, device="cuda"),
-               win_k=rnd(W * B, 128), win_v=rnd(W * B, 128), win_rows=rows,
-               k_empty=torch.empty((0, 128), dtype=torch.float32, device="cuda"), **w)
+               win_k=rnd(W * B, 128), win_v=rnd(W * B, 128), win_rows=rows, **w)
     model = S.ModelStep(enc_caches, dec_cache, B, H, topk=topk, pool_blocks=pool)
     nbytes = dec_cache.nbytes + sum(c.nbytes for c in enc_caches)
     return model, (new, win, enc_args, dec_args), nbytes

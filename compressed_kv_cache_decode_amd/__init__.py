@@ -225,6 +225,8 @@ def rope_table(positions, base=10000.0):
 # ---------------------------------------------------------------------------
 def quant_fp4(k_tok, v_tok, kv_codes, kv_scales, ratio=1, rope_cs=None, dst_rows=None,
               stream=None):
+    if k_tok is None and v_tok is None:  # FP8 jobs only
+        k_tok = v_tok = torch.empty((0, HEAD_DIM), dtype=torch.float32, device=kv_codes.device)
     n_tok = k_tok.shape[0] if k_tok.dim() > 1 else 0
     if k_tok.shape != v_tok.shape or (k_tok.dim() != 2 or k_tok.shape[1] != HEAD_DIM):
         raise ValueError("k_tok, v_tok must be [n_tok][128]")
@@ -252,7 +254,8 @@ def quant_fp8(x, codes, sigma, layout=FP8_ROWS, dst_rows=None, stream=None):
 def write_entries(k_tok, v_tok, kv_codes, kv_scales, ratio=1, rope_cs=None, dst_rows=None,
                   fp8_jobs=(), stream=None, idx_proj=None, ik_codes=None, ik_sigma=None,
                   ik_scales4=None):
-    """quant_fp4(k_tok, v_tok, ...) and quant_fp8 of each job in one launch.
+    """quant_fp4(k_tok, v_tok, ...) and quant_fp8 of each job in one launch
+    (k_tok = v_tok = None: the FP8 jobs only).
 
     fp8_jobs: up to 3 dicts with the arguments of quant_fp8: x, codes, sigma,
     and optionally layout (FP8_ROWS) and dst_rows.
@@ -260,6 +263,8 @@ def write_entries(k_tok, v_tok, kv_codes, kv_scales, ratio=1, rope_cs=None, dst_
     on the device from its fp32 K and written in FP8 to ik_codes (tile layout)
     and ik_sigma at the entry's row (csa2_write_entries_proj), or as FP4 keys to
     ik_codes and ik_scales4 when ik_scales4 is given (csa2_write_entries_proj_fp4)."""
+    if k_tok is None and v_tok is None:  # FP8 jobs only
+        k_tok = v_tok = torch.empty((0, HEAD_DIM), dtype=torch.float32, device=kv_codes.device)
     n_tok = k_tok.shape[0] if k_tok.dim() > 1 else 0
     if k_tok.shape != v_tok.shape or (k_tok.dim() != 2 or k_tok.shape[1] != HEAD_DIM):
         raise ValueError("k_tok, v_tok must be [n_tok][128]")

@@ -234,13 +234,11 @@ class ModelStep:
         rows (only the window tokens are written);
         win: the window-only layers' dict: q [2][B][H][128], swk / swv
         [2][B][128][128] u8, sks / svs [2][B][128] f32, swa_len [B], the new
-        window rows win_k / win_v [2*B][128] f32 with their rows win_rows, and
-        k_empty, an f32 tensor of shape [0][128];
+        window rows win_k / win_v [2*B][128] f32 with their rows win_rows;
         enc_args / dec_args: per group a dict iq, iw, n_vis, q, swk, swv, sks,
         svs, swa_len with the meaning of DecodeStack.step's arguments.
         Returns, per group, the top-K buffers its layers attended with."""
-        write_entries(win["k_empty"], win["k_empty"], self.dec.cache.kv_codes,
-                      self.dec.cache.kv_scales,
+        write_entries(None, None, self.dec.cache.kv_codes, self.dec.cache.kv_scales,
                       fp8_jobs=[dict(x=win["win_k"], codes=win["swk"].view(-1, HEAD_DIM),
                                      sigma=win["sks"].view(-1), dst_rows=win["win_rows"]),
                                 dict(x=win["win_v"], codes=win["swv"].view(-1, HEAD_DIM),

@@ -369,7 +369,6 @@ def test_model_step_all_40_layers(gpu, oracle_mod):
     wsk, wsks, wsv, wsvs = quantize_windows(gpu, np.zeros_like(wk), np.zeros_like(wv))
     win = dict(q=dev(wq), swk=wsk, swv=wsv, sks=wsks, svs=wsvs,
                swa_len=dev(np.full(B, 128, np.int32)),
-               k_empty=torch.empty((0, 128), dtype=torch.float32, device="cuda"),
                win_k=dev(np.ascontiguousarray(wk[:, :, slot].reshape(-1, 128))),
                win_v=dev(np.ascontiguousarray(wv[:, :, slot].reshape(-1, 128))),
                win_rows=dev(((np.arange(W)[:, None] * B + np.arange(B)[None, :]) * 128 + slot)
