@@ -284,6 +284,38 @@ int index_full_valu(int fmt, const uint8_t* ikc, const float* iks, int64_t cap, 
                                pool_blocks > 0 ? pool_idx : nullptr, topk_idx, stream, sbkeys);
     return hip_status(e);
 }
+
+// The Full layer of a multi-query chunk on MFMA: bounds on MFMA, then per
+// query, in one workgroup: with a pool, the blocks the bounds decide plus the
+// best undecided ones by exact block key; then the candidate half-blocks
+// (upper bound reaches the K-th largest lower bound of a block, of the pool's
+// blocks with a pool), their exact keys and the top-K.  A query whose
+// candidates overflow is rescored over all its positions there and takes the
+// Full selection.  Arguments validated and the workspace checked by the caller.
+int index_full_mma(int fmt, const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
+                   const float* iq, const float* iw, const int32_t* n_vis, int topk,
+                   int pool_blocks, int32_t* topk_idx, int32_t* pool_idx, void* ws,
+                   hipStream_t stream, hipEvent_t scan_start, hipEvent_t scan_stop) {
+    const IndexLayout L = full_layout(B, Q, cap, topk, pool_blocks);
+    char* w = static_cast<char*>(ws);
+    float* qd = reinterpret_cast<float*>(w + L.qd);
+    float* wq = reinterpret_cast<float*>(w + L.wq);
+    uint32_t* keys = reinterpret_cast<uint32_t*>(w + L.keys);
+    uint32_t* bkeys = reinterpret_cast<uint32_t*>(w + L.bkeys);
+    float* cq = reinterpret_cast<float*>(w + L.cq);
+    _Float16* qh = reinterpret_cast<_Float16*>(w + L.qh);
+    uint32_t* hkeys_hi = reinterpret_cast<uint32_t*>(w + L.hkeys_hi);
+    const int64_t nq = (int64_t)B * Q;
+    hipError_t e = launch_prep_iq(iq, iw, nq, qd, wq, stream, cq, qh);
+    if (e == hipSuccess)
+        e = launch_scan_mma(ikc, iks, cap, B, Q, qh, wq, cq, n_vis, bkeys, hkeys_hi, stream,
+                            scan_start, scan_stop, fmt);
+    if (e == hipSuccess)
+        e = launch_chunk_select(ikc, iks, cap, Q, qd, wq, hkeys_hi, n_vis, nq, topk, keys, bkeys,
+                                topk_idx, stream, pool_blocks, pool_blocks > 0 ? pool_idx : nullptr,
+                                fmt);
+    return hip_status(e);
+}
 }  // namespace
 
 __attribute__((visibility("default"))) int csa2_index_full_timed(
@@ -294,36 +326,11 @@ __attribute__((visibility("default"))) int csa2_index_full_timed(
     int rc = validate_index_full(ik_codes, ik_sigma, cap, B, Q, iq, iw, n_vis, topk, pool_blocks,
                                  topk_idx, pool_idx);
     if (rc) return rc;
-    const IndexLayout L = full_layout(B, Q, cap, topk, pool_blocks);
-    if (!ws || ws_bytes < L.total) return CSA2_E_WORKSPACE;
-    char* w = static_cast<char*>(ws);
-    float* qd = reinterpret_cast<float*>(w + L.qd);
-    float* wq = reinterpret_cast<float*>(w + L.wq);
-    uint32_t* keys = reinterpret_cast<uint32_t*>(w + L.keys);
-    uint32_t* bkeys = reinterpret_cast<uint32_t*>(w + L.bkeys);
-    const int64_t nq = (int64_t)B * Q;
-    if (mma_path(Q, cap, pool_blocks, topk)) {
-        // bounds on MFMA, then per query, in one workgroup: with a pool, the
-        // blocks the bounds decide plus the best undecided ones by exact
-        // block key; then the candidate half-blocks (upper bound reaches the
-        // K-th largest lower bound of a block, of the pool's blocks with a
-        // pool), their exact keys and the top-K.  A query whose candidates
-        // overflow is rescored over all its positions there and takes the
-        // Full selection
-        float* cq = reinterpret_cast<float*>(w + L.cq);
-        _Float16* qh = reinterpret_cast<_Float16*>(w + L.qh);
-        uint32_t* hkeys_hi = reinterpret_cast<uint32_t*>(w + L.hkeys_hi);
-        hipError_t e = launch_prep_iq(iq, iw, nq, qd, wq, stream, cq, qh);
-        if (e == hipSuccess)
-            e = launch_scan_mma(ik_codes, ik_sigma, cap, B, Q, qh, wq, cq, n_vis, bkeys,
-                                hkeys_hi, stream, scan_start, scan_stop);
-        if (e == hipSuccess)
-            e = launch_chunk_select(ik_codes, ik_sigma, cap, Q, qd, wq, hkeys_hi, n_vis, nq, topk,
-                                    keys, bkeys, topk_idx, stream, pool_blocks,
-                                    pool_blocks > 0 ? pool_idx : nullptr);
-        return hip_status(e);
-    }
-
+    if (!ws || ws_bytes < full_layout(B, Q, cap, topk, pool_blocks).total)
+        return CSA2_E_WORKSPACE;
+    if (mma_path(Q, cap, pool_blocks, topk))
+        return index_full_mma(kIdxFp8, ik_codes, ik_sigma, cap, B, Q, iq, iw, n_vis, topk,
+                              pool_blocks, topk_idx, pool_idx, ws, stream, scan_start, scan_stop);
     return index_full_valu(kIdxFp8, ik_codes, ik_sigma, cap, B, Q, iq, iw, n_vis, topk,
                            pool_blocks, topk_idx, pool_idx, ws, stream, scan_start, scan_stop);
 }
@@ -397,9 +404,12 @@ __attribute__((visibility("default"))) int csa2_index_full_fp4_timed(
                                  pool_blocks, topk_idx, pool_idx);
     if (rc) return rc;
     if (!ws || ws_bytes < full_layout(B, Q, cap, topk, pool_blocks).total) return CSA2_E_WORKSPACE;
-    return index_full_valu(kIdxFp4, ik4_codes, reinterpret_cast<const float*>(ik4_scales), cap, B,
-                           Q, iq, iw, n_vis, topk, pool_blocks, topk_idx, pool_idx, ws, stream,
-                           scan_start, scan_stop);
+    const float* scales = reinterpret_cast<const float*>(ik4_scales);  // read as 32-bit words
+    if (mma_path(Q, cap, pool_blocks, topk))
+        return index_full_mma(kIdxFp4, ik4_codes, scales, cap, B, Q, iq, iw, n_vis, topk,
+                              pool_blocks, topk_idx, pool_idx, ws, stream, scan_start, scan_stop);
+    return index_full_valu(kIdxFp4, ik4_codes, scales, cap, B, Q, iq, iw, n_vis, topk,
+                           pool_blocks, topk_idx, pool_idx, ws, stream, scan_start, scan_stop);
 }
 
 __attribute__((visibility("default"))) int csa2_index_full_fp4(

@@ -83,6 +83,11 @@ __device__ __forceinline__ float relu(float x) {
 // S_h^T[16 positions x 16 queries] += K[16 x 32 channels] Q_h^T[32 x 16], two
 // channel steps per head.  Lane l holds rows 4(l/16) .. +4 of column l % 16;
 // lanes l and l ^ 16 share a block of 8 positions.
+// FMT kIdxFp4: FP4 keys (E2M1 codes, one E4M3 scale per 16 channels, no
+// per-position scale): the A operands are the keys' exact values e2m1 x scale
+// in fp16, sigma is 1, and |k| <= 6 x 448, so the guard constant, derived for
+// |k| <= 448, is taken 6 times.
+template <int FMT>
 __global__ __launch_bounds__(kMmaThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_scan_mma(
     const uint8_t* __restrict__ ikc, const float* __restrict__ iks, int64_t cap, int Q,
     const _Float16* __restrict__ qh, const float* __restrict__ wq, const float* __restrict__ cq,
@@ -114,13 +119,31 @@ __global__ __launch_bounds__(kMmaThreads) __attribute__((amdgpu_waves_per_eu(4))
         inside[st] = base < cap;  // cap is a multiple of 64: a row tile is wholly in or out
         if (inside[st]) {
             const int64_t row = (int64_t)b * cap + base + (lane & 15);
+            if constexpr (FMT == kIdxFp8) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const uint2 raw = *reinterpret_cast<const uint2*>(
-                    ikc + ik_offset(row, 2 * ks + (lane >> 5)) + 8 * ((lane >> 4) & 1));
-                a[st][ks] = e4m3x8_h8(raw.x, raw.y);
+                for (int ks = 0; ks < 2; ++ks) {
+                    const uint2 raw = *reinterpret_cast<const uint2*>(
+                        ikc + ik_offset(row, 2 * ks + (lane >> 5)) + 8 * ((lane >> 4) & 1));
+                    a[st][ks] = e4m3x8_h8(raw.x, raw.y);
+                }
+                sig[st] = *reinterpret_cast<const float4*>(iks + (int64_t)b * cap + base +
+                                                          4 * (lane >> 4));
+            } else {
+                // channels 32 ks + 8 (l / 16) .. +8: plane ks, code bytes
+                // 4 (l / 16) .. +4, scale byte 2 ks + l / 32
+                const uint32_t sc4 = reinterpret_cast<const uint32_t*>(iks)[row];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const uint32_t w = *reinterpret_cast<const uint32_t*>(
+                        ikc + ik4_offset(row, ks) + 4 * (lane >> 4));
+                    const uint32_t sb = (sc4 >> (8 * (2 * ks + (lane >> 5)))) & 0xFFu;
+                    const _Float16 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false)[0];
+                    _Float16 v[8];
+                    fp4x8_to_f16(w, sc, v);
+                    a[st][ks] = half8_t{v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
+                }
+                sig[st] = make_float4(1.f, 1.f, 1.f, 1.f);
             }
-            sig[st] = *reinterpret_cast<const float4*>(iks + (int64_t)b * cap + base + 4 * (lane >> 4));
         } else {
             const half8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
             a[st][0] = z;
@@ -171,7 +194,7 @@ __global__ __launch_bounds__(kMmaThreads) __attribute__((amdgpu_waves_per_eu(4))
                     bop[h][ks] = *reinterpret_cast<const half8_t*>(
                         sq + jj * kMmaPitch + h * kIdxDim + 32 * ks + 8 * (lane >> 4));
             const float4 w = *reinterpret_cast<const float4*>(sw + jj * 4);
-            const float cqj = sc[jj];
+            const float cqj = FMT == kIdxFp8 ? sc[jj] : 6.0f * sc[jj];
             const int nv = snv[jj];
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
@@ -233,14 +256,15 @@ __global__ __launch_bounds__(kMmaThreads) __attribute__((amdgpu_waves_per_eu(4))
 hipError_t launch_scan_mma(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                            const _Float16* qh, const float* wq, const float* cq,
                            const int32_t* n_vis, uint32_t* bkeys_lo, uint32_t* hkeys_hi,
-                           hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+                           hipStream_t stream, hipEvent_t start, hipEvent_t stop, int fmt) {
     dim3 grid((unsigned)((cap + kMmaPos - 1) / kMmaPos), (unsigned)B);
+    auto kern = fmt == kIdxFp4 ? k_scan_mma<kIdxFp4> : k_scan_mma<kIdxFp8>;
     if (start != nullptr && stop != nullptr) {
-        hipExtLaunchKernelGGL(k_scan_mma, grid, dim3(kMmaThreads), 0, stream, start, stop, 0, ikc,
-                              iks, cap, Q, qh, wq, cq, n_vis, bkeys_lo, hkeys_hi);
+        hipExtLaunchKernelGGL(kern, grid, dim3(kMmaThreads), 0, stream, start, stop, 0, ikc, iks,
+                              cap, Q, qh, wq, cq, n_vis, bkeys_lo, hkeys_hi);
     } else {
-        hipLaunchKernelGGL(k_scan_mma, grid, dim3(kMmaThreads), 0, stream, ikc, iks, cap, Q, qh,
-                           wq, cq, n_vis, bkeys_lo, hkeys_hi);
+        hipLaunchKernelGGL(kern, grid, dim3(kMmaThreads), 0, stream, ikc, iks, cap, Q, qh, wq, cq,
+                           n_vis, bkeys_lo, hkeys_hi);
     }
     return hipGetLastError();
 }

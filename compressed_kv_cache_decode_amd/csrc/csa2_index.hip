@@ -145,6 +145,7 @@ struct IdxRow {
 // blocks they fill), computed by a whole workgroup of `nthreads` threads with
 // k_scan's arithmetic: the replay chunk's fallback for a query whose MFMA
 // candidates overflowed.  Positions past nv in the last block get key 0.
+template <int FMT>
 __device__ __forceinline__ void scan_query_exact(const uint8_t* __restrict__ ikc,
                                                  const float* __restrict__ iks, int64_t row0,
                                                  const float* __restrict__ qd,
@@ -156,9 +157,9 @@ __device__ __forceinline__ void scan_query_exact(const uint8_t* __restrict__ ikc
         const int64_t p = p0 + threadIdx.x;
         uint32_t key = 0u;
         if (p < nv) {
-            uint4 raw[4];
-            load_ik_row(ikc, row0 + p, raw);
-            key = score_key(score_row(raw, iks[row0 + p], qd, wq));
+            IdxRow<FMT> r;
+            r.load(ikc, iks, row0 + p);
+            key = score_key(r.score(qd, wq));
         }
         const uint32_t bk = max8_u32(key);  // every lane of the wave takes part
         if (p < nv8) {
@@ -1014,6 +1015,7 @@ __device__ __forceinline__ uint32_t rank_of_count(uint32_t cnt, uint32_t* part, 
 // scored with k_scan's arithmetic into ck, then their top K into out (ties to
 // the lowest position, since the slots ascend).  Two slots per thread in
 // flight; consecutive threads take the 4 positions of a half-block.
+template <int FMT>
 __device__ __forceinline__ void topk_of_halves(const uint8_t* __restrict__ ikc,
                                                const float* __restrict__ iks, int64_t row0,
                                                const float* qrow, const float* wrow, int nv,
@@ -1022,23 +1024,19 @@ __device__ __forceinline__ void topk_of_halves(const uint8_t* __restrict__ ikc,
     const int tid = threadIdx.x;
     const int n_slots = (int)n_c * kHalf;
     for (int s0 = 0; s0 < n_slots; s0 += 2 * kSelThreads) {
-        uint4 raw[2][4];
-        float sg[2] = {0.0f, 0.0f};
+        IdxRow<FMT> r[2];
         bool vis[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int s = s0 + u * kSelThreads + tid;
             const int64_t pos = s < n_slots ? (int64_t)list[s >> 2] * kHalf + (s & 3) : nv;
             vis[u] = pos < nv;
-            if (vis[u]) {
-                load_ik_row(ikc, row0 + pos, raw[u]);
-                sg[u] = iks[row0 + pos];
-            }
+            if (vis[u]) r[u].load(ikc, iks, row0 + pos);
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int s = s0 + u * kSelThreads + tid;
-            if (s < n_slots) ck[s] = vis[u] ? score_key(score_row(raw[u], sg[u], qrow, wrow)) : 0u;
+            if (s < n_slots) ck[s] = vis[u] ? score_key(r[u].score(qrow, wrow)) : 0u;
         }
     }
     __syncthreads();
@@ -1054,6 +1052,7 @@ __device__ __forceinline__ void topk_of_halves(const uint8_t* __restrict__ ikc,
                 nullptr, rs);
 }
 
+template <int FMT>
 __global__ __launch_bounds__(kSelThreads) void k_chunk_select(
     const uint8_t* __restrict__ ikc, const float* __restrict__ iks, int64_t cap, int Q,
     const float* __restrict__ qd, const float* __restrict__ wq,
@@ -1118,7 +1117,7 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select(
     }
 
     if (n_c > (uint32_t)Pc) {  // uniform: the exact fallback
-        scan_query_exact(ikc, iks, row0, qrow, wrow, nv, kSelThreads, keys + bq * cap,
+        scan_query_exact<FMT>(ikc, iks, row0, qrow, wrow, nv, kSelThreads, keys + bq * cap,
                          bkeys + bq * nb);
         __syncthreads();  // the keys are the workgroup's own global writes
         select_full_query(keys, bkeys, cap, bq, nv, K, K, nullptr, topk_out, sh);
@@ -1127,7 +1126,7 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select(
     __syncthreads();  // the candidate list is complete
 
     // 3-4. exact keys of the candidates' positions, and their top-K
-    topk_of_halves(ikc, iks, row0, qrow, wrow, nv, n_c, sh.pool, ck, K, topk_out + bq * K, rs);
+    topk_of_halves<FMT>(ikc, iks, row0, qrow, wrow, nv, n_c, sh.pool, ck, K, topk_out + bq * K, rs);
 }
 
 // Full layer with a pool of P blocks, for one query of the multi-query MFMA
@@ -1152,6 +1151,7 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select(
 constexpr int kPoolUndecided = 1024;  // undecided blocks held in LDS
 static_assert(kMaxPoolBlocks >= kChunkMaxCand, "sh.pool holds either list");
 
+template <int FMT>
 __global__ __launch_bounds__(kSelThreads) void k_chunk_select_pool(
     const uint8_t* __restrict__ ikc, const float* __restrict__ iks, int64_t cap, int Q,
     const float* __restrict__ qd, const float* __restrict__ wq,
@@ -1209,7 +1209,7 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select_pool(
     const uint32_t need = (uint32_t)P - n_sure;  // n_sure <= P
 
     auto fallback = [&]() {
-        scan_query_exact(ikc, iks, row0, qrow, wrow, nv, kSelThreads, keys + bq * cap,
+        scan_query_exact<FMT>(ikc, iks, row0, qrow, wrow, nv, kSelThreads, keys + bq * cap,
                          bkeys + bq * nb);
         __syncthreads();  // the keys are the workgroup's own global writes
         select_full_query(keys, bkeys, cap, bq, nv, P, K, pool_out, topk_out, sh);
@@ -1233,9 +1233,9 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select_pool(
             const int64_t pos = s < n_pos ? (int64_t)ulist[s >> 3] * kBlock + (s & 7) : nv;
             uint32_t key = 0u;
             if (pos < nv) {
-                uint4 raw[4];
-                load_ik_row(ikc, row0 + pos, raw);
-                key = score_key(score_row(raw, iks[row0 + pos], qrow, wrow));
+                IdxRow<FMT> r;
+                r.load(ikc, iks, row0 + pos);
+                key = score_key(r.score(qrow, wrow));
             }
             key = max8_u32(key);
             if (s < n_pos && (s & 7) == 0) ukey[s >> 3] = key;
@@ -1294,7 +1294,7 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select_pool(
     for (uint32_t mm = cmask; mm != 0; mm &= mm - 1u, ++r)
         sh.pool[r] = 2 * b0 + __builtin_ctz(mm);
     __syncthreads();  // the candidate list is complete
-    topk_of_halves(ikc, iks, row0, qrow, wrow, nv, n_c, sh.pool, ck, K, topk_out + bq * K, rs);
+    topk_of_halves<FMT>(ikc, iks, row0, qrow, wrow, nv, n_c, sh.pool, ck, K, topk_out + bq * K, rs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1352,18 +1352,21 @@ hipError_t launch_chunk_select(const uint8_t* ikc, const float* iks, int64_t cap
                                const float* qd, const float* wq, const uint32_t* hkeys_hi,
                                const int32_t* n_vis, int64_t n_queries, int K, uint32_t* keys,
                                uint32_t* bkeys, int32_t* topk_out, hipStream_t stream, int P,
-                               int32_t* pool_out) {
+                               int32_t* pool_out, int fmt) {
     const int Pc = chunk_cand_halves(K);
     if (Pc > kChunkMaxCand) return hipErrorInvalidValue;
     if (P > 0) {
         if (cap / kBlock > kSelRegSlots || P > kMaxPoolBlocks || pool_out == nullptr)
             return hipErrorInvalidValue;
-        hipLaunchKernelGGL(k_chunk_select_pool, dim3((unsigned)n_queries), dim3(kSelThreads), 0,
+        hipLaunchKernelGGL(fmt == kIdxFp4 ? k_chunk_select_pool<kIdxFp4>
+                                          : k_chunk_select_pool<kIdxFp8>,
+                           dim3((unsigned)n_queries), dim3(kSelThreads), 0,
                            stream, ikc, iks, cap, Q, qd, wq, hkeys_hi, n_vis, P, K, Pc, keys,
                            bkeys, pool_out, topk_out);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_chunk_select, dim3((unsigned)n_queries), dim3(kSelThreads), 0, stream,
+    hipLaunchKernelGGL(fmt == kIdxFp4 ? k_chunk_select<kIdxFp4> : k_chunk_select<kIdxFp8>,
+                       dim3((unsigned)n_queries), dim3(kSelThreads), 0, stream,
                        ikc, iks, cap, Q, qd, wq, hkeys_hi, n_vis, K, Pc, keys, bkeys, topk_out);
     return hipGetLastError();
 }

@@ -73,7 +73,7 @@ hipError_t launch_scan_mma(const uint8_t* ikc, const float* iks, int64_t cap, in
                            const _Float16* qh, const float* wq, const float* cq,
                            const int32_t* n_vis, uint32_t* bkeys_lo, uint32_t* hkeys_hi,
                            hipStream_t stream, hipEvent_t start = nullptr,
-                           hipEvent_t stop = nullptr);
+                           hipEvent_t stop = nullptr, int fmt = kIdxFp8);
 // top-K of each query of the MFMA scan from its bounds (csa2_index.hip):
 // candidate half-blocks, their exact keys and the selection in one workgroup
 // per query; keys / bkeys: scratch rows of the exact fallback (bkeys holds the
@@ -83,7 +83,7 @@ hipError_t launch_chunk_select(const uint8_t* ikc, const float* iks, int64_t cap
                                const float* qd, const float* wq, const uint32_t* hkeys_hi,
                                const int32_t* n_vis, int64_t n_queries, int K, uint32_t* keys,
                                uint32_t* bkeys, int32_t* topk_out, hipStream_t stream, int P = 0,
-                               int32_t* pool_out = nullptr);
+                               int32_t* pool_out = nullptr, int fmt = kIdxFp8);
 // blocks per sequence up to which the MFMA path also selects pools (their
 // bound keys are held in registers, 16 per thread of a 1024-thread workgroup)
 constexpr int64_t kChunkPoolMaxBlocks = 16384;

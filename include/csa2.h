@@ -303,10 +303,11 @@ int csa2_write_entries_proj_fp4(const float* k_tok, const float* v_tok, int64_t 
                                 uint8_t* ik4_scales, const csa2_fp8_job* jobs, int n_jobs,
                                 hipStream_t stream);
 
-/* csa2_index_full_fp4 -- csa2_index_full over FP4 indexer keys (any Q; the
- * scan is the exact VALU scan for every Q).  Arguments, outputs, workspace
- * and errors as csa2_index_full; _timed brackets the scan as
- * csa2_index_full_timed does. */
+/* csa2_index_full_fp4 -- csa2_index_full over FP4 indexer keys, with the
+ * same two paths (the exact scan; for many queries per sequence the MFMA
+ * bounds with exact rescoring, whose guard band allows for keys up to
+ * 6 x 448).  Arguments, outputs, workspace and errors as csa2_index_full;
+ * _timed brackets the scan as csa2_index_full_timed does. */
 int csa2_index_full_fp4(const uint8_t* ik4_codes, const uint8_t* ik4_scales, int64_t cap, int B,
                         int Q, const float* iq, const float* iw, const int32_t* n_vis, int topk,
                         int pool_blocks, int32_t* topk_idx, int32_t* pool_idx, void* ws,

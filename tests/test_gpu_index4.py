@@ -92,6 +92,18 @@ def test_write_entries_proj_fp4_bit_exact(gpu, oracle_mod, n_tok, ratio, rope):
     (1, 1, 131072, [131072], 512, 2048),
     (1, 1, 262144, [262141], 512, 2048),          # more than 16384 blocks: streaming blocks
     (1, 1, 65536, [65533], 2048, 4096),           # the largest top-K and pool
+    # many queries per sequence: the MFMA bounds path with FP4 keys (guard
+    # band for |k| <= 6 x 448), ragged visibility down to none, a capacity
+    # that partly fills the last workgroup, more than 128 queries (two
+    # staging passes), and pools decided from the bounds
+    (1, 130, 8192, [[8192 - 37 * i if i % 5 else (97 * i) % 600 for i in range(130)]], 512, 0),
+    (2, 16, 16384, [[0, 1, 5, 300, 511, 512, 513, 4096, 8191, 8192, 12000, 16383, 16384,
+                     16384, 7, 9000], [16384 - 1000 * i for i in range(16)]], 512, 0),
+    (1, 5, 1088, [[1088, 1087, 1000, 700, 64]], 64, 0),
+    (2, 16, 16384, [[0, 1, 5, 300, 511, 512, 513, 4096, 8191, 8192, 12000, 16383, 16384,
+                     16384, 7, 9000], [16384 - 1000 * i for i in range(16)]], 512, 2048),
+    (1, 8, 131072, [[131072, 131000, 100001, 65536, 20000, 16385, 2048, 9]], 512, 2048),
+    (1, 6, 8192, [[8192, 8191, 4000, 1030, 1024, 1017]], 64, 128),
 ])
 def test_index_full_fp4_bit_exact(gpu, oracle_mod, B, Q, cap, nvis, topk, pool):
     say(f"index_full_fp4 B={B} Q={Q} cap={cap} topk={topk} pool={pool}")
@@ -202,3 +214,29 @@ def test_decoder_stack_fp4_keys(gpu, oracle_mod):
                                    int(inp.swa_len[b]), SM)
             err = row_rel_err(host(st.out)[layer, b], o)
             assert err.max() <= 2e-3, (layer, err.max())
+
+
+@pytest.mark.parametrize("pool", [0, 1024])
+def test_index_full_fp4_chunk_all_ties(gpu, oracle_mod, pool):
+    """Many queries over identical FP4 keys: every bound ties, the candidate
+    lists overflow, and each query falls back to its exact scan in the same
+    workgroup; the lowest positions and blocks win."""
+    say(f"index_full_fp4 chunk all ties pool={pool}")
+    B, Q, cap = 1, 8, 8192
+    x = np.tile(np.random.default_rng(64).standard_normal(64).astype(np.float32), (B, cap, 1))
+    kc4, ks4 = oracle_mod.idx4_quant_rows(x)
+    cache = gpu.Cache(B, cap, idx_fp4=True)
+    cache.ik_codes.copy_(dev(tile_ik4(kc4)))
+    cache.ik_scales4.copy_(dev(ks4.reshape(-1, 4)))
+    g = np.random.default_rng(65)
+    iq = np.abs(g.standard_normal((B, Q, 4, 64))).astype(np.float32)
+    iw = g.random((B, Q, 4)).astype(np.float32)
+    nv = np.array([[8192, 8000, 5000, 4097, 1024, 600, 100, 0]], np.int32)
+    tk_ref, pl_ref = oracle_mod.index_full4_batch(kc4, ks4, iq, iw, nv, 512, pool)
+    tk = torch.full((B, Q, 512), -7, dtype=torch.int32, device="cuda")
+    pl = torch.full((B, Q, max(pool, 1)), -7, dtype=torch.int32, device="cuda")
+    gpu.index_full(cache, dev(iq), dev(iw), dev(nv), tk, pl if pool else None, topk=512,
+                   pool_blocks=pool)
+    np.testing.assert_array_equal(host(tk), tk_ref)
+    if pool:
+        np.testing.assert_array_equal(host(pl), pl_ref)
