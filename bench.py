@@ -290,18 +290,23 @@ def run_chunk_bench(args, wl):
     }
     caches = []
     for s_ in range(args.cache_sets):
-        cache = csa2.Cache(B, cap)
+        cache = csa2.Cache(B, cap, idx_fp4=wl.idx_fp4)
         if s_ == 0:
             pre = np.arange(N - Q)
             csa2.quant_fp4(torch.from_numpy(inp.k_tok[0, :N - Q]).cuda(),
                            torch.from_numpy(inp.v_tok[0, :N - Q]).cuda(), cache.kv_codes,
                            cache.kv_scales, rope_cs=torch.from_numpy(csa2.rope_table(pre)).cuda(),
                            dst_rows=cache.rows(0, pre))
-            csa2.quant_fp8(torch.from_numpy(inp.idx_k[0, :N - Q]).cuda(), cache.ik_codes,
-                           cache.ik_sigma, layout=csa2.FP8_IDX_TILED, dst_rows=cache.rows(0, pre))
+            ik = torch.from_numpy(inp.idx_k[0, :N - Q]).cuda()
+            if wl.idx_fp4:
+                csa2.quant_idx_fp4(ik, cache.ik_codes, cache.ik_scales4, dst_rows=cache.rows(0, pre))
+            else:
+                csa2.quant_fp8(ik, cache.ik_codes, cache.ik_sigma, layout=csa2.FP8_IDX_TILED,
+                               dst_rows=cache.rows(0, pre))
         else:
-            for name in ("kv_codes", "kv_scales", "ik_codes", "ik_sigma"):
+            for name in ("kv_codes", "kv_scales", "ik_codes"):
                 getattr(cache, name).copy_(getattr(caches[0], name))
+            cache.ik_aux.copy_(caches[0].ik_aux)
         caches.append(cache)
     rows_new = caches[0].rows(0, pos_new)
     swk = torch.empty((B, Q, 128), dtype=torch.uint8, device="cuda")
@@ -320,6 +325,7 @@ def run_chunk_bench(args, wl):
         csa2.write_entries(d["k_new"], d["v_new"], cache.kv_codes, cache.kv_scales,
                            rope_cs=d["rope_new"], dst_rows=rows_new, idx_proj=d["proj"],
                            ik_codes=cache.ik_codes, ik_sigma=cache.ik_sigma,
+                           ik_scales4=cache.ik_scales4,
                            fp8_jobs=[dict(x=d["swa_k"], codes=swk, sigma=sks),
                                      dict(x=d["swa_v"], codes=swv, sigma=svs)])
         csa2.index_full(cache, d["iq"], d["iw"], d["n_vis"], tk, None, topk=wl.topk,
@@ -363,7 +369,8 @@ def run_chunk_bench(args, wl):
     peak = 2500.0
     rl = {"bound": "mfma", "achieved": round(scan_tfs, 2), "peak": peak, "unit": "TFLOP/s",
           "frac": round(scan_tfs / peak, 4), "traffic": load_traffic(wl.name).get("k_scan_mma"),
-          "kernel": "k_scan_mma (Full-layer indexer bounds of 128 chunk queries, fp16 MFMA)",
+          "kernel": "k_scan_mma (Full-layer indexer bounds of 128 chunk queries, fp16 MFMA"
+                    + (", FP4 keys)" if wl.idx_fp4 else ")"),
           "flops_per_launch": flops, "mean_us": round(scan_mean * 1e3, 2)}
     return {
         "metric": "CSA2 bounded-replay chunk queries/s (128 replayed tokens over 128K entries, one layer)",
@@ -372,6 +379,7 @@ def run_chunk_bench(args, wl):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "sequences": B, "entries": N, "queries": Q, "heads": H,
+                   "indexer_key": "fp4" if wl.idx_fp4 else "fp8",
                    "topk": wl.topk, "cache_sets": args.cache_sets,
                    "launch": "eager" if args.no_graph else "hip-graph"},
         "roofline": rl,

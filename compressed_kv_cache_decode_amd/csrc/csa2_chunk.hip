@@ -85,8 +85,9 @@ __device__ __forceinline__ float relu(float x) {
 // lanes l and l ^ 16 share a block of 8 positions.
 // FMT kIdxFp4: FP4 keys (E2M1 codes, one E4M3 scale per 16 channels, no
 // per-position scale): the A operands are the keys' exact values e2m1 x scale
-// in fp16, sigma is 1, and |k| <= 6 x 448, so the guard constant, derived for
-// |k| <= 448, is taken 6 times.
+// in fp16 and the score is not scaled (sigma 1); the guard band, derived for
+// keys |k| <= 448 sigma, takes for a row the factor g = 6 max_g scale_g / 448,
+// since its values satisfy |k| <= 6 max_g scale_g.
 template <int FMT>
 __global__ __launch_bounds__(kMmaThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_scan_mma(
     const uint8_t* __restrict__ ikc, const float* __restrict__ iks, int64_t cap, int Q,
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(kMmaThreads) __attribute__((amdgpu_waves_per_eu(4))
     // output rows 4 (l / 16) + i
     half8_t a[2][2];
     float4 sig[2];
-    float gmax[2];
+    float gmax[2];  // the guard-band factor of the lane's four output rows
     bool inside[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -151,6 +152,23 @@ __global__ __launch_bounds__(kMmaThreads) __attribute__((amdgpu_waves_per_eu(4))
             sig[st] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
         gmax[st] = fmaxf(fmaxf(sig[st].x, sig[st].y), fmaxf(sig[st].z, sig[st].w));
+        if constexpr (FMT == kIdxFp4) {
+            // largest E4M3 scale of the four output rows 4 (l / 16) + i
+            float smax = 0.0f;
+            if (inside[st]) {
+                const uint4 w4 = *reinterpret_cast<const uint4*>(
+                    reinterpret_cast<const uint32_t*>(iks) + (int64_t)b * cap + base +
+                    4 * (lane >> 4));
+                const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+                    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+                    smax = fmaxf(smax, fmaxf(fmaxf(lo[0], lo[1]), fmaxf(hi[0], hi[1])));
+                }
+            }
+            gmax[st] = smax * (6.0f / 448.0f);
+        }
     }
 
     for (int q0 = 0; q0 < Q; q0 += kMmaQ) {
@@ -194,7 +212,7 @@ __global__ __launch_bounds__(kMmaThreads) __attribute__((amdgpu_waves_per_eu(4))
                     bop[h][ks] = *reinterpret_cast<const half8_t*>(
                         sq + jj * kMmaPitch + h * kIdxDim + 32 * ks + 8 * (lane >> 4));
             const float4 w = *reinterpret_cast<const float4*>(sw + jj * 4);
-            const float cqj = FMT == kIdxFp8 ? sc[jj] : 6.0f * sc[jj];
+            const float cqj = sc[jj];
             const int nv = snv[jj];
 #pragma unroll
             for (int st = 0; st < 2; ++st) {

@@ -75,6 +75,9 @@ WORKLOADS = {
                                         pool_blocks=POOL_BLOCKS, planted=True, idx_fp4=True),
     "replay_chunk_128k": Workload("replay_chunk_128k", 1004, B=1, n_ent=131072, ratio=1, H=64,
                                   plan="F", pool_blocks=0, Q=128),
+    "replay_chunk_128k_fp4idx": Workload("replay_chunk_128k_fp4idx", 1004, B=1, n_ent=131072,
+                                         ratio=1, H=64, plan="F", pool_blocks=0, Q=128,
+                                         idx_fp4=True),
     "replay_stack_128k": Workload("replay_stack_128k", 1005, B=1, n_ent=131072, ratio=1, H=64,
                                   plan=DECODER_PLAN, pool_blocks=POOL_BLOCKS, Q=128),
 }
