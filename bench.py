@@ -45,8 +45,8 @@ def log(msg):
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decoder_stack_128k")
     p.add_argument("--cache-sets", type=int, default=3)
     p.add_argument("--no-graph", action="store_true", help="time eager launches, no HIP graph")
