@@ -569,7 +569,15 @@ def cpu_baseline(args, wl, inp):
                                  swv[layer], sks[layer], svs[layer], inp.swa_len[:S], sm)
     dt = time.perf_counter() - t0
     del L
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")),
+                         "")
+    except OSError:
+        pass
     return {"value": S / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "host_cpus": os.cpu_count(),
             "sample": f"{S} of the {wl.B} sequences, one full {len(wl.plan)}-layer stack step "
                       f"each ({N} entries); oracle caches built before timing",
             "seconds": dt}
