@@ -243,9 +243,14 @@ def time_gpu(args, wl, csa2, sets):
         torch.cuda.synchronize()
         step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
 
-        # per-kernel durations, HIP events recorded around each kernel's own dispatch
+        # per-kernel durations, HIP events recorded around each kernel's own
+        # dispatch.  A bounded spin kernel first lets the host queue the eager
+        # launches ahead of the GPU, so that they run back to back as in the
+        # graph replays instead of waiting for the host between kernels
         timer = csa2.KernelTimer(args.steps)
         attn_timer = csa2.KernelTimer(args.steps * len(wl.plan))
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(int(3e6 * args.steps))  # about 1.2 ms of spinning per step
         for i in range(args.steps):
             sets[i % len(sets)].run(scan_timer=timer, attn_timer=attn_timer)
         torch.cuda.synchronize()
