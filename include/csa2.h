@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 1
+#define CSA2_ABI_VERSION 2
 
 #define CSA2_HEAD_DIM 128        /* main K and V width */
 #define CSA2_KV_CODE_BYTES 128   /* per entry: K 64 B | V 64 B */
