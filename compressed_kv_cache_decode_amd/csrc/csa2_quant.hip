@@ -21,13 +21,17 @@ namespace csa2 {
 // channel j = lane: key_j = fp32 chain over input channels c = 0..127 of
 // proj[j][c] * x[c], one fused multiply-add per channel, from +0; x[c] is
 // read from lane c/2 (k0 for even c, k1 for odd c), wave-uniform.
-__device__ __forceinline__ float project_idx_key(const float* __restrict__ proj, float k0,
-                                                 float k1, int lane) {
-    const float4* wr = reinterpret_cast<const float4*>(proj + lane * kHeadDim);
+// The projection, row j at proj[j * kProjPitch]: staged in LDS by the
+// workgroup (a pitch of 129 floats keeps the lanes' rows in distinct banks).
+constexpr int kProjPitch = kHeadDim + 1;
+
+__device__ __forceinline__ float project_idx_key(const float* proj, float k0, float k1,
+                                                 int lane) {
+    const float* wr = proj + lane * kProjPitch;
     float acc = 0.0f;
 #pragma unroll
     for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
-        const float4 w = wr[c4];
+        const float4 w = make_float4(wr[4 * c4], wr[4 * c4 + 1], wr[4 * c4 + 2], wr[4 * c4 + 3]);
         const float x0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k0), 2 * c4));
         const float x1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k1), 2 * c4));
         const float x2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k0), 2 * c4 + 1));
@@ -191,11 +195,23 @@ __global__ __launch_bounds__(256) void k_quant_idx4(const float* __restrict__ x,
 // w as k_quant_fp4 does, the following waves the rows of the FP8 jobs in
 // order, each as k_quant_fp8 does.
 __global__ __launch_bounds__(256) void k_write_entries(Fp4Job f, Fp8Jobs j) {
+    __shared__ float proj_l[kIdxDim * kProjPitch];
     const int lane = threadIdx.x & 63;
     int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    // a workgroup holding entry waves stages the projection once, with every
+    // thread (uniform over the workgroup, before any wave leaves)
+    const bool stage = f.proj != nullptr && (int64_t)blockIdx.x * 4 < f.n_ent;
+    if (stage) {
+        for (int i = threadIdx.x; i < kIdxDim * kHeadDim / 4; i += 256) {
+            const float4 v = reinterpret_cast<const float4*>(f.proj)[i];
+            float* d = proj_l + (i / (kHeadDim / 4)) * kProjPitch + 4 * (i % (kHeadDim / 4));
+            d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+        }
+        __syncthreads();
+    }
     if (w < f.n_ent) {
         quant_fp4_entry(f.k, f.v, w, f.ratio, f.rope_cs, f.dst_rows, f.codes, f.scales, lane,
-                        f.proj, f.ik_codes, f.ik_sigma, f.ik_scales4);
+                        stage ? proj_l : nullptr, f.ik_codes, f.ik_sigma, f.ik_scales4);
         return;
     }
     w -= f.n_ent;
