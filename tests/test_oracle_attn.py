@@ -147,3 +147,24 @@ def test_chunk_window_slides_past_128_tokens(oracle_mod):
         o, l = dense_attention(q[0, i], kk, vv, SM)
         np.testing.assert_allclose(out[0, i], o, rtol=1e-6, atol=1e-6)
         np.testing.assert_allclose(lse[0, i], l, rtol=1e-6, atol=1e-6)
+
+
+def test_decode_batch_equals_single(oracle_mod):
+    g = np.random.default_rng(9)
+    B, H, cap, topk = 3, 16, 96, 40
+    k = g.standard_normal((B * cap, 128)).astype(np.float32)
+    v = g.standard_normal((B * cap, 128)).astype(np.float32)
+    codes, scales = oracle_mod.quant_fp4(k, v)
+    codes, scales = codes.reshape(B, cap, 128), scales.reshape(B, cap, 16)
+    q = g.standard_normal((B, H, 128)).astype(np.float32)
+    idx = np.stack([np.sort(g.choice(cap, topk, replace=False)) for _ in range(B)]).astype(np.int32)
+    idx[1, 30:] = -1  # a row padded with -1
+    sk, sks = oracle_mod.quant_fp8_rows(g.standard_normal((B, 128, 128)).astype(np.float32))
+    sv, svs = oracle_mod.quant_fp8_rows(g.standard_normal((B, 128, 128)).astype(np.float32))
+    swa_len = np.array([128, 0, 57], np.int32)
+    out, lse = oracle_mod.attn_decode_batch(q, codes, scales, idx, sk, sv, sks, svs, swa_len, SM)
+    for b in range(B):
+        o1, l1 = oracle_mod.attn(q[b], codes[b], scales[b], idx[b], sk[b], sv[b], sks[b], svs[b],
+                                 swa_len[b], SM)
+        np.testing.assert_array_equal(out[b], o1)
+        np.testing.assert_array_equal(lse[b], l1)

@@ -199,3 +199,62 @@ def test_batch_equals_single(oracle_mod):
             t1, p1 = oracle_mod.index_full(ikc[b], iks[b], nv[b, q], iq[b, q], iw[b, q], 9, 10)
             np.testing.assert_array_equal(tk[b, q], t1)
             np.testing.assert_array_equal(pl[b, q], p1)
+
+
+def test_query_scale_fold_at_random_scales(oracle_mod):
+    """The indexer query's per-head scale sq = fl(amax / 448) reaches the score
+    only through the folded head weight w' = fl(w * sq).  Queries of random
+    magnitude (sq far from 1) pin the fold: the codes are RNE_E4M3(fl(q / sq)),
+    w' equals fl(w * sq) bit for bit with sq computed here, and every score of
+    the Full scan lies within the fp32 rounding bound of an fp64 score computed
+    from the dequantised query sq * E4M3(code), the unfolded weight w and the
+    decoded key.  A dropped fold (w' = w) or an inverted one (w / sq) misses
+    that bound by orders of magnitude."""
+    g = np.random.default_rng(12)
+    u = 2.0 ** -24
+    for trial in range(40):
+        # sq is about mag / 180: magnitudes on both sides of 180, away from it
+        mag = 10.0 ** (g.uniform(-3.0, 1.3) if trial % 2 else g.uniform(3.0, 4.5))
+        iq = (g.standard_normal((4, 64)) * mag).astype(np.float32)
+        iw = g.random(4).astype(np.float32)
+        qc, wq = oracle_mod.quant_iq(iq, iw)
+        sq = np.abs(iq).max(axis=1) / np.float32(448.0)  # fp32 division, one rounding
+        assert sq.dtype == np.float32 and np.all(np.abs(np.log2(sq)) > 1.0)
+        np.testing.assert_array_equal(qc, e4m3_rne(iq / sq[:, None]))
+        np.testing.assert_array_equal(wq.view(np.uint32), (iw * sq).view(np.uint32))
+
+        n = 24
+        x = g.standard_normal((n, 64)).astype(np.float32)
+        ikc, iks = oracle_mod.quant_fp8_rows(x)
+        _, _, sc = oracle_mod.index_full(ikc, iks, n, iq, iw, 4, 0, want_scores=True)
+        qhat = e4m3_value(qc) * sq[:, None].astype(np.float64)
+        for s in range(n):
+            kv = e4m3_value(ikc[s])
+            dots = qhat @ kv
+            exact = float(iks[s]) * sum(float(iw[h]) * max(dots[h], 0.0) for h in range(4))
+            absp = np.abs(qhat * kv[None, :]).sum(axis=1)
+            # 63 roundings of the channel chain, the fold, the weight product,
+            # 3 head adds and the sigma product, each at most u relative
+            bound = float(iks[s]) * sum(float(iw[h]) * 70 * u * absp[h] for h in range(4))
+            bound += 8 * u * abs(exact) + 1e-45
+            assert abs(float(sc[s]) - exact) <= bound, (trial, s, sc[s], exact, bound)
+            assert sc[s] == oracle_mod.score(qc, wq, ikc[s], iks[s])
+
+
+def test_reindex_batch_equals_single(oracle_mod):
+    g = np.random.default_rng(71)
+    B, Q, cap, P = 2, 3, 256, 6
+    x = g.standard_normal((B, cap, 64)).astype(np.float32)
+    ikc, iks = oracle_mod.quant_fp8_rows(x)
+    iq = g.standard_normal((B, Q, 4, 64)).astype(np.float32)
+    iw = g.random((B, Q, 4)).astype(np.float32)
+    nv = np.array([[256, 130, 9], [1, 64, 200]], np.int32)
+    _, pl = oracle_mod.index_full_batch(ikc, iks, iq, iw, nv, 8, P)
+    iq2 = (g.standard_normal((B, Q, 4, 64)) * 3.0).astype(np.float32)
+    iw2 = g.random((B, Q, 4)).astype(np.float32)
+    tk = oracle_mod.index_reindex_batch(ikc, iks, iq2, iw2, nv, pl, 11)
+    for b in range(B):
+        for q in range(Q):
+            t1 = oracle_mod.index_reindex(ikc[b], iks[b], nv[b, q], iq2[b, q], iw2[b, q],
+                                          pl[b, q], 11)
+            np.testing.assert_array_equal(tk[b, q], t1)

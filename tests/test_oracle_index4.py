@@ -182,3 +182,26 @@ def test_batch4_equals_single(oracle_mod):
             r1 = oracle_mod.index_reindex4(codes[b], scales[b], nv[b, q], iq[b, Q - 1 - q],
                                            iw[b, Q - 1 - q], pl[b, q], 16)
             np.testing.assert_array_equal(rk[b, q], r1)
+
+
+def test_score4_query_scale_fold_at_random_scales(oracle_mod):
+    """FP4 keys take the same folded weight w' = fl(w * sq): scores of queries
+    with sq far from 1 lie within the rounding bound of the fp64 score over the
+    dequantised query sq * E4M3(code) with the unfolded weight w."""
+    g = np.random.default_rng(46)
+    x = g.standard_normal((50, 64)).astype(np.float32)
+    codes, scales = oracle_mod.idx4_quant_rows(x)
+    for i in range(50):
+        mag = 10.0 ** (g.uniform(-3.0, 1.3) if i % 2 else g.uniform(3.0, 4.5))
+        iq = (g.standard_normal((4, 64)) * mag).astype(np.float32)
+        iw = g.random(4).astype(np.float32)
+        qc, wq = oracle_mod.quant_iq(iq, iw)
+        sq = np.abs(iq).max(axis=1) / np.float32(448.0)
+        assert np.all(np.abs(np.log2(sq)) > 1.0)
+        qhat = e4m3_value(qc) * sq[:, None].astype(np.float64)
+        k = dequant4(codes[i], scales[i])
+        dots = qhat @ k
+        exact = sum(float(w) * max(d, 0.0) for w, d in zip(iw, dots))
+        mag = sum(float(w) * float(np.abs(qhat[h] * k).sum()) for h, w in enumerate(iw))
+        got = oracle_mod.score4(qc, wq, codes[i], scales[i])
+        assert abs(got - exact) <= 2.0 ** -18 * mag + 2.0 ** -21 * abs(exact) + 1e-45, (i, got, exact)
