@@ -52,7 +52,7 @@ EXPORTS = ("csa2_quant_fp4", "csa2_quant_fp8", "csa2_write_entries", "csa2_write
            "csa2_workspace_size",
            "csa2_status_str", "csa2_abi_version", "csa2_codec_probe",
            "csa2_quant_idx_fp4", "csa2_write_entries_proj_fp4", "csa2_index_full_fp4",
-           "csa2_index_full_fp4_timed", "csa2_index_reindex_fp4")
+           "csa2_index_full_fp4_timed", "csa2_index_reindex_fp4", "csa2_rope_table")
 
 _lib = None
 
@@ -93,6 +93,7 @@ _SIGS = {
     "csa2_workspace_size": (_sz, [_int, _int, _int, _i64, _int, _int, _int]),
     "csa2_status_str": (ctypes.c_char_p, [_int]),
     "csa2_abi_version": (_int, []),
+    "csa2_rope_table": (_int, [_vp, _i64, ctypes.c_double, _vp]),
     "csa2_codec_probe": (_int, [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),
     "csa2_quant_idx_fp4": (_int, [_vp, _i64, _vp, _vp, _vp, _vp]),
     "csa2_write_entries_proj_fp4": (_int, [_vp, _vp, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -146,6 +147,13 @@ def _ptr(t, dtype, name, numel=None):
     if numel is not None and t.numel() < numel:
         raise ValueError(f"{name}: needs at least {numel} elements, has {t.numel()}")
     return t.data_ptr()
+
+
+def _check_batch(cache, B, what):
+    """The kernels address cache rows b*cap + position for b < B: a query batch
+    larger than the cache's would read past its arrays."""
+    if B < 0 or B > cache.B:
+        raise ValueError(f"{what}: a batch of {B} sequences does not fit the cache's {cache.B}")
 
 
 def _stream(stream):
@@ -211,13 +219,13 @@ class Cache:
 
 
 def rope_table(positions, base=10000.0):
-    """(cos, sin) of position * base^(-j/32), j < 32, in fp64, rounded to fp32.
-
-    Host-side table that csa2_quant_fp4 takes as input: [n][32][2] float32."""
-    pos = np.asarray(positions, dtype=np.float64).reshape(-1, 1)
-    theta = np.power(float(base), -np.arange(32, dtype=np.float64) / 32.0)
-    ang = pos * theta[None, :]
-    return np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+    """The write path's rotation table for these positions: [n][32][2] float32
+    (cos, sin), computed by the library's host function csa2_rope_table."""
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int64).reshape(-1))
+    cs = np.empty((pos.size, 32, 2), np.float32)
+    rc = lib().csa2_rope_table(pos.ctypes.data, pos.size, float(base), cs.ctypes.data)
+    _check(rc, "csa2_rope_table")
+    return cs
 
 
 # ---------------------------------------------------------------------------
@@ -328,6 +336,7 @@ def index_full(cache, iq, iw, n_vis, topk_idx, pool_idx=None, topk=DEFAULT_TOPK,
     topk_idx [B][Q][topk] i32, pool_idx [B][Q][pool_blocks] i32.
     scan_timer: optional KernelTimer whose events bracket the scan kernel."""
     B, Q = iq.shape[0], iq.shape[1]
+    _check_batch(cache, B, "index_full")
     need = workspace_size(OP_INDEX_FULL, B, Q, cache.cap, topk, pool_blocks, 0)
     if ws is None:
         ws = alloc_workspace(need, iq.device)
@@ -345,6 +354,7 @@ def index_full(cache, iq, iw, n_vis, topk_idx, pool_idx=None, topk=DEFAULT_TOPK,
 def index_reindex(cache, iq, iw, n_vis, pool_idx, topk_idx, topk=DEFAULT_TOPK, ws=None,
                   stream=None):
     B, Q = iq.shape[0], iq.shape[1]
+    _check_batch(cache, B, "index_reindex")
     pool_blocks = pool_idx.shape[-1]
     need = workspace_size(OP_INDEX_REINDEX, B, Q, cache.cap, topk, pool_blocks, 0)
     if ws is None:
@@ -365,6 +375,7 @@ def sparse_attn_decode(q, cache, topk_idx, swa_k, swa_v, swa_ks, swa_vs, swa_len
     swa_len [B] i32 -> out [B][H][128], lse [B][H].
     timer: optional KernelTimer; its next event pair brackets the kernel's dispatch."""
     B, H = q.shape[0], q.shape[1]
+    _check_batch(cache, B, "sparse_attn_decode")
     topk = topk_idx.shape[-1]
     sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else sm_scale
     need = workspace_size(OP_ATTN_DECODE, B, 1, cache.cap, topk, 0, H)
@@ -395,6 +406,8 @@ def sparse_attn_decode_reuse(q, cache, topk_idx, topk, stage, stage_mode, swa_k,
     bytes); STAGE_READ: take the records from `stage` (cache and topk_idx may
     be None)."""
     B, H = q.shape[0], q.shape[1]
+    if cache is not None:
+        _check_batch(cache, B, "sparse_attn_decode_reuse")
     sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else sm_scale
     cap = cache.cap if cache is not None else 1
     need = workspace_size(OP_ATTN_DECODE, B, 1, cap, topk, 0, H)
@@ -428,6 +441,7 @@ def sparse_attn_chunk(q, cache, topk_idx, swa_k, swa_v, swa_ks, swa_vs, out, lse
                       ws=None, stream=None):
     """q [B][Q][H][128]; topk_idx [B][Q][topk]; chunk window swa_k/v [B][Q][128], swa_ks/vs [B][Q]."""
     B, Q, H = q.shape[0], q.shape[1], q.shape[2]
+    _check_batch(cache, B, "sparse_attn_chunk")
     topk = topk_idx.shape[-1]
     sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else sm_scale
     need = workspace_size(OP_ATTN_CHUNK, B, Q, cache.cap, topk, 0, H)

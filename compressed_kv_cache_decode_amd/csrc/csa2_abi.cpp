@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <cmath>
+
 #include <hip/hip_runtime.h>
 
 #include "csa2.h"
@@ -124,6 +126,28 @@ int hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_E_HIP; }
 extern "C" {
 
 __attribute__((visibility("default"))) int csa2_abi_version(void) { return CSA2_ABI_VERSION; }
+
+// Rotation table of the write path: entries are quantised after RoPE.  For
+// each position p and channel pair j < 32 the angle is p * base^(-j/32),
+// formed in double precision; its cosine and sine are rounded once to fp32.
+__attribute__((visibility("default"))) int csa2_rope_table(const int64_t* positions, int64_t n,
+                                                           double base, float* cs) {
+    if (n < 0 || !(base > 1.0) || !(base < 1.0e300)) return CSA2_E_ARG;
+    if (n == 0) return CSA2_OK;
+    if (!positions || !cs) return CSA2_E_ARG;
+    double freq[32];
+    for (int j = 0; j < 32; ++j) freq[j] = std::pow(base, -(double)j / 32.0);
+    for (int64_t i = 0; i < n; ++i) {
+        const double pos = (double)positions[i];
+        float* row = cs + i * 64;
+        for (int j = 0; j < 32; ++j) {
+            const double angle = pos * freq[j];
+            row[2 * j] = (float)std::cos(angle);
+            row[2 * j + 1] = (float)std::sin(angle);
+        }
+    }
+    return CSA2_OK;
+}
 
 __attribute__((visibility("default"))) const char* csa2_status_str(int status) {
     switch (status) {

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 2
+#define CSA2_ABI_VERSION 3
 
 #define CSA2_HEAD_DIM 128        /* main K and V width */
 #define CSA2_KV_CODE_BYTES 128   /* per entry: K 64 B | V 64 B */
@@ -424,6 +424,22 @@ const char* csa2_status_str(int status);
 
 /* CSA2_ABI_VERSION of the built library. */
 int csa2_abi_version(void);
+
+/*
+ * csa2_rope_table -- HOST function: the rotation table that csa2_quant_fp4 and
+ * the write-entry calls take as `rope_cs` ("DeepSeek V4.1 Flash is live",
+ * section "cache precision and persistence tiers": entries are quantised after
+ * RoPE; RoPE on K channels 0..63 in interleaved pairs, base 10000).
+ *   positions  [n] int64 HOST array: absolute position of each entry.
+ *   n          number of positions (0: nothing is written).
+ *   base       rotation base (10000 for CSA2), > 1.
+ *   cs         [n][32][2] fp32 HOST array, caller-owned, written only:
+ *              cs[i][j] = (cos a, sin a) with a = positions[i] * base^(-j/32)
+ *              evaluated in double precision and rounded once to fp32.
+ * Returns CSA2_E_ARG for n < 0, base <= 1 or a null array with n > 0.  Runs on
+ * the calling thread; touches no HIP state.
+ */
+int csa2_rope_table(const int64_t* positions, int64_t n, double base, float* cs);
 
 /*
  * csa2_codec_probe -- diagnostics: runs the library's own device codecs.

@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.csa2_abi_version() == 2
+    assert lib.csa2_abi_version() == 3
     for st in (0, -1, -2, -3, -4):
         assert lib.csa2_status_str(st)
     assert lib.csa2_status_str(12345) == b"unknown status"
@@ -198,3 +198,43 @@ def test_projected_write_and_fp4_key_validation(lib):
 def test_reindex_query_count_limit(lib):
     r = lib.csa2_index_reindex
     assert r(FAKE, FAKE, 1024, 2, 40000, FAKE, FAKE, FAKE, FAKE, 16, 8, FAKE, FAKE, 1 << 40, None) == -2
+
+
+def test_rope_table_host_export(lib, oracle_mod):
+    """The library's rotation table equals the oracle's independent one bit for
+    bit, at small and large positions, and rejects bad arguments."""
+    import numpy as np
+    import compressed_kv_cache_decode_amd as csa2
+    pos = np.concatenate([np.arange(0, 300), np.arange(131000, 131100), [1 << 20, (1 << 24) - 1]])
+    np.testing.assert_array_equal(csa2.rope_table(pos), oracle_mod.rope_table(pos))
+    assert csa2.rope_table(np.zeros(0, np.int64)).shape == (0, 32, 2)
+    out = (ctypes.c_float * 64)()
+    p = (ctypes.c_int64 * 1)(5)
+    assert lib.csa2_rope_table(p, -1, 10000.0, out) == -1
+    assert lib.csa2_rope_table(p, 1, 1.0, out) == -1
+    assert lib.csa2_rope_table(None, 1, 10000.0, out) == -1
+    assert lib.csa2_rope_table(p, 1, 10000.0, out) == 0
+
+
+def test_batch_larger_than_the_cache_is_rejected_before_any_launch():
+    """The binding refuses a query batch larger than the cache's: the kernels
+    would address rows past the cache arrays.  Checked on the host first, so
+    no GPU is needed here."""
+    import types
+    import torch
+    import compressed_kv_cache_decode_amd as csa2
+    cache = types.SimpleNamespace(B=2, cap=64, idx_fp4=False)
+    iq = torch.zeros((3, 1, 4, 64))
+    with pytest.raises(ValueError, match="does not fit"):
+        csa2.index_full(cache, iq, None, None, None)
+    with pytest.raises(ValueError, match="does not fit"):
+        csa2.index_reindex(cache, iq, None, None, torch.zeros((3, 1, 8)), None)
+    q = torch.zeros((3, 16, 128))
+    with pytest.raises(ValueError, match="does not fit"):
+        csa2.sparse_attn_decode(q, cache, None, None, None, None, None, None, None, None)
+    with pytest.raises(ValueError, match="does not fit"):
+        csa2.sparse_attn_decode_reuse(q, cache, None, 512, None, csa2.STAGE_READ, None, None,
+                                      None, None, None, None, None)
+    with pytest.raises(ValueError, match="does not fit"):
+        csa2.sparse_attn_chunk(torch.zeros((3, 4, 16, 128)), cache, None, None, None, None, None,
+                               None, None)
