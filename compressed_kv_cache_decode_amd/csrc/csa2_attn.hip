@@ -7,37 +7,45 @@
 // section 4: the FP4 cache is dequantised on read and fed to ordinary
 // attention (the saving is storage, not FP4 arithmetic); the SWA KV stays FP8.
 //
-// Design (gfx950).  The entry list of a query (selected records, then window
-// tokens) is cut into tiles of 32 entries.  One workgroup of 8 waves serves
-// one (query, group of 16 heads); wave w takes tiles w, w + 8, w + 16, ... and
-// keeps its own online softmax; the 8 partial states are merged through LDS at
-// the end, so one launch produces the output (no partials in HBM, no second
-// kernel).  All heads share one KV head (MQA), so per tile the logits are a
-// dense [16 heads x 32 entries] contraction on MFMA (v_mfma_f32_16x16x32_f16):
-//   - S^T = K Q^T: the K operand is dequantised straight from the gathered
-//     bytes into registers.  Lane (entry e, quarter g) loads channels
-//     [32g, 32g + 32) of its record, and MFMA step ks consumes channels
-//     32g + 8ks .. +8 from that lane group; q is laid out with the same
-//     channel permutation, which leaves the dot products unchanged.
-//   - O^T += V^T P^T: P comes straight from the S^T registers (each lane holds
-//     entries 4g..4g+3 and 16+4g..16+4g+3 of its head); V is dequantised by the
-//     lanes that own those entries and transposed through a wave-private LDS
-//     tile, so no workgroup barrier sits inside the tile loop.
-//   - dequantised E2M1 x E4M3 values have at most 6 significant bits and lie
-//     in [2^-10, 2688], so they are exact in fp16; E4M3 window codes are exact
-//     in fp16 and their fp32 row scale is applied to the logit (K) or to the
-//     probability (V) in fp32;
-//   - q is split into fp16 hi + lo parts, so q.k carries ~22 bits;
-//   - accumulation is fp32, softmax is online in fp32 (base-2 exponentials).
-// Memory instructions, not bytes, bound a gather this small: every vector load
-// costs the address unit about the same time whatever its width.  So the
-// workgroup reads q, the top-K row and the window scales once into LDS, and
-// each wave gathers a tile's rows with 16-byte loads only: the K operand
-// directly, the V codes and the scale bytes through a wave-private LDS stage
-// from which the lanes pick their operand bytes.  Each wave keeps two tiles'
-// bytes in flight.  Workgroups are numbered so that the head groups of one
-// query land on the same XCD (consecutive workgroup ids go round-robin over
-// the 8 XCDs), sharing its L2 for the gathered rows.
+// Design (gfx950).  A query's entries (selected records, then window tokens)
+// are cut into tiles of 32.  One workgroup of W waves serves one (query, group
+// of 16 heads); wave w takes tiles w, w + W, w + 2W, ..., keeps its own online
+// softmax state, and the W states are merged through LDS at the end, so one
+// launch produces the output.  All heads share one KV head (MQA), so per tile
+// the logits are a dense [32 entries x 16 heads] contraction on MFMA
+// (v_mfma_f32_16x16x32_f16):
+//   - S^T = K Q^T: lane (entry c, quarter g) of row block blk holds channels
+//     [32g, 32g + 32) of entry 16 blk + c (16 bytes of E2M1 codes, or 32 bytes
+//     of E4M3 for a window token); MFMA step ks consumes channels
+//     32g + 8ks .. +8 of that lane group, and q is laid out with the same
+//     channel permutation, which leaves every dot product unchanged.  The lane
+//     loads the two E4M3 group scales of exactly those channels itself (one
+//     2-byte load), so no scale is moved between lanes.
+//   - O^T += V^T P^T: P comes straight from the S^T registers (a lane holds
+//     entries 4g..4g+3 and 16+4g..16+4g+3 of its head); V is dequantised by
+//     the lane that loaded it, written row-major into a wave-private LDS tile
+//     and read back transposed (ds_read_b64_tr_b16) as the A operand.
+//   - the softmax denominator of the selected records is one more MFMA per
+//     tile with an all-ones A operand: it sums exactly the fp16 probabilities
+//     that weight the values.
+//   - dequantised E2M1 x E4M3 values have at most 6 significant bits in
+//     [2^-10, 2688], so they are exact in fp16; E4M3 window codes are exact in
+//     fp16 and their fp32 row scales are applied to the logit (K) and to the
+//     probability (V) in fp32.  A window tile's probabilities times V scales
+//     are brought into [128, 256) per head by a power of two before the fp16
+//     cast, and its PV product is scaled back in fp32, so small window scales
+//     do not fall into fp16 subnormals.
+//   - q * sm_scale * log2(e) is split into fp16 hi + lo (22 significant bits)
+//     after a per-head power-of-two scaling that puts the head's largest
+//     magnitude into [2^14, 2^15); logits are scaled back in fp32.
+//   - softmax is online in fp32 with base-2 exponentials; a wave's reference
+//     maximum moves only when a tile's maximum passes it by more than 8
+//     (log2 units), so most tiles skip the rescale.
+// Absent entries (slots past top-K, positions outside [0, cap), window tokens
+// past the window length) are read from a valid row and masked to -inf, so
+// the loads need no per-entry branches.  Workgroups are numbered so that the
+// head groups of one query land on the same XCD (consecutive workgroup ids go
+// round-robin over the 8 XCDs), sharing its L2 for the gathered rows.
 #include <hip/hip_ext.h>
 
 #include "csa2_device.hpp"
@@ -52,8 +60,8 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 32;           // entries per tile
 // waves per workgroup: 8, or 4 when there are enough (query, head group)
-// workgroups for two of them to share each CU (its LDS holds two 4-wave
-// workgroups, not two 8-wave ones), so that they all run in one round
+// workgroups for two of them to share each CU, so that they all run in one
+// round
 constexpr int kWavesWide = 8, kWavesNarrow = 4;
 constexpr int kGroupHeads = 16;     // heads per workgroup (one MFMA column block)
 constexpr int kVPitch = 144;        // fp16 per V row in LDS (128 + 16)
@@ -61,140 +69,145 @@ constexpr int kMergePitch = kHeadDim + 4;  // fp32 per merged output row in LDS
 constexpr int kXcds = 8;
 constexpr int kCusPerChip = 256;
 constexpr int kMaxWindow = 128;     // window tokens a query attends to
+constexpr int kPosRegs = 4;         // position registers per wave: 2 tiles each
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag the true max
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// LDS map (bytes)
-constexpr int kWaveBytes = kTile * kVPitch * 2;              // one wave's V tile
-constexpr int kOffQ = 0;                                     // q [16][128] fp32
-constexpr int kOffWin = kOffQ + kGroupHeads * kHeadDim * 4;  // window K scales [128], V scales [128]
-constexpr int kOffWave = kOffWin + 2 * kMaxWindow * 4;       // per-wave V tiles
-constexpr int lds_bytes(int W) { return kOffWave + W * kWaveBytes; }
-constexpr int merge_bytes(int W) {
-    return (W * kGroupHeads * kMergePitch + 2 * W * kGroupHeads) * 4;
-}
-static_assert(merge_bytes(kWavesWide) <= kWavesWide * kWaveBytes, "merge area aliases the wave areas");
-static_assert(merge_bytes(kWavesNarrow) <= kWavesNarrow * kWaveBytes, "merge area aliases the wave areas");
+// LDS: per-wave V tiles, then the merge area (each wave's output rows,
+// reference maxima and sums), so a wave can store its state as soon as its
+// own tiles are done
+constexpr int kWaveBytes = kTile * kVPitch * 2;
+constexpr int merge_bytes(int W) { return (W * kGroupHeads * kMergePitch + 2 * W * kGroupHeads) * 4; }
+// q of the workgroup's 16 heads as fp16 hi and lo rows, and each head's scale
+constexpr int kQPitch = kHeadDim + 8;  // fp16 per q row
+constexpr int kQBytes = 2 * kGroupHeads * kQPitch * 2 + kGroupHeads * 4;
+constexpr int lds_bytes(int W) { return W * kWaveBytes + merge_bytes(W) + kQBytes; }
 static_assert(lds_bytes(kWavesWide) <= 160 * 1024, "LDS");
 static_assert(2 * lds_bytes(kWavesNarrow) <= 160 * 1024, "two narrow workgroups per CU");
 
+// Stage of a layer group (raw bytes of the selected records as the lanes hold
+// them): per tile four 1 KiB planes of 16 bytes per lane (K block 0, K block
+// 1, V half 0, V half 1), two 256-byte planes of one dword per lane (K scale
+// pairs, V scale pairs) and the 32-bit presence mask.
+constexpr int kStageK0 = 0, kStageK1 = 1024, kStageV0 = 2048, kStageV1 = 3072;
+constexpr int kStageKs = 4096, kStageVs = 4352, kStageValid = 4608;
+static_assert(kStageValid + 4 <= kStageTileBytes, "stage tile");
+
 size_t attn_workspace_bytes(int64_t, int, int, int) { return 0; }
 
-// What one workgroup needs to locate its entries.
+// Where one workgroup finds its entries.
 struct SeqView {
-    const uint8_t* kvc;
-    const uint8_t* kvs;
-    const uint8_t* swk;
+    const uint8_t* kvc;    // this sequence's code rows
+    const uint8_t* kvs;    // this sequence's scale rows
+    const uint8_t* swk;    // this query's first window row (K codes)
     const uint8_t* swv;
+    const float* swks;     // this query's first window row scale
+    const float* swvs;
     const int32_t* idx;    // this query's top-K row
-    uint8_t* stage;        // this query's staged tiles (stage mode), or null
+    uint8_t* stage;        // this query's staged tiles, or null
     int stage_rem, stage_mod;  // a writing workgroup writes the tiles t with t % mod == rem
     int64_t cap;
-    int64_t b;
     int topk;
-    int swa_rows;
-    int swa_start;  // first window row of this query (chunk: the last 128 tokens up to it)
-    int swa_len;
+    int swa_len;   // window tokens attended (known at process time)
+    int win_rows;  // window rows readable from swk / swv (known at entry)
     int n_tiles_global;
 };
 
-// Position of entry lane % 32 of global tile t, or -1 when absent (slot past
-// topk, or a position outside [0, cap)); lanes 32..63 repeat lanes 0..31.
-__device__ __forceinline__ int32_t tile_position(const SeqView& s, int t, int lane) {
-    const int slot = t * kTile + (lane & (kTile - 1));
-    const int32_t p = slot < s.topk ? s.idx[slot] : -1;
-    return (p >= 0 && p < s.cap) ? p : -1;
-}
+// Raw bytes of one tile of selected records held by one lane (c = lane & 15,
+// g = lane >> 4, q4 = lane & 3):
+//   k[blk]  E2M1 codes of entry 16 blk + c, channels [32g, 32g + 32)
+//   v[j]    E2M1 codes of entry 16j + lane/4, channels [32 q4, +32)
+//   ks      E4M3 scales of the lane's K channels: bits 0..15 for block 0
+//           (groups 2g, 2g + 1), bits 16..31 for block 1
+//   vs      the same for the lane's V channels (groups 2 q4, 2 q4 + 1)
+//   valid   bit e: entry e of the tile is present (equal in every lane)
+struct GTile {
+    u32x4_t k[2];
+    u32x4_t v[2];
+    uint32_t ks, vs;
+    uint32_t valid;
+};
 
-// position of entry e of the tile, from the lane that loaded it (or -1)
-__device__ __forceinline__ int32_t entry_position(int32_t pos, int e) {
-    return __builtin_amdgcn_ds_bpermute(e << 2, pos);
-}
-
-// window row of token e of window tile t, or -1
-__device__ __forceinline__ int64_t window_row(const SeqView& s, int t, int e) {
-    const int tok = (t - s.n_tiles_global) * kTile + e;
-    return tok < s.swa_len ? s.b * s.swa_rows + s.swa_start + tok : -1;
-}
-
-// Raw bytes of one tile held by one lane (c = lane & 15, g = lane >> 4).
-// Absent rows load nothing and read as zero.
-//   k[blk]  K operand of entry 16 blk + c, channels [32g, 32g + 32):
-//           global 16 B of E2M1 codes (k[blk][0]); window 32 B of E4M3 (k[blk][0..1])
-//   v       V codes, whole 64-byte sectors per group of lanes: global v[j] = channels
-//           [32q, 32q + 32) of entry 16j + lane/4 (q = lane & 3); window v[j] =
-//           channels [16q8, 16q8 + 16) of token 8j + lane/8 (q8 = lane & 7)
-//   sc      global, lanes 0..31: the 16 scale bytes (K 0..7, V 8..15) of entry `lane`
-//   valid   bit e: entry e of the tile is present (same in every lane)
-struct TileRegs {
+// Raw bytes of one tile of window tokens held by one lane (q8 = lane & 7):
+//   k[blk][h]  E4M3 codes of token 16 blk + c, channels [32g + 16h, +16)
+//   v[j]       E4M3 codes of token 8j + lane/8, channels [16 q8, +16)
+//   sc         lanes 0..31: fp32 K row scale of token `lane`; lanes 32..63:
+//              V row scale of token `lane - 32`
+struct WTile {
     u32x4_t k[2][2];
     u32x4_t v[4];
-    u32x4_t sc;
-    uint32_t valid;
+    float sc;
 };
 
 __device__ __forceinline__ u32x4_t ld16(const uint8_t* p) {
     return *reinterpret_cast<const u32x4_t*>(p);
 }
 
-// Issue the loads of tile t.  pos: tile_position(s, t, lane) for a global
-// tile (unused for a window tile, or when the tile comes from the stage).
+__device__ __forceinline__ uint32_t ld2(const uint8_t* p) {
+    return *reinterpret_cast<const uint16_t*>(p);
+}
+
+// position of entry e held by lane `src` of a position register
+__device__ __forceinline__ int32_t lane_value(int32_t v, int src) {
+    return __builtin_amdgcn_ds_bpermute(src << 2, v);
+}
+
+// Issue the loads of global tile t.  P: the position register holding the
+// tile (entry e in lane 32 * half + e); STAGE_READ ignores it.
 template <int STAGE>
-__device__ __forceinline__ void fetch_tile(const SeqView& s, int t, int32_t pos, int lane,
-                                           TileRegs& r) {
-    const int c = lane & 15, g = lane >> 4;
-    const u32x4_t z = {0u, 0u, 0u, 0u};
-    if (STAGE == kStageRead && t < s.n_tiles_global) {
-        // the lanes' bytes as the gathering layer held them: 16 coalesced bytes
-        // per lane and register
-        const uint8_t* src = s.stage + (int64_t)t * kStageTileBytes + 16 * lane;
-        r.k[0][0] = ld16(src);
-        r.k[1][0] = ld16(src + 1024);
-        r.v[0] = ld16(src + 2048);
-        r.v[1] = ld16(src + 3072);
-        r.sc = lane < kTile ? ld16(src + 4096) : z;
-        r.valid = *reinterpret_cast<const uint32_t*>(s.stage + (int64_t)t * kStageTileBytes + 4608);
-        r.k[0][1] = z;
-        r.k[1][1] = z;
-        r.v[2] = z;
-        r.v[3] = z;
-    } else if (t < s.n_tiles_global) {
-        const int64_t base = s.b * s.cap;
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            const int32_t p = entry_position(pos, 16 * blk + c);
-            r.k[blk][0] = p >= 0 ? ld16(s.kvc + (base + (p >= 0 ? p : 0)) * 128 + 16 * g) : z;
-            r.k[blk][1] = z;
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int32_t p = entry_position(pos, 16 * j + (lane >> 2));
-            r.v[j] = p >= 0 ? ld16(s.kvc + (base + (p >= 0 ? p : 0)) * 128 + 64 + 16 * (lane & 3)) : z;
-        }
-        r.v[2] = z;
-        r.v[3] = z;
-        const bool has = lane < kTile && pos >= 0;
-        r.sc = has ? ld16(s.kvs + (base + (has ? pos : 0)) * 16) : z;
-        r.valid = (uint32_t)__builtin_amdgcn_ballot_w64(has);
-    } else {
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            const int64_t row = window_row(s, t, 16 * blk + c);
-            const uint8_t* src = s.swk + (row >= 0 ? row : 0) * kHeadDim + 32 * g;
-            r.k[blk][0] = row >= 0 ? ld16(src) : z;
-            r.k[blk][1] = row >= 0 ? ld16(src + 16) : z;
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t vrow = window_row(s, t, 8 * j + (lane >> 3));
-            r.v[j] = vrow >= 0 ? ld16(s.swv + (vrow >= 0 ? vrow : 0) * kHeadDim + 16 * (lane & 7)) : z;
-        }
-        r.sc = z;
-        const int tok0 = (t - s.n_tiles_global) * kTile;
-        const int nv = s.swa_len - tok0;  // >= 1: window tiles end at swa_len
-        r.valid = nv >= kTile ? 0xFFFFFFFFu : ((1u << nv) - 1u);
+__device__ __forceinline__ void fetch_global(const SeqView& s, int t, int32_t P, int half,
+                                             int lane, GTile& r) {
+    const int c = lane & 15, g = lane >> 4, q4 = lane & 3;
+    if (STAGE == kStageRead) {
+        const uint8_t* src = s.stage + (int64_t)t * kStageTileBytes;
+        r.k[0] = ld16(src + kStageK0 + 16 * lane);
+        r.k[1] = ld16(src + kStageK1 + 16 * lane);
+        r.v[0] = ld16(src + kStageV0 + 16 * lane);
+        r.v[1] = ld16(src + kStageV1 + 16 * lane);
+        r.ks = *reinterpret_cast<const uint32_t*>(src + kStageKs + 4 * lane);
+        r.vs = *reinterpret_cast<const uint32_t*>(src + kStageVs + 4 * lane);
+        r.valid = *reinterpret_cast<const uint32_t*>(src + kStageValid);  // same in every lane
+        return;
     }
+    // P holds -1 for absent entries; they read row 0 and are masked later
+    const int base = 32 * half;
+    const int32_t pk0 = lane_value(P, base + c), pk1 = lane_value(P, base + 16 + c);
+    const int32_t pv0 = lane_value(P, base + (lane >> 2)), pv1 = lane_value(P, base + 16 + (lane >> 2));
+    const int64_t rk0 = pk0 < 0 ? 0 : pk0, rk1 = pk1 < 0 ? 0 : pk1;
+    const int64_t rv0 = pv0 < 0 ? 0 : pv0, rv1 = pv1 < 0 ? 0 : pv1;
+    r.k[0] = ld16(s.kvc + rk0 * 128 + 16 * g);
+    r.k[1] = ld16(s.kvc + rk1 * 128 + 16 * g);
+    r.v[0] = ld16(s.kvc + rv0 * 128 + 64 + 16 * q4);
+    r.v[1] = ld16(s.kvc + rv1 * 128 + 64 + 16 * q4);
+    const uint32_t ks0 = ld2(s.kvs + rk0 * 16 + 2 * g), ks1 = ld2(s.kvs + rk1 * 16 + 2 * g);
+    const uint32_t vs0 = ld2(s.kvs + rv0 * 16 + 8 + 2 * q4), vs1 = ld2(s.kvs + rv1 * 16 + 8 + 2 * q4);
+    r.ks = ks0 | (ks1 << 16);
+    r.vs = vs0 | (vs1 << 16);
+    r.valid = (uint32_t)(__builtin_amdgcn_ballot_w64(P >= 0) >> base);
+}
+
+// Issue the loads of window tile j (tokens [32j, 32j + 32) of the query's
+// window).  Rows past the readable window rows read its first row; which
+// tokens count is decided when the tile is processed.
+__device__ __forceinline__ void fetch_window(const SeqView& s, int j, int lane, WTile& r) {
+    const int c = lane & 15, g = lane >> 4;
+    const int tok0 = j * kTile;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const int tok = tok0 + 16 * blk + c;
+        const uint8_t* src = s.swk + (int64_t)(tok < s.win_rows ? tok : 0) * kHeadDim + 32 * g;
+        r.k[blk][0] = ld16(src);
+        r.k[blk][1] = ld16(src + 16);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const int tok = tok0 + 8 * jj + (lane >> 3);
+        r.v[jj] = ld16(s.swv + (int64_t)(tok < s.win_rows ? tok : 0) * kHeadDim + 16 * (lane & 7));
+    }
+    const int tok = tok0 + (lane & 31);
+    const int row = tok < s.win_rows ? tok : 0;
+    r.sc = lane < 32 ? s.swks[row] : s.swvs[row];
 }
 
 // max / sum over the four lanes c, c+16, c+32, c+48 (v_permlane*_swap: each
@@ -219,9 +232,11 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Eight E2M1 codes times an fp16 scale, as one MFMA operand.
-__device__ __forceinline__ half8_t fp4x8_h8(uint32_t w, _Float16 sc) {
-    const half2_t s2 = {sc, sc};
+// Eight E2M1 codes times an fp16 scale pair element (SEL 0: low, 1: high), as
+// one MFMA operand.
+template <int SEL>
+__device__ __forceinline__ half8_t fp4x8_h8(uint32_t w, half2_t s) {
+    const half2_t s2 = __builtin_shufflevector(s, s, SEL, SEL);
     const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
     const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
     const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
@@ -244,169 +259,194 @@ __device__ __forceinline__ half8_t fp8x8_h8(uint32_t w0, uint32_t w1) {
 
 struct WaveState {
     float4_t o[8];  // O^T[dim 16 dt + 4g + r][head c], relative to m
+    float4_t lsum;  // sum of the fp16 probabilities of selected records (all four equal)
+    float lwin;     // this lane's share of the window tokens' probabilities
     float m;        // reference (base-2 logit) of head c; lags its running max by < 8
-    float l;        // this lane's share of the running sum, relative to m
 };
 
 // The lane's C entries: 4g + i (i < 4) and 16 + 4g + i - 4 (i >= 4).
 __device__ __forceinline__ int c_entry(int i, int g) { return i < 4 ? 4 * g + i : 12 + 4 * g + i; }
 
-// One tile: V into LDS, logits, online softmax, PV.  GLOBAL: a tile of
-// selected FP4 records, else a tile of FP8 window tokens.
-template <bool GLOBAL, int STAGE>
-__device__ __forceinline__ void process_tile(const SeqView& s, int t, const TileRegs& r,
-                                             const float* __restrict__ win_l,
-                                             const half8_t (&qhi)[4], const half8_t (&qlo)[4],
-                                             _Float16* __restrict__ vtile, int lane,
-                                             WaveState& st) {
-    const int c = lane & 15, g = lane >> 4;
-    constexpr bool global = GLOBAL;
-
-    if (global && STAGE == kStageWrite && t % s.stage_mod == s.stage_rem) {
-        // hand the gathered bytes on to the layers that reuse this selection
-        uint8_t* dst = s.stage + (int64_t)t * kStageTileBytes;
-        u32x4_t* d = reinterpret_cast<u32x4_t*>(dst + 16 * lane);
-        d[0] = r.k[0][0];
-        d[64] = r.k[1][0];
-        d[128] = r.v[0];
-        d[192] = r.v[1];
-        if (lane < kTile) d[256] = r.sc;
-        if (lane == 0) *reinterpret_cast<uint32_t*>(dst + 4608) = r.valid;
-    }
-
-    // scale bytes come from the lane that loaded the entry's 16-byte chunk:
-    // K scales 2g, 2g + 1 of entries c and 16 + c; V scales 2q, 2q + 1 of
-    // entries lane/4 and 16 + lane/4
-    const int q4 = lane & 3;
-    uint32_t ksc[2] = {0u, 0u}, vsc[2] = {0u, 0u};
-    if (global) {
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            const int src = (16 * blk + c) << 2;
-            const uint32_t d0 = __builtin_amdgcn_ds_bpermute(src, r.sc[0]);
-            const uint32_t d1 = __builtin_amdgcn_ds_bpermute(src, r.sc[1]);
-            ksc[blk] = ((g >> 1) ? d1 : d0) >> (16 * (g & 1));
-            const int vsrc = (16 * blk + (lane >> 2)) << 2;
-            const uint32_t d2 = __builtin_amdgcn_ds_bpermute(vsrc, r.sc[2]);
-            const uint32_t d3 = __builtin_amdgcn_ds_bpermute(vsrc, r.sc[3]);
-            vsc[blk] = ((q4 >> 1) ? d3 : d2) >> (16 * (q4 & 1));
-        }
-    }
-
-    // ---- V codes of the lane, dequantised, row-major into the wave's V tile ----
-    if (global) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            half8_t* dst = reinterpret_cast<half8_t*>(vtile + (16 * j + (lane >> 2)) * kVPitch + 32 * q4);
-            const _Float16 s0 = e4m3_to_f16(vsc[j] & 0xFFu), s1 = e4m3_to_f16((vsc[j] >> 8) & 0xFFu);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) dst[m] = fp4x8_h8(r.v[j][m], m < 2 ? s0 : s1);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            half8_t* dst = reinterpret_cast<half8_t*>(vtile + (8 * j + (lane >> 3)) * kVPitch + 16 * (lane & 7));
-            dst[0] = fp8x8_h8(r.v[j][0], r.v[j][1]);
-            dst[1] = fp8x8_h8(r.v[j][2], r.v[j][3]);
-        }
-    }
-
-    // ---- S^T = K Q^T (base-2 logits up to the window row scale) ----
-    float4_t sacc[2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-        half8_t ka[4];
-        if (global) {
-            const uint32_t sb = ksc[blk];
-            const _Float16 s0 = e4m3_to_f16(sb & 0xFFu), s1 = e4m3_to_f16((sb >> 8) & 0xFFu);
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) ka[ks] = fp4x8_h8(r.k[blk][0][ks], ks < 2 ? s0 : s1);
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                ka[ks] = fp8x8_h8(r.k[blk][ks >> 1][2 * (ks & 1)], r.k[blk][ks >> 1][2 * (ks & 1) + 1]);
-        }
-        float4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[ks], qhi[ks], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[ks], qlo[ks], acc, 0, 0, 0);
-        }
-        sacc[blk] = acc;
-    }
-
-    // ---- logits of the lane's C entries; absent entries are -inf ----
-    float x[8], vmul[8];
-    const uint32_t vbits = ((r.valid >> (4 * g)) & 0xFu) | (((r.valid >> (16 + 4 * g)) & 0xFu) << 4);
-    if (global) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            x[i] = (vbits >> i & 1u) ? sacc[i >> 2][i & 3] : -INFINITY;
-            vmul[i] = 1.0f;
-        }
-    } else {
-        const int tok0 = (t - s.n_tiles_global) * kTile;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int tok = tok0 + c_entry(i, g);
-            x[i] = (vbits >> i & 1u) ? sacc[i >> 2][i & 3] * win_l[tok] : -INFINITY;
-            vmul[i] = win_l[kMaxWindow + tok];
-        }
-    }
-
-    // ---- online softmax; the reference m moves only when the tile max passes
-    // it by more than the slack, so most tiles skip the rescale ----
-    float tmax = x[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
-    tmax = xmax4(tmax);
+// Raise the reference maximum when this tile's maximum passes it by more than
+// the slack (uniform branch over the wave).
+__device__ __forceinline__ void online_rescale(float tmax, WaveState& st) {
     const bool move = tmax > st.m + kRescaleSlack || (st.m == -INFINITY && tmax != -INFINITY);
-    if (__builtin_amdgcn_ballot_w64(move)) {  // uniform branch
+    if (__builtin_amdgcn_ballot_w64(move)) {
         const float m_new = move ? tmax : st.m;
         const float alpha = (st.m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(st.m - m_new);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) st.o[dt] *= alpha;
-        st.l *= alpha;
+        st.lsum *= alpha;
+        st.lwin *= alpha;
         st.m = m_new;
     }
-    half8_t pb;
-    float psum = 0.0f;
-    if (st.m == -INFINITY) {
+}
+
+// Transposed V operands from the wave's row-major V tile: in each 16-lane
+// group, lane 4j + i/4 supplies channels [16dt + 4(i/4), +4) of the entry at
+// k slot j, and lane i receives channel 16dt + i of the four entries.
+__device__ __forceinline__ half8_t v_operand(const _Float16* vtile, int lane, int dt) {
+    const int sq = lane & 15, g = lane >> 4;
+    const int ent0 = 4 * g + (sq >> 2), ent1 = 16 + 4 * g + (sq >> 2);
+    const int col = 16 * dt + 4 * (sq & 3);
+    const half4_t v0 = __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) short4_t*)(vtile + ent0 * kVPitch + col)));
+    const half4_t v1 = __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) short4_t*)(vtile + ent1 * kVPitch + col)));
+    return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// One tile of selected FP4 records.
+template <int STAGE>
+__device__ __forceinline__ void process_global(const SeqView& s, int t, const GTile& r,
+                                               const half8_t (&qhi)[4], const half8_t (&qlo)[4],
+                                               float qmul, _Float16* __restrict__ vtile, int lane,
+                                               WaveState& st) {
+    const int g = lane >> 4;
+    if (STAGE == kStageWrite && t % s.stage_mod == s.stage_rem) {
+        // hand the gathered bytes on to the layers that reuse this selection
+        uint8_t* dst = s.stage + (int64_t)t * kStageTileBytes;
+        *reinterpret_cast<u32x4_t*>(dst + kStageK0 + 16 * lane) = r.k[0];
+        *reinterpret_cast<u32x4_t*>(dst + kStageK1 + 16 * lane) = r.k[1];
+        *reinterpret_cast<u32x4_t*>(dst + kStageV0 + 16 * lane) = r.v[0];
+        *reinterpret_cast<u32x4_t*>(dst + kStageV1 + 16 * lane) = r.v[1];
+        *reinterpret_cast<uint32_t*>(dst + kStageKs + 4 * lane) = r.ks;
+        *reinterpret_cast<uint32_t*>(dst + kStageVs + 4 * lane) = r.vs;
+        if (lane == 0) *reinterpret_cast<uint32_t*>(dst + kStageValid) = r.valid;
+    }
+    const uint32_t valid = __builtin_amdgcn_readfirstlane(r.valid);
+    if (valid == 0u) return;  // uniform: nothing present (padding)
+
+    // ---- V: dequantised row-major into the wave's V tile ----
+    {
+        const int q4 = lane & 3;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pb[i] = (_Float16)0.0f;
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float p = __builtin_amdgcn_exp2f(x[i] - st.m);  // x - m <= 8; -inf -> 0
-            psum += p;
-            pb[i] = (_Float16)(p * vmul[i]);
+        for (int j = 0; j < 2; ++j) {
+            half8_t* dst = reinterpret_cast<half8_t*>(vtile + (16 * j + (lane >> 2)) * kVPitch + 32 * q4);
+            const half2_t sv = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.vs >> (16 * j), 1.0f, false);
+            dst[0] = fp4x8_h8<0>(r.v[j][0], sv);
+            dst[1] = fp4x8_h8<0>(r.v[j][1], sv);
+            dst[2] = fp4x8_h8<1>(r.v[j][2], sv);
+            dst[3] = fp4x8_h8<1>(r.v[j][3], sv);
         }
     }
-    st.l += psum;
+
+    // ---- S^T = K Q^T (scaled base-2 logits) ----
+    float4_t sacc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const half2_t sk = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.ks >> (16 * blk), 1.0f, false);
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const half8_t ka = ks < 2 ? fp4x8_h8<0>(r.k[blk][ks], sk) : fp4x8_h8<1>(r.k[blk][ks], sk);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qhi[ks], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qlo[ks], acc, 0, 0, 0);
+        }
+        sacc[blk] = acc;
+    }
+
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = sacc[i >> 2][i & 3];
+    if (valid != 0xFFFFFFFFu) {  // uniform: mask the absent entries
+        const uint32_t vb = ((valid >> (4 * g)) & 0xFu) | (((valid >> (16 + 4 * g)) & 0xFu) << 4);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (vb >> i) & 1u ? x[i] : -INFINITY;
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    tmax = xmax4(tmax) * qmul;
+    online_rescale(tmax, st);
+    half8_t pb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pb[i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(x[i], qmul, -st.m));
 
     wave_lds_sync();
-    // ---- O^T += V^T P^T; the A operand is read transposed from the row-major
-    // V tile: in each 16-lane group, lane 4j + i/4 supplies channels
-    // [16dt + 4(i/4), +4) of the entry at k slot j, and lane i receives channel
-    // 16dt + i of the four entries ----
-    const int sq = lane & 15;
-    const int ent0 = 4 * g + (sq >> 2), ent1 = 16 + 4 * g + (sq >> 2);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-        const int col = 16 * dt + 4 * (sq & 3);
-        const half4_t v0 = __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) short4_t*)(vtile + ent0 * kVPitch + col)));
-        const half4_t v1 = __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) short4_t*)(vtile + ent1 * kVPitch + col)));
-        const half8_t va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, st.o[dt], 0, 0, 0);
-    }
+    for (int dt = 0; dt < 8; ++dt)
+        st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v_operand(vtile, lane, dt), pb, st.o[dt], 0, 0, 0);
+    const half8_t ones = {1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16};
+    st.lsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb, st.lsum, 0, 0, 0);
     wave_lds_sync();  // the next tile rewrites the V tile
 }
 
-// grid = ceil(n_q / 8) * 8 * (H / 16) workgroups of 512 threads.
-// Workgroup id -> (query bq, head group hg): ids with the same id % 8 share an
-// XCD, and all head groups of one query get ids with the same id % 8.
+// One tile of FP8 window tokens, of which the first n (>= 1) are attended.
+__device__ __forceinline__ void process_window(const WTile& r, int n, const half8_t (&qhi)[4],
+                                               const half8_t (&qlo)[4], float qmul,
+                                               _Float16* __restrict__ vtile, int lane,
+                                               WaveState& st) {
+    const int g = lane >> 4;
+    const uint32_t valid = n >= kTile ? 0xFFFFFFFFu : ((1u << n) - 1u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        half8_t* dst = reinterpret_cast<half8_t*>(vtile + (8 * j + (lane >> 3)) * kVPitch + 16 * (lane & 7));
+        dst[0] = fp8x8_h8(r.v[j][0], r.v[j][1]);
+        dst[1] = fp8x8_h8(r.v[j][2], r.v[j][3]);
+    }
+    float4_t sacc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const half8_t ka = fp8x8_h8(r.k[blk][ks >> 1][2 * (ks & 1)], r.k[blk][ks >> 1][2 * (ks & 1) + 1]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qhi[ks], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qlo[ks], acc, 0, 0, 0);
+        }
+        sacc[blk] = acc;
+    }
+    float ksc[8], vsc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int e = c_entry(i, g);
+        ksc[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(e << 2, __float_as_int(r.sc)));
+        vsc[i] = __int_as_float(__builtin_amdgcn_ds_bpermute((32 + e) << 2, __float_as_int(r.sc)));
+    }
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = sacc[i >> 2][i & 3] * qmul * ksc[i];
+    if (valid != 0xFFFFFFFFu) {
+        const uint32_t vb = ((valid >> (4 * g)) & 0xFu) | (((valid >> (16 + 4 * g)) & 0xFu) << 4);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (vb >> i) & 1u ? x[i] : -INFINITY;
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    tmax = xmax4(tmax);
+    online_rescale(tmax, st);
+    float w[8], wmax = 0.0f, psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float p = __builtin_amdgcn_exp2f(x[i] - st.m);
+        psum += p;
+        w[i] = p * vsc[i];
+        wmax = fmaxf(wmax, w[i]);
+    }
+    st.lwin += psum;
+    wmax = xmax4(wmax);
+    // p * V scale of the head, brought into [128, 256) by a power of two; the
+    // exponent is clamped so that both factors stay normal fp32 numbers (a
+    // head whose window weights are all below 2^-100 keeps them as they are,
+    // scaled by 2^108: still far inside the fp16 range)
+    int e = wmax > 0.0f ? __builtin_amdgcn_frexp_expf(wmax) : 0;
+    e = e < -100 ? -100 : (e > 120 ? 120 : e);
+    const float up = __builtin_amdgcn_ldexpf(1.0f, 8 - e), down = __builtin_amdgcn_ldexpf(1.0f, e - 8);
+    half8_t pb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pb[i] = (_Float16)(w[i] * up);
+
+    wave_lds_sync();
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        const float4_t zero = {0.f, 0.f, 0.f, 0.f};
+        const float4_t pv = __builtin_amdgcn_mfma_f32_16x16x32_f16(v_operand(vtile, lane, dt), pb, zero, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.o[dt][i] = fmaf(pv[i], down, st.o[dt][i]);
+    }
+    wave_lds_sync();
+}
+
 // Every argument is needed before the first gather; touching them all at
 // kernel entry makes the compiler fetch them in one batch of scalar loads
 // instead of one dependent batch per first use.
@@ -415,8 +455,11 @@ __device__ __forceinline__ void touch(const T& v) {
     asm volatile("" ::"s"(v));
 }
 
+// grid = ceil(n_q / 8) * 8 * (H / 16) workgroups of W waves.
+// Workgroup id -> (query bq, head group hg): ids with the same id % 8 share an
+// XCD, and all head groups of one query get ids with the same id % 8.
 template <int STAGE, int kWaves>
-__global__ __launch_bounds__(kWaves * 64) void k_attn(AttnArgs a, int n_tiles_global) {
+__global__ __launch_bounds__(kWaves * 64, 2) void k_attn(AttnArgs a, int n_tiles_global) {
     constexpr int kThreads = kWaves * 64;
     __shared__ __attribute__((aligned(16))) unsigned char smem[lds_bytes(kWaves)];
     touch(a.q); touch(a.H); touch(a.Q); touch(a.kvc); touch(a.kvs); touch(a.cap);
@@ -431,120 +474,157 @@ __global__ __launch_bounds__(kWaves * 64) void k_attn(AttnArgs a, int n_tiles_gl
     const int hg = (id / kXcds) - round * G;
     const int64_t bq = (int64_t)round * kXcds + (id % kXcds);
     if (bq >= a.n_q) return;  // uniform over the workgroup
-
-    float* q_l = reinterpret_cast<float*>(smem + kOffQ);
-    float* win_l = reinterpret_cast<float*>(smem + kOffWin);
+    const int64_t b = bq / a.Q;
 
     SeqView s;
-    s.kvc = a.kvc; s.kvs = a.kvs; s.swk = a.swk; s.swv = a.swv;
+    s.kvc = a.kvc + b * a.cap * 128;
+    s.kvs = a.kvs + b * a.cap * 16;
     s.idx = a.idx + bq * a.topk;
     // in a gathering launch the head groups' workgroups share the stage writes
     s.stage = STAGE != 0 ? a.stage + bq * n_tiles_global * kStageTileBytes : nullptr;
     s.stage_rem = hg;
     s.stage_mod = G;
     s.cap = a.cap;
-    s.b = bq / a.Q;
     s.topk = a.topk;
-    s.swa_rows = a.swa_rows;
     s.n_tiles_global = n_tiles_global;
-    const float logit_mul = a.sm_scale * kLog2e;
-
-    // ---- each wave starts gathering its first two tiles at once; tiles of
-    // selected records do not wait for the window length ----
-    const int t0 = wave, t1 = wave + kWaves;
-    TileRegs ra, rb;
-    {
-        const bool pos = STAGE != kStageRead;  // positions needed
-        const int32_t p0 = pos && t0 < n_tiles_global ? tile_position(s, t0, lane) : -1;
-        const int32_t p1 = pos && t1 < n_tiles_global ? tile_position(s, t1, lane) : -1;
-        s.swa_len = 0;  // not read on the path of selected records
-        if (t0 < n_tiles_global) fetch_tile<STAGE>(s, t0, p0, lane, ra);
-        if (t1 < n_tiles_global) fetch_tile<STAGE>(s, t1, p1, lane, rb);
-    }
+    int64_t w0;
     if (a.swa_len != nullptr) {
-        const int sl = a.swa_len[s.b];
-        s.swa_start = 0;
-        s.swa_len = sl < 0 ? 0 : (sl > a.swa_rows ? a.swa_rows : sl);
+        // decode: the sequence's window rows; how many count is read below
+        w0 = b * a.swa_rows;
+        s.win_rows = a.swa_rows;
     } else {
         // chunk query i sees the window tokens [max(0, i - 127), i]
         const int i = (int)(bq % a.Q);
-        s.swa_start = i + 1 > kMaxWindow ? i + 1 - kMaxWindow : 0;
-        s.swa_len = i + 1 - s.swa_start;
+        const int start = i + 1 > kMaxWindow ? i + 1 - kMaxWindow : 0;
+        w0 = b * a.swa_rows + start;
+        s.win_rows = i + 1 - start;
     }
-    const int n_tiles = n_tiles_global + (s.swa_len + kTile - 1) / kTile;
-    if (t0 >= n_tiles_global && t0 < n_tiles) fetch_tile<STAGE>(s, t0, -1, lane, ra);
-    if (t1 >= n_tiles_global && t1 < n_tiles) fetch_tile<STAGE>(s, t1, -1, lane, rb);
+    s.swk = a.swk + w0 * kHeadDim;
+    s.swv = a.swv + w0 * kHeadDim;
+    s.swks = a.swks + w0;
+    s.swvs = a.swvs + w0;
 
-    // ---- meanwhile, once per workgroup: q of the 16 heads, window scales ----
-    {
-        static_assert(kGroupHeads * kHeadDim / 4 % kThreads == 0, "q staging");
-        static_assert(2 * kMaxWindow <= kThreads, "window scales staging");
+    // The wave's tiles: selected-record tiles wave, wave + W, ... (two in
+    // flight), and at most one window tile: window tile j is the
+    // (n_tiles_global + j)-th tile of the query, dealt round robin like the
+    // others.  Every load the wave's first tiles need is issued before
+    // anything waits.
+    const int n_win_max = (s.win_rows + kTile - 1) / kTile;
+    const int jw = ((wave - n_tiles_global) % kWaves + kWaves) % kWaves;
+    const bool has_win = jw < n_win_max;
+    const int t0 = wave, t1 = wave + kWaves;
+    GTile ra, rb;
+    WTile rw;
+    int32_t P[kPosRegs];
+    if (STAGE == kStageRead) {
+        if (t0 < n_tiles_global) fetch_global<STAGE>(s, t0, 0, 0, lane, ra);
+        if (t1 < n_tiles_global) fetch_global<STAGE>(s, t1, 0, 0, lane, rb);
+    } else {
+        // positions of the wave's tiles: tile wave + kW in lanes
+        // 32 (k & 1) .. + 31 of register k / 2 (-1: absent)
 #pragma unroll
-        for (int i = tid; i < kGroupHeads * kHeadDim / 4; i += kThreads)
-            reinterpret_cast<float4*>(q_l)[i] = reinterpret_cast<const float4*>(
-                a.q + (bq * a.H + hg * kGroupHeads) * kHeadDim)[i];
-        float wv = 0.0f;
-        const int tok = tid & (kMaxWindow - 1);
-        if (tid < 2 * kMaxWindow && tok < s.swa_len)
-            wv = (tid < kMaxWindow ? a.swks : a.swvs)[s.b * s.swa_rows + s.swa_start + tok];
-        if (tid < 2 * kMaxWindow) win_l[tid] = wv;
-    }
-    __syncthreads();
-
-    // q * sm_scale * log2(e) (so that logits come out in base-2 units) as fp16
-    // hi + lo, B-operand layout: head c, MFMA step ks takes channels 32g + 8ks .. +8
-    half8_t qhi[4], qlo[4];
-    {
-        const float4* qrow = reinterpret_cast<const float4*>(q_l + c * kHeadDim + 32 * g);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const float4 x0 = qrow[2 * ks], x1 = qrow[2 * ks + 1];
-            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float xq = xs[i] * logit_mul;
-                const _Float16 hq = (_Float16)xq;
-                qhi[ks][i] = hq;
-                qlo[ks][i] = (_Float16)(xq - (float)hq);
-            }
+        for (int k = 0; k < kPosRegs; ++k) {
+            const int t = wave + kWaves * (2 * k + (lane >> 5));
+            const int slot = t * kTile + (lane & 31);
+            int32_t p = -1;
+            if (t < n_tiles_global && slot < s.topk) p = s.idx[slot];
+            P[k] = (p >= 0 && p < s.cap) ? p : -1;
         }
     }
+    // this wave's share of q: heads wave * HPW .. + HPW, 4 channels per lane
+    // and load (lane: head + (lane >> 5), channels 4 (lane & 31) .. + 4)
+    constexpr int kHPW = kGroupHeads / kWaves;
+    float4 xq[kHPW / 2];
+#pragma unroll
+    for (int i = 0; i < kHPW / 2; ++i)
+        xq[i] = reinterpret_cast<const float4*>(
+            a.q + (bq * a.H + hg * kGroupHeads + wave * kHPW + 2 * i + (lane >> 5)) * kHeadDim)[lane & 31];
+    if (has_win) fetch_window(s, jw, lane, rw);
+    if (STAGE != kStageRead) {
+        if (t0 < n_tiles_global) fetch_global<STAGE>(s, t0, P[0], 0, lane, ra);
+        if (t1 < n_tiles_global) fetch_global<STAGE>(s, t1, P[0], 1, lane, rb);
+    }
+    if (a.swa_len != nullptr) {
+        const int sl = a.swa_len[b];
+        s.swa_len = sl < 0 ? 0 : (sl > a.swa_rows ? a.swa_rows : sl);
+    } else {
+        s.swa_len = s.win_rows;
+    }
+    // the position register of the wave's k-th selected tile, loaded now when
+    // it is past the preloaded ones
+    auto tile_pos = [&](int k) -> int32_t {
+        if (k < 2 * kPosRegs) return P[k >> 1];
+        const int t = wave + kWaves * k;
+        const int slot = t * kTile + (lane & 31);
+        int32_t p = slot < s.topk ? s.idx[slot] : -1;
+        return (p >= 0 && p < s.cap) ? p : -1;
+    };
+
+    // q * sm_scale * log2(e), scaled per head by a power of two into
+    // [2^14, 2^15), as fp16 hi + lo rows in LDS; then every wave reads its
+    // B operands: head c, MFMA step ks takes channels 32g + 8ks .. +8
+    _Float16* q_hi = reinterpret_cast<_Float16*>(smem + kWaves * kWaveBytes + merge_bytes(kWaves));
+    _Float16* q_lo = q_hi + kGroupHeads * kQPitch;
+    float* q_mul = reinterpret_cast<float*>(q_lo + kGroupHeads * kQPitch);
+    {
+        const float logit_mul = a.sm_scale * kLog2e;
+#pragma unroll
+        for (int i = 0; i < kHPW / 2; ++i) {
+            const float x[4] = {xq[i].x * logit_mul, xq[i].y * logit_mul, xq[i].z * logit_mul,
+                                xq[i].w * logit_mul};
+            float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+#pragma unroll
+            for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+            int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 0;  // amax in [2^(e-1), 2^e)
+            e = e < -100 ? -100 : (e > 100 ? 100 : e);
+            const int head = wave * kHPW + 2 * i + (lane >> 5);
+            half4_t hv, lv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float v = __builtin_amdgcn_ldexpf(x[j], 15 - e);
+                hv[j] = (_Float16)v;
+                lv[j] = (_Float16)(v - (float)hv[j]);
+            }
+            *reinterpret_cast<half4_t*>(q_hi + head * kQPitch + 4 * (lane & 31)) = hv;
+            *reinterpret_cast<half4_t*>(q_lo + head * kQPitch + 4 * (lane & 31)) = lv;
+            if ((lane & 31) == 0) q_mul[head] = __builtin_amdgcn_ldexpf(1.0f, e - 15);
+        }
+    }
+    __syncthreads();
+    half8_t qhi[4], qlo[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        qhi[ks] = *reinterpret_cast<const half8_t*>(q_hi + c * kQPitch + 32 * g + 8 * ks);
+        qlo[ks] = *reinterpret_cast<const half8_t*>(q_lo + c * kQPitch + 32 * g + 8 * ks);
+    }
+    const float qmul = q_mul[c];
 
     WaveState st;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) st.o[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    st.lsum = float4_t{0.f, 0.f, 0.f, 0.f};
+    st.lwin = 0.0f;
     st.m = -INFINITY;
-    st.l = 0.0f;
-    _Float16* vtile = reinterpret_cast<_Float16*>(smem + kOffWave + wave * kWaveBytes);
+    _Float16* vtile = reinterpret_cast<_Float16*>(smem + wave * kWaveBytes);
 
-    for (int t = t0; t < n_tiles; t += 2 * kWaves) {
-        if (t < n_tiles_global)
-            process_tile<true, STAGE>(s, t, ra, win_l, qhi, qlo, vtile, lane, st);
-        else
-            process_tile<false, STAGE>(s, t, ra, win_l, qhi, qlo, vtile, lane, st);
-        const int ta = t + 2 * kWaves;
-        if (ta < n_tiles)
-            fetch_tile<STAGE>(s, ta,
-                              STAGE != kStageRead && ta < n_tiles_global ? tile_position(s, ta, lane) : -1,
-                              lane, ra);
+    int k = 0;  // index of tile t among the wave's selected-record tiles
+    for (int t = t0; t < n_tiles_global; t += 2 * kWaves, k += 2) {
+        process_global<STAGE>(s, t, ra, qhi, qlo, qmul, vtile, lane, st);
+        if (t + 2 * kWaves < n_tiles_global)
+            fetch_global<STAGE>(s, t + 2 * kWaves, tile_pos(k + 2), (k + 2) & 1, lane, ra);
         const int u = t + kWaves;
-        if (u < n_tiles) {
-            if (u < n_tiles_global)
-                process_tile<true, STAGE>(s, u, rb, win_l, qhi, qlo, vtile, lane, st);
-            else
-                process_tile<false, STAGE>(s, u, rb, win_l, qhi, qlo, vtile, lane, st);
-            const int ub = u + 2 * kWaves;
-            if (ub < n_tiles)
-                fetch_tile<STAGE>(s, ub,
-                                  STAGE != kStageRead && ub < n_tiles_global ? tile_position(s, ub, lane) : -1,
-                                  lane, rb);
+        if (u < n_tiles_global) {
+            process_global<STAGE>(s, u, rb, qhi, qlo, qmul, vtile, lane, st);
+            if (u + 2 * kWaves < n_tiles_global)
+                fetch_global<STAGE>(s, u + 2 * kWaves, tile_pos(k + 3), (k + 3) & 1, lane, rb);
         }
     }
+    if (has_win && jw * kTile < s.swa_len)
+        process_window(rw, s.swa_len - jw * kTile, qhi, qlo, qmul, vtile, lane, st);
 
-    // ---- merge the 8 waves' states through LDS (aliases the wave areas) ----
-    const float l_wave = xsum4(st.l);
-    __syncthreads();
-    float* mo = reinterpret_cast<float*>(smem + kOffWave);
+    // ---- merge the waves' states through LDS ----
+    const float l_wave = st.lsum[0] + xsum4(st.lwin);
+    float* mo = reinterpret_cast<float*>(smem + kWaves * kWaveBytes);
     float* mm = mo + kWaves * kGroupHeads * kMergePitch;
     float* ml = mm + kWaves * kGroupHeads;
     {
