@@ -52,7 +52,8 @@ EXPORTS = ("csa2_quant_fp4", "csa2_quant_fp8", "csa2_write_entries", "csa2_write
            "csa2_workspace_size",
            "csa2_status_str", "csa2_abi_version", "csa2_codec_probe",
            "csa2_quant_idx_fp4", "csa2_write_entries_proj_fp4", "csa2_index_full_fp4",
-           "csa2_index_full_fp4_timed", "csa2_index_reindex_fp4", "csa2_rope_table")
+           "csa2_index_full_fp4_timed", "csa2_index_reindex_fp4", "csa2_rope_table",
+           "csa2_index_full_noalloc")
 
 _lib = None
 
@@ -94,6 +95,8 @@ _SIGS = {
     "csa2_status_str": (ctypes.c_char_p, [_int]),
     "csa2_abi_version": (_int, []),
     "csa2_rope_table": (_int, [_vp, _i64, ctypes.c_double, _vp]),
+    "csa2_index_full_noalloc": (_int, [_vp, _vp, _i64, _int, _int, _vp, _vp, _vp, _int, _int, _vp,
+                                       _vp, _vp]),
     "csa2_codec_probe": (_int, [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),
     "csa2_quant_idx_fp4": (_int, [_vp, _i64, _vp, _vp, _vp, _vp]),
     "csa2_write_entries_proj_fp4": (_int, [_vp, _vp, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -349,6 +352,28 @@ def index_full(cache, iq, iw, n_vis, topk_idx, pool_idx=None, topk=DEFAULT_TOPK,
         _ptr(pool_idx, torch.int32, "pool_idx", B * Q * pool_blocks) if pool_blocks else None,
         _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream), ev[0], ev[1])
     _check(rc, "csa2_index_full")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def index_full_noalloc(cache, iq, iw, n_vis, topk_idx, pool_idx=None, topk=DEFAULT_TOPK,
+                       pool_blocks=0, stream=None):
+    """index_full without a workspace (FP8 indexer keys): the library's own
+    fixed scratch of NOALLOC_SCRATCH_BYTES per GPU; calls that overlap on one
+    GPU race."""
+    B, Q = iq.shape[0], iq.shape[1]
+    _check_batch(cache, B, "index_full_noalloc")
+    if cache.idx_fp4:
+        raise ValueError("index_full_noalloc takes FP8 indexer keys")
+    rc = lib().csa2_index_full_noalloc(
+        _ptr(cache.ik_codes, torch.uint8, "ik_codes"), _ik_aux_ptr(cache), cache.cap, B, Q,
+        _ptr(iq, torch.float32, "iq", B * Q * 256), _ptr(iw, torch.float32, "iw", B * Q * 4),
+        _ptr(n_vis, torch.int32, "n_vis", B * Q), topk, pool_blocks,
+        _ptr(topk_idx, torch.int32, "topk_idx", B * Q * topk),
+        _ptr(pool_idx, torch.int32, "pool_idx", B * Q * pool_blocks) if pool_blocks else None,
+        _stream(stream))
+    _check(rc, "csa2_index_full_noalloc")
 
 
 def index_reindex(cache, iq, iw, n_vis, pool_idx, topk_idx, topk=DEFAULT_TOPK, ws=None,

@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <cmath>
+#include <mutex>
 
 #include <hip/hip_runtime.h>
 
@@ -365,6 +366,61 @@ __attribute__((visibility("default"))) int csa2_index_full(
     int32_t* pool_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
     return csa2_index_full_timed(ik_codes, ik_sigma, cap, B, Q, iq, iw, n_vis, topk, pool_blocks,
                                  topk_idx, pool_idx, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// csa2_index_full without a caller workspace: the scratch is a fixed device
+// array of this library (one copy per GPU, loaded with the library's code and
+// kept until the process ends).  Host code never passes the array's name to a
+// kernel: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = CSA2_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `dev`'s copy of the scratch array (null on error).
+void* scratch_on(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || ptr == nullptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+__attribute__((visibility("default"))) int csa2_index_full_noalloc(
+    const uint8_t* ik_codes, const float* ik_sigma, int64_t cap, int B, int Q, const float* iq,
+    const float* iw, const int32_t* n_vis, int topk, int pool_blocks, int32_t* topk_idx,
+    int32_t* pool_idx, hipStream_t stream) {
+    int rc = validate_index_full(ik_codes, ik_sigma, cap, B, Q, iq, iw, n_vis, topk, pool_blocks,
+                                 topk_idx, pool_idx);
+    if (rc) return rc;
+    if (full_layout(B, Q, cap, topk, pool_blocks).total > kNoAllocScratchBytes)
+        return CSA2_E_WORKSPACE;
+    int dev = -1;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return CSA2_E_HIP;
+    void* ws = scratch_on(dev);
+    if (ws == nullptr) return CSA2_E_HIP;
+    if (mma_path(Q, cap, pool_blocks, topk))
+        return index_full_mma(kIdxFp8, ik_codes, ik_sigma, cap, B, Q, iq, iw, n_vis, topk,
+                              pool_blocks, topk_idx, pool_idx, ws, stream, nullptr, nullptr);
+    return index_full_valu(kIdxFp8, ik_codes, ik_sigma, cap, B, Q, iq, iw, n_vis, topk,
+                           pool_blocks, topk_idx, pool_idx, ws, stream, nullptr, nullptr);
 }
 
 __attribute__((visibility("default"))) int csa2_index_reindex(

@@ -426,6 +426,30 @@ const char* csa2_status_str(int status);
 int csa2_abi_version(void);
 
 /*
+ * csa2_index_full_noalloc -- csa2_index_full for callers that cannot allocate
+ * device memory (code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument; the call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).
+ *   Arguments, results and errors as csa2_index_full, without ws / ws_bytes.
+ *   Its scratch is a fixed array of CSA2_NOALLOC_SCRATCH_BYTES bytes inside
+ *   the library, one copy per GPU, held until the process ends.  A call whose
+ *   csa2_workspace_size(CSA2_OP_INDEX_FULL, ...) exceeds that limit returns
+ *   CSA2_E_WORKSPACE before touching the GPU (16 queries over 131072 positions
+ *   need 9.2 MiB, 4 queries over 1048576 positions 18.3 MiB).  The device is
+ *   the one `stream` belongs to; the first call on a device looks up that
+ *   device's copy (CSA2_E_HIP if the lookup fails).
+ *   Every call on one GPU shares that GPU's copy, which keeps the last call's
+ *   contents: calls that overlap on one GPU (other streams, other threads)
+ *   race and must be serialised by the caller.  No part of the scratch needs
+ *   to start at zero (every value read is written earlier in the same call).
+ */
+#define CSA2_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int csa2_index_full_noalloc(const uint8_t* ik_codes, const float* ik_sigma, int64_t cap, int B,
+                            int Q, const float* iq, const float* iw, const int32_t* n_vis,
+                            int topk, int pool_blocks, int32_t* topk_idx, int32_t* pool_idx,
+                            hipStream_t stream);
+
+/*
  * csa2_rope_table -- HOST function: the rotation table that csa2_quant_fp4 and
  * the write-entry calls take as `rope_cs` ("DeepSeek V4.1 Flash is live",
  * section "cache precision and persistence tiers": entries are quantised after

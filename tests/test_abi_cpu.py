@@ -238,3 +238,17 @@ def test_batch_larger_than_the_cache_is_rejected_before_any_launch():
     with pytest.raises(ValueError, match="does not fit"):
         csa2.sparse_attn_chunk(torch.zeros((3, 4, 16, 128)), cache, None, None, None, None, None,
                                None, None)
+
+
+def test_noalloc_index_full_rejects_before_touching_the_gpu(lib):
+    """csa2_index_full_noalloc refuses sizes whose workspace exceeds its fixed
+    scratch, and bad scalars, with the documented codes and no HIP call."""
+    f = lib.csa2_index_full_noalloc
+    big = 1 << 24  # 16 sequences x 16M positions need far more than 32 MiB
+    assert f(FAKE, FAKE, big, 16, 1, FAKE, FAKE, FAKE, 512, 2048, FAKE, FAKE, None) == -3
+    assert f(None, FAKE, 1024, 1, 1, FAKE, FAKE, FAKE, 512, 0, FAKE, None, None) == -1
+    assert f(FAKE, FAKE, 1000, 1, 1, FAKE, FAKE, FAKE, 512, 0, FAKE, None, None) == -1  # cap % 64
+    assert f(FAKE, FAKE, 1024, 1, 1, FAKE, FAKE, FAKE, 4096, 0, FAKE, None, None) == -2  # topk
+    import compressed_kv_cache_decode_amd as csa2
+    need = csa2.workspace_size(csa2.OP_INDEX_FULL, 16, 1, 131072, 512, 2048, 0)
+    assert need <= csa2.NOALLOC_SCRATCH_BYTES
