@@ -381,7 +381,7 @@ static_assert(kSelBins >= kMaxTopk, "the histogram area stages a top-K row");
 
 struct SelShared {
     // also holds the register path's state (SelRegShared)
-    alignas(16) uint32_t hist[kSelBins * kSelSub + 3 * kSelWaves + 4];
+    alignas(16) uint32_t hist[kSelBins * kSelSub + 5 * kSelWaves + 4];
     uint32_t keys[1];  // unused by the streaming path (keys are re-read)
     int32_t pool[kMaxPoolBlocks];
     uint32_t red[3][kSelWaves];
@@ -647,85 +647,154 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 // different words.
 struct SelRegShared {
     alignas(16) uint32_t hist[kSelBins * kSelSub];
-    uint32_t part[3][kSelWaves];
+    alignas(16) uint32_t part[5][kSelWaves];
     uint32_t pick[3];
 };
 static_assert(sizeof(SelRegShared) <= sizeof(SelShared::hist), "register state fits the histogram area");
 static_assert(kSelSub == 4, "a bin's counters are read as one uint4");
 
+// One range-refinement pass: the N values per thread that lie in [lo, hi]
+// are counted into at most 2048 equal bins (with skip_lowest, values in the
+// lowest bin are not counted: the caller knows in_range, the number of values
+// in [lo, hi], so that bin's count is in_range minus the others), and the bin
+// that holds the remaining-th largest is picked: its index, the count above
+// it and its own count.
+struct BinPick {
+    uint32_t bin, before, in_bin;
+    int shift;
+};
+
+template <int N>
+__device__ __forceinline__ BinPick hist_pick(const uint32_t (&v)[N], uint32_t lo, uint32_t hi,
+                                             uint32_t remaining, bool skip_lowest,
+                                             uint32_t in_range, SelRegShared& sh) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t width = hi - lo;  // > 0
+    const int bits = 32 - __clz((int)width);
+    const int shift = bits > 11 ? bits - 11 : 0;
+    const int nbins = (int)(width >> shift) + 1;
+    const uint32_t first = skip_lowest ? lo + (1u << shift) : lo;  // smallest value counted
+    __syncthreads();  // earlier readers of hist / part / pick are done
+    static_assert(kSelBins * kSelSub == 8 * kSelThreads, "two 16-byte clears per thread");
+    reinterpret_cast<uint4*>(sh.hist)[2 * tid] = make_uint4(0u, 0u, 0u, 0u);
+    reinterpret_cast<uint4*>(sh.hist)[2 * tid + 1] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    const uint32_t sub = (uint32_t)lane & (kSelSub - 1);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        if (v[i] >= first && v[i] <= hi && v[i] != 0)
+            atomicAdd(&sh.hist[((v[i] - lo) >> shift) * kSelSub + sub], 1u);
+    __syncthreads();
+    // thread t owns bins nbins-1-2t and nbins-2-2t (descending order)
+    const int b0 = nbins - 1 - 2 * tid, b1 = b0 - 1;
+    uint32_t h0 = 0, h1 = 0;
+    if (b0 >= 0) {
+        const uint4 c = reinterpret_cast<const uint4*>(sh.hist)[b0];
+        h0 = c.x + c.y + c.z + c.w;
+    }
+    if (b1 >= 0) {
+        const uint4 c = reinterpret_cast<const uint4*>(sh.hist)[b1];
+        h1 = c.x + c.y + c.z + c.w;
+    }
+    uint32_t mine = h0 + h1;  // a skipped lowest bin counts 0 here: it is last in the order
+    const uint32_t incl = wave_incl_scan(mine);
+    if (lane == 63) sh.part[0][wave] = incl;
+    __syncthreads();
+    uint32_t above = incl - mine;
+    {
+        static_assert(kSelWaves == 16, "per-wave totals read as four uint4");
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint4 x = reinterpret_cast<const uint4*>(sh.part[0])[j];
+            above += (4 * j + 0 < wave ? x.x : 0u) + (4 * j + 1 < wave ? x.y : 0u) +
+                     (4 * j + 2 < wave ? x.z : 0u) + (4 * j + 3 < wave ? x.w : 0u);
+        }
+    }
+    if (skip_lowest) {  // the lowest bin's count: the values in range not in any other bin
+        if (b0 == 0) h0 = in_range - above;
+        if (b1 == 0) h1 = in_range - above - h0;
+        mine = h0 + h1;
+    }
+    if (above < remaining && above + mine >= remaining) {
+        if (above + h0 >= remaining) { sh.pick[0] = (uint32_t)b0; sh.pick[1] = above; sh.pick[2] = h0; }
+        else { sh.pick[0] = (uint32_t)b1; sh.pick[1] = above + h0; sh.pick[2] = h1; }
+    }
+    __syncthreads();
+    return BinPick{sh.pick[0], sh.pick[1], sh.pick[2], shift};
+}
+
+// The K-th largest of the workgroup's register keys (16 per thread), as the
+// take rule of a Threshold.  The non-zero keys' range [kmin, kmax] is refined
+// by 2048-bin histogram passes.  Before them, a pass over group maxima (each
+// thread's maximum when K <= 1024, else the maxima of its four groups of four
+// keys) finds a lower bound: the lower edge of the bin holding the K-th
+// largest group maximum has at least K group maxima, hence at least K keys, at
+// or above it, so the K-th largest key is at or above it, and the key passes
+// only count keys from there up (a few hundred instead of every key).
 __device__ __forceinline__ Threshold threshold_reg(const uint32_t (&k)[kSelKpt], int K,
                                                    SelRegShared& sh) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t cnt = 0, kmin = 0xFFFFFFFFu, kmax = 0;
+    uint32_t gm[4];  // maxima of the four groups of four keys
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gm[j] = max(max(k[4 * j], k[4 * j + 1]), max(k[4 * j + 2], k[4 * j + 3]));
 #pragma unroll
     for (int i = 0; i < kSelKpt; ++i) {
         cnt += k[i] != 0;
         kmin = k[i] ? min(kmin, k[i]) : kmin;
-        kmax = max(kmax, k[i]);
     }
+    kmax = max(max(gm[0], gm[1]), max(gm[2], gm[3]));
+    uint32_t ngm1 = kmax != 0, ngm4 = (gm[0] != 0) + (gm[1] != 0) + (gm[2] != 0) + (gm[3] != 0);
     cnt = wave_sum(cnt);
+    ngm1 = wave_sum(ngm1);
+    ngm4 = wave_sum(ngm4);
     kmin = wave_reduce(kmin, [](uint32_t x, uint32_t y) { return min(x, y); });
     kmax = wave_reduce(kmax, [](uint32_t x, uint32_t y) { return max(x, y); });
-    if (lane == 0) { sh.part[0][wave] = cnt; sh.part[1][wave] = kmin; sh.part[2][wave] = kmax; }
+    __syncthreads();  // earlier readers of part are done
+    if (lane == 0) {
+        sh.part[0][wave] = cnt; sh.part[1][wave] = kmin; sh.part[2][wave] = kmax;
+        sh.part[3][wave] = ngm1; sh.part[4][wave] = ngm4;
+    }
     __syncthreads();
-    cnt = 0; kmin = 0xFFFFFFFFu; kmax = 0;
+    cnt = 0; kmin = 0xFFFFFFFFu; kmax = 0; ngm1 = 0; ngm4 = 0;
 #pragma unroll
     for (int w = 0; w < kSelWaves; ++w) {
         cnt += sh.part[0][w];
         kmin = min(kmin, sh.part[1][w]);
         kmax = max(kmax, sh.part[2][w]);
+        ngm1 += sh.part[3][w];
+        ngm4 += sh.part[4][w];
     }
     if (cnt <= (uint32_t)K) return Threshold{1u, 0u, 0u, cnt};
 
-    uint32_t lo = kmin, hi = kmax, remaining = (uint32_t)K;
+    uint32_t lo = kmin, hi = kmax;
+    bool known = true;  // in_range is the count of keys in [lo, hi]
+    uint32_t in_range = cnt;
+    if (kmax > kmin && (K <= 1024 ? ngm1 : ngm4) >= (uint32_t)K) {
+        BinPick bp;
+        if (K <= 1024) {
+            const uint32_t t1[1] = {max(max(gm[0], gm[1]), max(gm[2], gm[3]))};
+            bp = hist_pick(t1, lo, hi, (uint32_t)K, false, 0u, sh);
+        } else {
+            bp = hist_pick(gm, lo, hi, (uint32_t)K, false, 0u, sh);
+        }
+        lo = lo + (bp.bin << bp.shift);
+        known = lo == kmin;
+    }
+    uint32_t remaining = (uint32_t)K;
     for (int pass = 0; pass < 4; ++pass) {
         const uint32_t width = hi - lo;
         if (width == 0) return Threshold{lo + 1, lo, remaining, (uint32_t)K};
-        const int bits = 32 - __clz((int)width);
-        const int shift = bits > 11 ? bits - 11 : 0;
-        const int nbins = (int)(width >> shift) + 1;
-        __syncthreads();  // earlier readers of hist / part are done
-        static_assert(kSelBins * kSelSub == 8 * kSelThreads, "two 16-byte clears per thread");
-        reinterpret_cast<uint4*>(sh.hist)[2 * tid] = make_uint4(0u, 0u, 0u, 0u);
-        reinterpret_cast<uint4*>(sh.hist)[2 * tid + 1] = make_uint4(0u, 0u, 0u, 0u);
-        __syncthreads();
-        const uint32_t sub = (uint32_t)lane & (kSelSub - 1);
-#pragma unroll
-        for (int i = 0; i < kSelKpt; ++i)
-            if (k[i] >= lo && k[i] <= hi)
-                atomicAdd(&sh.hist[((k[i] - lo) >> shift) * kSelSub + sub], 1u);
-        __syncthreads();
-        // thread t owns bins nbins-1-2t and nbins-2-2t (descending order)
-        const int b0 = nbins - 1 - 2 * tid, b1 = b0 - 1;
-        uint32_t h0 = 0, h1 = 0;
-        if (b0 >= 0) {
-            const uint4 c = reinterpret_cast<const uint4*>(sh.hist)[b0];
-            h0 = c.x + c.y + c.z + c.w;
-        }
-        if (b1 >= 0) {
-            const uint4 c = reinterpret_cast<const uint4*>(sh.hist)[b1];
-            h1 = c.x + c.y + c.z + c.w;
-        }
-        const uint32_t mine = h0 + h1;
-        const uint32_t incl = wave_incl_scan(mine);
-        if (lane == 63) sh.part[0][wave] = incl;
-        __syncthreads();
-        uint32_t above = incl - mine;
-        for (int w = 0; w < wave; ++w) above += sh.part[0][w];
-        if (above < remaining && above + mine >= remaining) {
-            if (above + h0 >= remaining) { sh.pick[0] = (uint32_t)b0; sh.pick[1] = above; sh.pick[2] = h0; }
-            else { sh.pick[0] = (uint32_t)b1; sh.pick[1] = above + h0; sh.pick[2] = h1; }
-        }
-        __syncthreads();
-        const uint32_t d = sh.pick[0];
-        const uint32_t in_bin = sh.pick[2];
-        remaining -= sh.pick[1];
-        const uint32_t new_lo = lo + (d << shift);
-        const uint32_t span = (shift == 0) ? 0u : ((1u << shift) - 1u);
+        const BinPick bp = hist_pick(k, lo, hi, remaining, known, in_range, sh);
+        remaining -= bp.before;
+        const uint32_t new_lo = lo + (bp.bin << bp.shift);
+        const uint32_t span = (bp.shift == 0) ? 0u : ((1u << bp.shift) - 1u);
         const uint32_t new_hi = (hi - new_lo > span) ? new_lo + span : hi;
-        if (in_bin == remaining) return Threshold{new_lo, 0u, 0u, (uint32_t)K};
+        if (bp.in_bin == remaining) return Threshold{new_lo, 0u, 0u, (uint32_t)K};
         lo = new_lo;
         hi = new_hi;
+        in_range = bp.in_bin;
+        known = true;
     }
     return Threshold{lo + 1, lo, remaining, (uint32_t)K};  // not reached: width hits 0
 }
