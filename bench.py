@@ -36,6 +36,14 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
 METRIC = "CSA2 decode queries/s per layer stack at 128K ctx; achieved HBM GB/s vs peak"
+# the arithmetic the path computes in: fp32 indexer scores (sequential FMA
+# chains over E4M3 / E2M1 values), attention on fp16 MFMA with fp32
+# accumulation (dequantised FP4 / FP8 operands exact in fp16, q split into fp16
+# hi + lo), fp32 online softmax; storage is FP4 (E2M1 + E4M3 scales) and FP8
+DTYPE = "f32+f16mfma"
+DTYPE_DETAIL = ("indexer scores fp32 (exact-order FMA chains over E4M3/E2M1 values); attention "
+                "fp16 MFMA with fp32 accumulate (FP4/FP8 operands exact in fp16, q as fp16 hi+lo "
+                "= 22 bits), fp32 online softmax; cache storage FP4 E2M1+E4M3 scales, FP8 E4M3")
 
 
 def log(msg):
@@ -62,6 +70,9 @@ def parse_args():
     p.add_argument("--replay-tokens", type=int, default=0,
                    help="replay_stack_128k workload: tokens per replay chunk (default 128; 2560 "
                         "is the exact replay of a 20-layer stack)")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the measurements beside the headline workload (copy and read "
+                        "ceilings, large-batch attention, the 1M-entry stack)")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="also run one device-to-device copy of this many MiB (a known-size "
                         "kernel for scaling hardware byte counters)")
@@ -111,7 +122,7 @@ class StepSet:
         self.inp = {k: v.clone() for k, v in dev_inputs.items()}
         self.csa2 = csa2
 
-    def run(self, scan_timer=None, attn_timer=None):
+    def run(self, scan_timer=None, attn_timer=None, index_events=None):
         i = self.inp
         # write path of the new token of every sequence (position n_ent - 1),
         # in one launch: its FP4 record, its indexer key projected on the
@@ -120,7 +131,8 @@ class StepSet:
                          i["win_v"], i["win_rows"], i["swk"], i["swv"], i["sks"], i["svs"],
                          ratio=self.ratio, rope_cs=i.get("rope_new"))
         self.stack.step(i["iq"], i["iw"], i["n_vis"], i["q"], i["swk"], i["swv"], i["sks"],
-                        i["svs"], i["swa_len"], scan_timer=scan_timer, attn_timer=attn_timer)
+                        i["svs"], i["swa_len"], scan_timer=scan_timer, attn_timer=attn_timer,
+                        index_events=index_events)
 
 
 def build_sets(args, wl, inp):
@@ -251,9 +263,13 @@ def time_gpu(args, wl, csa2, sets):
         attn_timer = csa2.KernelTimer(args.steps * len(wl.plan))
         if hasattr(torch.cuda, "_sleep"):
             torch.cuda._sleep(int(3e6 * args.steps))  # about 1.2 ms of spinning per step
+        index_events = []
         for i in range(args.steps):
-            sets[i % len(sets)].run(scan_timer=timer, attn_timer=attn_timer)
+            sets[i % len(sets)].run(scan_timer=timer, attn_timer=attn_timer,
+                                    index_events=index_events)
         torch.cuda.synchronize()
+        full_ms = [a.elapsed_time(b) for m, a, b in index_events if m == "F"]
+        reindex_ms = [a.elapsed_time(b) for m, a, b in index_events if m == "X"]
         scan_ms = timer.durations_ms()
         attn_ms = attn_timer.durations_ms()
         timer.close()
@@ -263,7 +279,8 @@ def time_gpu(args, wl, csa2, sets):
             sets[i % len(sets)].run()
         torch.cuda.synchronize()
         eager_elapsed = time.perf_counter() - t1
-    return elapsed, {"scan": scan_ms, "attn": attn_ms, "step": step_ms}, eager_elapsed
+    return elapsed, {"scan": scan_ms, "attn": attn_ms, "step": step_ms, "full_call": full_ms,
+                     "reindex_call": reindex_ms}, eager_elapsed
 
 
 # --------------------------------------------------------------------------- replay chunk
@@ -383,7 +400,7 @@ def run_chunk_bench(args, wl):
         "metric": "CSA2 bounded-replay chunk queries/s (128 replayed tokens over 128K entries, one layer)",
         "value": round(Q * B * args.steps / elapsed, 1), "unit": "queries/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE,
         "data": "synthetic",
         "config": {"workload": wl.name, "sequences": B, "entries": N, "queries": Q, "heads": H,
                    "indexer_key": "fp4" if wl.idx_fp4 else "fp8",
@@ -499,7 +516,7 @@ def run_chunk_stack_bench(args, wl):
         "value": round(Q * B * args.steps / elapsed, 1), "unit": "queries/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE, "data": "synthetic",
         "config": {"workload": wl.name, "sequences": B, "entries": N, "queries": Q, "heads": H,
                    "plan": wl.plan, "topk": wl.topk, "pool_blocks": wl.pool_blocks,
                    "cache_sets": args.cache_sets,
@@ -773,7 +790,7 @@ def run_model_sweep(args):
         "metric": MODEL_METRIC, "value": head["queries_per_s"], "unit": "queries/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": DTYPE, "data": "synthetic",
         "config": {"workload": "model_step", "sequences": B, "context": head["context"],
                    "layers": 40, "heads": H, "topk": topk, "pool_blocks": pool, "window": 128,
                    "cache_sets": 2, "launch": "hip-graph"},
@@ -783,21 +800,20 @@ def run_model_sweep(args):
 
 
 # --------------------------------------------------------------------------- gather sweep
-def run_attn_sweep(args):
+def attn_sweep_points(batches, n_launch):
     """The gathering sparse attention (csa2_sparse_attn_decode: 512 selected
     FP4 records and a 128-token FP8 window per query, 64 heads) at each batch
-    of --batches, timed with HIP events around its dispatch: where the kernel
-    leaves the latency regime.  Each sequence's cache holds 16384 entries
-    written by the library from N(0, 1) K and V drawn on the device; three
-    sets of indices, queries and windows rotate so that consecutive launches
-    gather different records."""
+    of `batches`, timed with HIP events around its dispatch.  Each sequence's
+    cache holds 16384 entries written by the library from N(0, 1) K and V
+    drawn on the device; three sets of indices, queries and windows rotate so
+    that consecutive launches gather different records."""
     import torch
 
     import compressed_kv_cache_decode_amd as csa2
     from compressed_kv_cache_decode_amd import synth
     H, topk, cap = 64, 512, 16384
     sweep = []
-    for B in [int(x) for x in args.batches.split(",")]:
+    for B in batches:
         gen = synth.device_generator(4000 + B)
         rnd = lambda *shape: synth.device_normal(gen, shape)
         cache = csa2.Cache(B, cap)
@@ -820,11 +836,12 @@ def run_attn_sweep(args):
                              swa_len=torch.full((B,), 128, dtype=torch.int32, device="cuda"),
                              out=torch.empty((B, H, 128), dtype=torch.float32, device="cuda"),
                              lse=torch.empty((B, H), dtype=torch.float32, device="cuda")))
-        n_launch = max(args.steps, 30)
         timer = csa2.KernelTimer(n_launch)
         for rep in range(2):  # the first pass warms up
             if rep:
                 timer.reset()
+                if hasattr(torch.cuda, "_sleep"):  # queue the timed launches back to back
+                    torch.cuda._sleep(int(2e5 * n_launch))
             for i in range(n_launch):
                 d = sets[i % 3]
                 csa2.sparse_attn_decode(d["q"], cache, d["idx"], d["swk"], d["swv"], d["sks"],
@@ -844,12 +861,21 @@ def run_attn_sweep(args):
             f"{nbytes / (mean * 1e-3) / 1e9:.0f} GB/s")
         del cache, sets
         torch.cuda.empty_cache()
+    return sweep
+
+
+def run_attn_sweep(args):
+    """Batch sweep of the gathering attention: where the kernel leaves the
+    latency regime (attn_sweep_points over --batches)."""
+    H, topk, cap = 64, 512, 16384
+    n_launch = max(args.steps, 30)
+    sweep = attn_sweep_points([int(x) for x in args.batches.split(",")], n_launch)
     best = max(sweep, key=lambda r: r["achieved_GBps"])
     return {"metric": "CSA2 sparse attention (gathering, 512 FP4 records + 128 FP8 window tokens "
                       "per query, 64 heads): HBM GB/s vs batch",
             "value": best["achieved_GBps"], "unit": "GB/s", "n_gpus": 1, "steps": n_launch,
-            "warmup": n_launch, "higher_is_better": True, "vs_baseline": None, "dtype": "f32",
-            "data": "synthetic",
+            "warmup": n_launch, "higher_is_better": True, "vs_baseline": None,
+            "dtype": DTYPE, "dtype_detail": DTYPE_DETAIL, "data": "synthetic",
             "config": {"workload": "attn_batch_sweep", "heads": H, "topk": topk, "window": 128,
                        "entries_per_sequence": cap, "launch": "eager, HIP events per dispatch"},
             "roofline": {"bound": "hbm", "achieved": best["achieved_GBps"], "peak": HBM_PEAK_GBS,
@@ -858,6 +884,54 @@ def run_attn_sweep(args):
                          "bytes_per_launch": best["bytes_per_launch"],
                          "mean_us": best["mean_us"]},
             "sweep": sweep}
+
+
+def measure_ceilings(mib=1024, reps=10):
+    """Streaming ceilings of this GPU, measured in the same run with the
+    library's probe kernels (csa2_stream_probe): a read-only pass over `mib`
+    MiB and a copy of `mib` MiB (reads and writes `mib` MiB each), 16-byte
+    non-temporal loads, best of a few grid sizes, each the mean of `reps`
+    back-to-back launches timed with events."""
+    import torch
+
+    import compressed_kv_cache_decode_amd as csa2
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    best = {}
+    configs = [(0, b) for b in (1024, 2048, 4096, 8192)] + [(2, 1)] + \
+              [(1, b) for b in (1024, 2048, 4096, 8192)]
+    for mode, blocks in configs:
+        for _ in range(2):
+            csa2.stream_probe(mode, src, dst if mode == 1 else None, n_blocks=blocks)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            csa2.stream_probe(mode, src, dst if mode == 1 else None, n_blocks=blocks)
+        ev[1].record()
+        torch.cuda.synchronize()
+        sec = ev[0].elapsed_time(ev[1]) * 1e-3 / reps
+        kind = 1 if mode == 1 else 0
+        gbs = (2 * n if kind else n) / sec / 1e9
+        if gbs > best.get(kind, (0, ""))[0]:
+            best[kind] = (gbs, "one load per thread" if mode == 2 else f"{blocks} workgroups")
+    del src, dst
+    torch.cuda.empty_cache()
+    out = {"read_GBps": round(best[0][0], 1), "copy_GBps": round(best[1][0], 1), "bytes": n,
+           "how": f"csa2_stream_probe over {mib} MiB (read; copy = reads + writes), best of "
+                  f"grid-stride 1024-8192 workgroups and one load per thread (read: "
+                  f"{best[0][1]}; copy: {best[1][1]}), mean of {reps} launches"}
+    log(f"ceilings: read {out['read_GBps']} GB/s, copy {out['copy_GBps']} GB/s")
+    return out
+
+
+def with_ceilings(entry, ceil):
+    """A roofline entry with its fraction of the measured copy and read ceilings."""
+    e = dict(entry)
+    e["frac_of_copy"] = round(e["achieved"] / ceil["copy_GBps"], 4)
+    e["frac_of_read"] = round(e["achieved"] / ceil["read_GBps"], 4)
+    return e
 
 
 def copy_calibration(mib):
@@ -899,10 +973,24 @@ def main():
         run = run_chunk_bench if wl.plan == "F" else run_chunk_stack_bench
         print(json.dumps(run(args, wl)), flush=True)
         return
+    result = measure_decode(args, wl, cpu=not args.skip_cpu_baseline)
+    if wl.name == "decoder_stack_128k" and not args.no_extras:
+        extras(args, result)
+    print(json.dumps(result), flush=True)
+
+
+def measure_decode(args, wl, cpu=True):
+    """One decode workload: HIP-graph step time, per-kernel rooflines and the
+    Full / Reindex call times, and (cpu) the oracle on a sample."""
+    import torch
+
+    from compressed_kv_cache_decode_amd import synth
     log(f"workload {wl.name}: drawing inputs (seed {wl.seed})")
     inp = synth.decode_inputs(wl)
     csa2, sets = build_sets(args, wl, inp)
     elapsed, kernel_ms, eager_elapsed = time_gpu(args, wl, csa2, sets)
+    del sets
+    torch.cuda.empty_cache()
 
     total_bytes, scan_bytes = step_bytes(wl)
     ms_per_step = elapsed / args.steps * 1e3
@@ -917,6 +1005,10 @@ def main():
                        kernel_ms["scan"], scan_bytes, 1, ms_per_step, traffic),
     ]
     dominant = max(rooflines, key=lambda r: r["us_per_step"])
+    mean = lambda xs: sum(xs) / len(xs) if xs else None
+    full_us = mean(kernel_ms["full_call"]) * 1e3
+    scan_us = mean(kernel_ms["scan"]) * 1e3
+    reindex_us = mean(kernel_ms["reindex_call"])
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -928,7 +1020,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": DTYPE,
+        "dtype_detail": DTYPE_DETAIL,
         "data": "synthetic",
         "config": {"workload": wl.name, "sequences": wl.B, "entries": wl.n_ent,
                    "indexer_key": "fp4" if wl.idx_fp4 else "fp8",
@@ -945,12 +1038,47 @@ def main():
                  "eager_ms_per_step": round(eager_elapsed / args.steps * 1e3, 4),
                  "ms_p10_median_p90": [round(percentile(kernel_ms["step"], f), 4)
                                        for f in (0.1, 0.5, 0.9)]},
+        # eager call times (HIP events around each library call, queued back to
+        # back): the Full layer's index call is the query prep, the scan and the
+        # pool + top-K selection; a Reindex call is the pool rescore and its
+        # selection
+        "index": {"full_call_us": round(full_us, 2), "scan_us": round(scan_us, 2),
+                  "full_select_and_prep_us": round(full_us - scan_us, 2),
+                  "reindex_call_us": round(reindex_us * 1e3, 2) if reindex_us else None},
     }
-    if not args.skip_cpu_baseline:
+    if cpu:
         cb = cpu_baseline(args, wl, inp)
         result["cpu_baseline"] = {k: (round(v, 3) if isinstance(v, float) else v)
                                   for k, v in cb.items()}
-    print(json.dumps(result), flush=True)
+    return result
+
+
+def extras(args, result):
+    """Beside the headline: the copy and read ceilings of this GPU (every
+    roofline entry also as a fraction of them), the gathering attention at
+    large batches (where it is bandwidth- rather than latency-bound), and the
+    1M-entry decoder stack as a secondary workload."""
+    import torch
+
+    from compressed_kv_cache_decode_amd import synth
+    ceil = measure_ceilings()
+    result["ceilings"] = ceil
+    result["rooflines"] = [with_ceilings(r, ceil) for r in result["rooflines"]]
+    for B, pt in zip((256, 1024), attn_sweep_points([256, 1024], 30)):
+        result["rooflines"].append(with_ceilings({
+            "kernel": f"k_attn (sparse attention, gathering, batch {B}, 64 heads, top-512 + "
+                      f"128-token window)", "bound": "hbm", "achieved": pt["achieved_GBps"],
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": pt["frac"], "traffic": None,
+            "bytes_per_launch": pt["bytes_per_launch"], "mean_us": pt["mean_us"]}, ceil))
+    sub = argparse.Namespace(**vars(args))
+    sub.steps, sub.warmup, sub.cache_sets = min(args.steps, 30), min(args.warmup, 5), 2
+    r1m = measure_decode(sub, synth.WORKLOADS["decoder_stack_1m"], cpu=False)
+    torch.cuda.empty_cache()
+    result["secondary"] = {
+        "decoder_stack_1m": {k: r1m[k] for k in ("value", "unit", "ms_per_step", "steps",
+                                                  "warmup", "config", "step", "index")}}
+    result["secondary"]["decoder_stack_1m"]["rooflines"] = [with_ceilings(r, ceil)
+                                                             for r in r1m["rooflines"]]
 
 
 if __name__ == "__main__":

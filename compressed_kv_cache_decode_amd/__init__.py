@@ -53,7 +53,7 @@ EXPORTS = ("csa2_quant_fp4", "csa2_quant_fp8", "csa2_write_entries", "csa2_write
            "csa2_status_str", "csa2_abi_version", "csa2_codec_probe",
            "csa2_quant_idx_fp4", "csa2_write_entries_proj_fp4", "csa2_index_full_fp4",
            "csa2_index_full_fp4_timed", "csa2_index_reindex_fp4", "csa2_rope_table",
-           "csa2_index_full_noalloc")
+           "csa2_index_full_noalloc", "csa2_stream_probe")
 
 _lib = None
 
@@ -95,6 +95,7 @@ _SIGS = {
     "csa2_status_str": (ctypes.c_char_p, [_int]),
     "csa2_abi_version": (_int, []),
     "csa2_rope_table": (_int, [_vp, _i64, ctypes.c_double, _vp]),
+    "csa2_stream_probe": (_int, [_int, _vp, _vp, _sz, _vp, _int, _vp]),
     "csa2_index_full_noalloc": (_int, [_vp, _vp, _i64, _int, _int, _vp, _vp, _vp, _int, _int, _vp,
                                        _vp, _vp]),
     "csa2_codec_probe": (_int, [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),
@@ -504,6 +505,19 @@ def codec_probe(x, stream=None):
                                 _stream(stream))
     _check(rc, "csa2_codec_probe")
     return e4, e4h, fp4, enc4, enc2
+
+
+def stream_probe(mode, src, dst=None, sink=None, n_blocks=2048, stream=None):
+    """Diagnostics: mode 0 streams src (u8, a multiple of 16 bytes) with
+    16-byte loads (grid-stride), mode 2 with one load per thread, mode 1
+    copies it to dst (csa2_stream_probe)."""
+    if sink is None and mode != 1:
+        sink = torch.empty(n_blocks, dtype=torch.int32, device=src.device)
+    rc = lib().csa2_stream_probe(mode, _ptr(src, torch.uint8, "src"),
+                                 _ptr(dst, torch.uint8, "dst", src.numel()) if dst is not None else None,
+                                 src.numel(), _ptr(sink, torch.int32, "sink", n_blocks) if sink is not None else None,
+                                 n_blocks, _stream(stream))
+    _check(rc, "csa2_stream_probe")
 
 
 # ---------------------------------------------------------------------------

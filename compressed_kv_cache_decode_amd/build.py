@@ -19,7 +19,8 @@ LIB = os.path.join(HERE, "libcsa2.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["csa2_abi.cpp", "csa2_quant.hip", "csa2_index.hip", "csa2_chunk.hip", "csa2_attn.hip"]
+SOURCES = ["csa2_abi.cpp", "csa2_quant.hip", "csa2_index.hip", "csa2_chunk.hip", "csa2_attn.hip",
+           "csa2_probe.hip"]
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-fvisibility=hidden", "-Wall", "-Wno-unused-function",

@@ -368,6 +368,16 @@ __attribute__((visibility("default"))) int csa2_index_full(
                                  topk_idx, pool_idx, ws, ws_bytes, stream, nullptr, nullptr);
 }
 
+__attribute__((visibility("default"))) int csa2_stream_probe(int mode, const void* src, void* dst,
+                                                             size_t n_bytes, uint32_t* sink,
+                                                             int n_blocks, hipStream_t stream) {
+    if (mode < 0 || mode > 2 || !src || n_bytes % 16 != 0 || n_blocks < 1 || n_blocks > 65535)
+        return CSA2_E_ARG;
+    if ((mode != 1 && !sink) || (mode == 1 && !dst)) return CSA2_E_ARG;
+    if (n_bytes == 0) return CSA2_OK;
+    return hip_status(launch_stream_probe(mode, src, dst, n_bytes, sink, n_blocks, stream));
+}
+
 // ---------------------------------------------------------------------------
 // csa2_index_full without a caller workspace: the scratch is a fixed device
 // array of this library (one copy per GPU, loaded with the library's code and

@@ -110,6 +110,11 @@ hipError_t launch_select_pool(const uint32_t* ckeys, const int32_t* pool, int P,
                               const int32_t* n_vis, int64_t cap, int64_t n_queries, int K,
                               int32_t* topk_out, hipStream_t stream);
 
+// streaming probes (csa2_probe.hip): mode 0 reads n_bytes of src (one word
+// per workgroup to sink), mode 1 copies src to dst; n_bytes a multiple of 16
+hipError_t launch_stream_probe(int mode, const void* src, void* dst, size_t n_bytes,
+                               uint32_t* sink, int n_blocks, hipStream_t stream);
+
 struct AttnArgs {
     const float* q;          // [n_q][H][128]
     int H;

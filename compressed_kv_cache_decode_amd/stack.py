@@ -96,17 +96,23 @@ class DecodeStack:
                       stream=stream)
 
     def step(self, iq, iw, n_vis, q, swa_k, swa_v, swa_ks, swa_vs, swa_len, stream=None,
-             scan_timer=None, attn_timer=None):
+             scan_timer=None, attn_timer=None, index_events=None):
         """One decode step.
 
         iq [n_idx][B][1][4][64], iw [n_idx][B][1][4]: one indexer query per
         Full/Reindex layer; n_vis [B][1] int32; q [L][B][H][128];
         swa_k/v [L][B][128][128] u8, swa_ks/vs [L][B][128] f32, swa_len [B].
         scan_timer: optional KernelTimer bracketing the Full layer's scan;
-        attn_timer: optional KernelTimer bracketing every layer's attention kernel.
+        attn_timer: optional KernelTimer bracketing every layer's attention kernel;
+        index_events: optional list; each Full / Reindex call is appended to it
+        as (mode, start, end) timing events recorded on the current stream.
         Returns the list of top-K buffers each layer attended with."""
         used, cur, k = [], None, 0
         for layer, mode in enumerate(self.plan):
+            if index_events is not None and mode in "FX":
+                ev = (mode, torch.cuda.Event(enable_timing=True),
+                      torch.cuda.Event(enable_timing=True))
+                ev[1].record()
             if mode == "F":
                 index_full(self.cache, iq[k], iw[k], n_vis, self.topk_bufs[k],
                            self.pool if self.pool_blocks else None, topk=self.topk,
@@ -117,6 +123,9 @@ class DecodeStack:
                 index_reindex(self.cache, iq[k], iw[k], n_vis, self.pool, self.topk_bufs[k],
                               topk=self.topk, ws=self.ws_reindex, stream=stream)
                 cur, k = self.topk_bufs[k], k + 1
+            if index_events is not None and mode in "FX":
+                ev[2].record()
+                index_events.append(ev)
             if self.stage is None:
                 sparse_attn_decode(q[layer], self.cache, cur.view(self.B, self.topk),
                                    swa_k[layer], swa_v[layer], swa_ks[layer], swa_vs[layer],

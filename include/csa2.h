@@ -426,6 +426,21 @@ const char* csa2_status_str(int status);
 int csa2_abi_version(void);
 
 /*
+ * csa2_stream_probe -- diagnostics: the streaming ceilings of this GPU, for
+ * comparing the kernels above against in the same run (not part of the
+ * method).  mode 0 reads n_bytes of src with 16-byte non-temporal loads and
+ * writes one word per workgroup to sink [n_blocks]; mode 1 copies n_bytes of
+ * src to dst; both grid-stride over n_blocks workgroups of 256 threads, four
+ * loads in flight per thread.  mode 2 reads src with one 16-byte load per
+ * thread over a grid covering it (n_blocks unused; sink [1] is written only
+ * by a data-dependent test that keeps the loads).  n_bytes a multiple of 16;
+ * device pointers; enqueued on `stream`.  CSA2_E_ARG for a bad mode, size or
+ * null pointer.
+ */
+int csa2_stream_probe(int mode, const void* src, void* dst, size_t n_bytes, uint32_t* sink,
+                      int n_blocks, hipStream_t stream);
+
+/*
  * csa2_index_full_noalloc -- csa2_index_full for callers that cannot allocate
  * device memory (code being captured into a HIP graph, tight serving loops,
  * harnesses that forbid hipMalloc): no workspace argument; the call allocates
