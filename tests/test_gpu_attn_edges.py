@@ -97,7 +97,7 @@ def build_decode_case(oracle_mod, name, B=3, cap=2048, H=64, topk=512, seed=0):
     sks, svs = sks.reshape(B, 128), svs.reshape(B, 128)
     idx = np.stack([np.sort(g.choice(cap, topk, replace=False)) for _ in range(B)]).astype(np.int32)
     q = (g.standard_normal((B, H, 128)) * qs).astype(np.float32)
-    sl = np.array([128, 77, 128][:B], np.int32)
+    sl = np.resize(np.array([128, 77, 128], np.int32), B)
     for b in range(B):
         if dom == "global_last" or dom == "global_late":
             # global_last: slot 511 sits in the last selected tile (tile 15,

@@ -161,10 +161,10 @@ def test_decoder_stack_128k_full_size(gpu, oracle_mod):
 
 
 def test_decoder_stack_1m_full_size(gpu, oracle_mod):
-    """1M-position stack (B=4) with planted clusters; oracle on 2 sequences;
-    the planted blocks must dominate the Full layer's pool."""
+    """1M-position stack (B=4) with planted clusters, all 20 layers; oracle on
+    2 sequences; the planted blocks must dominate the Full layer's pool."""
     wl = synth.WORKLOADS["decoder_stack_1m"]
-    inp, tk_all = run_stack_case(gpu, oracle_mod, wl, sample=[0, 3], layers=5)
+    inp, tk_all = run_stack_case(gpu, oracle_mod, wl, sample=[0, 3])
     for b in range(wl.B):
         planted = set((inp.planted[b][:, None] * 8 + np.arange(8)).ravel().tolist())
         sel = [p for p in tk_all[0][b, 0].tolist() if p >= 0]
@@ -179,10 +179,11 @@ def test_decoder_stack_128k_fp4idx_full_size(gpu, oracle_mod):
 
 
 def test_decoder_stack_1m_fp4idx_full_size(gpu, oracle_mod):
-    """1M positions with FP4 indexer keys (B=4, planted clusters); oracle on one
-    sequence; the planted blocks dominate the Full layer's selection."""
+    """1M positions with FP4 indexer keys (B=4, planted clusters), all 20
+    layers; oracle on one sequence; the planted blocks dominate the Full
+    layer's selection."""
     wl = synth.WORKLOADS["decoder_stack_1m_fp4idx"]
-    inp, tk_all = run_stack_case(gpu, oracle_mod, wl, sample=[2], layers=5)
+    inp, tk_all = run_stack_case(gpu, oracle_mod, wl, sample=[2])
     for b in range(wl.B):
         planted = set((inp.planted[b][:, None] * 8 + np.arange(8)).ravel().tolist())
         sel = [p for p in tk_all[0][b, 0].tolist() if p >= 0]
