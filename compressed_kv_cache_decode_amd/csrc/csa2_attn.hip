@@ -78,13 +78,16 @@ constexpr float kLn2 = 0.6931471805599453f;
 // reference maxima and sums), so a wave can store its state as soon as its
 // own tiles are done
 constexpr int kWaveBytes = kTile * kVPitch * 2;
-constexpr int merge_bytes(int W) { return (W * kGroupHeads * kMergePitch + 2 * W * kGroupHeads) * 4; }
+// a wave's merge rows (16 heads x 128 fp32, its running max and sum per
+// head) go into its own V-tile area once it is done with its tiles
+constexpr int kWaveMergeBytes = (kGroupHeads * kMergePitch + 2 * kGroupHeads) * 4;
 // q of the workgroup's 16 heads as fp16 hi and lo rows, and each head's scale
 constexpr int kQPitch = kHeadDim + 8;  // fp16 per q row
 constexpr int kQBytes = 2 * kGroupHeads * kQPitch * 2 + kGroupHeads * 4;
-constexpr int lds_bytes(int W) { return W * kWaveBytes + merge_bytes(W) + kQBytes; }
+constexpr int lds_bytes(int W) { return W * kWaveBytes + kQBytes; }
+static_assert(kWaveMergeBytes <= kWaveBytes, "a wave's merge rows fit its tile area");
 static_assert(lds_bytes(kWavesWide) <= 160 * 1024, "LDS");
-static_assert(2 * lds_bytes(kWavesNarrow) <= 160 * 1024, "two narrow workgroups per CU");
+static_assert(3 * lds_bytes(kWavesNarrow) <= 160 * 1024, "three narrow workgroups per CU");
 
 // Stage of a layer group (raw bytes of the selected records as the lanes hold
 // them): per tile four 1 KiB planes of 16 bytes per lane (K block 0, K block
@@ -296,11 +299,27 @@ __device__ __forceinline__ half8_t v_operand(const _Float16* vtile, int lane, in
     return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// The MFMA B operands of the wave's q (head c, MFMA step ks: channels
+// 32g + 8ks .. +8, fp16 hi and lo parts): held in registers for the whole
+// kernel (QRegs), or read from the workgroup's LDS rows at each use (QLds,
+// 32 registers fewer).
+struct QRegs {
+    half8_t h[4], l[4];
+    __device__ __forceinline__ half8_t hi(int ks) const { return h[ks]; }
+    __device__ __forceinline__ half8_t lo(int ks) const { return l[ks]; }
+};
+struct QLds {
+    const _Float16* h;  // q_hi + c * kQPitch + 32 g
+    const _Float16* l;
+    __device__ __forceinline__ half8_t hi(int ks) const { return *reinterpret_cast<const half8_t*>(h + 8 * ks); }
+    __device__ __forceinline__ half8_t lo(int ks) const { return *reinterpret_cast<const half8_t*>(l + 8 * ks); }
+};
+
 // One tile of selected FP4 records.
-template <int STAGE>
+template <int STAGE, class QOps>
 __device__ __forceinline__ void process_global(const SeqView& s, int t, const GTile& r,
-                                               const half8_t (&qhi)[4], const half8_t (&qlo)[4],
-                                               float qmul, _Float16* __restrict__ vtile, int lane,
+                                               const QOps& q, float qmul,
+                                               _Float16* __restrict__ vtile, int lane,
                                                WaveState& st) {
     const int g = lane >> 4;
     if (STAGE == kStageWrite && t % s.stage_mod == s.stage_rem) {
@@ -340,8 +359,8 @@ __device__ __forceinline__ void process_global(const SeqView& s, int t, const GT
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const half8_t ka = ks < 2 ? fp4x8_h8<0>(r.k[blk][ks], sk) : fp4x8_h8<1>(r.k[blk][ks], sk);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qhi[ks], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qlo[ks], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, q.hi(ks), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, q.lo(ks), acc, 0, 0, 0);
         }
         sacc[blk] = acc;
     }
@@ -372,8 +391,8 @@ __device__ __forceinline__ void process_global(const SeqView& s, int t, const GT
 }
 
 // One tile of FP8 window tokens, of which the first n (>= 1) are attended.
-__device__ __forceinline__ void process_window(const WTile& r, int n, const half8_t (&qhi)[4],
-                                               const half8_t (&qlo)[4], float qmul,
+template <class QOps>
+__device__ __forceinline__ void process_window(const WTile& r, int n, const QOps& q, float qmul,
                                                _Float16* __restrict__ vtile, int lane,
                                                WaveState& st) {
     const int g = lane >> 4;
@@ -391,8 +410,8 @@ __device__ __forceinline__ void process_window(const WTile& r, int n, const half
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const half8_t ka = fp8x8_h8(r.k[blk][ks >> 1][2 * (ks & 1)], r.k[blk][ks >> 1][2 * (ks & 1) + 1]);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qhi[ks], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qlo[ks], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, q.hi(ks), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, q.lo(ks), acc, 0, 0, 0);
         }
         sacc[blk] = acc;
     }
@@ -459,7 +478,7 @@ __device__ __forceinline__ void touch(const T& v) {
 // Workgroup id -> (query bq, head group hg): ids with the same id % 8 share an
 // XCD, and all head groups of one query get ids with the same id % 8.
 template <int STAGE, int kWaves>
-__global__ __launch_bounds__(kWaves * 64, 2) void k_attn(AttnArgs a, int n_tiles_global) {
+__global__ __launch_bounds__(kWaves * 64, kWaves == kWavesNarrow ? 3 : 2) void k_attn(AttnArgs a, int n_tiles_global) {
     constexpr int kThreads = kWaves * 64;
     __shared__ __attribute__((aligned(16))) unsigned char smem[lds_bytes(kWaves)];
     touch(a.q); touch(a.H); touch(a.Q); touch(a.kvc); touch(a.kvs); touch(a.cap);
@@ -508,7 +527,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_attn(AttnArgs a, int n_tiles
     // flight), and at most one window tile: window tile j is the
     // (n_tiles_global + j)-th tile of the query, dealt round robin like the
     // others.  Every load the wave's first tiles need is issued before
-    // anything waits.
+    // anything waits, and the window tile, whose rows do not wait for the
+    // positions, is attended first, while the selected records are on their
+    // way.  Narrow workgroups run three to a CU, so a wave has 168 registers:
+    // it reads its q operands from LDS at each tile.
+    constexpr bool kLean = kWaves == kWavesNarrow;
     const int n_win_max = (s.win_rows + kTile - 1) / kTile;
     const int jw = ((wave - n_tiles_global) % kWaves + kWaves) % kWaves;
     const bool has_win = jw < n_win_max;
@@ -563,7 +586,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_attn(AttnArgs a, int n_tiles
     // q * sm_scale * log2(e), scaled per head by a power of two into
     // [2^14, 2^15), as fp16 hi + lo rows in LDS; then every wave reads its
     // B operands: head c, MFMA step ks takes channels 32g + 8ks .. +8
-    _Float16* q_hi = reinterpret_cast<_Float16*>(smem + kWaves * kWaveBytes + merge_bytes(kWaves));
+    _Float16* q_hi = reinterpret_cast<_Float16*>(smem + kWaves * kWaveBytes);
     _Float16* q_lo = q_hi + kGroupHeads * kQPitch;
     float* q_mul = reinterpret_cast<float*>(q_lo + kGroupHeads * kQPitch);
     {
@@ -591,11 +614,16 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_attn(AttnArgs a, int n_tiles
         }
     }
     __syncthreads();
-    half8_t qhi[4], qlo[4];
+    typename std::conditional<kLean, QLds, QRegs>::type qo;
+    if constexpr (kLean) {
+        qo.h = q_hi + c * kQPitch + 32 * g;
+        qo.l = q_lo + c * kQPitch + 32 * g;
+    } else {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        qhi[ks] = *reinterpret_cast<const half8_t*>(q_hi + c * kQPitch + 32 * g + 8 * ks);
-        qlo[ks] = *reinterpret_cast<const half8_t*>(q_lo + c * kQPitch + 32 * g + 8 * ks);
+        for (int ks = 0; ks < 4; ++ks) {
+            qo.h[ks] = *reinterpret_cast<const half8_t*>(q_hi + c * kQPitch + 32 * g + 8 * ks);
+            qo.l[ks] = *reinterpret_cast<const half8_t*>(q_lo + c * kQPitch + 32 * g + 8 * ks);
+        }
     }
     const float qmul = q_mul[c];
 
@@ -607,35 +635,35 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_attn(AttnArgs a, int n_tiles
     st.m = -INFINITY;
     _Float16* vtile = reinterpret_cast<_Float16*>(smem + wave * kWaveBytes);
 
+    if (has_win && jw * kTile < s.swa_len)
+        process_window(rw, s.swa_len - jw * kTile, qo, qmul, vtile, lane, st);
     int k = 0;  // index of tile t among the wave's selected-record tiles
     for (int t = t0; t < n_tiles_global; t += 2 * kWaves, k += 2) {
-        process_global<STAGE>(s, t, ra, qhi, qlo, qmul, vtile, lane, st);
+        process_global<STAGE>(s, t, ra, qo, qmul, vtile, lane, st);
         if (t + 2 * kWaves < n_tiles_global)
             fetch_global<STAGE>(s, t + 2 * kWaves, tile_pos(k + 2), (k + 2) & 1, lane, ra);
         const int u = t + kWaves;
         if (u < n_tiles_global) {
-            process_global<STAGE>(s, u, rb, qhi, qlo, qmul, vtile, lane, st);
+            process_global<STAGE>(s, u, rb, qo, qmul, vtile, lane, st);
             if (u + 2 * kWaves < n_tiles_global)
                 fetch_global<STAGE>(s, u + 2 * kWaves, tile_pos(k + 3), (k + 3) & 1, lane, rb);
         }
     }
-    if (has_win && jw * kTile < s.swa_len)
-        process_window(rw, s.swa_len - jw * kTile, qhi, qlo, qmul, vtile, lane, st);
 
-    // ---- merge the waves' states through LDS ----
+    // ---- merge the waves' states through LDS: each wave's rows, max and
+    // sum in its own tile area (m_rows(w)), which only it has used so far ----
     const float l_wave = st.lsum[0] + xsum4(st.lwin);
-    float* mo = reinterpret_cast<float*>(smem + kWaves * kWaveBytes);
-    float* mm = mo + kWaves * kGroupHeads * kMergePitch;
-    float* ml = mm + kWaves * kGroupHeads;
+    auto m_rows = [&](int w) { return reinterpret_cast<float*>(smem + w * kWaveBytes); };
+    constexpr int kMaxOff = kGroupHeads * kMergePitch, kSumOff = kMaxOff + kGroupHeads;
     {
-        float* orow = mo + (wave * kGroupHeads + c) * kMergePitch + 4 * g;
+        float* orow = m_rows(wave) + c * kMergePitch + 4 * g;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
             *reinterpret_cast<float4*>(orow + 16 * dt) =
                 make_float4(st.o[dt][0], st.o[dt][1], st.o[dt][2], st.o[dt][3]);
         if (g == 0) {
-            mm[wave * kGroupHeads + c] = st.m;
-            ml[wave * kGroupHeads + c] = l_wave;
+            m_rows(wave)[kMaxOff + c] = st.m;
+            m_rows(wave)[kSumOff + c] = l_wave;
         }
     }
     __syncthreads();
@@ -643,17 +671,16 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_attn(AttnArgs a, int n_tiles
         const int hh = item / (kHeadDim / 4), d4 = item % (kHeadDim / 4);
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mm[w * kGroupHeads + hh]);
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, m_rows(w)[kMaxOff + hh]);
         float L = 0.0f;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         if (M != -INFINITY) {
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) {
-                const float mw = mm[w * kGroupHeads + hh];
+                const float mw = m_rows(w)[kMaxOff + hh];
                 const float wt = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-                L += wt * ml[w * kGroupHeads + hh];
-                const float4 ow = *reinterpret_cast<const float4*>(
-                    mo + (w * kGroupHeads + hh) * kMergePitch + 4 * d4);
+                L += wt * m_rows(w)[kSumOff + hh];
+                const float4 ow = *reinterpret_cast<const float4*>(m_rows(w) + hh * kMergePitch + 4 * d4);
                 acc.x += wt * ow.x;
                 acc.y += wt * ow.y;
                 acc.z += wt * ow.z;
