@@ -849,16 +849,32 @@ def attn_sweep_points(batches, n_launch):
                                         timer=timer if rep else None)
             torch.cuda.synchronize()
         ms = sorted(timer.durations_ms())
+        # the same launches with no arithmetic: csa2_gather_probe reads the
+        # same bytes (records, window, q) and writes the same row count
+        timer.reset()
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(int(2e5 * n_launch))
+        for i in range(n_launch):
+            d = sets[i % 3]
+            csa2.gather_probe(d["q"], cache, d["idx"], d["swk"], d["swv"], d["sks"], d["svs"],
+                              d["out"], timer=timer)
+        torch.cuda.synchronize()
+        gms = sorted(timer.durations_ms())
         timer.close()
         mean = sum(ms) / len(ms)
+        gmean = sum(gms) / len(gms)
         nbytes = B * attn_bytes(topk, 128, H)
         sweep.append({"batch": B, "mean_us": round(mean * 1e3, 2),
                       "median_us": round(percentile(ms, 0.5) * 1e3, 2),
                       "bytes_per_launch": nbytes,
                       "achieved_GBps": round(nbytes / (mean * 1e-3) / 1e9, 1),
-                      "frac": round(nbytes / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+                      "frac": round(nbytes / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "gather_probe_us": round(gmean * 1e3, 2),
+                      "gather_probe_GBps": round(nbytes / (gmean * 1e-3) / 1e9, 1),
+                      "frac_of_gather": round(gmean / mean, 4)})
         log(f"attention sweep: B={B}: {mean * 1e3:.2f} us, "
-            f"{nbytes / (mean * 1e-3) / 1e9:.0f} GB/s")
+            f"{nbytes / (mean * 1e-3) / 1e9:.0f} GB/s; memory-only gather probe "
+            f"{gmean * 1e3:.2f} us, {nbytes / (gmean * 1e-3) / 1e9:.0f} GB/s")
         del cache, sets
         torch.cuda.empty_cache()
     return sweep
@@ -1056,8 +1072,9 @@ def measure_decode(args, wl, cpu=True):
 def extras(args, result):
     """Beside the headline: the copy and read ceilings of this GPU (every
     roofline entry also as a fraction of them), the gathering attention at
-    large batches (where it is bandwidth- rather than latency-bound), and the
-    1M-entry decoder stack as a secondary workload."""
+    large batches (where it is bandwidth- rather than latency-bound) beside
+    the memory-only gather probe over the same bytes, and the 1M-entry
+    decoder stack as a secondary workload."""
     import torch
 
     from compressed_kv_cache_decode_amd import synth
@@ -1069,7 +1086,12 @@ def extras(args, result):
             "kernel": f"k_attn (sparse attention, gathering, batch {B}, 64 heads, top-512 + "
                       f"128-token window)", "bound": "hbm", "achieved": pt["achieved_GBps"],
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": pt["frac"], "traffic": None,
-            "bytes_per_launch": pt["bytes_per_launch"], "mean_us": pt["mean_us"]}, ceil))
+            "bytes_per_launch": pt["bytes_per_launch"], "mean_us": pt["mean_us"],
+            # the same bytes read and written by csa2_gather_probe, no arithmetic:
+            # the access pattern's own ceiling (random 144-byte records)
+            "gather_probe_us": pt["gather_probe_us"],
+            "gather_probe_GBps": pt["gather_probe_GBps"],
+            "frac_of_gather": pt["frac_of_gather"]}, ceil))
     sub = argparse.Namespace(**vars(args))
     sub.steps, sub.warmup, sub.cache_sets = min(args.steps, 30), min(args.warmup, 5), 2
     r1m = measure_decode(sub, synth.WORKLOADS["decoder_stack_1m"], cpu=False)

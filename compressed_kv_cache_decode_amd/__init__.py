@@ -53,7 +53,7 @@ EXPORTS = ("csa2_quant_fp4", "csa2_quant_fp8", "csa2_write_entries", "csa2_write
            "csa2_status_str", "csa2_abi_version", "csa2_codec_probe",
            "csa2_quant_idx_fp4", "csa2_write_entries_proj_fp4", "csa2_index_full_fp4",
            "csa2_index_full_fp4_timed", "csa2_index_reindex_fp4", "csa2_rope_table",
-           "csa2_index_full_noalloc", "csa2_stream_probe")
+           "csa2_index_full_noalloc", "csa2_stream_probe", "csa2_gather_probe")
 
 _lib = None
 
@@ -96,6 +96,8 @@ _SIGS = {
     "csa2_abi_version": (_int, []),
     "csa2_rope_table": (_int, [_vp, _i64, ctypes.c_double, _vp]),
     "csa2_stream_probe": (_int, [_int, _vp, _vp, _sz, _vp, _int, _vp]),
+    "csa2_gather_probe": (_int, [_vp, _vp, _vp, _int, _int, _i64, _vp, _vp, _vp, _vp, _vp, _int,
+                                 _vp, _vp, _vp, _vp]),
     "csa2_index_full_noalloc": (_int, [_vp, _vp, _i64, _int, _int, _vp, _vp, _vp, _int, _int, _vp,
                                        _vp, _vp]),
     "csa2_codec_probe": (_int, [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),
@@ -518,6 +520,28 @@ def stream_probe(mode, src, dst=None, sink=None, n_blocks=2048, stream=None):
                                  src.numel(), _ptr(sink, torch.int32, "sink", n_blocks) if sink is not None else None,
                                  n_blocks, _stream(stream))
     _check(rc, "csa2_stream_probe")
+
+
+def gather_probe(q, cache, topk_idx, swa_k, swa_v, swa_ks, swa_vs, out, stream=None, timer=None):
+    """Diagnostics: reads what sparse_attn_decode reads for a full window
+    (q [B][H][128], the selected records, the 128 window rows) and writes out
+    [B][H][128] with no arithmetic: each word i of a query's row is word
+    i mod 4 of the XOR of every 16-byte unit read for it (csa2_gather_probe).
+    timer: optional KernelTimer; its next event pair brackets the dispatch."""
+    B, H = q.shape[0], q.shape[1]
+    _check_batch(cache, B, "gather_probe")
+    topk = topk_idx.shape[-1]
+    ev = timer.next_pair() if timer is not None else (None, None)
+    rc = lib().csa2_gather_probe(
+        _ptr(cache.kv_codes, torch.uint8, "kv_codes"), _ptr(cache.kv_scales, torch.uint8, "kv_scales"),
+        _ptr(topk_idx, torch.int32, "topk_idx", B * topk), B, topk, cache.cap,
+        _ptr(swa_k, torch.uint8, "swa_k", B * WINDOW * HEAD_DIM),
+        _ptr(swa_v, torch.uint8, "swa_v", B * WINDOW * HEAD_DIM),
+        _ptr(swa_ks, torch.float32, "swa_ks", B * WINDOW),
+        _ptr(swa_vs, torch.float32, "swa_vs", B * WINDOW),
+        _ptr(q, torch.float32, "q", B * H * HEAD_DIM), H,
+        _ptr(out, torch.float32, "out", B * H * HEAD_DIM), _stream(stream), ev[0], ev[1])
+    _check(rc, "csa2_gather_probe")
 
 
 # ---------------------------------------------------------------------------

@@ -378,6 +378,22 @@ __attribute__((visibility("default"))) int csa2_stream_probe(int mode, const voi
     return hip_status(launch_stream_probe(mode, src, dst, n_bytes, sink, n_blocks, stream));
 }
 
+__attribute__((visibility("default"))) int csa2_gather_probe(
+    const uint8_t* kv_codes, const uint8_t* kv_scales, const int32_t* topk_idx, int n_q, int topk,
+    int64_t cap, const uint8_t* swa_k, const uint8_t* swa_v, const float* swa_ks,
+    const float* swa_vs, const float* q, int H, float* out, hipStream_t stream, hipEvent_t start,
+    hipEvent_t stop) {
+    if (n_q < 0 || topk < 0 || topk > 2048 || cap <= 0 || H < 1 || H > 1024) return CSA2_E_ARG;
+    if (n_q == 0) return CSA2_OK;
+    const void* ptrs[] = {kv_codes, kv_scales, swa_k, swa_v, swa_ks, swa_vs, q, out};
+    for (const void* p : ptrs)
+        if (p == nullptr || reinterpret_cast<uintptr_t>(p) % 16 != 0) return CSA2_E_ARG;
+    if (topk > 0 && topk_idx == nullptr) return CSA2_E_ARG;
+    return hip_status(launch_gather_probe(kv_codes, kv_scales, topk_idx, n_q, topk, cap, swa_k,
+                                          swa_v, swa_ks, swa_vs, q, H, out, stream, start,
+                                          stop));
+}
+
 // ---------------------------------------------------------------------------
 // csa2_index_full without a caller workspace: the scratch is a fixed device
 // array of this library (one copy per GPU, loaded with the library's code and

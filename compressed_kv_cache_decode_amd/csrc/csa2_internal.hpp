@@ -112,6 +112,11 @@ hipError_t launch_select_pool(const uint32_t* ckeys, const int32_t* pool, int P,
 
 // streaming probes (csa2_probe.hip): mode 0 reads n_bytes of src (one word
 // per workgroup to sink), mode 1 copies src to dst; n_bytes a multiple of 16
+hipError_t launch_gather_probe(const uint8_t* kvc, const uint8_t* kvs, const int32_t* idx,
+                               int n_q, int topk, int64_t cap, const uint8_t* swk,
+                               const uint8_t* swv, const float* swks, const float* swvs,
+                               const float* q, int H, float* out, hipStream_t stream,
+                               hipEvent_t start, hipEvent_t stop);
 hipError_t launch_stream_probe(int mode, const void* src, void* dst, size_t n_bytes,
                                uint32_t* sink, int n_blocks, hipStream_t stream);
 

@@ -441,6 +441,27 @@ int csa2_stream_probe(int mode, const void* src, void* dst, size_t n_bytes, uint
                       int n_blocks, hipStream_t stream);
 
 /*
+ * csa2_gather_probe -- diagnostics: the memory-side ceiling of the gathering
+ * decode attention's access pattern (not part of the method).  For each of
+ * the n_q queries it reads exactly what csa2_sparse_attn_decode reads for a
+ * full window: the topk selected records (kv_codes [n_q][cap][128] and
+ * kv_scales [n_q][cap][16] at the positions of topk_idx [n_q][topk]; -1 or a
+ * position past cap is skipped), the 128 window rows swa_k / swa_v
+ * [n_q][128][128] with swa_ks / swa_vs [n_q][128], and q [n_q][H][128] fp32,
+ * and writes out [n_q][H][128]; no arithmetic.  Each 32-bit word i of a
+ * query's output row holds word i mod 4 of the XOR of all the 16-byte units
+ * read for that query.  One workgroup of 256 threads per query.  Device
+ * pointers, 16-byte aligned; enqueued on `stream`; start / stop (both or
+ * neither) are recorded immediately around the dispatch.  CSA2_E_ARG for
+ * topk outside [0, 2048], H outside [1, 1024], cap <= 0, a null or
+ * misaligned pointer.
+ */
+int csa2_gather_probe(const uint8_t* kv_codes, const uint8_t* kv_scales, const int32_t* topk_idx,
+                      int n_q, int topk, int64_t cap, const uint8_t* swa_k, const uint8_t* swa_v,
+                      const float* swa_ks, const float* swa_vs, const float* q, int H, float* out,
+                      hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
+/*
  * csa2_index_full_noalloc -- csa2_index_full for callers that cannot allocate
  * device memory (code being captured into a HIP graph, tight serving loops,
  * harnesses that forbid hipMalloc): no workspace argument; the call allocates

@@ -252,3 +252,25 @@ def test_noalloc_index_full_rejects_before_touching_the_gpu(lib):
     import compressed_kv_cache_decode_amd as csa2
     need = csa2.workspace_size(csa2.OP_INDEX_FULL, 16, 1, 131072, 512, 2048, 0)
     assert need <= csa2.NOALLOC_SCRATCH_BYTES
+
+
+def test_probes_reject_bad_arguments_before_touching_the_gpu(lib):
+    """The measurement probes (stream and gather) validate their scalars and
+    pointers on the host."""
+    s = lib.csa2_stream_probe
+    assert s(3, FAKE, FAKE, 64, FAKE, 16, None) == -1          # mode
+    assert s(0, FAKE, None, 63, FAKE, 16, None) == -1          # not a multiple of 16
+    assert s(0, FAKE, None, 64, None, 16, None) == -1          # read without a sink
+    assert s(1, FAKE, None, 64, None, 16, None) == -1          # copy without dst
+    assert s(0, FAKE, None, 64, FAKE, 0, None) == -1           # no workgroups
+    assert s(0, FAKE, None, 0, FAKE, 16, None) == 0            # nothing to do
+    g = lib.csa2_gather_probe
+    args = [FAKE, FAKE, FAKE, 4, 512, 1024, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, None, None, None]
+    for i, v in ((4, 4096), (4, -1), (5, 0), (11, 0), (0, None), (12, None),
+                 (6, ctypes.c_void_p(0x1008))):  # topk, cap, H, null and misaligned pointers
+        a = list(args)
+        a[i] = v
+        assert g(*a) == -1, (i, v)
+    a = list(args)
+    a[3] = 0
+    assert g(*a) == 0  # no queries
