@@ -695,6 +695,403 @@ __global__ __launch_bounds__(kWaves * 64, kWaves == kWavesNarrow ? 3 : 2) void k
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large launches with H a multiple of 32: one workgroup of 4 waves per (query,
+// group of 32 heads), two 16-head MFMA column blocks per wave, so each tile of
+// records is dequantised once for 32 heads (the 16-head workgroups above
+// dequantise it once per 16 heads).  Two workgroups per CU (54.4 KB of LDS,
+// up to 256 registers per wave).  The lane layouts, q scaling, softmax and
+// window handling of k_attn; the window tile first; the merge in two rounds
+// of one column block through each wave's own tile area.
+// ---------------------------------------------------------------------------
+constexpr int kPairCB = 2;                         // 16-head column blocks per wave
+constexpr int kPairHeads = kPairCB * kGroupHeads;  // 32
+constexpr int kPairWaves = 4;
+constexpr int kPairQBytes = 2 * kPairHeads * kQPitch * 2 + kPairHeads * 4;
+constexpr int kPairLds = kPairWaves * kWaveBytes + kPairQBytes;
+static_assert(2 * kPairLds <= 160 * 1024, "two pair workgroups per CU");
+
+struct PairState {
+    float4_t o[kPairCB][8];
+    float4_t lsum[kPairCB];
+    float lwin[kPairCB];
+    float m[kPairCB];
+};
+
+__device__ __forceinline__ void pair_rescale(float tmax, PairState& st, int cb) {
+    const bool move = tmax > st.m[cb] + kRescaleSlack || (st.m[cb] == -INFINITY && tmax != -INFINITY);
+    if (__builtin_amdgcn_ballot_w64(move)) {
+        const float m_new = move ? tmax : st.m[cb];
+        const float alpha = (st.m[cb] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(st.m[cb] - m_new);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) st.o[cb][dt] *= alpha;
+        st.lsum[cb] *= alpha;
+        st.lwin[cb] *= alpha;
+        st.m[cb] = m_new;
+    }
+}
+
+// S^T = K Q^T of both column blocks, channel step ks outer: the MFMAs of one
+// step for every (column block, row block) pair are issued before the next
+// step, four independent accumulations; q is read from the workgroup's LDS
+// rows (head cb*16 + c, channels 32g + 8ks .. +8).
+__device__ __forceinline__ void pair_scores(const half8_t (&ka)[2][4], const _Float16* q_hi,
+                                            const _Float16* q_lo, int c, int g,
+                                            float4_t (&sacc)[kPairCB][2]) {
+#pragma unroll
+    for (int cb = 0; cb < kPairCB; ++cb)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) sacc[cb][blk] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int cb = 0; cb < kPairCB; ++cb) {
+            const int off = (cb * kGroupHeads + c) * kQPitch + 32 * g + 8 * ks;
+            const half8_t qh = *reinterpret_cast<const half8_t*>(q_hi + off);
+            const half8_t ql = *reinterpret_cast<const half8_t*>(q_lo + off);
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+                sacc[cb][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[blk][ks], qh, sacc[cb][blk], 0, 0, 0);
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+                sacc[cb][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[blk][ks], ql, sacc[cb][blk], 0, 0, 0);
+        }
+    }
+}
+
+__device__ __forceinline__ void pair_global(const GTile& r, const _Float16* q_hi,
+                                            const _Float16* q_lo, const float (&qmul)[kPairCB],
+                                            _Float16* __restrict__ vtile, int lane, PairState& st) {
+    const int c = lane & 15, g = lane >> 4;
+    const uint32_t valid = __builtin_amdgcn_readfirstlane(r.valid);
+    if (valid == 0u) return;
+    {
+        const int q4 = lane & 3;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            half8_t* dst = reinterpret_cast<half8_t*>(vtile + (16 * j + (lane >> 2)) * kVPitch + 32 * q4);
+            const half2_t sv = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.vs >> (16 * j), 1.0f, false);
+            dst[0] = fp4x8_h8<0>(r.v[j][0], sv);
+            dst[1] = fp4x8_h8<0>(r.v[j][1], sv);
+            dst[2] = fp4x8_h8<1>(r.v[j][2], sv);
+            dst[3] = fp4x8_h8<1>(r.v[j][3], sv);
+        }
+    }
+    half8_t ka[2][4];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const half2_t sk = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.ks >> (16 * blk), 1.0f, false);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            ka[blk][ks] = ks < 2 ? fp4x8_h8<0>(r.k[blk][ks], sk) : fp4x8_h8<1>(r.k[blk][ks], sk);
+    }
+    const uint32_t vb = ((valid >> (4 * g)) & 0xFu) | (((valid >> (16 + 4 * g)) & 0xFu) << 4);
+    // S for every column block at once, channel steps outer: eight
+    // independent accumulation chains keep the MFMA pipe busy
+    float4_t sacc[kPairCB][2];
+    pair_scores(ka, q_hi, q_lo, c, g, sacc);
+    half8_t pb[kPairCB];
+#pragma unroll
+    for (int cb = 0; cb < kPairCB; ++cb) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = sacc[cb][i >> 2][i & 3];
+        if (valid != 0xFFFFFFFFu) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = (vb >> i) & 1u ? x[i] : -INFINITY;
+        }
+        float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        tmax = xmax4(tmax) * qmul[cb];
+        pair_rescale(tmax, st, cb);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            pb[cb][i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(x[i], qmul[cb], -st.m[cb]));
+    }
+    wave_lds_sync();
+    const half8_t ones = {1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16};
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        const half8_t va = v_operand(vtile, lane, dt);
+#pragma unroll
+        for (int cb = 0; cb < kPairCB; ++cb)
+            st.o[cb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[cb], st.o[cb][dt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int cb = 0; cb < kPairCB; ++cb)
+        st.lsum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[cb], st.lsum[cb], 0, 0, 0);
+    wave_lds_sync();
+}
+
+__device__ __forceinline__ void pair_window(const WTile& r, int n, const _Float16* q_hi,
+                                            const _Float16* q_lo, const float (&qmul)[kPairCB],
+                                            _Float16* __restrict__ vtile, int lane, PairState& st) {
+    const int c = lane & 15, g = lane >> 4;
+    const uint32_t valid = n >= kTile ? 0xFFFFFFFFu : ((1u << n) - 1u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        half8_t* dst = reinterpret_cast<half8_t*>(vtile + (8 * j + (lane >> 3)) * kVPitch + 16 * (lane & 7));
+        dst[0] = fp8x8_h8(r.v[j][0], r.v[j][1]);
+        dst[1] = fp8x8_h8(r.v[j][2], r.v[j][3]);
+    }
+    half8_t ka[2][4];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            ka[blk][ks] = fp8x8_h8(r.k[blk][ks >> 1][2 * (ks & 1)], r.k[blk][ks >> 1][2 * (ks & 1) + 1]);
+    float ksc[8], vsc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int e = c_entry(i, g);
+        ksc[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(e << 2, __float_as_int(r.sc)));
+        vsc[i] = __int_as_float(__builtin_amdgcn_ds_bpermute((32 + e) << 2, __float_as_int(r.sc)));
+    }
+    const uint32_t vb = ((valid >> (4 * g)) & 0xFu) | (((valid >> (16 + 4 * g)) & 0xFu) << 4);
+    float4_t sacc[kPairCB][2];
+    pair_scores(ka, q_hi, q_lo, c, g, sacc);
+    half8_t pb[kPairCB];
+    float down[kPairCB];
+#pragma unroll
+    for (int cb = 0; cb < kPairCB; ++cb) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = sacc[cb][i >> 2][i & 3] * qmul[cb] * ksc[i];
+        if (valid != 0xFFFFFFFFu) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = (vb >> i) & 1u ? x[i] : -INFINITY;
+        }
+        float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        tmax = xmax4(tmax);
+        pair_rescale(tmax, st, cb);
+        float w[8], wmax = 0.0f, psum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p = __builtin_amdgcn_exp2f(x[i] - st.m[cb]);
+            psum += p;
+            w[i] = p * vsc[i];
+            wmax = fmaxf(wmax, w[i]);
+        }
+        st.lwin[cb] += psum;
+        wmax = xmax4(wmax);
+        int e = wmax > 0.0f ? __builtin_amdgcn_frexp_expf(wmax) : 0;
+        e = e < -100 ? -100 : (e > 120 ? 120 : e);
+        const float up = __builtin_amdgcn_ldexpf(1.0f, 8 - e);
+        down[cb] = __builtin_amdgcn_ldexpf(1.0f, e - 8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[cb][i] = (_Float16)(w[i] * up);
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        const half8_t va = v_operand(vtile, lane, dt);
+#pragma unroll
+        for (int cb = 0; cb < kPairCB; ++cb) {
+            const float4_t zero = {0.f, 0.f, 0.f, 0.f};
+            const float4_t pv = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[cb], zero, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st.o[cb][dt][i] = fmaf(pv[i], down[cb], st.o[cb][dt][i]);
+        }
+    }
+    wave_lds_sync();
+}
+
+// grid = ceil(n_q / 8) * 8 * (H / 32) workgroups of 4 waves; the head groups
+// of one query share an XCD, as in k_attn.
+__global__ __launch_bounds__(kPairWaves * 64, 2) void k_attn_pair(AttnArgs a, int n_tiles_global) {
+    constexpr int kWaves = kPairWaves, kThreads = kWaves * 64;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kPairLds];
+    touch(a.q); touch(a.H); touch(a.Q); touch(a.kvc); touch(a.kvs); touch(a.cap);
+    touch(a.idx); touch(a.topk); touch(a.swk); touch(a.swv); touch(a.swks); touch(a.swvs);
+    touch(a.swa_len); touch(a.swa_rows); touch(a.sm_scale); touch(a.out); touch(a.lse);
+    touch(a.n_q); touch(n_tiles_global);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = lane & 15, g = lane >> 4;
+    const int G = a.H / kPairHeads;
+    const int id = blockIdx.x;
+    const int round = (id / kXcds) / G;
+    const int hg = (id / kXcds) - round * G;
+    const int64_t bq = (int64_t)round * kXcds + (id % kXcds);
+    if (bq >= a.n_q) return;  // uniform over the workgroup
+    const int64_t b = bq / a.Q;
+
+    SeqView s;
+    s.kvc = a.kvc + b * a.cap * 128;
+    s.kvs = a.kvs + b * a.cap * 16;
+    s.idx = a.idx + bq * a.topk;
+    s.stage = nullptr;
+    s.stage_rem = 0;
+    s.stage_mod = 1;
+    s.cap = a.cap;
+    s.topk = a.topk;
+    s.n_tiles_global = n_tiles_global;
+    int64_t w0;
+    if (a.swa_len != nullptr) {
+        w0 = b * a.swa_rows;
+        s.win_rows = a.swa_rows;
+    } else {
+        const int i = (int)(bq % a.Q);
+        const int start = i + 1 > kMaxWindow ? i + 1 - kMaxWindow : 0;
+        w0 = b * a.swa_rows + start;
+        s.win_rows = i + 1 - start;
+    }
+    s.swk = a.swk + w0 * kHeadDim;
+    s.swv = a.swv + w0 * kHeadDim;
+    s.swks = a.swks + w0;
+    s.swvs = a.swvs + w0;
+
+    const int n_win_max = (s.win_rows + kTile - 1) / kTile;
+    const int jw = ((wave - n_tiles_global) % kWaves + kWaves) % kWaves;
+    const int t0 = wave, t1 = wave + kWaves;
+    GTile ra, rb;
+    WTile rw;
+    int32_t P[kPosRegs];
+#pragma unroll
+    for (int k = 0; k < kPosRegs; ++k) {
+        const int t = wave + kWaves * (2 * k + (lane >> 5));
+        const int slot = t * kTile + (lane & 31);
+        int32_t p = -1;
+        if (t < n_tiles_global && slot < s.topk) p = s.idx[slot];
+        P[k] = (p >= 0 && p < s.cap) ? p : -1;
+    }
+    // this wave's share of q: 8 heads, 32 channels per lane and head pair
+    constexpr int kHPW = kPairHeads / kWaves;
+    float4 xq[kHPW / 2];
+#pragma unroll
+    for (int i = 0; i < kHPW / 2; ++i)
+        xq[i] = reinterpret_cast<const float4*>(
+            a.q + (bq * a.H + hg * kPairHeads + wave * kHPW + 2 * i + (lane >> 5)) * kHeadDim)[lane & 31];
+    // at most one window tile a wave (at most 128 window rows, 4 waves)
+    const bool has_win = jw < n_win_max;
+    if (has_win) fetch_window(s, jw, lane, rw);
+    if (t0 < n_tiles_global) fetch_global<0>(s, t0, P[0], 0, lane, ra);
+    if (t1 < n_tiles_global) fetch_global<0>(s, t1, P[0], 1, lane, rb);
+    if (a.swa_len != nullptr) {
+        const int sl = a.swa_len[b];
+        s.swa_len = sl < 0 ? 0 : (sl > a.swa_rows ? a.swa_rows : sl);
+    } else {
+        s.swa_len = s.win_rows;
+    }
+    auto tile_pos = [&](int k) -> int32_t {
+        if (k < 2 * kPosRegs) return P[k >> 1];
+        const int t = wave + kWaves * k;
+        const int slot = t * kTile + (lane & 31);
+        int32_t p = slot < s.topk ? s.idx[slot] : -1;
+        return (p >= 0 && p < s.cap) ? p : -1;
+    };
+
+    _Float16* q_hi = reinterpret_cast<_Float16*>(smem + kWaves * kWaveBytes);
+    _Float16* q_lo = q_hi + kPairHeads * kQPitch;
+    float* q_mul = reinterpret_cast<float*>(q_lo + kPairHeads * kQPitch);
+    {
+        const float logit_mul = a.sm_scale * kLog2e;
+#pragma unroll
+        for (int i = 0; i < kHPW / 2; ++i) {
+            const float x[4] = {xq[i].x * logit_mul, xq[i].y * logit_mul, xq[i].z * logit_mul,
+                                xq[i].w * logit_mul};
+            float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+#pragma unroll
+            for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+            int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 0;
+            e = e < -100 ? -100 : (e > 100 ? 100 : e);
+            const int head = wave * kHPW + 2 * i + (lane >> 5);
+            half4_t hv, lv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float v = __builtin_amdgcn_ldexpf(x[j], 15 - e);
+                hv[j] = (_Float16)v;
+                lv[j] = (_Float16)(v - (float)hv[j]);
+            }
+            *reinterpret_cast<half4_t*>(q_hi + head * kQPitch + 4 * (lane & 31)) = hv;
+            *reinterpret_cast<half4_t*>(q_lo + head * kQPitch + 4 * (lane & 31)) = lv;
+            if ((lane & 31) == 0) q_mul[head] = __builtin_amdgcn_ldexpf(1.0f, e - 15);
+        }
+    }
+    __syncthreads();
+    float qmul[kPairCB];
+#pragma unroll
+    for (int cb = 0; cb < kPairCB; ++cb) qmul[cb] = q_mul[cb * kGroupHeads + c];
+
+    PairState st;
+#pragma unroll
+    for (int cb = 0; cb < kPairCB; ++cb) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) st.o[cb][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+        st.lsum[cb] = float4_t{0.f, 0.f, 0.f, 0.f};
+        st.lwin[cb] = 0.0f;
+        st.m[cb] = -INFINITY;
+    }
+    _Float16* vtile = reinterpret_cast<_Float16*>(smem + wave * kWaveBytes);
+
+    // the window tile first: its rows do not wait for the positions
+    if (has_win && jw * kTile < s.swa_len)
+        pair_window(rw, s.swa_len - jw * kTile, q_hi, q_lo, qmul, vtile, lane, st);
+    int k = 0;
+    for (int t = t0; t < n_tiles_global; t += 2 * kWaves, k += 2) {
+        pair_global(ra, q_hi, q_lo, qmul, vtile, lane, st);
+        if (t + 2 * kWaves < n_tiles_global)
+            fetch_global<0>(s, t + 2 * kWaves, tile_pos(k + 2), (k + 2) & 1, lane, ra);
+        const int u = t + kWaves;
+        if (u < n_tiles_global) {
+            pair_global(rb, q_hi, q_lo, qmul, vtile, lane, st);
+            if (u + 2 * kWaves < n_tiles_global)
+                fetch_global<0>(s, u + 2 * kWaves, tile_pos(k + 3), (k + 3) & 1, lane, rb);
+        }
+    }
+
+    // ---- merge, one column block per round, each wave's rows, max and sum
+    // in its own tile area (m_rows(w)); the first round's writes need no
+    // barrier, since only this wave has used its area ----
+    float lw[kPairCB];
+#pragma unroll
+    for (int cb = 0; cb < kPairCB; ++cb) lw[cb] = st.lsum[cb][0] + xsum4(st.lwin[cb]);
+    auto m_rows = [&](int w) { return reinterpret_cast<float*>(smem + w * kWaveBytes); };
+    constexpr int kMaxOff = kGroupHeads * kMergePitch, kSumOff = kMaxOff + kGroupHeads;
+#pragma unroll
+    for (int cb = 0; cb < kPairCB; ++cb) {
+        if (cb > 0) __syncthreads();  // the previous round's readers are done
+        {
+            float* orow = m_rows(wave) + c * kMergePitch + 4 * g;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+                *reinterpret_cast<float4*>(orow + 16 * dt) =
+                    make_float4(st.o[cb][dt][0], st.o[cb][dt][1], st.o[cb][dt][2], st.o[cb][dt][3]);
+            if (g == 0) {
+                m_rows(wave)[kMaxOff + c] = st.m[cb];
+                m_rows(wave)[kSumOff + c] = lw[cb];
+            }
+        }
+        __syncthreads();
+        for (int item = tid; item < kGroupHeads * (kHeadDim / 4); item += kThreads) {
+            const int hh = item / (kHeadDim / 4), d4 = item % (kHeadDim / 4);
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) M = fmaxf(M, m_rows(w)[kMaxOff + hh]);
+            float L = 0.0f;
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (M != -INFINITY) {
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) {
+                    const float mw = m_rows(w)[kMaxOff + hh];
+                    const float wt = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+                    L += wt * m_rows(w)[kSumOff + hh];
+                    const float4 ow = *reinterpret_cast<const float4*>(m_rows(w) + hh * kMergePitch + 4 * d4);
+                    acc.x += wt * ow.x;
+                    acc.y += wt * ow.y;
+                    acc.z += wt * ow.z;
+                    acc.w += wt * ow.w;
+                }
+            }
+            const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+            const int64_t oh = bq * a.H + hg * kPairHeads + cb * kGroupHeads + hh;
+            *reinterpret_cast<float4*>(a.out + oh * kHeadDim + 4 * d4) =
+                make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+            if (d4 == 0) a.lse[oh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+        }
+    }
+}
+
 hipError_t launch_attn(const AttnArgs& a, void* /*ws*/, size_t /*ws_bytes*/, hipStream_t stream,
                        hipEvent_t start, hipEvent_t stop) {
     if (a.n_q <= 0) return hipSuccess;
@@ -708,6 +1105,19 @@ hipError_t launch_attn(const AttnArgs& a, void* /*ws*/, size_t /*ws_bytes*/, hip
     const int64_t rounds = (a.n_q + kXcds - 1) / kXcds;
     const unsigned grid = (unsigned)(rounds * kXcds * G);
     if (a.stage_mode != 0 && (a.stage == nullptr || a.Q != 1)) return hipErrorInvalidValue;
+    // enough (query, 16-head group) pairs to fill the chip twice and H a
+    // multiple of 32: workgroups of 32 heads, each tile dequantised once for
+    // all of them
+    if (a.stage_mode == 0 && a.H % kPairHeads == 0 && (int64_t)grid >= 2 * kCusPerChip) {
+        const unsigned pgrid = (unsigned)(rounds * kXcds * (a.H / kPairHeads));
+        if (start != nullptr && stop != nullptr)
+            hipExtLaunchKernelGGL(k_attn_pair, dim3(pgrid), dim3(kPairWaves * 64), 0, stream, start,
+                                  stop, 0, a, n_tiles_global);
+        else
+            hipLaunchKernelGGL(k_attn_pair, dim3(pgrid), dim3(kPairWaves * 64), 0, stream, a,
+                               n_tiles_global);
+        return hipGetLastError();
+    }
     // narrow workgroups once two rounds of wide ones would be needed
     const bool narrow = a.stage_mode == 0 && (int64_t)grid >= 2 * kCusPerChip;
     void (*kern)(AttnArgs, int) = a.stage_mode == kStageWrite  ? k_attn<kStageWrite, kWavesWide>

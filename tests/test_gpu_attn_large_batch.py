@@ -1,6 +1,7 @@
 """Sparse attention at large decode batches: the launches with at least 512
-(query, 16-head group) pairs, which the library runs with its narrow
-(4-wave) workgroups.  Compared with the oracle row by row
+(query, 16-head group) pairs, which the library runs with 4-wave workgroups
+of 32 heads (two MFMA column blocks per wave) when H is a multiple of 32, and
+of 16 heads otherwise.  Compared with the oracle row by row
 (max |o - o_ref| / max |o_ref| <= 2e-3, lse within 2e-3), including the
 softmax and number-format edge cases of test_gpu_attn_edges."""
 import math
@@ -22,7 +23,8 @@ def say(msg):
 
 
 @pytest.mark.parametrize("B,cap,H,topk", [(160, 2048, 64, 512), (80, 1024, 128, 100),
-                                          (128, 4096, 64, 2048)])
+                                          (128, 4096, 64, 2048), (176, 1024, 48, 512),
+                                          (136, 512, 32, 300)])
 def test_attn_large_batch_decode(gpu, oracle_mod, B, cap, H, topk):
     say(f"decode B={B} cap={cap} H={H} topk={topk}")
     g = np.random.default_rng(9300 + B)
