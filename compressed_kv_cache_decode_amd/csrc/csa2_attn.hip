@@ -213,13 +213,18 @@ __device__ __forceinline__ void fetch_window(const SeqView& s, int j, int lane, 
     r.sc = lane < 32 ? s.swks[row] : s.swvs[row];
 }
 
+// IEEE 754-2019 maximum (v_maximum3_f32 on gfx950): the same value as fmaxf
+// for every input but NaN, without the NaN-quieting instruction fmaxf costs
+// per operand here (MFMA results and lane swaps are not known to be quiet)
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // max / sum over the four lanes c, c+16, c+32, c+48 (v_permlane*_swap: each
 // call hands every lane its partner's value 32 resp. 16 lanes away)
 __device__ __forceinline__ float xmax4(float v) {
     auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    v = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
     auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float xsum4(float v) {
@@ -276,11 +281,16 @@ __device__ __forceinline__ void online_rescale(float tmax, WaveState& st) {
     const bool move = tmax > st.m + kRescaleSlack || (st.m == -INFINITY && tmax != -INFINITY);
     if (__builtin_amdgcn_ballot_w64(move)) {
         const float m_new = move ? tmax : st.m;
-        const float alpha = (st.m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(st.m - m_new);
+        // a head whose maximum is still -inf has accumulated nothing (every
+        // tile has a present entry, so its first one sets the maximum): the
+        // scaling is skipped while that holds for the whole wave
+        if (__builtin_amdgcn_ballot_w64(st.m != -INFINITY)) {
+            const float alpha = (st.m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(st.m - m_new);
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) st.o[dt] *= alpha;
-        st.lsum *= alpha;
-        st.lwin *= alpha;
+            for (int dt = 0; dt < 8; ++dt) st.o[dt] *= alpha;
+            st.lsum *= alpha;
+            st.lwin *= alpha;
+        }
         st.m = m_new;
     }
 }
@@ -373,8 +383,8 @@ __device__ __forceinline__ void process_global(const SeqView& s, int t, const GT
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = (vb >> i) & 1u ? x[i] : -INFINITY;
     }
-    float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    float tmax = vmax(vmax(vmax(x[0], x[1]), vmax(x[2], x[3])),
+                      vmax(vmax(x[4], x[5]), vmax(x[6], x[7])));
     tmax = xmax4(tmax) * qmul;
     online_rescale(tmax, st);
     half8_t pb;
@@ -430,8 +440,8 @@ __device__ __forceinline__ void process_window(const WTile& r, int n, const QOps
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = (vb >> i) & 1u ? x[i] : -INFINITY;
     }
-    float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    float tmax = vmax(vmax(vmax(x[0], x[1]), vmax(x[2], x[3])),
+                      vmax(vmax(x[4], x[5]), vmax(x[6], x[7])));
     tmax = xmax4(tmax);
     online_rescale(tmax, st);
     float w[8], wmax = 0.0f, psum = 0.0f;
@@ -440,7 +450,7 @@ __device__ __forceinline__ void process_window(const WTile& r, int n, const QOps
         const float p = __builtin_amdgcn_exp2f(x[i] - st.m);
         psum += p;
         w[i] = p * vsc[i];
-        wmax = fmaxf(wmax, w[i]);
+        wmax = vmax(wmax, w[i]);
     }
     st.lwin += psum;
     wmax = xmax4(wmax);
@@ -722,11 +732,13 @@ __device__ __forceinline__ void pair_rescale(float tmax, PairState& st, int cb) 
     const bool move = tmax > st.m[cb] + kRescaleSlack || (st.m[cb] == -INFINITY && tmax != -INFINITY);
     if (__builtin_amdgcn_ballot_w64(move)) {
         const float m_new = move ? tmax : st.m[cb];
-        const float alpha = (st.m[cb] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(st.m[cb] - m_new);
+        if (__builtin_amdgcn_ballot_w64(st.m[cb] != -INFINITY)) {  // as in online_rescale
+            const float alpha = (st.m[cb] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(st.m[cb] - m_new);
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) st.o[cb][dt] *= alpha;
-        st.lsum[cb] *= alpha;
-        st.lwin[cb] *= alpha;
+            for (int dt = 0; dt < 8; ++dt) st.o[cb][dt] *= alpha;
+            st.lsum[cb] *= alpha;
+            st.lwin[cb] *= alpha;
+        }
         st.m[cb] = m_new;
     }
 }
@@ -800,8 +812,8 @@ __device__ __forceinline__ void pair_global(const GTile& r, const _Float16* q_hi
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = (vb >> i) & 1u ? x[i] : -INFINITY;
         }
-        float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        float tmax = vmax(vmax(vmax(x[0], x[1]), vmax(x[2], x[3])),
+                          vmax(vmax(x[4], x[5]), vmax(x[6], x[7])));
         tmax = xmax4(tmax) * qmul[cb];
         pair_rescale(tmax, st, cb);
 #pragma unroll
@@ -861,8 +873,8 @@ __device__ __forceinline__ void pair_window(const WTile& r, int n, const _Float1
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = (vb >> i) & 1u ? x[i] : -INFINITY;
         }
-        float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        float tmax = vmax(vmax(vmax(x[0], x[1]), vmax(x[2], x[3])),
+                          vmax(vmax(x[4], x[5]), vmax(x[6], x[7])));
         tmax = xmax4(tmax);
         pair_rescale(tmax, st, cb);
         float w[8], wmax = 0.0f, psum = 0.0f;
@@ -871,7 +883,7 @@ __device__ __forceinline__ void pair_window(const WTile& r, int n, const _Float1
             const float p = __builtin_amdgcn_exp2f(x[i] - st.m[cb]);
             psum += p;
             w[i] = p * vsc[i];
-            wmax = fmaxf(wmax, w[i]);
+            wmax = vmax(wmax, w[i]);
         }
         st.lwin[cb] += psum;
         wmax = xmax4(wmax);
