@@ -59,12 +59,13 @@ def test_attn_large_batch_decode(gpu, oracle_mod, B, cap, H, topk):
     np.testing.assert_allclose(l[~empty], ref_lse[~empty], rtol=2e-3, atol=2e-3)
 
 
+@pytest.mark.parametrize("B,H", [(128, 64), (176, 48)])  # 32-head, then 16-head workgroups
 @pytest.mark.parametrize("name", ["peaked_x32", "dominant_global_first_then_later",
                                   "dominant_window", "all_extremes",
                                   "window_sigmas_2^-20_to_2^4"])
-def test_attn_large_batch_edges(gpu, oracle_mod, name):
-    say(f"edges {name}")
-    c = build_decode_case(oracle_mod, name, B=128, cap=1024, seed=40)
+def test_attn_large_batch_edges(gpu, oracle_mod, name, B, H):
+    say(f"edges {name} B={B} H={H}")
+    c = build_decode_case(oracle_mod, name, B=B, cap=1024, H=H, seed=40)
     cache = upload_cache(gpu, c)
     ref_out, ref_lse = oracle_mod.attn_decode_batch(c["q"], c["codes"], c["scales"], c["idx"],
                                                     c["sk"], c["sv"], c["sks"], c["svs"], c["sl"],
