@@ -504,6 +504,10 @@ __global__ __launch_bounds__(kWaves * 64, kWaves == kWavesNarrow ? 3 : 2) void k
     const int64_t bq = (int64_t)round * kXcds + (id % kXcds);
     if (bq >= a.n_q) return;  // uniform over the workgroup
     const int64_t b = bq / a.Q;
+    // the decode window length is loaded first: loads complete in issue
+    // order, so one issued after the tiles would hold back the q set-up
+    int sl = 0;
+    if (a.swa_len != nullptr) sl = a.swa_len[b];
 
     SeqView s;
     s.kvc = a.kvc + b * a.cap * 128;
@@ -548,20 +552,17 @@ __global__ __launch_bounds__(kWaves * 64, kWaves == kWavesNarrow ? 3 : 2) void k
     const int t0 = wave, t1 = wave + kWaves;
     GTile ra, rb;
     WTile rw;
-    int32_t P[kPosRegs];
-    if (STAGE == kStageRead) {
-        if (t0 < n_tiles_global) fetch_global<STAGE>(s, t0, 0, 0, lane, ra);
-        if (t1 < n_tiles_global) fetch_global<STAGE>(s, t1, 0, 0, lane, rb);
-    } else {
-        // positions of the wave's tiles: tile wave + kW in lanes
-        // 32 (k & 1) .. + 31 of register k / 2 (-1: absent)
+    // positions of the wave's tiles: tile wave + kW in lanes 32 (k & 1) ..
+    // + 31 of register k / 2 (-1: absent; unused by a stage-reading launch).
+    // Every lane loads (a slot past top-K reads a valid word and takes -1),
+    // so the waits count exactly the loads issued after these.
+    int32_t P[kPosRegs] = {};
+    if (STAGE != kStageRead) {
+        const int32_t* any = s.topk > 0 ? s.idx : reinterpret_cast<const int32_t*>(a.q);
 #pragma unroll
         for (int k = 0; k < kPosRegs; ++k) {
-            const int t = wave + kWaves * (2 * k + (lane >> 5));
-            const int slot = t * kTile + (lane & 31);
-            int32_t p = -1;
-            if (t < n_tiles_global && slot < s.topk) p = s.idx[slot];
-            P[k] = (p >= 0 && p < s.cap) ? p : -1;
+            const int slot = (wave + kWaves * (2 * k + (lane >> 5))) * kTile + (lane & 31);
+            P[k] = *(slot < s.topk ? s.idx + slot : any);
         }
     }
     // this wave's share of q: heads wave * HPW .. + HPW, 4 channels per lane
@@ -572,17 +573,27 @@ __global__ __launch_bounds__(kWaves * 64, kWaves == kWavesNarrow ? 3 : 2) void k
     for (int i = 0; i < kHPW / 2; ++i)
         xq[i] = reinterpret_cast<const float4*>(
             a.q + (bq * a.H + hg * kGroupHeads + wave * kHPW + 2 * i + (lane >> 5)) * kHeadDim)[lane & 31];
-    if (has_win) fetch_window(s, jw, lane, rw);
+    // Loads complete in issue order: q, then the window tile, then the
+    // selected-record tiles, in the order the wave consumes them.  They are
+    // issued unconditionally, so that each wait counts exactly the loads
+    // behind it: a wave without a window tile reads rows clamped to the
+    // window's first row, and one past the last selected tile reads stage
+    // tile 0 (a staging launch always has one) or, through positions of -1,
+    // cache row 0; neither tile is processed.
+    fetch_window(s, jw, lane, rw);
     if (STAGE != kStageRead) {
-        if (t0 < n_tiles_global) fetch_global<STAGE>(s, t0, P[0], 0, lane, ra);
-        if (t1 < n_tiles_global) fetch_global<STAGE>(s, t1, P[0], 1, lane, rb);
+        // the q and window loads stay ahead of the wait for the positions
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < kPosRegs; ++k) {
+            const int slot = (wave + kWaves * (2 * k + (lane >> 5))) * kTile + (lane & 31);
+            P[k] = (slot < s.topk && P[k] >= 0 && P[k] < s.cap) ? P[k] : -1;
+        }
     }
-    if (a.swa_len != nullptr) {
-        const int sl = a.swa_len[b];
-        s.swa_len = sl < 0 ? 0 : (sl > a.swa_rows ? a.swa_rows : sl);
-    } else {
-        s.swa_len = s.win_rows;
-    }
+    fetch_global<STAGE>(s, t0 < n_tiles_global ? t0 : 0, P[0], 0, lane, ra);
+    fetch_global<STAGE>(s, t1 < n_tiles_global ? t1 : 0, P[0], 1, lane, rb);
+    s.swa_len = a.swa_len != nullptr ? (sl < 0 ? 0 : (sl > a.swa_rows ? a.swa_rows : sl))
+                                     : s.win_rows;
     // the position register of the wave's k-th selected tile, loaded now when
     // it is past the preloaded ones
     auto tile_pos = [&](int k) -> int32_t {
@@ -927,6 +938,10 @@ __global__ __launch_bounds__(kPairWaves * 64, 2) void k_attn_pair(AttnArgs a, in
     const int64_t bq = (int64_t)round * kXcds + (id % kXcds);
     if (bq >= a.n_q) return;  // uniform over the workgroup
     const int64_t b = bq / a.Q;
+    // the decode window length is loaded first: loads complete in issue
+    // order, so one issued after the tiles would hold back the q set-up
+    int sl = 0;
+    if (a.swa_len != nullptr) sl = a.swa_len[b];
 
     SeqView s;
     s.kvc = a.kvc + b * a.cap * 128;
@@ -958,14 +973,14 @@ __global__ __launch_bounds__(kPairWaves * 64, 2) void k_attn_pair(AttnArgs a, in
     const int t0 = wave, t1 = wave + kWaves;
     GTile ra, rb;
     WTile rw;
+    // positions loaded by every lane, range-checked after the q and window
+    // loads are issued, as in k_attn
     int32_t P[kPosRegs];
+    const int32_t* any = s.topk > 0 ? s.idx : reinterpret_cast<const int32_t*>(a.q);
 #pragma unroll
     for (int k = 0; k < kPosRegs; ++k) {
-        const int t = wave + kWaves * (2 * k + (lane >> 5));
-        const int slot = t * kTile + (lane & 31);
-        int32_t p = -1;
-        if (t < n_tiles_global && slot < s.topk) p = s.idx[slot];
-        P[k] = (p >= 0 && p < s.cap) ? p : -1;
+        const int slot = (wave + kWaves * (2 * k + (lane >> 5))) * kTile + (lane & 31);
+        P[k] = *(slot < s.topk ? s.idx + slot : any);
     }
     // this wave's share of q: 8 heads, 32 channels per lane and head pair
     constexpr int kHPW = kPairHeads / kWaves;
@@ -976,15 +991,18 @@ __global__ __launch_bounds__(kPairWaves * 64, 2) void k_attn_pair(AttnArgs a, in
             a.q + (bq * a.H + hg * kPairHeads + wave * kHPW + 2 * i + (lane >> 5)) * kHeadDim)[lane & 31];
     // at most one window tile a wave (at most 128 window rows, 4 waves)
     const bool has_win = jw < n_win_max;
-    if (has_win) fetch_window(s, jw, lane, rw);
-    if (t0 < n_tiles_global) fetch_global<0>(s, t0, P[0], 0, lane, ra);
-    if (t1 < n_tiles_global) fetch_global<0>(s, t1, P[0], 1, lane, rb);
-    if (a.swa_len != nullptr) {
-        const int sl = a.swa_len[b];
-        s.swa_len = sl < 0 ? 0 : (sl > a.swa_rows ? a.swa_rows : sl);
-    } else {
-        s.swa_len = s.win_rows;
+    // issued unconditionally, as in k_attn (absent tiles read valid rows)
+    fetch_window(s, jw, lane, rw);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < kPosRegs; ++k) {
+        const int slot = (wave + kWaves * (2 * k + (lane >> 5))) * kTile + (lane & 31);
+        P[k] = (slot < s.topk && P[k] >= 0 && P[k] < s.cap) ? P[k] : -1;
     }
+    fetch_global<0>(s, t0, P[0], 0, lane, ra);
+    fetch_global<0>(s, t1, P[0], 1, lane, rb);
+    s.swa_len = a.swa_len != nullptr ? (sl < 0 ? 0 : (sl > a.swa_rows ? a.swa_rows : sl))
+                                     : s.win_rows;
     auto tile_pos = [&](int k) -> int32_t {
         if (k < 2 * kPosRegs) return P[k >> 1];
         const int t = wave + kWaves * k;
