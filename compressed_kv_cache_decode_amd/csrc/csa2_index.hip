@@ -334,19 +334,25 @@ __global__ __launch_bounds__(256) void k_pool_score(const uint8_t* __restrict__ 
     const int64_t b = bq / Q;
     const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t n_slots = (int64_t)P * kBlock;
+    // Loads complete in issue order.  The query's values and weight go out
+    // with the slot's block, and every lane then loads a key row (a slot past
+    // the pool or outside the visible positions reads the sequence's first
+    // row and is not scored), so the quantisation below waits for nothing
+    // and runs while the rows are in flight.
+    const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
+    const float x = iq[(bq * kIdxHeads + h) * kIdxDim + lane];
+    const float wh = iw[bq * kIdxHeads + h];
     const int nv = clamp_nvis(n_vis[bq], cap);
-    const int32_t blk = s < n_slots ? pool[bq * P + (s >> 3)] : -1;
+    const int32_t blk = pool[bq * P + (s < n_slots ? (s >> 3) : 0)];
     const int64_t pos = (int64_t)blk * kBlock + (s & 7);
-    const bool valid = blk >= 0 && pos < nv;
+    const bool valid = s < n_slots && blk >= 0 && pos < nv;
     IdxRow<FMT> r;
-    if (valid) r.load(ikc, iks, b * cap + pos);
+    r.load(ikc, iks, b * cap + (valid ? pos : 0));
     {   // the query's E4M3 codes (exact fp32 values) and folded weights
-        const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
-        const float x = iq[(bq * kIdxHeads + h) * kIdxDim + lane];
         const float sqh = wave_max_f32(fabsf(x)) / 448.0f;
         const uint32_t c = (sqh == 0.0f) ? ((__float_as_uint(x) >> 24) & 0x80u) : e4m3_encode(x / sqh);
         sq[h * kIdxDim + lane] = e4m3_decode_bits(c);
-        if (lane == 0) sw[h] = iw[bq * kIdxHeads + h] * sqh;
+        if (lane == 0) sw[h] = wh * sqh;
     }
     __syncthreads();
     if (s >= n_slots) return;

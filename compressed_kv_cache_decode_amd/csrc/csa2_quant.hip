@@ -87,10 +87,38 @@ __device__ __forceinline__ void quant_idx4_val(float x, int64_t row, uint8_t* __
 // proj (may be null): also the entry's indexer key, projected from its fp32 K
 // (after averaging and RoPE) and written in FP8 to ik_codes (tile layout) /
 // ik_sigma at the entry's row.
-__device__ __forceinline__ void quant_fp4_entry(const float* __restrict__ k,
-                                                const float* __restrict__ v, int64_t e, int ratio,
-                                                const float* __restrict__ rope_cs,
-                                                const int64_t* __restrict__ dst_rows,
+// The inputs of entry e as lane `lane` needs them: its K and V channel pair
+// (of both tokens of the pair when ratio is 2), its rotation pair (lanes
+// 32..63 load lane - 32's and ignore it) and the destination row.  Every load
+// is issued whatever the arguments (an unused one reads a valid word of the
+// entry's K row), so that a caller's later waits count them exactly.
+struct EntryIn {
+    float2 ka, kb, va, vb;  // kb, vb: second token (ratio 2)
+    float2 cs;
+    int64_t r, e;  // the loaded destination row (used when has_rows), the entry
+    bool has_rows;
+    __device__ __forceinline__ int64_t row() const { return has_rows ? r : e; }
+};
+
+__device__ __forceinline__ EntryIn load_fp4_entry(const float* __restrict__ k,
+                                                  const float* __restrict__ v, int64_t e,
+                                                  int ratio, const float* __restrict__ rope_cs,
+                                                  const int64_t* __restrict__ dst_rows, int lane) {
+    EntryIn in;
+    const int64_t t0 = ratio == 1 ? e : 2 * e, t1 = ratio == 1 ? t0 : t0 + 1;
+    const float* krow = k + t0 * kHeadDim;
+    in.ka = reinterpret_cast<const float2*>(krow)[lane];
+    in.va = reinterpret_cast<const float2*>(v + t0 * kHeadDim)[lane];
+    in.kb = reinterpret_cast<const float2*>(k + t1 * kHeadDim)[lane];
+    in.vb = reinterpret_cast<const float2*>(v + t1 * kHeadDim)[lane];
+    in.cs = reinterpret_cast<const float2*>(rope_cs != nullptr ? rope_cs + e * 64 : krow)[lane & 31];
+    in.r = *(dst_rows != nullptr ? dst_rows + e : reinterpret_cast<const int64_t*>(krow));
+    in.e = e;
+    in.has_rows = dst_rows != nullptr;
+    return in;
+}
+
+__device__ __forceinline__ void quant_fp4_entry(const EntryIn& in, int ratio, bool rope,
                                                 uint8_t* __restrict__ codes,
                                                 uint8_t* __restrict__ scales, int lane,
                                                 const float* __restrict__ proj = nullptr,
@@ -99,22 +127,15 @@ __device__ __forceinline__ void quant_fp4_entry(const float* __restrict__ k,
                                                 uint8_t* __restrict__ ik_scales4 = nullptr) {
     float k0, k1, v0, v1;
     if (ratio == 1) {
-        const float2 kk = reinterpret_cast<const float2*>(k + e * kHeadDim)[lane];
-        const float2 vv = reinterpret_cast<const float2*>(v + e * kHeadDim)[lane];
-        k0 = kk.x; k1 = kk.y; v0 = vv.x; v1 = vv.y;
+        k0 = in.ka.x; k1 = in.ka.y; v0 = in.va.x; v1 = in.va.y;
     } else {
         // mean of tokens 2e and 2e+1: fl(fl(a + b) * 0.5)
-        const float2 ka = reinterpret_cast<const float2*>(k + (2 * e) * kHeadDim)[lane];
-        const float2 kb = reinterpret_cast<const float2*>(k + (2 * e + 1) * kHeadDim)[lane];
-        const float2 va = reinterpret_cast<const float2*>(v + (2 * e) * kHeadDim)[lane];
-        const float2 vb = reinterpret_cast<const float2*>(v + (2 * e + 1) * kHeadDim)[lane];
-        k0 = (ka.x + kb.x) * 0.5f; k1 = (ka.y + kb.y) * 0.5f;
-        v0 = (va.x + vb.x) * 0.5f; v1 = (va.y + vb.y) * 0.5f;
+        k0 = (in.ka.x + in.kb.x) * 0.5f; k1 = (in.ka.y + in.kb.y) * 0.5f;
+        v0 = (in.va.x + in.vb.x) * 0.5f; v1 = (in.va.y + in.vb.y) * 0.5f;
     }
-    if (rope_cs != nullptr && lane < 32) {
+    if (rope && lane < 32) {
         // rotate the interleaved pair (2l, 2l+1) of the first 64 K channels
-        const float2 cs = reinterpret_cast<const float2*>(rope_cs + e * 64)[lane];
-        const float a = k0 * cs.x, b = k1 * cs.y, c = k0 * cs.y, d = k1 * cs.x;
+        const float a = k0 * in.cs.x, b = k1 * in.cs.y, c = k0 * in.cs.y, d = k1 * in.cs.x;
         k0 = a - b;
         k1 = c + d;
     }
@@ -134,7 +155,7 @@ __device__ __forceinline__ void quant_fp4_entry(const float* __restrict__ k,
     const uint32_t kb = code(k0, ksd) | (code(k1, ksd) << 4);
     const uint32_t vb = code(v0, vsd) | (code(v1, vsd) << 4);
 
-    const int64_t row = dst_rows ? dst_rows[e] : e;
+    const int64_t row = in.row();
     if (proj != nullptr) {
         const float key[1] = {project_idx_key(proj, k0, k1, lane)};
         if (ik_scales4 != nullptr) quant_idx4_val(key[0], row, ik_codes, ik_scales4, lane);
@@ -156,7 +177,9 @@ __global__ __launch_bounds__(256) void k_quant_fp4(const float* __restrict__ k,
                                                    uint8_t* __restrict__ scales) {
     const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (e >= n_ent) return;  // uniform over the wave
-    quant_fp4_entry(k, v, e, ratio, rope_cs, dst_rows, codes, scales, threadIdx.x & 63);
+    const int lane = threadIdx.x & 63;
+    quant_fp4_entry(load_fp4_entry(k, v, e, ratio, rope_cs, dst_rows, lane), ratio,
+                    rope_cs != nullptr, codes, scales, lane);
 }
 
 // Row r of 64 or 128 values by one wave.
@@ -201,16 +224,29 @@ __global__ __launch_bounds__(256) void k_write_entries(Fp4Job f, Fp8Jobs j) {
     // a workgroup holding entry waves stages the projection once, with every
     // thread (uniform over the workgroup, before any wave leaves)
     const bool stage = f.proj != nullptr && (int64_t)blockIdx.x * 4 < f.n_ent;
+    // the projection rows (all eight 16-byte loads of each thread at once)
+    // and an entry wave's own inputs go out together, before any wait
+    constexpr int kPer = kIdxDim * kHeadDim / 4 / 256;
+    static_assert(kPer * 256 * 4 == kIdxDim * kHeadDim, "the projection splits evenly");
+    float4 pv[kPer];
     if (stage) {
-        for (int i = threadIdx.x; i < kIdxDim * kHeadDim / 4; i += 256) {
-            const float4 v = reinterpret_cast<const float4*>(f.proj)[i];
+#pragma unroll
+        for (int r = 0; r < kPer; ++r)
+            pv[r] = reinterpret_cast<const float4*>(f.proj)[threadIdx.x + 256 * r];
+    }
+    EntryIn in;
+    if (w < f.n_ent) in = load_fp4_entry(f.k, f.v, w, f.ratio, f.rope_cs, f.dst_rows, lane);
+    if (stage) {
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+            const int i = threadIdx.x + 256 * r;
             float* d = proj_l + (i / (kHeadDim / 4)) * kProjPitch + 4 * (i % (kHeadDim / 4));
-            d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+            d[0] = pv[r].x; d[1] = pv[r].y; d[2] = pv[r].z; d[3] = pv[r].w;
         }
         __syncthreads();
     }
     if (w < f.n_ent) {
-        quant_fp4_entry(f.k, f.v, w, f.ratio, f.rope_cs, f.dst_rows, f.codes, f.scales, lane,
+        quant_fp4_entry(in, f.ratio, f.rope_cs != nullptr, f.codes, f.scales, lane,
                         stage ? proj_l : nullptr, f.ik_codes, f.ik_sigma, f.ik_scales4);
         return;
     }
@@ -240,13 +276,14 @@ __global__ __launch_bounds__(256) void k_prep_iq(const float* __restrict__ iq,
     const int64_t bq = blockIdx.x;
     if (bq >= n_q) return;
     const float x = iq[(bq * kIdxHeads + h) * kIdxDim + lane];
+    const float wh = iw[bq * kIdxHeads + h];  // loaded with the query, not after it
     const float amax = wave_max_f32(fabsf(x));
     const float sq = amax / 448.0f;
     const uint32_t c = (sq == 0.0f) ? ((__float_as_uint(x) >> 24) & 0x80u) : e4m3_encode(x / sq);
     const float v = e4m3_decode_bits(c);
     qd[(bq * kIdxHeads + h) * kIdxDim + lane] = v;
     if (qh != nullptr) qh[(bq * kIdxHeads + h) * kIdxDim + lane] = (_Float16)v;  // exact
-    const float w = iw[bq * kIdxHeads + h] * sq;
+    const float w = wh * sq;
     if (lane == 0) wq[bq * kIdxHeads + h] = w;
     if (cq != nullptr) {
         // guard-band constant of the MFMA scan (csa2_chunk.hip):
