@@ -23,6 +23,8 @@
 // wave-wide load a contiguous 1 KB: lane i reads its position's 16 bytes.
 #include <hip/hip_ext.h>
 
+#include <utility>
+
 #include "csa2_device.hpp"
 #include "csa2_internal.hpp"
 
@@ -31,10 +33,7 @@ namespace csa2 {
 // Score of one indexer-K row from its four 16-byte channel groups.
 // qd: the query's decoded E4M3 values [4][64] (uniform across the wave, read
 // through the scalar cache); wq: the 4 folded head weights.
-__device__ __forceinline__ float score_row(const uint4 (&raw)[4], float sigma,
-                                           const float* __restrict__ qd,
-                                           const float* __restrict__ wq) {
-    float kf[kIdxDim];
+__device__ __forceinline__ void decode_fp8_row(const uint4 (&raw)[4], float (&kf)[kIdxDim]) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         const uint32_t w[4] = {raw[g].x, raw[g].y, raw[g].z, raw[g].w};
@@ -48,6 +47,13 @@ __device__ __forceinline__ float score_row(const uint4 (&raw)[4], float sigma,
             kf[16 * g + 4 * i + 3] = hi.y;
         }
     }
+}
+
+__device__ __forceinline__ float score_row(const uint4 (&raw)[4], float sigma,
+                                           const float* __restrict__ qd,
+                                           const float* __restrict__ wq) {
+    float kf[kIdxDim];
+    decode_fp8_row(raw, kf);
     float t = 0.0f;
 #pragma unroll
     for (int h = 0; h < kIdxHeads; ++h) {
@@ -75,10 +81,7 @@ __device__ __forceinline__ void load_ik_row(const uint8_t* __restrict__ ikc, int
 //              E4M3(q_hc) * E2M1(k_c) (each product exact), from +0;
 //   dot_h    = fused multiply-add chain over g = 0..3 of scale_g * inner_hg;
 //   r_h, t as for the FP8 key; score = t.
-__device__ __forceinline__ float score_row4(const uint4 (&raw)[2], uint32_t sc4,
-                                            const float* __restrict__ qd,
-                                            const float* __restrict__ wq) {
-    float kf[kIdxDim];  // E2M1 values, unscaled
+__device__ __forceinline__ void decode_fp4_row(const uint4 (&raw)[2], float (&kf)[kIdxDim]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const uint32_t w[4] = {raw[h].x, raw[h].y, raw[h].z, raw[h].w};
@@ -94,6 +97,13 @@ __device__ __forceinline__ float score_row4(const uint4 (&raw)[2], uint32_t sc4,
             o[4] = v2[0]; o[5] = v2[1]; o[6] = v3[0]; o[7] = v3[1];
         }
     }
+}
+
+__device__ __forceinline__ float score_row4(const uint4 (&raw)[2], uint32_t sc4,
+                                            const float* __restrict__ qd,
+                                            const float* __restrict__ wq) {
+    float kf[kIdxDim];  // E2M1 values, unscaled
+    decode_fp4_row(raw, kf);
     const float2 s01 = e4m3x2_to_f32<false>(sc4);
     const float2 s23 = e4m3x2_to_f32<true>(sc4);
     const float sg[4] = {s01.x, s01.y, s23.x, s23.y};
@@ -114,6 +124,99 @@ __device__ __forceinline__ float score_row4(const uint4 (&raw)[2], uint32_t sc4,
         t = (h == 0) ? wr : t + wr;
     }
     return t;
+}
+
+// ---------------------------------------------------------------------------
+// The same scores with the query held in registers instead of read through
+// the scalar cache at every step.  Lane l holds q_h[4 (l % 16) + r] in
+// v[h][r], so channel c of head h sits in register c % 4 of lane c / 4 of
+// every 16-lane row, and a DPP row_newbcast operand hands it to all lanes
+// inside the multiply-add itself (v_fmac_f32_dpp: acc + q * k, one rounding,
+// the fmaf of the scalar versions).  The operations and their order are
+// those of score_row and score_row4.  DPP reads other lanes: these run with
+// every lane of the wave active.
+// ---------------------------------------------------------------------------
+struct QQuad {
+    float v[kIdxHeads][4];
+    // q: one query's decoded values [4][64], in global memory or LDS
+    __device__ __forceinline__ void load(const float* q) {
+#pragma unroll
+        for (int h = 0; h < kIdxHeads; ++h) {
+            const float4 x = reinterpret_cast<const float4*>(q + h * kIdxDim)[threadIdx.x & 15];
+            v[h][0] = x.x; v[h][1] = x.y; v[h][2] = x.z; v[h][3] = x.w;
+        }
+    }
+};
+
+// acc + (q of lane N of this 16-lane row) * k.  Volatile, so that the
+// compiler keeps it where the whole wave is active.
+template <int N>
+__device__ __forceinline__ float fmac_bcast(float acc, float q, float k) {
+    asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                 : "+v"(acc) : "v"(q), "v"(k), "i"(N));
+    return acc;
+}
+
+// channel C of every head: acc[h] += q_hC * k
+template <int C>
+__device__ __forceinline__ void fmac_heads(float (&acc)[kIdxHeads], const QQuad& q, float k) {
+#pragma unroll
+    for (int h = 0; h < kIdxHeads; ++h) acc[h] = fmac_bcast<(C >> 2)>(acc[h], q.v[h][C & 3], k);
+}
+
+template <int... C>
+__device__ __forceinline__ void fp8_dots(float (&dot)[kIdxHeads], const QQuad& q,
+                                         const float (&kf)[kIdxDim],
+                                         std::integer_sequence<int, C...>) {
+    (fmac_heads<C>(dot, q, kf[C]), ...);
+}
+
+// channels 16g .. 16g + 15 of group g = G: the group sums, then the scaled
+// add into each head's dot
+template <int G, int... J>
+__device__ __forceinline__ void fp4_group(float (&dot)[kIdxHeads], const QQuad& q,
+                                          const float (&kf)[kIdxDim], float sg,
+                                          std::integer_sequence<int, J...>) {
+    float inner[kIdxHeads] = {0.0f, 0.0f, 0.0f, 0.0f};
+    (fmac_heads<16 * G + J>(inner, q, kf[16 * G + J]), ...);
+#pragma unroll
+    for (int h = 0; h < kIdxHeads; ++h) dot[h] = fmaf(sg, inner[h], dot[h]);
+}
+
+__device__ __forceinline__ float weigh_heads(const float (&dot)[kIdxHeads],
+                                             const float* __restrict__ wq) {
+    float t = 0.0f;
+#pragma unroll
+    for (int h = 0; h < kIdxHeads; ++h) {
+        const float r = dot[h] > 0.0f ? dot[h] : 0.0f;
+        const float wr = wq[h] * r;
+        t = (h == 0) ? wr : t + wr;
+    }
+    return t;
+}
+
+__device__ __forceinline__ float score_row_q(const uint4 (&raw)[4], float sigma, const QQuad& q,
+                                             const float* __restrict__ wq) {
+    float kf[kIdxDim];
+    decode_fp8_row(raw, kf);
+    float dot[kIdxHeads] = {0.0f, 0.0f, 0.0f, 0.0f};
+    fp8_dots(dot, q, kf, std::make_integer_sequence<int, kIdxDim>{});
+    return sigma * weigh_heads(dot, wq);
+}
+
+__device__ __forceinline__ float score_row4_q(const uint4 (&raw)[2], uint32_t sc4, const QQuad& q,
+                                              const float* __restrict__ wq) {
+    float kf[kIdxDim];
+    decode_fp4_row(raw, kf);
+    const float2 s01 = e4m3x2_to_f32<false>(sc4);
+    const float2 s23 = e4m3x2_to_f32<true>(sc4);
+    float dot[kIdxHeads] = {0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr auto kG = std::make_integer_sequence<int, 16>{};
+    fp4_group<0>(dot, q, kf, s01.x, kG);
+    fp4_group<1>(dot, q, kf, s01.y, kG);
+    fp4_group<2>(dot, q, kf, s23.x, kG);
+    fp4_group<3>(dot, q, kf, s23.y, kG);
+    return weigh_heads(dot, wq);
 }
 
 // One position's key in either format: FP8 (codes in the 4-plane tiles, fp32
@@ -138,6 +241,11 @@ struct IdxRow {
                                            const float* __restrict__ wq) const {
         if constexpr (FMT == 0) return score_row(raw, __uint_as_float(aux), qd, wq);
         else return score_row4(raw, aux, qd, wq);
+    }
+    // the same score, query in registers (whole wave active)
+    __device__ __forceinline__ float score(const QQuad& q, const float* __restrict__ wq) const {
+        if constexpr (FMT == 0) return score_row_q(raw, __uint_as_float(aux), q, wq);
+        else return score_row4_q(raw, aux, q, wq);
     }
 };
 
@@ -170,7 +278,8 @@ __device__ __forceinline__ void scan_query_exact(const uint8_t* __restrict__ ikc
 }
 
 // ---------------------------------------------------------------------------
-// Full-layer scan.  grid = (ceil(cap / 256), B); 256 threads, one position each.
+// Full-layer scan.  grid = (ceil(cap / 256), B); 256 threads, one position each,
+// the query held in registers (QQuad).
 // For every query of the sequence: key of each position, the max key of each
 // 8-position block (DPP max over 8 adjacent lanes) and, when sbkeys is set,
 // of each 64-position superblock (one wave).  Tiles that no query of the
@@ -197,6 +306,10 @@ __global__ __launch_bounds__(256) void k_scan(const uint8_t* __restrict__ ikc,
     if (p0 + (threadIdx.x & ~63) >= cap) return;
 
     const int64_t row = (int64_t)b * cap + p;
+    // the first query's values (from L2, shared by every workgroup of the
+    // sequence), then the key row
+    QQuad qq;
+    qq.load(qd + (int64_t)b * Q * kIdxHeads * kIdxDim);
     IdxRow<FMT> r;
     r.load(ikc, iks, row);
     const int64_t nb = cap / kBlock;
@@ -204,7 +317,8 @@ __global__ __launch_bounds__(256) void k_scan(const uint8_t* __restrict__ ikc,
         const int64_t bq = (int64_t)b * Q + q;
         const int nv = clamp_nvis(n_vis[bq], cap);
         if (p0 >= nv) continue;  // uniform
-        const float s = r.score(qd + bq * kIdxHeads * kIdxDim, wq + bq * kIdxHeads);
+        if (q > 0) qq.load(qd + bq * kIdxHeads * kIdxDim);
+        const float s = r.score(qq, wq + bq * kIdxHeads);  // every lane of the wave is active
         const uint32_t key = (p < nv) ? score_key(s) : 0u;
         keys[bq * cap + p] = key;
         const uint32_t bk = max8_u32(key);
@@ -318,7 +432,7 @@ __global__ __launch_bounds__(256) void k_scan_multi(const uint8_t* __restrict__ 
 // The eight lanes of one block read 8 x 16 contiguous bytes per plane.
 // Each workgroup quantises its query itself (wave h: head h, E4M3 codes
 // decoded back to fp32 in LDS, w' = w * sq), while its row loads are in
-// flight; the score then reads q from LDS (broadcast reads).
+// flight; every lane then takes its quad of q values from LDS into registers.
 // ---------------------------------------------------------------------------
 template <int FMT>
 __global__ __launch_bounds__(256) void k_pool_score(const uint8_t* __restrict__ ikc,
@@ -355,10 +469,11 @@ __global__ __launch_bounds__(256) void k_pool_score(const uint8_t* __restrict__ 
         if (lane == 0) sw[h] = wh * sqh;
     }
     __syncthreads();
-    if (s >= n_slots) return;
-    uint32_t key = 0;
-    if (valid) key = score_key(r.score(sq, sw));
-    ckeys[bq * n_slots + s] = key;
+    // every lane scores (with the whole wave active), the absent ones are dropped
+    QQuad qq;
+    qq.load(sq);
+    const float sc = r.score(qq, sw);
+    if (s < n_slots) ckeys[bq * n_slots + s] = valid ? score_key(sc) : 0u;
 }
 
 // ---------------------------------------------------------------------------
