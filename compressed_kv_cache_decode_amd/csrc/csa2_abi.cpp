@@ -300,10 +300,10 @@ int index_full_valu(int fmt, const uint8_t* ikc, const float* iks, int64_t cap, 
     // so the position select only ever looks at P*8 candidates.  Without a
     // requested pool, P = K blocks are kept internally.
     const int P = pool_blocks > 0 ? pool_blocks : topk;
-    hipError_t e = launch_prep_iq(iq, iw, nq, qd, wq, stream);
-    if (e == hipSuccess)
-        e = launch_scan(ikc, iks, cap, B, Q, qd, wq, n_vis, keys, bkeys, stream, scan_start,
-                        scan_stop, sbkeys, fmt);
+    // the scan quantises the queries itself (with many FP8 queries a
+    // separate pass writes them to qd / wq first)
+    hipError_t e = launch_scan(ikc, iks, cap, B, Q, iq, iw, qd, wq, n_vis, keys, bkeys, stream,
+                               scan_start, scan_stop, sbkeys, fmt);
     if (e == hipSuccess)
         e = launch_select_full(keys, bkeys, cap, n_vis, nq, P, topk,
                                pool_blocks > 0 ? pool_idx : nullptr, topk_idx, stream, sbkeys);

@@ -140,6 +140,16 @@ __device__ __forceinline__ float wave_max_f32(float v) {
     return v;
 }
 
+// Indexer query of one head, lane = channel (a whole wave): sq = fl(amax /
+// 448), code = RNE_E4M3(fl(x / sq)) (a zero head keeps its signs as +-0
+// codes); returns the code's exact fp32 value.  The caller folds sq into the
+// head weight, w' = fl(w * sq).
+__device__ __forceinline__ float quantise_query_channel(float x, float& sq) {
+    sq = wave_max_f32(fabsf(x)) / 448.0f;
+    const uint32_t c = (sq == 0.0f) ? ((__float_as_uint(x) >> 24) & 0x80u) : e4m3_encode(x / sq);
+    return e4m3_decode_bits(c);
+}
+
 __device__ __forceinline__ float group8_max_f32(float v) {
     v = fmaxf(v, __shfl_xor(v, 1, 64));
     v = fmaxf(v, __shfl_xor(v, 2, 64));

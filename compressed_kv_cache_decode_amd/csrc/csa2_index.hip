@@ -278,8 +278,11 @@ __device__ __forceinline__ void scan_query_exact(const uint8_t* __restrict__ ikc
 }
 
 // ---------------------------------------------------------------------------
-// Full-layer scan.  grid = (ceil(cap / 256), B); 256 threads, one position each,
-// the query held in registers (QQuad).
+// Full-layer scan.  grid = (ceil(cap / 256), B); 256 threads, one position each.
+// Each workgroup quantises the query itself (wave h: head h, the E4M3 codes'
+// fp32 values and the folded weights w' = w * sq in LDS, as k_prep_iq
+// computes them) while its key rows are in flight, and every lane then holds
+// its quad of query values in registers (QQuad).
 // For every query of the sequence: key of each position, the max key of each
 // 8-position block (DPP max over 8 adjacent lanes) and, when sbkeys is set,
 // of each 64-position superblock (one wave).  Tiles that no query of the
@@ -287,38 +290,53 @@ __device__ __forceinline__ void scan_query_exact(const uint8_t* __restrict__ ikc
 // ---------------------------------------------------------------------------
 // FMT 0: FP8 keys (iks = fp32 sigma per row); FMT 1: FP4 keys (iks = the
 // rows' four E4M3 scale bytes, read as one 32-bit word per row).
+// iq [B*Q][4][64], iw [B*Q][4]: the queries and head weights as given.
 template <int FMT>
 __global__ __launch_bounds__(256) void k_scan(const uint8_t* __restrict__ ikc,
                                               const float* __restrict__ iks, int64_t cap, int Q,
-                                              const float* __restrict__ qd,
-                                              const float* __restrict__ wq,
+                                              const float* __restrict__ iq,
+                                              const float* __restrict__ iw,
                                               const int32_t* __restrict__ n_vis,
                                               uint32_t* __restrict__ keys,
                                               uint32_t* __restrict__ bkeys,
                                               uint32_t* __restrict__ sbkeys) {
+    __shared__ __attribute__((aligned(16))) float sq[kIdxHeads * kIdxDim];
+    __shared__ float sw[kIdxHeads];
     const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
     const int64_t p0 = (int64_t)blockIdx.x * 256;
     const int64_t p = p0 + threadIdx.x;
     int nv_max = 0;
     for (int q = 0; q < Q; ++q) nv_max = max(nv_max, clamp_nvis(n_vis[(int64_t)b * Q + q], cap));
     if (p0 >= nv_max) return;  // uniform over the block
-    // cap is a multiple of 64, so a wave is either wholly inside or wholly past it
-    if (p0 + (threadIdx.x & ~63) >= cap) return;
+    // cap is a multiple of 64, so a wave is either wholly inside or wholly
+    // past it; a wave past it takes part in the query set-up only
+    const bool live = p0 + (threadIdx.x & ~63) < cap;
 
-    const int64_t row = (int64_t)b * cap + p;
-    // the first query's values (from L2, shared by every workgroup of the
-    // sequence), then the key row
-    QQuad qq;
-    qq.load(qd + (int64_t)b * Q * kIdxHeads * kIdxDim);
+    // loads complete in issue order: the first query's channel and weight
+    // (from L2), then the key row
+    float x = iq[((int64_t)b * Q * kIdxHeads + h) * kIdxDim + lane];
+    float wh = iw[(int64_t)b * Q * kIdxHeads + h];
     IdxRow<FMT> r;
-    r.load(ikc, iks, row);
+    if (live) r.load(ikc, iks, (int64_t)b * cap + p);
     const int64_t nb = cap / kBlock;
     for (int q = 0; q < Q; ++q) {
         const int64_t bq = (int64_t)b * Q + q;
         const int nv = clamp_nvis(n_vis[bq], cap);
-        if (p0 >= nv) continue;  // uniform
-        if (q > 0) qq.load(qd + bq * kIdxHeads * kIdxDim);
-        const float s = r.score(qq, wq + bq * kIdxHeads);  // every lane of the wave is active
+        if (p0 >= nv) continue;  // uniform over the block
+        if (q > 0) {
+            x = iq[(bq * kIdxHeads + h) * kIdxDim + lane];
+            wh = iw[bq * kIdxHeads + h];
+            __syncthreads();  // the previous query's readers are done
+        }
+        float sqh;
+        sq[h * kIdxDim + lane] = quantise_query_channel(x, sqh);
+        if (lane == 0) sw[h] = wh * sqh;
+        __syncthreads();
+        if (!live) continue;  // uniform over the wave
+        QQuad qq;
+        qq.load(sq);
+        const float s = r.score(qq, sw);  // every lane of the wave is active
         const uint32_t key = (p < nv) ? score_key(s) : 0u;
         keys[bq * cap + p] = key;
         const uint32_t bk = max8_u32(key);
@@ -463,9 +481,8 @@ __global__ __launch_bounds__(256) void k_pool_score(const uint8_t* __restrict__ 
     IdxRow<FMT> r;
     r.load(ikc, iks, b * cap + (valid ? pos : 0));
     {   // the query's E4M3 codes (exact fp32 values) and folded weights
-        const float sqh = wave_max_f32(fabsf(x)) / 448.0f;
-        const uint32_t c = (sqh == 0.0f) ? ((__float_as_uint(x) >> 24) & 0x80u) : e4m3_encode(x / sqh);
-        sq[h * kIdxDim + lane] = e4m3_decode_bits(c);
+        float sqh;
+        sq[h * kIdxDim + lane] = quantise_query_channel(x, sqh);
         if (lane == 0) sw[h] = wh * sqh;
     }
     __syncthreads();
@@ -1491,20 +1508,27 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select_pool(
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
-                       const float* qd, const float* wq, const int32_t* n_vis, uint32_t* keys,
-                       uint32_t* bkeys, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
-                       uint32_t* sbkeys, int fmt) {
+                       const float* iq, const float* iw, float* qd, float* wq,
+                       const int32_t* n_vis, uint32_t* keys, uint32_t* bkeys, hipStream_t stream,
+                       hipEvent_t start, hipEvent_t stop, uint32_t* sbkeys, int fmt) {
     dim3 grid((unsigned)((cap + 255) / 256), (unsigned)B);
-    // a few queries per sequence: k_scan reads them through the scalar cache;
-    // many (the replay chunk): k_scan_multi stages them in LDS
-    // FP4 keys: k_scan for any Q
-    auto kern = fmt == 1 ? k_scan<1> : (Q >= 4 ? k_scan_multi : k_scan<0>);
+    // a few queries per sequence (FP4 keys: any number): k_scan quantises
+    // them itself; many (the replay chunk, FP8 keys): k_prep_iq writes them
+    // to qd / wq once and k_scan_multi stages them in LDS
+    const bool multi = fmt == 0 && Q >= 4;
+    if (multi) {
+        const hipError_t e = launch_prep_iq(iq, iw, (int64_t)B * Q, qd, wq, stream);
+        if (e != hipSuccess) return e;
+    }
+    auto kern = fmt == 1 ? k_scan<1> : (multi ? k_scan_multi : k_scan<0>);
+    const float* qa = multi ? qd : iq;
+    const float* wa = multi ? wq : iw;
     if (start != nullptr && stop != nullptr) {
         // the runtime records `start` / `stop` immediately around this dispatch
         hipExtLaunchKernelGGL(kern, grid, dim3(256), 0, stream, start, stop, 0, ikc, iks, cap, Q,
-                              qd, wq, n_vis, keys, bkeys, sbkeys);
+                              qa, wa, n_vis, keys, bkeys, sbkeys);
     } else {
-        hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, ikc, iks, cap, Q, qd, wq, n_vis,
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, ikc, iks, cap, Q, qa, wa, n_vis,
                            keys, bkeys, sbkeys);
     }
     return hipGetLastError();

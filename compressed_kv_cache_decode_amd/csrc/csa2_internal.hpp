@@ -63,9 +63,10 @@ constexpr int kIdxFp4 = 1;
 // sbkeys (may be null): also the max key per superblock of kSuper positions
 constexpr int kSuper = 64;
 hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
-                       const float* qd, const float* wq, const int32_t* n_vis, uint32_t* keys,
-                       uint32_t* bkeys, hipStream_t stream, hipEvent_t start = nullptr,
-                       hipEvent_t stop = nullptr, uint32_t* sbkeys = nullptr, int fmt = kIdxFp8);
+                       const float* iq, const float* iw, float* qd, float* wq,
+                       const int32_t* n_vis, uint32_t* keys, uint32_t* bkeys, hipStream_t stream,
+                       hipEvent_t start = nullptr, hipEvent_t stop = nullptr,
+                       uint32_t* sbkeys = nullptr, int fmt = kIdxFp8);
 // MFMA scan of a multi-query chunk with guard-band bounds (csa2_chunk.hip):
 // the largest lower-bound score key per block of 8 positions [nq][cap / 8]
 // and the upper-bound key per half-block of 4 [nq][cap / 4]

@@ -277,10 +277,8 @@ __global__ __launch_bounds__(256) void k_prep_iq(const float* __restrict__ iq,
     if (bq >= n_q) return;
     const float x = iq[(bq * kIdxHeads + h) * kIdxDim + lane];
     const float wh = iw[bq * kIdxHeads + h];  // loaded with the query, not after it
-    const float amax = wave_max_f32(fabsf(x));
-    const float sq = amax / 448.0f;
-    const uint32_t c = (sq == 0.0f) ? ((__float_as_uint(x) >> 24) & 0x80u) : e4m3_encode(x / sq);
-    const float v = e4m3_decode_bits(c);
+    float sq;
+    const float v = quantise_query_channel(x, sq);
     qd[(bq * kIdxHeads + h) * kIdxDim + lane] = v;
     if (qh != nullptr) qh[(bq * kIdxHeads + h) * kIdxDim + lane] = (_Float16)v;  // exact
     const float w = wh * sq;
