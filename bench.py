@@ -951,6 +951,58 @@ def measure_ceilings(mib=1024, reps=10):
     return out
 
 
+def measure_read_at(nbytes, copies=3, reps=12):
+    """The streaming-read ceiling at one transfer size: csa2_stream_probe
+    reading `nbytes` (rounded up to 16) from one of `copies` buffers in turn
+    (together larger than the last-level cache, so reads come from HBM),
+    each launch timed alone with events; the best of one load per thread and
+    grid-stride 2048-8192 workgroups, median over `reps` launches.  A small
+    transfer does not reach the large-transfer ceiling (ramp-up and tail), so
+    a kernel moving that many bytes is compared with this."""
+    import statistics
+
+    import torch
+
+    import compressed_kv_cache_decode_amd as csa2
+    n = (nbytes + 15) // 16 * 16
+    bufs = [torch.ones(n, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    best = (0.0, "")
+    for mode, blocks in ((2, 1), (0, 2048), (0, 4096), (0, 8192)):
+        for b in bufs:
+            csa2.stream_probe(mode, b, n_blocks=blocks)
+        torch.cuda.synchronize()
+        us = []
+        for i in range(reps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+            csa2.stream_probe(mode, bufs[i % copies], n_blocks=blocks)
+            ev[1].record()
+            torch.cuda.synchronize()
+            us.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        gbs = n / statistics.median(us) / 1e3
+        if gbs > best[0]:
+            best = (gbs, "one load per thread" if mode == 2 else f"{blocks} workgroups")
+    del bufs
+    torch.cuda.empty_cache()
+    return {"bytes": n, "read_GBps": round(best[0], 1),
+            "how": f"csa2_stream_probe reading {n} bytes from one of {copies} buffers in turn, "
+                   f"each launch timed alone, median of {reps} ({best[1]})"}
+
+
+def with_same_size_read(entry, cache):
+    """A scan entry with the read ceiling at its own bytes per launch."""
+    if not entry["kernel"].startswith("k_scan"):
+        return entry
+    n = entry["bytes_per_launch"]
+    if n not in cache:
+        cache[n] = measure_read_at(n)
+        log(f"read ceiling at {n} bytes: {cache[n]['read_GBps']} GB/s")
+    e = dict(entry)
+    e["read_same_bytes_GBps"] = cache[n]["read_GBps"]
+    e["frac_of_read_same_bytes"] = round(e["achieved"] / cache[n]["read_GBps"], 4)
+    return e
+
+
 def with_ceilings(entry, ceil):
     """A roofline entry with its fraction of the measured copy and read ceilings."""
     e = dict(entry)
@@ -1089,7 +1141,9 @@ def extras(args, result):
     from compressed_kv_cache_decode_amd import synth
     ceil = measure_ceilings()
     result["ceilings"] = ceil
-    result["rooflines"] = [with_ceilings(r, ceil) for r in result["rooflines"]]
+    same = {}
+    result["rooflines"] = [with_same_size_read(with_ceilings(r, ceil), same)
+                           for r in result["rooflines"]]
     for B, pt in zip((256, 1024), attn_sweep_points([256, 1024], 30)):
         result["rooflines"].append(with_ceilings({
             "kernel": f"k_attn (sparse attention, gathering, batch {B}, 64 heads, top-512 + "
@@ -1108,8 +1162,9 @@ def extras(args, result):
     result["secondary"] = {
         "decoder_stack_1m": {k: r1m[k] for k in ("value", "unit", "ms_per_step", "steps",
                                                   "warmup", "config", "step", "index")}}
-    result["secondary"]["decoder_stack_1m"]["rooflines"] = [with_ceilings(r, ceil)
-                                                             for r in r1m["rooflines"]]
+    result["secondary"]["decoder_stack_1m"]["rooflines"] = [
+        with_same_size_read(with_ceilings(r, ceil), same) for r in r1m["rooflines"]]
+    result["ceilings"]["read_at_scan_bytes"] = [same[n] for n in sorted(same)]
 
 
 if __name__ == "__main__":
