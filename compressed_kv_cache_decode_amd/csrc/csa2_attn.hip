@@ -220,6 +220,17 @@ __device__ __forceinline__ float vmax(float a, float b) { return __builtin_eleme
 
 // max / sum over the four lanes c, c+16, c+32, c+48 (v_permlane*_swap: each
 // call hands every lane its partner's value 32 resp. 16 lanes away)
+// max over each half wave (lanes 0..31, 32..63; every lane active), in every
+// lane: DPP within each 16-lane row, then the row pair through a lane swap
+__device__ __forceinline__ float half_wave_max(float v) {
+    v = fmaxf(v, dppf<0xB1>(v));
+    v = fmaxf(v, dppf<0x4E>(v));
+    v = fmaxf(v, dppf<0x141>(v));
+    v = fmaxf(v, dppf<0x140>(v));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ float xmax4(float v) {
     auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     v = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
@@ -617,8 +628,7 @@ __global__ __launch_bounds__(kWaves * 64, kWaves == kWavesNarrow ? 3 : 2) void k
             const float x[4] = {xq[i].x * logit_mul, xq[i].y * logit_mul, xq[i].z * logit_mul,
                                 xq[i].w * logit_mul};
             float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
-#pragma unroll
-            for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+            amax = half_wave_max(amax);
             int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 0;  // amax in [2^(e-1), 2^e)
             e = e < -100 ? -100 : (e > 100 ? 100 : e);
             const int head = wave * kHPW + 2 * i + (lane >> 5);
@@ -1021,8 +1031,7 @@ __global__ __launch_bounds__(kPairWaves * 64, 2) void k_attn_pair(AttnArgs a, in
             const float x[4] = {xq[i].x * logit_mul, xq[i].y * logit_mul, xq[i].z * logit_mul,
                                 xq[i].w * logit_mul};
             float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
-#pragma unroll
-            for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+            amax = half_wave_max(amax);
             int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 0;
             e = e < -100 ? -100 : (e > 100 ? 100 : e);
             const int head = wave * kHPW + 2 * i + (lane >> 5);

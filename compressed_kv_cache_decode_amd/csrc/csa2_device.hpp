@@ -110,7 +110,7 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 // ---------------------------------------------------------------------------
 // Cross-lane helpers (wave64).  DPP controls: quad_perm [1,0,3,2] = 0xB1,
 // quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141 (lane i <-> 7-i within
-// each group of 8).
+// each group of 8), row_mirror = 0x140 (lane i <-> 15-i within each row of 16).
 // ---------------------------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
@@ -134,10 +134,24 @@ __device__ __forceinline__ uint32_t wave_max_of_groups8(uint32_t g8) {
     return m;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+    return __uint_as_float(dpp<CTRL>(__float_as_uint(v)));
+}
+
+// max over the wave (every lane active): DPP within each 16-lane row
+// (quad_perm, row_half_mirror, row_mirror = 0x140), then the four rows'
+// results read as scalars; the result is the same in every lane
 __device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+    v = fmaxf(v, dppf<0xB1>(v));
+    v = fmaxf(v, dppf<0x4E>(v));
+    v = fmaxf(v, dppf<0x141>(v));
+    v = fmaxf(v, dppf<0x140>(v));
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 // Indexer query of one head, lane = channel (a whole wave): sq = fl(amax /
@@ -150,10 +164,12 @@ __device__ __forceinline__ float quantise_query_channel(float x, float& sq) {
     return e4m3_decode_bits(c);
 }
 
+// max over each aligned group of 8 lanes (every lane active), in every lane
+// of the group
 __device__ __forceinline__ float group8_max_f32(float v) {
-    v = fmaxf(v, __shfl_xor(v, 1, 64));
-    v = fmaxf(v, __shfl_xor(v, 2, 64));
-    v = fmaxf(v, __shfl_xor(v, 4, 64));
+    v = fmaxf(v, dppf<0xB1>(v));
+    v = fmaxf(v, dppf<0x4E>(v));
+    v = fmaxf(v, dppf<0x141>(v));
     return v;
 }
 

@@ -73,12 +73,12 @@ __device__ __forceinline__ void quant_fp8_vals(const float* xv, int per, int lay
 __device__ __forceinline__ void quant_idx4_val(float x, int64_t row, uint8_t* __restrict__ codes,
                                                uint8_t* __restrict__ scales, int lane) {
     float amax = fabsf(x);
-    amax = fmaxf(amax, __shfl_xor(amax, 8, 64));
+    amax = fmaxf(amax, dppf<0x128>(amax));  // row_ror:8, the other half of the 16-lane group
     amax = group8_max_f32(amax);
     const uint32_t sc = e4m3_encode(amax / 6.0f);
     const float sd = e4m3_decode_bits(sc);
     const uint32_t code = (sd == 0.0f) ? ((__float_as_uint(x) >> 28) & 8u) : e2m1_encode(x / sd);
-    const uint32_t odd = __shfl_xor(code, 1, 64);
+    const uint32_t odd = dpp<0xB1>(code);  // the neighbouring lane's code
     if ((lane & 1) == 0)
         codes[ik4_offset(row, lane >> 5) + ((lane & 31) >> 1)] = (uint8_t)(code | (odd << 4));
     if ((lane & 15) == 0) scales[row * 4 + (lane >> 4)] = (uint8_t)sc;
