@@ -24,7 +24,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct IndexLayout {
-    size_t qd, wq, keys, bkeys, sbkeys, total;
+    size_t qd, wq, keys, bkeys, sbkeys, parts, total;
     // MFMA chunk path only
     size_t cq, qh, hkeys_hi;
 };
@@ -58,12 +58,14 @@ IndexLayout full_layout(int B, int Q, int64_t cap, int topk, int pool_blocks) {
     return L;
 }
 
-// workspace of csa2_index_reindex: pool keys
+// workspace of csa2_index_reindex: pool keys, and a 16-byte summary per 64
+// of them
 IndexLayout reindex_layout(int B, int Q, int pool_blocks) {
     IndexLayout L{};
     const size_t nq = (size_t)B * Q;
     size_t off = 0;
     L.keys = off; off += align_up(nq * (size_t)pool_blocks * 8 * sizeof(uint32_t));
+    L.parts = off; off += align_up(nq * (size_t)((pool_blocks * 8 + 63) / 64) * 16);
     L.total = off;
     return L;
 }
@@ -460,12 +462,13 @@ __attribute__((visibility("default"))) int csa2_index_reindex(
     if (!ws || ws_bytes < L.total) return CSA2_E_WORKSPACE;
     char* w = static_cast<char*>(ws);
     uint32_t* ckeys = reinterpret_cast<uint32_t*>(w + L.keys);
+    uint4* parts = reinterpret_cast<uint4*>(w + L.parts);
     const int64_t nq = (int64_t)B * Q;
     hipError_t e = launch_pool_score(ik_codes, ik_sigma, cap, B, Q, iq, iw, n_vis, pool_idx,
-                                     pool_blocks, ckeys, stream);
+                                     pool_blocks, ckeys, parts, stream);
     if (e == hipSuccess)
-        e = launch_select_pool(ckeys, pool_idx, pool_blocks, n_vis, cap, nq, topk, topk_idx,
-                               stream);
+        e = launch_select_pool(ckeys, parts, pool_idx, pool_blocks, n_vis, cap, nq, topk,
+                               topk_idx, stream);
     return hip_status(e);
 }
 
@@ -537,12 +540,13 @@ __attribute__((visibility("default"))) int csa2_index_reindex_fp4(
     const IndexLayout L = reindex_layout(B, Q, pool_blocks);
     if (!ws || ws_bytes < L.total) return CSA2_E_WORKSPACE;
     uint32_t* ckeys = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + L.keys);
+    uint4* parts = reinterpret_cast<uint4*>(static_cast<char*>(ws) + L.parts);
     hipError_t e = launch_pool_score(ik4_codes, reinterpret_cast<const float*>(ik4_scales), cap,
-                                     B, Q, iq, iw, n_vis, pool_idx, pool_blocks, ckeys, stream,
-                                     kIdxFp4);
+                                     B, Q, iq, iw, n_vis, pool_idx, pool_blocks, ckeys, parts,
+                                     stream, kIdxFp4);
     if (e == hipSuccess)
-        e = launch_select_pool(ckeys, pool_idx, pool_blocks, n_vis, cap, (int64_t)B * Q, topk,
-                               topk_idx, stream);
+        e = launch_select_pool(ckeys, parts, pool_idx, pool_blocks, n_vis, cap, (int64_t)B * Q,
+                               topk, topk_idx, stream);
     return hip_status(e);
 }
 

@@ -444,6 +444,42 @@ __global__ __launch_bounds__(256) void k_scan_multi(const uint8_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// Wave-wide scans and reductions of uint32 values (whole wave active).
+// ---------------------------------------------------------------------------
+// inclusive prefix sum over the 64 lanes (DPP row shifts, then row broadcasts)
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false); // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false); // row_bcast:31
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(v), 63);
+}
+
+template <class OP>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, OP op) {
+    v = op(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = op(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = op(v, dpp<0x141>(v));  // row_half_mirror
+    v = op(v, dpp<0x140>(v));  // row_mirror
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return op(op(r0, r1), op(r2, r3));
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+// ---------------------------------------------------------------------------
 // Reindex: score the positions of the pool blocks with the layer's own query.
 // grid = (ceil(P*8 / 256), B*Q), 256 threads.  Slot s of query bq is position
 // pool[j]*8 + (s & 7) with j = s / 8; invisible or empty slots get key 0.
@@ -451,6 +487,9 @@ __global__ __launch_bounds__(256) void k_scan_multi(const uint8_t* __restrict__ 
 // Each workgroup quantises its query itself (wave h: head h, E4M3 codes
 // decoded back to fp32 in LDS, w' = w * sq), while its row loads are in
 // flight; every lane then takes its quad of q values from LDS into registers.
+// With `parts`, each wave also writes a summary of its 64 keys for the
+// selection that follows: the largest key of each of its four groups of 16
+// slots (0: none visible) at parts[bq * nw + s / 64], nw = ceil(P*8 / 64).
 // ---------------------------------------------------------------------------
 template <int FMT>
 __global__ __launch_bounds__(256) void k_pool_score(const uint8_t* __restrict__ ikc,
@@ -459,7 +498,8 @@ __global__ __launch_bounds__(256) void k_pool_score(const uint8_t* __restrict__ 
                                                     const float* __restrict__ iw,
                                                     const int32_t* __restrict__ n_vis,
                                                     const int32_t* __restrict__ pool, int P,
-                                                    uint32_t* __restrict__ ckeys) {
+                                                    uint32_t* __restrict__ ckeys,
+                                                    uint4* __restrict__ parts) {
     __shared__ __attribute__((aligned(16))) float sq[kIdxHeads * kIdxDim];
     __shared__ float sw[kIdxHeads];
     const int64_t bq = blockIdx.y;
@@ -490,7 +530,17 @@ __global__ __launch_bounds__(256) void k_pool_score(const uint8_t* __restrict__ 
     QQuad qq;
     qq.load(sq);
     const float sc = r.score(qq, sw);
-    if (s < n_slots) ckeys[bq * n_slots + s] = valid ? score_key(sc) : 0u;
+    const uint32_t key = valid ? score_key(sc) : 0u;
+    if (s < n_slots) ckeys[bq * n_slots + s] = key;
+    if (parts != nullptr) {  // every lane of a 16-lane row ends with the row's maximum
+        uint32_t m = max(key, dpp<0xB1>(key));
+        m = max(m, dpp<0x4E>(m));
+        m = max(m, dpp<0x141>(m));
+        m = max(m, dpp<0x140>(m));
+        const int64_t nw = (n_slots + 63) / 64, wv = (int64_t)blockIdx.x * 4 + h;
+        if ((lane & 15) == 0 && wv < nw)
+            reinterpret_cast<uint32_t*>(parts)[(bq * nw + wv) * 4 + (lane >> 4)] = m;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -606,6 +656,12 @@ struct Threshold {
     uint32_t t_eq;   // plus the first `quota` keys equal to t_eq
     uint32_t quota;
     uint32_t total;  // number taken
+};
+
+// What a selection may know of its keys beforehand: at least K non-zero keys
+// lie at or above lo and none lies above hi.  lo == 0: nothing is known.
+struct KeyBound {
+    uint32_t lo, hi;
 };
 
 template <bool REG>
@@ -746,39 +802,6 @@ __device__ __forceinline__ void compact(const KeySrc& ks, const uint32_t* reg, c
 // ---------------------------------------------------------------------------
 constexpr int kSelKpt = 16;
 
-// inclusive prefix sum over the 64 lanes (DPP row shifts, then row broadcasts)
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false); // row_bcast:15
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false); // row_bcast:31
-    return v;
-}
-
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(v), 63);
-}
-
-template <class OP>
-__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, OP op) {
-    v = op(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
-    v = op(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
-    v = op(v, dpp<0x141>(v));  // row_half_mirror
-    v = op(v, dpp<0x140>(v));  // row_mirror
-    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
-    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
-    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
-    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
-    return op(op(r0, r1), op(r2, r3));
-}
-
-__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-}
-
 // One counter per bin.  (Spreading a bin over four counters picked by lane,
 // so that lanes of one atomic instruction landing in one bin hit different
 // words, cost more in clearing and summing than it saved: 25.2 against
@@ -786,7 +809,7 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 struct SelRegShared {
     alignas(16) uint32_t hist[kSelBins];
     alignas(16) uint32_t part[5][kSelWaves];
-    uint32_t pick[3];
+    uint32_t pick[4];
 };
 static_assert(sizeof(SelRegShared) <= sizeof(SelShared::hist), "register state fits the histogram area");
 
@@ -795,16 +818,19 @@ static_assert(sizeof(SelRegShared) <= sizeof(SelShared::hist), "register state f
 // lowest bin are not counted: the caller knows in_range, the number of values
 // in [lo, hi], so that bin's count is in_range minus the others), and the bin
 // that holds the remaining-th largest is picked: its index, the count above
-// it and its own count.
+// it and its own count.  With second != 0 (and skip_lowest false), the bin
+// that holds the second-th largest is picked as well (bin2; second <=
+// remaining, so it exists whenever the first does).
 struct BinPick {
-    uint32_t bin, before, in_bin;
+    uint32_t bin, before, in_bin, bin2;
     int shift;
 };
 
 template <int N>
 __device__ __forceinline__ BinPick hist_pick(const uint32_t (&v)[N], uint32_t lo, uint32_t hi,
                                              uint32_t remaining, bool skip_lowest,
-                                             uint32_t in_range, SelRegShared& sh) {
+                                             uint32_t in_range, SelRegShared& sh,
+                                             uint32_t second = 0u) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint32_t width = hi - lo;  // > 0
     const int bits = 32 - __clz((int)width);
@@ -846,8 +872,10 @@ __device__ __forceinline__ BinPick hist_pick(const uint32_t (&v)[N], uint32_t lo
         if (above + h0 >= remaining) { sh.pick[0] = (uint32_t)b0; sh.pick[1] = above; sh.pick[2] = h0; }
         else { sh.pick[0] = (uint32_t)b1; sh.pick[1] = above + h0; sh.pick[2] = h1; }
     }
+    if (second != 0u && above < second && above + mine >= second)
+        sh.pick[3] = above + h0 >= second ? (uint32_t)b0 : (uint32_t)b1;
     __syncthreads();
-    return BinPick{sh.pick[0], sh.pick[1], sh.pick[2], shift};
+    return BinPick{sh.pick[0], sh.pick[1], sh.pick[2], second != 0u ? sh.pick[3] : 0u, shift};
 }
 
 // The K-th largest of the workgroup's register keys (16 per thread), as the
@@ -858,55 +886,70 @@ __device__ __forceinline__ BinPick hist_pick(const uint32_t (&v)[N], uint32_t lo
 // largest group maximum has at least K group maxima, hence at least K keys, at
 // or above it, so the K-th largest key is at or above it, and the key passes
 // only count keys from there up (a few hundred instead of every key).
+// A caller that already holds such a bound (kb.lo != 0) skips the range and
+// group-maxima passes.  With second != 0 (second <= K) and `next`, the
+// group-maxima pass also yields a bound for the second-th largest key: the
+// lower edge of the bin holding the second-th largest group maximum, with
+// hi = kmax (next->lo == 0 when that pass did not run).
 __device__ __forceinline__ Threshold threshold_reg(const uint32_t (&k)[kSelKpt], int K,
-                                                   SelRegShared& sh) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t cnt = 0, kmin = 0xFFFFFFFFu, kmax = 0;
-    uint32_t gm[4];  // maxima of the four groups of four keys
+                                                   SelRegShared& sh, KeyBound kb = {0u, 0u},
+                                                   uint32_t second = 0u,
+                                                   KeyBound* next = nullptr) {
+    if (next != nullptr) *next = KeyBound{0u, 0u};
+    uint32_t lo = kb.lo, hi = kb.hi;
+    bool known = false;  // in_range is the count of keys in [lo, hi]
+    uint32_t in_range = 0;
+    if (kb.lo == 0u) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        uint32_t cnt = 0, kmin = 0xFFFFFFFFu, kmax = 0;
+        uint32_t gm[4];  // maxima of the four groups of four keys
 #pragma unroll
-    for (int j = 0; j < 4; ++j) gm[j] = max(max(k[4 * j], k[4 * j + 1]), max(k[4 * j + 2], k[4 * j + 3]));
+        for (int j = 0; j < 4; ++j) gm[j] = max(max(k[4 * j], k[4 * j + 1]), max(k[4 * j + 2], k[4 * j + 3]));
 #pragma unroll
-    for (int i = 0; i < kSelKpt; ++i) {
-        cnt += k[i] != 0;
-        kmin = k[i] ? min(kmin, k[i]) : kmin;
-    }
-    kmax = max(max(gm[0], gm[1]), max(gm[2], gm[3]));
-    uint32_t ngm1 = kmax != 0, ngm4 = (gm[0] != 0) + (gm[1] != 0) + (gm[2] != 0) + (gm[3] != 0);
-    cnt = wave_sum(cnt);
-    ngm1 = wave_sum(ngm1);
-    ngm4 = wave_sum(ngm4);
-    kmin = wave_reduce(kmin, [](uint32_t x, uint32_t y) { return min(x, y); });
-    kmax = wave_reduce(kmax, [](uint32_t x, uint32_t y) { return max(x, y); });
-    __syncthreads();  // earlier readers of part are done
-    if (lane == 0) {
-        sh.part[0][wave] = cnt; sh.part[1][wave] = kmin; sh.part[2][wave] = kmax;
-        sh.part[3][wave] = ngm1; sh.part[4][wave] = ngm4;
-    }
-    __syncthreads();
-    cnt = 0; kmin = 0xFFFFFFFFu; kmax = 0; ngm1 = 0; ngm4 = 0;
-#pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) {
-        cnt += sh.part[0][w];
-        kmin = min(kmin, sh.part[1][w]);
-        kmax = max(kmax, sh.part[2][w]);
-        ngm1 += sh.part[3][w];
-        ngm4 += sh.part[4][w];
-    }
-    if (cnt <= (uint32_t)K) return Threshold{1u, 0u, 0u, cnt};
-
-    uint32_t lo = kmin, hi = kmax;
-    bool known = true;  // in_range is the count of keys in [lo, hi]
-    uint32_t in_range = cnt;
-    if (kmax > kmin && (K <= 1024 ? ngm1 : ngm4) >= (uint32_t)K) {
-        BinPick bp;
-        if (K <= 1024) {
-            const uint32_t t1[1] = {max(max(gm[0], gm[1]), max(gm[2], gm[3]))};
-            bp = hist_pick(t1, lo, hi, (uint32_t)K, false, 0u, sh);
-        } else {
-            bp = hist_pick(gm, lo, hi, (uint32_t)K, false, 0u, sh);
+        for (int i = 0; i < kSelKpt; ++i) {
+            cnt += k[i] != 0;
+            kmin = k[i] ? min(kmin, k[i]) : kmin;
         }
-        lo = lo + (bp.bin << bp.shift);
-        known = lo == kmin;
+        kmax = max(max(gm[0], gm[1]), max(gm[2], gm[3]));
+        uint32_t ngm1 = kmax != 0, ngm4 = (gm[0] != 0) + (gm[1] != 0) + (gm[2] != 0) + (gm[3] != 0);
+        cnt = wave_sum(cnt);
+        ngm1 = wave_sum(ngm1);
+        ngm4 = wave_sum(ngm4);
+        kmin = wave_reduce(kmin, [](uint32_t x, uint32_t y) { return min(x, y); });
+        kmax = wave_reduce(kmax, [](uint32_t x, uint32_t y) { return max(x, y); });
+        __syncthreads();  // earlier readers of part are done
+        if (lane == 0) {
+            sh.part[0][wave] = cnt; sh.part[1][wave] = kmin; sh.part[2][wave] = kmax;
+            sh.part[3][wave] = ngm1; sh.part[4][wave] = ngm4;
+        }
+        __syncthreads();
+        cnt = 0; kmin = 0xFFFFFFFFu; kmax = 0; ngm1 = 0; ngm4 = 0;
+#pragma unroll
+        for (int w = 0; w < kSelWaves; ++w) {
+            cnt += sh.part[0][w];
+            kmin = min(kmin, sh.part[1][w]);
+            kmax = max(kmax, sh.part[2][w]);
+            ngm1 += sh.part[3][w];
+            ngm4 += sh.part[4][w];
+        }
+        if (cnt <= (uint32_t)K) return Threshold{1u, 0u, 0u, cnt};
+
+        lo = kmin;
+        hi = kmax;
+        known = true;
+        in_range = cnt;
+        if (kmax > kmin && (K <= 1024 ? ngm1 : ngm4) >= (uint32_t)K) {
+            BinPick bp;
+            if (K <= 1024) {
+                const uint32_t t1[1] = {max(max(gm[0], gm[1]), max(gm[2], gm[3]))};
+                bp = hist_pick(t1, lo, hi, (uint32_t)K, false, 0u, sh, second);
+            } else {
+                bp = hist_pick(gm, lo, hi, (uint32_t)K, false, 0u, sh, second);
+            }
+            if (second != 0u && next != nullptr) *next = KeyBound{lo + (bp.bin2 << bp.shift), hi};
+            lo = lo + (bp.bin << bp.shift);
+            known = lo == kmin;
+        }
     }
     uint32_t remaining = (uint32_t)K;
     for (int pass = 0; pass < 4; ++pass) {
@@ -1030,17 +1073,20 @@ __device__ __forceinline__ uint32_t kth_key_reg(const uint32_t (&k)[kSelKpt], co
 }
 
 // Select through the register path when the slot count allows it, else the
-// streaming path.  `ks` gives keys and indices of slots.
+// streaming path.  `ks` gives keys and indices of slots; kb, second and next
+// as for threshold_reg (the streaming path takes no bound and yields none).
 __device__ __forceinline__ void select_into(const KeySrc& ks, int K, int32_t* out, int32_t* lds_out,
-                                            SelShared& sh) {
+                                            SelShared& sh, KeyBound kb = {0u, 0u},
+                                            uint32_t second = 0u, KeyBound* next = nullptr) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (ks.n <= kSelRegSlots) {
         uint32_t k[kSelKpt];
         ks.load16((int64_t)wave * 1024 + 16 * lane, k);
         SelRegShared& rs = *reinterpret_cast<SelRegShared*>(&sh.hist[0]);
-        const Threshold th = threshold_reg(k, K, rs);
+        const Threshold th = threshold_reg(k, K, rs, kb, second, next);
         compact_reg(k, th, K, [&](int64_t s) { return ks.index(s); }, out, lds_out, rs);
     } else {
+        if (next != nullptr) *next = KeyBound{0u, 0u};
         const SelRange r = wave_range(ks.n, wave);
         const Threshold th = find_threshold<false>(ks, sh.keys, r, K, sh);
         compact<false>(ks, sh.keys, r, th, K, out, lds_out, sh);
@@ -1061,7 +1107,8 @@ static_assert(2 * kSuperCand <= kMaxPoolBlocks, "pool and superblock list share 
 __device__ __forceinline__ bool select_blocks_super(const uint32_t* __restrict__ bkeys,
                                                     const uint32_t* __restrict__ sbkeys,
                                                     int64_t nbv, int64_t nsv, int P,
-                                                    int32_t* pool_out, SelShared& sh) {
+                                                    int32_t* pool_out, SelShared& sh,
+                                                    uint32_t second, KeyBound* next) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     SelRegShared& rs = *reinterpret_cast<SelRegShared*>(&sh.hist[0]);
     const KeySrc sup{sbkeys, nullptr, nsv, (int)nsv, 0};
@@ -1092,13 +1139,19 @@ __device__ __forceinline__ bool select_blocks_super(const uint32_t* __restrict__
     __syncthreads();  // the list is complete
     // block s of the candidates is block 8 list[s / 8] + s % 8 (absent past nbv)
     const KeySrc cand{bkeys, list, (int64_t)total * kBlock, (int)nbv, 1};
-    select_into(cand, P, pool_out, sh.pool, sh);
+    select_into(cand, P, pool_out, sh.pool, sh, KeyBound{0u, 0u}, second, next);
     return true;
 }
 
 // Full layer for query bq: best P blocks (pool), then the best K positions
 // inside it.  pool_out may be null (internal pool).  sbkeys: null, or the
 // scan's superblock keys, used when the blocks do not fit the register path.
+// With K <= P, the block selection's group-maxima pass bounds the K-th
+// largest block key x from below by some y; the pool holds K blocks whose
+// keys are >= x (the P best include the K best), each block key is the key of
+// one of its positions, so K positions of the pool have keys >= y, and no
+// position key exceeds the largest block key: the position selection starts
+// from that bound.
 __device__ __forceinline__ void select_full_query(const uint32_t* __restrict__ keys,
                                                   const uint32_t* __restrict__ bkeys, int64_t cap,
                                                   int64_t bq, int nv, int P, int K,
@@ -1109,17 +1162,19 @@ __device__ __forceinline__ void select_full_query(const uint32_t* __restrict__ k
     const int64_t nsv = ((int64_t)nv + kSuper - 1) / kSuper;
     int32_t* prow = pool_out ? pool_out + bq * P : nullptr;
     bool done = false;
+    const uint32_t second = K <= P ? (uint32_t)K : 0u;
+    KeyBound nb{0u, 0u};
     if (sbkeys != nullptr && nbv > kSelRegSlots && nsv <= kSelRegSlots && P <= kSuperCand)
         done = select_blocks_super(bkeys + bq * (cap / kBlock), sbkeys + bq * (cap / kSuper), nbv,
-                                   nsv, P, prow, sh);
+                                   nsv, P, prow, sh, second, &nb);
     if (!done) {
         __syncthreads();
         KeySrc blocks{bkeys + bq * (cap / kBlock), nullptr, nbv, nv, 0};
-        select_into(blocks, P, prow, sh.pool, sh);
+        select_into(blocks, P, prow, sh.pool, sh, KeyBound{0u, 0u}, second, &nb);
     }
     __syncthreads();
     KeySrc pos{keys + bq * cap, sh.pool, (int64_t)P * kBlock, nv, 1};
-    select_into(pos, K, topk_out + bq * K, nullptr, sh);
+    select_into(pos, K, topk_out + bq * K, nullptr, sh, nb);
 }
 
 __global__ __launch_bounds__(kSelThreads) void k_select_full(
@@ -1132,9 +1187,37 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(
                       sh, sbkeys);
 }
 
-// Reindex: best K positions of the compact pool-ordered keys.
+// Lower bound of the K-th largest pool key from k_pool_score's wave summaries
+// (p: this lane's summaries of waves lane + 64 j, j < 4, valid below nw <=
+// 256; each the maxima of four disjoint groups of slots).  A wave whose
+// second-largest group maximum is non-zero holds two keys at or above it;
+// when such waves number at least K / 2, at least K keys lie at or above the
+// smallest of those values, and none above the largest maximum.  Every wave
+// reduces all summaries itself (no barrier).
+__device__ __forceinline__ KeyBound pool_bound(const uint4 (&p)[4], int nw, int K) {
+    const int lane = threadIdx.x & 63;
+    uint32_t n2 = 0, lo = 0xFFFFFFFFu, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const bool in = lane + 64 * j < nw;
+        const uint32_t a = max(p[j].x, p[j].y), b = min(p[j].x, p[j].y);
+        const uint32_t c = max(p[j].z, p[j].w), d = min(p[j].z, p[j].w);
+        const uint32_t second = max(min(a, c), max(b, d));
+        const bool two = in && second != 0u;
+        n2 += two;
+        lo = two ? min(lo, second) : lo;
+        hi = in ? max(hi, max(a, c)) : hi;
+    }
+    n2 = wave_sum(n2);
+    lo = wave_reduce(lo, [](uint32_t a, uint32_t b) { return min(a, b); });
+    hi = wave_reduce(hi, [](uint32_t a, uint32_t b) { return max(a, b); });
+    return 2u * n2 >= (uint32_t)K ? KeyBound{lo, hi} : KeyBound{0u, 0u};
+}
+
+// Reindex: best K positions of the compact pool-ordered keys; parts: the
+// scoring launch's wave summaries (ceil(P*8 / 64) per query).
 __global__ __launch_bounds__(kSelThreads) void k_select_pool(
-    const uint32_t* __restrict__ ckeys, const int32_t* __restrict__ pool, int P,
+    const uint32_t* __restrict__ ckeys, const uint4* __restrict__ parts, const int32_t* __restrict__ pool, int P,
     const int32_t* __restrict__ n_vis, int64_t cap, int K, int32_t* __restrict__ topk_out) {
     __shared__ SelShared sh;
     const int64_t bq = blockIdx.x;
@@ -1148,16 +1231,21 @@ __global__ __launch_bounds__(kSelThreads) void k_select_pool(
         }
     };
     if (ks.n <= kSelRegSlots) {
-        // compact keys do not go through the pool: their loads go out first,
-        // and the pool (needed only to name the selected positions) is staged
-        // meanwhile; the threshold search's first barrier orders it before
-        // compact_reg reads it
+        // the wave summaries and the compact keys (which do not go through
+        // the pool) are loaded first, and the pool (needed only to name the
+        // selected positions) is staged meanwhile; the threshold search's
+        // first barrier orders it before compact_reg reads it
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int nw = (P * kBlock + 63) / 64;
+        uint4 pw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pw[j] = parts[bq * nw + (lane + 64 * j < nw ? lane + 64 * j : 0)];
         uint32_t k[kSelKpt];
         ks.load16((int64_t)wave * 1024 + 16 * lane, k);
         stage_pool();
+        const KeyBound kb = pool_bound(pw, nw, K);
         SelRegShared& rs = *reinterpret_cast<SelRegShared*>(&sh.hist[0]);
-        const Threshold th = threshold_reg(k, K, rs);
+        const Threshold th = threshold_reg(k, K, rs, kb);
         compact_reg(k, th, K, [&](int64_t s) { return ks.index(s); }, topk_out + bq * K, nullptr,
                     rs);
     } else {
@@ -1525,12 +1613,12 @@ hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B,
 
 hipError_t launch_pool_score(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                              const float* iq, const float* iw, const int32_t* n_vis,
-                             const int32_t* pool, int P, uint32_t* ckeys, hipStream_t stream,
-                             int fmt) {
+                             const int32_t* pool, int P, uint32_t* ckeys, uint4* parts,
+                             hipStream_t stream, int fmt) {
     const int64_t n_slots = (int64_t)P * kBlock;
     dim3 grid((unsigned)((n_slots + 255) / 256), (unsigned)(B * Q));
     hipLaunchKernelGGL(fmt == 1 ? k_pool_score<1> : k_pool_score<0>, grid, dim3(256), 0, stream,
-                       ikc, iks, cap, Q, iq, iw, n_vis, pool, P, ckeys);
+                       ikc, iks, cap, Q, iq, iw, n_vis, pool, P, ckeys, parts);
     return hipGetLastError();
 }
 
@@ -1543,11 +1631,11 @@ hipError_t launch_select_full(const uint32_t* keys, const uint32_t* bkeys, int64
     return hipGetLastError();
 }
 
-hipError_t launch_select_pool(const uint32_t* ckeys, const int32_t* pool, int P,
-                              const int32_t* n_vis, int64_t cap, int64_t n_queries, int K,
+hipError_t launch_select_pool(const uint32_t* ckeys, const uint4* parts, const int32_t* pool,
+                              int P, const int32_t* n_vis, int64_t cap, int64_t n_queries, int K,
                               int32_t* topk_out, hipStream_t stream) {
     hipLaunchKernelGGL(k_select_pool, dim3((unsigned)n_queries), dim3(kSelThreads), 0, stream,
-                       ckeys, pool, P, n_vis, cap, K, topk_out);
+                       ckeys, parts, pool, P, n_vis, cap, K, topk_out);
     return hipGetLastError();
 }
 

@@ -93,10 +93,11 @@ constexpr int64_t kChunkPoolMaxBlocks = 16384;
 inline int chunk_cand_halves(int K) { return 3 * K < 512 ? 512 : 3 * K; }
 // the MFMA scan path takes top-K up to this (its candidates' keys stay in LDS)
 constexpr int kChunkMaxTopk = 1024;
+// parts: [B*Q][ceil(P*8 / 64)] wave summaries of the keys for the selection
 hipError_t launch_pool_score(const uint8_t* ikc, const float* iks, int64_t cap, int B, int Q,
                              const float* iq, const float* iw, const int32_t* n_vis,
-                             const int32_t* pool, int P, uint32_t* ckeys, hipStream_t stream,
-                             int fmt = kIdxFp8);
+                             const int32_t* pool, int P, uint32_t* ckeys, uint4* parts,
+                             hipStream_t stream, int fmt = kIdxFp8);
 // FP4 indexer keys of n_rows fp32 rows [n_rows][64] into the 2-plane tiles and
 // the per-row scale bytes (row dst_rows[r], or r)
 hipError_t launch_quant_idx4(const float* x, int64_t n_rows, const int64_t* dst_rows,
@@ -107,8 +108,8 @@ hipError_t launch_select_full(const uint32_t* keys, const uint32_t* bkeys, int64
                               const int32_t* n_vis, int64_t n_queries, int P, int K,
                               int32_t* pool_out, int32_t* topk_out, hipStream_t stream,
                               const uint32_t* sbkeys = nullptr);
-hipError_t launch_select_pool(const uint32_t* ckeys, const int32_t* pool, int P,
-                              const int32_t* n_vis, int64_t cap, int64_t n_queries, int K,
+hipError_t launch_select_pool(const uint32_t* ckeys, const uint4* parts, const int32_t* pool,
+                              int P, const int32_t* n_vis, int64_t cap, int64_t n_queries, int K,
                               int32_t* topk_out, hipStream_t stream);
 
 // streaming probes (csa2_probe.hip): mode 0 reads n_bytes of src (one word

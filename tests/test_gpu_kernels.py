@@ -367,6 +367,9 @@ def test_index_full_all_ties_streaming_blocks(gpu, oracle_mod):
 
 @pytest.mark.parametrize("B,cap,nvis,pool,topk", [(2, 8192, [8192, 5001], 512, 512),
                                                   (3, 32768, [32768, 30000, 77], 2048, 512),
+                                                  # part of the pool past the visible blocks
+                                                  (2, 16384, [16384, 14001], 2048, 256),
+                                                  (1, 131072, [131067], 2048, 511),
                                                   (1, 4096, [4096], 64, 100),
                                                   (1, 65536, [65531], 4096, 2048)])
 def test_index_reindex_bit_exact(gpu, oracle_mod, B, cap, nvis, pool, topk):
@@ -399,6 +402,40 @@ def test_full_topk_equals_reindex_with_own_query(gpu, oracle_mod):
     gpu.index_full(cache, iq, iw, nv, tk, pl, topk=512, pool_blocks=2048)
     gpu.index_reindex(cache, iq, iw, nv, pl, tk2, topk=512)
     np.testing.assert_array_equal(host(tk), host(tk2))
+
+
+@pytest.mark.parametrize("n_vals,topk", [(1, 512), (2, 512), (3, 511), (6, 512)])
+def test_index_few_valued_scores(gpu, oracle_mod, n_vals, topk):
+    """Key rows drawn from a few vectors, so every score takes one of a few
+    values: the selections start from lower bounds of the cut (the block
+    selection's group maxima for the Full layer's positions, the pool
+    scoring's group maxima for Reindex) and meet heavy ties at and above it.
+    4096 blocks, pool 2048, Full and Reindex against the oracle."""
+    say(f"index_full / reindex with {n_vals}-valued scores, topk={topk}")
+    B, cap = 2, 32768
+    g = np.random.default_rng(70 + n_vals)
+    base = g.standard_normal((n_vals, 64)).astype(np.float32)
+    p = 0.5 ** np.arange(n_vals)
+    x = base[g.choice(n_vals, size=(B, cap), p=p / p.sum())]
+    ikc, iks = oracle_mod.quant_fp8_rows(x)
+    cache = gpu.Cache(B, cap)
+    cache.ik_codes.copy_(dev(tile_ik(ikc)))
+    cache.ik_sigma.copy_(dev(iks.reshape(-1)))
+    iq = g.standard_normal((B, 1, 4, 64)).astype(np.float32)
+    iw = g.random((B, 1, 4)).astype(np.float32)
+    iq2 = g.standard_normal((B, 1, 4, 64)).astype(np.float32)
+    iw2 = g.random((B, 1, 4)).astype(np.float32)
+    nv = np.array([[32765], [30001]], np.int32)
+    tk_ref, pl_ref = oracle_mod.index_full_batch(ikc, iks, iq, iw, nv, topk, 2048)
+    tk = torch.full((B, 1, topk), -7, dtype=torch.int32, device="cuda")
+    pl = torch.full((B, 1, 2048), -7, dtype=torch.int32, device="cuda")
+    gpu.index_full(cache, dev(iq), dev(iw), dev(nv), tk, pl, topk=topk, pool_blocks=2048)
+    np.testing.assert_array_equal(host(pl), pl_ref)
+    np.testing.assert_array_equal(host(tk), tk_ref)
+    tk2_ref = oracle_mod.index_reindex_batch(ikc, iks, iq2, iw2, nv, pl_ref, topk)
+    tk2 = torch.full((B, 1, topk), -7, dtype=torch.int32, device="cuda")
+    gpu.index_reindex(cache, dev(iq2), dev(iw2), dev(nv), dev(pl_ref), tk2, topk=topk)
+    np.testing.assert_array_equal(host(tk2), tk2_ref)
 
 
 # --------------------------------------------------------------------------- attention
