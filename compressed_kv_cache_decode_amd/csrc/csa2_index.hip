@@ -164,23 +164,32 @@ __device__ __forceinline__ void fmac_heads(float (&acc)[kIdxHeads], const QQuad&
     for (int h = 0; h < kIdxHeads; ++h) acc[h] = fmac_bcast<(C >> 2)>(acc[h], q.v[h][C & 3], k);
 }
 
-template <int... C>
-__device__ __forceinline__ void fp8_dots(float (&dot)[kIdxHeads], const QQuad& q,
-                                         const float (&kf)[kIdxDim],
-                                         std::integer_sequence<int, C...>) {
-    (fmac_heads<C>(dot, q, kf[C]), ...);
-}
-
-// channels 16g .. 16g + 15 of group g = G: the group sums, then the scaled
-// add into each head's dot
+// channels 16g .. 16g + 15 of group g = G (words 2 (G % 2) and 2 (G % 2) + 1
+// of plane G / 2), decoded right before their multiply-adds: the group sums,
+// then the scaled add into each head's dot (the scheduling barrier keeps the
+// next group's decode below these)
 template <int G, int... J>
 __device__ __forceinline__ void fp4_group(float (&dot)[kIdxHeads], const QQuad& q,
-                                          const float (&kf)[kIdxDim], float sg,
+                                          const uint4& plane, float sg,
                                           std::integer_sequence<int, J...>) {
+    const uint32_t w[2] = {(G & 1) ? plane.z : plane.x, (G & 1) ? plane.w : plane.y};
+    float kf[16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        // byte b of the word: channels 2b (low nibble) and 2b + 1
+        const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 0);
+        const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 1);
+        const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 2);
+        const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.0f, 3);
+        float* o = kf + 8 * i;
+        o[0] = v0[0]; o[1] = v0[1]; o[2] = v1[0]; o[3] = v1[1];
+        o[4] = v2[0]; o[5] = v2[1]; o[6] = v3[0]; o[7] = v3[1];
+    }
     float inner[kIdxHeads] = {0.0f, 0.0f, 0.0f, 0.0f};
-    (fmac_heads<16 * G + J>(inner, q, kf[16 * G + J]), ...);
+    (fmac_heads<16 * G + J>(inner, q, kf[J]), ...);
 #pragma unroll
     for (int h = 0; h < kIdxHeads; ++h) dot[h] = fmaf(sg, inner[h], dot[h]);
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ __forceinline__ float weigh_heads(const float (&dot)[kIdxHeads],
@@ -195,27 +204,49 @@ __device__ __forceinline__ float weigh_heads(const float (&dot)[kIdxHeads],
     return t;
 }
 
+// channels 16G .. 16G + 15 (plane G of the row), decoded right before their
+// multiply-adds: the plane waits for its own load only, and at most 16
+// decoded values are live (the scheduling barrier keeps the next plane's
+// decode from being hoisted above these)
+template <int G, int... J>
+__device__ __forceinline__ void fp8_plane(float (&dot)[kIdxHeads], const QQuad& q, const uint4& raw,
+                                          std::integer_sequence<int, J...>) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    float kf[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float2 lo = e4m3x2_to_f32<false>(w[i]);
+        const float2 hi = e4m3x2_to_f32<true>(w[i]);
+        kf[4 * i + 0] = lo.x;
+        kf[4 * i + 1] = lo.y;
+        kf[4 * i + 2] = hi.x;
+        kf[4 * i + 3] = hi.y;
+    }
+    (fmac_heads<16 * G + J>(dot, q, kf[J]), ...);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ float score_row_q(const uint4 (&raw)[4], float sigma, const QQuad& q,
                                              const float* __restrict__ wq) {
-    float kf[kIdxDim];
-    decode_fp8_row(raw, kf);
     float dot[kIdxHeads] = {0.0f, 0.0f, 0.0f, 0.0f};
-    fp8_dots(dot, q, kf, std::make_integer_sequence<int, kIdxDim>{});
+    constexpr auto kP = std::make_integer_sequence<int, 16>{};
+    fp8_plane<0>(dot, q, raw[0], kP);
+    fp8_plane<1>(dot, q, raw[1], kP);
+    fp8_plane<2>(dot, q, raw[2], kP);
+    fp8_plane<3>(dot, q, raw[3], kP);
     return sigma * weigh_heads(dot, wq);
 }
 
 __device__ __forceinline__ float score_row4_q(const uint4 (&raw)[2], uint32_t sc4, const QQuad& q,
                                               const float* __restrict__ wq) {
-    float kf[kIdxDim];
-    decode_fp4_row(raw, kf);
     const float2 s01 = e4m3x2_to_f32<false>(sc4);
     const float2 s23 = e4m3x2_to_f32<true>(sc4);
     float dot[kIdxHeads] = {0.0f, 0.0f, 0.0f, 0.0f};
     constexpr auto kG = std::make_integer_sequence<int, 16>{};
-    fp4_group<0>(dot, q, kf, s01.x, kG);
-    fp4_group<1>(dot, q, kf, s01.y, kG);
-    fp4_group<2>(dot, q, kf, s23.x, kG);
-    fp4_group<3>(dot, q, kf, s23.y, kG);
+    fp4_group<0>(dot, q, raw[0], s01.x, kG);
+    fp4_group<1>(dot, q, raw[0], s01.y, kG);
+    fp4_group<2>(dot, q, raw[1], s23.x, kG);
+    fp4_group<3>(dot, q, raw[1], s23.y, kG);
     return weigh_heads(dot, wq);
 }
 
@@ -291,7 +322,9 @@ __device__ __forceinline__ void scan_query_exact(const uint8_t* __restrict__ ikc
 // FMT 0: FP8 keys (iks = fp32 sigma per row); FMT 1: FP4 keys (iks = the
 // rows' four E4M3 scale bytes, read as one 32-bit word per row).
 // iq [B*Q][4][64], iw [B*Q][4]: the queries and head weights as given.
-template <int FMT>
+// ONE: one query per sequence (Q == 1), which then needs no loop: the query
+// channel, loaded before the key row, is waited for alone.
+template <int FMT, bool ONE>
 __global__ __launch_bounds__(256) void k_scan(const uint8_t* __restrict__ ikc,
                                               const float* __restrict__ iks, int64_t cap, int Q,
                                               const float* __restrict__ iq,
@@ -303,7 +336,9 @@ __global__ __launch_bounds__(256) void k_scan(const uint8_t* __restrict__ ikc,
     __shared__ __attribute__((aligned(16))) float sq[kIdxHeads * kIdxDim];
     __shared__ float sw[kIdxHeads];
     const int b = blockIdx.y;
-    const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
+    // h is the wave's index: taken as wave-uniform, the head weights load
+    // through the scalar cache and no vector wait orders them
+    const int lane = threadIdx.x & 63, h = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t p0 = (int64_t)blockIdx.x * 256;
     const int64_t p = p0 + threadIdx.x;
     int nv_max = 0;
@@ -314,26 +349,22 @@ __global__ __launch_bounds__(256) void k_scan(const uint8_t* __restrict__ ikc,
     const bool live = p0 + (threadIdx.x & ~63) < cap;
 
     // loads complete in issue order: the first query's channel and weight
-    // (from L2), then the key row
+    // (from L2), then the key row (a wave past cap reads the sequence's first
+    // rows and scores nothing)
     float x = iq[((int64_t)b * Q * kIdxHeads + h) * kIdxDim + lane];
     float wh = iw[(int64_t)b * Q * kIdxHeads + h];
+    __builtin_amdgcn_sched_barrier(0);  // keep the channel's load ahead of the row's
     IdxRow<FMT> r;
-    if (live) r.load(ikc, iks, (int64_t)b * cap + p);
+    r.load(ikc, iks, (int64_t)b * cap + (live ? p : lane));
     const int64_t nb = cap / kBlock;
-    for (int q = 0; q < Q; ++q) {
-        const int64_t bq = (int64_t)b * Q + q;
-        const int nv = clamp_nvis(n_vis[bq], cap);
-        if (p0 >= nv) continue;  // uniform over the block
-        if (q > 0) {
-            x = iq[(bq * kIdxHeads + h) * kIdxDim + lane];
-            wh = iw[bq * kIdxHeads + h];
-            __syncthreads();  // the previous query's readers are done
-        }
+    // one query: quantise it in the workgroup, score the row, write the keys
+    const auto one_query = [&](int64_t bq, int nv, float xq, float wq) {
         float sqh;
-        sq[h * kIdxDim + lane] = quantise_query_channel(x, sqh);
-        if (lane == 0) sw[h] = wh * sqh;
+        sq[h * kIdxDim + lane] = quantise_query_channel(xq, sqh);
+        if (lane == 0) sw[h] = wq * sqh;
         __syncthreads();
-        if (!live) continue;  // uniform over the wave
+        __builtin_amdgcn_sched_barrier(0);  // the row is decoded after the barrier
+        if (!live) return;  // uniform over the wave
         QQuad qq;
         qq.load(sq);
         const float s = r.score(qq, sw);  // every lane of the wave is active
@@ -345,6 +376,21 @@ __global__ __launch_bounds__(256) void k_scan(const uint8_t* __restrict__ ikc,
             const uint32_t sk = wave_max_of_groups8(bk);
             if ((threadIdx.x & 63) == 0) sbkeys[bq * (cap / kSuper) + (p / kSuper)] = sk;
         }
+    };
+    if constexpr (ONE) {
+        one_query(b, nv_max, x, wh);  // p0 < nv_max, the one query's count
+        return;
+    }
+    for (int q = 0; q < Q; ++q) {
+        const int64_t bq = (int64_t)b * Q + q;
+        const int nv = clamp_nvis(n_vis[bq], cap);
+        if (p0 >= nv) continue;  // uniform over the block
+        if (q > 0) {
+            x = iq[(bq * kIdxHeads + h) * kIdxDim + lane];
+            wh = iw[bq * kIdxHeads + h];
+            __syncthreads();  // the previous query's readers are done
+        }
+        one_query(bq, nv, x, wh);
     }
 }
 
@@ -511,7 +557,7 @@ __global__ __launch_bounds__(256) void k_pool_score(const uint8_t* __restrict__ 
     // the pool or outside the visible positions reads the sequence's first
     // row and is not scored), so the quantisation below waits for nothing
     // and runs while the rows are in flight.
-    const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, h = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float x = iq[(bq * kIdxHeads + h) * kIdxDim + lane];
     const float wh = iw[bq * kIdxHeads + h];
     const int nv = clamp_nvis(n_vis[bq], cap);
@@ -526,6 +572,9 @@ __global__ __launch_bounds__(256) void k_pool_score(const uint8_t* __restrict__ 
         if (lane == 0) sw[h] = wh * sqh;
     }
     __syncthreads();
+    // nothing of the row is decoded before the barrier: a wave waits for its
+    // own rows only, not for the slowest wave's
+    __builtin_amdgcn_sched_barrier(0);
     // every lane scores (with the whole wave active), the absent ones are dropped
     QQuad qq;
     qq.load(sq);
@@ -1597,7 +1646,8 @@ hipError_t launch_scan(const uint8_t* ikc, const float* iks, int64_t cap, int B,
         const hipError_t e = launch_prep_iq(iq, iw, (int64_t)B * Q, qd, wq, stream);
         if (e != hipSuccess) return e;
     }
-    auto kern = fmt == 1 ? k_scan<1> : (multi ? k_scan_multi : k_scan<0>);
+    auto kern = fmt == 1 ? (Q == 1 ? k_scan<1, true> : k_scan<1, false>)
+                         : (multi ? k_scan_multi : (Q == 1 ? k_scan<0, true> : k_scan<0, false>));
     const float* qa = multi ? qd : iq;
     const float* wa = multi ? wq : iw;
     if (start != nullptr && stop != nullptr) {
