@@ -911,41 +911,52 @@ def run_attn_sweep(args):
             "sweep": sweep}
 
 
+# the read probes that cover the buffer with one grid (the others grid-stride)
+PROBE_FORM = {2: "one load per thread", 3: "one 16 KB chunk per workgroup"}
+
+
 def measure_ceilings(mib=1024, reps=10):
     """Streaming ceilings of this GPU, measured in the same run with the
     library's probe kernels (csa2_stream_probe): a read-only pass over `mib`
     MiB and a copy of `mib` MiB (reads and writes `mib` MiB each), 16-byte
     non-temporal loads, best of a few grid sizes, each the mean of `reps`
-    back-to-back launches timed with events."""
+    back-to-back launches timed with events (queued behind a bounded spin, so
+    that the host's launch path is not inside the interval)."""
     import torch
 
     import compressed_kv_cache_decode_amd as csa2
     n = mib << 20
     src = torch.ones(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
+    sink = torch.empty(8192, dtype=torch.int32, device="cuda")
     best = {}
-    configs = [(0, b) for b in (1024, 2048, 4096, 8192)] + [(2, 1)] + \
+    configs = [(0, b) for b in (1024, 2048, 4096, 8192)] + [(2, 1), (3, 1)] + \
               [(1, b) for b in (1024, 2048, 4096, 8192)]
     for mode, blocks in configs:
+        probe = (lambda: csa2.stream_probe(1, src, dst, n_blocks=blocks)) if mode == 1 else \
+                (lambda: csa2.stream_probe(mode, src, sink=sink, n_blocks=blocks))
         for _ in range(2):
-            csa2.stream_probe(mode, src, dst if mode == 1 else None, n_blocks=blocks)
+            probe()
         torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(int(1e6 * reps))  # lets the host queue every launch
         ev[0].record()
         for _ in range(reps):
-            csa2.stream_probe(mode, src, dst if mode == 1 else None, n_blocks=blocks)
+            probe()
         ev[1].record()
         torch.cuda.synchronize()
         sec = ev[0].elapsed_time(ev[1]) * 1e-3 / reps
         kind = 1 if mode == 1 else 0
         gbs = (2 * n if kind else n) / sec / 1e9
         if gbs > best.get(kind, (0, ""))[0]:
-            best[kind] = (gbs, "one load per thread" if mode == 2 else f"{blocks} workgroups")
+            best[kind] = (gbs, PROBE_FORM.get(mode, f"{blocks} workgroups"))
     del src, dst
     torch.cuda.empty_cache()
     out = {"read_GBps": round(best[0][0], 1), "copy_GBps": round(best[1][0], 1), "bytes": n,
            "how": f"csa2_stream_probe over {mib} MiB (read; copy = reads + writes), best of "
-                  f"grid-stride 1024-8192 workgroups and one load per thread (read: "
+                  f"grid-stride 1024-8192 workgroups, one load per thread and 16 KB chunks per "
+                  f"workgroup (read: "
                   f"{best[0][1]}; copy: {best[1][1]}), mean of {reps} launches"}
     log(f"ceilings: read {out['read_GBps']} GB/s, copy {out['copy_GBps']} GB/s")
     return out
@@ -955,10 +966,14 @@ def measure_read_at(nbytes, copies=3, reps=12):
     """The streaming-read ceiling at one transfer size: csa2_stream_probe
     reading `nbytes` (rounded up to 16) from one of `copies` buffers in turn
     (together larger than the last-level cache, so reads come from HBM),
-    each launch timed alone with events; the best of one load per thread and
-    grid-stride 2048-8192 workgroups, median over `reps` launches.  A small
-    transfer does not reach the large-transfer ceiling (ramp-up and tail), so
-    a kernel moving that many bytes is compared with this."""
+    each launch timed by the events recorded just before and after it, with
+    the launches queued behind a bounded spin so that the host's launch path
+    is not inside any interval (the GPU runs them back to back, as the scan
+    is timed); the best of one load per thread, 16 KB chunks per workgroup
+    (the scan's own access) and grid-stride 2048-8192 workgroups, median over
+    `reps` launches.  A small transfer does not reach the large-transfer
+    ceiling (ramp-up and tail), so a kernel moving that many bytes is compared
+    with this."""
     import statistics
 
     import torch
@@ -966,27 +981,30 @@ def measure_read_at(nbytes, copies=3, reps=12):
     import compressed_kv_cache_decode_amd as csa2
     n = (nbytes + 15) // 16 * 16
     bufs = [torch.ones(n, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    sink = torch.empty(8192, dtype=torch.int32, device="cuda")
     best = (0.0, "")
-    for mode, blocks in ((2, 1), (0, 2048), (0, 4096), (0, 8192)):
+    for mode, blocks in ((2, 1), (3, 1), (0, 2048), (0, 4096), (0, 8192)):
         for b in bufs:
-            csa2.stream_probe(mode, b, n_blocks=blocks)
+            csa2.stream_probe(mode, b, sink=sink, n_blocks=blocks)
         torch.cuda.synchronize()
-        us = []
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(int(1e6 * reps))  # lets the host queue every launch
+        ev[0].record()
         for i in range(reps):
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            ev[0].record()
-            csa2.stream_probe(mode, bufs[i % copies], n_blocks=blocks)
-            ev[1].record()
-            torch.cuda.synchronize()
-            us.append(ev[0].elapsed_time(ev[1]) * 1e3)
+            csa2.stream_probe(mode, bufs[i % copies], sink=sink, n_blocks=blocks)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        us = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps)]
         gbs = n / statistics.median(us) / 1e3
         if gbs > best[0]:
-            best = (gbs, "one load per thread" if mode == 2 else f"{blocks} workgroups")
+            best = (gbs, PROBE_FORM.get(mode, f"{blocks} workgroups"))
     del bufs
     torch.cuda.empty_cache()
     return {"bytes": n, "read_GBps": round(best[0], 1),
             "how": f"csa2_stream_probe reading {n} bytes from one of {copies} buffers in turn, "
-                   f"each launch timed alone, median of {reps} ({best[1]})"}
+                   f"launches queued back to back behind a spin, each timed by the events "
+                   f"around it, median of {reps} ({best[1]})"}
 
 
 def with_same_size_read(entry, cache):

@@ -511,8 +511,9 @@ def codec_probe(x, stream=None):
 
 def stream_probe(mode, src, dst=None, sink=None, n_blocks=2048, stream=None):
     """Diagnostics: mode 0 streams src (u8, a multiple of 16 bytes) with
-    16-byte loads (grid-stride), mode 2 with one load per thread, mode 1
-    copies it to dst (csa2_stream_probe)."""
+    16-byte loads (grid-stride), mode 2 with one load per thread, mode 3 in
+    16 KB chunks (one per workgroup, four loads per thread), mode 1 copies it
+    to dst (csa2_stream_probe)."""
     if sink is None and mode != 1:
         sink = torch.empty(n_blocks, dtype=torch.int32, device=src.device)
     rc = lib().csa2_stream_probe(mode, _ptr(src, torch.uint8, "src"),

@@ -373,7 +373,7 @@ __attribute__((visibility("default"))) int csa2_index_full(
 __attribute__((visibility("default"))) int csa2_stream_probe(int mode, const void* src, void* dst,
                                                              size_t n_bytes, uint32_t* sink,
                                                              int n_blocks, hipStream_t stream) {
-    if (mode < 0 || mode > 2 || !src || n_bytes % 16 != 0 || n_blocks < 1 || n_blocks > 65535)
+    if (mode < 0 || mode > 3 || !src || n_bytes % 16 != 0 || n_blocks < 1 || n_blocks > 65535)
         return CSA2_E_ARG;
     if ((mode != 1 && !sink) || (mode == 1 && !dst)) return CSA2_E_ARG;
     if (n_bytes == 0) return CSA2_OK;

@@ -8,7 +8,10 @@
 // loads in flight per step of a grid-stride loop over n_blocks workgroups;
 // the read pass folds what it loads into one XOR per thread and writes one
 // word per workgroup, so the loads cannot be dropped.  Mode 2 (read): one
-// 16-byte load per thread over a grid that covers the buffer.
+// 16-byte load per thread over a grid that covers the buffer.  Mode 3 (read):
+// one 16 KB chunk per workgroup, four 16-byte loads per thread 4 KB apart (the
+// indexer scan's access: a 256-position tile of 64-byte rows), a grid that
+// covers the buffer.
 #include <hip/hip_ext.h>
 
 #include "csa2_device.hpp"
@@ -67,6 +70,25 @@ __global__ __launch_bounds__(kProbeThreads) void k_stream_read1(const u32x4_t* _
         const u32x4_t v = __builtin_nontemporal_load(src + i);
         acc = v[0] ^ v[1] ^ v[2] ^ v[3];
     }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, 64);
+    if ((threadIdx.x & 63) == 0 && acc == 0x9E3779B9u) sink[0] = acc;  // keeps the loads
+}
+
+// one 16 KB chunk per workgroup, four 16-byte loads per thread, a grid that
+// covers the whole buffer
+__global__ __launch_bounds__(kProbeThreads) void k_stream_read_chunk(const u32x4_t* __restrict__ src,
+                                                                     int64_t n16, uint32_t* sink) {
+    const int64_t i0 = (int64_t)blockIdx.x * (kProbeUnroll * kProbeThreads) + threadIdx.x;
+    u32x4_t v[kProbeUnroll];
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) {
+        const int64_t i = i0 + u * kProbeThreads;
+        v[u] = i < n16 ? __builtin_nontemporal_load(src + i) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    uint32_t acc = 0;
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, 64);
     if ((threadIdx.x & 63) == 0 && acc == 0x9E3779B9u) sink[0] = acc;  // keeps the loads
@@ -162,11 +184,13 @@ hipError_t launch_gather_probe(const uint8_t* kvc, const uint8_t* kvs, const int
 hipError_t launch_stream_probe(int mode, const void* src, void* dst, size_t n_bytes,
                                uint32_t* sink, int n_blocks, hipStream_t stream) {
     const int64_t n16 = (int64_t)(n_bytes / 16);
-    if (mode == 2) {
-        const int64_t blocks = (n16 + kProbeThreads - 1) / kProbeThreads;
+    if (mode == 2 || mode == 3) {
+        const int64_t per = mode == 2 ? kProbeThreads : kProbeUnroll * kProbeThreads;
+        const int64_t blocks = (n16 + per - 1) / per;
         if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(k_stream_read1, dim3((unsigned)blocks), dim3(kProbeThreads), 0, stream,
-                           static_cast<const u32x4_t*>(src), n16, sink);
+        hipLaunchKernelGGL(mode == 2 ? k_stream_read1 : k_stream_read_chunk, dim3((unsigned)blocks),
+                           dim3(kProbeThreads), 0, stream, static_cast<const u32x4_t*>(src), n16,
+                           sink);
         return hipGetLastError();
     }
     if (mode == 0)

@@ -432,8 +432,11 @@ int csa2_abi_version(void);
  * writes one word per workgroup to sink [n_blocks]; mode 1 copies n_bytes of
  * src to dst; both grid-stride over n_blocks workgroups of 256 threads, four
  * loads in flight per thread.  mode 2 reads src with one 16-byte load per
- * thread over a grid covering it (n_blocks unused; sink [1] is written only
- * by a data-dependent test that keeps the loads).  n_bytes a multiple of 16;
+ * thread over a grid covering it; mode 3 reads it in 16 KB chunks, one per
+ * workgroup of 256 threads, four 16-byte loads per thread 4 KB apart (the
+ * indexer scan's access), over a grid covering it (modes 2 and 3: n_blocks
+ * unused; sink [1] is written only by a data-dependent test that keeps the
+ * loads).  n_bytes a multiple of 16;
  * device pointers; enqueued on `stream`.  CSA2_E_ARG for a bad mode, size or
  * null pointer.
  */

@@ -258,7 +258,8 @@ def test_probes_reject_bad_arguments_before_touching_the_gpu(lib):
     """The measurement probes (stream and gather) validate their scalars and
     pointers on the host."""
     s = lib.csa2_stream_probe
-    assert s(3, FAKE, FAKE, 64, FAKE, 16, None) == -1          # mode
+    assert s(4, FAKE, FAKE, 64, FAKE, 16, None) == -1          # mode
+    assert s(-1, FAKE, FAKE, 64, FAKE, 16, None) == -1         # mode
     assert s(0, FAKE, None, 63, FAKE, 16, None) == -1          # not a multiple of 16
     assert s(0, FAKE, None, 64, None, 16, None) == -1          # read without a sink
     assert s(1, FAKE, None, 64, None, 16, None) == -1          # copy without dst

@@ -32,6 +32,23 @@ def test_stream_copy_probe_copies(gpu):
     assert torch.equal(src, dst)
 
 
+@pytest.mark.parametrize("mode", [0, 2, 3])
+def test_stream_read_probes_cover_a_ragged_buffer(gpu, mode):
+    """The read probes run over a buffer that is not a whole number of their
+    chunks (the last workgroup partly past it) and leave the sink untouched:
+    only a data-dependent test on an all-ones buffer could write it (mode 0
+    writes its per-workgroup XOR, zero for an even number of equal words)."""
+    say(f"stream read mode {mode}, 3 MiB + 48 bytes")
+    src = torch.ones((3 << 20) + 48, dtype=torch.uint8, device="cuda")
+    sink = torch.full((300,), 7, dtype=torch.int32, device="cuda")
+    gpu.stream_probe(mode, src, sink=sink, n_blocks=300)
+    torch.cuda.synchronize()
+    if mode == 0:
+        assert torch.all(sink == 0)
+    else:
+        assert torch.all(sink == 7)
+
+
 @pytest.mark.parametrize("B,cap,H,topk", [(3, 1024, 16, 512), (2, 4096, 64, 700), (1, 256, 128, 5)])
 def test_gather_probe_reads_the_attention_bytes(gpu, B, cap, H, topk):
     say(f"gather B={B} cap={cap} H={H} topk={topk}")
