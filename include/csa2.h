@@ -62,7 +62,9 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 3
+/* 4: the Reindex workspace also holds the pool scoring's per-wave summaries
+ * (csa2_workspace_size reports the size); csa2_stream_probe mode 3. */
+#define CSA2_ABI_VERSION 4
 
 #define CSA2_HEAD_DIM 128        /* main K and V width */
 #define CSA2_KV_CODE_BYTES 128   /* per entry: K 64 B | V 64 B */

@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.csa2_abi_version() == 3
+    assert lib.csa2_abi_version() == 4
     for st in (0, -1, -2, -3, -4):
         assert lib.csa2_status_str(st)
     assert lib.csa2_status_str(12345) == b"unknown status"
