@@ -147,6 +147,11 @@ def test_workspace_sizes(lib):
     assert 16 * 131072 * 4.5 <= n_full < 16 * 131072 * 4.5 + (1 << 20)
     assert ws(1, 16, 1, 131072, 512, 0, 0) == n_full         # internal pool lives in LDS
     assert ws(2, 16, 1, 131072, 512, 2048, 0) >= 16 * 2048 * 8 * 4
+    # Reindex: the pool keys (4 B per pool position) and a 16-byte summary
+    # per 64 of them (the selection's lower bound), each 256-byte aligned
+    al = lambda n: (n + 255) // 256 * 256
+    assert ws(2, 16, 1, 131072, 512, 2048, 0) == al(16 * 2048 * 8 * 4) + al(16 * 256 * 16)
+    assert ws(2, 3, 1, 4096, 100, 61, 0) == al(3 * 61 * 8 * 4) + al(3 * 8 * 16)
     assert ws(1, 16, 1, 1000, 512, 2048, 0) == big
     assert ws(99, 1, 1, 64, 1, 1, 16) == big
     assert ws(5, 16, 1, 131072, 512, 0, 64) == 16 * 16 * 4672  # staged records
