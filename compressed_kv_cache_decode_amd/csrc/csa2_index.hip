@@ -1356,6 +1356,10 @@ __device__ __forceinline__ void topk_of_halves(const uint8_t* __restrict__ ikc,
                                                int K, int32_t* out, SelRegShared& rs) {
     const int tid = threadIdx.x;
     const int n_slots = (int)n_c * kHalf;
+    // the query's values held in registers and broadcast by DPP, as in k_scan
+    QQuad qq;
+    qq.load(qrow);
+    const float w4[kIdxHeads] = {wrow[0], wrow[1], wrow[2], wrow[3]};
     for (int s0 = 0; s0 < n_slots; s0 += 2 * kSelThreads) {
         IdxRow<FMT> r[2];
         bool vis[2];
@@ -1364,12 +1368,16 @@ __device__ __forceinline__ void topk_of_halves(const uint8_t* __restrict__ ikc,
             const int s = s0 + u * kSelThreads + tid;
             const int64_t pos = s < n_slots ? (int64_t)list[s >> 2] * kHalf + (s & 3) : nv;
             vis[u] = pos < nv;
-            if (vis[u]) r[u].load(ikc, iks, row0 + pos);
+            r[u].load(ikc, iks, row0 + (vis[u] ? pos : 0));  // an absent slot reads row 0
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int s = s0 + u * kSelThreads + tid;
-            if (s < n_slots) ck[s] = vis[u] ? score_key(r[u].score(qrow, wrow)) : 0u;
+            // a wave with no slot left skips the round; otherwise every lane
+            // scores (DPP reads other lanes) and the absent ones are dropped
+            if (__ballot(s < n_slots) == 0) continue;
+            const float sc = r[u].score(qq, w4);
+            if (s < n_slots) ck[s] = vis[u] ? score_key(sc) : 0u;
         }
     }
     __syncthreads();
