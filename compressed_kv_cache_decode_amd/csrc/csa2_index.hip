@@ -1568,17 +1568,20 @@ __global__ __launch_bounds__(kSelThreads) void k_chunk_select_pool(
         __syncthreads();
         // exact block keys: a block's 8 positions on 8 consecutive lanes (the
         // trip count is uniform, so every lane takes part in the group max)
+        // (the query in registers, broadcast by DPP: every lane of a wave
+        // scores, an absent position reads row 0 and is dropped)
         const int n_pos = (int)n_und * kBlock;
+        QQuad qq;
+        qq.load(qrow);
+        const float w4[kIdxHeads] = {wrow[0], wrow[1], wrow[2], wrow[3]};
         for (int s0 = 0; s0 < n_pos; s0 += kSelThreads) {
             const int s = s0 + tid;
             const int64_t pos = s < n_pos ? (int64_t)ulist[s >> 3] * kBlock + (s & 7) : nv;
-            uint32_t key = 0u;
-            if (pos < nv) {
-                IdxRow<FMT> r;
-                r.load(ikc, iks, row0 + pos);
-                key = score_key(r.score(qrow, wrow));
-            }
-            key = max8_u32(key);
+            if (__ballot(s < n_pos) == 0) continue;  // uniform over the wave
+            IdxRow<FMT> r;
+            r.load(ikc, iks, row0 + (pos < nv ? pos : 0));
+            const float sc = r.score(qq, w4);
+            const uint32_t key = max8_u32(pos < nv ? score_key(sc) : 0u);
             if (s < n_pos && (s & 7) == 0) ukey[s >> 3] = key;
         }
         __syncthreads();
